@@ -1,0 +1,225 @@
+/*
+ * lbq.h - C ABI of the packed low-bit GEMV library (liblbq.so) for AMD MI355X (gfx950).
+ *
+ * Three packed-weight formats, each with a host packer and a device entry point:
+ *
+ *   2-bit integer MLP   Z80-uLM digest ("a 40KB tiny conversational AI model"), the feature
+ *                       list (2-bit weights in {-2,-1,0,+1}, four per byte; 16-bit integer
+ *                       arithmetic), the architecture list (256 inputs, hidden layers, one output
+ *                       per character, ReLU between hidden layers) and the unpack / MULADD /
+ *                       shift listings of its inner loop.
+ *   Q1_0_g128           Bonsai-27B-gguf whitepaper digest, section "technical architecture
+ *                       highlights": one sign bit per weight, one FP16 scale shared by every
+ *                       128 weights, 1.125 bits per weight.
+ *   INT4, group 128     Acorn framework page (acorn-llm 0.11.4), section "int4 quantization
+ *                       quality: group quantization (g=128)": one scale per 128 values along
+ *                       the input dimension.
+ *
+ * Conventions (all entry points):
+ *   - Every d_* pointer is DEVICE memory owned by the caller; every other pointer is HOST
+ *     memory owned by the caller. The library never frees or retains caller memory.
+ *   - bf16 and fp16 values cross the ABI as uint16_t bit patterns.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream). Device entry points are
+ *     asynchronous on `stream`; argument validation is synchronous and a failed validation
+ *     launches nothing. A kernel launch failure is reported as LBQ_E_DEVICE; faults inside a
+ *     kernel surface at the caller's next synchronisation, as usual for HIP.
+ *   - Errors are returned as negative lbq_status codes, never as exceptions.
+ *   - Matrices are [n][k]: n output rows, k inputs (the reduction dimension).
+ *   - Every device entry point may be called concurrently from several host threads on
+ *     different streams, except where noted (split-K workspace, see lbq_gemv_q1g128).
+ */
+#ifndef LBQ_H
+#define LBQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LBQ_ABI_VERSION 1
+#define LBQ_MAX_BATCH 16
+#define LBQ_MLP_MAX_LAYERS 8
+#define LBQ_MLP_MAX_DIM 1024
+
+typedef int32_t lbq_status;
+enum {
+  LBQ_OK = 0,
+  LBQ_E_NULL = -1,        /* a required pointer is NULL                                  */
+  LBQ_E_SHAPE = -2,       /* a size is out of range or not a multiple the format needs  */
+  LBQ_E_ALIGN = -3,       /* a pointer is not aligned as documented                      */
+  LBQ_E_UNSUPPORTED = -4, /* valid request the library does not implement (e.g. batch)   */
+  LBQ_E_ALIAS = -5,       /* an output overlaps an input                                 */
+  LBQ_E_DEVICE = -6,      /* a HIP runtime call or kernel launch failed                  */
+  LBQ_E_NOMEM = -7        /* the library could not obtain its device workspace           */
+};
+
+/* Returns LBQ_ABI_VERSION of the built library. */
+int32_t lbq_abi_version(void);
+
+/* Static, never-NULL description of a status code. */
+const char* lbq_status_string(lbq_status s);
+
+/* ------------------------------------------------------------------------------------------
+ * 2-bit integer MLP (Z80-uLM semantics).
+ *
+ * Canonical layout (input of the packer): codes[n][k/4] uint8, code c in 0..3 of weight
+ * (row, j) stored in bits [2*(j%4)+1 : 2*(j%4)] of byte codes[row][j/4] (least significant pair
+ * first, as the unpack listing rotates the byte right by two after taking its low two bits).
+ * Weight value = c - 2, i.e. 0,1,2,3 -> -2,-1,0,+1 (the unpack listing subtracts 2).
+ * ------------------------------------------------------------------------------------------ */
+
+/* Device-layout bytes for one n x k layer: n*k/4. Returns 0 for invalid shapes. */
+size_t lbq_2bit_bytes(int32_t n, int32_t k);
+
+/* Canonical codes (host) -> device layout (host buffer of lbq_2bit_bytes(n,k) bytes).
+ * Requires n >= 1, k >= 4, k % 4 == 0. */
+lbq_status lbq_pack_2bit(const uint8_t* codes, int32_t n, int32_t k, void* dst);
+
+/* Inverse of lbq_pack_2bit (host -> host). */
+lbq_status lbq_unpack_2bit(const void* src, int32_t n, int32_t k, uint8_t* codes);
+
+/* Evaluates an n_layers-deep MLP on `batch` int16 input vectors, entirely on the device.
+ *   d_layer_w : host array of n_layers device pointers; layer l holds the device layout of a
+ *               dims[l+1] x dims[l] matrix (lbq_pack_2bit output copied to the device).
+ *   dims      : host array of n_layers+1 sizes; dims[0] = input width.
+ *   d_x       : int16 [batch][dims[0]]          (device)
+ *   d_logits  : int16 [batch][dims[n_layers]]   (device, output)
+ *   d_argmax  : int32 [batch] or NULL           (device, output)
+ * Per layer and output neuron: acc = sum_k (c-2)*a[k] taken modulo 2^16 (16-bit register pair
+ * arithmetic of the MULADD listing), read as two's-complement int16, then an arithmetic
+ * shift right by 2 (the shift listing: floor division by 4), then ReLU on every layer but the
+ * last (ReLU between hidden layers). argmax = lowest index among equal maxima.
+ * Requires 1 <= n_layers <= LBQ_MLP_MAX_LAYERS, dims[l] % 4 == 0 and 4 <= dims[l] <=
+ * LBQ_MLP_MAX_DIM for l < n_layers, 1 <= dims[n_layers] <= LBQ_MLP_MAX_DIM, batch >= 0
+ * (batch == 0 is a no-op). Inputs and outputs must not overlap (LBQ_E_ALIAS). */
+lbq_status lbq_mlp_2bit_i16(const void* const* d_layer_w, const int32_t* dims, int32_t n_layers,
+                            const int16_t* d_x, int16_t* d_logits, int32_t* d_argmax,
+                            int32_t batch, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Q1_0_g128 (Bonsai digest, "technical architecture highlights").
+ *
+ * Canonical layout: signs[n][k/8] uint8, bit (j%8) of signs[row][j/8] is the sign of weight
+ * (row, j): 1 -> +1, 0 -> -1. scales[n][k/128] fp16: scale of the 128 weights j in
+ * [128g, 128g+128) of the row.
+ * Device layout (owned by the packer, consumed only by this library): rows in tiles of 64
+ * (the row count is padded up to a multiple of 64 with zero bytes); per tile and per block of
+ * eight groups, 1 KiB of scales (16 bytes = eight fp16 per row) followed by 1 KiB of sign bits
+ * per group (16 bytes per row), so every scale sits next to the groups it weights. Bytes =
+ * n*k*9/64 exactly when n % 64 == 0 and k % 1024 == 0 (1.125 bits per weight).
+ * ------------------------------------------------------------------------------------------ */
+
+/* Device-layout bytes (see above). Returns 0 for invalid shapes. */
+size_t lbq_q1g128_bytes(int32_t n, int32_t k);
+
+/* Canonical (host) -> device layout (host buffer of lbq_q1g128_bytes(n,k) bytes).
+ * Requires n >= 1, k >= 128, k % 128 == 0. */
+lbq_status lbq_pack_q1g128(const uint8_t* signs, const uint16_t* scales, int32_t n, int32_t k,
+                           void* dst);
+
+/* Inverse of lbq_pack_q1g128 (host -> host). */
+lbq_status lbq_unpack_q1g128(const void* src, int32_t n, int32_t k, uint8_t* signs,
+                             uint16_t* scales);
+
+/* y[b][row] = bf16_rne( sum_g f32(scale[row][g]) * sum_{j in g} sign[row][j] * x[b][j] )
+ * with fp32 accumulation and the bf16 result rounded to nearest even.
+ *   d_w : device layout (lbq_pack_q1g128), 16-byte aligned
+ *   d_x : bf16 [batch][k], 4-byte aligned     d_y : bf16 [batch][n], 4-byte aligned
+ * Requires k % 128 == 0, 1 <= n, 0 <= batch <= LBQ_MAX_BATCH (0 = no-op). d_y must not
+ * overlap d_x or the weights. Large-k calls may split the reduction over workgroups through a
+ * library-owned device workspace (allocated once per device on first need, kept until the
+ * process exits); calls that split share it, so concurrent split calls on one device must be
+ * ordered on one stream. LBQ_E_NOMEM if it cannot be allocated (e.g. inside graph capture). */
+lbq_status lbq_gemv_q1g128(const void* d_w, int32_t n, int32_t k, const uint16_t* d_x,
+                           uint16_t* d_y, int32_t batch, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * INT4, group 128 along k (Acorn, "int4 quantization quality: group quantization (g=128)").
+ *
+ * Canonical layout: nib[n][k/2] uint8, weight (row, j) is the low nibble of nib[row][j/2] for
+ * even j and the high nibble for odd j, read as a two's-complement value q in -8..7.
+ * scales[n][k/128] fp16, one per 128 consecutive weights of a row. Symmetric: no zero point.
+ * Device layout: rows in tiles of 64; per tile and per block of eight groups, 1 KiB of scales
+ * followed by 4 KiB of codes per group (stored offset-binary, q+8). Bytes = n*k*33/64 exactly
+ * when n % 64 == 0 and k % 1024 == 0 (4.125 bits per weight).
+ * ------------------------------------------------------------------------------------------ */
+
+size_t lbq_i4g128_bytes(int32_t n, int32_t k);
+lbq_status lbq_pack_i4g128(const uint8_t* nib, const uint16_t* scales, int32_t n, int32_t k,
+                           void* dst);
+lbq_status lbq_unpack_i4g128(const void* src, int32_t n, int32_t k, uint8_t* nib,
+                             uint16_t* scales);
+
+/* y[b][row] = bf16_rne( sum_g f32(scale[row][g]) * sum_{j in g} q[row][j] * x[b][j] ), fp32
+ * accumulation. Same pointer, alignment, batch and workspace rules as lbq_gemv_q1g128. */
+lbq_status lbq_gemv_i4g128(const void* d_w, int32_t n, int32_t k, const uint16_t* d_x,
+                           uint16_t* d_y, int32_t batch, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * RMS rescale: the glue that carries bf16 activations from one GEMV to the next in a decode
+ * step of the 27B-shaped 1-bit stream (64 layers, Bonsai digest, "262K context window").
+ * The pages name no normalisation formula; the library's reading is
+ *   h[b][j] = y[b][j] * (d_y2 ? y2[b][j] : 1)          (exact: a product of two bf16 fits fp32)
+ *   x[b][j] = bf16_rne( h[b][j] / sqrt(mean_j h[b][j]^2 + eps) )      (gain 1, fp32 compute)
+ *   d_y, d_y2 : bf16 [batch][n] (d_y2 may be NULL)    d_x : bf16 [batch][n] (output)
+ * Requires n >= 1, 0 <= batch <= LBQ_MAX_BATCH, eps >= 0; d_x must not overlap the inputs.
+ * ------------------------------------------------------------------------------------------ */
+lbq_status lbq_rms_rescale_bf16(const uint16_t* d_y, const uint16_t* d_y2, uint16_t* d_x,
+                                int32_t n, int32_t batch, float eps, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * One decode step over a stack of Q1_0_g128 layers (q, k, v, o, gate, up, down projections
+ * of a hybrid-attention 27B model; the digest says the model has 64 layers and that the
+ * attention and MLP projections are all 1-bit). Attention itself is outside this library;
+ * the data flow between projections is the library's reading:
+ *   q,k,v,gate,up = W(x_l)                       (k, v are computed and kept, not consumed)
+ *   xo = rms(q);  o = W_o(xo)                    (o is computed and kept, not consumed)
+ *   xd = rms(gate * up);  down = W_down(xd)
+ *   x_{l+1} = rms(down)
+ * where rms is lbq_rms_rescale_bf16 with the given eps. Every GEMV has the semantics of
+ * lbq_gemv_q1g128 (bf16 outputs).
+ *   layers : host array of n_layers lbq_q1_layer records of device pointers (device layouts
+ *            of hidden x hidden (q, o), kv x hidden (k, v), ffn x hidden (gate, up) and
+ *            hidden x ffn (down) matrices)
+ *   d_x0   : bf16 [batch][hidden] input of layer 0
+ *   d_act  : bf16 activation record, lbq_decode_act_elems(...) elements, laid out as
+ *            [layer][slot][batch][dim] with the slots, in order:
+ *            x(hidden) q(hidden) k(kv) v(kv) gate(ffn) up(ffn) xo(hidden) o(hidden) xd(ffn)
+ *            down(hidden), followed by the final x_{n_layers} [batch][hidden].
+ *            Slot x of layer 0 receives a copy of d_x0.
+ * Requires hidden, kv, ffn multiples of 128, 1 <= batch <= LBQ_MAX_BATCH, n_layers >= 1.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct lbq_q1_layer {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* gate;
+  const void* up;
+  const void* down;
+} lbq_q1_layer;
+
+enum {
+  LBQ_ACT_X = 0, LBQ_ACT_Q, LBQ_ACT_K, LBQ_ACT_V, LBQ_ACT_GATE, LBQ_ACT_UP,
+  LBQ_ACT_XO, LBQ_ACT_O, LBQ_ACT_XD, LBQ_ACT_DOWN, LBQ_ACT_NSLOTS
+};
+
+/* Number of bf16 elements of the activation record. 0 for invalid shapes. */
+size_t lbq_decode_act_elems(int32_t n_layers, int32_t hidden, int32_t kv, int32_t ffn,
+                            int32_t batch);
+
+/* Element offset of slot `slot` of layer `layer` inside the activation record (slot ==
+ * LBQ_ACT_NSLOTS with layer == n_layers addresses the final x). -1 for invalid arguments. */
+int64_t lbq_decode_act_offset(int32_t layer, int32_t slot, int32_t n_layers, int32_t hidden,
+                              int32_t kv, int32_t ffn, int32_t batch);
+
+lbq_status lbq_decode_step_q1g128(const lbq_q1_layer* layers, int32_t n_layers, int32_t hidden,
+                                  int32_t kv, int32_t ffn, const uint16_t* d_x0,
+                                  uint16_t* d_act, int32_t batch, float eps, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LBQ_H */

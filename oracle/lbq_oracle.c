@@ -1,0 +1,244 @@
+/*
+ * lbq_oracle.c - TEST INFRASTRUCTURE ONLY. A plain, slow CPU oracle of what the packed
+ * low-bit GEMV library computes, written straight from the definitions on the pages, in
+ * exact integer arithmetic (2-bit path) and IEEE double precision (float paths). It reads the
+ * canonical layouts only and shares no code, header, table or helper with the library under
+ * test; only tests, the smoke check and the bench's CPU-baseline leg may load it.
+ *
+ * Every loop runs in the plain order of the definition: no blocking, no fusion, no reordering.
+ *
+ * Pins (tests/test_oracle_*.py) hold each function to facts the pages and mathematics fix.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+/* ---------------------------------------------------------------------------------------
+ * Number formats, decoded from their IEEE / bfloat16 bit-level definitions.
+ * ------------------------------------------------------------------------------------- */
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. Subnormals are
+ * kept (a scale drawn from |N(0, 0.02)| is subnormal now and then and must not be flushed). */
+double oracle_f16_to_f64(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 0x1F;
+  int f = h & 0x3FF;
+  double v;
+  if (e == 0) {
+    v = ldexp((double)f, -24);                 /* 0.f x 2^-14 = f x 2^-24 */
+  } else if (e == 31) {
+    v = f ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(1024 + f), e - 25);     /* 1.f x 2^(e-15) = (1024+f) x 2^(e-25) */
+  }
+  return sign ? -v : v;
+}
+
+/* bfloat16: 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits. */
+double oracle_bf16_to_f64(uint16_t b) {
+  int sign = (b >> 15) & 1;
+  int e = (b >> 7) & 0xFF;
+  int f = b & 0x7F;
+  double v;
+  if (e == 0) {
+    v = ldexp((double)f, -133);                /* 0.f x 2^-126 = f x 2^-133 */
+  } else if (e == 255) {
+    v = f ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(128 + f), e - 134);     /* 1.f x 2^(e-127) = (128+f) x 2^(e-134) */
+  }
+  return sign ? -v : v;
+}
+
+/* Round a double to the nearest bfloat16, ties to even (the rounding every bf16 output of the
+ * library is defined with). Overflow goes to infinity, NaN to the canonical quiet NaN. */
+uint16_t oracle_f64_to_bf16_rne(double v) {
+  if (isnan(v)) return 0x7FC0;
+  uint16_t sign = signbit(v) ? 0x8000 : 0;
+  double a = fabs(v);
+  if (a == 0.0) return sign;
+  if (isinf(a)) return sign | 0x7F80;
+  int E;
+  frexp(a, &E);                 /* a = m x 2^E, m in [0.5, 1): unbiased exponent is E-1 */
+  int e = (E - 1) + 127;        /* biased bf16 exponent if a were normal */
+  if (e >= 1) {
+    double q = ldexp(a, 8 - E); /* significand scaled to [128, 256): exact */
+    double qi = nearbyint(q);   /* default rounding mode: to nearest, ties to even */
+    if (qi >= 256.0) {          /* rounded up into the next binade */
+      qi = 128.0;
+      e += 1;
+    }
+    if (e >= 255) return sign | 0x7F80;
+    return sign | (uint16_t)(e << 7) | (uint16_t)((int)qi - 128);
+  }
+  /* subnormal range: value = f x 2^-133 with f in 0..127 (f == 128 is the least normal) */
+  double q = ldexp(a, 133);
+  double qi = nearbyint(q);
+  return sign | (uint16_t)(int)qi;
+}
+
+/* ---------------------------------------------------------------------------------------
+ * 2-bit integer MLP (Z80-uLM digest: feature list, architecture list, and the unpack,
+ * MULADD and shift listings of the inner loop).
+ * ------------------------------------------------------------------------------------- */
+
+/* Floor division by 4 of a signed 16-bit value: what two rounds of an arithmetic shift right
+ * of the 16-bit accumulator (sra on the high byte, rotate-through-carry on the low byte) do. */
+static int16_t floor_div4(int16_t s) {
+  int v = s;
+  int q = v / 4;                   /* C truncates toward zero ... */
+  if (v < 0 && q * 4 != v) q -= 1; /* ... floor rounds toward minus infinity */
+  return (int16_t)q;
+}
+
+/* One layer for one input vector. codes: canonical [n][k/4], the code of input j of row r in
+ * bits [2*(j%4)+1 : 2*(j%4)] of codes[r*(k/4) + j/4]. The accumulator is a 16-bit register
+ * pair: every multiply-accumulate wraps modulo 2^16. relu != 0 on hidden layers only. */
+static void mlp_layer(const uint8_t* codes, int n, int k, const int16_t* a, int16_t* out,
+                      int relu) {
+  for (int r = 0; r < n; ++r) {
+    uint16_t acc = 0;
+    for (int j = 0; j < k; ++j) {
+      int c = (codes[(size_t)r * (k / 4) + j / 4] >> (2 * (j % 4))) & 3; /* mask low 2 bits */
+      int w = c - 2;                                                     /* 0..3 -> -2..+1 */
+      uint16_t prod = (uint16_t)(uint32_t)(int32_t)(w * (int32_t)a[j]);
+      acc = (uint16_t)(acc + prod);                                     /* mod 2^16 */
+    }
+    int16_t s = (int16_t)acc;      /* two's-complement reading of the register pair */
+    int16_t h = floor_div4(s);     /* arithmetic shift right by 2 after each layer */
+    if (relu && h < 0) h = 0;      /* ReLU between hidden layers */
+    out[r] = h;
+  }
+}
+
+/* Full chain for `batch` vectors. layer_codes[l] points to the canonical codes of a
+ * dims[l+1] x dims[l] matrix. logits: int16 [batch][dims[L]], argmax: int32 [batch] (lowest
+ * index among equal maxima). Returns 0, or -1 if a dimension exceeds the scratch size. */
+int oracle_mlp_2bit(const uint8_t* const* layer_codes, const int32_t* dims, int n_layers,
+                    const int16_t* x, int batch, int16_t* logits, int32_t* argmax) {
+  enum { MAXD = 4096 };
+  static int16_t buf_a[MAXD], buf_b[MAXD];
+  for (int l = 0; l <= n_layers; ++l)
+    if (dims[l] < 1 || dims[l] > MAXD) return -1;
+  for (int b = 0; b < batch; ++b) {
+    int16_t* cur = buf_a;
+    int16_t* nxt = buf_b;
+    for (int j = 0; j < dims[0]; ++j) cur[j] = x[(size_t)b * dims[0] + j];
+    for (int l = 0; l < n_layers; ++l) {
+      mlp_layer(layer_codes[l], dims[l + 1], dims[l], cur, nxt, l < n_layers - 1);
+      int16_t* t = cur;
+      cur = nxt;
+      nxt = t;
+    }
+    int nout = dims[n_layers];
+    int best = 0;
+    for (int j = 0; j < nout; ++j) {
+      logits[(size_t)b * nout + j] = cur[j];
+      if (cur[j] > cur[best]) best = j;
+    }
+    if (argmax) argmax[b] = best;
+  }
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------------------
+ * Q1_0_g128 GEMV (Bonsai digest, "technical architecture highlights": one sign bit per
+ * weight, -1 or +1; one FP16 scale per 128 weights). Sign map bit 1 -> +1, bit 0 -> -1; the
+ * 128-weight groups run along k inside a row.
+ *
+ * For each of the `n_rows` rows listed in `rows` (all rows if rows == NULL) and each batch
+ * vector b: y = sum_g s_g * sum_{j in g} w_j x_j, and l1 = sum_g |s_g| * sum_{j in g} |x_j|,
+ * the bound the tolerance is measured against. Outputs are [batch][n_rows].
+ * ------------------------------------------------------------------------------------- */
+void oracle_gemv_q1g128(const uint8_t* signs, const uint16_t* scales, int n, int k,
+                        const uint16_t* x, int batch, const int32_t* rows, int n_rows,
+                        double* y, double* l1) {
+  int ng = k / 128;
+  int nr = rows ? n_rows : n;
+  for (int b = 0; b < batch; ++b) {
+    for (int i = 0; i < nr; ++i) {
+      int r = rows ? rows[i] : i;
+      double acc = 0.0, mag = 0.0;
+      for (int g = 0; g < ng; ++g) {
+        double s = oracle_f16_to_f64(scales[(size_t)r * ng + g]);
+        double part = 0.0, xsum = 0.0;
+        for (int j = 128 * g; j < 128 * g + 128; ++j) {
+          int bit = (signs[(size_t)r * (k / 8) + j / 8] >> (j % 8)) & 1;
+          double w = bit ? 1.0 : -1.0;
+          double xv = oracle_bf16_to_f64(x[(size_t)b * k + j]);
+          part += w * xv;
+          xsum += fabs(xv);
+        }
+        acc += s * part;
+        mag += fabs(s) * xsum;
+      }
+      y[(size_t)b * nr + i] = acc;
+      l1[(size_t)b * nr + i] = mag;
+    }
+  }
+}
+
+/* ---------------------------------------------------------------------------------------
+ * INT4 group-128 GEMV (Acorn page, "int4 quantization quality: group quantization (g=128)":
+ * one scale per 128 values along the input dimension). Codes are two's-complement nibbles,
+ * low nibble = even j; symmetric, no zero point.
+ * l1 = sum_g |s_g| * sum_{j in g} |q_j x_j|.
+ * ------------------------------------------------------------------------------------- */
+void oracle_gemv_i4g128(const uint8_t* nib, const uint16_t* scales, int n, int k,
+                        const uint16_t* x, int batch, const int32_t* rows, int n_rows,
+                        double* y, double* l1) {
+  int ng = k / 128;
+  int nr = rows ? n_rows : n;
+  for (int b = 0; b < batch; ++b) {
+    for (int i = 0; i < nr; ++i) {
+      int r = rows ? rows[i] : i;
+      double acc = 0.0, mag = 0.0;
+      for (int g = 0; g < ng; ++g) {
+        double s = oracle_f16_to_f64(scales[(size_t)r * ng + g]);
+        double part = 0.0, amag = 0.0;
+        for (int j = 128 * g; j < 128 * g + 128; ++j) {
+          uint8_t byte = nib[(size_t)r * (k / 2) + j / 2];
+          int u = (j % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+          int q = u >= 8 ? u - 16 : u;
+          double xv = oracle_bf16_to_f64(x[(size_t)b * k + j]);
+          part += q * xv;
+          amag += fabs(q * xv);
+        }
+        acc += s * part;
+        mag += fabs(s) * amag;
+      }
+      y[(size_t)b * nr + i] = acc;
+      l1[(size_t)b * nr + i] = mag;
+    }
+  }
+}
+
+/* ---------------------------------------------------------------------------------------
+ * RMS rescale between GEMVs of the decode-step stream (a reading: the pages name no
+ * formula). h = y * y2 (or y), x = bf16_rne(h / sqrt(mean(h^2) + eps)). `exact` receives the
+ * unrounded quotient so tests can tell rounding-boundary cases apart. Arrays are [batch][n].
+ * ------------------------------------------------------------------------------------- */
+void oracle_rms_rescale(const uint16_t* yv, const uint16_t* y2, int n, int batch, double eps,
+                        uint16_t* out, double* exact) {
+  for (int b = 0; b < batch; ++b) {
+    double ss = 0.0;
+    for (int j = 0; j < n; ++j) {
+      double h = oracle_bf16_to_f64(yv[(size_t)b * n + j]);
+      if (y2) h *= oracle_bf16_to_f64(y2[(size_t)b * n + j]);
+      ss += h * h;
+    }
+    double denom = sqrt(ss / n + eps);
+    for (int j = 0; j < n; ++j) {
+      double h = oracle_bf16_to_f64(yv[(size_t)b * n + j]);
+      if (y2) h *= oracle_bf16_to_f64(y2[(size_t)b * n + j]);
+      double q = h / denom;
+      if (exact) exact[(size_t)b * n + j] = q;
+      out[(size_t)b * n + j] = oracle_f64_to_bf16_rne(q);
+    }
+  }
+}
+
+/* Rounds an array of doubles to bf16 (ties to even), as every library output is rounded. */
+void oracle_round_bf16(const double* v, size_t count, uint16_t* out) {
+  for (size_t i = 0; i < count; ++i) out[i] = oracle_f64_to_bf16_rne(v[i]);
+}
