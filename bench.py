@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Bench: packed-weight HBM GB/s (and % of the 8 TB/s peak) plus decode tok/s-equivalent of the
+27B-shaped Q1_0_g128 decode-step weight stream at batch 1 on one MI355X.
+
+A step is one decode step of the whole stream: 64 layers x (q, o 5120x5120; k, v 1024x5120;
+gate, up 17408x5120; down 5120x17408) Q1_0_g128 GEMVs with the RMS rescales between them
+(lbq_decode_step_q1g128), over seeded synthetic weights (sign bits Bernoulli(0.5), fp16 scales
+|N(0, 0.02)|) and a bf16 N(0, 1) input, all resident in HBM before timing starts. The step is
+replayed from a HIP graph; W untimed warm-up steps precede exactly K timed steps bracketed by
+device synchronisation.
+
+Printed: one JSON line on stdout (progress goes to stderr).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--layers", type=int, default=64)
+    ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly")
+    ap.add_argument("--cpu-layers", type=int, default=2,
+                    help="layers of the stream the CPU oracle baseline runs (0 = skip)")
+    ap.add_argument("--kernel-steps", type=int, default=3,
+                    help="instrumented steps timing each GEMV launch with HIP events")
+    return ap.parse_args()
+
+
+def main() -> int:
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from packed_weight_gemv_amd import build as lbq_build
+    if not os.path.exists(lbq_build.LIB):
+        import __graft_entry__
+        __graft_entry__.build()
+    import packed_weight_gemv_amd as lbq
+    from packed_weight_gemv_amd import synth
+
+    lbq.load()
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), CUs {props.multi_processor_count}")
+
+    L, B = args.layers, args.batch
+    hid, kv, ffn = synth.STREAM_HIDDEN, synth.STREAM_KV, synth.STREAM_FFN
+    shapes = {nm: synth.stream_shape(nm) for nm in synth.STREAM_MATRICES}
+    bytes_per_layer = synth.stream_bytes_per_layer()
+    bytes_per_step = bytes_per_layer * L
+
+    # ---- weights resident in HBM -------------------------------------------------------------
+    t0 = time.time()
+    layers = []
+    for l in range(L):
+        d = {}
+        for nm in synth.STREAM_MATRICES:
+            m = synth.stream_matrix(l, nm)
+            d[nm] = torch.from_numpy(lbq.lbq_pack_q1g128(m.signs, m.scales)).to(dev)
+        layers.append(d)
+        if l % 8 == 7 or l == L - 1:
+            log(f"packed and uploaded {l + 1}/{L} layers ({time.time() - t0:.1f} s)")
+    arr = lbq.make_layers(layers)
+    x0_np = synth.activations(B, hid, workload=synth.W_Q1_STREAM)
+    x0 = torch.from_numpy(x0_np.view(np.int16)).to(dev)
+    act = torch.zeros(lbq.lbq_decode_act_elems(L, hid, kv, ffn, B), dtype=torch.int16, device=dev)
+
+    def step():
+        lbq.lbq_decode_step_q1g128(arr, L, hid, kv, ffn, x0, act)
+
+    # ---- warm-up, graph capture, timed steps -------------------------------------------------
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+    run = graph.replay if graph is not None else step
+    log(f"timing {args.steps} steps ({'graph' if graph is not None else 'eager'})")
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        run()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    gbs = bytes_per_step / (ms * 1e-3) / 1e9
+
+    # ---- dominant kernel: every Q1 GEMV launch of a step bracketed by events -------------------
+    stream = torch.cuda.current_stream()
+    gemv_ms, gemv_bytes, launches = 0.0, 0, 0
+    for _ in range(args.kernel_steps):
+        evs = []
+        for l in range(L):
+            src = {"q": "x", "k": "x", "v": "x", "gate": "x", "up": "x", "o": "xo", "down": "xd"}
+            for nm in ("q", "k", "v", "gate", "up", "o", "down"):
+                n, k = shapes[nm]
+                xin = lbq.act_view(act, src[nm], l, L, hid, kv, ffn, B)
+                yout = lbq.act_view(act, nm, l, L, hid, kv, ffn, B)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                lbq.lbq_gemv_q1g128(layers[l][nm], n, k, xin, yout)
+                e1.record(stream)
+                evs.append((e0, e1, n * k * 9 // 64))
+        torch.cuda.synchronize()
+        for e0, e1, nb in evs:
+            gemv_ms += e0.elapsed_time(e1)
+            gemv_bytes += nb
+            launches += 1
+    kern_avg_ms = gemv_ms / max(launches, 1)
+    kern_bytes = gemv_bytes / max(launches, 1)
+    kern_gbs = kern_bytes / (kern_avg_ms * 1e-3) / 1e9
+    # restore the activation record of a full step for the parity check below
+    run()
+    torch.cuda.synchronize()
+
+    # ---- CPU oracle baseline (bounded sample) + teacher-forced parity of that sample ----------
+    cpu = None
+    if args.cpu_layers > 0:
+        import oracle
+        from tests._gpu import check_within  # the tolerance rule shared with the tests
+        cpu_s, cpu_bytes, worst = 0.0, 0, 0.0
+        src = {"q": "x", "k": "x", "v": "x", "gate": "x", "up": "x", "o": "xo", "down": "xd"}
+        sample_layers = list(range(min(args.cpu_layers, L)))
+        for l in sample_layers:
+            for nm in synth.STREAM_MATRICES:
+                m = synth.stream_matrix(l, nm)
+                xin = lbq.act_view(act, src[nm], l, L, hid, kv, ffn, B).cpu().view(torch.int16)
+                xin = xin.numpy().view(np.uint16)
+                t = time.perf_counter()
+                ref, l1 = oracle.gemv_q1g128(m.signs, m.scales, xin)
+                cpu_s += time.perf_counter() - t
+                cpu_bytes += m.shape[0] * m.shape[1] * 9 // 64 * B
+                y = lbq.act_view(act, nm, l, L, hid, kv, ffn, B).cpu().view(torch.int16)
+                worst = max(worst, check_within(y.numpy().view(np.uint16), ref, l1,
+                                                f"bench layer {l} {nm}"))
+        log(f"parity: layers {sample_layers} all 7 GEMVs within 2e-3*L1 "
+            f"(worst |err|/L1 = {worst:.2e}); oracle {cpu_s:.1f} s")
+        cpu = {"value": round(cpu_bytes / cpu_s / 1e9, 6), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"{len(sample_layers)} of {L} layers (all 7 GEMVs of each, every row, "
+                         f"batch {B}), plain scalar C oracle in float64, one thread; "
+                         f"{cpu_bytes / 1e6:.1f} MB of packed weights in {cpu_s:.1f} s",
+               "tok_s_equiv": round(B * cpu_bytes / bytes_per_step / cpu_s, 6)}
+
+    out = {
+        "metric": "packed-weight HBM GB/s (% of peak) + decode tok/s-equiv, batch 1, 27B-shape",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "tok_s_equiv": round(B / (ms * 1e-3), 2),
+        "config": {
+            "workload": (f"27B-shaped Q1_0_g128 decode-step weight stream: {L} layers x "
+                         f"(q,o {hid}x{hid}; k,v {kv}x{hid}; gate,up {ffn}x{hid}; down {hid}x{ffn}) "
+                         f"+ RMS rescales, batch {B}"),
+            "layers": L, "batch": B, "packed_bytes_per_step": bytes_per_step,
+            "launch": "HIP graph" if graph is not None else "eager",
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(kern_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "q1_gemv_kernel<1>",
+            "avg_launch_us": round(kern_avg_ms * 1e3, 3),
+            "bytes_per_launch": round(kern_bytes),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -24,6 +24,8 @@
  *     launches nothing. A kernel launch failure is reported as LBQ_E_DEVICE; faults inside a
  *     kernel surface at the caller's next synchronisation, as usual for HIP.
  *   - Errors are returned as negative lbq_status codes, never as exceptions.
+ *   - batch == 0 is a valid no-op: once the shape arguments pass validation the call returns
+ *     LBQ_OK without looking at the data pointers (an empty tensor may have a NULL pointer).
  *   - Matrices are [n][k]: n output rows, k inputs (the reduction dimension).
  *   - Every device entry point may be called concurrently from several host threads on
  *     different streams, except where noted (split-K workspace, see lbq_gemv_q1g128).

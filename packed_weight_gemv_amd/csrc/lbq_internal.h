@@ -1,0 +1,59 @@
+// lbq_internal.h - device-layout geometry shared by the host packers and the kernel launchers
+// of liblbq.so. Not part of the public ABI (include/lbq.h is).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/lbq.h"
+
+namespace lbq {
+
+constexpr int kTileRows = 64;        // rows per tile: one row per lane of a wave64
+constexpr int kGroup = 128;          // weights per fp16 scale (both float formats)
+constexpr int kSuper = 8;            // groups per scale block (8 fp16 = 16 bytes per row)
+constexpr int kBlock = 1024;         // one 16-byte record per row of a tile
+
+// Q1: per tile, per super-group j: [scales 1 KiB][signs 1 KiB per group]
+// I4: per tile, per super-group j: [scales 1 KiB][codes 4 KiB per group]
+constexpr int kQ1GroupBlocks = 1;
+constexpr int kI4GroupBlocks = 4;
+
+struct Geometry {
+  int64_t n, k;       // logical shape
+  int64_t np;         // rows padded to a multiple of kTileRows
+  int64_t tiles;      // np / kTileRows
+  int64_t groups;     // k / kGroup
+  int64_t supers;     // ceil(groups / kSuper)
+  int64_t tile_bytes; // bytes of one tile
+  int64_t super_bytes;// stride between full super-groups inside a tile
+  int64_t group_bytes;// bytes of one group's codes inside a super-group
+};
+
+inline bool make_geometry(int64_t n, int64_t k, int group_blocks, Geometry* g) {
+  if (n < 1 || k < kGroup || k % kGroup != 0) return false;
+  if (n > (int64_t)1 << 24 || k > (int64_t)1 << 24) return false;
+  g->n = n;
+  g->k = k;
+  g->np = (n + kTileRows - 1) / kTileRows * kTileRows;
+  g->tiles = g->np / kTileRows;
+  g->groups = k / kGroup;
+  g->supers = (g->groups + kSuper - 1) / kSuper;
+  g->group_bytes = (int64_t)group_blocks * kBlock;
+  g->super_bytes = kBlock + kSuper * g->group_bytes;
+  g->tile_bytes = g->supers * kBlock + g->groups * g->group_bytes;
+  return true;
+}
+
+inline size_t layout_bytes(const Geometry& g) { return (size_t)(g.tiles * g.tile_bytes); }
+
+// Byte offset of the scale record of (tile t, super-group j) and of the code block of group gi.
+inline int64_t scale_offset(const Geometry& g, int64_t t, int64_t j) {
+  return t * g.tile_bytes + j * g.super_bytes;
+}
+inline int64_t group_offset(const Geometry& g, int64_t t, int64_t gi) {
+  int64_t j = gi / kSuper, i = gi % kSuper;
+  return t * g.tile_bytes + j * g.super_bytes + kBlock + i * g.group_bytes;
+}
+
+}  // namespace lbq

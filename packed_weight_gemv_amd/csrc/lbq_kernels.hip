@@ -1,0 +1,601 @@
+// lbq_kernels.hip - gfx950 (MI355X) kernels of liblbq.so and the device entry points of
+// include/lbq.h. Everything here is written for CDNA4 wave64: one row of a 64-row weight tile
+// per lane, 16-byte coalesced loads of packed rows, unpacking in registers, fp32 accumulation.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "lbq_internal.h"
+
+using namespace lbq;
+
+// ---------------------------------------------------------------------------------------------
+// small device helpers
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// fp32 -> bf16, round to nearest, ties to even (NaN -> quiet NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// (s >> 8) & m with the byte-1 source select of SDWA: one VALU op (the compiler emits a shift
+// and a mask for this pattern, while it already uses one op for bytes 0, 2 and 3).
+__device__ __forceinline__ uint32_t and_byte1(uint32_t s, uint32_t m) {
+  uint32_t r;
+  asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 "
+      "src1_sel:DWORD"
+      : "=v"(r)
+      : "v"(s), "v"(m));
+  return r;
+}
+
+// Byte offset (4-bit field x 4) of the table entry for field q (0..3) of a 32-bit word whose
+// fields sit at bits [8q+2, 8q+5].
+__device__ __forceinline__ uint32_t field4(uint32_t s, int q) {
+  if (q == 1) return and_byte1(s, 0x3Cu);
+  return (s >> (8 * q)) & 0x3Cu;
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// 16-byte streaming load of packed weights (read once: non-temporal hint)
+__device__ __forceinline__ u32x4 ld_stream16(const void* p) {
+  return __builtin_nontemporal_load((const u32x4*)p);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// ---------------------------------------------------------------------------------------------
+// library-owned split-K workspace (one per device, grown on demand, never freed)
+// ---------------------------------------------------------------------------------------------
+namespace {
+constexpr int kMaxDevices = 64;
+constexpr size_t kCounterBytes = 1 << 20;   // 256 Ki tile counters, self-resetting
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+Workspace g_ws[kMaxDevices];
+std::mutex g_ws_mutex;
+
+// Returns device memory of at least kCounterBytes + partial_bytes; the first kCounterBytes are
+// zero-initialised tile counters that every kernel leaves at zero.
+lbq_status get_workspace(size_t partial_bytes, hipStream_t stream, unsigned** counters,
+                         float** partials) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LBQ_E_DEVICE;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  Workspace& w = g_ws[dev];
+  size_t need = kCounterBytes + partial_bytes;
+  if (w.bytes < need) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+      return LBQ_E_NOMEM;
+    size_t grow = need < ((size_t)64 << 20) ? ((size_t)64 << 20) : need;
+    void* p = nullptr;
+    if (hipMalloc(&p, grow) != hipSuccess) return LBQ_E_NOMEM;
+    if (hipMemset(p, 0, kCounterBytes) != hipSuccess) return LBQ_E_DEVICE;
+    if (w.ptr) {
+      // the old buffer may still be in use by queued kernels: wait before releasing it
+      (void)hipDeviceSynchronize();
+      (void)hipFree(w.ptr);
+    }
+    w.ptr = p;
+    w.bytes = grow;
+  }
+  *counters = (unsigned*)w.ptr;
+  *partials = (float*)((char*)w.ptr + kCounterBytes);
+  return LBQ_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+}  // namespace
+
+// ---------------------------------------------------------------------------------------------
+// Split-K epilogue shared by the GEMV kernels: every workgroup of a tile has written its fp32
+// partial sums; the last one to arrive adds them in super-group order (deterministic), rounds
+// to bf16 and re-arms the tile counter for the next call.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ void splitk_finish(const float* partial, unsigned* counter,
+                                              uint16_t* y, int n, int np, int supers, int batch,
+                                              int row) {
+  __shared__ unsigned s_last;
+  __threadfence();
+  if (threadIdx.x == 0) {
+    unsigned prev = atomicAdd(counter, 1u);
+    s_last = (prev == (unsigned)supers - 1u) ? 1u : 0u;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  for (int b = 0; b < batch; ++b) {
+    float sum = 0.f;
+    for (int j = 0; j < supers; ++j)
+      sum += __builtin_nontemporal_load(&partial[((size_t)b * supers + j) * np + row]);
+    if (row < n) y[(size_t)b * n + row] = f32_to_bf16(sum);
+  }
+  if (threadIdx.x == 0) atomicExch(counter, 0u);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Q1_0_g128 GEMV.
+//
+// One wave per (64-row tile, super-group of eight 128-weight groups). The wave first turns its
+// slice of x into lookup tables in LDS: for every 4 consecutive inputs (a "chunk") a table of
+// the 16 signed sums +-x0 +-x1 +-x2 +-x3, indexed by the 4 sign bits. Each lane then streams its
+// row's 16-byte sign record per group and adds one table entry per 4 weights: the 4-bit field
+// times 4 is the byte offset of the entry, extracted with one mask from the dword or its
+// rotation by four (the packer stores each dword rotated left by two for this). Group partial
+// sums are weighted by the fp16 scale and accumulated in fp32.
+// ---------------------------------------------------------------------------------------------
+template <int NB>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8))) void q1_gemv_kernel(
+    const uint8_t* __restrict__ w, const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
+    float* __restrict__ partial, unsigned* __restrict__ counters, int n, int k, int np,
+    int groups, int supers, long long tile_bytes, int batch) {
+  extern __shared__ float lut[];  // [NB][8 groups][32 chunks][16 entries]
+  const int tile = blockIdx.x, sg = blockIdx.y, lane = threadIdx.x;
+  const int g0 = sg * kSuper;
+  const int gcount = min(kSuper, groups - g0);
+  const uint8_t* base = w + (size_t)tile * tile_bytes + (size_t)sg * (kBlock * (1 + kSuper));
+
+  // issue every load of this super-group up front: 16 B of scales + 16 B per group
+  const u32x4 sc = *(const u32x4*)(base + lane * 16);
+  u32x4 wq[kSuper];
+#pragma unroll
+  for (int i = 0; i < kSuper; ++i)
+    if (i < gcount) wq[i] = ld_stream16(base + kBlock * (1 + i) + lane * 16);
+  float scale[kSuper];
+  scale[0] = f16_to_f32(sc.x & 0xFFFF); scale[1] = f16_to_f32(sc.x >> 16);
+  scale[2] = f16_to_f32(sc.y & 0xFFFF); scale[3] = f16_to_f32(sc.y >> 16);
+  scale[4] = f16_to_f32(sc.z & 0xFFFF); scale[5] = f16_to_f32(sc.z >> 16);
+  scale[6] = f16_to_f32(sc.w & 0xFFFF); scale[7] = f16_to_f32(sc.w >> 16);
+
+  const int row = tile * kTileRows + lane;
+  for (int b0 = 0; b0 < batch; b0 += NB) {
+    const int nb = min(NB, batch - b0);
+    __syncthreads();
+    // build the tables of this pass: nb vectors x gcount groups x 32 chunks
+    const int nchunks = nb * gcount * 32;
+    for (int ch = lane; ch < nchunks; ch += 64) {
+      const int bb = ch / (gcount * 32), rem = ch % (gcount * 32);
+      const int i = rem >> 5, c = rem & 31;
+      const uint32_t* xp = (const uint32_t*)(x + (size_t)(b0 + bb) * k + kGroup * (g0 + i) + 4 * c);
+      const uint32_t xa = xp[0], xb = xp[1];
+      const float x0 = bf16_lo(xa), x1 = bf16_hi(xa), x2 = bf16_lo(xb), x3 = bf16_hi(xb);
+      const float p0 = -x0 - x1, p1 = x0 - x1, p2 = x1 - x0, p3 = x0 + x1;
+      const float q0 = -x2 - x3, q1 = x2 - x3, q2 = x3 - x2, q3 = x2 + x3;
+      float4* dst = (float4*)(lut + ((bb * kSuper + i) * 32 + c) * 16);
+      dst[0] = make_float4(p0 + q0, p1 + q0, p2 + q0, p3 + q0);
+      dst[1] = make_float4(p0 + q1, p1 + q1, p2 + q1, p3 + q1);
+      dst[2] = make_float4(p0 + q2, p1 + q2, p2 + q2, p3 + q2);
+      dst[3] = make_float4(p0 + q3, p1 + q3, p2 + q3, p3 + q3);
+    }
+    __syncthreads();
+
+    float acc[NB];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) acc[bb] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kSuper; ++i) {
+      if (i < gcount) {
+        uint32_t s4[4] = {wq[i].x, wq[i].y, wq[i].z, wq[i].w};
+        // an empty asm fence: the field extraction of this group cannot be hoisted above it,
+        // so only one group's lookups are live at a time
+        asm volatile("" : "+v"(s4[0]), "+v"(s4[1]), "+v"(s4[2]), "+v"(s4[3]));
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+          if (bb < nb) {
+            const char* lb = (const char*)lut + (size_t)((bb * kSuper + i) * 32) * 64;
+            float pa = 0.f, pb = 0.f;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+              const uint32_t s = s4[d];
+              const uint32_t r = __builtin_amdgcn_alignbit(s, s, 4);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                pa += *(const float*)(lb + (8 * d + 2 * q) * 64 + field4(s, q));
+                pb += *(const float*)(lb + (8 * d + 2 * q + 1) * 64 + field4(r, q));
+              }
+            }
+            acc[bb] = fmaf(scale[i], pa + pb, acc[bb]);
+          }
+        }
+      }
+      // keep each group's lookups together: hoisting all of them costs hundreds of VGPRs
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      if (bb < nb) {
+        if (supers == 1) {
+          if (row < n) y[(size_t)(b0 + bb) * n + row] = f32_to_bf16(acc[bb]);
+        } else {
+          partial[((size_t)(b0 + bb) * supers + sg) * np + row] = acc[bb];
+        }
+      }
+    }
+  }
+  if (supers > 1) splitk_finish(partial, counters + tile, y, n, np, supers, batch, row);
+}
+
+// ---------------------------------------------------------------------------------------------
+// INT4 g128 GEMV.
+//
+// One wave per (64-row tile, super-group). x of the super-group sits in LDS as bf16 and is read
+// by broadcast. Codes are stored offset-binary (n = q + 8); two codes at a time are placed in
+// the top four mantissa bits of a pair of bf16 ones, giving 1 + n/16, and multiplied into the
+// matching x pair with one dot2: sum (1 + n/16) x = S + sum(n x)/16, so per group
+// sum q x = 16 * acc - 24 * S with S the group's sum of x (kept in LDS).
+// ---------------------------------------------------------------------------------------------
+template <int NB>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8))) void i4_gemv_kernel(
+    const uint8_t* __restrict__ w, const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
+    float* __restrict__ partial, unsigned* __restrict__ counters, int n, int k, int np,
+    int groups, int supers, long long tile_bytes, int batch) {
+  __shared__ __attribute__((aligned(16))) uint32_t xs[NB][kSuper * kGroup / 2];  // bf16 pairs
+  __shared__ float gsum[NB][kSuper];
+  const int tile = blockIdx.x, sg = blockIdx.y, lane = threadIdx.x;
+  const int g0 = sg * kSuper;
+  const int gcount = min(kSuper, groups - g0);
+  const uint8_t* base = w + (size_t)tile * tile_bytes + (size_t)sg * (kBlock * (1 + kSuper * kI4GroupBlocks));
+  const u32x4 sc = *(const u32x4*)(base + lane * 16);
+  float scale[kSuper];
+  scale[0] = f16_to_f32(sc.x & 0xFFFF); scale[1] = f16_to_f32(sc.x >> 16);
+  scale[2] = f16_to_f32(sc.y & 0xFFFF); scale[3] = f16_to_f32(sc.y >> 16);
+  scale[4] = f16_to_f32(sc.z & 0xFFFF); scale[5] = f16_to_f32(sc.z >> 16);
+  scale[6] = f16_to_f32(sc.w & 0xFFFF); scale[7] = f16_to_f32(sc.w >> 16);
+  const int row = tile * kTileRows + lane;
+
+  for (int b0 = 0; b0 < batch; b0 += NB) {
+    const int nb = min(NB, batch - b0);
+    __syncthreads();
+    // stage x pairs of this super-group and the per-group sums
+    for (int bb = 0; bb < nb; ++bb) {
+      const uint32_t* xp = (const uint32_t*)(x + (size_t)(b0 + bb) * k + kGroup * g0);
+      for (int p = lane; p < gcount * kGroup / 2; p += 64) xs[bb][p] = xp[p];
+    }
+    __syncthreads();
+    if (lane < nb * kSuper) {
+      const int bb = lane / kSuper, i = lane % kSuper;
+      float s = 0.f;
+      if (i < gcount)
+        for (int p = 0; p < kGroup / 2; ++p) {
+          const uint32_t v = xs[bb][i * (kGroup / 2) + p];
+          s += bf16_lo(v) + bf16_hi(v);
+        }
+      gsum[bb][i] = s;
+    }
+    __syncthreads();
+
+    float acc[NB];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) acc[bb] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kSuper; ++i) {
+      if (i >= gcount) break;
+      const uint8_t* gp = base + kBlock + (size_t)i * (kI4GroupBlocks * kBlock) + lane * 16;
+      u32x4 wv[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) wv[m] = ld_stream16(gp + m * kBlock);
+      float ga[NB];
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) ga[bb] = 0.f;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t s4[4] = {wv[m].x, wv[m].y, wv[m].z, wv[m].w};
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+          const uint32_t s = s4[ww];
+          const uint32_t t0 = ((s << 3) & 0x00780078u) | 0x3F803F80u;
+          const uint32_t t1 = ((s >> 1) & 0x00780078u) | 0x3F803F80u;
+          const uint32_t t2 = ((s >> 5) & 0x00780078u) | 0x3F803F80u;
+          const uint32_t t3 = ((s >> 9) & 0x00780078u) | 0x3F803F80u;
+#pragma unroll
+          for (int bb = 0; bb < NB; ++bb) {
+            if (bb < nb) {
+              const u32x4 xv = *(const u32x4*)&xs[bb][i * (kGroup / 2) + 16 * m + 4 * ww];
+              float a = ga[bb];
+              a = dot2_bf16(t0, xv.x, a);
+              a = dot2_bf16(t1, xv.y, a);
+              a = dot2_bf16(t2, xv.z, a);
+              a = dot2_bf16(t3, xv.w, a);
+              ga[bb] = a;
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        if (bb < nb) {
+          const float sx = gsum[bb][i];
+          acc[bb] = fmaf(scale[i], fmaf(16.f, ga[bb], -24.f * sx), acc[bb]);
+        }
+      }
+    }
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      if (bb < nb) {
+        if (supers == 1) {
+          if (row < n) y[(size_t)(b0 + bb) * n + row] = f32_to_bf16(acc[bb]);
+        } else {
+          partial[((size_t)(b0 + bb) * supers + sg) * np + row] = acc[bb];
+        }
+      }
+    }
+  }
+  if (supers > 1) splitk_finish(partial, counters + tile, y, n, np, supers, batch, row);
+}
+
+// ---------------------------------------------------------------------------------------------
+// 2-bit integer MLP, all layers fused in one kernel. A workgroup carries kMlpVec input vectors
+// through every layer with the activations in LDS. Per neuron the kernel accumulates
+// sum_k c_k a_k exactly in int32 (c = code 0..3) and subtracts 2 sum_k a_k: the same value as
+// sum_k (c_k - 2) a_k, and since reduction modulo 2^16 is a ring homomorphism, truncating it
+// once to 16 bits gives exactly the 16-bit register-pair result of wrapping after every
+// multiply-accumulate. Then the arithmetic shift right by 2 and, between hidden layers, ReLU.
+// ---------------------------------------------------------------------------------------------
+constexpr int kMlpVec = 4;
+struct MlpArgs {
+  const uint8_t* w[LBQ_MLP_MAX_LAYERS];
+  int dims[LBQ_MLP_MAX_LAYERS + 1];
+  int n_layers;
+};
+
+__global__ __launch_bounds__(256) void mlp2bit_kernel(MlpArgs P, const int16_t* __restrict__ x,
+                                                      int16_t* __restrict__ logits,
+                                                      int32_t* __restrict__ argmax, int batch) {
+  __shared__ int16_t act[2][kMlpVec][LBQ_MLP_MAX_DIM];
+  __shared__ int32_t asum[kMlpVec];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int v0 = blockIdx.x * kMlpVec;
+  const int nv = min(kMlpVec, batch - v0);
+  const int d0 = P.dims[0];
+  for (int i = tid; i < nv * d0; i += 256) act[0][i / d0][i % d0] = x[(size_t)v0 * d0 + i];
+  int cur = 0;
+  for (int l = 0; l < P.n_layers; ++l) {
+    const int kin = P.dims[l], nout = P.dims[l + 1], kb = kin / 4;
+    __syncthreads();
+    if (wave < nv) {   // one wave per vector: sum of the layer input
+      int s = 0;
+      for (int j = lane; j < kin; j += 64) s += act[cur][wave][j];
+      for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+      if (lane == 0) asum[wave] = s;
+    }
+    __syncthreads();
+    const uint8_t* W = P.w[l];
+    const bool relu = l < P.n_layers - 1;
+    for (int item = tid; item < nv * nout; item += 256) {
+      const int v = item / nout, r = item % nout;
+      const uint8_t* wr = W + (size_t)r * kb;
+      const int16_t* a = act[cur][v];
+      int acc = 0;
+      for (int j = 0; j < kb; ++j) {
+        const uint32_t byte = wr[j];
+        acc += (int)(byte & 3u) * a[4 * j];
+        acc += (int)((byte >> 2) & 3u) * a[4 * j + 1];
+        acc += (int)((byte >> 4) & 3u) * a[4 * j + 2];
+        acc += (int)(byte >> 6) * a[4 * j + 3];
+      }
+      const int16_t s = (int16_t)(uint16_t)(uint32_t)(acc - 2 * asum[v]);
+      int16_t h = (int16_t)(s >> 2);   // arithmetic shift: floor(s / 4)
+      if (relu && h < 0) h = 0;
+      act[cur ^ 1][v][r] = h;
+    }
+    cur ^= 1;
+  }
+  __syncthreads();
+  const int nout = P.dims[P.n_layers];
+  for (int i = tid; i < nv * nout; i += 256)
+    logits[(size_t)v0 * nout + i] = act[cur][i / nout][i % nout];
+  if (argmax && tid < nv) {
+    int best = 0;
+    for (int j = 1; j < nout; ++j)
+      if (act[cur][tid][j] > act[cur][tid][best]) best = j;
+    argmax[v0 + tid] = best;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// RMS rescale: one workgroup per vector; fixed-order tree reduction of sum h^2 in fp32.
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void rms_kernel(const uint16_t* __restrict__ y,
+                                                  const uint16_t* __restrict__ y2,
+                                                  uint16_t* __restrict__ out, int n, float eps) {
+  __shared__ float red[256];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const uint16_t* yb = y + (size_t)b * n;
+  const uint16_t* y2b = y2 ? y2 + (size_t)b * n : nullptr;
+  float ss = 0.f;
+  for (int j = tid; j < n; j += 256) {
+    float h = bf16_to_f32(yb[j]);
+    if (y2b) h *= bf16_to_f32(y2b[j]);
+    ss = fmaf(h, h, ss);
+  }
+  red[tid] = ss;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) red[tid] += red[tid + s];
+    __syncthreads();
+  }
+  const float denom = sqrtf(red[0] / (float)n + eps);
+  for (int j = tid; j < n; j += 256) {
+    float h = bf16_to_f32(yb[j]);
+    if (y2b) h *= bf16_to_f32(y2b[j]);
+    out[(size_t)b * n + j] = f32_to_bf16(h / denom);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// device entry points
+// ---------------------------------------------------------------------------------------------
+static lbq_status launch_status() {
+  return hipGetLastError() == hipSuccess ? LBQ_OK : LBQ_E_DEVICE;
+}
+
+extern "C" lbq_status lbq_mlp_2bit_i16(const void* const* d_layer_w, const int32_t* dims,
+                                       int32_t n_layers, const int16_t* d_x, int16_t* d_logits,
+                                       int32_t* d_argmax, int32_t batch, void* stream) {
+  if (!d_layer_w || !dims) return LBQ_E_NULL;
+  if (n_layers < 1 || n_layers > LBQ_MLP_MAX_LAYERS || batch < 0) return LBQ_E_SHAPE;
+  MlpArgs P;
+  memset(&P, 0, sizeof(P));
+  P.n_layers = n_layers;
+  for (int l = 0; l <= n_layers; ++l) {
+    const int d = dims[l];
+    if (d < 1 || d > LBQ_MLP_MAX_DIM) return LBQ_E_SHAPE;
+    if (l < n_layers && (d < 4 || d % 4 != 0)) return LBQ_E_SHAPE;
+    P.dims[l] = d;
+  }
+  for (int l = 0; l < n_layers; ++l) {
+    if (!d_layer_w[l]) return LBQ_E_NULL;
+    P.w[l] = (const uint8_t*)d_layer_w[l];
+  }
+  if (batch == 0) return LBQ_OK;
+  if (!d_x || !d_logits) return LBQ_E_NULL;
+  if ((uintptr_t)d_x % 2 || (uintptr_t)d_logits % 2 || (uintptr_t)d_argmax % 4) return LBQ_E_ALIGN;
+  const size_t xb = (size_t)batch * dims[0] * 2, lb = (size_t)batch * dims[n_layers] * 2;
+  if (overlaps(d_logits, lb, d_x, xb)) return LBQ_E_ALIAS;
+  if (d_argmax && (overlaps(d_argmax, (size_t)batch * 4, d_x, xb) ||
+                   overlaps(d_argmax, (size_t)batch * 4, d_logits, lb)))
+    return LBQ_E_ALIAS;
+  for (int l = 0; l < n_layers; ++l) {
+    const size_t wb = (size_t)dims[l + 1] * (dims[l] / 4);
+    if (overlaps(d_logits, lb, d_layer_w[l], wb) ||
+        (d_argmax && overlaps(d_argmax, (size_t)batch * 4, d_layer_w[l], wb)))
+      return LBQ_E_ALIAS;
+  }
+  const int grid = (batch + kMlpVec - 1) / kMlpVec;
+  hipLaunchKernelGGL(mlp2bit_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, P, d_x,
+                     d_logits, d_argmax, batch);
+  return launch_status();
+}
+
+enum class Fmt { Q1, I4 };
+
+static lbq_status gemv_common(Fmt fmt, const void* d_w, int32_t n, int32_t k,
+                              const uint16_t* d_x, uint16_t* d_y, int32_t batch, void* stream) {
+  Geometry g;
+  if (!make_geometry(n, k, fmt == Fmt::Q1 ? kQ1GroupBlocks : kI4GroupBlocks, &g)) return LBQ_E_SHAPE;
+  if (batch < 0 || batch > LBQ_MAX_BATCH) return LBQ_E_SHAPE;
+  if (batch == 0) return LBQ_OK;
+  if (!d_w || !d_x || !d_y) return LBQ_E_NULL;
+  if ((uintptr_t)d_w % 16 || (uintptr_t)d_x % 4 || (uintptr_t)d_y % 4) return LBQ_E_ALIGN;
+  const size_t yb = (size_t)batch * n * 2;
+  if (overlaps(d_y, yb, d_x, (size_t)batch * k * 2) || overlaps(d_y, yb, d_w, layout_bytes(g)))
+    return LBQ_E_ALIAS;
+  hipStream_t s = (hipStream_t)stream;
+  unsigned* counters = nullptr;
+  float* partials = nullptr;
+  if (g.supers > 1) {
+    if (g.tiles * sizeof(unsigned) > kCounterBytes) return LBQ_E_SHAPE;
+    lbq_status st = get_workspace((size_t)batch * g.supers * g.np * sizeof(float), s, &counters,
+                                  &partials);
+    if (st != LBQ_OK) return st;
+  }
+  const dim3 grid((unsigned)g.tiles, (unsigned)g.supers);
+  const int nbp = batch <= 1 ? 1 : (batch <= 2 ? 2 : 4);
+  if (fmt == Fmt::Q1) {
+    const size_t lds = (size_t)nbp * kSuper * 32 * 16 * sizeof(float);
+#define LAUNCH_Q1(NB)                                                                            \
+  hipLaunchKernelGGL(q1_gemv_kernel<NB>, grid, dim3(64), lds, s, (const uint8_t*)d_w, d_x, d_y, \
+                     partials, counters, n, k, (int)g.np, (int)g.groups, (int)g.supers,         \
+                     (long long)g.tile_bytes, batch)
+    if (nbp == 1) LAUNCH_Q1(1); else if (nbp == 2) LAUNCH_Q1(2); else LAUNCH_Q1(4);
+#undef LAUNCH_Q1
+  } else {
+#define LAUNCH_I4(NB)                                                                            \
+  hipLaunchKernelGGL(i4_gemv_kernel<NB>, grid, dim3(64), 0, s, (const uint8_t*)d_w, d_x, d_y,   \
+                     partials, counters, n, k, (int)g.np, (int)g.groups, (int)g.supers,         \
+                     (long long)g.tile_bytes, batch)
+    if (nbp == 1) LAUNCH_I4(1); else if (nbp == 2) LAUNCH_I4(2); else LAUNCH_I4(4);
+#undef LAUNCH_I4
+  }
+  return launch_status();
+}
+
+extern "C" lbq_status lbq_gemv_q1g128(const void* d_w, int32_t n, int32_t k, const uint16_t* d_x,
+                                      uint16_t* d_y, int32_t batch, void* stream) {
+  return gemv_common(Fmt::Q1, d_w, n, k, d_x, d_y, batch, stream);
+}
+
+extern "C" lbq_status lbq_gemv_i4g128(const void* d_w, int32_t n, int32_t k, const uint16_t* d_x,
+                                      uint16_t* d_y, int32_t batch, void* stream) {
+  return gemv_common(Fmt::I4, d_w, n, k, d_x, d_y, batch, stream);
+}
+
+extern "C" lbq_status lbq_rms_rescale_bf16(const uint16_t* d_y, const uint16_t* d_y2,
+                                           uint16_t* d_x, int32_t n, int32_t batch, float eps,
+                                           void* stream) {
+  if (n < 1 || batch < 0 || batch > LBQ_MAX_BATCH || !(eps >= 0.f)) return LBQ_E_SHAPE;
+  if (batch == 0) return LBQ_OK;
+  if (!d_y || !d_x) return LBQ_E_NULL;
+  if ((uintptr_t)d_y % 2 || (uintptr_t)d_x % 2 || (uintptr_t)d_y2 % 2) return LBQ_E_ALIGN;
+  const size_t bytes = (size_t)batch * n * 2;
+  if (overlaps(d_x, bytes, d_y, bytes) || (d_y2 && overlaps(d_x, bytes, d_y2, bytes)))
+    return LBQ_E_ALIAS;
+  hipLaunchKernelGGL(rms_kernel, dim3(batch), dim3(256), 0, (hipStream_t)stream, d_y, d_y2, d_x,
+                     n, eps);
+  return launch_status();
+}
+
+extern "C" lbq_status lbq_decode_step_q1g128(const lbq_q1_layer* layers, int32_t n_layers,
+                                             int32_t hidden, int32_t kv, int32_t ffn,
+                                             const uint16_t* d_x0, uint16_t* d_act,
+                                             int32_t batch, float eps, void* stream) {
+  if (!layers || !d_x0 || !d_act) return LBQ_E_NULL;
+  const size_t elems = lbq_decode_act_elems(n_layers, hidden, kv, ffn, batch);
+  if (!elems || !(eps >= 0.f)) return LBQ_E_SHAPE;
+  if ((uintptr_t)d_x0 % 4 || (uintptr_t)d_act % 4) return LBQ_E_ALIGN;
+  for (int l = 0; l < n_layers; ++l) {
+    const lbq_q1_layer& L = layers[l];
+    if (!L.q || !L.k || !L.v || !L.o || !L.gate || !L.up || !L.down) return LBQ_E_NULL;
+  }
+  if (overlaps(d_x0, (size_t)batch * hidden * 2, d_act, elems * 2)) return LBQ_E_ALIAS;
+  hipStream_t s = (hipStream_t)stream;
+  auto at = [&](int layer, int slot) {
+    return d_act + lbq_decode_act_offset(layer, slot, n_layers, hidden, kv, ffn, batch);
+  };
+  if (hipMemcpyAsync(at(0, LBQ_ACT_X), d_x0, (size_t)batch * hidden * 2, hipMemcpyDeviceToDevice,
+                     s) != hipSuccess)
+    return LBQ_E_DEVICE;
+  lbq_status st = LBQ_OK;
+#define CHECK(expr) do { st = (expr); if (st != LBQ_OK) return st; } while (0)
+  for (int l = 0; l < n_layers; ++l) {
+    const lbq_q1_layer& L = layers[l];
+    const uint16_t* x = at(l, LBQ_ACT_X);
+    CHECK(lbq_gemv_q1g128(L.q, hidden, hidden, x, at(l, LBQ_ACT_Q), batch, s));
+    CHECK(lbq_gemv_q1g128(L.k, kv, hidden, x, at(l, LBQ_ACT_K), batch, s));
+    CHECK(lbq_gemv_q1g128(L.v, kv, hidden, x, at(l, LBQ_ACT_V), batch, s));
+    CHECK(lbq_gemv_q1g128(L.gate, ffn, hidden, x, at(l, LBQ_ACT_GATE), batch, s));
+    CHECK(lbq_gemv_q1g128(L.up, ffn, hidden, x, at(l, LBQ_ACT_UP), batch, s));
+    CHECK(lbq_rms_rescale_bf16(at(l, LBQ_ACT_Q), nullptr, at(l, LBQ_ACT_XO), hidden, batch, eps, s));
+    CHECK(lbq_rms_rescale_bf16(at(l, LBQ_ACT_GATE), at(l, LBQ_ACT_UP), at(l, LBQ_ACT_XD), ffn, batch,
+                               eps, s));
+    CHECK(lbq_gemv_q1g128(L.o, hidden, hidden, at(l, LBQ_ACT_XO), at(l, LBQ_ACT_O), batch, s));
+    CHECK(lbq_gemv_q1g128(L.down, hidden, ffn, at(l, LBQ_ACT_XD), at(l, LBQ_ACT_DOWN), batch, s));
+    uint16_t* xn = (l + 1 < n_layers) ? at(l + 1, LBQ_ACT_X)
+                                      : d_act + lbq_decode_act_offset(n_layers, LBQ_ACT_NSLOTS,
+                                                                      n_layers, hidden, kv, ffn, batch);
+    CHECK(lbq_rms_rescale_bf16(at(l, LBQ_ACT_DOWN), nullptr, xn, hidden, batch, eps, s));
+  }
+#undef CHECK
+  return LBQ_OK;
+}

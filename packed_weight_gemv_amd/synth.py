@@ -52,9 +52,10 @@ def random_bytes(r: np.random.Generator, shape) -> np.ndarray:
 
 
 def fp16_abs_normal(r: np.random.Generator, shape, sigma: float) -> np.ndarray:
-    """fp16 bit patterns of |N(0, sigma)| (numpy's float64 -> float16 cast rounds to nearest
-    even and keeps subnormals)."""
-    return np.abs(r.normal(0.0, sigma, size=shape)).astype(np.float16).view(np.uint16)
+    """fp16 bit patterns of |N(0, sigma)|, drawn in float32 (numpy's float32 -> float16 cast
+    rounds to nearest even and keeps subnormals)."""
+    z = r.standard_normal(size=shape, dtype=np.float32)
+    return np.abs(z * np.float32(sigma)).astype(np.float16).view(np.uint16)
 
 
 def f32_to_bf16_bits(v: np.ndarray) -> np.ndarray:

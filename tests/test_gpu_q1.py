@@ -1,0 +1,118 @@
+"""GPU parity of lbq_gemv_q1g128 against the CPU oracle (tolerance: |err| <= 2e-3 * sum|s w x|),
+plus exact one-hot probes and bitwise metamorphic properties."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from packed_weight_gemv_amd import synth
+from tests._gpu import bits, check_within, empty_bf16, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(lbq, m, x):
+    n, k = m.shape
+    w = to_dev(lbq.lbq_pack_q1g128(m.signs, m.scales))
+    y = empty_bf16(x.shape[0], n)
+    lbq.lbq_gemv_q1g128(w, n, k, to_dev(x), y)
+    torch.cuda.synchronize()
+    return bits(y)
+
+
+@pytest.mark.parametrize("n,k", [(130, 1152), (64, 128), (1, 256), (200, 2176), (333, 9216)])
+def test_parity_small_shapes_with_ragged_tails(lbq, n, k):
+    m = synth.q1_matrix(n, k, workload=20, matrix=n)
+    x = synth.activations(1, k, workload=20, matrix=n)
+    y = _run(lbq, m, x)
+    ref, l1 = oracle.gemv_q1g128(m.signs, m.scales, x)
+    check_within(y, ref, l1, f"q1 {n}x{k}")
+
+
+@pytest.mark.parametrize("batch", [1, 2, 3, 4, 5, 8, 16])
+def test_parity_batches(lbq, batch):
+    n, k = 192, 2176
+    m = synth.q1_matrix(n, k, workload=21)
+    x = synth.activations(batch, k, workload=21, extra=batch)
+    y = _run(lbq, m, x)
+    ref, l1 = oracle.gemv_q1g128(m.signs, m.scales, x)
+    check_within(y, ref, l1, f"q1 batch {batch}")
+
+
+@pytest.mark.parametrize("name,n,k,batch", [
+    ("square", 5120, 5120, 1),
+    ("gate", 17408, 5120, 1), ("gate", 17408, 5120, 4), ("gate", 17408, 5120, 16),
+    ("down", 5120, 17408, 1), ("down", 5120, 17408, 16),
+    ("kv", 1024, 5120, 8),
+])
+def test_parity_full_size_sampled_rows(lbq, name, n, k, batch):
+    wl = synth.W_Q1_SQUARE if name == "square" else synth.W_Q1_MLP
+    m = synth.q1_matrix(n, k, workload=wl, matrix=n + k)
+    x = synth.activations(batch, k, workload=wl, matrix=n + k, extra=batch)
+    y = _run(lbq, m, x)
+    rows = np.unique(np.concatenate([np.arange(0, n, max(1, n // 97)), [n - 1, 63, 64]])).astype(np.int32)
+    ref, l1 = oracle.gemv_q1g128(m.signs, m.scales, x, rows=rows)
+    check_within(y[:, rows], ref, l1, f"q1 {name} B={batch}")
+
+
+def test_one_hot_probes_are_exact(lbq):
+    n, k = 70, 256
+    m = synth.q1_matrix(n, k, workload=22)
+    one = synth.f32_to_bf16_bits(np.ones(1, dtype=np.float32))[0]
+    bitsm = np.unpackbits(m.signs, axis=1, bitorder="little")
+    for j0 in range(0, k, 16):
+        x = np.zeros((16, k), dtype=np.uint16)
+        x[np.arange(16), j0 + np.arange(16)] = one
+        y = _run(lbq, m, x)
+        for i in range(16):
+            j = j0 + i
+            expect = np.where(bitsm[:, j] == 1, 1.0, -1.0) * oracle.f16_to_f64(m.scales[:, j // 128])
+            assert np.array_equal(y[i], oracle.round_bf16(expect)), j
+
+
+def test_flipping_every_sign_negates_exactly(lbq):
+    n, k = 128, 3072
+    m = synth.q1_matrix(n, k, workload=23)
+    x = synth.activations(2, k, workload=23)
+    y1 = _run(lbq, m, x)
+    flipped = synth.Q1Matrix(np.bitwise_not(m.signs), m.scales)
+    y2 = _run(lbq, flipped, x)
+    assert np.array_equal(y2, y1 ^ 0x8000)
+
+
+def test_power_of_two_input_scaling_is_exact_and_runs_are_deterministic(lbq):
+    n, k = 256, 5120
+    m = synth.q1_matrix(n, k, workload=24)
+    x = synth.activations(1, k, workload=24)
+    x4 = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(x) * np.float32(4.0))
+    y1 = _run(lbq, m, x)
+    y4 = _run(lbq, m, x4)
+    assert np.array_equal(oracle.bf16_to_f64(y4), 4.0 * oracle.bf16_to_f64(y1))
+    assert np.array_equal(_run(lbq, m, x), y1)
+
+
+def test_scale_edge_values(lbq):
+    # subnormal, zero, negative and large fp16 scales; all-ones and all-zero sign rows
+    n, k = 64, 1024
+    m = synth.q1_matrix(n, k, workload=25)
+    m.scales[0, :] = 0x0001
+    m.scales[1, :] = 0x0000
+    m.scales[2, :] = 0x8000 | 0x2A3C
+    m.scales[3, :] = 0x7BFF
+    m.signs[4, :] = 0xFF
+    m.signs[5, :] = 0x00
+    x = synth.activations(3, k, workload=25)
+    y = _run(lbq, m, x)
+    ref, l1 = oracle.gemv_q1g128(m.signs, m.scales, x)
+    check_within(y, ref, l1, "q1 scale edges")
+    assert np.all((y[:, 1] & 0x7FFF) == 0)
+
+
+def test_batch_zero_is_a_no_op(lbq):
+    m = synth.q1_matrix(64, 128, workload=26)
+    w = to_dev(lbq.lbq_pack_q1g128(m.signs, m.scales))
+    y = torch.full((1, 64), 7, dtype=torch.int16, device="cuda:0")
+    x = torch.zeros((0, 128), dtype=torch.int16, device="cuda:0")
+    lbq.lbq_gemv_q1g128(w, 64, 128, x, y)
+    torch.cuda.synchronize()
+    assert (y == 7).all()
