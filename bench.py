@@ -5,9 +5,10 @@
 A step is one decode step of the whole stream: 64 layers x (q, o 5120x5120; k, v 1024x5120;
 gate, up 17408x5120; down 5120x17408) Q1_0_g128 GEMVs with the RMS rescales between them
 (lbq_decode_step_q1g128), over seeded synthetic weights (sign bits Bernoulli(0.5), fp16 scales
-|N(0, 0.02)|) and a bf16 N(0, 1) input, all resident in HBM before timing starts. The step is
-replayed from a HIP graph; W untimed warm-up steps precede exactly K timed steps bracketed by
-device synchronisation.
+|N(0, 0.02)|) and a bf16 N(0, 1) input, all resident in HBM before timing starts. At batch 1 a
+step is one cooperative launch of the persistent engine; larger batches replay a HIP graph of
+the per-projection launches. W untimed warm-up steps precede exactly K timed steps bracketed
+by device synchronisation.
 
 Printed: one JSON line on stdout (progress goes to stderr).
 """
@@ -100,7 +101,7 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
     graph = None
-    if not args.no_graph:
+    if not args.no_graph and B > 1:   # batch 1 is a single cooperative launch per step
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             step()
@@ -109,45 +110,59 @@ def main() -> int:
         torch.cuda.synchronize()
     run = graph.replay if graph is not None else step
     log(f"timing {args.steps} steps ({'graph' if graph is not None else 'eager'})")
+    # every step is bracketed by its own event pair on the launch stream, inside the timed
+    # region: at batch 1 a step is exactly one launch of the persistent kernel, so these give
+    # that kernel's average duration
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
+    start.record(stream)
+    for i in range(args.steps):
+        evs[i][0].record(stream)
         run()
-    end.record()
+        evs[i][1].record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
+    lbq.lbq_device_check()
     ms = start.elapsed_time(end) / args.steps
     gbs = bytes_per_step / (ms * 1e-3) / 1e9
+    step_kernel_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
 
-    # ---- dominant kernel: every Q1 GEMV launch of a step bracketed by events -------------------
-    stream = torch.cuda.current_stream()
-    gemv_ms, gemv_bytes, launches = 0.0, 0, 0
-    for _ in range(args.kernel_steps):
-        evs = []
-        for l in range(L):
-            src = {"q": "x", "k": "x", "v": "x", "gate": "x", "up": "x", "o": "xo", "down": "xd"}
-            for nm in ("q", "k", "v", "gate", "up", "o", "down"):
-                n, k = shapes[nm]
-                xin = lbq.act_view(act, src[nm], l, L, hid, kv, ffn, B)
-                yout = lbq.act_view(act, nm, l, L, hid, kv, ffn, B)
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                lbq.lbq_gemv_q1g128(layers[l][nm], n, k, xin, yout)
-                e1.record(stream)
-                evs.append((e0, e1, n * k * 9 // 64))
+    # ---- dominant kernel ---------------------------------------------------------------------
+    if B == 1:
+        kern_name = "q1_engine_kernel (whole decode step, one cooperative launch)"
+        kern_avg_ms, kern_bytes = step_kernel_ms, bytes_per_step
+    else:
+        # host-driven step: every Q1 GEMV launch of a step bracketed by events
+        kern_name = "q1_gemv_kernel (per-projection launches)"
+        gemv_ms, gemv_bytes, launches = 0.0, 0, 0
+        src = {"q": "x", "k": "x", "v": "x", "gate": "x", "up": "x", "o": "xo", "down": "xd"}
+        for _ in range(max(1, args.kernel_steps)):
+            lst = []
+            for l in range(L):
+                for nm in ("q", "k", "v", "gate", "up", "o", "down"):
+                    n, k = shapes[nm]
+                    xin = lbq.act_view(act, src[nm], l, L, hid, kv, ffn, B)
+                    yout = lbq.act_view(act, nm, l, L, hid, kv, ffn, B)
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    lbq.lbq_gemv_q1g128(layers[l][nm], n, k, xin, yout)
+                    e1.record(stream)
+                    lst.append((e0, e1, n * k * 9 // 64))
+            torch.cuda.synchronize()
+            for e0, e1, nb in lst:
+                gemv_ms += e0.elapsed_time(e1)
+                gemv_bytes += nb
+                launches += 1
+        kern_avg_ms = gemv_ms / launches
+        kern_bytes = gemv_bytes / launches
+        run()   # restore the activation record of a full step for the parity check below
         torch.cuda.synchronize()
-        for e0, e1, nb in evs:
-            gemv_ms += e0.elapsed_time(e1)
-            gemv_bytes += nb
-            launches += 1
-    kern_avg_ms = gemv_ms / max(launches, 1)
-    kern_bytes = gemv_bytes / max(launches, 1)
     kern_gbs = kern_bytes / (kern_avg_ms * 1e-3) / 1e9
-    # restore the activation record of a full step for the parity check below
-    run()
-    torch.cuda.synchronize()
 
     # ---- CPU oracle baseline (bounded sample) + teacher-forced parity of that sample ----------
     cpu = None
@@ -208,7 +223,7 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
             "traffic": None,
-            "kernel": "q1_gemv_kernel<1>",
+            "kernel": kern_name,
             "avg_launch_us": round(kern_avg_ms * 1e3, 3),
             "bytes_per_launch": round(kern_bytes),
         },

@@ -1,0 +1,73 @@
+// lbq_engine.h - program format of the persistent Q1_0_g128 streaming engine (internal).
+//
+// A program is a list of stages. A stage multiplies up to kEngMaxMats Q1_0_g128 matrices with
+// up to kEngMaxSrcs bf16 input vectors (batch 1); the outputs of a stage may feed the inputs of
+// later stages through an RMS rescale. One cooperative launch runs the whole program: every
+// workgroup owns a contiguous, equal share of each stage's work units (64 rows x one block of
+// eight 128-weight groups), and data passes between workgroups as (value, tag) pairs that the
+// reader polls for, so no grid-wide barrier or cache flush is ever needed.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace lbq {
+
+constexpr int kEngMaxMats = 5;
+constexpr int kEngMaxSrcs = 2;
+constexpr int kEngWaves = 8;                        // compute waves: one group of a block each
+constexpr int kEngThreads = (kEngWaves + 1) * 64;   // + one communication wave
+constexpr int kEngRing = 8;                         // weight records in flight per compute wave
+constexpr int kEngSlots = 8;                        // partial hand-off slots (compute -> comm)
+constexpr int kEngMaxStages = 255;
+
+enum EngSrcKind : int32_t { kSrcDirect = 0, kSrcRms = 1, kSrcRmsProd = 2 };
+enum EngMatKind : int32_t { kMatPlain = 0, kMatSumSq = 1, kMatPair = 2 };
+
+// 8-byte tagged word: low 32 bits = payload (fp32 bits, or bf16 bits), high 32 bits = tag.
+typedef unsigned long long tagged_t;
+
+struct EngMat {
+  const uint8_t* w;        // Q1 device layout
+  uint16_t* y;             // plain bf16 output [n] (may be null)
+  tagged_t* yt;            // tagged bf16 output [np]
+  tagged_t* stat;          // tagged per-tile statistic [tiles] (kMatSumSq / kMatPair) or null
+  const tagged_t* partner; // kMatPair: tagged outputs of the partner matrix (same shape)
+  long long tile_bytes;
+  int32_t n, k, tiles, groups, supers, src, kind, unit_base, units, pad;
+};
+
+struct EngSrc {
+  const uint16_t* x;       // kSrcDirect: bf16 input [k]
+  const tagged_t* yt;      // kSrcRms*: tagged outputs of an earlier stage
+  const tagged_t* y2t;     // kSrcRmsProd: second factor
+  const tagged_t* stats;   // kSrcRms*: per-tile statistics of the producer
+  uint16_t* record;        // bf16 copy of the vector for the caller (may be null)
+  float eps;
+  int32_t kind, k, nstats, src_stage, pad;
+};
+
+struct EngStage {
+  EngMat mat[kEngMaxMats];
+  EngSrc src[kEngMaxSrcs];
+  int32_t nmat, nsrc, units, pad;
+};
+
+struct EngProgram {
+  int32_t nstages, nwg, pad0, pad1;
+  EngStage st[1];   // nstages entries
+};
+
+struct EngArgs {
+  const EngProgram* prog;
+  tagged_t* partial;       // two buffers of max_units * 64 tagged partials (by stage parity)
+  long long partial_stride;// elements per buffer
+  uint32_t* error;         // set non-zero on a poll time-out (then every wave exits)
+  uint32_t epoch;          // launch number (>= 1): tags are epoch * 256 + stage
+  int32_t pad;
+};
+
+__host__ __device__ inline uint32_t eng_tag(uint32_t epoch, int stage) { return epoch * 256u + (uint32_t)stage; }
+
+}  // namespace lbq

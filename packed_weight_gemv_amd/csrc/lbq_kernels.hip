@@ -109,29 +109,42 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 }  // namespace
 
 // ---------------------------------------------------------------------------------------------
-// Split-K epilogue shared by the GEMV kernels: every workgroup of a tile has written its fp32
-// partial sums; the last one to arrive adds them in super-group order (deterministic), rounds
-// to bf16 and re-arms the tile counter for the next call.
+// Cross-workgroup exchange without whole-cache maintenance. On gfx950 every XCD has its own L2
+// and the L2s are not coherent with each other; agent-scope relaxed atomic loads and stores are
+// issued with the sc1 bit (write-through / re-fetch), so they are coherent per location across
+// the device. Data passed between workgroups goes through such accesses only, and a producer
+// waits for its stores to complete (vmcnt(0)) before it signals through an atomic counter.
+// This avoids the L2 writeback + invalidate a device-scope fence costs on every workgroup.
 // ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ void st_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores_complete() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Split-K epilogue shared by the GEMV kernels: every workgroup of a tile has stored its fp32
+// partial sums (st_coherent); the last one to arrive adds them in super-group order
+// (deterministic), rounds to bf16 and re-arms the tile counter for the next call.
 __device__ __forceinline__ void splitk_finish(const float* partial, unsigned* counter,
                                               uint16_t* y, int n, int np, int supers, int batch,
                                               int row) {
   __shared__ unsigned s_last;
-  __threadfence();
+  wait_stores_complete();
+  __syncthreads();
   if (threadIdx.x == 0) {
-    unsigned prev = atomicAdd(counter, 1u);
+    unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (prev == (unsigned)supers - 1u) ? 1u : 0u;
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
   for (int b = 0; b < batch; ++b) {
     float sum = 0.f;
-    for (int j = 0; j < supers; ++j)
-      sum += __builtin_nontemporal_load(&partial[((size_t)b * supers + j) * np + row]);
+    for (int j = 0; j < supers; ++j) sum += ld_coherent(&partial[((size_t)b * supers + j) * np + row]);
     if (row < n) y[(size_t)b * n + row] = f32_to_bf16(sum);
   }
-  if (threadIdx.x == 0) atomicExch(counter, 0u);
+  if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -228,7 +241,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8))) void
         if (supers == 1) {
           if (row < n) y[(size_t)(b0 + bb) * n + row] = f32_to_bf16(acc[bb]);
         } else {
-          partial[((size_t)(b0 + bb) * supers + sg) * np + row] = acc[bb];
+          st_coherent(&partial[((size_t)(b0 + bb) * supers + sg) * np + row], acc[bb]);
         }
       }
     }
@@ -336,7 +349,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8))) void
         if (supers == 1) {
           if (row < n) y[(size_t)(b0 + bb) * n + row] = f32_to_bf16(acc[bb]);
         } else {
-          partial[((size_t)(b0 + bb) * supers + sg) * np + row] = acc[bb];
+          st_coherent(&partial[((size_t)(b0 + bb) * supers + sg) * np + row], acc[bb]);
         }
       }
     }
@@ -490,6 +503,13 @@ extern "C" lbq_status lbq_mlp_2bit_i16(const void* const* d_layer_w, const int32
 
 enum class Fmt { Q1, I4 };
 
+// persistent engine (lbq_engine.hip)
+lbq_status lbq_engine_gemv_q1(const void* d_w, int32_t n, int32_t k, const uint16_t* d_x,
+                              uint16_t* d_y, hipStream_t stream);
+lbq_status lbq_engine_decode_q1(const lbq_q1_layer* layers, int32_t L, int32_t hidden, int32_t kv,
+                                int32_t ffn, const uint16_t* d_x0, uint16_t* d_act, float eps,
+                                hipStream_t stream);
+
 static lbq_status gemv_common(Fmt fmt, const void* d_w, int32_t n, int32_t k,
                               const uint16_t* d_x, uint16_t* d_y, int32_t batch, void* stream) {
   Geometry g;
@@ -502,6 +522,10 @@ static lbq_status gemv_common(Fmt fmt, const void* d_w, int32_t n, int32_t k,
   if (overlaps(d_y, yb, d_x, (size_t)batch * k * 2) || overlaps(d_y, yb, d_w, layout_bytes(g)))
     return LBQ_E_ALIAS;
   hipStream_t s = (hipStream_t)stream;
+  if (fmt == Fmt::Q1 && batch == 1) {
+    const lbq_status st = lbq_engine_gemv_q1(d_w, n, k, d_x, d_y, s);
+    if (st != LBQ_E_UNSUPPORTED) return st;
+  }
   unsigned* counters = nullptr;
   float* partials = nullptr;
   if (g.supers > 1) {
@@ -570,6 +594,10 @@ extern "C" lbq_status lbq_decode_step_q1g128(const lbq_q1_layer* layers, int32_t
   }
   if (overlaps(d_x0, (size_t)batch * hidden * 2, d_act, elems * 2)) return LBQ_E_ALIAS;
   hipStream_t s = (hipStream_t)stream;
+  if (batch == 1) {
+    const lbq_status st = lbq_engine_decode_q1(layers, n_layers, hidden, kv, ffn, d_x0, d_act, eps, s);
+    if (st != LBQ_E_UNSUPPORTED) return st;
+  }
   auto at = [&](int layer, int slot) {
     return d_act + lbq_decode_act_offset(layer, slot, n_layers, hidden, kv, ffn, batch);
   };
