@@ -21,6 +21,7 @@ constexpr int kEngThreads = (kEngWaves + 1) * 64;   // + one communication wave
 constexpr int kEngRing = 8;                         // weight records in flight per compute wave
 constexpr int kEngSlots = 8;                        // partial hand-off slots (compute -> comm)
 constexpr int kEngMaxStages = 255;
+constexpr int kEngMaxFinal = 24;                    // block partials summed by one finalisation
 
 enum EngSrcKind : int32_t { kSrcDirect = 0, kSrcRms = 1, kSrcRmsProd = 2 };
 enum EngMatKind : int32_t { kMatPlain = 0, kMatSumSq = 1, kMatPair = 2 };
@@ -33,9 +34,11 @@ struct EngMat {
   uint16_t* y;             // plain bf16 output [n] (may be null)
   tagged_t* yt;            // tagged bf16 output [np]
   tagged_t* stat;          // tagged per-tile statistic [tiles] (kMatSumSq / kMatPair) or null
-  const tagged_t* partner; // kMatPair: tagged outputs of the partner matrix (same shape)
   long long tile_bytes;
-  int32_t n, k, tiles, groups, supers, src, kind, unit_base, units, pad;
+  int32_t n, k, tiles, groups, supers, src, kind, unit_base, units;
+  int32_t item_base;       // finalisation item of tile 0 (-1: finalised with its pair partner)
+  int32_t pair;            // kMatPair partner finalised together with this matrix, or -1
+  int32_t pad;
 };
 
 struct EngSrc {
@@ -45,13 +48,15 @@ struct EngSrc {
   const tagged_t* stats;   // kSrcRms*: per-tile statistics of the producer
   uint16_t* record;        // bf16 copy of the vector for the caller (may be null)
   float eps;
-  int32_t kind, k, nstats, src_stage, pad;
+  int32_t kind, k, nstats, src_stage;
+  int32_t rec_mat;         // a matrix of the stage reading this source (its tile-0 units own the record)
 };
 
 struct EngStage {
   EngMat mat[kEngMaxMats];
   EngSrc src[kEngMaxSrcs];
-  int32_t nmat, nsrc, units, pad;
+  tagged_t* part;                      // tagged unit partials [units * 64], one slot per unit
+  int32_t nmat, nsrc, units, nitems;   // nitems: tiles to finalise (a pair counts once)
 };
 
 struct EngProgram {
@@ -61,8 +66,6 @@ struct EngProgram {
 
 struct EngArgs {
   const EngProgram* prog;
-  tagged_t* partial;       // two buffers of max_units * 64 tagged partials (by stage parity)
-  long long partial_stride;// elements per buffer
   uint32_t* error;         // set non-zero on a poll time-out (then every wave exits)
   uint32_t epoch;          // launch number (>= 1): tags are epoch * 256 + stage
   int32_t pad;

@@ -13,11 +13,16 @@
 //    offset, extracted with one masked operand select (the packer stores each sign dword
 //    rotated left by two so every field sits at bits [8i+2, 8i+5] of the dword or of its
 //    rotation by four).
-//  * The communication wave sums the 8 group partials of a unit, publishes the unit partial
-//    as a (value, tag) word, finalises a tile when all its block partials are published, and
-//    prepares the next stage's input (RMS rescale of earlier outputs). Consumers poll tags;
-//    there is no grid barrier and no cache flush. Every wait is bounded: on a time-out the
-//    error word is set and every wave runs to the end without further work.
+//  * The communication wave sums the 8 group partials of a unit and publishes the unit partial
+//    as a (value, tag) word in the stage's partial array, without waiting on global memory.
+//    Once its units are done, each workgroup finalises its round-robin share of the stage's
+//    output tiles (a gate tile together with the matching up tile, so the pair statistic needs
+//    no second exchange), polling the block partials of a tile in one sweep.
+//  * At a stage start all nine waves fetch the stage's input blocks in one sweep of tagged
+//    loads (the communication wave fetches the producers' tile statistics in the same trip)
+//    and apply the RMS rescale. Consumers poll tags; there is no grid barrier and no cache
+//    flush. Every wait is bounded: on a time-out the error word is set and every wave runs to
+//    the end without further work.
 #include <hip/hip_runtime.h>
 #include <string.h>
 
@@ -131,10 +136,8 @@ struct __attribute__((aligned(16))) EngLds {
   float part[kEngSlots][kEngWaves][64];        // compute -> comm hand-off
   uint32_t ready[kEngSlots];
   uint32_t freed[kEngSlots];
-  int32_t blk_src[2][2], blk_sg[2][2], nblk[2];
+  float denom[2][kEngMaxSrcs];
   int32_t abort_flag;
-  int32_t pend_m[64], pend_t[64];
-  int32_t npend;
 };
 
 // The workgroup's share of a stage: units [u0, u1) (unit counts stay far below 2^21).
@@ -189,17 +192,239 @@ INL void it_next(PP P, int wg, UnitIt& it) {
   }
 }
 
-// Block (LUT region) of a unit: position of (src, sg) in the workgroup's block list.
-INL int block_of(const EngLds& L, int par, int src, int sg) {
-  return (L.nblk[par] > 1 && L.blk_src[par][1] == src && L.blk_sg[par][1] == sg) ? 1 : 0;
+// Distinct (source, block) pairs of the workgroup's share of stage S, in unit order. The host
+// only builds programs whose shares touch at most two; n == 3 flags a violation. Scalar work,
+// repeated by every wave rather than shared through LDS.
+struct Blocks {
+  int n;
+  int src0, sg0, src1, sg1;
+};
+INL Blocks wg_blocks(SP S, int u0, int u1) {
+  Blocks B;
+  B.n = 0;
+  B.src0 = B.src1 = B.sg0 = B.sg1 = 0;
+  if (u1 <= u0) return B;
+  int m = 0;
+  while (u0 >= S->mat[m].unit_base + S->mat[m].units) ++m;
+  const int c = u0 - S->mat[m].unit_base;
+  int sg = c / S->mat[m].tiles;
+  int tile = c - sg * S->mat[m].tiles;
+  for (int u = u0; u < u1;) {
+    const int src = S->mat[m].src;
+    if (B.n == 0) {
+      B.src0 = src;
+      B.sg0 = sg;
+      B.n = 1;
+    } else if (B.n == 1 && (src != B.src0 || sg != B.sg0)) {
+      B.src1 = src;
+      B.sg1 = sg;
+      B.n = 2;
+    } else if (B.n == 2 && (src != B.src1 || sg != B.sg1)) {
+      B.n = 3;
+      return B;
+    }
+    u += S->mat[m].tiles - tile;
+    tile = 0;
+    if (++sg == S->mat[m].supers) {
+      sg = 0;
+      ++m;
+    }
+  }
+  return B;
+}
+
+INL int block_index(const Blocks& B, int src, int sg) {
+  return (B.n > 1 && B.src1 == src && B.sg1 == sg) ? 1 : 0;
+}
+
+// Sum over the wave of a per-lane value, fixed butterfly order (identical on every lane).
+INL float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Bounded-wait bookkeeping shared by every polling loop: true (after raising the error word
+// and the workgroup's abort flag) once the loop has spun too long or another wave or
+// workgroup has given up.
+INL bool poll_expired(int it, uint32_t* error, int32_t* abort_lds) {
+  if (it >= kPollLimit || ((it & 63) == 63 && (lds_poll_i(abort_lds) || ld_err(error)))) {
+    set_err(error);
+    *abort_lds = 1;
+    return true;
+  }
+  return false;
+}
+
+// Polls N tagged words per lane (word i only where want[i]) until each carries its tag; the
+// loads of one sweep are all issued before any is tested, so a sweep costs one round trip.
+template <int N>
+INL bool wait_words(const tagged_t* const* p, const bool* want, const uint32_t* tag, uint32_t* out,
+                    uint32_t* error, int32_t* abort_lds) {
+  bool done[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    done[i] = !want[i];
+    out[i] = 0;
+  }
+  for (int it = 0;; ++it) {
+    tagged_t v[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = done[i] ? 0 : ld_tag(p[i]);
+    bool all = true;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if (!done[i]) {
+        if (tag_of(v[i]) == tag[i]) {
+          done[i] = true;
+          out[i] = (uint32_t)v[i];
+        } else {
+          all = false;
+        }
+      }
+    }
+    if (__builtin_amdgcn_ballot_w64(!all) == 0) return true;
+    if (poll_expired(it, error, abort_lds)) return false;
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// Stage-start duties, run by all nine waves (tid = thread index in the workgroup):
+//  1. every thread fetches up to four positions of the workgroup's (at most two) 1024-wide
+//     input blocks in one sweep of tagged loads, while the communication wave also fetches the
+//     producers' tile statistics and turns them into RMS denominators;
+//  2. after a barrier every thread rescales its positions to bf16 and stores them to the
+//     staging area; the workgroup owning the tile-0 unit of a block (of the source's record
+//     matrix) also writes that block to the caller's record. A stage without matrices (the
+//     final rescale of a decode step) splits its source's record evenly over all workgroups.
+INL void stage_inputs(PP P, EngLds& L, int s, int wg, int tid, bool comm, uint32_t epoch,
+                      uint32_t* error) {
+  SP S = &P->st[s];
+  XP X0 = &S->src[0];
+  XP X1 = &S->src[1];
+  const int par = s & 1;
+  const int nwg = P->nwg;
+  const int lane = tid & 63;
+  int u0, u1;
+  wg_range(S->units, wg, nwg, &u0, &u1);
+  const Blocks B = wg_blocks(S, u0, u1);
+  if (B.n > 2 && comm) {
+    set_err(error);
+    L.abort_flag = 1;
+  }
+  const int nb = B.n > 2 ? 0 : B.n;
+  const bool live = lds_poll_i(&L.abort_flag) == 0;
+  const bool slice = S->nmat == 0 && S->nsrc > 0 && X0->record != nullptr;
+  int kpos[4];
+  bool one[4], valid[4], staged[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int p = tid + kEngThreads * j;
+    kpos[j] = 0;
+    one[j] = false;
+    valid[j] = false;
+    staged[j] = false;
+    if (p < nb * 1024) {
+      const int b = p >> 10;
+      one[j] = (b ? B.src1 : B.src0) != 0;
+      kpos[j] = (b ? B.sg1 : B.sg0) * 1024 + (p & 1023);
+      staged[j] = true;
+      valid[j] = kpos[j] < (one[j] ? X1->k : X0->k);
+    } else if (nb == 0 && slice) {
+      const int K = X0->k;
+      const int a = (K * wg) / nwg, e = (K * (wg + 1)) / nwg;
+      kpos[j] = a + p;
+      valid[j] = kpos[j] < e;
+    }
+  }
+  // 1. one sweep of tagged loads (two words per position of a product source)
+  uint32_t w[8];
+  {
+    const tagged_t* ptr[8];
+    bool want[8];
+    uint32_t tg[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int kind = one[j] ? X1->kind : X0->kind;
+      const bool tagged = live && valid[j] && kind != kSrcDirect;
+      const int off = tagged ? kpos[j] : 0;
+      ptr[2 * j] = (one[j] ? X1->yt : X0->yt) + off;
+      ptr[2 * j + 1] = (one[j] ? X1->y2t : X0->y2t) + off;
+      want[2 * j] = tagged;
+      want[2 * j + 1] = tagged && kind == kSrcRmsProd;
+      tg[2 * j] = tg[2 * j + 1] = eng_tag(epoch, one[j] ? X1->src_stage : X0->src_stage);
+    }
+    wait_words<8>(ptr, want, tg, w, error, &L.abort_flag);
+  }
+  uint32_t direct[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int kind = one[j] ? X1->kind : X0->kind;
+    direct[j] = (valid[j] && kind == kSrcDirect) ? (one[j] ? X1->x : X0->x)[kpos[j]] : 0u;
+  }
+  if (comm) {
+    for (int j = 0; j < S->nsrc; ++j) {
+      XP X = j ? X1 : X0;
+      float d = 1.f;
+      const bool used = (nb > 0 && (B.src0 == j || (nb > 1 && B.src1 == j))) ||
+                        (nb == 0 && slice && j == 0);
+      if (live && used && X->kind != kSrcDirect) {
+        const uint32_t tag = eng_tag(epoch, X->src_stage);
+        float part = 0.f;
+        for (int base = 0; base < X->nstats; base += 64 * 8) {
+          const tagged_t* ptr[8];
+          bool want[8];
+          uint32_t tg[8], v[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int idx = base + i * 64 + lane;
+            want[i] = idx < X->nstats;
+            ptr[i] = X->stats + (want[i] ? idx : 0);
+            tg[i] = tag;
+          }
+          if (!wait_words<8>(ptr, want, tg, v, error, &L.abort_flag)) break;
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (want[i]) part += __uint_as_float(v[i]);
+        }
+        d = sqrtf(wave_sum(part) / (float)X->k + X->eps);
+      }
+      if (lane == 0) L.denom[par][j] = d;
+    }
+  }
+  __syncthreads();
+  // 2. rescale, stage, record
+  MP R0 = &S->mat[X0->rec_mat];
+  MP R1 = &S->mat[X1->rec_mat];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int kind = one[j] ? X1->kind : X0->kind;
+    uint32_t xb = direct[j];
+    if (valid[j] && kind != kSrcDirect) {
+      float h = e_bf16(w[2 * j]);
+      if (kind == kSrcRmsProd) h *= e_bf16(w[2 * j + 1]);
+      xb = e_to_bf16(h / L.denom[par][one[j] ? 1 : 0]);
+    }
+    uint16_t* rec = one[j] ? X1->record : X0->record;
+    if (staged[j]) {
+      const int p = tid + kEngThreads * j;
+      L.staging[par][p >> 10][p & 1023] = valid[j] ? e_bf16(xb) : 0.f;
+      const int owner = one[j] ? R1->unit_base + (kpos[j] >> 10) * R1->tiles
+                               : R0->unit_base + (kpos[j] >> 10) * R0->tiles;
+      if (valid[j] && rec != nullptr && owner >= u0 && owner < u1) rec[kpos[j]] = (uint16_t)xb;
+    } else if (valid[j] && live) {
+      rec[kpos[j]] = (uint16_t)xb;
+    }
+  }
+  __syncthreads();
 }
 
 // ------------------------------------------------------------------------------------------
 // compute wave V
 // ------------------------------------------------------------------------------------------
-template <int V, int B>
+template <int V, int Bk>
 INL float lookup_group(const EngLds& L, const uint32_t s4[4]) {
-  const char* lb = (const char*)&L.lut[B][V][0];
+  const char* lb = (const char*)&L.lut[Bk][V][0];
   float pa = 0.f, pb = 0.f;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
@@ -231,7 +456,7 @@ INL void issue_unit(PP P, const UnitIt& it, EngLds& L, int slot, int lane) {
 }
 
 template <int V>
-INL void compute_wave(PP P, EngLds& L, int wg, int lane) {
+INL void compute_wave(PP P, EngLds& L, int wg, int lane, uint32_t epoch, uint32_t* error) {
   const int nwg = P->nwg;
   UnitIt pf, cur;
   it_seek_stage(P, wg, pf, 0);
@@ -242,14 +467,15 @@ INL void compute_wave(PP P, EngLds& L, int wg, int lane) {
   }
   unsigned cnt = 0;
   for (int s = 0; s < P->nstages; ++s) {
-    __syncthreads();   // stage s inputs staged by the communication wave
+    stage_inputs(P, L, s, wg, V * 64 + lane, false, epoch, error);
     SP S = &P->st[s];
     int u0, u1;
     wg_range(S->units, wg, nwg, &u0, &u1);
-    if (L.abort_flag || u1 <= u0) continue;
+    if (lds_poll_i(&L.abort_flag) || u1 <= u0) continue;
     const int par = s & 1;
+    const Blocks B = wg_blocks(S, u0, u1);
     // this wave's group of every block: 32 tables of 16 signed sums, two lanes per table
-    for (int b = 0; b < L.nblk[par]; ++b) {
+    for (int b = 0; b < B.n; ++b) {
       const int c = lane >> 1, h = lane & 1;
       const float* xs = &L.staging[par][b][kGroup * V + 4 * c];
       const float x0 = xs[0], x1 = xs[1], x2 = xs[2], x3 = xs[3];
@@ -272,7 +498,7 @@ INL void compute_wave(PP P, EngLds& L, int wg, int lane) {
         uint32_t s4[4] = {rw[0], rw[1], rw[2], rw[3]};
         const uint32_t sw = L.ring_s[V][slot][lane];
         const float scale = e_f16((V & 1) ? (sw >> 16) : (sw & 0xFFFFu));
-        const int b = block_of(L, par, M->src, cur.sg);
+        const int b = block_index(B, M->src, cur.sg);
         const float sum = b ? lookup_group<V, 1>(L, s4) : lookup_group<V, 0>(L, s4);
         partial = scale * sum;
       }
@@ -280,8 +506,7 @@ INL void compute_wave(PP P, EngLds& L, int wg, int lane) {
       const int ps = cnt % kEngSlots;
       const unsigned round = cnt / kEngSlots;
       for (int it = 0; lds_poll(&L.freed[ps]) < round; ++it) {
-        if (lds_poll_i(&L.abort_flag)) break;
-        if (it > kPollLimit) {
+        if (lds_poll_i(&L.abort_flag) || it >= kPollLimit) {
           L.abort_flag = 1;
           break;
         }
@@ -297,383 +522,134 @@ INL void compute_wave(PP P, EngLds& L, int wg, int lane) {
       ++cnt;
     }
   }
+  // the ring runs ahead of the program's end (dummy records): let the last copies land
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // ------------------------------------------------------------------------------------------
 // communication wave
 // ------------------------------------------------------------------------------------------
-struct Comm {
-  PP P;
-  EngLds* L;
-  tagged_t* partial;
-  long long pstride;
-  uint32_t* error;
-  uint32_t epoch;
-  int wg, lane;
-  bool fail;
-};
 
-INL bool comm_error(Comm& C) {
-  if (C.fail) return true;
-  if (ld_err(C.error)) C.fail = true;
-  return C.fail;
-}
-INL void comm_abort(Comm& C) {
-  C.fail = true;
-  set_err(C.error);
-}
-
-// All lanes: waits until word i (i < n, n per lane, n <= N) carries `tag`; returns payloads.
-template <int N>
-INL bool comm_wait_words(Comm& C, const tagged_t* const* p, int n, uint32_t tag, uint32_t* out) {
-  bool done[N];
+// Finalises item `item` of stage S (number s): one output tile of a matrix, or the same tile of
+// a matrix and its pair partner (gate and up), from the published block partials, polled in
+// one sweep: bf16 outputs (tagged copy for consumers, plain copy for the caller) and the tile
+// statistic (sum of squares of the outputs, or the pair's sum of (own * partner)^2).
+INL void finalize_item(SP S, EngLds& L, int s, int item, int lane, uint32_t epoch,
+                       uint32_t* error) {
+  int m = 0;
+  for (; m < S->nmat; ++m) {
+    const int b = S->mat[m].item_base;
+    if (b >= 0 && item >= b && item < b + S->mat[m].tiles) break;
+  }
+  if (m == S->nmat) return;   // not produced by the host
+  MP M = &S->mat[m];
+  const int tile = item - M->item_base;
+  const int m2 = M->pair;
+  MP M2 = &S->mat[m2 < 0 ? m : m2];
+  const int s1 = M->supers, s2 = m2 < 0 ? 0 : M2->supers;
+  const uint32_t tag = eng_tag(epoch, s);
+  const tagged_t* pb = S->part + lane;
+  uint32_t v[kEngMaxFinal];
+  bool done[kEngMaxFinal];
 #pragma unroll
-  for (int i = 0; i < N; ++i) done[i] = i >= n;
+  for (int i = 0; i < kEngMaxFinal; ++i) {
+    done[i] = i >= s1 + s2;
+    v[i] = 0;
+  }
   for (int it = 0;; ++it) {
-    tagged_t v[N];
+    tagged_t t[kEngMaxFinal];
 #pragma unroll
-    for (int i = 0; i < N; ++i) v[i] = done[i] ? 0 : ld_tag(p[i]);
+    for (int i = 0; i < kEngMaxFinal; ++i) {
+      const int u = i < s1 ? M->unit_base + i * M->tiles + tile
+                           : M2->unit_base + (i - s1) * M2->tiles + tile;
+      t[i] = done[i] ? 0 : ld_tag(pb + (size_t)u * 64);
+    }
     bool all = true;
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
+    for (int i = 0; i < kEngMaxFinal; ++i) {
       if (!done[i]) {
-        if (tag_of(v[i]) == tag) {
+        if (tag_of(t[i]) == tag) {
           done[i] = true;
-          out[i] = (uint32_t)v[i];
+          v[i] = (uint32_t)t[i];
         } else {
           all = false;
         }
       }
     }
-    if (__builtin_amdgcn_uicmp(all ? 1u : 0u, 0u, 32) == 0) return true;   // every lane done
-    if (it > kPollLimit || ((it & 255) == 255 && comm_error(C))) {
-      if (!C.fail) comm_abort(C);
-      return false;
-    }
+    if (__builtin_amdgcn_ballot_w64(!all) == 0) break;
+    if (poll_expired(it, error, &L.abort_flag)) return;
     __builtin_amdgcn_s_sleep(2);
   }
-}
-
-// Sum over the wave of a per-lane value, fixed butterfly order (identical on every lane).
-INL float wave_sum(float v) {
+  float y1 = 0.f, y2 = 0.f;
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
-// sqrt(mean(h^2) + eps) of a source from the producer's tile statistics.
-INL bool comm_denominator(Comm& C, XP X, uint32_t tag, float* denom) {
-  float part = 0.f;
-  const int ns = X->nstats;
-  for (int base = 0; base < ns; base += 64 * 8) {
-    const tagged_t* p[8];
-    uint32_t val[8];
-    int n = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int j = base + i * 64 + C.lane;
-      p[i] = X->stats + (j < ns ? j : 0);
-      if (j < ns) n = i + 1;
-    }
-    if (!comm_wait_words<8>(C, p, n, tag, val)) return false;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (i < n) part += __uint_as_float(val[i]);
+  for (int i = 0; i < kEngMaxFinal; ++i) {
+    if (i < s1) y1 += __uint_as_float(v[i]);
+    else if (i < s1 + s2) y2 += __uint_as_float(v[i]);
   }
-  *denom = sqrtf(wave_sum(part) / (float)X->k + X->eps);
-  return true;
-}
-
-// bf16 bits of source elements pos[i], i < n (n per lane, n <= 8).
-INL bool comm_source_values(Comm& C, XP X, uint32_t tag, float denom, const int* pos, int n,
-                            uint32_t* xbits) {
-  if (X->kind == kSrcDirect) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) xbits[i] = i < n ? X->x[pos[i]] : 0u;
-    return true;
-  }
-  const tagged_t* p[8];
-  uint32_t a[8], b[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) p[i] = X->yt + pos[i];
-  if (!comm_wait_words<8>(C, p, n, tag, a)) return false;
-  const bool prod = X->kind == kSrcRmsProd;
-  if (prod) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = X->y2t + pos[i];
-    if (!comm_wait_words<8>(C, p, n, tag, b)) return false;
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float h = e_bf16(a[i]);
-    if (prod) h *= e_bf16(b[i]);
-    xbits[i] = e_to_bf16(h / denom);
-  }
-  return true;
-}
-
-// Stage-start duties: block list, staged inputs of the blocks, caller's copy of the sources.
-INL void comm_stage_inputs(Comm& C, int s) {
-  PP P = C.P;
-  SP S = &P->st[s];
-  EngLds& L = *C.L;
-  const int par = s & 1;
-  int u0, u1;
-  wg_range(S->units, C.wg, P->nwg, &u0, &u1);
-  // distinct (source, block) pairs of this workgroup's units, in order (at most two); every
-  // lane writes the same values
-  int nb = 0;
-  if (u1 > u0) {
-    int m = 0;
-    while (u0 >= S->mat[m].unit_base + S->mat[m].units) ++m;
-    const int c = u0 - S->mat[m].unit_base;
-    int sg = c / S->mat[m].tiles;
-    int tile = c - sg * S->mat[m].tiles;
-    for (int u = u0; u < u1;) {
-      const int src = S->mat[m].src;
-      if (nb == 0 || L.blk_src[par][nb - 1] != src || L.blk_sg[par][nb - 1] != sg) {
-        if (nb == 2) {   // the host sizes the grid so that this never happens
-          comm_abort(C);
-          break;
-        }
-        L.blk_src[par][nb] = src;
-        L.blk_sg[par][nb] = sg;
-        ++nb;
-      }
-      u += S->mat[m].tiles - tile;
-      tile = 0;
-      if (++sg == S->mat[m].supers) {
-        sg = 0;
-        ++m;
-      }
-    }
-  }
-  L.nblk[par] = nb;
-  if (C.fail) return;
-  float denom[kEngMaxSrcs] = {1.f, 1.f};
-  for (int j = 0; j < S->nsrc; ++j) {
-    XP X = &S->src[j];
-    bool needed = X->record != nullptr;
-    for (int b = 0; b < nb; ++b) needed |= L.blk_src[par][b] == j;
-    if (!needed || X->kind == kSrcDirect) continue;
-    if (!comm_denominator(C, X, eng_tag(C.epoch, X->src_stage), &denom[j])) return;
-  }
-  // staged inputs of the blocks: 1024 positions per block, 8 per lane per pass
-  for (int b = 0; b < nb; ++b) {
-    const int j = L.blk_src[par][b];
-    XP X = &S->src[j];
-    const uint32_t tag = eng_tag(C.epoch, X->src_stage);
-    const int k0 = L.blk_sg[par][b] * 1024;
-    for (int base = 0; base < 1024; base += 64 * 8) {
-      int pos[8], n = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int q = k0 + base + i * 64 + C.lane;
-        pos[i] = q < X->k ? q : 0;
-        if (q < X->k) n = i + 1;
-      }
-      uint32_t xb[8];
-      if (!comm_source_values(C, X, tag, j == 0 ? denom[0] : denom[1], pos, n, xb)) return;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) L.staging[par][b][base + i * 64 + C.lane] = i < n ? e_bf16(xb[i]) : 0.f;
-    }
-  }
-  // this workgroup's slice of each source the caller wants a copy of
-  for (int j = 0; j < S->nsrc; ++j) {
-    XP X = &S->src[j];
-    uint16_t* rec = X->record;
-    if (!rec) continue;
-    const uint32_t tag = eng_tag(C.epoch, X->src_stage);
-    const int a = (X->k * C.wg) / P->nwg;
-    const int e = (X->k * (C.wg + 1)) / P->nwg;
-    for (int base = a; base < e; base += 64 * 8) {
-      int pos[8], n = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int q = base + i * 64 + C.lane;
-        pos[i] = q < e ? q : a;
-        if (q < e) n = i + 1;
-      }
-      uint32_t xb[8];
-      if (!comm_source_values(C, X, tag, j == 0 ? denom[0] : denom[1], pos, n, xb)) return;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (i < n) rec[base + i * 64 + C.lane] = (uint16_t)xb[i];
-    }
-  }
-}
-
-// Pair statistic of tile `tile` (matrix m is the second factor of an RMS product): sum over its
-// rows of (partner * own)^2, from the two tagged finals. Non-blocking mode returns false when a
-// final is not published yet; blocking mode returns true once done or aborted.
-INL bool comm_pair_stat(Comm& C, int s, int m, int tile, bool block) {
-  MP M = &C.P->st[s].mat[m];
-  const uint32_t tag = eng_tag(C.epoch, s);
-  const int row = tile * kTileRows + C.lane;
-  const tagged_t* p[8];
-  uint32_t v[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) p[i] = (i & 1) ? M->yt + row : M->partner + row;
-  if (!block) {
-    const tagged_t g = ld_tag(p[0]), u = ld_tag(p[1]);
-    const bool ok = tag_of(g) == tag && tag_of(u) == tag;
-    if (__builtin_amdgcn_uicmp(ok ? 1u : 0u, 0u, 32) != 0) return false;
-    v[0] = (uint32_t)g;
-    v[1] = (uint32_t)u;
-  } else if (!comm_wait_words<8>(C, p, 2, tag, v)) {
-    return true;   // aborted
-  }
-  const float h = row < M->n ? e_bf16(v[0]) * e_bf16(v[1]) : 0.f;
-  const float ss = wave_sum(h * h);
-  if (C.lane == 0) st_tag(M->stat + tile, __float_as_uint(ss), tag);
-  return true;
-}
-
-INL void comm_push_pending(Comm& C, int m, int tile, int kind) {
-  EngLds& L = *C.L;
-  const int np = L.npend;   // every lane keeps the same view: all lanes write identical values
-  L.pend_m[np] = m | (kind << 16);
-  L.pend_t[np] = tile;
-  L.npend = np + 1;
-}
-
-// Finalises tile `tile` of matrix m of stage s from its published block partials: bf16 output
-// (tagged copy for consumers, plain copy for the caller) and, for kMatSumSq, the tile's sum of
-// squares. A kMatPair tile then needs its pair statistic, attempted at once or queued.
-// Non-blocking mode returns false when a block partial is still missing.
-INL bool comm_try_finalize(Comm& C, int s, int m, int tile, bool block) {
-  MP M = &C.P->st[s].mat[m];
-  const uint32_t tag = eng_tag(C.epoch, s);
-  const tagged_t* pb = C.partial + (s & 1) * C.pstride;
-  const int supers = M->supers, tiles = M->tiles, ubase = M->unit_base;
-  float sum = 0.f;
-  for (int j0 = 0; j0 < supers; j0 += 8) {
-    const tagged_t* p[8];
-    uint32_t v[8];
-    const int n = min(8, supers - j0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      p[i] = pb + (size_t)(ubase + (j0 + (i < n ? i : 0)) * tiles + tile) * 64 + C.lane;
-    if (!block) {
-      bool ok = true;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (i < n) {
-          const tagged_t t = ld_tag(p[i]);
-          ok &= tag_of(t) == tag;
-          v[i] = (uint32_t)t;
-        }
-      }
-      if (__builtin_amdgcn_uicmp(ok ? 1u : 0u, 0u, 32) != 0) return false;
-    } else if (!comm_wait_words<8>(C, p, n, tag, v)) {
-      return true;   // aborted
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (i < n) sum += __uint_as_float(v[i]);
-  }
-  const int row = tile * kTileRows + C.lane;
-  const int nrows = M->n;
-  const uint32_t yb = e_to_bf16(sum);
-  st_tag(M->yt + row, yb, tag);
-  if (M->y && row < nrows) M->y[row] = (uint16_t)yb;
+  const int row = tile * kTileRows + lane;
+  const uint32_t b1 = e_to_bf16(y1);
+  st_tag(M->yt + row, b1, tag);
+  if (M->y && row < M->n) M->y[row] = (uint16_t)b1;
   if (M->kind == kMatSumSq) {
-    const float yv = row < nrows ? e_bf16(yb) : 0.f;
+    const float yv = row < M->n ? e_bf16(b1) : 0.f;
     const float ss = wave_sum(yv * yv);
-    if (C.lane == 0) st_tag(M->stat + tile, __float_as_uint(ss), tag);
-  } else if (M->kind == kMatPair) {
-    if (!comm_pair_stat(C, s, m, tile, false)) comm_push_pending(C, m, tile, 1);
+    if (lane == 0) st_tag(M->stat + tile, __float_as_uint(ss), tag);
   }
-  return true;
-}
-
-// Retries queued work. Non-blocking: one attempt at the oldest entry. Blocking (stage end):
-// every tile finalisation first (they depend only on block partials, all published by now),
-// then every pair statistic (they depend only on finals), so no two workgroups can wait on
-// each other.
-INL void comm_retry_pending(Comm& C, int s, bool block) {
-  EngLds& L = *C.L;
-  if (!block) {
-    if (L.npend == 0 || C.fail) return;
-    const int e = L.pend_m[0], m = e & 0xFFFF, kind = e >> 16, t = L.pend_t[0];
-    const bool done = kind ? comm_pair_stat(C, s, m, t, false) : comm_try_finalize(C, s, m, t, false);
-    if (done) {   // drop the head (a finalisation may have appended a pair entry: keep it)
-      const int n = L.npend;
-      for (int i = 1; i < n; ++i) {
-        L.pend_m[i - 1] = L.pend_m[i];
-        L.pend_t[i - 1] = L.pend_t[i];
-      }
-      L.npend = n - 1;
-    }
-    return;
-  }
-  for (int pass = 0; pass < 2; ++pass) {
-    for (int i = 0; i < L.npend && !C.fail; ++i) {
-      const int e = L.pend_m[i], m = e & 0xFFFF, kind = e >> 16, t = L.pend_t[i];
-      if (kind != pass) continue;
-      if (kind) comm_pair_stat(C, s, m, t, true);
-      else comm_try_finalize(C, s, m, t, true);
+  if (m2 >= 0) {
+    const uint32_t b2 = e_to_bf16(y2);
+    st_tag(M2->yt + row, b2, tag);
+    if (M2->y && row < M2->n) M2->y[row] = (uint16_t)b2;
+    if (M2->kind == kMatPair) {
+      const float h = row < M2->n ? e_bf16(b1) * e_bf16(b2) : 0.f;
+      const float ss = wave_sum(h * h);
+      if (lane == 0) st_tag(M2->stat + tile, __float_as_uint(ss), tag);
     }
   }
-  L.npend = 0;
 }
 
-INL void comm_wave(Comm& C) {
-  PP P = C.P;
-  EngLds& L = *C.L;
+INL void comm_wave(PP P, EngLds& L, int wg, int lane, uint32_t epoch, uint32_t* error) {
   unsigned cnt = 0;
   for (int s = 0; s < P->nstages; ++s) {
-    if (!C.fail) comm_stage_inputs(C, s);
-    if (C.fail && C.lane == 0) L.abort_flag = 1;
-    __syncthreads();   // B_s: inputs of stage s are staged
+    stage_inputs(P, L, s, wg, kEngWaves * 64 + lane, true, epoch, error);
     SP S = &P->st[s];
     int u0, u1;
-    wg_range(S->units, C.wg, P->nwg, &u0, &u1);
-    if (C.fail || u1 <= u0) continue;
-    const uint32_t tag = eng_tag(C.epoch, s);
-    tagged_t* pb = C.partial + (s & 1) * C.pstride;
-    int m = 0;
-    while (u0 >= S->mat[m].unit_base + S->mat[m].units) ++m;
-    const int c0 = u0 - S->mat[m].unit_base;
-    int sg = c0 / S->mat[m].tiles;
-    int tile = c0 - sg * S->mat[m].tiles;
-    L.npend = 0;
+    wg_range(S->units, wg, P->nwg, &u0, &u1);
+    const uint32_t tag = eng_tag(epoch, s);
+    if (lds_poll_i(&L.abort_flag)) {
+      cnt += (unsigned)(u1 - u0);
+      continue;
+    }
+    // publish this workgroup's unit partials as they complete (never waits on global memory)
     for (int u = u0; u < u1; ++u) {
       const int ps = cnt % kEngSlots;
       const unsigned want = (cnt / kEngSlots + 1) * kEngWaves;
+      bool ok = true;
       for (int it = 0; lds_poll(&L.ready[ps]) < want; ++it) {
-        if (L.npend > 0) comm_retry_pending(C, s, false);
-        if (C.fail || it > kPollLimit) {
-          if (!C.fail) comm_abort(C);
+        if (lds_poll_i(&L.abort_flag) || it >= kPollLimit) {
+          ok = false;
           break;
         }
         __builtin_amdgcn_s_sleep(1);
       }
-      if (C.fail) break;
+      if (!ok) {
+        set_err(error);
+        L.abort_flag = 1;
+        break;
+      }
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       float p = 0.f;
 #pragma unroll
-      for (int v = 0; v < kEngWaves; ++v) p += L.part[ps][v][C.lane];
+      for (int v = 0; v < kEngWaves; ++v) p += L.part[ps][v][lane];
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
-      if (C.lane == 0) L.freed[ps] = cnt / kEngSlots + 1;
-      st_tag(pb + (size_t)u * 64 + C.lane, __float_as_uint(p), tag);
-      const int msupers = S->mat[m].supers, mtiles = S->mat[m].tiles;
-      if (sg == msupers - 1) {
-        // at most one finalisation per unit and one pair entry per finalisation: the queue
-        // (64) holds every entry of a workgroup's share (host-checked)
-        if (!comm_try_finalize(C, s, m, tile, false)) comm_push_pending(C, m, tile, 0);
-      }
+      if (lane == 0) L.freed[ps] = cnt / kEngSlots + 1;
+      st_tag(S->part + (size_t)u * 64 + lane, __float_as_uint(p), tag);
       ++cnt;
-      if (++tile == mtiles) {
-        tile = 0;
-        if (++sg == msupers) {
-          sg = 0;
-          ++m;
-        }
-      }
     }
-    if (!C.fail && L.npend > 0) comm_retry_pending(C, s, true);
-    if (C.fail && C.lane == 0) L.abort_flag = 1;
+    // then this workgroup's share of the stage's finalisation items
+    for (int item = wg; item < S->nitems; item += P->nwg) {
+      if (lds_poll_i(&L.abort_flag)) break;
+      finalize_item(S, L, s, item, lane, epoch, error);
+    }
   }
 }
 
@@ -688,24 +664,18 @@ __global__ __launch_bounds__(kEngThreads) void q1_engine_kernel(EngArgs A) {
     L.ready[threadIdx.x] = 0;
     L.freed[threadIdx.x] = 0;
   }
-  if (threadIdx.x == 0) {
-    L.abort_flag = 0;
-    L.npend = 0;
-  }
+  if (threadIdx.x == 0) L.abort_flag = 0;
   __syncthreads();
   switch (wave) {
-    case 0: compute_wave<0>(P, L, wg, lane); break;
-    case 1: compute_wave<1>(P, L, wg, lane); break;
-    case 2: compute_wave<2>(P, L, wg, lane); break;
-    case 3: compute_wave<3>(P, L, wg, lane); break;
-    case 4: compute_wave<4>(P, L, wg, lane); break;
-    case 5: compute_wave<5>(P, L, wg, lane); break;
-    case 6: compute_wave<6>(P, L, wg, lane); break;
-    case 7: compute_wave<7>(P, L, wg, lane); break;
-    default: {
-      Comm C{P, &L, A.partial, A.partial_stride, A.error, A.epoch, wg, lane, false};
-      comm_wave(C);
-    } break;
+    case 0: compute_wave<0>(P, L, wg, lane, A.epoch, A.error); break;
+    case 1: compute_wave<1>(P, L, wg, lane, A.epoch, A.error); break;
+    case 2: compute_wave<2>(P, L, wg, lane, A.epoch, A.error); break;
+    case 3: compute_wave<3>(P, L, wg, lane, A.epoch, A.error); break;
+    case 4: compute_wave<4>(P, L, wg, lane, A.epoch, A.error); break;
+    case 5: compute_wave<5>(P, L, wg, lane, A.epoch, A.error); break;
+    case 6: compute_wave<6>(P, L, wg, lane, A.epoch, A.error); break;
+    case 7: compute_wave<7>(P, L, wg, lane, A.epoch, A.error); break;
+    default: comm_wave(P, L, wg, lane, A.epoch, A.error); break;
   }
 }
 
@@ -721,7 +691,7 @@ constexpr int kProgSlots = 16;
 struct EngDevice {
   int nwg = 0;
   uint32_t epoch = 0;
-  void* ws = nullptr;   // [error word | program slots | partials x2 | tagged outputs + statistics]
+  void* ws = nullptr;   // [error word | program slots | per-stage partials, tagged outputs, stats]
   size_t ws_bytes = 0;
   std::vector<char> slot_prog[kProgSlots];   // host copy of what each device program slot holds
   int next_slot = 0;
@@ -732,14 +702,6 @@ static std::mutex g_eng_mutex;
 static constexpr size_t kProgBytes = sizeof(EngProgram) + (kEngMaxStages) * sizeof(EngStage);
 static constexpr size_t kErrBytes = 256;
 static constexpr size_t kHeadBytes = kErrBytes + kProgSlots * kProgBytes;
-
-// Bytes of tagged outputs and statistics a program layout needs (see build_*).
-struct EngLayout {
-  size_t tagged_elems = 0;   // tagged_t words for outputs and statistics
-  size_t max_units = 0;
-};
-
-static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 static lbq_status eng_device(int* dev_out, EngDevice** out) {
   int dev = 0;
@@ -783,8 +745,7 @@ static lbq_status eng_workspace(EngDevice& E, size_t need, hipStream_t stream) {
 // Runs a program laid out in `prog` (host memory; pointers into the workspace were computed
 // against E.ws). Programs are kept in a small ring of device slots and uploaded only when no
 // slot already holds the same bytes; uploads are stream-ordered, never synchronous.
-static lbq_status eng_launch(EngDevice& E, std::vector<char>& prog, size_t max_units,
-                             hipStream_t stream) {
+static lbq_status eng_launch(EngDevice& E, std::vector<char>& prog, hipStream_t stream) {
   char* base = (char*)E.ws;
   int slot = -1;
   for (int i = 0; i < kProgSlots; ++i)
@@ -803,8 +764,6 @@ static lbq_status eng_launch(EngDevice& E, std::vector<char>& prog, size_t max_u
   EngArgs a;
   memset(&a, 0, sizeof(a));
   a.prog = (const EngProgram*)(base + kErrBytes + (size_t)slot * kProgBytes);
-  a.partial = (tagged_t*)(base + kHeadBytes);
-  a.partial_stride = (long long)max_units * 64;
   a.error = (uint32_t*)base;
   if (++E.epoch >= (1u << 23)) E.epoch = 1;
   a.epoch = E.epoch;
@@ -815,11 +774,17 @@ static lbq_status eng_launch(EngDevice& E, std::vector<char>& prog, size_t max_u
   return LBQ_OK;
 }
 
-// Fills the geometry fields of a stage matrix and appends its tagged outputs.
-static bool eng_mat(EngMat& M, const void* w, int n, int k, uint16_t* y, int src, int kind,
-                    int unit_base, tagged_t** cursor) {
+// Workspace words (tagged_t) a matrix of a stage needs: outputs plus per-tile statistics.
+static size_t eng_mat_words(const Geometry& g, bool stat) {
+  return (size_t)g.np + (stat ? (size_t)g.tiles : 0);
+}
+
+// Fills the geometry fields of a stage matrix and carves its tagged outputs from the workspace.
+static bool eng_mat(EngStage& S, int idx, const void* w, int n, int k, uint16_t* y, int src,
+                    int kind, tagged_t** cursor) {
   Geometry g;
   if (!make_geometry(n, k, kQ1GroupBlocks, &g)) return false;
+  EngMat& M = S.mat[idx];
   memset(&M, 0, sizeof(M));
   M.w = (const uint8_t*)w;
   M.y = y;
@@ -831,27 +796,53 @@ static bool eng_mat(EngMat& M, const void* w, int n, int k, uint16_t* y, int src
   M.tile_bytes = g.tile_bytes;
   M.src = src;
   M.kind = kind;
-  M.unit_base = unit_base;
+  M.unit_base = S.units;
   M.units = M.tiles * M.supers;
+  M.item_base = S.nitems;
+  M.pair = -1;
   M.yt = *cursor;
   *cursor += g.np;
   if (kind != kMatPlain) {
     M.stat = *cursor;
     *cursor += g.tiles;
   }
+  S.units += M.units;
+  S.nitems += M.tiles;
+  S.nmat = idx + 1;
   return true;
 }
 
+// Makes matrix b (a kMatPair matrix whose statistic pairs it with matrix a, same shape) part of
+// a's finalisation items.
+static void eng_pair(EngStage& S, int a, int b) {
+  S.mat[a].pair = b;
+  S.nitems -= S.mat[b].tiles;
+  S.mat[b].item_base = -1;
+}
+
+// Carves a stage's unit partials from the workspace.
+static void eng_part(EngStage& S, tagged_t** cursor) {
+  S.part = *cursor;
+  *cursor += (size_t)S.units * 64;
+}
+
 static bool eng_fits(const EngProgram* P) {
-  // every workgroup's share of a stage must touch at most two (source, block) pairs: guaranteed
-  // when each share is no longer than the shortest column of tiles
   for (int s = 0; s < P->nstages; ++s) {
     const EngStage& S = P->st[s];
+    // every workgroup's share of a stage must touch at most two (source, block) pairs:
+    // guaranteed when each share is no longer than the shortest column of tiles
     int min_tiles = 1 << 30;
-    for (int m = 0; m < S.nmat; ++m) min_tiles = min_tiles < S.mat[m].tiles ? min_tiles : S.mat[m].tiles;
+    for (int m = 0; m < S.nmat; ++m) {
+      const EngMat& M = S.mat[m];
+      min_tiles = min_tiles < M.tiles ? min_tiles : M.tiles;
+      const int fin = M.supers + (M.pair >= 0 ? S.mat[M.pair].supers : 0);
+      if (M.item_base >= 0 && fin > kEngMaxFinal) return false;
+    }
     const int share = (S.units + P->nwg - 1) / P->nwg;
     if (S.nmat && share > min_tiles) return false;
-    if (2 * share > 64) return false;   // pending-queue capacity of the communication wave
+    for (int j = 0; j < S.nsrc; ++j)
+      if ((long long)S.src[j].k * P->nwg >= (1LL << 31)) return false;
+    if ((long long)S.units * P->nwg >= (1LL << 31)) return false;
   }
   return true;
 }
@@ -872,8 +863,7 @@ lbq_status lbq_engine_gemv_q1(const void* d_w, int32_t n, int32_t k, const uint1
   Geometry g;
   if (!make_geometry(n, k, kQ1GroupBlocks, &g)) return LBQ_E_SHAPE;
   const size_t units = (size_t)g.tiles * g.supers;
-  const size_t need = kHeadBytes + 2 * units * 64 * sizeof(tagged_t) +
-                      align_up((size_t)g.np, 64) * sizeof(tagged_t) + 4096;
+  const size_t need = kHeadBytes + (units * 64 + eng_mat_words(g, false)) * sizeof(tagged_t) + 4096;
   st = eng_workspace(*E, need < ((size_t)32 << 20) ? ((size_t)32 << 20) : need, stream);
   if (st != LBQ_OK) return st;
   std::vector<char> prog(sizeof(EngProgram), 0);
@@ -881,19 +871,21 @@ lbq_status lbq_engine_gemv_q1(const void* d_w, int32_t n, int32_t k, const uint1
   P->nstages = 1;
   P->nwg = E->nwg;
   EngStage& S = P->st[0];
-  tagged_t* cursor = (tagged_t*)((char*)E->ws + kHeadBytes) + 2 * units * 64;
-  if (!eng_mat(S.mat[0], d_w, n, k, d_y, 0, kMatPlain, 0, &cursor)) return LBQ_E_SHAPE;
-  S.nmat = 1;
+  tagged_t* cursor = (tagged_t*)((char*)E->ws + kHeadBytes);
+  if (!eng_mat(S, 0, d_w, n, k, d_y, 0, kMatPlain, &cursor)) return LBQ_E_SHAPE;
+  eng_part(S, &cursor);
   S.nsrc = 1;
-  S.units = (int)units;
   S.src[0].kind = kSrcDirect;
   S.src[0].x = d_x;
   S.src[0].k = k;
+  S.src[0].rec_mat = 0;
   if (!eng_fits(P)) return LBQ_E_UNSUPPORTED;
-  return eng_launch(*E, prog, units, stream);
+  return eng_launch(*E, prog, stream);
 }
 
-// Whole decode step (batch 1) through the engine.
+// Whole decode step (batch 1) through the engine: per layer a stage for q, k, v, gate, up (input
+// x = rescale of the previous down output) and a stage for o and down (inputs rescale(q) and
+// rescale(gate * up)), then a final stage that only rescales the last down output.
 lbq_status lbq_engine_decode_q1(const lbq_q1_layer* layers, int32_t L, int32_t hidden, int32_t kv,
                                 int32_t ffn, const uint16_t* d_x0, uint16_t* d_act, float eps,
                                 hipStream_t stream) {
@@ -908,20 +900,19 @@ lbq_status lbq_engine_decode_q1(const lbq_q1_layer* layers, int32_t L, int32_t h
   if (!make_geometry(hidden, hidden, 1, &gq) || !make_geometry(kv, hidden, 1, &gk) ||
       !make_geometry(ffn, hidden, 1, &gf) || !make_geometry(hidden, ffn, 1, &gd))
     return LBQ_E_SHAPE;
-  const size_t units_a = (size_t)(gq.tiles + 2 * gk.tiles + 2 * gf.tiles) * gq.supers;
-  const size_t units_b = (size_t)gq.tiles * gq.supers + (size_t)gd.tiles * gd.supers;
-  const size_t max_units = units_a > units_b ? units_a : units_b;
-  const size_t per_layer = (size_t)(3 * gq.np + 2 * gk.np + 2 * gf.np + gd.np) +
-                           (size_t)(gq.tiles + gf.tiles + gd.tiles) + 64;
-  const size_t need = kHeadBytes + 2 * max_units * 64 * sizeof(tagged_t) +
-                      per_layer * L * sizeof(tagged_t) + 4096;
+  const size_t units = (size_t)(gq.tiles + 2 * gk.tiles + 2 * gf.tiles) * gq.supers +
+                       (size_t)gq.tiles * gq.supers + (size_t)gd.tiles * gd.supers;
+  const size_t per_layer = units * 64 + eng_mat_words(gq, true) + 2 * eng_mat_words(gk, false) +
+                           eng_mat_words(gf, false) + eng_mat_words(gf, true) +
+                           eng_mat_words(gq, false) + eng_mat_words(gd, true);
+  const size_t need = kHeadBytes + per_layer * L * sizeof(tagged_t) + 4096;
   st = eng_workspace(*E, need, stream);
   if (st != LBQ_OK) return st;
   std::vector<char> prog(sizeof(EngProgram) + (size_t)(nst - 1) * sizeof(EngStage), 0);
   EngProgram* P = (EngProgram*)prog.data();
   P->nstages = nst;
   P->nwg = E->nwg;
-  tagged_t* cursor = (tagged_t*)((char*)E->ws + kHeadBytes) + 2 * max_units * 64;
+  tagged_t* cursor = (tagged_t*)((char*)E->ws + kHeadBytes);
   auto at = [&](int layer, int slot) {
     return d_act + lbq_decode_act_offset(layer, slot, L, hidden, kv, ffn, 1);
   };
@@ -929,25 +920,19 @@ lbq_status lbq_engine_decode_q1(const lbq_q1_layer* layers, int32_t L, int32_t h
   for (int l = 0; l < L; ++l) {
     EngStage& A = P->st[2 * l];
     EngStage& Bs = P->st[2 * l + 1];
-    int base = 0;
-    bool ok = eng_mat(A.mat[0], layers[l].q, hidden, hidden, at(l, LBQ_ACT_Q), 0, kMatSumSq, base, &cursor);
-    base += A.mat[0].units;
-    ok &= eng_mat(A.mat[1], layers[l].k, kv, hidden, at(l, LBQ_ACT_K), 0, kMatPlain, base, &cursor);
-    base += A.mat[1].units;
-    ok &= eng_mat(A.mat[2], layers[l].v, kv, hidden, at(l, LBQ_ACT_V), 0, kMatPlain, base, &cursor);
-    base += A.mat[2].units;
-    ok &= eng_mat(A.mat[3], layers[l].gate, ffn, hidden, at(l, LBQ_ACT_GATE), 0, kMatPlain, base, &cursor);
-    base += A.mat[3].units;
-    ok &= eng_mat(A.mat[4], layers[l].up, ffn, hidden, at(l, LBQ_ACT_UP), 0, kMatPair, base, &cursor);
-    base += A.mat[4].units;
+    bool ok = eng_mat(A, 0, layers[l].q, hidden, hidden, at(l, LBQ_ACT_Q), 0, kMatSumSq, &cursor);
+    ok = ok && eng_mat(A, 1, layers[l].k, kv, hidden, at(l, LBQ_ACT_K), 0, kMatPlain, &cursor);
+    ok = ok && eng_mat(A, 2, layers[l].v, kv, hidden, at(l, LBQ_ACT_V), 0, kMatPlain, &cursor);
+    ok = ok && eng_mat(A, 3, layers[l].gate, ffn, hidden, at(l, LBQ_ACT_GATE), 0, kMatPlain, &cursor);
+    ok = ok && eng_mat(A, 4, layers[l].up, ffn, hidden, at(l, LBQ_ACT_UP), 0, kMatPair, &cursor);
     if (!ok) return LBQ_E_SHAPE;
-    A.mat[4].partner = A.mat[3].yt;
-    A.nmat = 5;
-    A.units = base;
+    eng_pair(A, 3, 4);
+    eng_part(A, &cursor);
     A.nsrc = 1;
     EngSrc& xs = A.src[0];
     xs.k = hidden;
     xs.record = at(l, LBQ_ACT_X);
+    xs.rec_mat = 0;
     if (l == 0) {
       xs.kind = kSrcDirect;
       xs.x = d_x0;
@@ -959,14 +944,10 @@ lbq_status lbq_engine_decode_q1(const lbq_q1_layer* layers, int32_t L, int32_t h
       xs.src_stage = 2 * l - 1;
       xs.eps = eps;
     }
-    base = 0;
-    ok = eng_mat(Bs.mat[0], layers[l].o, hidden, hidden, at(l, LBQ_ACT_O), 0, kMatPlain, base, &cursor);
-    base += Bs.mat[0].units;
-    ok &= eng_mat(Bs.mat[1], layers[l].down, hidden, ffn, at(l, LBQ_ACT_DOWN), 1, kMatSumSq, base, &cursor);
-    base += Bs.mat[1].units;
+    ok = eng_mat(Bs, 0, layers[l].o, hidden, hidden, at(l, LBQ_ACT_O), 0, kMatPlain, &cursor);
+    ok = ok && eng_mat(Bs, 1, layers[l].down, hidden, ffn, at(l, LBQ_ACT_DOWN), 1, kMatSumSq, &cursor);
     if (!ok) return LBQ_E_SHAPE;
-    Bs.nmat = 2;
-    Bs.units = base;
+    eng_part(Bs, &cursor);
     Bs.nsrc = 2;
     EngSrc& xo = Bs.src[0];
     xo.kind = kSrcRms;
@@ -977,6 +958,7 @@ lbq_status lbq_engine_decode_q1(const lbq_q1_layer* layers, int32_t L, int32_t h
     xo.src_stage = 2 * l;
     xo.eps = eps;
     xo.record = at(l, LBQ_ACT_XO);
+    xo.rec_mat = 0;
     EngSrc& xd = Bs.src[1];
     xd.kind = kSrcRmsProd;
     xd.k = ffn;
@@ -987,11 +969,13 @@ lbq_status lbq_engine_decode_q1(const lbq_q1_layer* layers, int32_t L, int32_t h
     xd.src_stage = 2 * l;
     xd.eps = eps;
     xd.record = at(l, LBQ_ACT_XD);
+    xd.rec_mat = 1;
     prev_down = &Bs.mat[1];
   }
   EngStage& F = P->st[2 * L];
   F.nmat = 0;
   F.units = 0;
+  F.nitems = 0;
   F.nsrc = 1;
   F.src[0].kind = kSrcRms;
   F.src[0].k = hidden;
@@ -1001,8 +985,9 @@ lbq_status lbq_engine_decode_q1(const lbq_q1_layer* layers, int32_t L, int32_t h
   F.src[0].src_stage = 2 * L - 1;
   F.src[0].eps = eps;
   F.src[0].record = d_act + lbq_decode_act_offset(L, LBQ_ACT_NSLOTS, L, hidden, kv, ffn, 1);
+  if ((size_t)((char*)cursor - (char*)E->ws) > E->ws_bytes) return LBQ_E_NOMEM;   // sizing bug guard
   if (!eng_fits(P)) return LBQ_E_UNSUPPORTED;
-  return eng_launch(*E, prog, max_units, stream);
+  return eng_launch(*E, prog, stream);
 }
 
 // Synchronises the stream and reports (then clears) an engine time-out on the current device.
