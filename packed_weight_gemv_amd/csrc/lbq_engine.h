@@ -2,10 +2,13 @@
 //
 // A program is a list of stages. A stage multiplies up to kEngMaxMats Q1_0_g128 matrices with
 // up to kEngMaxSrcs bf16 input vectors (batch 1); the outputs of a stage may feed the inputs of
-// later stages through an RMS rescale. One cooperative launch runs the whole program: every
-// workgroup owns a contiguous, equal share of each stage's work units (64 rows x one block of
-// eight 128-weight groups), and data passes between workgroups as (value, tag) pairs that the
-// reader polls for, so no grid-wide barrier or cache flush is ever needed.
+// later stages through an RMS rescale. One cooperative launch runs the whole program. Streaming
+// workgroups each own an equal, contiguous share of every part of every stage's work units
+// (64 rows x one block of eight 128-weight groups) and publish one partial sum per unit;
+// finalising workgroups (no weight traffic, so their memory round trips stay short) sum the
+// partials of each output tile and publish the outputs and their statistics. Data passes
+// between workgroups as (value, tag) pairs that the reader polls for, so no grid-wide barrier
+// or cache flush is ever needed.
 #pragma once
 
 #include <stdint.h>
@@ -22,6 +25,7 @@ constexpr int kEngRing = 8;                         // weight records in flight 
 constexpr int kEngSlots = 8;                        // partial hand-off slots (compute -> comm)
 constexpr int kEngMaxStages = 255;
 constexpr int kEngMaxFinal = 24;                    // block partials summed by one finalisation
+constexpr int kEngMaxBlocks = 4;                    // input blocks one workgroup stages per stage
 
 enum EngSrcKind : int32_t { kSrcDirect = 0, kSrcRms = 1, kSrcRmsProd = 2 };
 enum EngMatKind : int32_t { kMatPlain = 0, kMatSumSq = 1, kMatPair = 2 };
@@ -57,11 +61,14 @@ struct EngStage {
   EngSrc src[kEngMaxSrcs];
   tagged_t* part;                      // tagged unit partials [units * 64], one slot per unit
   int32_t nmat, nsrc, units, nitems;   // nitems: tiles to finalise (a pair counts once)
+  int32_t part0;                       // units of part 0 (the leading matrices); rest = part 1
+  int32_t drain;                       // publish this stage's last partial before prefetching on
+  int32_t pad0, pad1;
 };
 
 struct EngProgram {
-  int32_t nstages, nwg, pad0, pad1;
-  EngStage st[1];   // nstages entries
+  int32_t nstages, nwg, nstream, pad0;   // workgroups [0, nstream) stream, the rest finalise
+  EngStage st[1];                        // nstages entries
 };
 
 struct EngArgs {

@@ -24,6 +24,7 @@
 //    flush. Every wait is bounded: on a time-out the error word is set and every wave runs to
 //    the end without further work.
 #include <hip/hip_runtime.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -36,8 +37,6 @@ using namespace lbq;
 
 namespace {
 
-#define LBQ_STR2(x) #x
-#define LBQ_STR(x) LBQ_STR2(x)
 #define INL __device__ __forceinline__
 #define AS_CONST __attribute__((address_space(4)))
 #define AS_GLOBAL __attribute__((address_space(1)))
@@ -85,35 +84,62 @@ INL uint32_t tag_of(tagged_t v) { return (uint32_t)(v >> 32); }
 INL uint32_t ld_err(uint32_t* p) {
   return __hip_atomic_load((AS_GLOBAL uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Program fields pinned to scalar registers. Without this the compiler may turn a per-lane
+// choice between two sources' fields into a per-lane (vector memory) load of the field.
+INL int rfl(int v) { return __builtin_amdgcn_readfirstlane(v); }
+template <typename T>
+INL T* rfl(T* p) {
+  const unsigned long long v = (unsigned long long)p;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return (T*)(((unsigned long long)hi << 32) | lo);
+}
+struct SrcFields {
+  const tagged_t* yt;
+  const tagged_t* y2t;
+  const uint16_t* x;
+  int kind, k, src_stage;
+};
+INL SrcFields src_fields(XP X) {
+  SrcFields f;
+  f.yt = rfl(X->yt);
+  f.y2t = rfl(X->y2t);
+  f.x = rfl(X->x);
+  f.kind = rfl(X->kind);
+  f.k = rfl(X->k);
+  f.src_stage = rfl(X->src_stage);
+  return f;
+}
+
+// Plain global accesses through pointers held in the program: casting to the global address
+// space keeps them off FLAT instructions, which the compiler must assume may touch LDS (and
+// would then make every later LDS read wait for all outstanding memory operations).
+INL uint32_t g_ld16(const uint16_t* p) { return *(const AS_GLOBAL uint16_t*)p; }
+INL void g_st16(uint16_t* p, uint32_t v) { *(AS_GLOBAL uint16_t*)p = (uint16_t)v; }
 INL void set_err(uint32_t* p) {
   __hip_atomic_store((AS_GLOBAL uint32_t*)p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// LDS-direct loads issued from asm so the compiler does not guard every later LDS read with a
-// full vmcnt wait; the ring waits are explicit. No VGPR is written; m0 is restored.
-INL void dma16(const void* g, uint32_t lds) {
+// LDS-direct loads of one ring slot (a sign record and a scale word per lane), issued from asm
+// so the compiler does not guard every later LDS read with a full vmcnt wait; the ring waits
+// are explicit. Scalar base + per-lane 32-bit offset; no VGPR is written; m0 is restored.
+// Weights are read once per launch: the copies are nontemporal, so they neither evict the
+// small, hot exchange data (unit partials, outputs, statistics) from the caches nor wait behind
+// it.
+INL void dma_slot(const void* base, uint32_t voff_w, uint32_t voff_s, uint32_t lds_w,
+                  uint32_t lds_s) {
   uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %3, %5 nt\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dword %4, %5 nt\n\t"
+      "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(lds), "v"(g)
+      : "s"(lds_w), "s"(lds_s), "v"(voff_w), "v"(voff_s), "s"(base)
       : "memory");
 }
-INL void dma4(const void* g, uint32_t lds) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(g)
-      : "memory");
-}
-// Every ring slot is filled by exactly two vector-memory instructions issued in order, so the
-// oldest slot has landed once at most 2*(kRing-1) are still outstanding (loads complete in
-// order; any other outstanding load only makes this wait longer, never shorter).
-#define LBQ_RING_WAIT 14
-static_assert(LBQ_RING_WAIT == 2 * (kEngRing - 1), "ring wait count must match the ring depth");
-INL void wait_ring() { asm volatile("s_waitcnt vmcnt(" LBQ_STR(LBQ_RING_WAIT) ")" ::: "memory"); }
-
 // LDS words polled by one wave and written by another: workgroup-scope atomic loads keep them
 // on the LDS path (a volatile cast would go through a generic pointer and the vector memory
 // counters).
@@ -128,113 +154,185 @@ INL uint32_t lds_addr(T* p) {
   return (uint32_t)(uintptr_t)p;
 }
 
+// The lookup tables come first: every table entry's LDS address then fits the 16-bit
+// immediate offset of ds_read, so a lookup's address is the extracted field alone.
 struct __attribute__((aligned(16))) EngLds {
+  float lut[kEngWaves][32 * 16];               // [group][chunk*16 + entry] of the current block
   uint32_t ring_w[kEngWaves][kRing][64 * 4];   // sign records
   uint32_t ring_s[kEngWaves][kRing][64];       // scale words
-  float lut[2][kEngWaves][32 * 16];            // [block][group][chunk*16 + entry]
-  float staging[2][2][1024];                   // [stage parity][block][position]
-  float part[kEngSlots][kEngWaves][64];        // compute -> comm hand-off
-  uint32_t ready[kEngSlots];
-  uint32_t freed[kEngSlots];
-  float denom[2][kEngMaxSrcs];
+  float staging[kEngMaxBlocks][1024];          // the stage's input blocks (exact bf16 values)
+  // compute -> comm hand-off: per lane (partial bits | (round + 1) << 32), one 64-bit store
+  unsigned long long part[kEngSlots][kEngWaves][64];
+  uint32_t freed[kEngSlots];                   // rounds of each slot the comm wave has consumed
+  float denom[kEngMaxSrcs];
+  int32_t published;                           // last stage whose partials were all issued
   int32_t abort_flag;
 };
 
-// The workgroup's share of a stage: units [u0, u1) (unit counts stay far below 2^21).
-INL void wg_range(int units, int wg, int nwg, int* u0, int* u1) {
-  *u0 = (units * wg) / nwg;
-  *u1 = (units * (wg + 1)) / nwg;
-}
-
-// Iterator over the workgroup's units of all stages, in program order.
-struct UnitIt {
-  int s, u, uend, m, sg, tile;
-  bool valid;
+// A streaming workgroup's units of a stage: range [a0, b0) of part 0, then [a1, b1) of part 1.
+struct Share {
+  int a0, b0, a1, b1;
 };
+INL Share stage_share(SP S, int w, int n) {
+  Share r;
+  const int p0 = S->part0, p1 = S->units - S->part0;
+  r.a0 = (p0 * w) / n;
+  r.b0 = (p0 * (w + 1)) / n;
+  r.a1 = p0 + (p1 * w) / n;
+  r.b1 = p0 + (p1 * (w + 1)) / n;
+  return r;
+}
+INL int share_units(const Share& r) { return (r.b0 - r.a0) + (r.b1 - r.a1); }
+INL bool share_has(const Share& r, int u) { return (u >= r.a0 && u < r.b0) || (u >= r.a1 && u < r.b1); }
 
-INL void it_seek_stage(PP P, int wg, UnitIt& it, int s) {
-  for (; s < P->nstages; ++s) {
-    SP S = &P->st[s];
-    int u0, u1;
-    wg_range(S->units, wg, P->nwg, &u0, &u1);
-    if (u1 > u0) {
-      it.s = s;
-      it.u = u0;
-      it.uend = u1;
-      int m = 0;
-      while (u0 >= S->mat[m].unit_base + S->mat[m].units) ++m;
-      const int c = u0 - S->mat[m].unit_base;
-      it.m = m;
-      it.sg = c / S->mat[m].tiles;
-      it.tile = c - it.sg * S->mat[m].tiles;
-      it.valid = true;
-      return;
-    }
-  }
-  it.valid = false;
-  it.s = P->nstages;
+// (matrix, super-group, tile) of stage unit u; units are ordered matrix, super-group, tile.
+struct UnitPos {
+  int m, sg, tile;
+};
+INL UnitPos unit_pos(SP S, int u) {
+  int m = 0;
+  while (u >= S->mat[m].unit_base + S->mat[m].units) ++m;
+  UnitPos r;
+  r.m = m;
+  const int k = u - S->mat[m].unit_base;
+  r.sg = k / S->mat[m].tiles;
+  r.tile = k - r.sg * S->mat[m].tiles;
+  return r;
 }
 
-INL void it_next(PP P, int wg, UnitIt& it) {
-  if (!it.valid) return;
-  ++it.u;
-  if (it.u >= it.uend) {
-    it_seek_stage(P, wg, it, it.s + 1);
-    return;
-  }
-  MP M = &P->st[it.s].mat[it.m];
-  if (++it.tile == M->tiles) {
-    it.tile = 0;
-    if (++it.sg == M->supers) {
-      it.sg = 0;
-      ++it.m;
-    }
-  }
-}
-
-// Distinct (source, block) pairs of the workgroup's share of stage S, in unit order. The host
-// only builds programs whose shares touch at most two; n == 3 flags a violation. Scalar work,
-// repeated by every wave rather than shared through LDS.
+// Distinct input blocks ((source, super-group) keys) of a share, in unit order. The host only
+// builds programs whose shares need at most kEngMaxBlocks; n > kEngMaxBlocks flags a violation.
+// Scalar work, repeated by every wave rather than shared through LDS.
 struct Blocks {
-  int n;
-  int src0, sg0, src1, sg1;
+  int n, k0, k1, k2, k3;
 };
-INL Blocks wg_blocks(SP S, int u0, int u1) {
+INL int blk_key(int src, int sg) { return (src << 16) | sg; }
+INL int blk_get(const Blocks& B, int i) { return i == 0 ? B.k0 : i == 1 ? B.k1 : i == 2 ? B.k2 : B.k3; }
+INL int blk_find(const Blocks& B, int key) {
+  return key == B.k0 ? 0 : key == B.k1 ? 1 : key == B.k2 ? 2 : 3;
+}
+INL void blk_add(Blocks& B, int key) {
+  if ((B.n > 0 && key == B.k0) || (B.n > 1 && key == B.k1) || (B.n > 2 && key == B.k2) ||
+      (B.n > 3 && key == B.k3))
+    return;
+  if (B.n == 0) B.k0 = key;
+  else if (B.n == 1) B.k1 = key;
+  else if (B.n == 2) B.k2 = key;
+  else if (B.n == 3) B.k3 = key;
+  ++B.n;
+}
+INL void blk_range(SP S, Blocks& B, int a, int b) {
+  for (int u = a; u < b;) {
+    const UnitPos q = unit_pos(S, u);
+    MP M = &S->mat[q.m];
+    blk_add(B, blk_key(M->src, q.sg));
+    u += M->tiles - q.tile;
+  }
+}
+INL Blocks stage_blocks(SP S, const Share& r) {
   Blocks B;
   B.n = 0;
-  B.src0 = B.src1 = B.sg0 = B.sg1 = 0;
-  if (u1 <= u0) return B;
-  int m = 0;
-  while (u0 >= S->mat[m].unit_base + S->mat[m].units) ++m;
-  const int c = u0 - S->mat[m].unit_base;
-  int sg = c / S->mat[m].tiles;
-  int tile = c - sg * S->mat[m].tiles;
-  for (int u = u0; u < u1;) {
-    const int src = S->mat[m].src;
-    if (B.n == 0) {
-      B.src0 = src;
-      B.sg0 = sg;
-      B.n = 1;
-    } else if (B.n == 1 && (src != B.src0 || sg != B.sg0)) {
-      B.src1 = src;
-      B.sg1 = sg;
-      B.n = 2;
-    } else if (B.n == 2 && (src != B.src1 || sg != B.sg1)) {
-      B.n = 3;
-      return B;
-    }
-    u += S->mat[m].tiles - tile;
-    tile = 0;
-    if (++sg == S->mat[m].supers) {
-      sg = 0;
-      ++m;
-    }
-  }
+  B.k0 = B.k1 = B.k2 = B.k3 = -1;
+  blk_range(S, B, r.a0, r.b0);
+  blk_range(S, B, r.a1, r.b1);
   return B;
 }
 
-INL int block_index(const Blocks& B, int src, int sg) {
-  return (B.n > 1 && B.src1 == src && B.sg1 == sg) ? 1 : 0;
+// Per-wave cursor over the streaming workgroup's units of all stages, in program order, in
+// scalar registers. A segment is a run of consecutive tiles of one (matrix, super-group)
+// column; its units lie tile_bytes apart, so stepping inside a segment is one 64-bit add.
+struct Cursor {
+  int s;              // stage (nstages once exhausted)
+  int left;           // units left in the current segment, this one included
+  int u;              // stage unit of the current unit
+  int rend;           // end of the current range
+  int na, nb;         // the part-1 range still to come ([na, nb), empty once entered)
+  Blocks B;           // the stage's block list (compute cursor only)
+  int b;              // block index of the current segment (compute cursor only)
+  const uint8_t* p;   // super-group record of the current unit
+  uint32_t step;      // tile_bytes of the segment's matrix
+  bool ok;            // this wave's group exists in the segment's super-group
+};
+
+template <int V, bool Blk>
+INL void cur_segment(SP S, Cursor& c) {
+  const UnitPos q = unit_pos(S, c.u);
+  MP M = &S->mat[q.m];
+  c.left = min(M->tiles - q.tile, c.rend - c.u);
+  c.step = (uint32_t)M->tile_bytes;
+  c.p = M->w + (size_t)q.tile * (size_t)c.step + (size_t)q.sg * (kBlock * (1 + kSuper));
+  c.ok = q.sg * kSuper + V < M->groups;
+  if (Blk) c.b = blk_find(c.B, blk_key(M->src, q.sg));
+}
+
+template <int V, bool Blk>
+INL void cur_stage(PP P, Cursor& c, int w, int s) {
+  for (; s < P->nstages; ++s) {
+    SP S = &P->st[s];
+    const Share r = stage_share(S, w, P->nstream);
+    if (share_units(r) == 0) continue;
+    c.s = s;
+    if (Blk) c.B = stage_blocks(S, r);
+    if (r.b0 > r.a0) {
+      c.u = r.a0;
+      c.rend = r.b0;
+      c.na = r.a1;
+      c.nb = r.b1;
+    } else {
+      c.u = r.a1;
+      c.rend = r.b1;
+      c.na = c.nb = 0;
+    }
+    cur_segment<V, Blk>(S, c);
+    return;
+  }
+  c.s = P->nstages;
+  c.left = 0;
+  c.u = c.rend = c.na = c.nb = 0;
+  c.ok = false;
+  c.b = 0;
+  c.p = nullptr;
+  c.step = 0;
+}
+
+template <int V, bool Blk>
+INL void cur_next(PP P, Cursor& c, int w) {
+  if (c.left > 1) {
+    --c.left;
+    ++c.u;
+    c.p += c.step;
+  } else if (c.u + 1 < c.rend) {
+    ++c.u;
+    cur_segment<V, Blk>(&P->st[c.s], c);
+  } else if (c.nb > c.na) {
+    c.u = c.na;
+    c.rend = c.nb;
+    c.na = c.nb = 0;
+    cur_segment<V, Blk>(&P->st[c.s], c);
+  } else if (c.s < P->nstages) {
+    cur_stage<V, Blk>(P, c, w, c.s + 1);
+  }
+}
+
+// Pulls a stage descriptor into the scalar cache with one batch of loads (one round trip)
+// instead of a chain of dependent misses, each a full memory round trip, as its fields are
+// first used. The loaded values are discarded; the wait sits in the same asm block.
+// Loads at every 64 bytes from the start plus one at the last dword cover every line of a
+// 608-byte descriptor whatever its alignment.
+static_assert(sizeof(EngStage) == 608, "warm_stage covers a 608-byte stage descriptor");
+INL void warm_stage(SP S) {
+  uint32_t d0, d1, d2, d3, d4, d5, d6, d7, d8, d9, d10;
+  asm volatile(
+      "s_load_dword %0, %11, 0x0\n\ts_load_dword %1, %11, 0x40\n\t"
+      "s_load_dword %2, %11, 0x80\n\ts_load_dword %3, %11, 0xc0\n\t"
+      "s_load_dword %4, %11, 0x100\n\ts_load_dword %5, %11, 0x140\n\t"
+      "s_load_dword %6, %11, 0x180\n\ts_load_dword %7, %11, 0x1c0\n\t"
+      "s_load_dword %8, %11, 0x200\n\ts_load_dword %9, %11, 0x240\n\t"
+      "s_load_dword %10, %11, 0x25c\n\ts_waitcnt lgkmcnt(0)"
+      : "=&s"(d0), "=&s"(d1), "=&s"(d2), "=&s"(d3), "=&s"(d4), "=&s"(d5), "=&s"(d6), "=&s"(d7),
+        "=&s"(d8), "=&s"(d9), "=&s"(d10)
+      : "s"(S)
+      : "memory");
 }
 
 // Sum over the wave of a per-lane value, fixed butterfly order (identical on every lane).
@@ -289,92 +387,90 @@ INL bool wait_words(const tagged_t* const* p, const bool* want, const uint32_t* 
   }
 }
 
-// Stage-start duties, run by all nine waves (tid = thread index in the workgroup):
-//  1. every thread fetches up to four positions of the workgroup's (at most two) 1024-wide
-//     input blocks in one sweep of tagged loads, while the communication wave also fetches the
-//     producers' tile statistics and turns them into RMS denominators;
+constexpr int kPosPerThread = (kEngMaxBlocks * 1024 + kEngThreads - 1) / kEngThreads;
+
+// Stage-start duties of a streaming workgroup, run by all nine waves (tid = thread index):
+//  1. every thread fetches its positions of the share's (at most four) 1024-wide input blocks
+//     in one sweep of tagged loads, while the communication wave also fetches the producers'
+//     tile statistics and turns them into RMS denominators;
 //  2. after a barrier every thread rescales its positions to bf16 and stores them to the
-//     staging area; the workgroup owning the tile-0 unit of a block (of the source's record
-//     matrix) also writes that block to the caller's record. A stage without matrices (the
-//     final rescale of a decode step) splits its source's record evenly over all workgroups.
-INL void stage_inputs(PP P, EngLds& L, int s, int wg, int tid, bool comm, uint32_t epoch,
-                      uint32_t* error) {
+//     staging area; after a second barrier the communication wave copies each block whose
+//     tile-0 unit (of the source's record matrix) this workgroup owns to the caller's record.
+// A stage without matrices (the final rescale of a decode step) splits its source's record
+// evenly over the streaming workgroups; the communication wave handles that slice alone.
+// Compute waves (Comm = false) issue no global stores here: a store's registers would make the
+// compiler wait for every outstanding load, ring copies included, before the next LDS read.
+template <bool Comm>
+INL void stage_inputs(PP P, EngLds& L, int s, int w, int tid, uint32_t epoch, uint32_t* error) {
   SP S = &P->st[s];
   XP X0 = &S->src[0];
   XP X1 = &S->src[1];
-  const int par = s & 1;
-  const int nwg = P->nwg;
+  const int nst = P->nstream;
   const int lane = tid & 63;
-  int u0, u1;
-  wg_range(S->units, wg, nwg, &u0, &u1);
-  const Blocks B = wg_blocks(S, u0, u1);
-  if (B.n > 2 && comm) {
+  const Share r = stage_share(S, w, nst);
+  const Blocks B = stage_blocks(S, r);
+  if (Comm && B.n > kEngMaxBlocks) {
     set_err(error);
     L.abort_flag = 1;
   }
-  const int nb = B.n > 2 ? 0 : B.n;
+  const int nb = B.n > kEngMaxBlocks ? 0 : B.n;
   const bool live = lds_poll_i(&L.abort_flag) == 0;
   const bool slice = S->nmat == 0 && S->nsrc > 0 && X0->record != nullptr;
-  int kpos[4];
-  bool one[4], valid[4], staged[4];
+  const SrcFields F0 = src_fields(X0), F1 = src_fields(X1);
+  int kpos[kPosPerThread];
+  bool one[kPosPerThread], valid[kPosPerThread];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int p = tid + kEngThreads * j;
+  for (int j = 0; j < kPosPerThread; ++j) {
     kpos[j] = 0;
     one[j] = false;
     valid[j] = false;
-    staged[j] = false;
+    const int p = tid + kEngThreads * j;
     if (p < nb * 1024) {
-      const int b = p >> 10;
-      one[j] = (b ? B.src1 : B.src0) != 0;
-      kpos[j] = (b ? B.sg1 : B.sg0) * 1024 + (p & 1023);
-      staged[j] = true;
-      valid[j] = kpos[j] < (one[j] ? X1->k : X0->k);
-    } else if (nb == 0 && slice) {
-      const int K = X0->k;
-      const int a = (K * wg) / nwg, e = (K * (wg + 1)) / nwg;
-      kpos[j] = a + p;
+      const int key = blk_get(B, p >> 10);
+      one[j] = (key >> 16) != 0;
+      kpos[j] = (key & 0xFFFF) * 1024 + (p & 1023);
+      valid[j] = kpos[j] < (one[j] ? F1.k : F0.k);
+    } else if (Comm && nb == 0 && slice && j < 4) {
+      const int K = F0.k;
+      const int a = (K * w) / nst, e = (K * (w + 1)) / nst;
+      kpos[j] = a + lane + 64 * j;
       valid[j] = kpos[j] < e;
     }
   }
-  // 1. one sweep of tagged loads (two words per position of a product source)
-  uint32_t w[8];
-  {
-    const tagged_t* ptr[8];
-    bool want[8];
-    uint32_t tg[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int kind = one[j] ? X1->kind : X0->kind;
-      const bool tagged = live && valid[j] && kind != kSrcDirect;
-      const int off = tagged ? kpos[j] : 0;
-      ptr[2 * j] = (one[j] ? X1->yt : X0->yt) + off;
-      ptr[2 * j + 1] = (one[j] ? X1->y2t : X0->y2t) + off;
-      want[2 * j] = tagged;
-      want[2 * j + 1] = tagged && kind == kSrcRmsProd;
-      tg[2 * j] = tg[2 * j + 1] = eng_tag(epoch, one[j] ? X1->src_stage : X0->src_stage);
+  if (Comm && live) {
+    // 1. the first row of every producer tile of the staged blocks (both factors of a product
+    //    source), 64 per load, is polled until published: the full sweep below then almost
+    //    always succeeds at once, and the wait costs one small load per round trip instead of
+    //    every thread's whole share of the blocks
+    for (int base = 0; base < nb * 32; base += 64) {
+      const int i = base + lane;
+      const int b = i >> 5, f = (i >> 4) & 1, t = i & 15;
+      bool want = false;
+      const tagged_t* ptr = F0.yt;
+      uint32_t tg = 0, got;
+      if (b < nb) {
+        const int key = blk_get(B, b);
+        const bool o = (key >> 16) != 0;
+        const int kind = o ? F1.kind : F0.kind;
+        const int k = (key & 0xFFFF) * 1024 + t * 64;
+        want = kind != kSrcDirect && k < (o ? F1.k : F0.k) && (f == 0 || kind == kSrcRmsProd);
+        ptr = (f ? (o ? F1.y2t : F0.y2t) : (o ? F1.yt : F0.yt)) + (want ? k : 0);
+        tg = eng_tag(epoch, o ? F1.src_stage : F0.src_stage);
+      }
+      if (!wait_words<1>(&ptr, &want, &tg, &got, error, &L.abort_flag)) break;
     }
-    wait_words<8>(ptr, want, tg, w, error, &L.abort_flag);
-  }
-  uint32_t direct[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int kind = one[j] ? X1->kind : X0->kind;
-    direct[j] = (valid[j] && kind == kSrcDirect) ? (one[j] ? X1->x : X0->x)[kpos[j]] : 0u;
-  }
-  if (comm) {
     for (int j = 0; j < S->nsrc; ++j) {
       XP X = j ? X1 : X0;
       float d = 1.f;
-      const bool used = (nb > 0 && (B.src0 == j || (nb > 1 && B.src1 == j))) ||
-                        (nb == 0 && slice && j == 0);
+      bool used = nb == 0 && slice && j == 0;
+      for (int b = 0; b < nb; ++b) used = used || (blk_get(B, b) >> 16) == j;
       if (live && used && X->kind != kSrcDirect) {
         const uint32_t tag = eng_tag(epoch, X->src_stage);
         float part = 0.f;
         for (int base = 0; base < X->nstats; base += 64 * 8) {
           const tagged_t* ptr[8];
           bool want[8];
-          uint32_t tg[8], v[8];
+          uint32_t tg[8], sv[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const int idx = base + i * 64 + lane;
@@ -382,49 +478,88 @@ INL void stage_inputs(PP P, EngLds& L, int s, int wg, int tid, bool comm, uint32
             ptr[i] = X->stats + (want[i] ? idx : 0);
             tg[i] = tag;
           }
-          if (!wait_words<8>(ptr, want, tg, v, error, &L.abort_flag)) break;
+          if (!wait_words<8>(ptr, want, tg, sv, error, &L.abort_flag)) break;
 #pragma unroll
           for (int i = 0; i < 8; ++i)
-            if (want[i]) part += __uint_as_float(v[i]);
+            if (want[i]) part += __uint_as_float(sv[i]);
         }
         d = sqrtf(wave_sum(part) / (float)X->k + X->eps);
       }
-      if (lane == 0) L.denom[par][j] = d;
+      if (lane == 0) L.denom[j] = d;
     }
   }
   __syncthreads();
-  // 2. rescale, stage, record
-  MP R0 = &S->mat[X0->rec_mat];
-  MP R1 = &S->mat[X1->rec_mat];
+  // 2. every thread's positions in one sweep of tagged loads (two words per position of a
+  //    product source); the directly given input of a plain source is read as is
+  uint32_t v[2 * kPosPerThread];
+  {
+    const tagged_t* ptr[2 * kPosPerThread];
+    bool want[2 * kPosPerThread];
+    uint32_t tg[2 * kPosPerThread];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int kind = one[j] ? X1->kind : X0->kind;
+    for (int j = 0; j < kPosPerThread; ++j) {
+      const int kind = one[j] ? F1.kind : F0.kind;
+      const bool tagged = live && valid[j] && kind != kSrcDirect;
+      const int off = tagged ? kpos[j] : 0;
+      ptr[2 * j] = (one[j] ? F1.yt : F0.yt) + off;
+      ptr[2 * j + 1] = (one[j] ? F1.y2t : F0.y2t) + off;
+      want[2 * j] = tagged;
+      want[2 * j + 1] = tagged && kind == kSrcRmsProd;
+      tg[2 * j] = tg[2 * j + 1] = eng_tag(epoch, one[j] ? F1.src_stage : F0.src_stage);
+    }
+    wait_words<2 * kPosPerThread>(ptr, want, tg, v, error, &L.abort_flag);
+  }
+  uint32_t direct[kPosPerThread];
+#pragma unroll
+  for (int j = 0; j < kPosPerThread; ++j) direct[j] = 0u;
+  if (F0.kind == kSrcDirect || F1.kind == kSrcDirect) {
+#pragma unroll
+    for (int j = 0; j < kPosPerThread; ++j) {
+      const int kind = one[j] ? F1.kind : F0.kind;
+      if (valid[j] && kind == kSrcDirect) direct[j] = g_ld16((one[j] ? F1.x : F0.x) + kpos[j]);
+    }
+    // Settle these loads here, seen by the compiler: a load whose result is dead on some path
+    // would otherwise stay pending as far as it knows, and the first reuse of its register in
+    // the unit loop would then wait for every outstanding memory operation on each iteration
+    // (ring copies in compute waves, partial stores in the communication wave).
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt and lgkmcnt untouched
+  }
+  // 3. rescale and stage (the slice of a matrix-free stage goes straight to the record)
+#pragma unroll
+  for (int j = 0; j < kPosPerThread; ++j) {
+    const int kind = one[j] ? F1.kind : F0.kind;
     uint32_t xb = direct[j];
     if (valid[j] && kind != kSrcDirect) {
-      float h = e_bf16(w[2 * j]);
-      if (kind == kSrcRmsProd) h *= e_bf16(w[2 * j + 1]);
-      xb = e_to_bf16(h / L.denom[par][one[j] ? 1 : 0]);
+      float h = e_bf16(v[2 * j]);
+      if (kind == kSrcRmsProd) h *= e_bf16(v[2 * j + 1]);
+      xb = e_to_bf16(h / L.denom[one[j] ? 1 : 0]);
     }
-    uint16_t* rec = one[j] ? X1->record : X0->record;
-    if (staged[j]) {
-      const int p = tid + kEngThreads * j;
-      L.staging[par][p >> 10][p & 1023] = valid[j] ? e_bf16(xb) : 0.f;
-      const int owner = one[j] ? R1->unit_base + (kpos[j] >> 10) * R1->tiles
-                               : R0->unit_base + (kpos[j] >> 10) * R0->tiles;
-      if (valid[j] && rec != nullptr && owner >= u0 && owner < u1) rec[kpos[j]] = (uint16_t)xb;
-    } else if (valid[j] && live) {
-      rec[kpos[j]] = (uint16_t)xb;
-    }
+    const int p = tid + kEngThreads * j;
+    if (p < nb * 1024) L.staging[p >> 10][p & 1023] = valid[j] ? e_bf16(xb) : 0.f;
+    if (Comm && nb == 0 && valid[j] && live) g_st16(X0->record + kpos[j], xb);
   }
   __syncthreads();
+  if (Comm && live) {
+    // records of the blocks this workgroup owns, from the staged (exactly bf16) values
+    for (int b = 0; b < nb; ++b) {
+      const int key = blk_get(B, b);
+      const int src = key >> 16, sg = key & 0xFFFF;
+      XP X = src ? X1 : X0;
+      MP R = &S->mat[X->rec_mat];
+      if (X->record == nullptr || !share_has(r, R->unit_base + sg * R->tiles)) continue;
+      const int n = min(1024, X->k - sg * 1024);
+      for (int q = lane; q < n; q += 64)
+        g_st16(X->record + sg * 1024 + q, __float_as_uint(L.staging[b][q]) >> 16);
+    }
+  }
 }
 
 // ------------------------------------------------------------------------------------------
 // compute wave V
 // ------------------------------------------------------------------------------------------
-template <int V, int Bk>
+template <int V>
 INL float lookup_group(const EngLds& L, const uint32_t s4[4]) {
-  const char* lb = (const char*)&L.lut[Bk][V][0];
+  const char* lb = (const char*)&L.lut[V][0];
   float pa = 0.f, pb = 0.f;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
@@ -439,95 +574,195 @@ INL float lookup_group(const EngLds& L, const uint32_t s4[4]) {
   return pa + pb;
 }
 
+// Builds this wave's 32 tables of 16 signed sums (group V of staged block b), two lanes per
+// table. Entry e = m + 4 j of the table for inputs (x0, x1, x2, x3) is pair term m of (x0, x1)
+// plus pair term j of (x2, x3), where pair term 0 = -a-b, 1 = a-b, 2 = b-a, 3 = a+b.
 template <int V>
-INL void issue_unit(PP P, const UnitIt& it, EngLds& L, int slot, int lane) {
-  const uint8_t* gs = (const uint8_t*)P + lane * 16;   // harmless dummy source
-  const uint8_t* gc = (const uint8_t*)P + lane * 4;
-  if (it.valid) {
-    MP M = &P->st[it.s].mat[it.m];
-    if (it.sg * kSuper + V < M->groups) {
-      const uint8_t* t = M->w + (size_t)it.tile * M->tile_bytes + (size_t)it.sg * (kBlock * (1 + kSuper));
-      gs = t + kBlock * (1 + V) + lane * 16;
-      gc = t + lane * 16 + (V / 2) * 4;
-    }
+INL void build_lut(EngLds& L, int b, int lane) {
+  const int c = lane >> 1, h = lane & 1;
+  const float* xs = &L.staging[b][kGroup * V + 4 * c];
+  const float x0 = xs[0], x1 = xs[1], x2 = xs[2], x3 = xs[3];
+  const float p0 = -x0 - x1, p1 = x0 - x1, p2 = x1 - x0, p3 = x0 + x1;
+  // this lane writes entries 8h..8h+7, i.e. pair terms j = 2h and 2h+1 of (x2, x3)
+  const float q0 = h ? x3 - x2 : -x2 - x3;
+  const float q1 = h ? x2 + x3 : x2 - x3;
+  float4* dst = (float4*)&L.lut[V][c * 16 + 8 * h];
+  dst[0] = make_float4(p0 + q0, p1 + q0, p2 + q0, p3 + q0);
+  dst[1] = make_float4(p0 + q1, p1 + q1, p2 + q1, p3 + q1);
+}
+
+// Starts the ring copy of the cursor's unit into slot `slot` (a dummy copy from the program
+// when this wave's group does not exist there).
+template <int V>
+INL void issue_unit(PP P, const Cursor& c, EngLds& L, int slot, uint32_t voff_w, uint32_t voff_s) {
+  const void* base = c.ok ? (const void*)c.p : (const void*)P;
+  dma_slot(base, voff_w, voff_s, lds_addr(&L.ring_w[V][slot][0]), lds_addr(&L.ring_s[V][slot][0]));
+}
+
+// Waits until the ring slot of the next unit has landed, given how many slots were issued after
+// it (each slot is two vector-memory instructions, completing in order).
+INL void wait_ring(int ahead) {
+  switch (ahead) {
+    case 7: asm volatile("s_waitcnt vmcnt(14)" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
   }
-  dma16(gs, lds_addr(&L.ring_w[V][slot][0]));
-  dma4(gc, lds_addr(&L.ring_s[V][slot][0]));
+}
+static_assert(kEngRing == 8, "wait_ring covers a ring of eight slots");
+
+// First stage >= s whose end holds prefetching back (its last partial goes out first).
+INL int next_gate(PP P, int s) {
+  while (s < P->nstages && !P->st[s].drain) ++s;
+  return s;
 }
 
 template <int V>
-INL void compute_wave(PP P, EngLds& L, int wg, int lane, uint32_t epoch, uint32_t* error) {
-  const int nwg = P->nwg;
-  UnitIt pf, cur;
-  it_seek_stage(P, wg, pf, 0);
-  cur = pf;
-  for (int j = 0; j < kRing; ++j) {
-    issue_unit<V>(P, pf, L, j, lane);
-    it_next(P, wg, pf);
-  }
-  unsigned cnt = 0;
-  for (int s = 0; s < P->nstages; ++s) {
-    stage_inputs(P, L, s, wg, V * 64 + lane, false, epoch, error);
-    SP S = &P->st[s];
-    int u0, u1;
-    wg_range(S->units, wg, nwg, &u0, &u1);
-    if (lds_poll_i(&L.abort_flag) || u1 <= u0) continue;
-    const int par = s & 1;
-    const Blocks B = wg_blocks(S, u0, u1);
-    // this wave's group of every block: 32 tables of 16 signed sums, two lanes per table
-    for (int b = 0; b < B.n; ++b) {
-      const int c = lane >> 1, h = lane & 1;
-      const float* xs = &L.staging[par][b][kGroup * V + 4 * c];
-      const float x0 = xs[0], x1 = xs[1], x2 = xs[2], x3 = xs[3];
-      const float p0 = -x0 - x1, p1 = x0 - x1, p2 = x1 - x0, p3 = x0 + x1;
-      // entry e = m + 4 j adds pair term j of (x2, x3): j = 0: -x2-x3, 1: x2-x3, 2: x3-x2,
-      // 3: x2+x3; this lane writes entries 8h..8h+7, i.e. j = 2h and 2h+1
-      const float q0 = h ? x3 - x2 : -x2 - x3;
-      const float q1 = h ? x2 + x3 : x2 - x3;
-      float4* dst = (float4*)&L.lut[b][V][c * 16 + 8 * h];
-      dst[0] = make_float4(p0 + q0, p1 + q0, p2 + q0, p3 + q0);
-      dst[1] = make_float4(p0 + q1, p1 + q1, p2 + q1, p3 + q1);
+INL void compute_wave(PP P, EngLds& L, int w, int lane, uint32_t epoch, uint32_t* error) {
+  // per-lane offsets of this wave's sign record (group V) and scale word within a super-group
+  const uint32_t voff_w = (uint32_t)(lane * 16 + kBlock * (1 + V));
+  const uint32_t voff_s = (uint32_t)(lane * 16 + (V / 2) * 4);
+  Cursor pf, cu;
+  cur_stage<V, false>(P, pf, w, 0);
+  cur_stage<V, true>(P, cu, w, 0);
+  unsigned issued = 0, cnt = 0;
+  int gate = next_gate(P, 0);
+  // refill: keep up to kRing units in flight, never past the gate stage
+  auto refill = [&]() {
+    while (issued - cnt < (unsigned)kRing && pf.s < P->nstages && pf.s <= gate) {
+      issue_unit<V>(P, pf, L, issued % kRing, voff_w, voff_s);
+      ++issued;
+      cur_next<V, false>(P, pf, w);
     }
-    for (int k = u0; k < u1; ++k) {
-      const int slot = cnt % kRing;
-      wait_ring();
-      MP M = &S->mat[cur.m];
-      float partial = 0.f;
-      if (cur.sg * kSuper + V < M->groups) {
-        const uint32_t* rw = &L.ring_w[V][slot][lane * 4];
-        uint32_t s4[4] = {rw[0], rw[1], rw[2], rw[3]};
-        const uint32_t sw = L.ring_s[V][slot][lane];
-        const float scale = e_f16((V & 1) ? (sw >> 16) : (sw & 0xFFFFu));
-        const int b = block_index(B, M->src, cur.sg);
-        const float sum = b ? lookup_group<V, 1>(L, s4) : lookup_group<V, 0>(L, s4);
-        partial = scale * sum;
-      }
-      // hand the partial to the communication wave
-      const int ps = cnt % kEngSlots;
-      const unsigned round = cnt / kEngSlots;
-      for (int it = 0; lds_poll(&L.freed[ps]) < round; ++it) {
-        if (lds_poll_i(&L.abort_flag) || it >= kPollLimit) {
+  };
+  refill();
+  for (int s = 0; s < P->nstages; ++s) {
+    if (s > gate) {
+      // the gate stage's partials are all issued: prefetch past it
+      for (int it = 0; (int)lds_poll((const uint32_t*)&L.published) < gate &&
+                       !lds_poll_i(&L.abort_flag);
+           ++it) {
+        if (it >= kPollLimit) {
           L.abort_flag = 1;
           break;
         }
         __builtin_amdgcn_s_sleep(1);
       }
+      gate = next_gate(P, s);
+      refill();
+    }
+    stage_inputs<false>(P, L, s, w, V * 64 + lane, epoch, error);
+    SP S = &P->st[s];
+    const int n = share_units(stage_share(S, w, P->nstream));
+    if (lds_poll_i(&L.abort_flag) || n == 0) continue;
+    int lut_b = -1;   // block the tables currently hold
+    for (int k = 0; k < n; ++k) {
+      const int slot = cnt % kRing;
+      const int ps = cnt % kEngSlots;
+      const unsigned round = cnt / kEngSlots;
+      const uint32_t fr = lds_poll(&L.freed[ps]);   // read early, tested after the lookups
+      wait_ring((int)(issued - cnt) - 1);
+      float partial = 0.f;
+      if (cu.ok) {
+        const uint32_t* rw = &L.ring_w[V][slot][lane * 4];
+        uint32_t s4[4] = {rw[0], rw[1], rw[2], rw[3]};
+        const uint32_t sw = L.ring_s[V][slot][lane];
+        const float scale = e_f16((V & 1) ? (sw >> 16) : (sw & 0xFFFFu));
+        if (cu.b != lut_b) {   // at most kEngMaxBlocks times per stage
+          build_lut<V>(L, cu.b, lane);
+          lut_b = cu.b;
+        }
+        partial = scale * lookup_group<V>(L, s4);
+      }
+      // hand the partial to the communication wave (slot ps must have been consumed)
+      if (fr < round) {
+        for (int it = 0; lds_poll(&L.freed[ps]) < round; ++it) {
+          if (lds_poll_i(&L.abort_flag) || it >= kPollLimit) {
+            L.abort_flag = 1;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      L.part[ps][V][lane] = partial;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      if (lane == 0) atomicAdd(&L.ready[ps], 1u);
-      issue_unit<V>(P, pf, L, slot, lane);
-      it_next(P, wg, pf);
-      it_next(P, wg, cur);
+      __hip_atomic_store(&L.part[ps][V][lane],
+                         ((unsigned long long)(round + 1) << 32) | __float_as_uint(partial),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       ++cnt;
+      cur_next<V, true>(P, cu, w);
+      refill();
     }
   }
-  // the ring runs ahead of the program's end (dummy records): let the last copies land
+  // let any copy still in flight land before the wave ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // ------------------------------------------------------------------------------------------
-// communication wave
+// communication wave of a streaming workgroup
+// ------------------------------------------------------------------------------------------
+INL void comm_wave(PP P, EngLds& L, int w, int lane, uint32_t epoch, uint32_t* error) {
+  unsigned cnt = 0;
+  for (int s = 0; s < P->nstages; ++s) {
+    stage_inputs<true>(P, L, s, w, kEngWaves * 64 + lane, epoch, error);
+    SP S = &P->st[s];
+    const Share r = stage_share(S, w, P->nstream);
+    const uint32_t tag = eng_tag(epoch, s);
+    bool live = !lds_poll_i(&L.abort_flag);
+    if (s + 1 < P->nstages) warm_stage(&P->st[s + 1]);
+    // publish this workgroup's unit partials as they complete (never waits on global memory)
+    for (int pass = 0; pass < 2; ++pass) {
+      const int a = pass ? r.a1 : r.a0, b = pass ? r.b1 : r.b0;
+      for (int u = a; u < b; ++u) {
+        if (!live) {
+          ++cnt;
+          continue;
+        }
+        const int ps = cnt % kEngSlots;
+        const uint32_t want = cnt / kEngSlots + 1;
+        uint32_t wv[kEngWaves];
+        for (int it = 0;; ++it) {
+          bool all = true;
+#pragma unroll
+          for (int v = 0; v < kEngWaves; ++v) {
+            const unsigned long long t = __hip_atomic_load(&L.part[ps][v][lane], __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_WORKGROUP);
+            wv[v] = (uint32_t)t;
+            all = all && (uint32_t)(t >> 32) == want;
+          }
+          if (__builtin_amdgcn_ballot_w64(!all) == 0) break;
+          if (lds_poll_i(&L.abort_flag) || it >= kPollLimit) {
+            live = false;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        if (!live) {
+          set_err(error);
+          L.abort_flag = 1;
+          ++cnt;
+          continue;
+        }
+        float p = 0.f;
+#pragma unroll
+        for (int v = 0; v < kEngWaves; ++v) p += __uint_as_float(wv[v]);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        if (lane == 0) L.freed[ps] = want;
+        st_tag(S->part + (size_t)u * 64 + lane, __float_as_uint(p), tag);
+        ++cnt;
+      }
+    }
+    // every partial of this stage has been issued: compute waves may prefetch past it
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    if (lane == 0) __hip_atomic_store(&L.published, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// finalising workgroups
 // ------------------------------------------------------------------------------------------
 
 // Finalises item `item` of stage S (number s): one output tile of a matrix, or the same tile of
@@ -548,6 +783,16 @@ INL void finalize_item(SP S, EngLds& L, int s, int item, int lane, uint32_t epoc
   MP M2 = &S->mat[m2 < 0 ? m : m2];
   const int s1 = M->supers, s2 = m2 < 0 ? 0 : M2->supers;
   const uint32_t tag = eng_tag(epoch, s);
+  {
+    // wait cheaply first: lane i watches the first word of block partial i (one small load per
+    // round trip), then read every lane's words, which are then almost always all there
+    const bool want = lane < s1 + s2;
+    const int u = lane < s1 ? M->unit_base + lane * M->tiles + tile
+                            : M2->unit_base + (lane - s1) * M2->tiles + tile;
+    const tagged_t* ptr = S->part + (size_t)(want ? u : 0) * 64;
+    uint32_t got;
+    if (!wait_words<1>(&ptr, &want, &tag, &got, error, &L.abort_flag)) return;
+  }
   const tagged_t* pb = S->part + lane;
   uint32_t v[kEngMaxFinal];
   bool done[kEngMaxFinal];
@@ -578,7 +823,7 @@ INL void finalize_item(SP S, EngLds& L, int s, int item, int lane, uint32_t epoc
     }
     if (__builtin_amdgcn_ballot_w64(!all) == 0) break;
     if (poll_expired(it, error, &L.abort_flag)) return;
-    __builtin_amdgcn_s_sleep(2);
+    __builtin_amdgcn_s_sleep(1);
   }
   float y1 = 0.f, y2 = 0.f;
 #pragma unroll
@@ -589,65 +834,33 @@ INL void finalize_item(SP S, EngLds& L, int s, int item, int lane, uint32_t epoc
   const int row = tile * kTileRows + lane;
   const uint32_t b1 = e_to_bf16(y1);
   st_tag(M->yt + row, b1, tag);
-  if (M->y && row < M->n) M->y[row] = (uint16_t)b1;
   if (M->kind == kMatSumSq) {
     const float yv = row < M->n ? e_bf16(b1) : 0.f;
     const float ss = wave_sum(yv * yv);
     if (lane == 0) st_tag(M->stat + tile, __float_as_uint(ss), tag);
   }
+  uint32_t b2 = 0;
   if (m2 >= 0) {
-    const uint32_t b2 = e_to_bf16(y2);
+    b2 = e_to_bf16(y2);
     st_tag(M2->yt + row, b2, tag);
-    if (M2->y && row < M2->n) M2->y[row] = (uint16_t)b2;
     if (M2->kind == kMatPair) {
       const float h = row < M2->n ? e_bf16(b1) * e_bf16(b2) : 0.f;
       const float ss = wave_sum(h * h);
       if (lane == 0) st_tag(M2->stat + tile, __float_as_uint(ss), tag);
     }
   }
+  // the caller's plain copies last: they are off the critical path
+  if (M->y && row < M->n) g_st16(M->y + row, b1);
+  if (m2 >= 0 && M2->y && row < M2->n) g_st16(M2->y + row, b2);
 }
 
-INL void comm_wave(PP P, EngLds& L, int wg, int lane, uint32_t epoch, uint32_t* error) {
-  unsigned cnt = 0;
+// Finalising wave c of nc: items c, c + nc, ... of every stage, in program order.
+INL void final_wave(PP P, EngLds& L, int c, int nc, int lane, uint32_t epoch, uint32_t* error) {
   for (int s = 0; s < P->nstages; ++s) {
-    stage_inputs(P, L, s, wg, kEngWaves * 64 + lane, true, epoch, error);
     SP S = &P->st[s];
-    int u0, u1;
-    wg_range(S->units, wg, P->nwg, &u0, &u1);
-    const uint32_t tag = eng_tag(epoch, s);
-    if (lds_poll_i(&L.abort_flag)) {
-      cnt += (unsigned)(u1 - u0);
-      continue;
-    }
-    // publish this workgroup's unit partials as they complete (never waits on global memory)
-    for (int u = u0; u < u1; ++u) {
-      const int ps = cnt % kEngSlots;
-      const unsigned want = (cnt / kEngSlots + 1) * kEngWaves;
-      bool ok = true;
-      for (int it = 0; lds_poll(&L.ready[ps]) < want; ++it) {
-        if (lds_poll_i(&L.abort_flag) || it >= kPollLimit) {
-          ok = false;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-      if (!ok) {
-        set_err(error);
-        L.abort_flag = 1;
-        break;
-      }
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      float p = 0.f;
-#pragma unroll
-      for (int v = 0; v < kEngWaves; ++v) p += L.part[ps][v][lane];
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
-      if (lane == 0) L.freed[ps] = cnt / kEngSlots + 1;
-      st_tag(S->part + (size_t)u * 64 + lane, __float_as_uint(p), tag);
-      ++cnt;
-    }
-    // then this workgroup's share of the stage's finalisation items
-    for (int item = wg; item < S->nitems; item += P->nwg) {
-      if (lds_poll_i(&L.abort_flag)) break;
+    warm_stage(S);
+    for (int item = c; item < S->nitems; item += nc) {
+      if (lds_poll_i(&L.abort_flag)) return;
       finalize_item(S, L, s, item, lane, epoch, error);
     }
   }
@@ -660,12 +873,22 @@ __global__ __launch_bounds__(kEngThreads) void q1_engine_kernel(EngArgs A) {
   const int lane = threadIdx.x & 63;
   const int wg = blockIdx.x;
   PP P = (PP)A.prog;
-  if (threadIdx.x < kEngSlots) {
-    L.ready[threadIdx.x] = 0;
-    L.freed[threadIdx.x] = 0;
+  // LDS holds whatever the previous kernel left: clear the hand-off tags (rounds start at 1)
+  for (int i = threadIdx.x; i < kEngSlots * kEngWaves * 64; i += kEngThreads)
+    (&L.part[0][0][0])[i] = 0;
+  if (threadIdx.x < kEngSlots) L.freed[threadIdx.x] = 0;
+  if (threadIdx.x == 0) {
+    L.abort_flag = 0;
+    L.published = -1;
   }
-  if (threadIdx.x == 0) L.abort_flag = 0;
+  if (wave == 0) warm_stage(&P->st[0]);
   __syncthreads();
+  const int nst = P->nstream;
+  if (wg >= nst) {   // finalising workgroup: all nine waves finalise
+    const int nc = (P->nwg - nst) * (kEngWaves + 1);
+    final_wave(P, L, (wg - nst) * (kEngWaves + 1) + wave, nc, lane, A.epoch, A.error);
+    return;
+  }
   switch (wave) {
     case 0: compute_wave<0>(P, L, wg, lane, A.epoch, A.error); break;
     case 1: compute_wave<1>(P, L, wg, lane, A.epoch, A.error); break;
@@ -690,6 +913,8 @@ constexpr int kProgSlots = 16;
 
 struct EngDevice {
   int nwg = 0;
+  int nfinal = 0;   // finalising workgroups
+  bool cooperative = false;
   uint32_t epoch = 0;
   void* ws = nullptr;   // [error word | program slots | per-stage partials, tagged outputs, stats]
   size_t ws_bytes = 0;
@@ -716,6 +941,14 @@ static lbq_status eng_device(int* dev_out, EngDevice** out) {
         per_cu < 1)
       return LBQ_E_DEVICE;
     E.nwg = prop.multiProcessorCount;
+    // a eighth of the workgroups finalise (a multiple of the eight XCDs keeps them spread out)
+    int nf = E.nwg / 8;
+    if (const char* env = getenv("LBQ_ENGINE_FINALIZERS")) nf = atoi(env);
+    if (nf < 1) nf = 1;
+    if (nf > E.nwg - 1) nf = E.nwg - 1;
+    E.nfinal = nf;
+    const char* coop = getenv("LBQ_ENGINE_COOPERATIVE");
+    E.cooperative = coop != nullptr && atoi(coop) != 0;
   }
   *dev_out = dev;
   *out = &E;
@@ -768,10 +1001,18 @@ static lbq_status eng_launch(EngDevice& E, std::vector<char>& prog, hipStream_t 
   if (++E.epoch >= (1u << 23)) E.epoch = 1;
   a.epoch = E.epoch;
   void* args[] = {&a};
-  if (hipLaunchCooperativeKernel((const void*)q1_engine_kernel, dim3(E.nwg), dim3(kEngThreads),
-                                 args, 0, stream) != hipSuccess)
-    return LBQ_E_DEVICE;
-  return LBQ_OK;
+  // One workgroup per compute unit (the LDS footprint allows no more), so on an otherwise idle
+  // device every workgroup is resident at once. A plain launch costs a few microseconds; the
+  // cooperative launch, which guarantees residency, costs about twenty. Should another kernel
+  // hold compute units meanwhile, the bounded waits time out and the error word reports it
+  // (lbq_device_check) rather than the device hanging.
+  const hipError_t e =
+      E.cooperative
+          ? hipLaunchCooperativeKernel((const void*)q1_engine_kernel, dim3(E.nwg), dim3(kEngThreads),
+                                       args, 0, stream)
+          : hipLaunchKernel((const void*)q1_engine_kernel, dim3(E.nwg), dim3(kEngThreads), args, 0,
+                            stream);
+  return e == hipSuccess ? LBQ_OK : LBQ_E_DEVICE;
 }
 
 // Workspace words (tagged_t) a matrix of a stage needs: outputs plus per-tile statistics.
@@ -826,23 +1067,49 @@ static void eng_part(EngStage& S, tagged_t** cursor) {
   *cursor += (size_t)S.units * 64;
 }
 
+// Host mirror of the device's share and block computations: every streaming workgroup's share
+// of a stage may need at most kEngMaxBlocks input blocks.
+static int host_blocks(const EngStage& S, int w, int n) {
+  int keys[16], nk = 0;
+  const int p0 = S.part0, p1 = S.units - S.part0;
+  const int ra[2] = {(int)((long long)p0 * w / n), p0 + (int)((long long)p1 * w / n)};
+  const int rb[2] = {(int)((long long)p0 * (w + 1) / n), p0 + (int)((long long)p1 * (w + 1) / n)};
+  for (int r = 0; r < 2; ++r) {
+    for (int u = ra[r]; u < rb[r];) {
+      int m = 0;
+      while (u >= S.mat[m].unit_base + S.mat[m].units) ++m;
+      const EngMat& M = S.mat[m];
+      const int k = u - M.unit_base, sg = k / M.tiles, tile = k - sg * M.tiles;
+      const int key = (M.src << 16) | sg;
+      bool seen = false;
+      for (int i = 0; i < nk; ++i) seen = seen || keys[i] == key;
+      if (!seen) {
+        if (nk == 16) return 17;
+        keys[nk++] = key;
+      }
+      u += M.tiles - tile;
+    }
+  }
+  return nk;
+}
+
 static bool eng_fits(const EngProgram* P) {
+  if (P->nstream < 1 || P->nstream >= P->nwg) return false;
   for (int s = 0; s < P->nstages; ++s) {
     const EngStage& S = P->st[s];
-    // every workgroup's share of a stage must touch at most two (source, block) pairs:
-    // guaranteed when each share is no longer than the shortest column of tiles
-    int min_tiles = 1 << 30;
     for (int m = 0; m < S.nmat; ++m) {
       const EngMat& M = S.mat[m];
-      min_tiles = min_tiles < M.tiles ? min_tiles : M.tiles;
       const int fin = M.supers + (M.pair >= 0 ? S.mat[M.pair].supers : 0);
       if (M.item_base >= 0 && fin > kEngMaxFinal) return false;
+      if (M.tile_bytes >= (1LL << 31)) return false;
     }
-    const int share = (S.units + P->nwg - 1) / P->nwg;
-    if (S.nmat && share > min_tiles) return false;
     for (int j = 0; j < S.nsrc; ++j)
       if ((long long)S.src[j].k * P->nwg >= (1LL << 31)) return false;
     if ((long long)S.units * P->nwg >= (1LL << 31)) return false;
+    if (S.nmat == 0 && S.nsrc > 0 && (S.src[0].k + P->nstream - 1) / P->nstream > 4 * 64)
+      return false;   // slice of a matrix-free stage: four positions per lane of one wave
+    for (int w = 0; w < P->nstream; ++w)
+      if (host_blocks(S, w, P->nstream) > kEngMaxBlocks) return false;
   }
   return true;
 }
@@ -870,10 +1137,12 @@ lbq_status lbq_engine_gemv_q1(const void* d_w, int32_t n, int32_t k, const uint1
   EngProgram* P = (EngProgram*)prog.data();
   P->nstages = 1;
   P->nwg = E->nwg;
+  P->nstream = E->nwg - E->nfinal;
   EngStage& S = P->st[0];
   tagged_t* cursor = (tagged_t*)((char*)E->ws + kHeadBytes);
   if (!eng_mat(S, 0, d_w, n, k, d_y, 0, kMatPlain, &cursor)) return LBQ_E_SHAPE;
   eng_part(S, &cursor);
+  S.part0 = S.units;
   S.nsrc = 1;
   S.src[0].kind = kSrcDirect;
   S.src[0].x = d_x;
@@ -883,9 +1152,14 @@ lbq_status lbq_engine_gemv_q1(const void* d_w, int32_t n, int32_t k, const uint1
   return eng_launch(*E, prog, stream);
 }
 
-// Whole decode step (batch 1) through the engine: per layer a stage for q, k, v, gate, up (input
-// x = rescale of the previous down output) and a stage for o and down (inputs rescale(q) and
-// rescale(gate * up)), then a final stage that only rescales the last down output.
+// Whole decode step (batch 1) through the engine. Per layer three stages:
+//  A  : q, k, v (part 0) then gate, up (part 1), input x = rescale of the previous down output
+//       (the caller's x0 for layer 0); q comes first in every workgroup's share so its tiles
+//       are finalised while gate and up still stream;
+//  B1 : o, input rescale(q);
+//  B2 : down, input rescale(gate * up);
+// then a final stage that only rescales the last down output into the caller's record.
+// Stages A and B2 drain: their last partials feed the next stage but one and the next stage.
 lbq_status lbq_engine_decode_q1(const lbq_q1_layer* layers, int32_t L, int32_t hidden, int32_t kv,
                                 int32_t ffn, const uint16_t* d_x0, uint16_t* d_act, float eps,
                                 hipStream_t stream) {
@@ -894,7 +1168,7 @@ lbq_status lbq_engine_decode_q1(const lbq_q1_layer* layers, int32_t L, int32_t h
   EngDevice* E;
   lbq_status st = eng_device(&dev, &E);
   if (st != LBQ_OK) return st;
-  const int nst = 2 * L + 1;
+  const int nst = 3 * L + 1;
   if (nst > kEngMaxStages) return LBQ_E_UNSUPPORTED;
   Geometry gq, gk, gf, gd;
   if (!make_geometry(hidden, hidden, 1, &gq) || !make_geometry(kv, hidden, 1, &gk) ||
@@ -912,79 +1186,69 @@ lbq_status lbq_engine_decode_q1(const lbq_q1_layer* layers, int32_t L, int32_t h
   EngProgram* P = (EngProgram*)prog.data();
   P->nstages = nst;
   P->nwg = E->nwg;
+  P->nstream = E->nwg - E->nfinal;
   tagged_t* cursor = (tagged_t*)((char*)E->ws + kHeadBytes);
   auto at = [&](int layer, int slot) {
     return d_act + lbq_decode_act_offset(layer, slot, L, hidden, kv, ffn, 1);
   };
+  auto rms_src = [&](EngSrc& X, int kind, int k, const EngMat& y, const EngMat* y2,
+                     const EngMat& stats, int src_stage, uint16_t* record, int rec_mat) {
+    X.kind = kind;
+    X.k = k;
+    X.yt = y.yt;
+    X.y2t = y2 ? y2->yt : nullptr;
+    X.stats = stats.stat;
+    X.nstats = stats.tiles;
+    X.src_stage = src_stage;
+    X.eps = eps;
+    X.record = record;
+    X.rec_mat = rec_mat;
+  };
   const EngMat* prev_down = nullptr;
   for (int l = 0; l < L; ++l) {
-    EngStage& A = P->st[2 * l];
-    EngStage& Bs = P->st[2 * l + 1];
+    EngStage& A = P->st[3 * l];
+    EngStage& B1 = P->st[3 * l + 1];
+    EngStage& B2 = P->st[3 * l + 2];
     bool ok = eng_mat(A, 0, layers[l].q, hidden, hidden, at(l, LBQ_ACT_Q), 0, kMatSumSq, &cursor);
     ok = ok && eng_mat(A, 1, layers[l].k, kv, hidden, at(l, LBQ_ACT_K), 0, kMatPlain, &cursor);
     ok = ok && eng_mat(A, 2, layers[l].v, kv, hidden, at(l, LBQ_ACT_V), 0, kMatPlain, &cursor);
+    A.part0 = A.units;
     ok = ok && eng_mat(A, 3, layers[l].gate, ffn, hidden, at(l, LBQ_ACT_GATE), 0, kMatPlain, &cursor);
     ok = ok && eng_mat(A, 4, layers[l].up, ffn, hidden, at(l, LBQ_ACT_UP), 0, kMatPair, &cursor);
     if (!ok) return LBQ_E_SHAPE;
     eng_pair(A, 3, 4);
     eng_part(A, &cursor);
+    A.drain = 1;
     A.nsrc = 1;
-    EngSrc& xs = A.src[0];
-    xs.k = hidden;
-    xs.record = at(l, LBQ_ACT_X);
-    xs.rec_mat = 0;
     if (l == 0) {
-      xs.kind = kSrcDirect;
-      xs.x = d_x0;
+      A.src[0].kind = kSrcDirect;
+      A.src[0].x = d_x0;
+      A.src[0].k = hidden;
+      A.src[0].record = at(l, LBQ_ACT_X);
+      A.src[0].rec_mat = 0;
     } else {
-      xs.kind = kSrcRms;
-      xs.yt = prev_down->yt;
-      xs.stats = prev_down->stat;
-      xs.nstats = prev_down->tiles;
-      xs.src_stage = 2 * l - 1;
-      xs.eps = eps;
+      rms_src(A.src[0], kSrcRms, hidden, *prev_down, nullptr, *prev_down, 3 * l - 1,
+              at(l, LBQ_ACT_X), 0);
     }
-    ok = eng_mat(Bs, 0, layers[l].o, hidden, hidden, at(l, LBQ_ACT_O), 0, kMatPlain, &cursor);
-    ok = ok && eng_mat(Bs, 1, layers[l].down, hidden, ffn, at(l, LBQ_ACT_DOWN), 1, kMatSumSq, &cursor);
-    if (!ok) return LBQ_E_SHAPE;
-    eng_part(Bs, &cursor);
-    Bs.nsrc = 2;
-    EngSrc& xo = Bs.src[0];
-    xo.kind = kSrcRms;
-    xo.k = hidden;
-    xo.yt = A.mat[0].yt;
-    xo.stats = A.mat[0].stat;
-    xo.nstats = A.mat[0].tiles;
-    xo.src_stage = 2 * l;
-    xo.eps = eps;
-    xo.record = at(l, LBQ_ACT_XO);
-    xo.rec_mat = 0;
-    EngSrc& xd = Bs.src[1];
-    xd.kind = kSrcRmsProd;
-    xd.k = ffn;
-    xd.yt = A.mat[3].yt;
-    xd.y2t = A.mat[4].yt;
-    xd.stats = A.mat[4].stat;
-    xd.nstats = A.mat[4].tiles;
-    xd.src_stage = 2 * l;
-    xd.eps = eps;
-    xd.record = at(l, LBQ_ACT_XD);
-    xd.rec_mat = 1;
-    prev_down = &Bs.mat[1];
+    if (!eng_mat(B1, 0, layers[l].o, hidden, hidden, at(l, LBQ_ACT_O), 0, kMatPlain, &cursor))
+      return LBQ_E_SHAPE;
+    eng_part(B1, &cursor);
+    B1.part0 = B1.units;
+    B1.nsrc = 1;
+    rms_src(B1.src[0], kSrcRms, hidden, A.mat[0], nullptr, A.mat[0], 3 * l, at(l, LBQ_ACT_XO), 0);
+    if (!eng_mat(B2, 0, layers[l].down, hidden, ffn, at(l, LBQ_ACT_DOWN), 0, kMatSumSq, &cursor))
+      return LBQ_E_SHAPE;
+    eng_part(B2, &cursor);
+    B2.part0 = B2.units;
+    B2.drain = 1;
+    B2.nsrc = 1;
+    rms_src(B2.src[0], kSrcRmsProd, ffn, A.mat[3], &A.mat[4], A.mat[4], 3 * l, at(l, LBQ_ACT_XD), 0);
+    prev_down = &B2.mat[0];
   }
-  EngStage& F = P->st[2 * L];
-  F.nmat = 0;
-  F.units = 0;
-  F.nitems = 0;
+  EngStage& F = P->st[3 * L];
   F.nsrc = 1;
-  F.src[0].kind = kSrcRms;
-  F.src[0].k = hidden;
-  F.src[0].yt = prev_down->yt;
-  F.src[0].stats = prev_down->stat;
-  F.src[0].nstats = prev_down->tiles;
-  F.src[0].src_stage = 2 * L - 1;
-  F.src[0].eps = eps;
-  F.src[0].record = d_act + lbq_decode_act_offset(L, LBQ_ACT_NSLOTS, L, hidden, kv, ffn, 1);
+  rms_src(F.src[0], kSrcRms, hidden, *prev_down, nullptr, *prev_down, 3 * L - 1,
+          d_act + lbq_decode_act_offset(L, LBQ_ACT_NSLOTS, L, hidden, kv, ffn, 1), 0);
   if ((size_t)((char*)cursor - (char*)E->ws) > E->ws_bytes) return LBQ_E_NOMEM;   // sizing bug guard
   if (!eng_fits(P)) return LBQ_E_UNSUPPORTED;
   return eng_launch(*E, prog, stream);
