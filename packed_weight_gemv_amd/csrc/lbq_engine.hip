@@ -335,11 +335,23 @@ INL void warm_stage(SP S) {
       : "memory");
 }
 
-// Sum over the wave of a per-lane value, fixed butterfly order (identical on every lane).
+// Sum over the wave of a per-lane value in a fixed order, identical on every lane: DPP swaps
+// within each row of 16 lanes (pairs, quads, mirrored halves, mirrored rows), then the four row
+// sums in lane order.
+template <int Ctrl>
+INL float dpp_swap_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), Ctrl, 0xF, 0xF, false));
+}
 INL float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+  v = dpp_swap_add<0xB1>(v);    // quad_perm [1,0,3,2]
+  v = dpp_swap_add<0x4E>(v);    // quad_perm [2,3,0,1]
+  v = dpp_swap_add<0x141>(v);   // row_half_mirror
+  v = dpp_swap_add<0x140>(v);   // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return ((r0 + r1) + r2) + r3;
 }
 
 // Bounded-wait bookkeeping shared by every polling loop: true (after raising the error word
@@ -354,17 +366,15 @@ INL bool poll_expired(int it, uint32_t* error, int32_t* abort_lds) {
   return false;
 }
 
-// Polls N tagged words per lane (word i only where want[i]) until each carries its tag; the
-// loads of one sweep are all issued before any is tested, so a sweep costs one round trip.
+// Sweeps N tagged words per lane (word i only while !done[i]) until each carries its tag, at
+// most max_sweeps times (0: until done or timed out); the loads of one sweep are all issued
+// before any is tested, so a sweep costs one round trip. Returns whether every word of the wave
+// is in; false after max_sweeps, or after raising the error and abort flags on a time-out
+// (*timed_out then tells the two apart).
 template <int N>
-INL bool wait_words(const tagged_t* const* p, const bool* want, const uint32_t* tag, uint32_t* out,
-                    uint32_t* error, int32_t* abort_lds) {
-  bool done[N];
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    done[i] = !want[i];
-    out[i] = 0;
-  }
+INL bool sweep_words(const tagged_t* const* p, bool* done, const uint32_t* tag, uint32_t* out,
+                     int max_sweeps, uint32_t* error, int32_t* abort_lds, bool* timed_out) {
+  *timed_out = false;
   for (int it = 0;; ++it) {
     tagged_t v[N];
 #pragma unroll
@@ -382,20 +392,42 @@ INL bool wait_words(const tagged_t* const* p, const bool* want, const uint32_t* 
       }
     }
     if (__builtin_amdgcn_ballot_w64(!all) == 0) return true;
-    if (poll_expired(it, error, abort_lds)) return false;
+    if (max_sweeps > 0 && it + 1 >= max_sweeps) return false;
+    if (poll_expired(it, error, abort_lds)) {
+      *timed_out = true;
+      return false;
+    }
     __builtin_amdgcn_s_sleep(2);
   }
+}
+
+// Polls N tagged words per lane (word i only where want[i]) until each carries its tag.
+template <int N>
+INL bool wait_words(const tagged_t* const* p, const bool* want, const uint32_t* tag, uint32_t* out,
+                    uint32_t* error, int32_t* abort_lds) {
+  bool done[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    done[i] = !want[i];
+    out[i] = 0;
+  }
+  bool t;
+  return sweep_words<N>(p, done, tag, out, 0, error, abort_lds, &t);
 }
 
 constexpr int kPosPerThread = (kEngMaxBlocks * 1024 + kEngThreads - 1) / kEngThreads;
 
 // Stage-start duties of a streaming workgroup, run by all nine waves (tid = thread index):
-//  1. every thread fetches its positions of the share's (at most four) 1024-wide input blocks
-//     in one sweep of tagged loads, while the communication wave also fetches the producers'
-//     tile statistics and turns them into RMS denominators;
-//  2. after a barrier every thread rescales its positions to bf16 and stores them to the
-//     staging area; after a second barrier the communication wave copies each block whose
-//     tile-0 unit (of the source's record matrix) this workgroup owns to the caller's record.
+//  1. one optimistic sweep: every thread loads its positions of the share's (at most four)
+//     1024-wide input blocks as tagged words, the communication wave also the producers' tile
+//     statistics. When the producers are done (the usual case away from the critical stage
+//     boundaries) that is the only round trip. Otherwise the communication wave polls the first
+//     row of every producer tile (one small load per round trip instead of the whole share) and
+//     the statistics until they are in, and every thread then sweeps again for its missing words;
+//  2. the communication wave turns the statistics into RMS denominators; after a barrier every
+//     thread rescales its positions to bf16 and stores them to the staging area;
+//  3. after a second barrier the communication wave copies each block whose tile-0 unit (of the
+//     source's record matrix) this workgroup owns to the caller's record.
 // A stage without matrices (the final rescale of a decode step) splits its source's record
 // evenly over the streaming workgroups; the communication wave handles that slice alone.
 // Compute waves (Comm = false) issue no global stores here: a store's registers would make the
@@ -437,77 +469,110 @@ INL void stage_inputs(PP P, EngLds& L, int s, int w, int tid, uint32_t epoch, ui
       valid[j] = kpos[j] < e;
     }
   }
-  if (Comm && live) {
-    // 1. the first row of every producer tile of the staged blocks (both factors of a product
-    //    source), 64 per load, is polled until published: the full sweep below then almost
-    //    always succeeds at once, and the wait costs one small load per round trip instead of
-    //    every thread's whole share of the blocks
-    for (int base = 0; base < nb * 32; base += 64) {
-      const int i = base + lane;
-      const int b = i >> 5, f = (i >> 4) & 1, t = i & 15;
-      bool want = false;
-      const tagged_t* ptr = F0.yt;
-      uint32_t tg = 0, got;
-      if (b < nb) {
-        const int key = blk_get(B, b);
-        const bool o = (key >> 16) != 0;
-        const int kind = o ? F1.kind : F0.kind;
-        const int k = (key & 0xFFFF) * 1024 + t * 64;
-        want = kind != kSrcDirect && k < (o ? F1.k : F0.k) && (f == 0 || kind == kSrcRmsProd);
-        ptr = (f ? (o ? F1.y2t : F0.y2t) : (o ? F1.yt : F0.yt)) + (want ? k : 0);
-        tg = eng_tag(epoch, o ? F1.src_stage : F0.src_stage);
+  // the tagged words of this thread's positions (two per position of a product source);
+  // addresses are rebuilt from the position on each sweep rather than kept in registers
+  constexpr int NW = 2 * kPosPerThread;
+  bool done[NW];
+  uint32_t v[NW];
+  const uint32_t tag0 = eng_tag(epoch, F0.src_stage), tag1 = eng_tag(epoch, F1.src_stage);
+#pragma unroll
+  for (int j = 0; j < kPosPerThread; ++j) {
+    const int kind = one[j] ? F1.kind : F0.kind;
+    const bool tagged = live && valid[j] && kind != kSrcDirect;
+    done[2 * j] = !tagged;
+    done[2 * j + 1] = !(tagged && kind == kSrcRmsProd);
+    v[2 * j] = v[2 * j + 1] = 0;
+  }
+  auto sweep_pos = [&](int max_sweeps) -> bool {
+    for (int it = 0;; ++it) {
+      tagged_t t[NW];
+#pragma unroll
+      for (int i = 0; i < NW; ++i) {
+        const int j = i >> 1;
+        const tagged_t* base = (i & 1) ? (one[j] ? F1.y2t : F0.y2t) : (one[j] ? F1.yt : F0.yt);
+        t[i] = done[i] ? 0 : ld_tag(base + kpos[j]);
       }
-      if (!wait_words<1>(&ptr, &want, &tg, &got, error, &L.abort_flag)) break;
+      bool all = true;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) {
+        if (!done[i]) {
+          if (tag_of(t[i]) == (one[i >> 1] ? tag1 : tag0)) {
+            done[i] = true;
+            v[i] = (uint32_t)t[i];
+          } else {
+            all = false;
+          }
+        }
+      }
+      if (__builtin_amdgcn_ballot_w64(!all) == 0) return true;
+      if (max_sweeps > 0 && it + 1 >= max_sweeps) return false;
+      if (poll_expired(it, error, &L.abort_flag)) return false;
+      __builtin_amdgcn_s_sleep(2);
+    }
+  };
+  // statistics (communication wave): up to 8 x 64 tile statistics per source
+  const tagged_t* sp[8];
+  bool sdone[8];
+  uint32_t stg[8], sv[8];
+  int stat_src = -1;   // the one source whose statistics are needed (at most one RMS source
+                       // per share is rescaled here; a second one gets its own sweep below)
+  bool stats_two = false;
+  if (Comm) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      sdone[i] = true;
+      sp[i] = F0.yt;
+      stg[i] = 0;
+      sv[i] = 0;
     }
     for (int j = 0; j < S->nsrc; ++j) {
       XP X = j ? X1 : X0;
-      float d = 1.f;
       bool used = nb == 0 && slice && j == 0;
       for (int b = 0; b < nb; ++b) used = used || (blk_get(B, b) >> 16) == j;
-      if (live && used && X->kind != kSrcDirect) {
-        const uint32_t tag = eng_tag(epoch, X->src_stage);
-        float part = 0.f;
-        for (int base = 0; base < X->nstats; base += 64 * 8) {
-          const tagged_t* ptr[8];
-          bool want[8];
-          uint32_t tg[8], sv[8];
+      if (!(live && used && X->kind != kSrcDirect)) continue;
+      if (stat_src < 0) stat_src = j;
+      else stats_two = true;
+    }
+    if (stat_src >= 0) {
+      XP X = stat_src ? X1 : X0;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int idx = base + i * 64 + lane;
-            want[i] = idx < X->nstats;
-            ptr[i] = X->stats + (want[i] ? idx : 0);
-            tg[i] = tag;
-          }
-          if (!wait_words<8>(ptr, want, tg, sv, error, &L.abort_flag)) break;
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            if (want[i]) part += __uint_as_float(sv[i]);
-        }
-        d = sqrtf(wave_sum(part) / (float)X->k + X->eps);
+      for (int i = 0; i < 8; ++i) {
+        const int idx = i * 64 + lane;
+        sdone[i] = idx >= X->nstats;
+        sp[i] = X->stats + (sdone[i] ? 0 : idx);
+        stg[i] = eng_tag(epoch, X->src_stage);
       }
-      if (lane == 0) L.denom[j] = d;
     }
   }
-  __syncthreads();
-  // 2. every thread's positions in one sweep of tagged loads (two words per position of a
-  //    product source); the directly given input of a plain source is read as is
-  uint32_t v[2 * kPosPerThread];
-  {
-    const tagged_t* ptr[2 * kPosPerThread];
-    bool want[2 * kPosPerThread];
-    uint32_t tg[2 * kPosPerThread];
-#pragma unroll
-    for (int j = 0; j < kPosPerThread; ++j) {
-      const int kind = one[j] ? F1.kind : F0.kind;
-      const bool tagged = live && valid[j] && kind != kSrcDirect;
-      const int off = tagged ? kpos[j] : 0;
-      ptr[2 * j] = (one[j] ? F1.yt : F0.yt) + off;
-      ptr[2 * j + 1] = (one[j] ? F1.y2t : F0.y2t) + off;
-      want[2 * j] = tagged;
-      want[2 * j + 1] = tagged && kind == kSrcRmsProd;
-      tg[2 * j] = tg[2 * j + 1] = eng_tag(epoch, one[j] ? F1.src_stage : F0.src_stage);
+  bool to;
+  bool ready = sweep_pos(1);
+  if (Comm && stat_src >= 0)
+    ready = sweep_words<8>(sp, sdone, stg, sv, 1, error, &L.abort_flag, &to) && ready;
+  if (__syncthreads_or(ready ? 0 : 1) && live) {
+    if (Comm) {
+      // wait cheaply: the first row of every producer tile of the staged blocks (both factors
+      // of a product source), 64 per load, then the statistics
+      for (int base = 0; base < nb * 32; base += 64) {
+        const int i = base + lane;
+        const int b = i >> 5, f = (i >> 4) & 1, t = i & 15;
+        bool want = false;
+        const tagged_t* q = F0.yt;
+        uint32_t qt = 0, got;
+        if (b < nb) {
+          const int key = blk_get(B, b);
+          const bool o = (key >> 16) != 0;
+          const int kind = o ? F1.kind : F0.kind;
+          const int k = (key & 0xFFFF) * 1024 + t * 64;
+          want = kind != kSrcDirect && k < (o ? F1.k : F0.k) && (f == 0 || kind == kSrcRmsProd);
+          q = (f ? (o ? F1.y2t : F0.y2t) : (o ? F1.yt : F0.yt)) + (want ? k : 0);
+          qt = eng_tag(epoch, o ? F1.src_stage : F0.src_stage);
+        }
+        if (!wait_words<1>(&q, &want, &qt, &got, error, &L.abort_flag)) break;
+      }
+      if (stat_src >= 0) sweep_words<8>(sp, sdone, stg, sv, 0, error, &L.abort_flag, &to);
     }
-    wait_words<2 * kPosPerThread>(ptr, want, tg, v, error, &L.abort_flag);
+    __syncthreads();
+    sweep_pos(0);
   }
   uint32_t direct[kPosPerThread];
 #pragma unroll
@@ -524,7 +589,48 @@ INL void stage_inputs(PP P, EngLds& L, int s, int w, int tid, uint32_t epoch, ui
     // (ring copies in compute waves, partial stores in the communication wave).
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt and lgkmcnt untouched
   }
-  // 3. rescale and stage (the slice of a matrix-free stage goes straight to the record)
+  if (Comm) {
+    // 2. denominators sqrt(mean(h^2) + eps) from the producers' tile statistics
+    float d0 = 1.f, d1 = 1.f;
+    if (stat_src >= 0) {
+      XP X = stat_src ? X1 : X0;
+      float part = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (i * 64 + lane < X->nstats) part += __uint_as_float(sv[i]);
+      const float d = sqrtf(wave_sum(part) / (float)X->k + X->eps);
+      if (stat_src) d1 = d;
+      else d0 = d;
+    }
+    if (stats_two && live) {   // both sources rescaled here: the second one's statistics
+      XP X = X1;
+      const uint32_t tag = eng_tag(epoch, X->src_stage);
+      float part = 0.f;
+      for (int base = 0; base < X->nstats; base += 64 * 8) {
+        const tagged_t* q[8];
+        bool want[8];
+        uint32_t qt[8], qv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int idx = base + i * 64 + lane;
+          want[i] = idx < X->nstats;
+          q[i] = X->stats + (want[i] ? idx : 0);
+          qt[i] = tag;
+        }
+        if (!wait_words<8>(q, want, qt, qv, error, &L.abort_flag)) break;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (want[i]) part += __uint_as_float(qv[i]);
+      }
+      d1 = sqrtf(wave_sum(part) / (float)X->k + X->eps);
+    }
+    if (lane == 0) {
+      L.denom[0] = d0;
+      L.denom[1] = d1;
+    }
+  }
+  __syncthreads();
+  // rescale and stage (the slice of a matrix-free stage goes straight to the record)
 #pragma unroll
   for (int j = 0; j < kPosPerThread; ++j) {
     const int kind = one[j] ? F1.kind : F0.kind;
@@ -540,7 +646,7 @@ INL void stage_inputs(PP P, EngLds& L, int s, int w, int tid, uint32_t epoch, ui
   }
   __syncthreads();
   if (Comm && live) {
-    // records of the blocks this workgroup owns, from the staged (exactly bf16) values
+    // 3. records of the blocks this workgroup owns, from the staged (exactly bf16) values
     for (int b = 0; b < nb; ++b) {
       const int key = blk_get(B, b);
       const int src = key >> 16, sg = key & 0xFFFF;
@@ -613,7 +719,7 @@ INL void wait_ring(int ahead) {
     default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
   }
 }
-static_assert(kEngRing == 8, "wait_ring covers a ring of eight slots");
+static_assert(kEngRing == 8 && kEngSlots == 8, "the unit loop assumes eight ring and hand-off slots");
 
 // First stage >= s whose end holds prefetching back (its last partial goes out first).
 INL int next_gate(PP P, int s) {
@@ -630,6 +736,7 @@ INL void compute_wave(PP P, EngLds& L, int w, int lane, uint32_t epoch, uint32_t
   cur_stage<V, false>(P, pf, w, 0);
   cur_stage<V, true>(P, cu, w, 0);
   unsigned issued = 0, cnt = 0;
+  const int nst_all = P->nstages;
   int gate = next_gate(P, 0);
   // refill: keep up to kRing units in flight, never past the gate stage
   auto refill = [&]() {
@@ -665,7 +772,10 @@ INL void compute_wave(PP P, EngLds& L, int w, int lane, uint32_t epoch, uint32_t
       const int ps = cnt % kEngSlots;
       const unsigned round = cnt / kEngSlots;
       const uint32_t fr = lds_poll(&L.freed[ps]);   // read early, tested after the lookups
-      wait_ring((int)(issued - cnt) - 1);
+      if (__builtin_expect(issued - cnt == (unsigned)kRing, 1))
+        asm volatile("s_waitcnt vmcnt(14)" ::: "memory");   // steady state: a full ring
+      else
+        wait_ring((int)(issued - cnt) - 1);
       float partial = 0.f;
       if (cu.ok) {
         const uint32_t* rw = &L.ring_w[V][slot][lane * 4];
@@ -694,7 +804,11 @@ INL void compute_wave(PP P, EngLds& L, int w, int lane, uint32_t epoch, uint32_t
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       ++cnt;
       cur_next<V, true>(P, cu, w);
-      refill();
+      if (pf.s < nst_all && pf.s <= gate) {   // steady state: one copy per consumed unit
+        issue_unit<V>(P, pf, L, issued % kRing, voff_w, voff_s);
+        ++issued;
+        cur_next<V, false>(P, pf, w);
+      }
     }
   }
   // let any copy still in flight land before the wave ends
@@ -781,44 +895,38 @@ INL void finalize_item(SP S, EngLds& L, int s, int item, int lane, uint32_t epoc
   const int tile = item - M->item_base;
   const int m2 = M->pair;
   MP M2 = &S->mat[m2 < 0 ? m : m2];
-  const int s1 = M->supers, s2 = m2 < 0 ? 0 : M2->supers;
+  // the block partials of this item: n of them, the first s1 from M; loaded once, kept scalar
+  const int s1 = rfl(M->supers), n = s1 + (m2 < 0 ? 0 : rfl(M2->supers));
+  const int ub1 = rfl(M->unit_base) + tile, t1 = rfl(M->tiles);
+  const int ub2 = rfl(M2->unit_base) + tile - s1 * rfl(M2->tiles), t2 = rfl(M2->tiles);
+  const tagged_t* part = rfl(S->part);
   const uint32_t tag = eng_tag(epoch, s);
   {
     // wait cheaply first: lane i watches the first word of block partial i (one small load per
     // round trip), then read every lane's words, which are then almost always all there
-    const bool want = lane < s1 + s2;
-    const int u = lane < s1 ? M->unit_base + lane * M->tiles + tile
-                            : M2->unit_base + (lane - s1) * M2->tiles + tile;
-    const tagged_t* ptr = S->part + (size_t)(want ? u : 0) * 64;
+    const bool want = lane < n;
+    const int u = lane < s1 ? ub1 + lane * t1 : ub2 + lane * t2;
+    const tagged_t* ptr = part + (size_t)(want ? u : 0) * 64;
     uint32_t got;
     if (!wait_words<1>(&ptr, &want, &tag, &got, error, &L.abort_flag)) return;
   }
-  const tagged_t* pb = S->part + lane;
+  // full sweeps: every word of the n partials is loaded on every sweep (a retry is rare), so
+  // the loads need no per-lane branches
+  const tagged_t* pb = part + lane;
   uint32_t v[kEngMaxFinal];
-  bool done[kEngMaxFinal];
 #pragma unroll
-  for (int i = 0; i < kEngMaxFinal; ++i) {
-    done[i] = i >= s1 + s2;
-    v[i] = 0;
-  }
+  for (int i = 0; i < kEngMaxFinal; ++i) v[i] = 0;
   for (int it = 0;; ++it) {
     tagged_t t[kEngMaxFinal];
 #pragma unroll
-    for (int i = 0; i < kEngMaxFinal; ++i) {
-      const int u = i < s1 ? M->unit_base + i * M->tiles + tile
-                           : M2->unit_base + (i - s1) * M2->tiles + tile;
-      t[i] = done[i] ? 0 : ld_tag(pb + (size_t)u * 64);
-    }
+    for (int i = 0; i < kEngMaxFinal; ++i)
+      if (i < n) t[i] = ld_tag(pb + (size_t)(i < s1 ? ub1 + i * t1 : ub2 + i * t2) * 64);
     bool all = true;
 #pragma unroll
     for (int i = 0; i < kEngMaxFinal; ++i) {
-      if (!done[i]) {
-        if (tag_of(t[i]) == tag) {
-          done[i] = true;
-          v[i] = (uint32_t)t[i];
-        } else {
-          all = false;
-        }
+      if (i < n) {
+        all = all && tag_of(t[i]) == tag;
+        v[i] = (uint32_t)t[i];
       }
     }
     if (__builtin_amdgcn_ballot_w64(!all) == 0) break;
@@ -829,29 +937,33 @@ INL void finalize_item(SP S, EngLds& L, int s, int item, int lane, uint32_t epoc
 #pragma unroll
   for (int i = 0; i < kEngMaxFinal; ++i) {
     if (i < s1) y1 += __uint_as_float(v[i]);
-    else if (i < s1 + s2) y2 += __uint_as_float(v[i]);
+    else if (i < n) y2 += __uint_as_float(v[i]);
   }
+  // outputs: tagged copies and statistics first (consumers wait on them), plain copies last
   const int row = tile * kTileRows + lane;
   const uint32_t b1 = e_to_bf16(y1);
-  st_tag(M->yt + row, b1, tag);
-  if (M->kind == kMatSumSq) {
-    const float yv = row < M->n ? e_bf16(b1) : 0.f;
+  st_tag(rfl(M->yt) + row, b1, tag);
+  const int n1 = rfl(M->n);
+  if (rfl(M->kind) == kMatSumSq) {
+    const float yv = row < n1 ? e_bf16(b1) : 0.f;
     const float ss = wave_sum(yv * yv);
-    if (lane == 0) st_tag(M->stat + tile, __float_as_uint(ss), tag);
+    if (lane == 0) st_tag(rfl(M->stat) + tile, __float_as_uint(ss), tag);
   }
   uint32_t b2 = 0;
+  const int n2 = rfl(M2->n);
   if (m2 >= 0) {
     b2 = e_to_bf16(y2);
-    st_tag(M2->yt + row, b2, tag);
-    if (M2->kind == kMatPair) {
-      const float h = row < M2->n ? e_bf16(b1) * e_bf16(b2) : 0.f;
+    st_tag(rfl(M2->yt) + row, b2, tag);
+    if (rfl(M2->kind) == kMatPair) {
+      const float h = row < n2 ? e_bf16(b1) * e_bf16(b2) : 0.f;
       const float ss = wave_sum(h * h);
-      if (lane == 0) st_tag(M2->stat + tile, __float_as_uint(ss), tag);
+      if (lane == 0) st_tag(rfl(M2->stat) + tile, __float_as_uint(ss), tag);
     }
   }
-  // the caller's plain copies last: they are off the critical path
-  if (M->y && row < M->n) g_st16(M->y + row, b1);
-  if (m2 >= 0 && M2->y && row < M2->n) g_st16(M2->y + row, b2);
+  uint16_t* y1p = rfl(M->y);
+  uint16_t* y2p = rfl(M2->y);
+  if (y1p && row < n1) g_st16(y1p + row, b1);
+  if (m2 >= 0 && y2p && row < n2) g_st16(y2p + row, b2);
 }
 
 // Finalising wave c of nc: items c, c + nc, ... of every stage, in program order.
