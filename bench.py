@@ -6,7 +6,7 @@ A step is one decode step of the whole stream: 64 layers x (q, o 5120x5120; k, v
 gate, up 17408x5120; down 5120x17408) Q1_0_g128 GEMVs with the RMS rescales between them
 (lbq_decode_step_q1g128), over seeded synthetic weights (sign bits Bernoulli(0.5), fp16 scales
 |N(0, 0.02)|) and a bf16 N(0, 1) input, all resident in HBM before timing starts. At batch 1 a
-step is one cooperative launch of the persistent engine; larger batches replay a HIP graph of
+step is one launch of the persistent engine; larger batches replay a HIP graph of
 the per-projection launches. W untimed warm-up steps precede exactly K timed steps bracketed
 by device synchronisation.
 
@@ -140,7 +140,7 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
     graph = None
-    if not args.no_graph and B > 1:   # batch 1 is a single cooperative launch per step
+    if not args.no_graph and B > 1:   # batch 1 is a single persistent launch per step
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             step()
@@ -172,7 +172,7 @@ def main() -> int:
 
     # ---- dominant kernel ---------------------------------------------------------------------
     if B == 1:
-        kern_name = "q1_engine_kernel (whole decode step, one cooperative launch)"
+        kern_name = "q1_engine_kernel (whole decode step, one persistent launch)"
         kern_avg_ms, kern_bytes = step_kernel_ms, bytes_per_step
     else:
         # host-driven step: every Q1 GEMV launch of a step bracketed by events

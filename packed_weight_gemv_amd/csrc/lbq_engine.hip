@@ -1,6 +1,6 @@
-// lbq_engine.hip - persistent streaming engine for Q1_0_g128 GEMV programs at batch 1 (one
-// cooperative launch per program), used for the whole decode step of a layer stack and for
-// single batch-1 GEMVs.
+// lbq_engine.hip - persistent streaming engine for Q1_0_g128 GEMV programs at batch 1: one
+// launch per program, one workgroup per compute unit. It runs the whole decode step of a layer
+// stack and single batch-1 GEMVs.
 //
 // Workgroup = 8 compute waves + 1 communication wave, one workgroup per CU.
 //  * Work unit = 64 rows (one lane per row) x one block of eight 128-weight groups; compute wave
