@@ -2,7 +2,7 @@
 //
 // A program is a list of stages. A stage multiplies up to kEngMaxMats Q1_0_g128 matrices with
 // up to kEngMaxSrcs bf16 input vectors (batch 1); the outputs of a stage may feed the inputs of
-// later stages through an RMS rescale. One cooperative launch runs the whole program. Streaming
+// later stages through an RMS rescale. One persistent launch runs the whole program. Streaming
 // workgroups each own an equal, contiguous share of every part of every stage's work units
 // (64 rows x one block of eight 128-weight groups) and publish one partial sum per unit;
 // finalising workgroups (no weight traffic, so their memory round trips stay short) sum the
@@ -19,10 +19,14 @@ namespace lbq {
 
 constexpr int kEngMaxMats = 5;
 constexpr int kEngMaxSrcs = 2;
-constexpr int kEngWaves = 8;                        // compute waves: one group of a block each
-constexpr int kEngThreads = (kEngWaves + 1) * 64;   // + one communication wave
-constexpr int kEngRing = 8;                         // weight records in flight per compute wave
-constexpr int kEngSlots = 8;                        // partial hand-off slots (compute -> comm)
+constexpr int kEngPairs = 4;                        // group pairs of a unit (two groups per wave)
+constexpr int kEngPhases = 3;                       // units a workgroup computes at once
+constexpr int kEngCompute = kEngPairs * kEngPhases; // compute waves
+constexpr int kEngWaves = kEngCompute + 2;          // + one loader wave + one communication wave
+constexpr int kEngThreads = kEngWaves * 64;
+constexpr int kEngRingSlots = 9;                    // units the LDS ring holds
+constexpr int kEngInFlight = 2;                     // units the loader keeps in flight
+constexpr int kEngHandSlots = 4;                    // partial hand-off slots (compute -> comm)
 constexpr int kEngMaxStages = 255;
 constexpr int kEngMaxFinal = 24;                    // block partials summed by one finalisation
 constexpr int kEngMaxBlocks = 4;                    // input blocks one workgroup stages per stage
@@ -62,8 +66,7 @@ struct EngStage {
   tagged_t* part;                      // tagged unit partials [units * 64], one slot per unit
   int32_t nmat, nsrc, units, nitems;   // nitems: tiles to finalise (a pair counts once)
   int32_t part0;                       // units of part 0 (the leading matrices); rest = part 1
-  int32_t drain;                       // publish this stage's last partial before prefetching on
-  int32_t pad0, pad1;
+  int32_t pad0, pad1, pad2;
 };
 
 struct EngProgram {

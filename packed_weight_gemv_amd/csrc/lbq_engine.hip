@@ -2,27 +2,35 @@
 // launch per program, one workgroup per compute unit. It runs the whole decode step of a layer
 // stack and single batch-1 GEMVs.
 //
-// Workgroup = 8 compute waves + 1 communication wave, one workgroup per CU.
-//  * Work unit = 64 rows (one lane per row) x one block of eight 128-weight groups; compute wave
-//    v always handles group v of the block, so its lookup tables sit at compile-time LDS offsets.
-//  * Compute waves stream their 16-byte sign records and scale words straight into an LDS ring
-//    (global_load_lds), kRing units ahead, across stage boundaries: weights never depend on
-//    activations, so the ring keeps HBM busy while a stage waits for its inputs.
-//  * Per 4 weights a compute wave adds one entry of a 16-entry table of signed sums of 4 inputs
-//    (built in LDS from the stage's input vector); the 4-bit field times 4 is the entry's byte
-//    offset, extracted with one masked operand select (the packer stores each sign dword
-//    rotated left by two so every field sits at bits [8i+2, 8i+5] of the dword or of its
-//    rotation by four).
-//  * The communication wave sums the 8 group partials of a unit and publishes the unit partial
-//    as a (value, tag) word in the stage's partial array, without waiting on global memory.
-//    Once its units are done, each workgroup finalises its round-robin share of the stage's
-//    output tiles (a gate tile together with the matching up tile, so the pair statistic needs
-//    no second exchange), polling the block partials of a tile in one sweep.
-//  * At a stage start all nine waves fetch the stage's input blocks in one sweep of tagged
-//    loads (the communication wave fetches the producers' tile statistics in the same trip)
-//    and apply the RMS rescale. Consumers poll tags; there is no grid barrier and no cache
-//    flush. Every wait is bounded: on a time-out the error word is set and every wave runs to
-//    the end without further work.
+// A streaming workgroup has 12 compute waves, one loader wave and one communication wave.
+//  * Work unit = 64 rows (one lane per row) x one super-group of eight 128-weight groups: 9 KiB
+//    of contiguous device-layout bytes (the 64 x 8 fp16 scales, then one sign record per group).
+//    Each workgroup owns an equal, contiguous share of every stage's units and walks its shares
+//    in program order.
+//  * The loader wave copies units straight into an LDS ring with nontemporal global_load_lds,
+//    keeping only kEngInFlight units in flight. That is enough for the compute unit's share of
+//    HBM bandwidth, and it keeps the queue in front of the workgroup's other memory operations
+//    (input loads, partial stores) short. The ring itself is deeper, so the copies run ahead
+//    across stage boundaries while a stage waits for its inputs. Weights never depend on
+//    activations.
+//  * Compute wave (pair p, phase f) handles groups 2p and 2p+1 of the units whose position in
+//    the sequence is f modulo 3, so three units are computed at once. It does no global
+//    memory access at all in its unit loop: per 4 weights it adds one entry of a 16-entry table
+//    of signed sums of 4 inputs, built in LDS from the stage's input vector. The 4-bit field
+//    times 4 is the entry's byte offset, extracted with one masked operand select: the packer
+//    stores each sign dword rotated left by two, so every field sits at bits [8i+2, 8i+5] of the
+//    dword or of its rotation by four.
+//  * The communication wave sums the four pair partials of each unit and publishes the unit
+//    partial as a (value, tag) word in the stage's partial array.
+//  * Finalising workgroups (no weight traffic, so their memory round trips stay short) sum the
+//    partials of each output tile and publish the outputs and their statistics; a gate tile is
+//    finalised together with the matching up tile, so the pair statistic needs no second
+//    exchange.
+//  * At a stage start the compute and communication waves fetch the stage's input blocks in one
+//    sweep of tagged loads (the communication wave fetches the producers' tile statistics in the
+//    same trip) and apply the RMS rescale. Consumers poll tags; there is no grid barrier and no
+//    cache flush. Every wait is bounded: on a time-out the error word is set and every wave runs
+//    to the end without further work.
 #include <hip/hip_runtime.h>
 #include <stdlib.h>
 #include <string.h>
@@ -48,7 +56,6 @@ typedef const AS_CONST EngStage* SP;
 typedef const AS_CONST EngMat* MP;
 typedef const AS_CONST EngSrc* XP;
 
-constexpr int kRing = kEngRing;
 constexpr int kPollLimit = 1 << 20;   // bounded waits: ~1 s at worst, microseconds normally
 
 INL float e_bf16(uint32_t v) { return __uint_as_float(v << 16); }
@@ -120,24 +127,20 @@ INL void set_err(uint32_t* p) {
   __hip_atomic_store((AS_GLOBAL uint32_t*)p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// LDS-direct loads of one ring slot (a sign record and a scale word per lane), issued from asm
-// so the compiler does not guard every later LDS read with a full vmcnt wait; the ring waits
-// are explicit. Scalar base + per-lane 32-bit offset; no VGPR is written; m0 is restored.
-// Weights are read once per launch: the copies are nontemporal, so they neither evict the
-// small, hot exchange data (unit partials, outputs, statistics) from the caches nor wait behind
-// it.
-INL void dma_slot(const void* base, uint32_t voff_w, uint32_t voff_s, uint32_t lds_w,
-                  uint32_t lds_s) {
+// LDS-direct copy of one 1 KiB chunk (16 bytes per lane, base + voff) to LDS address `lds`,
+// issued from asm so that the compiler does not guard later LDS accesses with vector-memory
+// waits; the loader's waits are explicit. No VGPR is written; m0 is restored. Weights are read
+// once per launch: the copies are nontemporal, so they do not evict the small, hot exchange
+// data (unit partials, outputs, statistics) from the caches.
+INL void dma_chunk(const void* base, uint32_t voff, uint32_t lds) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dwordx4 %3, %5 nt\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dword %4, %5 nt\n\t"
+      "global_load_lds_dwordx4 %2, %3 nt\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(lds_w), "s"(lds_s), "v"(voff_w), "v"(voff_s), "s"(base)
+      : "s"(lds), "v"(voff), "s"(base)
       : "memory");
 }
 // LDS words polled by one wave and written by another: workgroup-scope atomic loads keep them
@@ -149,25 +152,42 @@ INL uint32_t lds_poll(const uint32_t* p) {
 INL int32_t lds_poll_i(const int32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
+INL void lds_set(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
 template <typename T>
 INL uint32_t lds_addr(T* p) {
   return (uint32_t)(uintptr_t)p;
 }
 
+constexpr int kUnitBytes = kBlock * (1 + kSuper);        // one unit: scales + eight records
+constexpr int kGatherWaves = kEngCompute + 1;              // compute waves + communication wave
+constexpr int kGatherThreads = kGatherWaves * 64;
+constexpr int kLoaderWave = kEngCompute;
+
+// Ring slot bookkeeping the loader writes before a unit's copy and the compute waves read.
+struct SlotMeta {
+  int32_t blk;   // staging block holding the unit's inputs
+  int32_t ng;    // groups present in the unit's super-group (eight unless K ends inside it)
+};
+
 // The lookup tables come first: every table entry's LDS address then fits the 16-bit
 // immediate offset of ds_read, so a lookup's address is the extracted field alone.
 struct __attribute__((aligned(16))) EngLds {
-  float lut[kEngWaves][32 * 16];               // [group][chunk*16 + entry] of the current block
-  uint32_t ring_w[kEngWaves][kRing][64 * 4];   // sign records
-  uint32_t ring_s[kEngWaves][kRing][64];       // scale words
-  float staging[kEngMaxBlocks][1024];          // the stage's input blocks (exact bf16 values)
-  // compute -> comm hand-off: per lane (partial bits | (round + 1) << 32), one 64-bit store
-  unsigned long long part[kEngSlots][kEngWaves][64];
-  uint32_t freed[kEngSlots];                   // rounds of each slot the comm wave has consumed
+  float lut[kEngCompute][2][32 * 16];                  // [compute wave][group of its pair][chunk*16 + entry]
+  float staging[kEngMaxBlocks][1024];                  // the stage's input blocks (exact bf16 values)
+  unsigned long long hand[kEngHandSlots][kEngPairs][64];   // compute -> comm: (partial | (round + 1) << 32)
+  uint8_t ring[kEngRingSlots][kUnitBytes];             // units copied by the loader
+  SlotMeta meta[kEngRingSlots];
+  uint32_t consumed[kEngRingSlots];                    // compute-wave reads of each slot so far
+  uint32_t hfree[kEngHandSlots];                       // hand-off rounds the comm wave has consumed
+  uint32_t ready;                                      // units [0, ready) of the sequence have landed
+  uint32_t bar_count, bar_gen;                         // barrier of the gathering waves
+  int32_t need_poll;                                   // stage + 1 once a gathering wave missed a word
   float denom[kEngMaxSrcs];
-  int32_t published;                           // last stage whose partials were all issued
   int32_t abort_flag;
 };
+static_assert(sizeof(EngLds) <= 160 * 1024, "the engine's LDS must fit one compute unit");
 
 // A streaming workgroup's units of a stage: range [a0, b0) of part 0, then [a1, b1) of part 1.
 struct Share {
@@ -236,82 +256,6 @@ INL Blocks stage_blocks(SP S, const Share& r) {
   blk_range(S, B, r.a0, r.b0);
   blk_range(S, B, r.a1, r.b1);
   return B;
-}
-
-// Per-wave cursor over the streaming workgroup's units of all stages, in program order, in
-// scalar registers. A segment is a run of consecutive tiles of one (matrix, super-group)
-// column; its units lie tile_bytes apart, so stepping inside a segment is one 64-bit add.
-struct Cursor {
-  int s;              // stage (nstages once exhausted)
-  int left;           // units left in the current segment, this one included
-  int u;              // stage unit of the current unit
-  int rend;           // end of the current range
-  int na, nb;         // the part-1 range still to come ([na, nb), empty once entered)
-  Blocks B;           // the stage's block list (compute cursor only)
-  int b;              // block index of the current segment (compute cursor only)
-  const uint8_t* p;   // super-group record of the current unit
-  uint32_t step;      // tile_bytes of the segment's matrix
-  bool ok;            // this wave's group exists in the segment's super-group
-};
-
-template <int V, bool Blk>
-INL void cur_segment(SP S, Cursor& c) {
-  const UnitPos q = unit_pos(S, c.u);
-  MP M = &S->mat[q.m];
-  c.left = min(M->tiles - q.tile, c.rend - c.u);
-  c.step = (uint32_t)M->tile_bytes;
-  c.p = M->w + (size_t)q.tile * (size_t)c.step + (size_t)q.sg * (kBlock * (1 + kSuper));
-  c.ok = q.sg * kSuper + V < M->groups;
-  if (Blk) c.b = blk_find(c.B, blk_key(M->src, q.sg));
-}
-
-template <int V, bool Blk>
-INL void cur_stage(PP P, Cursor& c, int w, int s) {
-  for (; s < P->nstages; ++s) {
-    SP S = &P->st[s];
-    const Share r = stage_share(S, w, P->nstream);
-    if (share_units(r) == 0) continue;
-    c.s = s;
-    if (Blk) c.B = stage_blocks(S, r);
-    if (r.b0 > r.a0) {
-      c.u = r.a0;
-      c.rend = r.b0;
-      c.na = r.a1;
-      c.nb = r.b1;
-    } else {
-      c.u = r.a1;
-      c.rend = r.b1;
-      c.na = c.nb = 0;
-    }
-    cur_segment<V, Blk>(S, c);
-    return;
-  }
-  c.s = P->nstages;
-  c.left = 0;
-  c.u = c.rend = c.na = c.nb = 0;
-  c.ok = false;
-  c.b = 0;
-  c.p = nullptr;
-  c.step = 0;
-}
-
-template <int V, bool Blk>
-INL void cur_next(PP P, Cursor& c, int w) {
-  if (c.left > 1) {
-    --c.left;
-    ++c.u;
-    c.p += c.step;
-  } else if (c.u + 1 < c.rend) {
-    ++c.u;
-    cur_segment<V, Blk>(&P->st[c.s], c);
-  } else if (c.nb > c.na) {
-    c.u = c.na;
-    c.rend = c.nb;
-    c.na = c.nb = 0;
-    cur_segment<V, Blk>(&P->st[c.s], c);
-  } else if (c.s < P->nstages) {
-    cur_stage<V, Blk>(P, c, w, c.s + 1);
-  }
 }
 
 // Pulls a stage descriptor into the scalar cache with one batch of loads (one round trip)
@@ -415,261 +359,305 @@ INL bool wait_words(const tagged_t* const* p, const bool* want, const uint32_t* 
   return sweep_words<N>(p, done, tag, out, 0, error, abort_lds, &t);
 }
 
-constexpr int kPosPerThread = (kEngMaxBlocks * 1024 + kEngThreads - 1) / kEngThreads;
+// Barrier of the gathering waves (the compute waves and the communication wave; the loader
+// never joins): the last to arrive resets the count and advances the generation. `gen` counts
+// the barriers the calling wave has passed. Bounded like every wait.
+INL void gather_barrier(EngLds& L, int lane, uint32_t& gen, uint32_t* error) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  uint32_t old = 0;
+  if (lane == 0)
+    old = __hip_atomic_fetch_add(&L.bar_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  old = __builtin_amdgcn_readfirstlane(old);
+  if (old == kGatherWaves - 1) {
+    if (lane == 0) {
+      __hip_atomic_store(&L.bar_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_store(&L.bar_gen, gen + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  } else {
+    for (int it = 0; lds_poll(&L.bar_gen) == gen; ++it) {
+      if (poll_expired(it, error, &L.abort_flag)) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  ++gen;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
 
-// Stage-start duties of a streaming workgroup, run by all nine waves (tid = thread index):
+constexpr int kPosPerThread = (kEngMaxBlocks * 1024 + kGatherThreads - 1) / kGatherThreads;
+
+// Tagged word idx of a uniform base (32-bit index: the load takes a scalar base and a vector
+// offset).
+INL tagged_t ld_tag_at(const tagged_t* base, uint32_t idx) {
+  return ld_tag((const tagged_t*)((const char*)base + (size_t)(idx * 8u)));
+}
+
+// Polls the n tagged statistics base[0, n) (n <= 512: eight per lane, index i * 64 + lane)
+// until each carries `tag`, at most max_sweeps times (0: until done or timed out). `pend` holds
+// the missing ones (bit i); sv[i] receives the payloads. Returns whether the wave has them all.
+INL bool sweep_stats(const tagged_t* base, int n, uint32_t tag, uint32_t& pend, uint32_t (&sv)[8],
+                     int lane, int max_sweeps, EngLds& L, uint32_t* error) {
+  for (int it = 0;; ++it) {
+    tagged_t t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = ((pend >> i) & 1u) ? ld_tag_at(base, (uint32_t)(i * 64 + lane)) : 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (((pend >> i) & 1u) && tag_of(t[i]) == tag) {
+        pend &= ~(1u << i);
+        sv[i] = (uint32_t)t[i];
+      }
+    }
+    if (__builtin_amdgcn_ballot_w64(pend != 0) == 0) return true;
+    if (max_sweeps > 0 && it + 1 >= max_sweeps) return false;
+    if (poll_expired(it, error, &L.abort_flag)) return false;
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+INL uint32_t stats_pending(int n, int lane) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (i * 64 + lane < n) m |= 1u << i;
+  return m;
+}
+// sqrt(mean(h^2) + eps) from the tile statistics: per-lane sums in index order, then the
+// fixed-order wave sum (identical in every workgroup).
+INL float stats_denominator(const uint32_t (&sv)[8], int n, int k, float eps, int lane) {
+  float part = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (i * 64 + lane < n) part += __uint_as_float(sv[i]);
+  return sqrtf(wave_sum(part) / (float)k + eps);
+}
+
+// Stage-start duties of a streaming workgroup, run by every gathering wave (tid = its thread
+// index among them; the communication wave has the last 64). A stage reads one source vector.
 //  1. one optimistic sweep: every thread loads its positions of the share's (at most four)
-//     1024-wide input blocks as tagged words, the communication wave also the producers' tile
-//     statistics. When the producers are done (the usual case away from the critical stage
-//     boundaries) that is the only round trip. Otherwise the communication wave polls the first
-//     row of every producer tile (one small load per round trip instead of the whole share) and
-//     the statistics until they are in, and every thread then sweeps again for its missing words;
-//  2. the communication wave turns the statistics into RMS denominators; after a barrier every
-//     thread rescales its positions to bf16 and stores them to the staging area;
+//     1024-wide input blocks as tagged words (both factors of a product source), the
+//     communication wave also the producers' tile statistics, and, when they are all in, it
+//     turns them into the RMS denominator. When the producers are done, the usual case away
+//     from the critical stage boundaries, that is the only round trip. Otherwise the
+//     communication wave polls the first row of every producer tile (one small load per round
+//     trip instead of the whole share) and the statistics until they are in, and every thread
+//     then sweeps again for its missing words;
+//  2. after a barrier every thread rescales its positions to bf16 and stores them to the
+//     staging area;
 //  3. after a second barrier the communication wave copies each block whose tile-0 unit (of the
 //     source's record matrix) this workgroup owns to the caller's record.
-// A stage without matrices (the final rescale of a decode step) splits its source's record
-// evenly over the streaming workgroups; the communication wave handles that slice alone.
-// Compute waves (Comm = false) issue no global stores here: a store's registers would make the
-// compiler wait for every outstanding load, ring copies included, before the next LDS read.
-template <bool Comm>
-INL void stage_inputs(PP P, EngLds& L, int s, int w, int tid, uint32_t epoch, uint32_t* error) {
+// Compute waves issue no global stores here (and none anywhere else).
+INL void stage_inputs(PP P, EngLds& L, int s, int w, int tid, bool comm, uint32_t epoch,
+                      uint32_t* error, uint32_t& gen) {
   SP S = &P->st[s];
-  XP X0 = &S->src[0];
-  XP X1 = &S->src[1];
+  XP X = &S->src[0];
   const int nst = P->nstream;
   const int lane = tid & 63;
   const Share r = stage_share(S, w, nst);
   const Blocks B = stage_blocks(S, r);
-  if (Comm && B.n > kEngMaxBlocks) {
+  if (comm && B.n > kEngMaxBlocks) {
     set_err(error);
     L.abort_flag = 1;
   }
   const int nb = B.n > kEngMaxBlocks ? 0 : B.n;
   const bool live = lds_poll_i(&L.abort_flag) == 0;
-  const bool slice = S->nmat == 0 && S->nsrc > 0 && X0->record != nullptr;
-  const SrcFields F0 = src_fields(X0), F1 = src_fields(X1);
-  int kpos[kPosPerThread];
-  bool one[kPosPerThread], valid[kPosPerThread];
+  const SrcFields F = src_fields(X);
+  const bool direct = F.kind == kSrcDirect, prod = F.kind == kSrcRmsProd;
+  const uint32_t tag = eng_tag(epoch, F.src_stage);
+  // this thread's positions: kpos[j] for p = tid + j * kGatherThreads; bit j of vmask when the
+  // position exists (inside a staged block and below K); bit i of pend while word i (position
+  // i >> 1, factor i & 1) is missing
+  uint32_t kpos[kPosPerThread];
+  uint32_t vmask = 0, pend = 0;
 #pragma unroll
   for (int j = 0; j < kPosPerThread; ++j) {
     kpos[j] = 0;
-    one[j] = false;
-    valid[j] = false;
-    const int p = tid + kEngThreads * j;
+    const int p = tid + kGatherThreads * j;
     if (p < nb * 1024) {
-      const int key = blk_get(B, p >> 10);
-      one[j] = (key >> 16) != 0;
-      kpos[j] = (key & 0xFFFF) * 1024 + (p & 1023);
-      valid[j] = kpos[j] < (one[j] ? F1.k : F0.k);
-    } else if (Comm && nb == 0 && slice && j < 4) {
-      const int K = F0.k;
-      const int a = (K * w) / nst, e = (K * (w + 1)) / nst;
-      kpos[j] = a + lane + 64 * j;
-      valid[j] = kpos[j] < e;
+      const int k = (blk_get(B, p >> 10) & 0xFFFF) * 1024 + (p & 1023);
+      if (k < F.k) {
+        kpos[j] = (uint32_t)k;
+        vmask |= 1u << j;
+        if (live && !direct) pend |= (prod ? 3u : 1u) << (2 * j);
+      }
     }
   }
-  // the tagged words of this thread's positions (two per position of a product source);
-  // addresses are rebuilt from the position on each sweep rather than kept in registers
   constexpr int NW = 2 * kPosPerThread;
-  bool done[NW];
   uint32_t v[NW];
-  const uint32_t tag0 = eng_tag(epoch, F0.src_stage), tag1 = eng_tag(epoch, F1.src_stage);
 #pragma unroll
-  for (int j = 0; j < kPosPerThread; ++j) {
-    const int kind = one[j] ? F1.kind : F0.kind;
-    const bool tagged = live && valid[j] && kind != kSrcDirect;
-    done[2 * j] = !tagged;
-    done[2 * j + 1] = !(tagged && kind == kSrcRmsProd);
-    v[2 * j] = v[2 * j + 1] = 0;
-  }
+  for (int i = 0; i < NW; ++i) v[i] = 0;
   auto sweep_pos = [&](int max_sweeps) -> bool {
     for (int it = 0;; ++it) {
       tagged_t t[NW];
 #pragma unroll
-      for (int i = 0; i < NW; ++i) {
-        const int j = i >> 1;
-        const tagged_t* base = (i & 1) ? (one[j] ? F1.y2t : F0.y2t) : (one[j] ? F1.yt : F0.yt);
-        t[i] = done[i] ? 0 : ld_tag(base + kpos[j]);
-      }
-      bool all = true;
+      for (int i = 0; i < NW; ++i)
+        t[i] = ((pend >> i) & 1u) ? ld_tag_at((i & 1) ? F.y2t : F.yt, kpos[i >> 1]) : 0;
 #pragma unroll
       for (int i = 0; i < NW; ++i) {
-        if (!done[i]) {
-          if (tag_of(t[i]) == (one[i >> 1] ? tag1 : tag0)) {
-            done[i] = true;
-            v[i] = (uint32_t)t[i];
-          } else {
-            all = false;
-          }
+        if (((pend >> i) & 1u) && tag_of(t[i]) == tag) {
+          pend &= ~(1u << i);
+          v[i] = (uint32_t)t[i];
         }
       }
-      if (__builtin_amdgcn_ballot_w64(!all) == 0) return true;
+      if (__builtin_amdgcn_ballot_w64(pend != 0) == 0) return true;
       if (max_sweeps > 0 && it + 1 >= max_sweeps) return false;
       if (poll_expired(it, error, &L.abort_flag)) return false;
       __builtin_amdgcn_s_sleep(2);
     }
   };
-  // statistics (communication wave): up to 8 x 64 tile statistics per source
-  const tagged_t* sp[8];
-  bool sdone[8];
-  uint32_t stg[8], sv[8];
-  int stat_src = -1;   // the one source whose statistics are needed (at most one RMS source
-                       // per share is rescaled here; a second one gets its own sweep below)
-  bool stats_two = false;
-  if (Comm) {
+  // statistics (communication wave)
+  const bool stats = comm && live && nb > 0 && !direct;
+  const tagged_t* sbase = rfl(X->stats);
+  const int ns = rfl(X->nstats);
+  const uint32_t stag = eng_tag(epoch, rfl(X->src_stage));
+  uint32_t spend = stats ? stats_pending(ns, lane) : 0u, sv[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      sdone[i] = true;
-      sp[i] = F0.yt;
-      stg[i] = 0;
-      sv[i] = 0;
-    }
-    for (int j = 0; j < S->nsrc; ++j) {
-      XP X = j ? X1 : X0;
-      bool used = nb == 0 && slice && j == 0;
-      for (int b = 0; b < nb; ++b) used = used || (blk_get(B, b) >> 16) == j;
-      if (!(live && used && X->kind != kSrcDirect)) continue;
-      if (stat_src < 0) stat_src = j;
-      else stats_two = true;
-    }
-    if (stat_src >= 0) {
-      XP X = stat_src ? X1 : X0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int idx = i * 64 + lane;
-        sdone[i] = idx >= X->nstats;
-        sp[i] = X->stats + (sdone[i] ? 0 : idx);
-        stg[i] = eng_tag(epoch, X->src_stage);
-      }
+  for (int i = 0; i < 8; ++i) sv[i] = 0;
+  bool ready = sweep_pos(1);
+  bool stats_in = true;
+  if (stats) {
+    stats_in = sweep_stats(sbase, ns, stag, spend, sv, lane, 1, L, error);
+    if (stats_in) {   // the wave sum runs on every lane; lane 0 stores the result
+      const float d = stats_denominator(sv, ns, F.k, X->eps, lane);
+      if (lane == 0) L.denom[0] = d;
     }
   }
-  bool to;
-  bool ready = sweep_pos(1);
-  if (Comm && stat_src >= 0)
-    ready = sweep_words<8>(sp, sdone, stg, sv, 1, error, &L.abort_flag, &to) && ready;
-  if (__syncthreads_or(ready ? 0 : 1) && live) {
-    if (Comm) {
+  if (!(ready && stats_in) && lane == 0)
+    __hip_atomic_store(&L.need_poll, s + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  gather_barrier(L, lane, gen, error);
+  if (lds_poll_i(&L.need_poll) == s + 1 && live) {
+    if (comm && !direct) {
       // wait cheaply: the first row of every producer tile of the staged blocks (both factors
       // of a product source), 64 per load, then the statistics
       for (int base = 0; base < nb * 32; base += 64) {
         const int i = base + lane;
         const int b = i >> 5, f = (i >> 4) & 1, t = i & 15;
         bool want = false;
-        const tagged_t* q = F0.yt;
-        uint32_t qt = 0, got;
+        const tagged_t* q = F.yt;
+        uint32_t got;
         if (b < nb) {
-          const int key = blk_get(B, b);
-          const bool o = (key >> 16) != 0;
-          const int kind = o ? F1.kind : F0.kind;
-          const int k = (key & 0xFFFF) * 1024 + t * 64;
-          want = kind != kSrcDirect && k < (o ? F1.k : F0.k) && (f == 0 || kind == kSrcRmsProd);
-          q = (f ? (o ? F1.y2t : F0.y2t) : (o ? F1.yt : F0.yt)) + (want ? k : 0);
-          qt = eng_tag(epoch, o ? F1.src_stage : F0.src_stage);
+          const int k = (blk_get(B, b) & 0xFFFF) * 1024 + t * 64;
+          want = k < F.k && (f == 0 || prod);
+          q = (f ? F.y2t : F.yt) + (want ? k : 0);
         }
-        if (!wait_words<1>(&q, &want, &qt, &got, error, &L.abort_flag)) break;
+        if (!wait_words<1>(&q, &want, &tag, &got, error, &L.abort_flag)) break;
       }
-      if (stat_src >= 0) sweep_words<8>(sp, sdone, stg, sv, 0, error, &L.abort_flag, &to);
+      if (stats && !stats_in) {
+        sweep_stats(sbase, ns, stag, spend, sv, lane, 0, L, error);
+        const float d = stats_denominator(sv, ns, F.k, X->eps, lane);
+        if (lane == 0) L.denom[0] = d;
+      }
     }
-    __syncthreads();
+    gather_barrier(L, lane, gen, error);
     sweep_pos(0);
   }
-  uint32_t direct[kPosPerThread];
+  if (direct) {
 #pragma unroll
-  for (int j = 0; j < kPosPerThread; ++j) direct[j] = 0u;
-  if (F0.kind == kSrcDirect || F1.kind == kSrcDirect) {
-#pragma unroll
-    for (int j = 0; j < kPosPerThread; ++j) {
-      const int kind = one[j] ? F1.kind : F0.kind;
-      if (valid[j] && kind == kSrcDirect) direct[j] = g_ld16((one[j] ? F1.x : F0.x) + kpos[j]);
-    }
+    for (int j = 0; j < kPosPerThread; ++j)
+      if ((vmask >> j) & 1u) v[2 * j] = g_ld16(F.x + kpos[j]);
     // Settle these loads here, seen by the compiler: a load whose result is dead on some path
-    // would otherwise stay pending as far as it knows, and the first reuse of its register in
-    // the unit loop would then wait for every outstanding memory operation on each iteration
-    // (ring copies in compute waves, partial stores in the communication wave).
+    // would otherwise stay pending as far as it knows, and the first reuse of its register
+    // would then wait for every outstanding memory operation (partial stores in the
+    // communication wave).
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt and lgkmcnt untouched
   }
-  if (Comm) {
-    // 2. denominators sqrt(mean(h^2) + eps) from the producers' tile statistics
-    float d0 = 1.f, d1 = 1.f;
-    if (stat_src >= 0) {
-      XP X = stat_src ? X1 : X0;
-      float part = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (i * 64 + lane < X->nstats) part += __uint_as_float(sv[i]);
-      const float d = sqrtf(wave_sum(part) / (float)X->k + X->eps);
-      if (stat_src) d1 = d;
-      else d0 = d;
-    }
-    if (stats_two && live) {   // both sources rescaled here: the second one's statistics
-      XP X = X1;
-      const uint32_t tag = eng_tag(epoch, X->src_stage);
-      float part = 0.f;
-      for (int base = 0; base < X->nstats; base += 64 * 8) {
-        const tagged_t* q[8];
-        bool want[8];
-        uint32_t qt[8], qv[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int idx = base + i * 64 + lane;
-          want[i] = idx < X->nstats;
-          q[i] = X->stats + (want[i] ? idx : 0);
-          qt[i] = tag;
-        }
-        if (!wait_words<8>(q, want, qt, qv, error, &L.abort_flag)) break;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (want[i]) part += __uint_as_float(qv[i]);
-      }
-      d1 = sqrtf(wave_sum(part) / (float)X->k + X->eps);
-    }
-    if (lane == 0) {
-      L.denom[0] = d0;
-      L.denom[1] = d1;
-    }
-  }
-  __syncthreads();
-  // rescale and stage (the slice of a matrix-free stage goes straight to the record)
+  // rescale and stage (the denominator was written before one of the barriers above)
+  const float dn = direct ? 1.f : L.denom[0];
 #pragma unroll
   for (int j = 0; j < kPosPerThread; ++j) {
-    const int kind = one[j] ? F1.kind : F0.kind;
-    uint32_t xb = direct[j];
-    if (valid[j] && kind != kSrcDirect) {
-      float h = e_bf16(v[2 * j]);
-      if (kind == kSrcRmsProd) h *= e_bf16(v[2 * j + 1]);
-      xb = e_to_bf16(h / L.denom[one[j] ? 1 : 0]);
+    const int p = tid + kGatherThreads * j;
+    if (p >= nb * 1024) continue;
+    float xs = 0.f;
+    if ((vmask >> j) & 1u) {
+      if (direct) {
+        xs = e_bf16(v[2 * j]);
+      } else {
+        float h = e_bf16(v[2 * j]);
+        if (prod) h *= e_bf16(v[2 * j + 1]);
+        xs = e_bf16(e_to_bf16(h / dn));
+      }
     }
-    const int p = tid + kEngThreads * j;
-    if (p < nb * 1024) L.staging[p >> 10][p & 1023] = valid[j] ? e_bf16(xb) : 0.f;
-    if (Comm && nb == 0 && valid[j] && live) g_st16(X0->record + kpos[j], xb);
+    L.staging[p >> 10][p & 1023] = xs;
   }
-  __syncthreads();
-  if (Comm && live) {
+  gather_barrier(L, lane, gen, error);
+  if (comm && live && X->record != nullptr) {
     // 3. records of the blocks this workgroup owns, from the staged (exactly bf16) values
+    uint16_t* rec = rfl(X->record);
+    MP R = &S->mat[X->rec_mat];
     for (int b = 0; b < nb; ++b) {
-      const int key = blk_get(B, b);
-      const int src = key >> 16, sg = key & 0xFFFF;
-      XP X = src ? X1 : X0;
-      MP R = &S->mat[X->rec_mat];
-      if (X->record == nullptr || !share_has(r, R->unit_base + sg * R->tiles)) continue;
-      const int n = min(1024, X->k - sg * 1024);
+      const int sg = blk_get(B, b) & 0xFFFF;
+      if (!share_has(r, R->unit_base + sg * R->tiles)) continue;
+      const int n = min(1024, F.k - sg * 1024);
       for (int q = lane; q < n; q += 64)
-        g_st16(X->record + sg * 1024 + q, __float_as_uint(L.staging[b][q]) >> 16);
+        g_st16(rec + sg * 1024 + q, __float_as_uint(L.staging[b][q]) >> 16);
     }
   }
 }
 
+// A stage without matrices (the final rescale of a decode step): the communication wave of each
+// streaming workgroup rescales an even slice of the source into the caller's record.
+INL void slice_stage(PP P, EngLds& L, int s, int w, int lane, uint32_t epoch, uint32_t* error) {
+  SP S = &P->st[s];
+  if (S->nsrc < 1) return;
+  XP X = &S->src[0];
+  const SrcFields F = src_fields(X);
+  uint16_t* rec = rfl(X->record);
+  if (rec == nullptr || F.kind == kSrcDirect) return;
+  const bool prod = F.kind == kSrcRmsProd;
+  const int nst = P->nstream;
+  const int a = (int)(((long long)F.k * w) / nst), e = (int)(((long long)F.k * (w + 1)) / nst);
+  if (a >= e) return;
+  const uint32_t tag = eng_tag(epoch, F.src_stage);
+  const int ns = rfl(X->nstats);
+  uint32_t spend = stats_pending(ns, lane), sv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sv[i] = 0;
+  if (!sweep_stats(rfl(X->stats), ns, tag, spend, sv, lane, 0, L, error)) return;
+  const float d = stats_denominator(sv, ns, F.k, X->eps, lane);
+  // this workgroup's positions: at most four per lane (checked by the host)
+  uint32_t pend = 0, hv[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (a + lane + 64 * j < e) pend |= (prod ? 3u : 1u) << (2 * j);
+    hv[2 * j] = hv[2 * j + 1] = 0;
+  }
+  for (int it = 0;; ++it) {
+    tagged_t t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      t[i] = ((pend >> i) & 1u) ? ld_tag_at((i & 1) ? F.y2t : F.yt, (uint32_t)(a + lane + 64 * (i >> 1))) : 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (((pend >> i) & 1u) && tag_of(t[i]) == tag) {
+        pend &= ~(1u << i);
+        hv[i] = (uint32_t)t[i];
+      }
+    }
+    if (__builtin_amdgcn_ballot_w64(pend != 0) == 0) break;
+    if (poll_expired(it, error, &L.abort_flag)) return;
+    __builtin_amdgcn_s_sleep(2);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int k = a + lane + 64 * j;
+    if (k >= e) continue;
+    float h = e_bf16(hv[2 * j]);
+    if (prod) h *= e_bf16(hv[2 * j + 1]);
+    g_st16(rec + k, e_to_bf16(h / d));
+  }
+}
+
 // ------------------------------------------------------------------------------------------
-// compute wave V
+// compute waves
 // ------------------------------------------------------------------------------------------
-template <int V>
-INL float lookup_group(const EngLds& L, const uint32_t s4[4]) {
-  const char* lb = (const char*)&L.lut[V][0];
+
+// Sum over one 128-weight group of a row: 32 table lookups (tables of group H of this wave).
+template <int CW, int H>
+INL float lookup_group(const EngLds& L, const uint4 s4) {
+  const char* lb = (const char*)&L.lut[CW][H][0];
+  const uint32_t sd[4] = {s4.x, s4.y, s4.z, s4.w};
   float pa = 0.f, pb = 0.f;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    const uint32_t s = s4[d];
+    const uint32_t s = sd[d];
     const uint32_t r = __builtin_amdgcn_alignbit(s, s, 4);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -680,198 +668,204 @@ INL float lookup_group(const EngLds& L, const uint32_t s4[4]) {
   return pa + pb;
 }
 
-// Builds this wave's 32 tables of 16 signed sums (group V of staged block b), two lanes per
-// table. Entry e = m + 4 j of the table for inputs (x0, x1, x2, x3) is pair term m of (x0, x1)
-// plus pair term j of (x2, x3), where pair term 0 = -a-b, 1 = a-b, 2 = b-a, 3 = a+b.
-template <int V>
+// Builds this wave's 64 tables of 16 signed sums (32 per group of its pair, staged block b),
+// one table per lane. Entry e = m + 4 j of the table for inputs (x0, x1, x2, x3) is pair term
+// m of (x0, x1) plus pair term j of (x2, x3), where pair term 0 = -a-b, 1 = a-b, 2 = b-a,
+// 3 = a+b (bit i of e set: input i enters with +).
+template <int CW>
 INL void build_lut(EngLds& L, int b, int lane) {
-  const int c = lane >> 1, h = lane & 1;
-  const float* xs = &L.staging[b][kGroup * V + 4 * c];
-  const float x0 = xs[0], x1 = xs[1], x2 = xs[2], x3 = xs[3];
-  const float p0 = -x0 - x1, p1 = x0 - x1, p2 = x1 - x0, p3 = x0 + x1;
-  // this lane writes entries 8h..8h+7, i.e. pair terms j = 2h and 2h+1 of (x2, x3)
-  const float q0 = h ? x3 - x2 : -x2 - x3;
-  const float q1 = h ? x2 + x3 : x2 - x3;
-  float4* dst = (float4*)&L.lut[V][c * 16 + 8 * h];
+  constexpr int kPair = CW % kEngPairs;
+  const int h = lane >> 5, c = lane & 31;
+  const float4 xv = *(const float4*)&L.staging[b][kGroup * (2 * kPair + h) + 4 * c];
+  const float p0 = -xv.x - xv.y, p1 = xv.x - xv.y, p2 = xv.y - xv.x, p3 = xv.x + xv.y;
+  const float q0 = -xv.z - xv.w, q1 = xv.z - xv.w, q2 = xv.w - xv.z, q3 = xv.z + xv.w;
+  float4* dst = (float4*)&L.lut[CW][h][c * 16];
   dst[0] = make_float4(p0 + q0, p1 + q0, p2 + q0, p3 + q0);
   dst[1] = make_float4(p0 + q1, p1 + q1, p2 + q1, p3 + q1);
+  dst[2] = make_float4(p0 + q2, p1 + q2, p2 + q2, p3 + q2);
+  dst[3] = make_float4(p0 + q3, p1 + q3, p2 + q3, p3 + q3);
 }
 
-// Starts the ring copy of the cursor's unit into slot `slot` (a dummy copy from the program
-// when this wave's group does not exist there).
-template <int V>
-INL void issue_unit(PP P, const Cursor& c, EngLds& L, int slot, uint32_t voff_w, uint32_t voff_s) {
-  const void* base = c.ok ? (const void*)c.p : (const void*)P;
-  dma_slot(base, voff_w, voff_s, lds_addr(&L.ring_w[V][slot][0]), lds_addr(&L.ring_s[V][slot][0]));
-}
-
-// Waits until the ring slot of the next unit has landed, given how many slots were issued after
-// it (each slot is two vector-memory instructions, completing in order).
-INL void wait_ring(int ahead) {
-  switch (ahead) {
-    case 7: asm volatile("s_waitcnt vmcnt(14)" ::: "memory"); break;
-    case 6: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
-    case 5: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
-    case 4: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-    case 3: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-    case 1: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-  }
-}
-static_assert(kEngRing == 8 && kEngSlots == 8, "the unit loop assumes eight ring and hand-off slots");
-
-// First stage >= s whose end holds prefetching back (its last partial goes out first).
-INL int next_gate(PP P, int s) {
-  while (s < P->nstages && !P->st[s].drain) ++s;
-  return s;
-}
-
-template <int V>
+// Compute wave CW: pair p = CW % 4 (groups 2p, 2p+1) of the units q with q % 3 == CW / 4.
+template <int CW>
 INL void compute_wave(PP P, EngLds& L, int w, int lane, uint32_t epoch, uint32_t* error) {
-  // per-lane offsets of this wave's sign record (group V) and scale word within a super-group
-  const uint32_t voff_w = (uint32_t)(lane * 16 + kBlock * (1 + V));
-  const uint32_t voff_s = (uint32_t)(lane * 16 + (V / 2) * 4);
-  Cursor pf, cu;
-  cur_stage<V, false>(P, pf, w, 0);
-  cur_stage<V, true>(P, cu, w, 0);
-  unsigned issued = 0, cnt = 0;
-  const int nst_all = P->nstages;
-  int gate = next_gate(P, 0);
-  // refill: keep up to kRing units in flight, never past the gate stage
-  auto refill = [&]() {
-    while (issued - cnt < (unsigned)kRing && pf.s < P->nstages && pf.s <= gate) {
-      issue_unit<V>(P, pf, L, issued % kRing, voff_w, voff_s);
-      ++issued;
-      cur_next<V, false>(P, pf, w);
-    }
-  };
-  refill();
-  for (int s = 0; s < P->nstages; ++s) {
-    if (s > gate) {
-      // the gate stage's partials are all issued: prefetch past it
-      for (int it = 0; (int)lds_poll((const uint32_t*)&L.published) < gate &&
-                       !lds_poll_i(&L.abort_flag);
-           ++it) {
-        if (it >= kPollLimit) {
-          L.abort_flag = 1;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-      gate = next_gate(P, s);
-      refill();
-    }
-    stage_inputs<false>(P, L, s, w, V * 64 + lane, epoch, error);
+  constexpr int kPair = CW % kEngPairs, kPhase = CW / kEngPairs;
+  uint32_t gen = 0;
+  unsigned seq = 0;   // sequence number of the stage's first unit in this workgroup
+  const int nstages = P->nstages;
+  for (int s = 0; s < nstages; ++s) {
     SP S = &P->st[s];
     const int n = share_units(stage_share(S, w, P->nstream));
-    if (lds_poll_i(&L.abort_flag) || n == 0) continue;
+    if (n == 0) continue;
+    stage_inputs(P, L, s, w, CW * 64 + lane, false, epoch, error, gen);
+    const unsigned end = seq + (unsigned)n;
     int lut_b = -1;   // block the tables currently hold
-    for (int k = 0; k < n; ++k) {
-      const int slot = cnt % kRing;
-      const int ps = cnt % kEngSlots;
-      const unsigned round = cnt / kEngSlots;
-      const uint32_t fr = lds_poll(&L.freed[ps]);   // read early, tested after the lookups
-      if (__builtin_expect(issued - cnt == (unsigned)kRing, 1))
-        asm volatile("s_waitcnt vmcnt(14)" ::: "memory");   // steady state: a full ring
-      else
-        wait_ring((int)(issued - cnt) - 1);
-      float partial = 0.f;
-      if (cu.ok) {
-        const uint32_t* rw = &L.ring_w[V][slot][lane * 4];
-        uint32_t s4[4] = {rw[0], rw[1], rw[2], rw[3]};
-        const uint32_t sw = L.ring_s[V][slot][lane];
-        const float scale = e_f16((V & 1) ? (sw >> 16) : (sw & 0xFFFFu));
-        if (cu.b != lut_b) {   // at most kEngMaxBlocks times per stage
-          build_lut<V>(L, cu.b, lane);
-          lut_b = cu.b;
-        }
-        partial = scale * lookup_group<V>(L, s4);
-      }
-      // hand the partial to the communication wave (slot ps must have been consumed)
-      if (fr < round) {
-        for (int it = 0; lds_poll(&L.freed[ps]) < round; ++it) {
-          if (lds_poll_i(&L.abort_flag) || it >= kPollLimit) {
-            L.abort_flag = 1;
-            break;
-          }
+    for (unsigned q = seq + (kPhase + kEngPhases - seq % kEngPhases) % kEngPhases; q < end;
+         q += kEngPhases) {
+      if (lds_poll_i(&L.abort_flag)) break;
+      const int slot = (int)(q % kEngRingSlots);
+      if (lds_poll(&L.ready) <= q) {   // the loader normally runs far ahead
+        for (int it = 0; lds_poll(&L.ready) <= q; ++it) {
+          if (poll_expired(it, error, &L.abort_flag)) break;
           __builtin_amdgcn_s_sleep(1);
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      __hip_atomic_store(&L.part[ps][V][lane],
-                         ((unsigned long long)(round + 1) << 32) | __float_as_uint(partial),
+      const int blk = rfl(L.meta[slot].blk), ng = rfl(L.meta[slot].ng);
+      if (blk != lut_b) {   // at most kEngMaxBlocks times per stage
+        build_lut<CW>(L, blk, lane);
+        lut_b = blk;
+      }
+      const uint8_t* base = &L.ring[slot][0];
+      const uint4 ra = *(const uint4*)(base + kBlock * (1 + 2 * kPair) + lane * 16);
+      const uint4 rb = *(const uint4*)(base + kBlock * (2 + 2 * kPair) + lane * 16);
+      const uint32_t sw = *(const uint32_t*)(base + lane * 16 + 4 * kPair);
+      // this wave's bytes of the slot are in registers: count the read for the loader
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      if (lane == 0)
+        __hip_atomic_fetch_add(&L.consumed[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      float part = 0.f;
+      if (2 * kPair < ng) part = e_f16(sw & 0xFFFFu) * lookup_group<CW, 0>(L, ra);
+      if (2 * kPair + 1 < ng) part += e_f16(sw >> 16) * lookup_group<CW, 1>(L, rb);
+      // hand the partial to the communication wave (the slot's last round must be consumed)
+      const unsigned hs = q % kEngHandSlots, round = q / kEngHandSlots;
+      if (lds_poll(&L.hfree[hs]) < round) {
+        for (int it = 0; lds_poll(&L.hfree[hs]) < round; ++it) {
+          if (poll_expired(it, error, &L.abort_flag)) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      __hip_atomic_store(&L.hand[hs][kPair][lane],
+                         ((unsigned long long)(round + 1) << 32) | __float_as_uint(part),
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      ++cnt;
-      cur_next<V, true>(P, cu, w);
-      if (pf.s < nst_all && pf.s <= gate) {   // steady state: one copy per consumed unit
-        issue_unit<V>(P, pf, L, issued % kRing, voff_w, voff_s);
-        ++issued;
-        cur_next<V, false>(P, pf, w);
+    }
+    seq = end;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// loader wave: the workgroup's units of every stage, in program order, into the LDS ring
+// ------------------------------------------------------------------------------------------
+INL void store_ready(EngLds& L, int lane, unsigned v) {
+  if (lane == 0) lds_set(&L.ready, v);
+}
+
+INL void loader_wave(PP P, EngLds& L, int w, int lane, uint32_t* error) {
+  const uint32_t voff = (uint32_t)lane * 16u;
+  const uint32_t ring0 = lds_addr(&L.ring[0][0]);
+  unsigned q = 0;
+  bool live = true;
+  const int nstages = P->nstages, nstream = P->nstream;
+  for (int s = 0; s < nstages && live; ++s) {
+    SP S = &P->st[s];
+    const Share r = stage_share(S, w, nstream);
+    if (share_units(r) == 0) continue;
+    const Blocks B = stage_blocks(S, r);
+    for (int pass = 0; pass < 2 && live; ++pass) {
+      const int a = pass ? r.a1 : r.a0, e = pass ? r.b1 : r.b0;
+      for (int u = a; u < e && live;) {
+        // a segment: consecutive tiles of one (matrix, super-group) column, tile_bytes apart
+        const UnitPos pos = unit_pos(S, u);
+        MP M = &S->mat[pos.m];
+        const int len = min(M->tiles - pos.tile, e - u);
+        const size_t step = (size_t)M->tile_bytes;
+        const int ng = min(kSuper, M->groups - pos.sg * kSuper);
+        const int blk = blk_find(B, blk_key(M->src, pos.sg));
+        const uint8_t* src = M->w + (size_t)pos.tile * step + (size_t)pos.sg * kUnitBytes;
+        for (int i = 0; i < len; ++i, ++q, src += step) {
+          const unsigned slot = q % kEngRingSlots;
+          // the slot's previous unit must have been read by its four compute waves
+          const uint32_t need = (q / kEngRingSlots) * kEngPairs;
+          if (lds_poll(&L.consumed[slot]) < need) {
+            // ring full: announce everything issued so far, then wait for the slot
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            store_ready(L, lane, q);
+            for (int it = 0; lds_poll(&L.consumed[slot]) < need; ++it) {
+              if (poll_expired(it, error, &L.abort_flag)) {
+                live = false;
+                break;
+              }
+              __builtin_amdgcn_s_sleep(1);
+            }
+            if (!live) break;
+          }
+          if (lane == 0) {
+            L.meta[slot].blk = blk;
+            L.meta[slot].ng = ng;
+          }
+          const uint32_t dst = ring0 + slot * (uint32_t)kUnitBytes;
+          // always nine copies, so the in-flight accounting below is static: a group missing at
+          // a ragged end of K re-reads the scale block instead
+#pragma unroll
+          for (int j = 0; j <= kSuper; ++j)
+            dma_chunk(j <= ng ? src + j * kBlock : src, voff, dst + j * kBlock);
+          if (q + 1 >= (unsigned)kEngInFlight) {
+            // at most kEngInFlight units in flight: wait for the oldest beyond that to land
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"((1 + kSuper) * (kEngInFlight - 1)) : "memory");
+            store_ready(L, lane, q + 2 - kEngInFlight);
+          }
+        }
+        u += len;
       }
     }
   }
-  // let any copy still in flight land before the wave ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  store_ready(L, lane, q);
 }
 
 // ------------------------------------------------------------------------------------------
 // communication wave of a streaming workgroup
 // ------------------------------------------------------------------------------------------
 INL void comm_wave(PP P, EngLds& L, int w, int lane, uint32_t epoch, uint32_t* error) {
-  unsigned cnt = 0;
-  for (int s = 0; s < P->nstages; ++s) {
-    stage_inputs<true>(P, L, s, w, kEngWaves * 64 + lane, epoch, error);
+  uint32_t gen = 0;
+  unsigned seq = 0;
+  const int nstages = P->nstages;
+  for (int s = 0; s < nstages; ++s) {
     SP S = &P->st[s];
-    const Share r = stage_share(S, w, P->nstream);
-    const uint32_t tag = eng_tag(epoch, s);
-    bool live = !lds_poll_i(&L.abort_flag);
-    if (s + 1 < P->nstages) warm_stage(&P->st[s + 1]);
-    // publish this workgroup's unit partials as they complete (never waits on global memory)
-    for (int pass = 0; pass < 2; ++pass) {
-      const int a = pass ? r.a1 : r.a0, b = pass ? r.b1 : r.b0;
-      for (int u = a; u < b; ++u) {
-        if (!live) {
-          ++cnt;
-          continue;
-        }
-        const int ps = cnt % kEngSlots;
-        const uint32_t want = cnt / kEngSlots + 1;
-        uint32_t wv[kEngWaves];
-        for (int it = 0;; ++it) {
-          bool all = true;
-#pragma unroll
-          for (int v = 0; v < kEngWaves; ++v) {
-            const unsigned long long t = __hip_atomic_load(&L.part[ps][v][lane], __ATOMIC_RELAXED,
-                                                           __HIP_MEMORY_SCOPE_WORKGROUP);
-            wv[v] = (uint32_t)t;
-            all = all && (uint32_t)(t >> 32) == want;
-          }
-          if (__builtin_amdgcn_ballot_w64(!all) == 0) break;
-          if (lds_poll_i(&L.abort_flag) || it >= kPollLimit) {
-            live = false;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
-        if (!live) {
-          set_err(error);
-          L.abort_flag = 1;
-          ++cnt;
-          continue;
-        }
-        float p = 0.f;
-#pragma unroll
-        for (int v = 0; v < kEngWaves; ++v) p += __uint_as_float(wv[v]);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        if (lane == 0) L.freed[ps] = want;
-        st_tag(S->part + (size_t)u * 64 + lane, __float_as_uint(p), tag);
-        ++cnt;
-      }
+    if (S->nmat == 0) {
+      if (!lds_poll_i(&L.abort_flag)) slice_stage(P, L, s, w, lane, epoch, error);
+      continue;
     }
-    // every partial of this stage has been issued: compute waves may prefetch past it
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    if (lane == 0) __hip_atomic_store(&L.published, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const Share r = stage_share(S, w, P->nstream);
+    const int n = share_units(r);
+    if (n == 0) continue;
+    stage_inputs(P, L, s, w, kEngCompute * 64 + lane, true, epoch, error, gen);
+    const uint32_t tag = eng_tag(epoch, s);
+    tagged_t* part = rfl(S->part);
+    if (s + 1 < nstages) warm_stage(&P->st[s + 1]);
+    const int n0 = r.b0 - r.a0;
+    // publish this workgroup's unit partials as they complete (never waits on global memory)
+    for (int k = 0; k < n; ++k, ++seq) {
+      if (lds_poll_i(&L.abort_flag)) continue;
+      const int u = k < n0 ? r.a0 + k : r.a1 + (k - n0);
+      const unsigned hs = seq % kEngHandSlots;
+      const uint32_t want = seq / kEngHandSlots + 1;
+      uint32_t hv[kEngPairs];
+      bool live = true;
+      for (int it = 0;; ++it) {
+        bool all = true;
+#pragma unroll
+        for (int p = 0; p < kEngPairs; ++p) {
+          const unsigned long long t = __hip_atomic_load(&L.hand[hs][p][lane], __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_WORKGROUP);
+          hv[p] = (uint32_t)t;
+          all = all && (uint32_t)(t >> 32) == want;
+        }
+        if (__builtin_amdgcn_ballot_w64(!all) == 0) break;
+        if (poll_expired(it, error, &L.abort_flag)) {
+          live = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (!live) continue;
+      const float pv = ((__uint_as_float(hv[0]) + __uint_as_float(hv[1])) + __uint_as_float(hv[2])) +
+                       __uint_as_float(hv[3]);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      if (lane == 0) __hip_atomic_store(&L.hfree[hs], want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      st_tag(part + (size_t)u * 64 + lane, __float_as_uint(pv), tag);
+    }
   }
 }
 
@@ -911,33 +905,29 @@ INL void finalize_item(SP S, EngLds& L, int s, int item, int lane, uint32_t epoc
     if (!wait_words<1>(&ptr, &want, &tag, &got, error, &L.abort_flag)) return;
   }
   // full sweeps: every word of the n partials is loaded on every sweep (a retry is rare), so
-  // the loads need no per-lane branches
+  // the loads need no per-lane branches; the sums are formed in partial order as the tags are
+  // checked and simply redone by a retry
   const tagged_t* pb = part + lane;
-  uint32_t v[kEngMaxFinal];
-#pragma unroll
-  for (int i = 0; i < kEngMaxFinal; ++i) v[i] = 0;
+  float y1 = 0.f, y2 = 0.f;
   for (int it = 0;; ++it) {
     tagged_t t[kEngMaxFinal];
 #pragma unroll
     for (int i = 0; i < kEngMaxFinal; ++i)
       if (i < n) t[i] = ld_tag(pb + (size_t)(i < s1 ? ub1 + i * t1 : ub2 + i * t2) * 64);
     bool all = true;
+    y1 = 0.f;
+    y2 = 0.f;
 #pragma unroll
     for (int i = 0; i < kEngMaxFinal; ++i) {
       if (i < n) {
         all = all && tag_of(t[i]) == tag;
-        v[i] = (uint32_t)t[i];
+        if (i < s1) y1 += __uint_as_float((uint32_t)t[i]);
+        else y2 += __uint_as_float((uint32_t)t[i]);
       }
     }
     if (__builtin_amdgcn_ballot_w64(!all) == 0) break;
     if (poll_expired(it, error, &L.abort_flag)) return;
     __builtin_amdgcn_s_sleep(1);
-  }
-  float y1 = 0.f, y2 = 0.f;
-#pragma unroll
-  for (int i = 0; i < kEngMaxFinal; ++i) {
-    if (i < s1) y1 += __uint_as_float(v[i]);
-    else if (i < n) y2 += __uint_as_float(v[i]);
   }
   // outputs: tagged copies and statistics first (consumers wait on them), plain copies last
   const int row = tile * kTileRows + lane;
@@ -986,21 +976,27 @@ __global__ __launch_bounds__(kEngThreads) void q1_engine_kernel(EngArgs A) {
   const int wg = blockIdx.x;
   PP P = (PP)A.prog;
   // LDS holds whatever the previous kernel left: clear the hand-off tags (rounds start at 1)
-  for (int i = threadIdx.x; i < kEngSlots * kEngWaves * 64; i += kEngThreads)
-    (&L.part[0][0][0])[i] = 0;
-  if (threadIdx.x < kEngSlots) L.freed[threadIdx.x] = 0;
+  // and the control words
+  for (int i = threadIdx.x; i < kEngHandSlots * kEngPairs * 64; i += kEngThreads)
+    (&L.hand[0][0][0])[i] = 0;
+  if (threadIdx.x < kEngRingSlots) L.consumed[threadIdx.x] = 0;
+  if (threadIdx.x < kEngHandSlots) L.hfree[threadIdx.x] = 0;
   if (threadIdx.x == 0) {
+    L.ready = 0;
+    L.bar_count = 0;
+    L.bar_gen = 0;
+    L.need_poll = 0;
     L.abort_flag = 0;
-    L.published = -1;
   }
   if (wave == 0) warm_stage(&P->st[0]);
   __syncthreads();
   const int nst = P->nstream;
-  if (wg >= nst) {   // finalising workgroup: all nine waves finalise
-    const int nc = (P->nwg - nst) * (kEngWaves + 1);
-    final_wave(P, L, (wg - nst) * (kEngWaves + 1) + wave, nc, lane, A.epoch, A.error);
+  if (wg >= nst) {   // finalising workgroup: all its waves finalise
+    const int nc = (P->nwg - nst) * kEngWaves;
+    final_wave(P, L, (wg - nst) * kEngWaves + wave, nc, lane, A.epoch, A.error);
     return;
   }
+  static_assert(kEngCompute == 12, "one case per compute wave");
   switch (wave) {
     case 0: compute_wave<0>(P, L, wg, lane, A.epoch, A.error); break;
     case 1: compute_wave<1>(P, L, wg, lane, A.epoch, A.error); break;
@@ -1010,6 +1006,11 @@ __global__ __launch_bounds__(kEngThreads) void q1_engine_kernel(EngArgs A) {
     case 5: compute_wave<5>(P, L, wg, lane, A.epoch, A.error); break;
     case 6: compute_wave<6>(P, L, wg, lane, A.epoch, A.error); break;
     case 7: compute_wave<7>(P, L, wg, lane, A.epoch, A.error); break;
+    case 8: compute_wave<8>(P, L, wg, lane, A.epoch, A.error); break;
+    case 9: compute_wave<9>(P, L, wg, lane, A.epoch, A.error); break;
+    case 10: compute_wave<10>(P, L, wg, lane, A.epoch, A.error); break;
+    case 11: compute_wave<11>(P, L, wg, lane, A.epoch, A.error); break;
+    case kLoaderWave: loader_wave(P, L, wg, lane, A.error); break;
     default: comm_wave(P, L, wg, lane, A.epoch, A.error); break;
   }
 }
@@ -1209,14 +1210,18 @@ static bool eng_fits(const EngProgram* P) {
   if (P->nstream < 1 || P->nstream >= P->nwg) return false;
   for (int s = 0; s < P->nstages; ++s) {
     const EngStage& S = P->st[s];
+    // one source vector per stage, read by every matrix of the stage
+    if (S.nsrc != 1) return false;
     for (int m = 0; m < S.nmat; ++m) {
       const EngMat& M = S.mat[m];
       const int fin = M.supers + (M.pair >= 0 ? S.mat[M.pair].supers : 0);
       if (M.item_base >= 0 && fin > kEngMaxFinal) return false;
       if (M.tile_bytes >= (1LL << 31)) return false;
+      if (M.src != 0) return false;
     }
-    for (int j = 0; j < S.nsrc; ++j)
-      if ((long long)S.src[j].k * P->nwg >= (1LL << 31)) return false;
+    // statistics are read eight per lane of one wave; tagged words are indexed with 32 bits
+    if (S.src[0].kind != kSrcDirect && S.src[0].nstats > 8 * 64) return false;
+    if ((long long)S.src[0].k * P->nwg >= (1LL << 31)) return false;
     if ((long long)S.units * P->nwg >= (1LL << 31)) return false;
     if (S.nmat == 0 && S.nsrc > 0 && (S.src[0].k + P->nstream - 1) / P->nstream > 4 * 64)
       return false;   // slice of a matrix-free stage: four positions per lane of one wave
@@ -1271,7 +1276,6 @@ lbq_status lbq_engine_gemv_q1(const void* d_w, int32_t n, int32_t k, const uint1
 //  B1 : o, input rescale(q);
 //  B2 : down, input rescale(gate * up);
 // then a final stage that only rescales the last down output into the caller's record.
-// Stages A and B2 drain: their last partials feed the next stage but one and the next stage.
 lbq_status lbq_engine_decode_q1(const lbq_q1_layer* layers, int32_t L, int32_t hidden, int32_t kv,
                                 int32_t ffn, const uint16_t* d_x0, uint16_t* d_act, float eps,
                                 hipStream_t stream) {
@@ -1330,7 +1334,6 @@ lbq_status lbq_engine_decode_q1(const lbq_q1_layer* layers, int32_t L, int32_t h
     if (!ok) return LBQ_E_SHAPE;
     eng_pair(A, 3, 4);
     eng_part(A, &cursor);
-    A.drain = 1;
     A.nsrc = 1;
     if (l == 0) {
       A.src[0].kind = kSrcDirect;
@@ -1352,7 +1355,6 @@ lbq_status lbq_engine_decode_q1(const lbq_q1_layer* layers, int32_t L, int32_t h
       return LBQ_E_SHAPE;
     eng_part(B2, &cursor);
     B2.part0 = B2.units;
-    B2.drain = 1;
     B2.nsrc = 1;
     rms_src(B2.src[0], kSrcRmsProd, ffn, A.mat[3], &A.mat[4], A.mat[4], 3 * l, at(l, LBQ_ACT_XD), 0);
     prev_down = &B2.mat[0];
