@@ -40,7 +40,7 @@ typedef unsigned long long tagged_t;
 struct EngMat {
   const uint8_t* w;        // Q1 device layout
   uint16_t* y;             // plain bf16 output [n] (may be null)
-  tagged_t* yt;            // tagged bf16 output [np]
+  tagged_t* yt;            // tagged bf16 output [np] (with a pair partner: both outputs per word)
   tagged_t* stat;          // tagged per-tile statistic [tiles] (kMatSumSq / kMatPair) or null
   long long tile_bytes;
   int32_t n, k, tiles, groups, supers, src, kind, unit_base, units;
@@ -51,8 +51,8 @@ struct EngMat {
 
 struct EngSrc {
   const uint16_t* x;       // kSrcDirect: bf16 input [k]
-  const tagged_t* yt;      // kSrcRms*: tagged outputs of an earlier stage
-  const tagged_t* y2t;     // kSrcRmsProd: second factor
+  const tagged_t* yt;      // kSrcRms*: tagged outputs of an earlier stage (kSrcRmsProd: the
+                           // pair's words, both factors in one)
   const tagged_t* stats;   // kSrcRms*: per-tile statistics of the producer
   uint16_t* record;        // bf16 copy of the vector for the caller (may be null)
   float eps;

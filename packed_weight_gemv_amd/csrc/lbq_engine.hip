@@ -103,14 +103,12 @@ INL T* rfl(T* p) {
 }
 struct SrcFields {
   const tagged_t* yt;
-  const tagged_t* y2t;
   const uint16_t* x;
   int kind, k, src_stage;
 };
 INL SrcFields src_fields(XP X) {
   SrcFields f;
   f.yt = rfl(X->yt);
-  f.y2t = rfl(X->y2t);
   f.x = rfl(X->x);
   f.kind = rfl(X->kind);
   f.k = rfl(X->k);
@@ -188,6 +186,8 @@ struct __attribute__((aligned(16))) EngLds {
   int32_t abort_flag;
 };
 static_assert(sizeof(EngLds) <= 160 * 1024, "the engine's LDS must fit one compute unit");
+static_assert(kEngWaves * kEngMaxFinal * 64 * 4 <= offsetof(EngLds, meta),
+              "a finalising workgroup's scratch lies within its unused tables, staging and ring");
 
 // A streaming workgroup's units of a stage: range [a0, b0) of part 0, then [a1, b1) of part 1.
 struct Share {
@@ -262,8 +262,8 @@ INL Blocks stage_blocks(SP S, const Share& r) {
 // instead of a chain of dependent misses, each a full memory round trip, as its fields are
 // first used. The loaded values are discarded; the wait sits in the same asm block.
 // Loads at every 64 bytes from the start plus one at the last dword cover every line of a
-// 608-byte descriptor whatever its alignment.
-static_assert(sizeof(EngStage) == 608, "warm_stage covers a 608-byte stage descriptor");
+// 592-byte descriptor whatever its alignment.
+static_assert(sizeof(EngStage) == 592, "warm_stage covers a 592-byte stage descriptor");
 INL void warm_stage(SP S) {
   uint32_t d0, d1, d2, d3, d4, d5, d6, d7, d8, d9, d10;
   asm volatile(
@@ -272,7 +272,7 @@ INL void warm_stage(SP S) {
       "s_load_dword %4, %11, 0x100\n\ts_load_dword %5, %11, 0x140\n\t"
       "s_load_dword %6, %11, 0x180\n\ts_load_dword %7, %11, 0x1c0\n\t"
       "s_load_dword %8, %11, 0x200\n\ts_load_dword %9, %11, 0x240\n\t"
-      "s_load_dword %10, %11, 0x25c\n\ts_waitcnt lgkmcnt(0)"
+      "s_load_dword %10, %11, 0x24c\n\ts_waitcnt lgkmcnt(0)"
       : "=&s"(d0), "=&s"(d1), "=&s"(d2), "=&s"(d3), "=&s"(d4), "=&s"(d5), "=&s"(d6), "=&s"(d7),
         "=&s"(d8), "=&s"(d9), "=&s"(d10)
       : "s"(S)
@@ -383,7 +383,8 @@ INL void gather_barrier(EngLds& L, int lane, uint32_t& gen, uint32_t* error) {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-constexpr int kPosPerThread = (kEngMaxBlocks * 1024 + kGatherThreads - 1) / kGatherThreads;
+constexpr int kPosThreads = kEngCompute * 64;   // the compute waves load the input positions
+constexpr int kPosPerThread = (kEngMaxBlocks * 1024 + kPosThreads - 1) / kPosThreads;
 
 // Tagged word idx of a uniform base (32-bit index: the load takes a scalar base and a vector
 // offset).
@@ -431,20 +432,17 @@ INL float stats_denominator(const uint32_t (&sv)[8], int n, int k, float eps, in
 }
 
 // Stage-start duties of a streaming workgroup, run by every gathering wave (tid = its thread
-// index among them; the communication wave has the last 64). A stage reads one source vector.
-//  1. one optimistic sweep: every thread loads its positions of the share's (at most four)
-//     1024-wide input blocks as tagged words (both factors of a product source), the
-//     communication wave also the producers' tile statistics, and, when they are all in, it
-//     turns them into the RMS denominator. When the producers are done, the usual case away
-//     from the critical stage boundaries, that is the only round trip. Otherwise the
-//     communication wave polls the first row of every producer tile (one small load per round
-//     trip instead of the whole share) and the statistics until they are in, and every thread
-//     then sweeps again for its missing words;
-//  2. after a barrier every thread rescales its positions to bf16 and stores them to the
-//     staging area;
-//  3. after a second barrier the communication wave copies each block whose tile-0 unit (of the
-//     source's record matrix) this workgroup owns to the caller's record.
-// Compute waves issue no global stores here (and none anywhere else).
+// index among them; the communication wave has the last 64). A stage reads one source vector;
+// a position of an RMS source is one tagged word (a product source holds both factors in it).
+//  1. one optimistic sweep: every compute-wave thread loads its positions of the share's (at
+//     most four) 1024-wide input blocks while the communication wave loads the producers' tile
+//     statistics and, when they are all in, turns them into the RMS denominator. When the
+//     producers are done, that is the only round trip. Otherwise the communication wave polls
+//     the statistics (the producers write them after their outputs) until they are all in, and
+//     every compute-wave thread then sweeps again for its missing words;
+//  2. after a barrier every thread rescales its positions to bf16, stores them to the staging
+//     area and, for the blocks whose tile-0 unit (of the source's record matrix) this workgroup
+//     owns, to the caller's record.
 INL void stage_inputs(PP P, EngLds& L, int s, int w, int tid, bool comm, uint32_t epoch,
                       uint32_t* error, uint32_t& gen) {
   SP S = &P->st[s];
@@ -462,39 +460,36 @@ INL void stage_inputs(PP P, EngLds& L, int s, int w, int tid, bool comm, uint32_
   const SrcFields F = src_fields(X);
   const bool direct = F.kind == kSrcDirect, prod = F.kind == kSrcRmsProd;
   const uint32_t tag = eng_tag(epoch, F.src_stage);
-  // this thread's positions: kpos[j] for p = tid + j * kGatherThreads; bit j of vmask when the
-  // position exists (inside a staged block and below K); bit i of pend while word i (position
-  // i >> 1, factor i & 1) is missing
+  // this thread's positions: kpos[j] for p = tid + j * kPosThreads; bit j of vmask when the
+  // position exists (inside a staged block and below K), of pend while its word is missing
   uint32_t kpos[kPosPerThread];
   uint32_t vmask = 0, pend = 0;
 #pragma unroll
   for (int j = 0; j < kPosPerThread; ++j) {
     kpos[j] = 0;
-    const int p = tid + kGatherThreads * j;
-    if (p < nb * 1024) {
+    const int p = tid + kPosThreads * j;
+    if (!comm && p < nb * 1024) {
       const int k = (blk_get(B, p >> 10) & 0xFFFF) * 1024 + (p & 1023);
       if (k < F.k) {
         kpos[j] = (uint32_t)k;
         vmask |= 1u << j;
-        if (live && !direct) pend |= (prod ? 3u : 1u) << (2 * j);
       }
     }
   }
-  constexpr int NW = 2 * kPosPerThread;
-  uint32_t v[NW];
+  if (live && !direct) pend = vmask;
+  uint32_t v[kPosPerThread];
 #pragma unroll
-  for (int i = 0; i < NW; ++i) v[i] = 0;
+  for (int j = 0; j < kPosPerThread; ++j) v[j] = 0;
   auto sweep_pos = [&](int max_sweeps) -> bool {
     for (int it = 0;; ++it) {
-      tagged_t t[NW];
+      tagged_t t[kPosPerThread];
 #pragma unroll
-      for (int i = 0; i < NW; ++i)
-        t[i] = ((pend >> i) & 1u) ? ld_tag_at((i & 1) ? F.y2t : F.yt, kpos[i >> 1]) : 0;
+      for (int j = 0; j < kPosPerThread; ++j) t[j] = ((pend >> j) & 1u) ? ld_tag_at(F.yt, kpos[j]) : 0;
 #pragma unroll
-      for (int i = 0; i < NW; ++i) {
-        if (((pend >> i) & 1u) && tag_of(t[i]) == tag) {
-          pend &= ~(1u << i);
-          v[i] = (uint32_t)t[i];
+      for (int j = 0; j < kPosPerThread; ++j) {
+        if (((pend >> j) & 1u) && tag_of(t[j]) == tag) {
+          pend &= ~(1u << j);
+          v[j] = (uint32_t)t[j];
         }
       }
       if (__builtin_amdgcn_ballot_w64(pend != 0) == 0) return true;
@@ -507,14 +502,13 @@ INL void stage_inputs(PP P, EngLds& L, int s, int w, int tid, bool comm, uint32_
   const bool stats = comm && live && nb > 0 && !direct;
   const tagged_t* sbase = rfl(X->stats);
   const int ns = rfl(X->nstats);
-  const uint32_t stag = eng_tag(epoch, rfl(X->src_stage));
   uint32_t spend = stats ? stats_pending(ns, lane) : 0u, sv[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) sv[i] = 0;
-  bool ready = sweep_pos(1);
+  const bool ready = sweep_pos(1);
   bool stats_in = true;
   if (stats) {
-    stats_in = sweep_stats(sbase, ns, stag, spend, sv, lane, 1, L, error);
+    stats_in = sweep_stats(sbase, ns, tag, spend, sv, lane, 1, L, error);
     if (stats_in) {   // the wave sum runs on every lane; lane 0 stores the result
       const float d = stats_denominator(sv, ns, F.k, X->eps, lane);
       if (lane == 0) L.denom[0] = d;
@@ -524,27 +518,10 @@ INL void stage_inputs(PP P, EngLds& L, int s, int w, int tid, bool comm, uint32_
     __hip_atomic_store(&L.need_poll, s + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   gather_barrier(L, lane, gen, error);
   if (lds_poll_i(&L.need_poll) == s + 1 && live) {
-    if (comm && !direct) {
-      // wait cheaply: the first row of every producer tile of the staged blocks (both factors
-      // of a product source), 64 per load, then the statistics
-      for (int base = 0; base < nb * 32; base += 64) {
-        const int i = base + lane;
-        const int b = i >> 5, f = (i >> 4) & 1, t = i & 15;
-        bool want = false;
-        const tagged_t* q = F.yt;
-        uint32_t got;
-        if (b < nb) {
-          const int k = (blk_get(B, b) & 0xFFFF) * 1024 + t * 64;
-          want = k < F.k && (f == 0 || prod);
-          q = (f ? F.y2t : F.yt) + (want ? k : 0);
-        }
-        if (!wait_words<1>(&q, &want, &tag, &got, error, &L.abort_flag)) break;
-      }
-      if (stats && !stats_in) {
-        sweep_stats(sbase, ns, stag, spend, sv, lane, 0, L, error);
-        const float d = stats_denominator(sv, ns, F.k, X->eps, lane);
-        if (lane == 0) L.denom[0] = d;
-      }
+    if (stats && !stats_in) {
+      sweep_stats(sbase, ns, tag, spend, sv, lane, 0, L, error);
+      const float d = stats_denominator(sv, ns, F.k, X->eps, lane);
+      if (lane == 0) L.denom[0] = d;
     }
     gather_barrier(L, lane, gen, error);
     sweep_pos(0);
@@ -552,44 +529,40 @@ INL void stage_inputs(PP P, EngLds& L, int s, int w, int tid, bool comm, uint32_
   if (direct) {
 #pragma unroll
     for (int j = 0; j < kPosPerThread; ++j)
-      if ((vmask >> j) & 1u) v[2 * j] = g_ld16(F.x + kpos[j]);
+      if ((vmask >> j) & 1u) v[j] = g_ld16(F.x + kpos[j]);
     // Settle these loads here, seen by the compiler: a load whose result is dead on some path
     // would otherwise stay pending as far as it knows, and the first reuse of its register
-    // would then wait for every outstanding memory operation (partial stores in the
-    // communication wave).
+    // would then wait for every outstanding memory operation.
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt and lgkmcnt untouched
+  }
+  // blocks whose record this workgroup writes
+  uint32_t own = 0;
+  uint16_t* rec = rfl(X->record);
+  if (rec != nullptr && live) {
+    MP R = &S->mat[X->rec_mat];
+    for (int b = 0; b < nb; ++b)
+      if (share_has(r, R->unit_base + (blk_get(B, b) & 0xFFFF) * R->tiles)) own |= 1u << b;
   }
   // rescale and stage (the denominator was written before one of the barriers above)
   const float dn = direct ? 1.f : L.denom[0];
 #pragma unroll
   for (int j = 0; j < kPosPerThread; ++j) {
-    const int p = tid + kGatherThreads * j;
-    if (p >= nb * 1024) continue;
-    float xs = 0.f;
+    const int p = tid + kPosThreads * j;
+    if (comm || p >= nb * 1024) continue;
+    uint32_t xb = 0;
     if ((vmask >> j) & 1u) {
       if (direct) {
-        xs = e_bf16(v[2 * j]);
+        xb = v[j];
       } else {
-        float h = e_bf16(v[2 * j]);
-        if (prod) h *= e_bf16(v[2 * j + 1]);
-        xs = e_bf16(e_to_bf16(h / dn));
+        float h = e_bf16(v[j] & 0xFFFFu);
+        if (prod) h *= e_bf16(v[j] >> 16);
+        xb = e_to_bf16(h / dn);
       }
+      if ((own >> (p >> 10)) & 1u) g_st16(rec + kpos[j], xb);
     }
-    L.staging[p >> 10][p & 1023] = xs;
+    L.staging[p >> 10][p & 1023] = e_bf16(xb);
   }
   gather_barrier(L, lane, gen, error);
-  if (comm && live && X->record != nullptr) {
-    // 3. records of the blocks this workgroup owns, from the staged (exactly bf16) values
-    uint16_t* rec = rfl(X->record);
-    MP R = &S->mat[X->rec_mat];
-    for (int b = 0; b < nb; ++b) {
-      const int sg = blk_get(B, b) & 0xFFFF;
-      if (!share_has(r, R->unit_base + sg * R->tiles)) continue;
-      const int n = min(1024, F.k - sg * 1024);
-      for (int q = lane; q < n; q += 64)
-        g_st16(rec + sg * 1024 + q, __float_as_uint(L.staging[b][q]) >> 16);
-    }
-  }
 }
 
 // A stage without matrices (the final rescale of a decode step): the communication wave of each
@@ -613,22 +586,22 @@ INL void slice_stage(PP P, EngLds& L, int s, int w, int lane, uint32_t epoch, ui
   if (!sweep_stats(rfl(X->stats), ns, tag, spend, sv, lane, 0, L, error)) return;
   const float d = stats_denominator(sv, ns, F.k, X->eps, lane);
   // this workgroup's positions: at most four per lane (checked by the host)
-  uint32_t pend = 0, hv[8];
+  uint32_t pend = 0, hv[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    if (a + lane + 64 * j < e) pend |= (prod ? 3u : 1u) << (2 * j);
-    hv[2 * j] = hv[2 * j + 1] = 0;
+    if (a + lane + 64 * j < e) pend |= 1u << j;
+    hv[j] = 0;
   }
   for (int it = 0;; ++it) {
-    tagged_t t[8];
+    tagged_t t[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      t[i] = ((pend >> i) & 1u) ? ld_tag_at((i & 1) ? F.y2t : F.yt, (uint32_t)(a + lane + 64 * (i >> 1))) : 0;
+    for (int j = 0; j < 4; ++j)
+      t[j] = ((pend >> j) & 1u) ? ld_tag_at(F.yt, (uint32_t)(a + lane + 64 * j)) : 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (((pend >> i) & 1u) && tag_of(t[i]) == tag) {
-        pend &= ~(1u << i);
-        hv[i] = (uint32_t)t[i];
+    for (int j = 0; j < 4; ++j) {
+      if (((pend >> j) & 1u) && tag_of(t[j]) == tag) {
+        pend &= ~(1u << j);
+        hv[j] = (uint32_t)t[j];
       }
     }
     if (__builtin_amdgcn_ballot_w64(pend != 0) == 0) break;
@@ -639,8 +612,8 @@ INL void slice_stage(PP P, EngLds& L, int s, int w, int lane, uint32_t epoch, ui
   for (int j = 0; j < 4; ++j) {
     const int k = a + lane + 64 * j;
     if (k >= e) continue;
-    float h = e_bf16(hv[2 * j]);
-    if (prod) h *= e_bf16(hv[2 * j + 1]);
+    float h = e_bf16(hv[j] & 0xFFFFu);
+    if (prod) h *= e_bf16(hv[j] >> 16);
     g_st16(rec + k, e_to_bf16(h / d));
   }
 }
@@ -649,23 +622,30 @@ INL void slice_stage(PP P, EngLds& L, int s, int w, int lane, uint32_t epoch, ui
 // compute waves
 // ------------------------------------------------------------------------------------------
 
-// Sum over one 128-weight group of a row: 32 table lookups (tables of group H of this wave).
-template <int CW, int H>
-INL float lookup_group(const EngLds& L, const uint4 s4) {
-  const char* lb = (const char*)&L.lut[CW][H][0];
-  const uint32_t sd[4] = {s4.x, s4.y, s4.z, s4.w};
-  float pa = 0.f, pb = 0.f;
+// Sums over the two 128-weight groups of this wave's pair for one row: 2 x 32 table lookups,
+// in four independent chains so that the lookups of both groups overlap.
+template <int CW>
+INL void lookup_pair(const EngLds& L, const uint4 sa, const uint4 sb, float& ga, float& gb) {
+  const char* la = (const char*)&L.lut[CW][0][0];
+  const char* lb = (const char*)&L.lut[CW][1][0];
+  const uint32_t da[4] = {sa.x, sa.y, sa.z, sa.w};
+  const uint32_t db[4] = {sb.x, sb.y, sb.z, sb.w};
+  float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    const uint32_t s = sd[d];
-    const uint32_t r = __builtin_amdgcn_alignbit(s, s, 4);
+    const uint32_t s = da[d], t = db[d];
+    const uint32_t rs = __builtin_amdgcn_alignbit(s, s, 4);
+    const uint32_t rt = __builtin_amdgcn_alignbit(t, t, 4);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      pa += *(const float*)(lb + (8 * d + 2 * q) * 64 + e_field(s, q));
-      pb += *(const float*)(lb + (8 * d + 2 * q + 1) * 64 + e_field(r, q));
+      a0 += *(const float*)(la + (8 * d + 2 * q) * 64 + e_field(s, q));
+      a1 += *(const float*)(la + (8 * d + 2 * q + 1) * 64 + e_field(rs, q));
+      b0 += *(const float*)(lb + (8 * d + 2 * q) * 64 + e_field(t, q));
+      b1 += *(const float*)(lb + (8 * d + 2 * q + 1) * 64 + e_field(rt, q));
     }
   }
-  return pa + pb;
+  ga = a0 + a1;
+  gb = b0 + b1;
 }
 
 // Builds this wave's 64 tables of 16 signed sums (32 per group of its pair, staged block b),
@@ -720,13 +700,18 @@ INL void compute_wave(PP P, EngLds& L, int w, int lane, uint32_t epoch, uint32_t
       const uint4 ra = *(const uint4*)(base + kBlock * (1 + 2 * kPair) + lane * 16);
       const uint4 rb = *(const uint4*)(base + kBlock * (2 + 2 * kPair) + lane * 16);
       const uint32_t sw = *(const uint32_t*)(base + lane * 16 + 4 * kPair);
-      // this wave's bytes of the slot are in registers: count the read for the loader
+      float ga, gb;
+      lookup_pair<CW>(L, ra, rb, ga, gb);
+      // the slot's bytes were consumed before the lookups could start: count the read for the
+      // loader (only now, so that no wait stands between the record reads and the lookups)
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       if (lane == 0)
         __hip_atomic_fetch_add(&L.consumed[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      float part = 0.f;
-      if (2 * kPair < ng) part = e_f16(sw & 0xFFFFu) * lookup_group<CW, 0>(L, ra);
-      if (2 * kPair + 1 < ng) part += e_f16(sw >> 16) * lookup_group<CW, 1>(L, rb);
+      // groups missing at a ragged end of K contribute nothing (their table inputs are zero;
+      // the select also keeps their scale bits out)
+      const float sa = 2 * kPair < ng ? e_f16(sw & 0xFFFFu) : 0.f;
+      const float sb = 2 * kPair + 1 < ng ? e_f16(sw >> 16) : 0.f;
+      const float part = sa * ga + sb * gb;
       // hand the partial to the communication wave (the slot's last round must be consumed)
       const unsigned hs = q % kEngHandSlots, round = q / kEngHandSlots;
       if (lds_poll(&L.hfree[hs]) < round) {
@@ -877,7 +862,7 @@ INL void comm_wave(PP P, EngLds& L, int w, int lane, uint32_t epoch, uint32_t* e
 // a matrix and its pair partner (gate and up), from the published block partials, polled in
 // one sweep: bf16 outputs (tagged copy for consumers, plain copy for the caller) and the tile
 // statistic (sum of squares of the outputs, or the pair's sum of (own * partner)^2).
-INL void finalize_item(SP S, EngLds& L, int s, int item, int lane, uint32_t epoch,
+INL void finalize_item(SP S, EngLds& L, int s, int item, int wave, int lane, uint32_t epoch,
                        uint32_t* error) {
   int m = 0;
   for (; m < S->nmat; ++m) {
@@ -895,60 +880,53 @@ INL void finalize_item(SP S, EngLds& L, int s, int item, int lane, uint32_t epoc
   const int ub2 = rfl(M2->unit_base) + tile - s1 * rfl(M2->tiles), t2 = rfl(M2->tiles);
   const tagged_t* part = rfl(S->part);
   const uint32_t tag = eng_tag(epoch, s);
-  {
-    // wait cheaply first: lane i watches the first word of block partial i (one small load per
-    // round trip), then read every lane's words, which are then almost always all there
-    const bool want = lane < n;
-    const int u = lane < s1 ? ub1 + lane * t1 : ub2 + lane * t2;
-    const tagged_t* ptr = part + (size_t)(want ? u : 0) * 64;
-    uint32_t got;
-    if (!wait_words<1>(&ptr, &want, &tag, &got, error, &L.abort_flag)) return;
-  }
-  // full sweeps: every word of the n partials is loaded on every sweep (a retry is rare), so
-  // the loads need no per-lane branches; the sums are formed in partial order as the tags are
-  // checked and simply redone by a retry
-  const tagged_t* pb = part + lane;
-  float y1 = 0.f, y2 = 0.f;
+  // Poll with sweeps that load only the words still missing (this lane's word of each block
+  // partial not yet seen with its tag), so that the sweep after the last arrival completes the
+  // item. The words seen go to this wave's LDS scratch (a finalising workgroup has no ring);
+  // the sums are then formed in partial order.
+  float* seen = (float*)&L.lut[0][0][0] + (size_t)wave * (kEngMaxFinal * 64) + lane;
+  uint32_t pend = n >= 32 ? ~0u : ((1u << n) - 1u);
   for (int it = 0;; ++it) {
     tagged_t t[kEngMaxFinal];
 #pragma unroll
     for (int i = 0; i < kEngMaxFinal; ++i)
-      if (i < n) t[i] = ld_tag(pb + (size_t)(i < s1 ? ub1 + i * t1 : ub2 + i * t2) * 64);
-    bool all = true;
-    y1 = 0.f;
-    y2 = 0.f;
+      t[i] = ((pend >> i) & 1u)
+                 ? ld_tag_at(part, (uint32_t)((i < s1 ? ub1 + i * t1 : ub2 + i * t2) * 64 + lane))
+                 : 0;
 #pragma unroll
     for (int i = 0; i < kEngMaxFinal; ++i) {
-      if (i < n) {
-        all = all && tag_of(t[i]) == tag;
-        if (i < s1) y1 += __uint_as_float((uint32_t)t[i]);
-        else y2 += __uint_as_float((uint32_t)t[i]);
+      if (((pend >> i) & 1u) && tag_of(t[i]) == tag) {
+        pend &= ~(1u << i);
+        seen[i * 64] = __uint_as_float((uint32_t)t[i]);
       }
     }
-    if (__builtin_amdgcn_ballot_w64(!all) == 0) break;
+    if (__builtin_amdgcn_ballot_w64(pend != 0) == 0) break;
     if (poll_expired(it, error, &L.abort_flag)) return;
-    __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_s_sleep(8);
   }
-  // outputs: tagged copies and statistics first (consumers wait on them), plain copies last
+  float y1 = 0.f, y2 = 0.f;
+  for (int i = 0; i < n; ++i) {
+    if (i < s1) y1 += seen[i * 64];
+    else y2 += seen[i * 64];
+  }
+  // outputs: tagged copies and statistics first (consumers wait on them), plain copies last.
+  // A pair's tile goes out as one word per row holding both bf16 outputs (low: this matrix,
+  // high: the partner), so that a consumer of their product reads one word per position.
   const int row = tile * kTileRows + lane;
   const uint32_t b1 = e_to_bf16(y1);
-  st_tag(rfl(M->yt) + row, b1, tag);
+  const uint32_t b2 = m2 >= 0 ? e_to_bf16(y2) : 0u;
+  st_tag(rfl(M->yt) + row, b1 | (b2 << 16), tag);
   const int n1 = rfl(M->n);
   if (rfl(M->kind) == kMatSumSq) {
     const float yv = row < n1 ? e_bf16(b1) : 0.f;
     const float ss = wave_sum(yv * yv);
     if (lane == 0) st_tag(rfl(M->stat) + tile, __float_as_uint(ss), tag);
   }
-  uint32_t b2 = 0;
   const int n2 = rfl(M2->n);
-  if (m2 >= 0) {
-    b2 = e_to_bf16(y2);
-    st_tag(rfl(M2->yt) + row, b2, tag);
-    if (rfl(M2->kind) == kMatPair) {
-      const float h = row < n2 ? e_bf16(b1) * e_bf16(b2) : 0.f;
-      const float ss = wave_sum(h * h);
-      if (lane == 0) st_tag(rfl(M2->stat) + tile, __float_as_uint(ss), tag);
-    }
+  if (m2 >= 0 && rfl(M2->kind) == kMatPair) {
+    const float h = row < n2 ? e_bf16(b1) * e_bf16(b2) : 0.f;
+    const float ss = wave_sum(h * h);
+    if (lane == 0) st_tag(rfl(M2->stat) + tile, __float_as_uint(ss), tag);
   }
   uint16_t* y1p = rfl(M->y);
   uint16_t* y2p = rfl(M2->y);
@@ -956,14 +934,16 @@ INL void finalize_item(SP S, EngLds& L, int s, int item, int lane, uint32_t epoc
   if (m2 >= 0 && y2p && row < n2) g_st16(y2p + row, b2);
 }
 
-// Finalising wave c of nc: items c, c + nc, ... of every stage, in program order.
-INL void final_wave(PP P, EngLds& L, int c, int nc, int lane, uint32_t epoch, uint32_t* error) {
+// Finalising wave c of nc (wave `wave` of its workgroup): items c, c + nc, ... of every stage,
+// in program order.
+INL void final_wave(PP P, EngLds& L, int c, int nc, int wave, int lane, uint32_t epoch,
+                    uint32_t* error) {
   for (int s = 0; s < P->nstages; ++s) {
     SP S = &P->st[s];
     warm_stage(S);
     for (int item = c; item < S->nitems; item += nc) {
       if (lds_poll_i(&L.abort_flag)) return;
-      finalize_item(S, L, s, item, lane, epoch, error);
+      finalize_item(S, L, s, item, wave, lane, epoch, error);
     }
   }
 }
@@ -993,7 +973,7 @@ __global__ __launch_bounds__(kEngThreads) void q1_engine_kernel(EngArgs A) {
   const int nst = P->nstream;
   if (wg >= nst) {   // finalising workgroup: all its waves finalise
     const int nc = (P->nwg - nst) * kEngWaves;
-    final_wave(P, L, (wg - nst) * kEngWaves + wave, nc, lane, A.epoch, A.error);
+    final_wave(P, L, (wg - nst) * kEngWaves + wave, nc, wave, lane, A.epoch, A.error);
     return;
   }
   static_assert(kEngCompute == 12, "one case per compute wave");
@@ -1273,8 +1253,9 @@ lbq_status lbq_engine_gemv_q1(const void* d_w, int32_t n, int32_t k, const uint1
 //  A  : q, k, v (part 0) then gate, up (part 1), input x = rescale of the previous down output
 //       (the caller's x0 for layer 0); q comes first in every workgroup's share so its tiles
 //       are finalised while gate and up still stream;
-//  B1 : o, input rescale(q);
 //  B2 : down, input rescale(gate * up);
+//  B1 : o, input rescale(q). Nothing reads o, so it runs last: its units fill the wait for the
+//       next layer's input instead of delaying down;
 // then a final stage that only rescales the last down output into the caller's record.
 lbq_status lbq_engine_decode_q1(const lbq_q1_layer* layers, int32_t L, int32_t hidden, int32_t kv,
                                 int32_t ffn, const uint16_t* d_x0, uint16_t* d_act, float eps,
@@ -1307,12 +1288,13 @@ lbq_status lbq_engine_decode_q1(const lbq_q1_layer* layers, int32_t L, int32_t h
   auto at = [&](int layer, int slot) {
     return d_act + lbq_decode_act_offset(layer, slot, L, hidden, kv, ffn, 1);
   };
-  auto rms_src = [&](EngSrc& X, int kind, int k, const EngMat& y, const EngMat* y2,
-                     const EngMat& stats, int src_stage, uint16_t* record, int rec_mat) {
+  // an RMS source: the tagged outputs (one word per position; for a product, of the pair's
+  // first matrix, whose words carry both factors) and the producer's tile statistics
+  auto rms_src = [&](EngSrc& X, int kind, int k, const EngMat& y, const EngMat& stats,
+                     int src_stage, uint16_t* record, int rec_mat) {
     X.kind = kind;
     X.k = k;
     X.yt = y.yt;
-    X.y2t = y2 ? y2->yt : nullptr;
     X.stats = stats.stat;
     X.nstats = stats.tiles;
     X.src_stage = src_stage;
@@ -1323,8 +1305,8 @@ lbq_status lbq_engine_decode_q1(const lbq_q1_layer* layers, int32_t L, int32_t h
   const EngMat* prev_down = nullptr;
   for (int l = 0; l < L; ++l) {
     EngStage& A = P->st[3 * l];
-    EngStage& B1 = P->st[3 * l + 1];
-    EngStage& B2 = P->st[3 * l + 2];
+    EngStage& B2 = P->st[3 * l + 1];
+    EngStage& B1 = P->st[3 * l + 2];
     bool ok = eng_mat(A, 0, layers[l].q, hidden, hidden, at(l, LBQ_ACT_Q), 0, kMatSumSq, &cursor);
     ok = ok && eng_mat(A, 1, layers[l].k, kv, hidden, at(l, LBQ_ACT_K), 0, kMatPlain, &cursor);
     ok = ok && eng_mat(A, 2, layers[l].v, kv, hidden, at(l, LBQ_ACT_V), 0, kMatPlain, &cursor);
@@ -1342,7 +1324,7 @@ lbq_status lbq_engine_decode_q1(const lbq_q1_layer* layers, int32_t L, int32_t h
       A.src[0].record = at(l, LBQ_ACT_X);
       A.src[0].rec_mat = 0;
     } else {
-      rms_src(A.src[0], kSrcRms, hidden, *prev_down, nullptr, *prev_down, 3 * l - 1,
+      rms_src(A.src[0], kSrcRms, hidden, *prev_down, *prev_down, 3 * l - 2,
               at(l, LBQ_ACT_X), 0);
     }
     if (!eng_mat(B1, 0, layers[l].o, hidden, hidden, at(l, LBQ_ACT_O), 0, kMatPlain, &cursor))
@@ -1350,18 +1332,18 @@ lbq_status lbq_engine_decode_q1(const lbq_q1_layer* layers, int32_t L, int32_t h
     eng_part(B1, &cursor);
     B1.part0 = B1.units;
     B1.nsrc = 1;
-    rms_src(B1.src[0], kSrcRms, hidden, A.mat[0], nullptr, A.mat[0], 3 * l, at(l, LBQ_ACT_XO), 0);
+    rms_src(B1.src[0], kSrcRms, hidden, A.mat[0], A.mat[0], 3 * l, at(l, LBQ_ACT_XO), 0);
     if (!eng_mat(B2, 0, layers[l].down, hidden, ffn, at(l, LBQ_ACT_DOWN), 0, kMatSumSq, &cursor))
       return LBQ_E_SHAPE;
     eng_part(B2, &cursor);
     B2.part0 = B2.units;
     B2.nsrc = 1;
-    rms_src(B2.src[0], kSrcRmsProd, ffn, A.mat[3], &A.mat[4], A.mat[4], 3 * l, at(l, LBQ_ACT_XD), 0);
+    rms_src(B2.src[0], kSrcRmsProd, ffn, A.mat[3], A.mat[4], 3 * l, at(l, LBQ_ACT_XD), 0);
     prev_down = &B2.mat[0];
   }
   EngStage& F = P->st[3 * L];
   F.nsrc = 1;
-  rms_src(F.src[0], kSrcRms, hidden, *prev_down, nullptr, *prev_down, 3 * L - 1,
+  rms_src(F.src[0], kSrcRms, hidden, *prev_down, *prev_down, 3 * L - 2,
           d_act + lbq_decode_act_offset(L, LBQ_ACT_NSLOTS, L, hidden, kv, ffn, 1), 0);
   if ((size_t)((char*)cursor - (char*)E->ws) > E->ws_bytes) return LBQ_E_NOMEM;   // sizing bug guard
   if (!eng_fits(P)) return LBQ_E_UNSUPPORTED;
