@@ -2,13 +2,13 @@
 //
 // A program is a list of stages. A stage multiplies up to kEngMaxMats Q1_0_g128 matrices with
 // up to kEngMaxSrcs bf16 input vectors (batch 1); the outputs of a stage may feed the inputs of
-// later stages through an RMS rescale. One persistent launch runs the whole program. Streaming
-// workgroups each own an equal, contiguous share of every part of every stage's work units
-// (64 rows x one block of eight 128-weight groups) and publish one partial sum per unit;
-// finalising workgroups (no weight traffic, so their memory round trips stay short) sum the
-// partials of each output tile and publish the outputs and their statistics. Data passes
-// between workgroups as (value, tag) pairs that the reader polls for, so no grid-wide barrier
-// or cache flush is ever needed.
+// later stages through an RMS rescale. One persistent launch runs the whole program. Every
+// workgroup owns an equal, contiguous share of every part of every stage's work units (64 rows x
+// one block of eight 128-weight groups) and publishes one partial sum per unit; it also
+// finalises a round-robin share of every stage's output tiles: it sums the partials of each
+// tile and publishes the outputs and their statistics. Data passes between workgroups as
+// (value, tag) pairs that the reader polls for, so no grid-wide barrier or cache flush is ever
+// needed.
 #pragma once
 
 #include <stdint.h>
@@ -19,17 +19,14 @@ namespace lbq {
 
 constexpr int kEngMaxMats = 5;
 constexpr int kEngMaxSrcs = 2;
-constexpr int kEngPairs = 4;                        // group pairs of a unit (two groups per wave)
-constexpr int kEngPhases = 3;                       // units a workgroup computes at once
-constexpr int kEngCompute = kEngPairs * kEngPhases; // compute waves
+constexpr int kEngCompute = 14;                     // compute waves: one whole unit at a time each
 constexpr int kEngWaves = kEngCompute + 2;          // + one loader wave + one communication wave
 constexpr int kEngThreads = kEngWaves * 64;
-constexpr int kEngRingSlots = 9;                    // units the LDS ring holds
+constexpr int kEngRingSlots = 13;                   // units the LDS ring holds
 constexpr int kEngInFlight = 2;                     // units the loader keeps in flight
-constexpr int kEngHandSlots = 4;                    // partial hand-off slots (compute -> comm)
 constexpr int kEngMaxStages = 255;
 constexpr int kEngMaxFinal = 24;                    // block partials summed by one finalisation
-constexpr int kEngMaxBlocks = 4;                    // input blocks one workgroup stages per stage
+constexpr int kEngMaxBlocks = 2;                    // input blocks one workgroup stages per stage
 
 enum EngSrcKind : int32_t { kSrcDirect = 0, kSrcRms = 1, kSrcRmsProd = 2 };
 enum EngMatKind : int32_t { kMatPlain = 0, kMatSumSq = 1, kMatPair = 2 };
@@ -40,10 +37,13 @@ typedef unsigned long long tagged_t;
 struct EngMat {
   const uint8_t* w;        // Q1 device layout
   uint16_t* y;             // plain bf16 output [n] (may be null)
-  tagged_t* yt;            // tagged bf16 output [np] (with a pair partner: both outputs per word)
+  tagged_t* yt;            // tagged bf16 outputs: one word per two rows (low: the even row), or
+                           // with a pair partner one word per row holding both outputs
   tagged_t* stat;          // tagged per-tile statistic [tiles] (kMatSumSq / kMatPair) or null
   long long tile_bytes;
-  int32_t n, k, tiles, groups, supers, src, kind, unit_base, units;
+  int32_t n, k, tiles, groups, supers, src, kind;
+  int32_t tile_base;       // position of tile 0 in a super-group row of the stage's units
+  int32_t units;           // tiles * supers
   int32_t item_base;       // finalisation item of tile 0 (-1: finalised with its pair partner)
   int32_t pair;            // kMatPair partner finalised together with this matrix, or -1
   int32_t pad;
@@ -66,11 +66,12 @@ struct EngStage {
   tagged_t* part;                      // tagged unit partials [units * 64], one slot per unit
   int32_t nmat, nsrc, units, nitems;   // nitems: tiles to finalise (a pair counts once)
   int32_t part0;                       // units of part 0 (the leading matrices); rest = part 1
-  int32_t pad0, pad1, pad2;
+  int32_t row_tiles;                  // tiles of all matrices: units of one super-group row
+  int32_t pad1, pad2;
 };
 
 struct EngProgram {
-  int32_t nstages, nwg, nstream, pad0;   // workgroups [0, nstream) stream, the rest finalise
+  int32_t nstages, nwg, nstream, pad0;   // nstream: workgroups (all of them stream and finalise)
   EngStage st[1];                        // nstages entries
 };
 

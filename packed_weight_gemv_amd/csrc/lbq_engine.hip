@@ -2,35 +2,34 @@
 // launch per program, one workgroup per compute unit. It runs the whole decode step of a layer
 // stack and single batch-1 GEMVs.
 //
-// A streaming workgroup has 12 compute waves, one loader wave and one communication wave.
+// Every workgroup has 14 compute waves, one loader wave and one communication wave.
 //  * Work unit = 64 rows (one lane per row) x one super-group of eight 128-weight groups: 9 KiB
 //    of contiguous device-layout bytes (the 64 x 8 fp16 scales, then one sign record per group).
-//    Each workgroup owns an equal, contiguous share of every stage's units and walks its shares
-//    in program order.
+//    Each workgroup owns an equal, contiguous share of every stage's units (ordered super-group,
+//    matrix, tile, so a share reads at most two 1024-wide input blocks) and walks its shares in
+//    program order.
 //  * The loader wave copies units straight into an LDS ring with nontemporal global_load_lds,
 //    keeping only kEngInFlight units in flight. That is enough for the compute unit's share of
 //    HBM bandwidth, and it keeps the queue in front of the workgroup's other memory operations
-//    (input loads, partial stores) short. The ring itself is deeper, so the copies run ahead
-//    across stage boundaries while a stage waits for its inputs. Weights never depend on
-//    activations.
-//  * Compute wave (pair p, phase f) handles groups 2p and 2p+1 of the units whose position in
-//    the sequence is f modulo 3, so three units are computed at once. It does no global
-//    memory access at all in its unit loop: per 4 weights it adds one entry of a 16-entry table
-//    of signed sums of 4 inputs, built in LDS from the stage's input vector. The 4-bit field
-//    times 4 is the entry's byte offset, extracted with one masked operand select: the packer
-//    stores each sign dword rotated left by two, so every field sits at bits [8i+2, 8i+5] of the
-//    dword or of its rotation by four.
-//  * The communication wave sums the four pair partials of each unit and publishes the unit
-//    partial as a (value, tag) word in the stage's partial array.
-//  * Finalising workgroups (no weight traffic, so their memory round trips stay short) sum the
-//    partials of each output tile and publish the outputs and their statistics; a gate tile is
-//    finalised together with the matching up tile, so the pair statistic needs no second
-//    exchange.
-//  * At a stage start the compute and communication waves fetch the stage's input blocks in one
-//    sweep of tagged loads (the communication wave fetches the producers' tile statistics in the
-//    same trip) and apply the RMS rescale. Consumers poll tags; there is no grid barrier and no
-//    cache flush. Every wait is bounded: on a time-out the error word is set and every wave runs
-//    to the end without further work.
+//    (input loads, partial stores) short. The ring itself is deeper (a stage's whole share,
+//    typically), so the copies run ahead across stage boundaries while a stage waits for its
+//    inputs. Weights never depend on activations.
+//  * The compute waves take the jobs of a stage round-robin; a job is one pair of 128-weight
+//    groups of one unit. Per 4 weights a job adds one entry of a 16-entry table of signed sums
+//    of 4 inputs, built in LDS from the stage's input vector when the stage starts. The 4-bit
+//    field times 4 is the entry's byte offset, extracted with one masked operand select: the
+//    packer stores each sign dword rotated left by two, so every field sits at bits [8i+2, 8i+5]
+//    of the dword or of its rotation by four. The last of a unit's four jobs sums the pair
+//    partials and publishes the unit partial as a (value, tag) word.
+//  * The communication wave gathers the producers' statistics at each stage start and finalises
+//    the workgroup's round-robin share of every stage's output tiles: it sums their unit
+//    partials and publishes the outputs and statistics (a gate tile together with the matching
+//    up tile, so the pair statistic needs no second exchange).
+//  * At a stage start the compute waves fetch the stage's input blocks in one sweep of tagged
+//    loads while the communication wave fetches the producers' tile statistics, and they apply
+//    the RMS rescale. Consumers poll tags; there is no grid barrier and no cache flush. Every
+//    wait is bounded: on a time-out the error word is set and every wave runs to the end without
+//    further work.
 #include <hip/hip_runtime.h>
 #include <stdlib.h>
 #include <string.h>
@@ -159,35 +158,35 @@ INL uint32_t lds_addr(T* p) {
 }
 
 constexpr int kUnitBytes = kBlock * (1 + kSuper);        // one unit: scales + eight records
-constexpr int kGatherWaves = kEngCompute + 1;              // compute waves + communication wave
-constexpr int kGatherThreads = kGatherWaves * 64;
+constexpr int kGatherWaves = kEngCompute;                  // the compute waves gather stage inputs
+constexpr int kStatsWave = kEngCompute - 1;               // ... and this one the statistics (it has no chunks)
 constexpr int kLoaderWave = kEngCompute;
+constexpr int kCommWave = kEngCompute + 1;
+
 
 // Ring slot bookkeeping the loader writes before a unit's copy and the compute waves read.
 struct SlotMeta {
-  int32_t blk;   // staging block holding the unit's inputs
+  int32_t blk;   // input block (table set) of the unit's super-group
   int32_t ng;    // groups present in the unit's super-group (eight unless K ends inside it)
+  int32_t u;     // the unit's index within its stage
+  int32_t pad;
 };
 
 // The lookup tables come first: every table entry's LDS address then fits the 16-bit
 // immediate offset of ds_read, so a lookup's address is the extracted field alone.
 struct __attribute__((aligned(16))) EngLds {
-  float lut[kEngCompute][2][32 * 16];                  // [compute wave][group of its pair][chunk*16 + entry]
-  float staging[kEngMaxBlocks][1024];                  // the stage's input blocks (exact bf16 values)
-  unsigned long long hand[kEngHandSlots][kEngPairs][64];   // compute -> comm: (partial | (round + 1) << 32)
-  uint8_t ring[kEngRingSlots][kUnitBytes];             // units copied by the loader
+  float lut[kEngMaxBlocks][kSuper][32 * 16];    // [input block][group][chunk*16 + entry]
+  uint8_t ring[kEngRingSlots][kUnitBytes];      // units copied by the loader
+  float fin[kEngMaxFinal][64];                  // the communication wave's finalisation scratch
   SlotMeta meta[kEngRingSlots];
-  uint32_t consumed[kEngRingSlots];                    // compute-wave reads of each slot so far
-  uint32_t hfree[kEngHandSlots];                       // hand-off rounds the comm wave has consumed
-  uint32_t ready;                                      // units [0, ready) of the sequence have landed
-  uint32_t bar_count, bar_gen;                         // barrier of the gathering waves
-  int32_t need_poll;                                   // stage + 1 once a gathering wave missed a word
-  float denom[kEngMaxSrcs];
+  uint32_t consumed[kEngRingSlots];             // units of each slot the compute waves have summed
+  uint32_t jobs_done[kEngRingSlots];            // pair jobs of each slot done so far (4 per unit)
+  uint32_t ready;                               // units [0, ready) of the sequence have landed
+  uint32_t bar_count, bar_gen;                  // barrier of the gathering waves
+  float denom;                                  // RMS denominator of the stage's source
   int32_t abort_flag;
 };
 static_assert(sizeof(EngLds) <= 160 * 1024, "the engine's LDS must fit one compute unit");
-static_assert(kEngWaves * kEngMaxFinal * 64 * 4 <= offsetof(EngLds, meta),
-              "a finalising workgroup's scratch lies within its unused tables, staging and ring");
 
 // A streaming workgroup's units of a stage: range [a0, b0) of part 0, then [a1, b1) of part 1.
 struct Share {
@@ -205,18 +204,21 @@ INL Share stage_share(SP S, int w, int n) {
 INL int share_units(const Share& r) { return (r.b0 - r.a0) + (r.b1 - r.a1); }
 INL bool share_has(const Share& r, int u) { return (u >= r.a0 && u < r.b0) || (u >= r.a1 && u < r.b1); }
 
-// (matrix, super-group, tile) of stage unit u; units are ordered matrix, super-group, tile.
+// (matrix, super-group, tile) of stage unit u. Units are ordered super-group, then matrix, then
+// tile: a super-group row holds row_tiles units, every matrix's tiles at its tile_base (all
+// matrices of a stage share K), so a contiguous share of units needs few input blocks.
 struct UnitPos {
   int m, sg, tile;
 };
 INL UnitPos unit_pos(SP S, int u) {
-  int m = 0;
-  while (u >= S->mat[m].unit_base + S->mat[m].units) ++m;
+  const int rt = S->row_tiles;
   UnitPos r;
+  r.sg = u / rt;
+  const int t = u - r.sg * rt;
+  int m = 0;
+  while (t >= S->mat[m].tile_base + S->mat[m].tiles) ++m;
   r.m = m;
-  const int k = u - S->mat[m].unit_base;
-  r.sg = k / S->mat[m].tiles;
-  r.tile = k - r.sg * S->mat[m].tiles;
+  r.tile = t - S->mat[m].tile_base;
   return r;
 }
 
@@ -383,8 +385,6 @@ INL void gather_barrier(EngLds& L, int lane, uint32_t& gen, uint32_t* error) {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-constexpr int kPosThreads = kEngCompute * 64;   // the compute waves load the input positions
-constexpr int kPosPerThread = (kEngMaxBlocks * 1024 + kPosThreads - 1) / kPosThreads;
 
 // Tagged word idx of a uniform base (32-bit index: the load takes a scalar base and a vector
 // offset).
@@ -411,7 +411,7 @@ INL bool sweep_stats(const tagged_t* base, int n, uint32_t tag, uint32_t& pend, 
     if (__builtin_amdgcn_ballot_w64(pend != 0) == 0) return true;
     if (max_sweeps > 0 && it + 1 >= max_sweeps) return false;
     if (poll_expired(it, error, &L.abort_flag)) return false;
-    __builtin_amdgcn_s_sleep(2);
+    __builtin_amdgcn_s_sleep(8);
   }
 }
 INL uint32_t stats_pending(int n, int lane) {
@@ -431,27 +431,47 @@ INL float stats_denominator(const uint32_t (&sv)[8], int n, int k, float eps, in
   return sqrtf(wave_sum(part) / (float)k + eps);
 }
 
-// Stage-start duties of a streaming workgroup, run by every gathering wave (tid = its thread
-// index among them; the communication wave has the last 64). A stage reads one source vector;
-// a position of an RMS source is one tagged word (a product source holds both factors in it).
-//  1. one optimistic sweep: every compute-wave thread loads its positions of the share's (at
-//     most four) 1024-wide input blocks while the communication wave loads the producers' tile
-//     statistics and, when they are all in, turns them into the RMS denominator. When the
-//     producers are done, that is the only round trip. Otherwise the communication wave polls
-//     the statistics (the producers write them after their outputs) until they are all in, and
-//     every compute-wave thread then sweeps again for its missing words;
-//  2. after a barrier every thread rescales its positions to bf16, stores them to the staging
-//     area and, for the blocks whose tile-0 unit (of the source's record matrix) this workgroup
-//     owns, to the caller's record.
-INL void stage_inputs(PP P, EngLds& L, int s, int w, int tid, bool comm, uint32_t epoch,
+// Entries of one table of 16 signed sums of four inputs x0..x3, written to dst[0..15]: entry
+// e = m + 4 j is pair term m of (x0, x1) plus pair term j of (x2, x3), where pair term 0 = -a-b,
+// 1 = a-b, 2 = b-a, 3 = a+b (bit i of e set: input i enters with +).
+INL void write_table(float* dst, float x0, float x1, float x2, float x3) {
+  const float p0 = -x0 - x1, p1 = x0 - x1, p2 = x1 - x0, p3 = x0 + x1;
+  const float q0 = -x2 - x3, q1 = x2 - x3, q2 = x3 - x2, q3 = x2 + x3;
+  float4* d = (float4*)dst;
+  d[0] = make_float4(p0 + q0, p1 + q0, p2 + q0, p3 + q0);
+  d[1] = make_float4(p0 + q1, p1 + q1, p2 + q1, p3 + q1);
+  d[2] = make_float4(p0 + q2, p1 + q2, p2 + q2, p3 + q2);
+  d[3] = make_float4(p0 + q3, p1 + q3, p2 + q3, p3 + q3);
+}
+
+// The input positions come in chunks of four (one table each): chunk ch of the staged blocks is
+// block ch >> 8, positions 4 (ch & 255) .. +3 of that block, i.e. table ch & 31 of group
+// (ch >> 5) & 7. The compute waves load and tabulate them.
+constexpr int kChunkThreads = kEngCompute * 64;
+constexpr int kChunksPerThread = (kEngMaxBlocks * 256 + kChunkThreads - 1) / kChunkThreads;
+constexpr int kPosPerThread = 4 * kChunksPerThread;
+
+// Stage-start duties of a workgroup, run by every gathering wave (tid = its thread index among
+// them; the communication wave has the last 64). A stage reads one source vector; a position of
+// an RMS source is half a tagged word (a product source: one word holding both factors).
+//  1. every compute-wave thread polls its chunks of the share's (at most two) 1024-wide input
+//     blocks, loading only its words still missing on each sweep, while the communication wave
+//     polls the producers' tile statistics the same way and turns them into the RMS
+//     denominator;
+//  2. after a barrier every compute-wave thread rescales its positions to bf16, writes its
+//     chunks' tables and, for the blocks whose tile-0 unit (of the source's record matrix)
+//     this workgroup owns, its positions of the caller's record; a second barrier ends the
+//     stage start.
+INL void stage_inputs(PP P, EngLds& L, int s, int w, int cw, int lane, uint32_t epoch,
                       uint32_t* error, uint32_t& gen) {
   SP S = &P->st[s];
   XP X = &S->src[0];
   const int nst = P->nstream;
-  const int lane = tid & 63;
+  const int tid = cw * 64 + lane;
+  const bool comm = cw == kStatsWave;   // polls the statistics (and has no chunks)
   const Share r = stage_share(S, w, nst);
   const Blocks B = stage_blocks(S, r);
-  if (comm && B.n > kEngMaxBlocks) {
+  if (cw == 0 && B.n > kEngMaxBlocks) {
     set_err(error);
     L.abort_flag = 1;
   }
@@ -460,42 +480,55 @@ INL void stage_inputs(PP P, EngLds& L, int s, int w, int tid, bool comm, uint32_
   const SrcFields F = src_fields(X);
   const bool direct = F.kind == kSrcDirect, prod = F.kind == kSrcRmsProd;
   const uint32_t tag = eng_tag(epoch, F.src_stage);
-  // this thread's positions: kpos[j] for p = tid + j * kPosThreads; bit j of vmask when the
-  // position exists (inside a staged block and below K), of pend while its word is missing
-  uint32_t kpos[kPosPerThread];
-  uint32_t vmask = 0, pend = 0;
+  // this thread's chunks (ch = tid + j * kChunkThreads) and positions (4 j + i: k0[j] + i);
+  // bit j of cmask when the chunk exists, bit 4 j + i of vmask when the position is below K,
+  // of pend while its word is missing
+  uint32_t k0[kChunksPerThread];
+  uint32_t cmask = 0, vmask = 0, pend = 0;
 #pragma unroll
-  for (int j = 0; j < kPosPerThread; ++j) {
-    kpos[j] = 0;
-    const int p = tid + kPosThreads * j;
-    if (!comm && p < nb * 1024) {
-      const int k = (blk_get(B, p >> 10) & 0xFFFF) * 1024 + (p & 1023);
-      if (k < F.k) {
-        kpos[j] = (uint32_t)k;
-        vmask |= 1u << j;
-      }
+  for (int j = 0; j < kChunksPerThread; ++j) {
+    k0[j] = 0;
+    const int ch = tid + kChunkThreads * j;
+    if (ch < nb * 256) {
+      const int k = (blk_get(B, ch >> 8) & 0xFFFF) * 1024 + 4 * (ch & 255);
+      k0[j] = (uint32_t)k;
+      cmask |= 1u << j;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (k + i < F.k) vmask |= 1u << (4 * j + i);
     }
   }
-  if (live && !direct) pend = vmask;
+  // a chunk's words: four (one per position) for a product source, else two (two positions
+  // each, the even one low); word slot i of chunk j is v[4 j + i]. K is a multiple of 128, so a
+  // chunk's positions are all below K or all above.
+  const uint32_t wmask = prod ? 0xFu : 0x3u;
+  if (live && !direct) {
+#pragma unroll
+    for (int j = 0; j < kChunksPerThread; ++j)
+      if ((vmask >> (4 * j)) & 1u) pend |= wmask << (4 * j);
+  }
   uint32_t v[kPosPerThread];
 #pragma unroll
-  for (int j = 0; j < kPosPerThread; ++j) v[j] = 0;
+  for (int i = 0; i < kPosPerThread; ++i) v[i] = 0;
   auto sweep_pos = [&](int max_sweeps) -> bool {
     for (int it = 0;; ++it) {
       tagged_t t[kPosPerThread];
 #pragma unroll
-      for (int j = 0; j < kPosPerThread; ++j) t[j] = ((pend >> j) & 1u) ? ld_tag_at(F.yt, kpos[j]) : 0;
+      for (int i = 0; i < kPosPerThread; ++i)
+        t[i] = ((pend >> i) & 1u)
+                   ? ld_tag_at(F.yt, (prod ? k0[i >> 2] : k0[i >> 2] >> 1) + (i & 3))
+                   : 0;
 #pragma unroll
-      for (int j = 0; j < kPosPerThread; ++j) {
-        if (((pend >> j) & 1u) && tag_of(t[j]) == tag) {
-          pend &= ~(1u << j);
-          v[j] = (uint32_t)t[j];
+      for (int i = 0; i < kPosPerThread; ++i) {
+        if (((pend >> i) & 1u) && tag_of(t[i]) == tag) {
+          pend &= ~(1u << i);
+          v[i] = (uint32_t)t[i];
         }
       }
       if (__builtin_amdgcn_ballot_w64(pend != 0) == 0) return true;
       if (max_sweeps > 0 && it + 1 >= max_sweeps) return false;
       if (poll_expired(it, error, &L.abort_flag)) return false;
-      __builtin_amdgcn_s_sleep(2);
+      __builtin_amdgcn_s_sleep(8);
     }
   };
   // statistics (communication wave)
@@ -505,31 +538,20 @@ INL void stage_inputs(PP P, EngLds& L, int s, int w, int tid, bool comm, uint32_
   uint32_t spend = stats ? stats_pending(ns, lane) : 0u, sv[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) sv[i] = 0;
-  const bool ready = sweep_pos(1);
-  bool stats_in = true;
+  // Every thread polls its own missing words and the communication wave the statistics, each
+  // poll also being the fetch; the loads of a sweep are only the words still missing, so the
+  // sweep after the last producer's arrival completes the gather.
+  sweep_pos(0);
   if (stats) {
-    stats_in = sweep_stats(sbase, ns, tag, spend, sv, lane, 1, L, error);
-    if (stats_in) {   // the wave sum runs on every lane; lane 0 stores the result
-      const float d = stats_denominator(sv, ns, F.k, X->eps, lane);
-      if (lane == 0) L.denom[0] = d;
-    }
+    sweep_stats(sbase, ns, tag, spend, sv, lane, 0, L, error);
+    const float d = stats_denominator(sv, ns, F.k, X->eps, lane);   // every lane takes part
+    if (lane == 0) L.denom = d;
   }
-  if (!(ready && stats_in) && lane == 0)
-    __hip_atomic_store(&L.need_poll, s + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   gather_barrier(L, lane, gen, error);
-  if (lds_poll_i(&L.need_poll) == s + 1 && live) {
-    if (stats && !stats_in) {
-      sweep_stats(sbase, ns, tag, spend, sv, lane, 0, L, error);
-      const float d = stats_denominator(sv, ns, F.k, X->eps, lane);
-      if (lane == 0) L.denom[0] = d;
-    }
-    gather_barrier(L, lane, gen, error);
-    sweep_pos(0);
-  }
   if (direct) {
 #pragma unroll
-    for (int j = 0; j < kPosPerThread; ++j)
-      if ((vmask >> j) & 1u) v[j] = g_ld16(F.x + kpos[j]);
+    for (int i = 0; i < kPosPerThread; ++i)
+      if ((vmask >> i) & 1u) v[i] = g_ld16(F.x + k0[i >> 2] + (i & 3));
     // Settle these loads here, seen by the compiler: a load whose result is dead on some path
     // would otherwise stay pending as far as it knows, and the first reuse of its register
     // would then wait for every outstanding memory operation.
@@ -541,26 +563,33 @@ INL void stage_inputs(PP P, EngLds& L, int s, int w, int tid, bool comm, uint32_
   if (rec != nullptr && live) {
     MP R = &S->mat[X->rec_mat];
     for (int b = 0; b < nb; ++b)
-      if (share_has(r, R->unit_base + (blk_get(B, b) & 0xFFFF) * R->tiles)) own |= 1u << b;
+      if (share_has(r, (blk_get(B, b) & 0xFFFF) * rfl(S->row_tiles) + R->tile_base)) own |= 1u << b;
   }
-  // rescale and stage (the denominator was written before one of the barriers above)
-  const float dn = direct ? 1.f : L.denom[0];
+  // rescale, record and tabulate (the denominator was written before a barrier above)
+  const float dn = direct ? 1.f : L.denom;
 #pragma unroll
-  for (int j = 0; j < kPosPerThread; ++j) {
-    const int p = tid + kPosThreads * j;
-    if (comm || p >= nb * 1024) continue;
-    uint32_t xb = 0;
-    if ((vmask >> j) & 1u) {
-      if (direct) {
-        xb = v[j];
-      } else {
-        float h = e_bf16(v[j] & 0xFFFFu);
-        if (prod) h *= e_bf16(v[j] >> 16);
-        xb = e_to_bf16(h / dn);
+  for (int j = 0; j < kChunksPerThread; ++j) {
+    if (!((cmask >> j) & 1u)) continue;
+    const int ch = tid + kChunkThreads * j;
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pi = 4 * j + i;
+      uint32_t xb = 0;
+      if ((vmask >> pi) & 1u) {
+        if (direct) {
+          xb = v[pi];
+        } else if (prod) {
+          xb = e_to_bf16(e_bf16(v[pi] & 0xFFFFu) * e_bf16(v[pi] >> 16) / dn);
+        } else {
+          const uint32_t wd = v[4 * j + (i >> 1)];
+          xb = e_to_bf16(e_bf16((i & 1) ? (wd >> 16) : (wd & 0xFFFFu)) / dn);
+        }
+        if ((own >> (ch >> 8)) & 1u) g_st16(rec + k0[j] + i, xb);
       }
-      if ((own >> (p >> 10)) & 1u) g_st16(rec + kpos[j], xb);
+      x[i] = e_bf16(xb);
     }
-    L.staging[p >> 10][p & 1023] = e_bf16(xb);
+    write_table(&L.lut[ch >> 8][0][0] + (ch & 255) * 16, x[0], x[1], x[2], x[3]);
   }
   gather_barrier(L, lane, gen, error);
 }
@@ -596,7 +625,9 @@ INL void slice_stage(PP P, EngLds& L, int s, int w, int lane, uint32_t epoch, ui
     tagged_t t[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      t[j] = ((pend >> j) & 1u) ? ld_tag_at(F.yt, (uint32_t)(a + lane + 64 * j)) : 0;
+      t[j] = ((pend >> j) & 1u)
+                 ? ld_tag_at(F.yt, (uint32_t)(prod ? a + lane + 64 * j : (a + lane + 64 * j) >> 1))
+                 : 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (((pend >> j) & 1u) && tag_of(t[j]) == tag) {
@@ -612,22 +643,140 @@ INL void slice_stage(PP P, EngLds& L, int s, int w, int lane, uint32_t epoch, ui
   for (int j = 0; j < 4; ++j) {
     const int k = a + lane + 64 * j;
     if (k >= e) continue;
-    float h = e_bf16(hv[j] & 0xFFFFu);
-    if (prod) h *= e_bf16(hv[j] >> 16);
+    const float h = prod ? e_bf16(hv[j] & 0xFFFFu) * e_bf16(hv[j] >> 16)
+                         : e_bf16((k & 1) ? (hv[j] >> 16) : (hv[j] & 0xFFFFu));
     g_st16(rec + k, e_to_bf16(h / d));
   }
+}
+
+// ------------------------------------------------------------------------------------------
+// finalisation of output tiles (run by the communication waves)
+// ------------------------------------------------------------------------------------------
+
+// An output tile to finalise (item of a stage): tile `tile` of matrix m (and of its pair
+// partner m2, or m2 < 0). Its n block partials lie at units ub1 + i * rt (i < s1, from m) and
+// ub2 + i * rt (i >= s1, from the partner).
+struct Item {
+  int m, m2, tile, s1, n, ub1, ub2;
+};
+INL Item item_of(SP S, int item) {
+  Item it;
+  int m = 0;
+  for (; m < S->nmat; ++m) {
+    const int b = S->mat[m].item_base;
+    if (b >= 0 && item >= b && item < b + S->mat[m].tiles) break;
+  }
+  it.m = m;
+  it.m2 = -1;
+  it.tile = it.s1 = it.n = it.ub1 = it.ub2 = 0;
+  if (m == S->nmat) return it;   // not produced by the host
+  MP M = &S->mat[m];
+  it.tile = item - M->item_base;
+  it.m2 = M->pair;
+  MP M2 = &S->mat[it.m2 < 0 ? m : it.m2];
+  const int rt = S->row_tiles;
+  it.s1 = M->supers;
+  it.n = it.s1 + (it.m2 < 0 ? 0 : M2->supers);
+  it.ub1 = M->tile_base + it.tile;
+  it.ub2 = M2->tile_base + it.tile - it.s1 * rt;
+  return it;
+}
+INL int item_unit(const Item& it, int i, int rt) { return (i < it.s1 ? it.ub1 : it.ub2) + i * rt; }
+
+// The outputs of a finalised tile from its sums y1 (matrix m) and y2 (the partner): tagged
+// copies and statistics first (consumers wait on them), plain copies last. A pair's tile goes
+// out as one word per row holding both bf16 outputs (low: this matrix, high: the partner), so
+// that a consumer of their product reads one word per position; any other tile as one word per
+// two rows (low: the even row).
+INL void tile_outputs(SP S, const Item& it, float y1, float y2, uint32_t tag, int lane) {
+  MP M = &S->mat[it.m];
+  MP M2 = &S->mat[it.m2 < 0 ? it.m : it.m2];
+  const int row = it.tile * kTileRows + lane;
+  const uint32_t b1 = e_to_bf16(y1);
+  const uint32_t b2 = it.m2 >= 0 ? e_to_bf16(y2) : 0u;
+  if (it.m2 >= 0) {
+    st_tag(rfl(M->yt) + row, b1 | (b2 << 16), tag);
+  } else {
+    const uint32_t odd = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)b1, 0xB1, 0xF, 0xF, false);
+    if ((lane & 1) == 0) st_tag(rfl(M->yt) + row / 2, b1 | (odd << 16), tag);
+  }
+  const int n1 = rfl(M->n);
+  if (rfl(M->kind) == kMatSumSq) {
+    const float yv = row < n1 ? e_bf16(b1) : 0.f;
+    const float ss = wave_sum(yv * yv);
+    if (lane == 0) st_tag(rfl(M->stat) + it.tile, __float_as_uint(ss), tag);
+  }
+  const int n2 = rfl(M2->n);
+  if (it.m2 >= 0 && rfl(M2->kind) == kMatPair) {
+    const float h = row < n2 ? e_bf16(b1) * e_bf16(b2) : 0.f;
+    const float ss = wave_sum(h * h);
+    if (lane == 0) st_tag(rfl(M2->stat) + it.tile, __float_as_uint(ss), tag);
+  }
+  uint16_t* y1p = rfl(M->y);
+  uint16_t* y2p = rfl(M2->y);
+  if (y1p && row < n1) g_st16(y1p + row, b1);
+  if (it.m2 >= 0 && y2p && row < n2) g_st16(y2p + row, b2);
+}
+
+// Finalises items a and, when `two`, b of stage S (number s) together: the two tiles' block
+// partials (at most kEngMaxFinal in all) are polled in the same sweeps, each loading only the
+// words still missing (this lane's word of each partial not yet seen with its tag), so that the
+// sweep after the last arrival completes both: a poll is also the fetch. The words seen go to
+// the communication wave's LDS scratch; the sums are then formed in partial order.
+INL void finalize_items(SP S, EngLds& L, int s, const Item& a, const Item& b, bool two, int lane,
+                        uint32_t epoch, uint32_t* error) {
+  const int rt = rfl(S->row_tiles);
+  const tagged_t* part = rfl(S->part);
+  const uint32_t tag = eng_tag(epoch, s);
+  const int na = a.n, ntot = na + (two ? b.n : 0);
+  float* seen = &L.fin[0][lane];
+  uint32_t pend = ntot >= 32 ? ~0u : ((1u << ntot) - 1u);
+  for (int it = 0;; ++it) {
+    tagged_t t[kEngMaxFinal];
+#pragma unroll
+    for (int i = 0; i < kEngMaxFinal; ++i) {
+      const int u = i < na ? item_unit(a, i, rt) : item_unit(b, i - na, rt);
+      t[i] = ((pend >> i) & 1u) ? ld_tag_at(part, (uint32_t)(u * 64 + lane)) : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < kEngMaxFinal; ++i) {
+      if (((pend >> i) & 1u) && tag_of(t[i]) == tag) {
+        pend &= ~(1u << i);
+        seen[i * 64] = __uint_as_float((uint32_t)t[i]);
+      }
+    }
+    if (__builtin_amdgcn_ballot_w64(pend != 0) == 0) break;
+    if (poll_expired(it, error, &L.abort_flag)) return;
+    __builtin_amdgcn_s_sleep(8);
+  }
+  float y1 = 0.f, y2 = 0.f;
+  for (int i = 0; i < na; ++i) {
+    if (i < a.s1) y1 += seen[i * 64];
+    else y2 += seen[i * 64];
+  }
+  tile_outputs(S, a, y1, y2, tag, lane);
+  if (!two) return;
+  y1 = 0.f;
+  y2 = 0.f;
+  for (int i = 0; i < b.n; ++i) {
+    if (i < b.s1) y1 += seen[(na + i) * 64];
+    else y2 += seen[(na + i) * 64];
+  }
+  tile_outputs(S, b, y1, y2, tag, lane);
 }
 
 // ------------------------------------------------------------------------------------------
 // compute waves
 // ------------------------------------------------------------------------------------------
 
-// Sums over the two 128-weight groups of this wave's pair for one row: 2 x 32 table lookups,
-// in four independent chains so that the lookups of both groups overlap.
-template <int CW>
-INL void lookup_pair(const EngLds& L, const uint4 sa, const uint4 sb, float& ga, float& gb) {
-  const char* la = (const char*)&L.lut[CW][0][0];
-  const char* lb = (const char*)&L.lut[CW][1][0];
+// Sums over groups G and G+1 of a row (input block B): 2 x 32 table lookups in four
+// independent chains, so that the lookups of both groups overlap. The records are read here.
+template <int B, int G>
+INL void lookup_two(const EngLds& L, const uint8_t* rec, float& ga, float& gb) {
+  const uint4 sa = *(const uint4*)(rec + kBlock * (1 + G));
+  const uint4 sb = *(const uint4*)(rec + kBlock * (2 + G));
+  const char* la = (const char*)&L.lut[B][G][0];
+  const char* lb = (const char*)&L.lut[B][G + 1][0];
   const uint32_t da[4] = {sa.x, sa.y, sa.z, sa.w};
   const uint32_t db[4] = {sb.x, sb.y, sb.z, sb.w};
   float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
@@ -648,28 +797,30 @@ INL void lookup_pair(const EngLds& L, const uint4 sa, const uint4 sb, float& ga,
   gb = b0 + b1;
 }
 
-// Builds this wave's 64 tables of 16 signed sums (32 per group of its pair, staged block b),
-// one table per lane. Entry e = m + 4 j of the table for inputs (x0, x1, x2, x3) is pair term
-// m of (x0, x1) plus pair term j of (x2, x3), where pair term 0 = -a-b, 1 = a-b, 2 = b-a,
-// 3 = a+b (bit i of e set: input i enters with +).
-template <int CW>
-INL void build_lut(EngLds& L, int b, int lane) {
-  constexpr int kPair = CW % kEngPairs;
-  const int h = lane >> 5, c = lane & 31;
-  const float4 xv = *(const float4*)&L.staging[b][kGroup * (2 * kPair + h) + 4 * c];
-  const float p0 = -xv.x - xv.y, p1 = xv.x - xv.y, p2 = xv.y - xv.x, p3 = xv.x + xv.y;
-  const float q0 = -xv.z - xv.w, q1 = xv.z - xv.w, q2 = xv.w - xv.z, q3 = xv.z + xv.w;
-  float4* dst = (float4*)&L.lut[CW][h][c * 16];
-  dst[0] = make_float4(p0 + q0, p1 + q0, p2 + q0, p3 + q0);
-  dst[1] = make_float4(p0 + q1, p1 + q1, p2 + q1, p3 + q1);
-  dst[2] = make_float4(p0 + q2, p1 + q2, p2 + q2, p3 + q2);
-  dst[3] = make_float4(p0 + q3, p1 + q3, p2 + q3, p3 + q3);
+// Group pair p of a unit whose tables are input block blk: one code path per (block, pair), so
+// that every table offset is an immediate.
+INL void pair_sums(const EngLds& L, int blk, int p, const uint8_t* rec, float& ga, float& gb) {
+  switch (blk * 4 + p) {
+    case 0: lookup_two<0, 0>(L, rec, ga, gb); break;
+    case 1: lookup_two<0, 2>(L, rec, ga, gb); break;
+    case 2: lookup_two<0, 4>(L, rec, ga, gb); break;
+    case 3: lookup_two<0, 6>(L, rec, ga, gb); break;
+    case 4: lookup_two<1, 0>(L, rec, ga, gb); break;
+    case 5: lookup_two<1, 2>(L, rec, ga, gb); break;
+    case 6: lookup_two<1, 4>(L, rec, ga, gb); break;
+    default: lookup_two<1, 6>(L, rec, ga, gb); break;
+  }
 }
+static_assert(kEngMaxBlocks == 2, "one table set per block in pair_sums");
+static_assert(kStatsWave * 64 >= kEngMaxBlocks * 256, "the statistics wave has no input chunks");
 
-// Compute wave CW: pair p = CW % 4 (groups 2p, 2p+1) of the units q with q % 3 == CW / 4.
-template <int CW>
-INL void compute_wave(PP P, EngLds& L, int w, int lane, uint32_t epoch, uint32_t* error) {
-  constexpr int kPair = CW % kEngPairs, kPhase = CW / kEngPairs;
+// Compute wave cw. A job is one group pair of one unit (job j = 4 q + p: pair p of unit q of
+// the workgroup's sequence); the compute waves take the jobs round-robin, so a unit's four jobs
+// run on four waves at once and every wave keeps busy to the end of a stage. A job leaves its
+// pair partial in its slot, over the first bytes of the record it has read; the last of the
+// unit's four jobs sums the pair partials in pair order, publishes the unit partial and frees
+// the slot for the loader.
+INL void compute_wave(PP P, EngLds& L, int w, int cw, int lane, uint32_t epoch, uint32_t* error) {
   uint32_t gen = 0;
   unsigned seq = 0;   // sequence number of the stage's first unit in this workgroup
   const int nstages = P->nstages;
@@ -677,14 +828,17 @@ INL void compute_wave(PP P, EngLds& L, int w, int lane, uint32_t epoch, uint32_t
     SP S = &P->st[s];
     const int n = share_units(stage_share(S, w, P->nstream));
     if (n == 0) continue;
-    stage_inputs(P, L, s, w, CW * 64 + lane, false, epoch, error, gen);
-    const unsigned end = seq + (unsigned)n;
-    int lut_b = -1;   // block the tables currently hold
-    for (unsigned q = seq + (kPhase + kEngPhases - seq % kEngPhases) % kEngPhases; q < end;
-         q += kEngPhases) {
+    stage_inputs(P, L, s, w, cw, lane, epoch, error, gen);
+    const uint32_t tag = eng_tag(epoch, s);
+    tagged_t* part = rfl(S->part);
+    const unsigned j0 = 4 * seq, j1 = 4 * (seq + (unsigned)n);
+    for (unsigned j = j0 + (cw + kEngCompute - j0 % kEngCompute) % kEngCompute; j < j1;
+         j += kEngCompute) {
       if (lds_poll_i(&L.abort_flag)) break;
+      const unsigned q = j >> 2;
+      const int p = (int)(j & 3);
       const int slot = (int)(q % kEngRingSlots);
-      if (lds_poll(&L.ready) <= q) {   // the loader normally runs far ahead
+      if (lds_poll(&L.ready) <= q) {   // the loader normally runs ahead
         for (int it = 0; lds_poll(&L.ready) <= q; ++it) {
           if (poll_expired(it, error, &L.abort_flag)) break;
           __builtin_amdgcn_s_sleep(1);
@@ -692,40 +846,33 @@ INL void compute_wave(PP P, EngLds& L, int w, int lane, uint32_t epoch, uint32_t
       }
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       const int blk = rfl(L.meta[slot].blk), ng = rfl(L.meta[slot].ng);
-      if (blk != lut_b) {   // at most kEngMaxBlocks times per stage
-        build_lut<CW>(L, blk, lane);
-        lut_b = blk;
-      }
-      const uint8_t* base = &L.ring[slot][0];
-      const uint4 ra = *(const uint4*)(base + kBlock * (1 + 2 * kPair) + lane * 16);
-      const uint4 rb = *(const uint4*)(base + kBlock * (2 + 2 * kPair) + lane * 16);
-      const uint32_t sw = *(const uint32_t*)(base + lane * 16 + 4 * kPair);
+      uint8_t* base = &L.ring[slot][0];
+      const uint32_t sw = *(const uint32_t*)(base + lane * 16 + 4 * p);
       float ga, gb;
-      lookup_pair<CW>(L, ra, rb, ga, gb);
-      // the slot's bytes were consumed before the lookups could start: count the read for the
-      // loader (only now, so that no wait stands between the record reads and the lookups)
+      pair_sums(L, blk, p, base + lane * 16, ga, gb);
+      // groups missing at a ragged end of K contribute nothing (their table inputs are zero;
+      // the select also keeps their scale bits out)
+      const float sa = 2 * p < ng ? e_f16(sw & 0xFFFFu) : 0.f;
+      const float sb = 2 * p + 1 < ng ? e_f16(sw >> 16) : 0.f;
+      float* pp = (float*)(base + kBlock * (1 + 2 * p)) + lane;
+      *pp = sa * ga + sb * gb;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      uint32_t old = 0;
+      if (lane == 0)
+        old = __hip_atomic_fetch_add(&L.jobs_done[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      old = __builtin_amdgcn_readfirstlane(old);
+      if ((old & 3u) != 3u) continue;
+      // the unit's last job: sum its pair partials, publish, free the slot
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      const float* pb = (const float*)(base + kBlock) + lane;
+      const float pv = ((pb[0] + pb[2 * kBlock / 4]) + pb[4 * kBlock / 4]) + pb[6 * kBlock / 4];
+      const int u = rfl(L.meta[slot].u);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       if (lane == 0)
         __hip_atomic_fetch_add(&L.consumed[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      // groups missing at a ragged end of K contribute nothing (their table inputs are zero;
-      // the select also keeps their scale bits out)
-      const float sa = 2 * kPair < ng ? e_f16(sw & 0xFFFFu) : 0.f;
-      const float sb = 2 * kPair + 1 < ng ? e_f16(sw >> 16) : 0.f;
-      const float part = sa * ga + sb * gb;
-      // hand the partial to the communication wave (the slot's last round must be consumed)
-      const unsigned hs = q % kEngHandSlots, round = q / kEngHandSlots;
-      if (lds_poll(&L.hfree[hs]) < round) {
-        for (int it = 0; lds_poll(&L.hfree[hs]) < round; ++it) {
-          if (poll_expired(it, error, &L.abort_flag)) break;
-          __builtin_amdgcn_s_sleep(1);
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      __hip_atomic_store(&L.hand[hs][kPair][lane],
-                         ((unsigned long long)(round + 1) << 32) | __float_as_uint(part),
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      st_tag(part + (size_t)u * 64 + lane, __float_as_uint(pv), tag);
     }
-    seq = end;
+    seq += (unsigned)n;
   }
 }
 
@@ -760,8 +907,8 @@ INL void loader_wave(PP P, EngLds& L, int w, int lane, uint32_t* error) {
         const uint8_t* src = M->w + (size_t)pos.tile * step + (size_t)pos.sg * kUnitBytes;
         for (int i = 0; i < len; ++i, ++q, src += step) {
           const unsigned slot = q % kEngRingSlots;
-          // the slot's previous unit must have been read by its four compute waves
-          const uint32_t need = (q / kEngRingSlots) * kEngPairs;
+          // the slot's previous unit must have been read (by one compute wave)
+          const uint32_t need = q / kEngRingSlots;
           if (lds_poll(&L.consumed[slot]) < need) {
             // ring full: announce everything issued so far, then wait for the slot
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -778,6 +925,7 @@ INL void loader_wave(PP P, EngLds& L, int w, int lane, uint32_t* error) {
           if (lane == 0) {
             L.meta[slot].blk = blk;
             L.meta[slot].ng = ng;
+            L.meta[slot].u = u + i;
           }
           const uint32_t dst = ring0 + slot * (uint32_t)kUnitBytes;
           // always nine copies, so the in-flight accounting below is static: a group missing at
@@ -800,150 +948,31 @@ INL void loader_wave(PP P, EngLds& L, int w, int lane, uint32_t* error) {
 }
 
 // ------------------------------------------------------------------------------------------
-// communication wave of a streaming workgroup
+// communication wave of a workgroup: its round-robin share of every stage's output tiles
+// (items w, w + nstream, ...), finalised as soon as their partials are in, stage after stage,
+// and the slices of matrix-free stages. No other wave ever waits for it.
 // ------------------------------------------------------------------------------------------
 INL void comm_wave(PP P, EngLds& L, int w, int lane, uint32_t epoch, uint32_t* error) {
-  uint32_t gen = 0;
-  unsigned seq = 0;
-  const int nstages = P->nstages;
+  const int nstages = P->nstages, nstream = P->nstream;
   for (int s = 0; s < nstages; ++s) {
     SP S = &P->st[s];
     if (S->nmat == 0) {
       if (!lds_poll_i(&L.abort_flag)) slice_stage(P, L, s, w, lane, epoch, error);
       continue;
     }
-    const Share r = stage_share(S, w, P->nstream);
-    const int n = share_units(r);
-    if (n == 0) continue;
-    stage_inputs(P, L, s, w, kEngCompute * 64 + lane, true, epoch, error, gen);
-    const uint32_t tag = eng_tag(epoch, s);
-    tagged_t* part = rfl(S->part);
-    if (s + 1 < nstages) warm_stage(&P->st[s + 1]);
-    const int n0 = r.b0 - r.a0;
-    // publish this workgroup's unit partials as they complete (never waits on global memory)
-    for (int k = 0; k < n; ++k, ++seq) {
-      if (lds_poll_i(&L.abort_flag)) continue;
-      const int u = k < n0 ? r.a0 + k : r.a1 + (k - n0);
-      const unsigned hs = seq % kEngHandSlots;
-      const uint32_t want = seq / kEngHandSlots + 1;
-      uint32_t hv[kEngPairs];
-      bool live = true;
-      for (int it = 0;; ++it) {
-        bool all = true;
-#pragma unroll
-        for (int p = 0; p < kEngPairs; ++p) {
-          const unsigned long long t = __hip_atomic_load(&L.hand[hs][p][lane], __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_WORKGROUP);
-          hv[p] = (uint32_t)t;
-          all = all && (uint32_t)(t >> 32) == want;
-        }
-        if (__builtin_amdgcn_ballot_w64(!all) == 0) break;
-        if (poll_expired(it, error, &L.abort_flag)) {
-          live = false;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-      if (!live) continue;
-      const float pv = ((__uint_as_float(hv[0]) + __uint_as_float(hv[1])) + __uint_as_float(hv[2])) +
-                       __uint_as_float(hv[3]);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      if (lane == 0) __hip_atomic_store(&L.hfree[hs], want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      st_tag(part + (size_t)u * 64 + lane, __float_as_uint(pv), tag);
-    }
-  }
-}
-
-// ------------------------------------------------------------------------------------------
-// finalising workgroups
-// ------------------------------------------------------------------------------------------
-
-// Finalises item `item` of stage S (number s): one output tile of a matrix, or the same tile of
-// a matrix and its pair partner (gate and up), from the published block partials, polled in
-// one sweep: bf16 outputs (tagged copy for consumers, plain copy for the caller) and the tile
-// statistic (sum of squares of the outputs, or the pair's sum of (own * partner)^2).
-INL void finalize_item(SP S, EngLds& L, int s, int item, int wave, int lane, uint32_t epoch,
-                       uint32_t* error) {
-  int m = 0;
-  for (; m < S->nmat; ++m) {
-    const int b = S->mat[m].item_base;
-    if (b >= 0 && item >= b && item < b + S->mat[m].tiles) break;
-  }
-  if (m == S->nmat) return;   // not produced by the host
-  MP M = &S->mat[m];
-  const int tile = item - M->item_base;
-  const int m2 = M->pair;
-  MP M2 = &S->mat[m2 < 0 ? m : m2];
-  // the block partials of this item: n of them, the first s1 from M; loaded once, kept scalar
-  const int s1 = rfl(M->supers), n = s1 + (m2 < 0 ? 0 : rfl(M2->supers));
-  const int ub1 = rfl(M->unit_base) + tile, t1 = rfl(M->tiles);
-  const int ub2 = rfl(M2->unit_base) + tile - s1 * rfl(M2->tiles), t2 = rfl(M2->tiles);
-  const tagged_t* part = rfl(S->part);
-  const uint32_t tag = eng_tag(epoch, s);
-  // Poll with sweeps that load only the words still missing (this lane's word of each block
-  // partial not yet seen with its tag), so that the sweep after the last arrival completes the
-  // item. The words seen go to this wave's LDS scratch (a finalising workgroup has no ring);
-  // the sums are then formed in partial order.
-  float* seen = (float*)&L.lut[0][0][0] + (size_t)wave * (kEngMaxFinal * 64) + lane;
-  uint32_t pend = n >= 32 ? ~0u : ((1u << n) - 1u);
-  for (int it = 0;; ++it) {
-    tagged_t t[kEngMaxFinal];
-#pragma unroll
-    for (int i = 0; i < kEngMaxFinal; ++i)
-      t[i] = ((pend >> i) & 1u)
-                 ? ld_tag_at(part, (uint32_t)((i < s1 ? ub1 + i * t1 : ub2 + i * t2) * 64 + lane))
-                 : 0;
-#pragma unroll
-    for (int i = 0; i < kEngMaxFinal; ++i) {
-      if (((pend >> i) & 1u) && tag_of(t[i]) == tag) {
-        pend &= ~(1u << i);
-        seen[i * 64] = __uint_as_float((uint32_t)t[i]);
-      }
-    }
-    if (__builtin_amdgcn_ballot_w64(pend != 0) == 0) break;
-    if (poll_expired(it, error, &L.abort_flag)) return;
-    __builtin_amdgcn_s_sleep(8);
-  }
-  float y1 = 0.f, y2 = 0.f;
-  for (int i = 0; i < n; ++i) {
-    if (i < s1) y1 += seen[i * 64];
-    else y2 += seen[i * 64];
-  }
-  // outputs: tagged copies and statistics first (consumers wait on them), plain copies last.
-  // A pair's tile goes out as one word per row holding both bf16 outputs (low: this matrix,
-  // high: the partner), so that a consumer of their product reads one word per position.
-  const int row = tile * kTileRows + lane;
-  const uint32_t b1 = e_to_bf16(y1);
-  const uint32_t b2 = m2 >= 0 ? e_to_bf16(y2) : 0u;
-  st_tag(rfl(M->yt) + row, b1 | (b2 << 16), tag);
-  const int n1 = rfl(M->n);
-  if (rfl(M->kind) == kMatSumSq) {
-    const float yv = row < n1 ? e_bf16(b1) : 0.f;
-    const float ss = wave_sum(yv * yv);
-    if (lane == 0) st_tag(rfl(M->stat) + tile, __float_as_uint(ss), tag);
-  }
-  const int n2 = rfl(M2->n);
-  if (m2 >= 0 && rfl(M2->kind) == kMatPair) {
-    const float h = row < n2 ? e_bf16(b1) * e_bf16(b2) : 0.f;
-    const float ss = wave_sum(h * h);
-    if (lane == 0) st_tag(rfl(M2->stat) + tile, __float_as_uint(ss), tag);
-  }
-  uint16_t* y1p = rfl(M->y);
-  uint16_t* y2p = rfl(M2->y);
-  if (y1p && row < n1) g_st16(y1p + row, b1);
-  if (m2 >= 0 && y2p && row < n2) g_st16(y2p + row, b2);
-}
-
-// Finalising wave c of nc (wave `wave` of its workgroup): items c, c + nc, ... of every stage,
-// in program order.
-INL void final_wave(PP P, EngLds& L, int c, int nc, int wave, int lane, uint32_t epoch,
-                    uint32_t* error) {
-  for (int s = 0; s < P->nstages; ++s) {
-    SP S = &P->st[s];
     warm_stage(S);
-    for (int item = c; item < S->nitems; item += nc) {
+    for (int item = w; item < S->nitems;) {
       if (lds_poll_i(&L.abort_flag)) return;
-      finalize_item(S, L, s, item, wave, lane, epoch, error);
+      // this workgroup's next two tiles of the stage go together when their partials fit
+      const Item a = item_of(S, item);
+      Item b = a;
+      bool two = false;
+      if (item + nstream < S->nitems) {
+        b = item_of(S, item + nstream);
+        two = a.m < S->nmat && b.m < S->nmat && a.n + b.n <= kEngMaxFinal;
+      }
+      if (a.m < S->nmat) finalize_items(S, L, s, a, b, two, lane, epoch, error);
+      item += two ? 2 * nstream : nstream;
     }
   }
 }
@@ -955,44 +984,22 @@ __global__ __launch_bounds__(kEngThreads) void q1_engine_kernel(EngArgs A) {
   const int lane = threadIdx.x & 63;
   const int wg = blockIdx.x;
   PP P = (PP)A.prog;
-  // LDS holds whatever the previous kernel left: clear the hand-off tags (rounds start at 1)
-  // and the control words
-  for (int i = threadIdx.x; i < kEngHandSlots * kEngPairs * 64; i += kEngThreads)
-    (&L.hand[0][0][0])[i] = 0;
-  if (threadIdx.x < kEngRingSlots) L.consumed[threadIdx.x] = 0;
-  if (threadIdx.x < kEngHandSlots) L.hfree[threadIdx.x] = 0;
+  // LDS holds whatever the previous kernel left: clear the control words
+  if (threadIdx.x < kEngRingSlots) {
+    L.consumed[threadIdx.x] = 0;
+    L.jobs_done[threadIdx.x] = 0;
+  }
   if (threadIdx.x == 0) {
     L.ready = 0;
     L.bar_count = 0;
     L.bar_gen = 0;
-    L.need_poll = 0;
     L.abort_flag = 0;
   }
   if (wave == 0) warm_stage(&P->st[0]);
   __syncthreads();
-  const int nst = P->nstream;
-  if (wg >= nst) {   // finalising workgroup: all its waves finalise
-    const int nc = (P->nwg - nst) * kEngWaves;
-    final_wave(P, L, (wg - nst) * kEngWaves + wave, nc, wave, lane, A.epoch, A.error);
-    return;
-  }
-  static_assert(kEngCompute == 12, "one case per compute wave");
-  switch (wave) {
-    case 0: compute_wave<0>(P, L, wg, lane, A.epoch, A.error); break;
-    case 1: compute_wave<1>(P, L, wg, lane, A.epoch, A.error); break;
-    case 2: compute_wave<2>(P, L, wg, lane, A.epoch, A.error); break;
-    case 3: compute_wave<3>(P, L, wg, lane, A.epoch, A.error); break;
-    case 4: compute_wave<4>(P, L, wg, lane, A.epoch, A.error); break;
-    case 5: compute_wave<5>(P, L, wg, lane, A.epoch, A.error); break;
-    case 6: compute_wave<6>(P, L, wg, lane, A.epoch, A.error); break;
-    case 7: compute_wave<7>(P, L, wg, lane, A.epoch, A.error); break;
-    case 8: compute_wave<8>(P, L, wg, lane, A.epoch, A.error); break;
-    case 9: compute_wave<9>(P, L, wg, lane, A.epoch, A.error); break;
-    case 10: compute_wave<10>(P, L, wg, lane, A.epoch, A.error); break;
-    case 11: compute_wave<11>(P, L, wg, lane, A.epoch, A.error); break;
-    case kLoaderWave: loader_wave(P, L, wg, lane, A.error); break;
-    default: comm_wave(P, L, wg, lane, A.epoch, A.error); break;
-  }
+  if (wave < kEngCompute) compute_wave(P, L, wg, wave, lane, A.epoch, A.error);
+  else if (wave == kLoaderWave) loader_wave(P, L, wg, lane, A.error);
+  else comm_wave(P, L, wg, lane, A.epoch, A.error);
 }
 
 }  // namespace
@@ -1006,7 +1013,6 @@ constexpr int kProgSlots = 16;
 
 struct EngDevice {
   int nwg = 0;
-  int nfinal = 0;   // finalising workgroups
   bool cooperative = false;
   uint32_t epoch = 0;
   void* ws = nullptr;   // [error word | program slots | per-stage partials, tagged outputs, stats]
@@ -1034,12 +1040,6 @@ static lbq_status eng_device(int* dev_out, EngDevice** out) {
         per_cu < 1)
       return LBQ_E_DEVICE;
     E.nwg = prop.multiProcessorCount;
-    // a eighth of the workgroups finalise (a multiple of the eight XCDs keeps them spread out)
-    int nf = E.nwg / 8;
-    if (const char* env = getenv("LBQ_ENGINE_FINALIZERS")) nf = atoi(env);
-    if (nf < 1) nf = 1;
-    if (nf > E.nwg - 1) nf = E.nwg - 1;
-    E.nfinal = nf;
     const char* coop = getenv("LBQ_ENGINE_COOPERATIVE");
     E.cooperative = coop != nullptr && atoi(coop) != 0;
   }
@@ -1130,7 +1130,8 @@ static bool eng_mat(EngStage& S, int idx, const void* w, int n, int k, uint16_t*
   M.tile_bytes = g.tile_bytes;
   M.src = src;
   M.kind = kind;
-  M.unit_base = S.units;
+  if (idx > 0 && M.supers != S.mat[0].supers) return false;   // a stage's matrices share K
+  M.tile_base = S.row_tiles;
   M.units = M.tiles * M.supers;
   M.item_base = S.nitems;
   M.pair = -1;
@@ -1140,7 +1141,8 @@ static bool eng_mat(EngStage& S, int idx, const void* w, int n, int k, uint16_t*
     M.stat = *cursor;
     *cursor += g.tiles;
   }
-  S.units += M.units;
+  S.row_tiles += M.tiles;
+  S.units = S.row_tiles * M.supers;
   S.nitems += M.tiles;
   S.nmat = idx + 1;
   return true;
@@ -1169,10 +1171,10 @@ static int host_blocks(const EngStage& S, int w, int n) {
   const int rb[2] = {(int)((long long)p0 * (w + 1) / n), p0 + (int)((long long)p1 * (w + 1) / n)};
   for (int r = 0; r < 2; ++r) {
     for (int u = ra[r]; u < rb[r];) {
+      const int sg = u / S.row_tiles, t = u - sg * S.row_tiles;
       int m = 0;
-      while (u >= S.mat[m].unit_base + S.mat[m].units) ++m;
+      while (t >= S.mat[m].tile_base + S.mat[m].tiles) ++m;
       const EngMat& M = S.mat[m];
-      const int k = u - M.unit_base, sg = k / M.tiles, tile = k - sg * M.tiles;
       const int key = (M.src << 16) | sg;
       bool seen = false;
       for (int i = 0; i < nk; ++i) seen = seen || keys[i] == key;
@@ -1180,14 +1182,14 @@ static int host_blocks(const EngStage& S, int w, int n) {
         if (nk == 16) return 17;
         keys[nk++] = key;
       }
-      u += M.tiles - tile;
+      u += M.tiles - (t - M.tile_base);
     }
   }
   return nk;
 }
 
 static bool eng_fits(const EngProgram* P) {
-  if (P->nstream < 1 || P->nstream >= P->nwg) return false;
+  if (P->nstream < 1 || P->nstream > P->nwg) return false;
   for (int s = 0; s < P->nstages; ++s) {
     const EngStage& S = P->st[s];
     // one source vector per stage, read by every matrix of the stage
@@ -1234,7 +1236,7 @@ lbq_status lbq_engine_gemv_q1(const void* d_w, int32_t n, int32_t k, const uint1
   EngProgram* P = (EngProgram*)prog.data();
   P->nstages = 1;
   P->nwg = E->nwg;
-  P->nstream = E->nwg - E->nfinal;
+  P->nstream = E->nwg;
   EngStage& S = P->st[0];
   tagged_t* cursor = (tagged_t*)((char*)E->ws + kHeadBytes);
   if (!eng_mat(S, 0, d_w, n, k, d_y, 0, kMatPlain, &cursor)) return LBQ_E_SHAPE;
@@ -1250,9 +1252,8 @@ lbq_status lbq_engine_gemv_q1(const void* d_w, int32_t n, int32_t k, const uint1
 }
 
 // Whole decode step (batch 1) through the engine. Per layer three stages:
-//  A  : q, k, v (part 0) then gate, up (part 1), input x = rescale of the previous down output
-//       (the caller's x0 for layer 0); q comes first in every workgroup's share so its tiles
-//       are finalised while gate and up still stream;
+//  A  : q, k, v, gate, up, input x = rescale of the previous down output (the caller's x0 for
+//       layer 0); gate and up are finalised together (their product feeds down);
 //  B2 : down, input rescale(gate * up);
 //  B1 : o, input rescale(q). Nothing reads o, so it runs last: its units fill the wait for the
 //       next layer's input instead of delaying down;
@@ -1283,7 +1284,7 @@ lbq_status lbq_engine_decode_q1(const lbq_q1_layer* layers, int32_t L, int32_t h
   EngProgram* P = (EngProgram*)prog.data();
   P->nstages = nst;
   P->nwg = E->nwg;
-  P->nstream = E->nwg - E->nfinal;
+  P->nstream = E->nwg;
   tagged_t* cursor = (tagged_t*)((char*)E->ws + kHeadBytes);
   auto at = [&](int layer, int slot) {
     return d_act + lbq_decode_act_offset(layer, slot, L, hidden, kv, ffn, 1);
@@ -1310,12 +1311,12 @@ lbq_status lbq_engine_decode_q1(const lbq_q1_layer* layers, int32_t L, int32_t h
     bool ok = eng_mat(A, 0, layers[l].q, hidden, hidden, at(l, LBQ_ACT_Q), 0, kMatSumSq, &cursor);
     ok = ok && eng_mat(A, 1, layers[l].k, kv, hidden, at(l, LBQ_ACT_K), 0, kMatPlain, &cursor);
     ok = ok && eng_mat(A, 2, layers[l].v, kv, hidden, at(l, LBQ_ACT_V), 0, kMatPlain, &cursor);
-    A.part0 = A.units;
     ok = ok && eng_mat(A, 3, layers[l].gate, ffn, hidden, at(l, LBQ_ACT_GATE), 0, kMatPlain, &cursor);
     ok = ok && eng_mat(A, 4, layers[l].up, ffn, hidden, at(l, LBQ_ACT_UP), 0, kMatPair, &cursor);
     if (!ok) return LBQ_E_SHAPE;
     eng_pair(A, 3, 4);
     eng_part(A, &cursor);
+    A.part0 = A.units;
     A.nsrc = 1;
     if (l == 0) {
       A.src[0].kind = kSrcDirect;
