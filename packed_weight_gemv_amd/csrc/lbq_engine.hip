@@ -175,7 +175,7 @@ struct SlotMeta {
 // The lookup tables come first: every table entry's LDS address then fits the 16-bit
 // immediate offset of ds_read, so a lookup's address is the extracted field alone.
 struct __attribute__((aligned(16))) EngLds {
-  float lut[kEngMaxBlocks][kSuper][32 * 16];    // [input block][group][chunk*16 + entry]
+  int lut[kEngMaxBlocks][kSuper][32 * 16];      // [input block][group][chunk*16 + entry]
   uint8_t ring[kEngRingSlots][kUnitBytes];      // units copied by the loader
   float fin[kEngMaxFinal][64];                  // the communication wave's finalisation scratch
   SlotMeta meta[kEngRingSlots];
@@ -183,6 +183,7 @@ struct __attribute__((aligned(16))) EngLds {
   uint32_t jobs_done[kEngRingSlots];            // pair jobs of each slot done so far (4 per unit)
   uint32_t ready;                               // units [0, ready) of the sequence have landed
   uint32_t bar_count, bar_gen;                  // barrier of the gathering waves
+  float gscale[kEngMaxBlocks][kSuper];          // 2^(e - kFixBits) of each group's fixed-point form
   float denom;                                  // RMS denominator of the stage's source
   int32_t abort_flag;
 };
@@ -431,18 +432,28 @@ INL float stats_denominator(const uint32_t (&sv)[8], int n, int k, float eps, in
   return sqrtf(wave_sum(part) / (float)k + eps);
 }
 
-// Entries of one table of 16 signed sums of four inputs x0..x3, written to dst[0..15]: entry
-// e = m + 4 j is pair term m of (x0, x1) plus pair term j of (x2, x3), where pair term 0 = -a-b,
-// 1 = a-b, 2 = b-a, 3 = a+b (bit i of e set: input i enters with +).
-INL void write_table(float* dst, float x0, float x1, float x2, float x3) {
-  const float p0 = -x0 - x1, p1 = x0 - x1, p2 = x1 - x0, p3 = x0 + x1;
-  const float q0 = -x2 - x3, q1 = x2 - x3, q2 = x3 - x2, q3 = x2 + x3;
-  float4* d = (float4*)dst;
-  d[0] = make_float4(p0 + q0, p1 + q0, p2 + q0, p3 + q0);
-  d[1] = make_float4(p0 + q1, p1 + q1, p2 + q1, p3 + q1);
-  d[2] = make_float4(p0 + q2, p1 + q2, p2 + q2, p3 + q2);
-  d[3] = make_float4(p0 + q3, p1 + q3, p2 + q3, p3 + q3);
+// Entries of one table of 16 signed sums of four integer inputs q0..q3, written to dst[0..15]:
+// entry e = m + 4 j is pair term m of (q0, q1) plus pair term j of (q2, q3), where pair term
+// 0 = -a-b, 1 = a-b, 2 = b-a, 3 = a+b (bit i of e set: input i enters with +).
+INL void write_table(int* dst, int q0, int q1, int q2, int q3) {
+  const int p0 = -q0 - q1, p1 = q0 - q1, p2 = q1 - q0, p3 = q0 + q1;
+  const int r0 = -q2 - q3, r1 = q2 - q3, r2 = q3 - q2, r3 = q2 + q3;
+  int4* d = (int4*)dst;
+  d[0] = make_int4(p0 + r0, p1 + r0, p2 + r0, p3 + r0);
+  d[1] = make_int4(p0 + r1, p1 + r1, p2 + r1, p3 + r1);
+  d[2] = make_int4(p0 + r2, p1 + r2, p2 + r2, p3 + r2);
+  d[3] = make_int4(p0 + r3, p1 + r3, p2 + r3, p3 + r3);
 }
+
+// Fixed-point form of a group's inputs: x = q * 2^(e - kFixBits) with integer q, where 2^e
+// bounds the group's largest magnitude. A table entry (four inputs) and a row's sum over the
+// group's 32 entries (128 inputs) then stay below 2^(kFixBits + 7) < 2^31, and the sum is exact.
+// A bf16 input is represented exactly unless it is below 2^(e - 15); smaller ones are rounded
+// to the nearest multiple of 2^(e - kFixBits).
+// The exponent e is kept at or above kMinExp so that the scale 2^(e - kFixBits) stays a normal
+// float: a group whose inputs all lie below 2^kMinExp in magnitude keeps fewer bits.
+constexpr int kFixBits = 22;
+constexpr int kMinExp = -100;
 
 // The input positions come in chunks of four (one table each): chunk ch of the staged blocks is
 // block ch >> 8, positions 4 (ch & 255) .. +3 of that block, i.e. table ch & 31 of group
@@ -565,31 +576,46 @@ INL void stage_inputs(PP P, EngLds& L, int s, int w, int cw, int lane, uint32_t 
     for (int b = 0; b < nb; ++b)
       if (share_has(r, (blk_get(B, b) & 0xFFFF) * rfl(S->row_tiles) + R->tile_base)) own |= 1u << b;
   }
-  // rescale, record and tabulate (the denominator was written before a barrier above)
+  // rescale, record and tabulate (the denominator was written before a barrier above). A
+  // group's 32 chunks sit in 32 consecutive lanes of one wave (lanes 0-31 or 32-63), which find
+  // the group's largest magnitude together and tabulate its fixed-point form.
+  static_assert(kChunksPerThread == 1, "one chunk per thread: a group's chunks share half a wave");
   const float dn = direct ? 1.f : L.denom;
+  const int ch = tid;
+  float x[4];
 #pragma unroll
-  for (int j = 0; j < kChunksPerThread; ++j) {
-    if (!((cmask >> j) & 1u)) continue;
-    const int ch = tid + kChunkThreads * j;
-    float x[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int pi = 4 * j + i;
-      uint32_t xb = 0;
-      if ((vmask >> pi) & 1u) {
-        if (direct) {
-          xb = v[pi];
-        } else if (prod) {
-          xb = e_to_bf16(e_bf16(v[pi] & 0xFFFFu) * e_bf16(v[pi] >> 16) / dn);
-        } else {
-          const uint32_t wd = v[4 * j + (i >> 1)];
-          xb = e_to_bf16(e_bf16((i & 1) ? (wd >> 16) : (wd & 0xFFFFu)) / dn);
-        }
-        if ((own >> (ch >> 8)) & 1u) g_st16(rec + k0[j] + i, xb);
+  for (int i = 0; i < 4; ++i) {
+    uint32_t xb = 0;
+    if ((vmask >> i) & 1u) {
+      if (direct) {
+        xb = v[i];
+      } else if (prod) {
+        xb = e_to_bf16(e_bf16(v[i] & 0xFFFFu) * e_bf16(v[i] >> 16) / dn);
+      } else {
+        const uint32_t wd = v[i >> 1];
+        xb = e_to_bf16(e_bf16((i & 1) ? (wd >> 16) : (wd & 0xFFFFu)) / dn);
       }
-      x[i] = e_bf16(xb);
+      if ((own >> (ch >> 8)) & 1u) g_st16(rec + k0[0] + i, xb);
     }
-    write_table(&L.lut[ch >> 8][0][0] + (ch & 255) * 16, x[0], x[1], x[2], x[3]);
+    x[i] = e_bf16(xb);
+  }
+  // largest magnitude over the half wave (bit patterns of non-negative floats order as integers)
+  uint32_t mx = max(max(__float_as_uint(fabsf(x[0])), __float_as_uint(fabsf(x[1]))),
+                    max(__float_as_uint(fabsf(x[2])), __float_as_uint(fabsf(x[3]))));
+  mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+  mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+  mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x141, 0xF, 0xF, false));  // row half mirror
+  mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x140, 0xF, 0xF, false));  // row mirror
+  mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
+  // e with 2^e > largest magnitude: one above the largest's binary exponent, at least kMinExp
+  const int e = max((int)((mx >> 23) & 0xFFu) - 126, kMinExp);
+  if ((cmask & 1u) != 0) {
+    write_table(&L.lut[ch >> 8][0][0] + (ch & 255) * 16,
+                __float2int_rn(__builtin_ldexpf(x[0], kFixBits - e)),
+                __float2int_rn(__builtin_ldexpf(x[1], kFixBits - e)),
+                __float2int_rn(__builtin_ldexpf(x[2], kFixBits - e)),
+                __float2int_rn(__builtin_ldexpf(x[3], kFixBits - e)));
+    if ((lane & 31) == 0) L.gscale[ch >> 8][(ch >> 5) & 7] = __builtin_ldexpf(1.f, e - kFixBits);
   }
   gather_barrier(L, lane, gen, error);
 }
@@ -769,17 +795,18 @@ INL void finalize_items(SP S, EngLds& L, int s, const Item& a, const Item& b, bo
 // compute waves
 // ------------------------------------------------------------------------------------------
 
-// Sums over groups G and G+1 of a row (input block B): 2 x 32 table lookups in four
-// independent chains, so that the lookups of both groups overlap. The records are read here.
+// Sums over groups G and G+1 of a row (input block B), in the groups' fixed-point units: 2 x 32
+// integer table lookups, two per three-input add, in two independent chains. The records are
+// read here.
 template <int B, int G>
-INL void lookup_two(const EngLds& L, const uint8_t* rec, float& ga, float& gb) {
+INL void lookup_two(const EngLds& L, const uint8_t* rec, int& ga, int& gb) {
   const uint4 sa = *(const uint4*)(rec + kBlock * (1 + G));
   const uint4 sb = *(const uint4*)(rec + kBlock * (2 + G));
   const char* la = (const char*)&L.lut[B][G][0];
   const char* lb = (const char*)&L.lut[B][G + 1][0];
   const uint32_t da[4] = {sa.x, sa.y, sa.z, sa.w};
   const uint32_t db[4] = {sb.x, sb.y, sb.z, sb.w};
-  float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+  int a = 0, b = 0;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const uint32_t s = da[d], t = db[d];
@@ -787,19 +814,19 @@ INL void lookup_two(const EngLds& L, const uint8_t* rec, float& ga, float& gb) {
     const uint32_t rt = __builtin_amdgcn_alignbit(t, t, 4);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      a0 += *(const float*)(la + (8 * d + 2 * q) * 64 + e_field(s, q));
-      a1 += *(const float*)(la + (8 * d + 2 * q + 1) * 64 + e_field(rs, q));
-      b0 += *(const float*)(lb + (8 * d + 2 * q) * 64 + e_field(t, q));
-      b1 += *(const float*)(lb + (8 * d + 2 * q + 1) * 64 + e_field(rt, q));
+      a = a + *(const int*)(la + (8 * d + 2 * q) * 64 + e_field(s, q)) +
+          *(const int*)(la + (8 * d + 2 * q + 1) * 64 + e_field(rs, q));
+      b = b + *(const int*)(lb + (8 * d + 2 * q) * 64 + e_field(t, q)) +
+          *(const int*)(lb + (8 * d + 2 * q + 1) * 64 + e_field(rt, q));
     }
   }
-  ga = a0 + a1;
-  gb = b0 + b1;
+  ga = a;
+  gb = b;
 }
 
 // Group pair p of a unit whose tables are input block blk: one code path per (block, pair), so
 // that every table offset is an immediate.
-INL void pair_sums(const EngLds& L, int blk, int p, const uint8_t* rec, float& ga, float& gb) {
+INL void pair_sums(const EngLds& L, int blk, int p, const uint8_t* rec, int& ga, int& gb) {
   switch (blk * 4 + p) {
     case 0: lookup_two<0, 0>(L, rec, ga, gb); break;
     case 1: lookup_two<0, 2>(L, rec, ga, gb); break;
@@ -848,10 +875,12 @@ INL void compute_wave(PP P, EngLds& L, int w, int cw, int lane, uint32_t epoch, 
       const int blk = rfl(L.meta[slot].blk), ng = rfl(L.meta[slot].ng);
       uint8_t* base = &L.ring[slot][0];
       const uint32_t sw = *(const uint32_t*)(base + lane * 16 + 4 * p);
-      float ga, gb;
-      pair_sums(L, blk, p, base + lane * 16, ga, gb);
-      // groups missing at a ragged end of K contribute nothing (their table inputs are zero;
-      // the select also keeps their scale bits out)
+      int ia, ib;
+      pair_sums(L, blk, p, base + lane * 16, ia, ib);
+      // group sums back from fixed point (exact below 2^24 in magnitude); groups missing at a
+      // ragged end of K contribute nothing (their table inputs are zero; the select also keeps
+      // their scale bits out)
+      const float ga = (float)ia * L.gscale[blk][2 * p], gb = (float)ib * L.gscale[blk][2 * p + 1];
       const float sa = 2 * p < ng ? e_f16(sw & 0xFFFFu) : 0.f;
       const float sb = 2 * p + 1 < ng ? e_f16(sw >> 16) : 0.f;
       float* pp = (float*)(base + kBlock * (1 + 2 * p)) + lane;
