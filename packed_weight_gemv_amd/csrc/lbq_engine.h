@@ -23,7 +23,7 @@ constexpr int kEngCompute = 14;                     // compute waves: one whole 
 constexpr int kEngWaves = kEngCompute + 2;          // + one loader wave + one communication wave
 constexpr int kEngThreads = kEngWaves * 64;
 constexpr int kEngRingSlots = 13;                   // units the LDS ring holds
-constexpr int kEngInFlight = 2;                     // units the loader keeps in flight
+constexpr int kEngInFlight = 1;                     // units the loader keeps in flight
 constexpr int kEngMaxStages = 255;
 constexpr int kEngMaxFinal = 24;                    // block partials summed by one finalisation
 constexpr int kEngMaxBlocks = 2;                    // input blocks one workgroup stages per stage

@@ -9,9 +9,9 @@
 //    matrix, tile, so a share reads at most two 1024-wide input blocks) and walks its shares in
 //    program order.
 //  * The loader wave copies units straight into an LDS ring with nontemporal global_load_lds,
-//    keeping only kEngInFlight units in flight. That is enough for the compute unit's share of
-//    HBM bandwidth, and it keeps the queue in front of the workgroup's other memory operations
-//    (input loads, partial stores) short. The ring itself is deeper (a stage's whole share,
+//    keeping only kEngInFlight units in flight. One unit per compute unit streams a few TB/s
+//    across the chip, more than the stage dependencies let the workgroups consume, and a deeper
+//    queue delays the workgroup's latency-critical loads (input and partial polls) behind it. The ring itself is deeper (a stage's whole share,
 //    typically), so the copies run ahead across stage boundaries while a stage waits for its
 //    inputs. Weights never depend on activations.
 //  * The compute waves take the jobs of a stage round-robin; a job is one pair of 128-weight
