@@ -42,6 +42,7 @@ extern "C" {
 
 #define LBQ_ABI_VERSION 1
 #define LBQ_MAX_BATCH 16
+#define LBQ_MAX_GEMM_ROWS 65536
 #define LBQ_MLP_MAX_LAYERS 8
 #define LBQ_MLP_MAX_DIM 1024
 
@@ -137,6 +138,19 @@ lbq_status lbq_unpack_q1g128(const void* src, int32_t n, int32_t k, uint8_t* sig
 lbq_status lbq_gemv_q1g128(const void* d_w, int32_t n, int32_t k, const uint16_t* d_x,
                            uint16_t* d_y, int32_t batch, void* stream);
 
+/* Q1_0_g128 GEMM for many activation rows (prefill / large batch), on the matrix cores: the
+ * same y[b][row] as lbq_gemv_q1g128 for b < m. The Acorn page's own GPU int4 kernel section lists
+ * a multi-row GEMM next to its GEMV for prompt prefill; this is that operation for the Q1 format
+ * of the Bonsai digest ("technical architecture highlights"). Within each 128-weight group the
+ * products are summed by the matrix cores in fp32 (exact products, their own summation order);
+ * groups are then weighted by their scales and accumulated in fp32 as in the GEMV.
+ *   d_w : device layout (lbq_pack_q1g128), 16-byte aligned
+ *   d_x : bf16 [m][k], 16-byte aligned     d_y : bf16 [m][n], 2-byte aligned
+ * Requires k % 128 == 0, 1 <= n, 0 <= m <= LBQ_MAX_GEMM_ROWS (0 = no-op). d_y must not overlap
+ * d_x or the weights. Same split-K workspace rules as lbq_gemv_q1g128. */
+lbq_status lbq_gemm_q1g128(const void* d_w, int32_t n, int32_t k, const uint16_t* d_x,
+                           uint16_t* d_y, int32_t m, void* stream);
+
 /* ------------------------------------------------------------------------------------------
  * INT4, group 128 along k (Acorn, "int4 quantization quality: group quantization (g=128)").
  *
@@ -158,6 +172,13 @@ lbq_status lbq_unpack_i4g128(const void* src, int32_t n, int32_t k, uint8_t* nib
  * accumulation. Same pointer, alignment, batch and workspace rules as lbq_gemv_q1g128. */
 lbq_status lbq_gemv_i4g128(const void* d_w, int32_t n, int32_t k, const uint16_t* d_x,
                            uint16_t* d_y, int32_t batch, void* stream);
+
+/* INT4 g128 GEMM for many activation rows (prefill / large batch), on the matrix cores: the
+ * same y[b][row] as lbq_gemv_i4g128 for b < m (the Acorn page's GPU int4 kernel section: online
+ * nibble unpacking feeding a multi-row GEMM for prefill). Pointer, alignment, shape, workspace
+ * and error rules as lbq_gemm_q1g128. */
+lbq_status lbq_gemm_i4g128(const void* d_w, int32_t n, int32_t k, const uint16_t* d_x,
+                           uint16_t* d_y, int32_t m, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * RMS rescale: the glue that carries bf16 activations from one GEMV to the next in a decode

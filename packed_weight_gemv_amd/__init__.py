@@ -60,6 +60,8 @@ def load():
         "lbq_pack_i4g128": ([P, P, i32, i32, P], i32),
         "lbq_unpack_i4g128": ([P, i32, i32, P, P], i32),
         "lbq_gemv_i4g128": ([P, i32, i32, P, P, i32, P], i32),
+        "lbq_gemm_q1g128": ([P, i32, i32, P, P, i32, P], i32),
+        "lbq_gemm_i4g128": ([P, i32, i32, P, P, i32, P], i32),
         "lbq_rms_rescale_bf16": ([P, P, P, i32, i32, ctypes.c_float, P], i32),
         "lbq_decode_act_elems": ([i32, i32, i32, i32, i32], sz),
         "lbq_decode_act_offset": ([i32, i32, i32, i32, i32, i32, i32], i64),
@@ -207,6 +209,20 @@ def lbq_gemv_q1g128(w, n: int, k: int, x, y, stream=None) -> None:
 def lbq_gemv_i4g128(w, n: int, k: int, x, y, stream=None) -> None:
     B = x.shape[0] if x.dim() == 2 else 1
     _check("lbq_gemv_i4g128", load().lbq_gemv_i4g128(_dptr(w), n, k, _dptr(x), _dptr(y), B,
+                                                     _stream(stream)))
+
+
+def lbq_gemm_q1g128(w, n: int, k: int, x, y, stream=None) -> None:
+    """Many-row product on the matrix cores. w: lbq_pack_q1g128 layout; x: bf16/int16 [m][k]
+    (16-byte aligned); y: [m][n]."""
+    m = x.shape[0] if x.dim() == 2 else 1
+    _check("lbq_gemm_q1g128", load().lbq_gemm_q1g128(_dptr(w), n, k, _dptr(x), _dptr(y), m,
+                                                     _stream(stream)))
+
+
+def lbq_gemm_i4g128(w, n: int, k: int, x, y, stream=None) -> None:
+    m = x.shape[0] if x.dim() == 2 else 1
+    _check("lbq_gemm_i4g128", load().lbq_gemm_i4g128(_dptr(w), n, k, _dptr(x), _dptr(y), m,
                                                      _stream(stream)))
 
 

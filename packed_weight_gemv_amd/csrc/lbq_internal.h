@@ -56,4 +56,12 @@ inline int64_t group_offset(const Geometry& g, int64_t t, int64_t gi) {
   return t * g.tile_bytes + j * g.super_bytes + kBlock + i * g.group_bytes;
 }
 
+// Split-K workspace of the per-call kernels, one per device, grown on demand and never freed:
+// kSplitCounterBytes of zero-initialised tile counters (every kernel leaves them at zero),
+// followed by at least partial_bytes of fp32 partials. Fails with LBQ_E_NOMEM when it has to
+// grow while `stream` is being captured.
+constexpr size_t kSplitCounterBytes = 1 << 20;
+lbq_status splitk_workspace(size_t partial_bytes, void* stream, unsigned** counters,
+                            float** partials);
+
 }  // namespace lbq

@@ -64,7 +64,7 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // ---------------------------------------------------------------------------------------------
 namespace {
 constexpr int kMaxDevices = 64;
-constexpr size_t kCounterBytes = 1 << 20;   // 256 Ki tile counters, self-resetting
+constexpr size_t kCounterBytes = kSplitCounterBytes;   // 256 Ki tile counters, self-resetting
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
@@ -102,6 +102,14 @@ lbq_status get_workspace(size_t partial_bytes, hipStream_t stream, unsigned** co
   return LBQ_OK;
 }
 
+}  // namespace
+
+lbq_status lbq::splitk_workspace(size_t partial_bytes, void* stream, unsigned** counters,
+                                 float** partials) {
+  return get_workspace(partial_bytes, (hipStream_t)stream, counters, partials);
+}
+
+namespace {
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
   return a0 < b0 + nb && b0 < a0 + na;
