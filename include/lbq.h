@@ -131,8 +131,10 @@ lbq_status lbq_unpack_q1g128(const void* src, int32_t n, int32_t k, uint8_t* sig
  *   d_w : device layout (lbq_pack_q1g128), 16-byte aligned
  *   d_x : bf16 [batch][k], 4-byte aligned     d_y : bf16 [batch][n], 4-byte aligned
  * Requires k % 128 == 0, 1 <= n, 0 <= batch <= LBQ_MAX_BATCH (0 = no-op). d_y must not
- * overlap d_x or the weights. Large-k calls may split the reduction over workgroups through a
- * library-owned device workspace (allocated once per device on first need, kept until the
+ * overlap d_x or the weights. With batch >= 2 and d_x 16-byte aligned the call is the
+ * matrix-core product lbq_gemm_q1g128 (same result rule; within each group the matrix cores sum
+ * the exact products in their own order). Large-k calls may split the reduction over
+ * workgroups through a library-owned device workspace (allocated once per device on first need, kept until the
  * process exits); calls that split share it, so concurrent split calls on one device must be
  * ordered on one stream. LBQ_E_NOMEM if it cannot be allocated (e.g. inside graph capture). */
 lbq_status lbq_gemv_q1g128(const void* d_w, int32_t n, int32_t k, const uint16_t* d_x,

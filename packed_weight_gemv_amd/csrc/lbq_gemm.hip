@@ -29,8 +29,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
-constexpr int kXStride = 272;   // bytes per activation row of the LDS tile: 256 + 16 keeps the
-                                // 32 rows one ds_read_b128 touches on distinct banks
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t v) { return __uint_as_float(v << 16); }
 
@@ -57,26 +55,30 @@ __device__ __forceinline__ bf16x8 i4_unpack(uint32_t d) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// Weights of one group for one lane and one 32-row block: Q1 8 bytes, INT4 2 x 16 bytes.
-template <int FMT>
-struct WRegs;
-template <>
-struct WRegs<0> {
-  u32x2 v;
-};
-template <>
-struct WRegs<1> {
-  u32x4 a, b;
-};
-
-template <int FMT>
-__device__ __forceinline__ void load_w(WRegs<FMT>& r, const uint8_t* rec) {
-  if constexpr (FMT == 0) {
-    r.v = __builtin_nontemporal_load((const u32x2*)rec);
-  } else {
-    r.a = __builtin_nontemporal_load((const u32x4*)rec);
-    r.b = __builtin_nontemporal_load((const u32x4*)(rec + kBlock));
-  }
+// LDS-direct copy of 16 bytes per lane: lane i's bytes at base + voff land at LDS address
+// lds + 16 i. Issued from asm so that the compiler does not guard later LDS accesses with
+// vector-memory waits: the pipeline below counts its copies and waits for them explicitly.
+template <bool NT>
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  if constexpr (NT)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %3 nt\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved) : "s"(lds), "v"(voff), "s"(base) : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved) : "s"(lds), "v"(voff), "s"(base) : "memory");
+}
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(T* p) {
+  return (uint32_t)(uintptr_t)p;
+}
+// Waits until at most n of this wave's vector memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // Output accumulation across the split-K slices of one output tile: every workgroup of the tile
@@ -95,68 +97,94 @@ __device__ __forceinline__ bool splitk_last(unsigned* counter, int splits) {
   return s_last != 0;
 }
 
-// FMT: 0 = Q1_0_g128, 1 = INT4 g128. WB: 32-row activation blocks per wave; WN: 32-row weight
-// blocks per wave. Workgroup tile: 32 WB activation rows x 128 WN weight rows.
-template <int FMT, int WB, int WN>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_kernel(
+// Tile and pipeline shape per format and activation block count.
+template <int FMT, int WB>
+struct Cfg {
+  static constexpr int kBM = 32 * WB;                          // activation rows per workgroup
+  static constexpr int kBN = 256;                              // weight rows: one 64-row tile per wave
+  static constexpr int kXBytes = kBM * 256;                    // one group of activations
+  static constexpr int kWBytes = (FMT == 0 ? 1 : 4) * kBlock * kWaves;   // one group of weights
+  static constexpr int kStageBytes = kXBytes + kWBytes;
+  static constexpr int kStages = FMT == 0 ? (WB == 1 ? 8 : 6) : (WB == 1 ? 5 : 4);
+  static constexpr int kXCopies = kBM * 16 / 256;             // copies per wave and stage
+  static constexpr int kWCopies = FMT == 0 ? 1 : 4;
+  static constexpr int kCopies = kXCopies + kWCopies + 1;     // + the scale copy
+  // stages that must have landed beyond the one computed: INT4 sums the next group's
+  // activations one iteration ahead
+  static constexpr int kAhead = FMT == 0 ? 0 : 1;
+  static constexpr int kWaitCopies = kCopies * (kStages - 2 - kAhead);
+};
+
+// FMT: 0 = Q1_0_g128, 1 = INT4 g128. WB: 32-row activation blocks per wave. Each wave owns one
+// 64-row weight tile (two 32-row MFMA column blocks), so a workgroup covers 256 weight rows.
+//
+// The groups of the workgroup's K slice stream through an LDS ring of kStages stages with
+// LDS-direct copies: a stage holds one group's activations (kBM rows of 256 bytes, the 16-byte
+// chunks of row r XOR-swizzled by r % 16 so that the 32 rows one operand read touches sit on
+// distinct banks), the group's sign or code records of the four tiles, and, when the group
+// starts a super-group, the tiles' scale blocks (a one-lane dummy copy otherwise, so that every
+// stage is the same number of copies and one vmcnt wait finds the oldest stage).
+template <int FMT, int WB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(
     const uint8_t* __restrict__ w, const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
     float* __restrict__ partial, unsigned* __restrict__ counters, int m, int n, int k, int np,
-    int groups, long long tile_bytes, long long super_bytes, int group_bytes, int gps,
+    int tiles, int groups, long long tile_bytes, long long super_bytes, int group_bytes, int gps,
     int splits) {
-  constexpr int BM = 32 * WB;
-  constexpr int BN = 32 * WN * kWaves;
-  constexpr int kChunks = BM * 16 / 256;   // 16-byte activation chunks per thread and group
-  __shared__ __attribute__((aligned(16))) uint8_t xs[2][BM][kXStride];
-  __shared__ float xsum[2][BM];   // INT4: per-row sums of the group's activations
+  using C = Cfg<FMT, WB>;
+  constexpr int S = C::kStages, WN = 2;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[S][C::kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sblk[2][kWaves][kBlock];   // scale blocks by super-group parity
+  __shared__ __attribute__((aligned(16))) uint8_t dummy[16];
+  __shared__ float xsum[S][C::kBM];   // INT4: per-row sums of a stage's activations
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
-  const int nb0 = blockIdx.x * BN, mb0 = blockIdx.y * BM, split = blockIdx.z;
-  const int g0 = split * gps, g1 = min(groups, g0 + gps);
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nb0 = blockIdx.x * C::kBN, mb0 = blockIdx.y * C::kBM, split = blockIdx.z;
+  const int g0 = split * gps, g1 = min(groups, g0 + gps), ng = g1 - g0;
+  // this wave's weight tile (tiles past the last read the last one; their rows are not stored)
+  const int wt = min((int)blockIdx.x * kWaves + wave, tiles - 1);
+  const uint8_t* tbase = w + (size_t)wt * tile_bytes;
 
-  // this lane's weight rows (one per 32-row block) and their record bases; rows past the padded
-  // count read row 0 and are never stored
-  const uint8_t* rowbase[WN];
-  int rown[WN];
+  auto issue = [&](int i) {
+    const int g = g0 + i;
+    uint8_t* xsl = &ring[i % S][0];
+    // activations: this wave's copy q covers rows r0..r0+3 (16 lanes per row); lanes of rows
+    // past m are switched off, except lane 0, so that the copy always issues
 #pragma unroll
-  for (int t = 0; t < WN; ++t) {
-    const int r = nb0 + (wave * WN + t) * 32 + l32;
-    rown[t] = r;
-    const int rr = r < np ? r : 0;
-    rowbase[t] = w + (size_t)(rr / kTileRows) * tile_bytes + (size_t)(rr % kTileRows) * 16;
-  }
-  auto group_rec = [&](int t, int g) {
-    return rowbase[t] + (size_t)(g / kSuper) * super_bytes + kBlock + (size_t)(g % kSuper) * group_bytes +
-           (FMT == 0 ? 8 * h : 2 * h * kBlock);
-  };
-
-  // activations of group g -> registers (zero past m), then LDS buffer b
-  u32x4 xr[kChunks];
-  auto load_x = [&](int g) {
-#pragma unroll
-    for (int q = 0; q < kChunks; ++q) {
-      const int c = tid + 256 * q, row = c >> 4, col = c & 15;
-      const int b = mb0 + row;
-      xr[q] = b < m ? *(const u32x4*)(x + (size_t)b * k + (size_t)g * kGroup + 8 * col)
-                    : u32x4{0u, 0u, 0u, 0u};
+    for (int q = 0; q < C::kXCopies; ++q) {
+      const int r0 = 4 * wave + 16 * q, row = r0 + (lane >> 4), pos = lane & 15;
+      const int c = pos ^ (row & 15);
+      const int brow = min(mb0 + r0, m - 1), grow = min(mb0 + row, m - 1);
+      const uint16_t* base = x + (size_t)brow * k + (size_t)g * kGroup;
+      const uint32_t voff = (uint32_t)(((size_t)(grow - brow) * k + 8 * c) * 2);
+      if (mb0 + row < m || lane == 0) dma16<false>(base, voff, lds_addr(xsl + r0 * 256));
     }
+    // weights: this wave's tile's records of group g
+    const uint8_t* wg = tbase + (size_t)(g / kSuper) * super_bytes + kBlock + (size_t)(g % kSuper) * group_bytes;
+    uint8_t* wsl = xsl + C::kXBytes + wave * C::kWCopies * kBlock;
+#pragma unroll
+    for (int p = 0; p < C::kWCopies; ++p) dma16<true>(wg + p * kBlock, lane * 16, lds_addr(wsl + p * kBlock));
+    // scales: the tile's scale block when group g opens a super-group (or the slice)
+    const bool full = (g % kSuper) == 0 || i == 0;
+    if (full || lane == 0)
+      dma16<false>(tbase + (size_t)(g / kSuper) * super_bytes, lane * 16,
+                   full ? lds_addr(&sblk[(g / kSuper) & 1][wave][0]) : lds_addr(&dummy[0]));
   };
-  auto store_x = [&](int buf) {
+  // INT4: row sums of stage i's activations (16 lanes per row, fixed order)
+  auto row_sums = [&](int i) {
+    const uint8_t* xsl = &ring[i % S][0];
 #pragma unroll
-    for (int q = 0; q < kChunks; ++q) {
-      const int c = tid + 256 * q, row = c >> 4, col = c & 15;
-      *(u32x4*)&xs[buf][row][16 * col] = xr[q];
-      if constexpr (FMT == 1) {
-        // the 16 chunks of a row are held by 16 consecutive lanes: sum them in a fixed order
-        float s = 0.f;
+    for (int q = 0; q < C::kXCopies; ++q) {
+      const int e = tid + 256 * q, row = e >> 4;
+      const u32x4 v = *(const u32x4*)(xsl + 16 * e);
+      float sum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          s += bf16_bits_to_f32(xr[q][e] & 0xFFFFu) + bf16_bits_to_f32(xr[q][e] >> 16);
-        s += __shfl_xor(s, 1, 16);
-        s += __shfl_xor(s, 2, 16);
-        s += __shfl_xor(s, 4, 16);
-        s += __shfl_xor(s, 8, 16);
-        if (col == 0) xsum[buf][row] = s;
-      }
+      for (int j = 0; j < 4; ++j) sum += bf16_bits_to_f32(v[j] & 0xFFFFu) + bf16_bits_to_f32(v[j] >> 16);
+      sum += __shfl_xor(sum, 1, 16);
+      sum += __shfl_xor(sum, 2, 16);
+      sum += __shfl_xor(sum, 4, 16);
+      sum += __shfl_xor(sum, 8, 16);
+      if ((e & 15) == 0) xsum[i % S][row] = sum;
     }
   };
 
@@ -166,33 +194,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 #pragma unroll
     for (int t = 0; t < WN; ++t) acc[bt][t] = f32x16{};
 
-  WRegs<FMT> wr[WN], wn[WN];
-  u32x4 scv[WN];     // the current super-group's eight fp16 scales of this lane's rows
-  uint32_t sc[WN];   // the dword of scv holding the current group's scale
-  if (g0 < g1) {
-    load_x(g0);
+  // prologue: S - 1 stages in flight
 #pragma unroll
-    for (int t = 0; t < WN; ++t) load_w<FMT>(wr[t], group_rec(t, g0));
-    store_x(0);
+  for (int i = 0; i < S - 1; ++i)
+    if (i < ng) issue(i);
+  if constexpr (FMT == 1) {
+    if (ng >= S - 1) wait_vm<C::kCopies * (S - 2)>();
+    else wait_vm<0>();
+    __syncthreads();
+    row_sums(0);
   }
-  __syncthreads();
-  int sg_loaded = -1;
-  for (int g = g0; g < g1; ++g) {
-    const int buf = (g - g0) & 1;
-    const bool more = g + 1 < g1;
-    if (more) {
-      load_x(g + 1);
-#pragma unroll
-      for (int t = 0; t < WN; ++t) load_w<FMT>(wn[t], group_rec(t, g + 1));
+
+  for (int i = 0; i < ng; ++i) {
+    // stage i (INT4: i + 1) has landed once at most the stages issued after it are in flight
+    if (i + C::kAhead < ng && i + S - 2 <= ng - 1) wait_vm<C::kWaitCopies>();
+    else wait_vm<0>();
+    __syncthreads();   // ... for every wave; and every wave is done with stage i - 1's slot
+    if (i + S - 1 < ng) issue(i + S - 1);
+    if constexpr (FMT == 1) {
+      if (i + 1 < ng) row_sums(i + 1);
     }
-    if (g / kSuper != sg_loaded) {
-      sg_loaded = g / kSuper;
-#pragma unroll
-      for (int t = 0; t < WN; ++t)
-        scv[t] = *(const u32x4*)(rowbase[t] + (size_t)sg_loaded * super_bytes);
-    }
-#pragma unroll
-    for (int t = 0; t < WN; ++t) sc[t] = scv[t][(g % kSuper) >> 1];
+    const int g = g0 + i;
+    const uint8_t* xsl = &ring[i % S][0];
+    const uint8_t* wsl = xsl + C::kXBytes + wave * C::kWCopies * kBlock;
 
     f32x16 part[WB][WN];
     // Q1: per 32-row block, the two sign dwords of this lane's half, un-rotated and complemented
@@ -200,16 +224,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     // sits at i and i + 15 with no other bit at i + 16, so one shift brings a pair's two bits
     // to the sign positions 15 and 31 of a bf16 pair (yl: bytes 0 and 1, yh: bytes 2 and 3).
     uint32_t yl[WN][2], yh[WN][2];
-    if constexpr (FMT == 0) {
+    u32x4 ca[WN], cb[WN];
 #pragma unroll
-      for (int t = 0; t < WN; ++t)
+    for (int t = 0; t < WN; ++t) {
+      const uint8_t* rec = wsl + (32 * t + l32) * 16;
+      if constexpr (FMT == 0) {
+        const u32x2 v = *(const u32x2*)(rec + 8 * h);
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const uint32_t d = ~__builtin_amdgcn_alignbit(wr[t].v[e], wr[t].v[e], 2);
+          const uint32_t d = ~__builtin_amdgcn_alignbit(v[e], v[e], 2);
           const uint32_t vl = d & 0xFFFFu, vh = d >> 16;
           yl[t][e] = vl | (vl << 15);
           yh[t][e] = vh | (vh << 15);
         }
+      } else {
+        ca[t] = *(const u32x4*)(rec + 2 * h * kBlock);
+        cb[t] = *(const u32x4*)(rec + (2 * h + 1) * kBlock);
+      }
     }
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -224,18 +255,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
             const int c = 8 * byte + 2 * p;
-            const uint32_t sh = c < 16 ? (yl[t][e] << (15 - c)) : (yh[t][e] << (31 - c));   // c - 16 -> 15
+            const uint32_t sh = c < 16 ? (yl[t][e] << (15 - c)) : (yh[t][e] << (31 - c));
             r[p] = (sh & 0x80008000u) | 0x3F803F80u;
           }
           bw[t] = __builtin_bit_cast(bf16x8, r);
         } else {
-          const u32x4& pc = s < 4 ? wr[t].a : wr[t].b;
-          bw[t] = i4_unpack(pc[s & 3]);
+          bw[t] = i4_unpack(s < 4 ? ca[t][s & 3] : cb[t][s & 3]);
         }
       }
 #pragma unroll
       for (int bt = 0; bt < WB; ++bt) {
-        const bf16x8 xa = *(const bf16x8*)&xs[buf][32 * bt + l32][(64 * h + 8 * s) * 2];
+        const int row = 32 * bt + l32, c = 8 * h + s;
+        const bf16x8 xa = *(const bf16x8*)(xsl + row * 256 + 16 * (c ^ (row & 15)));
 #pragma unroll
         for (int t = 0; t < WN; ++t)
           part[bt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, bw[t], s == 0 ? f32x16{} : part[bt][t],
@@ -245,29 +276,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     // fold the group into the outputs with its scale (lane column = weight row)
 #pragma unroll
     for (int t = 0; t < WN; ++t) {
-      const float scale = f16_bits_to_f32((g & 1) ? (sc[t] >> 16) : (sc[t] & 0xFFFFu));
+      const uint16_t sb = *(const uint16_t*)&sblk[(g / kSuper) & 1][wave][(32 * t + l32) * 16 + 2 * (g % kSuper)];
+      const float scale = f16_bits_to_f32(sb);
 #pragma unroll
       for (int bt = 0; bt < WB; ++bt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float v = part[bt][t][r];
           if constexpr (FMT == 1) {
-            const int i = 8 * (r >> 2) + 4 * h + (r & 3);
-            v = fmaf(16.f, v, -24.f * xsum[buf][32 * bt + i]);
+            const int ii = 8 * (r >> 2) + 4 * h + (r & 3);
+            v = fmaf(16.f, v, -24.f * xsum[i % S][32 * bt + ii]);
           }
           acc[bt][t][r] = fmaf(scale, v, acc[bt][t][r]);
         }
       }
     }
-    if (more) {
-      store_x(buf ^ 1);
-#pragma unroll
-      for (int t = 0; t < WN; ++t) wr[t] = wn[t];
-    }
-    __syncthreads();
   }
 
-  // outputs: lane column = weight row rown[t], register r = activation row 8(r/4) + 4h + r%4
+  // outputs: lane column = weight row, register r = activation row 8(r/4) + 4h + r%4
+  int rown[WN];
+#pragma unroll
+  for (int t = 0; t < WN; ++t) rown[t] = nb0 + wave * 64 + 32 * t + l32;
   if (splits == 1) {
 #pragma unroll
     for (int bt = 0; bt < WB; ++bt)
@@ -282,7 +311,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       }
     return;
   }
-  const int mp = (int)gridDim.y * BM;   // activation rows of one slice of the partial buffer
+  const int mp = (int)gridDim.y * C::kBM;   // activation rows of one slice of the partial buffer
 #pragma unroll
   for (int bt = 0; bt < WB; ++bt)
 #pragma unroll
@@ -296,22 +325,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       }
   unsigned* counter = counters + (size_t)blockIdx.y * gridDim.x + blockIdx.x;
   if (!splitk_last(counter, splits)) return;
+  // the last workgroup of the tile: thread tid owns weight row nb0 + tid of every activation
+  // row of the tile and adds the slices in slice order; one slice's kBM loads are in flight at
+  // once (rows of consecutive threads are consecutive words)
+  const int row = nb0 + tid;
+  if (row < n) {
+    float sum[C::kBM];
 #pragma unroll
-  for (int bt = 0; bt < WB; ++bt)
+    for (int b = 0; b < C::kBM; ++b) sum[b] = 0.f;
+    for (int j = 0; j < splits; ++j) {
+      const float* pj = partial + ((size_t)j * mp + mb0) * np + row;
+      float v[C::kBM];
 #pragma unroll
-    for (int t = 0; t < WN; ++t) {
-      if (rown[t] >= n) continue;
+      for (int b = 0; b < C::kBM; ++b)
+        v[b] = __hip_atomic_load(pj + (size_t)b * np, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int b = mb0 + 32 * bt + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (b >= m) continue;
-        float sum = 0.f;
-        for (int j = 0; j < splits; ++j)
-          sum += __hip_atomic_load(&partial[((size_t)j * mp + b) * np + rown[t]], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        y[(size_t)b * n + rown[t]] = (uint16_t)to_bf16(sum);
-      }
+      for (int b = 0; b < C::kBM; ++b) sum[b] += v[b];
     }
+#pragma unroll
+    for (int b = 0; b < C::kBM; ++b)
+      if (mb0 + b < m) y[(size_t)(mb0 + b) * n + row] = (uint16_t)to_bf16(sum[b]);
+  }
   if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -345,16 +379,18 @@ lbq_status gemm_launch(const void* d_w, int32_t n, int32_t k, const uint16_t* d_
   if (overlaps(d_y, yb, d_x, (size_t)m * k * 2) || overlaps(d_y, yb, d_w, layout_bytes(g)))
     return LBQ_E_ALIAS;
   hipStream_t s = (hipStream_t)stream;
-  constexpr int WN = 2, BN = 32 * WN * kWaves;
+  constexpr int BN = 256;
   const int wb = m > 32 ? 2 : 1, bm = 32 * wb;
   const long long gx = (n + BN - 1) / BN, gy = (m + bm - 1) / bm;
   const int groups = (int)g.groups;
-  // enough workgroups to fill the device twice over, each slice at least two groups deep
+  // split K when the output tiles alone leave compute units idle; a slice is at least one
+  // super-group deep, so the pipeline fills and the final sum stays short
   int splits = 1;
-  const long long want = 2LL * cu_count();
+  const long long want = cu_count();
   if (gx * gy < want) {
     splits = (int)((want + gx * gy - 1) / (gx * gy));
-    splits = splits > groups / 2 ? groups / 2 : splits;
+    const int deep = groups / kSuper;
+    splits = splits > deep ? deep : splits;
     if (splits < 1) splits = 1;
   }
   int gps = (groups + splits - 1) / splits;
@@ -369,10 +405,10 @@ lbq_status gemm_launch(const void* d_w, int32_t n, int32_t k, const uint16_t* d_
   }
   const dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)splits);
 #define LAUNCH(WB)                                                                               \
-  hipLaunchKernelGGL((gemm_kernel<FMT, WB, WN>), grid, dim3(256), 0, s, (const uint8_t*)d_w, d_x, \
-                     d_y, partials, counters, (int)m, (int)n, (int)k, (int)g.np, groups,          \
-                     (long long)g.tile_bytes, (long long)g.super_bytes, (int)g.group_bytes, gps,  \
-                     splits)
+  hipLaunchKernelGGL((gemm_kernel<FMT, WB>), grid, dim3(256), 0, s, (const uint8_t*)d_w, d_x,     \
+                     d_y, partials, counters, (int)m, (int)n, (int)k, (int)g.np, (int)g.tiles,    \
+                     groups, (long long)g.tile_bytes, (long long)g.super_bytes,                   \
+                     (int)g.group_bytes, gps, splits)
   if (wb == 1) LAUNCH(1); else LAUNCH(2);
 #undef LAUNCH
   return hipGetLastError() == hipSuccess ? LBQ_OK : LBQ_E_DEVICE;

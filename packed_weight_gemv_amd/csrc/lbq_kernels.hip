@@ -534,6 +534,11 @@ static lbq_status gemv_common(Fmt fmt, const void* d_w, int32_t n, int32_t k,
     const lbq_status st = lbq_engine_gemv_q1(d_w, n, k, d_x, d_y, s);
     if (st != LBQ_E_UNSUPPORTED) return st;
   }
+  // two or more vectors: the matrix-core product (it needs 16-byte aligned rows of x; other
+  // alignments take the per-row lookup kernels below)
+  if (batch >= 2 && (uintptr_t)d_x % 16 == 0)
+    return fmt == Fmt::Q1 ? lbq_gemm_q1g128(d_w, n, k, d_x, d_y, batch, stream)
+                          : lbq_gemm_i4g128(d_w, n, k, d_x, d_y, batch, stream);
   unsigned* counters = nullptr;
   float* partials = nullptr;
   if (g.supers > 1) {

@@ -86,3 +86,22 @@ def test_power_of_two_input_scaling_is_exact_and_deterministic(lbq):
     y2 = _run(lbq, m, x2)
     assert np.array_equal(oracle.bf16_to_f64(y2), 0.5 * oracle.bf16_to_f64(y1))
     assert np.array_equal(_run(lbq, m, x), y1)
+
+
+@pytest.mark.parametrize("batch", [2, 4, 16])
+def test_parity_batches_with_rows_not_16_byte_aligned(lbq, batch):
+    # x at a 4-byte but not 16-byte aligned address: the per-row lookup kernels (aligned
+    # batches take the matrix-core product)
+    n, k = 192, 2176
+    m = synth.i4_matrix(n, k, workload=24)
+    x = synth.activations(batch, k, workload=24, extra=batch)
+    buf = torch.zeros(batch * k + 8, dtype=torch.int16, device="cuda:0")
+    xv = buf[2:2 + batch * k].view(batch, k)
+    assert xv.data_ptr() % 16 == 4
+    xv.copy_(to_dev(x))
+    w = to_dev(lbq.lbq_pack_i4g128(m.nib, m.scales))
+    y = empty_bf16(batch, n)
+    lbq.lbq_gemv_i4g128(w, n, k, xv, y)
+    torch.cuda.synchronize()
+    ref, l1 = oracle.gemv_i4g128(m.nib, m.scales, x)
+    check_within(bits(y), ref, l1, f"i4 unaligned batch {batch}")

@@ -116,3 +116,22 @@ def test_batch_zero_is_a_no_op(lbq):
     lbq.lbq_gemv_q1g128(w, 64, 128, x, y)
     torch.cuda.synchronize()
     assert (y == 7).all()
+
+
+@pytest.mark.parametrize("batch", [2, 4, 16])
+def test_parity_batches_with_rows_not_16_byte_aligned(lbq, batch):
+    # x at a 4-byte but not 16-byte aligned address: the per-row lookup kernels (aligned
+    # batches take the matrix-core product)
+    n, k = 192, 2176
+    m = synth.q1_matrix(n, k, workload=24)
+    x = synth.activations(batch, k, workload=24, extra=batch)
+    buf = torch.zeros(batch * k + 8, dtype=torch.int16, device="cuda:0")
+    xv = buf[2:2 + batch * k].view(batch, k)
+    assert xv.data_ptr() % 16 == 4
+    xv.copy_(to_dev(x))
+    w = to_dev(lbq.lbq_pack_q1g128(m.signs, m.scales))
+    y = empty_bf16(batch, n)
+    lbq.lbq_gemv_q1g128(w, n, k, xv, y)
+    torch.cuda.synchronize()
+    ref, l1 = oracle.gemv_q1g128(m.signs, m.scales, x)
+    check_within(bits(y), ref, l1, f"q1 unaligned batch {batch}")
