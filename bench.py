@@ -10,6 +10,10 @@ step is one launch of the persistent engine; larger batches replay a HIP graph o
 the per-projection launches. W untimed warm-up steps precede exactly K timed steps bracketed
 by device synchronisation.
 
+With --gemm the bench times the many-row products on the matrix cores instead (prefill and
+large batch: Q1 MLP and INT4 layer shapes at 32, 128 and 512 activation rows) and reports
+TFLOP/s against the bf16 matrix-core peak.
+
 Printed: one JSON line on stdout (progress goes to stderr).
 """
 from __future__ import annotations
@@ -68,6 +72,9 @@ def parse():
                     help="layers of the stream the CPU oracle baseline runs (0 = skip)")
     ap.add_argument("--kernel-steps", type=int, default=3,
                     help="instrumented steps timing each GEMV launch with HIP events")
+    ap.add_argument("--gemm", action="store_true",
+                    help="instead of the decode step, time the many-row products on the matrix "
+                         "cores (Q1 MLP and INT4 layer shapes, 32 to 512 activation rows)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (the reference for "
                          "scaling HBM byte counters), then exit")
@@ -109,6 +116,8 @@ def main() -> int:
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
     log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), CUs {props.multi_processor_count}")
+    if args.gemm:
+        return gemm_bench(args, lbq, synth, torch, np, dev)
 
     L, B = args.layers, args.batch
     hid, kv, ffn = synth.STREAM_HIDDEN, synth.STREAM_KV, synth.STREAM_FFN
@@ -268,6 +277,90 @@ def main() -> int:
             "bytes_per_launch": round(kern_bytes),
         },
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+
+
+def gemm_bench(args, lbq, synth, torch, np, dev) -> int:
+    """Many-row products (prefill / large batch) on the matrix cores: y[m][n] = x[m][k] W^T for
+    the Q1 MLP shapes (gate 17408x5120, down 5120x17408) and the INT4 layer shapes (gate
+    12288x4096, down 4096x12288) at m = 32, 128, 512 activation rows. Weights rotate through a
+    pool of at least 1 GiB of copies so that every call streams them from HBM; times are HIP
+    events around `steps` calls after `warmup` calls on the launch stream. Flops = 2 m n k."""
+    cases = []
+    shapes = [("q1", 17408, 5120), ("q1", 5120, 17408), ("i4", 12288, 4096), ("i4", 4096, 12288)]
+    stream = torch.cuda.current_stream()
+    for fmt, n, k in shapes:
+        wl = synth.W_Q1_MLP if fmt == "q1" else synth.W_I4_LAYER
+        mat = (synth.q1_matrix(n, k, workload=wl, matrix=n + k) if fmt == "q1"
+               else synth.i4_matrix(n, k, workload=wl, matrix=n + k))
+        packed = (lbq.lbq_pack_q1g128(mat.signs, mat.scales) if fmt == "q1"
+                  else lbq.lbq_pack_i4g128(mat.nib, mat.scales))
+        host = torch.from_numpy(packed)
+        pool = [host.to(dev) for _ in range(max(2, -(-(1 << 30) // packed.nbytes)))]
+        fn = lbq.lbq_gemm_q1g128 if fmt == "q1" else lbq.lbq_gemm_i4g128
+        for m in (32, 128, 512):
+            x = torch.from_numpy(synth.activations(m, k, workload=wl, matrix=n + k, extra=m)
+                                 .view(np.int16)).to(dev)
+            y = torch.empty((m, n), dtype=torch.int16, device=dev)
+            it = [0]
+
+            def call():
+                fn(pool[it[0] % len(pool)], n, k, x, y, stream=stream)
+                it[0] += 1
+
+            for _ in range(max(1, args.warmup)):
+                call()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.steps):
+                call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / args.steps
+            tflops = 2.0 * m * n * k / (us * 1e-6) / 1e12
+            cases.append({"format": fmt, "n": n, "k": k, "m": m, "us_per_call": round(us, 2),
+                          "tflops": round(tflops, 2), "weight_gbs": round(packed.nbytes / us / 1e3, 1),
+                          "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)})
+            log(f"gemm {fmt} {n}x{k} m={m}: {us:.1f} us, {tflops:.1f} TFLOP/s")
+        del pool
+        torch.cuda.empty_cache()
+    head = next(c for c in cases if c["format"] == "q1" and c["n"] == 17408 and c["m"] == 512)
+    # the oracle (one host thread) on the first 4 activation rows of the head case, all outputs
+    import oracle
+    mat = synth.q1_matrix(17408, 5120, workload=synth.W_Q1_MLP, matrix=17408 + 5120)
+    xs = synth.activations(512, 5120, workload=synth.W_Q1_MLP, matrix=17408 + 5120, extra=512)[:4]
+    t0 = time.perf_counter()
+    oracle.gemv_q1g128(mat.signs, mat.scales, xs)
+    dt = time.perf_counter() - t0
+    out = {
+        "metric": "packed-weight GEMM TFLOP/s on the matrix cores (prefill / large batch)",
+        "value": head["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["us_per_call"] / 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Q1_0_g128 gate 17408x5120, 512 activation rows (head); Q1 MLP and "
+                               "INT4 layer shapes at 32/128/512 rows in cases",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": head["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": head["mfma_frac"], "traffic": None,
+                     "kernel": "gemm_kernel<0, 2>"},
+        "cpu_baseline": {"value": round(2.0 * 4 * 17408 * 5120 / dt / 1e12, 6), "unit": "TFLOP/s",
+                         "cores": 1, "kind": "oracle",
+                         "sample": "4 activation rows x all 17408 outputs of the head case"},
+        "cases": cases,
     }
     print(json.dumps(out), flush=True)
     return 0

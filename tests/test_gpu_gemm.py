@@ -45,6 +45,7 @@ def _gemm(lbq, fmt, w, n, k, x):
     (333, 9216, 5),      # split-K over many groups
     (1000, 1024, 64),
     (512, 4096, 97),
+    (300, 2176, 150),    # 128-row activation tiles with a ragged last tile
 ])
 def test_parity_small_shapes(lbq, fmt, n, k, m):
     mat = _matrix(fmt, n, k, workload=40, matrix=n + m)
