@@ -60,6 +60,10 @@ def _load():
     lib.oracle_gemv_q1g128.restype = None
     lib.oracle_gemv_i4g128.argtypes = [P, P, i32, i32, P, i32, P, i32, P, P]
     lib.oracle_gemv_i4g128.restype = None
+    lib.oracle_quant_act_i8g128.argtypes = [P, i32, i32, P, P]
+    lib.oracle_quant_act_i8g128.restype = None
+    lib.oracle_gemv_i4g128_i8act.argtypes = [P, P, i32, i32, P, P, i32, P, i32, P, P]
+    lib.oracle_gemv_i4g128_i8act.restype = None
     lib.oracle_rms_rescale.argtypes = [P, P, i32, i32, ctypes.c_double, P, P]
     lib.oracle_rms_rescale.restype = None
     lib.oracle_round_bf16.argtypes = [P, ctypes.c_size_t, P]
@@ -178,6 +182,57 @@ def gemv_i4g128(nib, scales, x, rows=None):
     sc = _c(scales, np.uint16)
     assert sc.shape == (n, k // 128)
     return _gemv("oracle_gemv_i4g128", q, sc, n, k, x, rows)
+
+
+def quant_act_i8g128(x):
+    """int8 quantization of bf16 activations per row and per group of 128 (a reading: symmetric
+    absmax, d = fp32(max|x|)/127, q = rint(x/d) in fp32, clamped to +-127). Pinned by the
+    half-step reconstruction bound, the absmax element mapping to +-127, sign symmetry, exact
+    power-of-two scaling and the zero group (tests/test_oracle_i8act.py).
+
+    x: bf16 bits [B][k] or [k]. Returns (q int8 [B][k], d float32 [B][k/128])."""
+    lib = _load()
+    x2 = _c(x, np.uint16)
+    if x2.ndim == 1:
+        x2 = x2[None, :]
+    B, k = x2.shape
+    assert k % 128 == 0
+    q = np.zeros((B, k), dtype=np.int8)
+    d = np.zeros((B, k // 128), dtype=np.float32)
+    lib.oracle_quant_act_i8g128(_ptr(x2), k, B, _ptr(q), _ptr(d))
+    return q, d
+
+
+def gemv_i4g128_i8act(nib, scales, q, d, rows=None):
+    """INT4 g128 GEMV on int8-quantized activations: y = sum_g s d sum_j w q with an exact
+    integer inner sum (pinned: within the quantization bound of the unquantized product, exact
+    equality when every group's activations are integers with absmax 127, exact one-hot;
+    tests/test_oracle_i8act.py).
+
+    nib: canonical uint8 [n][k/2]; scales: fp16 bits [n][k/128]; q: int8 [B][k];
+    d: float32 [B][k/128]. Returns (y float64 [B][rows], l1 float64 [B][rows])."""
+    lib = _load()
+    w = _c(nib, np.uint8)
+    n, k2 = w.shape
+    k = k2 * 2
+    sc = _c(scales, np.uint16)
+    assert sc.shape == (n, k // 128)
+    q2 = _c(q, np.int8)
+    d2 = _c(d, np.float32)
+    if q2.ndim == 1:
+        q2, d2 = q2[None, :], d2[None, :]
+    B = q2.shape[0]
+    assert q2.shape == (B, k) and d2.shape == (B, k // 128)
+    if rows is None:
+        nr, rp = n, None
+    else:
+        ra = _c(rows, np.int32)
+        nr, rp = ra.size, _ptr(ra)
+    y = np.zeros((B, nr), dtype=np.float64)
+    l1 = np.zeros((B, nr), dtype=np.float64)
+    lib.oracle_gemv_i4g128_i8act(_ptr(w), _ptr(sc), n, k, _ptr(q2), _ptr(d2), B, rp, nr,
+                                 _ptr(y), _ptr(l1))
+    return y, l1
 
 
 def rms_rescale(y, y2=None, eps: float = 1e-6):

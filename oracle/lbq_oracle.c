@@ -214,6 +214,78 @@ void oracle_gemv_i4g128(const uint8_t* nib, const uint16_t* scales, int n, int k
 }
 
 /* ---------------------------------------------------------------------------------------
+ * INT4 weights x int8-quantized activations with integer dot products (Acorn page, the
+ * section on the gap to llama.cpp: int4 weights, int8 activations and integer dot products,
+ * with a logits deviation of about 1e-3 quoted for the switch that enables them). The pages
+ * give no quantization rule. The reading taken: per activation row and per group of 128
+ * along k (the weights' group), symmetric absmax,
+ *   d = fp32(max |x|) / 127   (an fp32 division, ties to even),
+ *   q = rint(x / d)            (an fp32 division, then round half to even), clamped to
+ *                              [-127, 127]; an all-zero group has d = 0 and q = 0.
+ * The codes are decided in fp32, the precision of the kernels, so both sides make the same
+ * decision. x: bf16 bits [batch][k]; q: int8 [batch][k]; d: fp32 [batch][k/128].
+ * ------------------------------------------------------------------------------------- */
+void oracle_quant_act_i8g128(const uint16_t* x, int k, int batch, int8_t* q, float* d) {
+  int ng = k / 128;
+  for (int b = 0; b < batch; ++b) {
+    for (int g = 0; g < ng; ++g) {
+      const uint16_t* xg = x + (size_t)b * k + (size_t)g * 128;
+      float a = 0.0f;
+      for (int j = 0; j < 128; ++j) {
+        float v = (float)oracle_bf16_to_f64(xg[j]);   /* exact: bf16 is a subset of fp32 */
+        float m = fabsf(v);
+        if (m > a) a = m;
+      }
+      float dd = a / 127.0f;
+      d[(size_t)b * ng + g] = dd;
+      for (int j = 0; j < 128; ++j) {
+        int code = 0;
+        if (dd != 0.0f) {
+          float v = (float)oracle_bf16_to_f64(xg[j]);
+          float t = rintf(v / dd);
+          if (t > 127.0f) t = 127.0f;
+          if (t < -127.0f) t = -127.0f;
+          code = (int)t;
+        }
+        q[(size_t)b * k + (size_t)g * 128 + j] = (int8_t)code;
+      }
+    }
+  }
+}
+
+/* The INT4 GEMV on quantized activations: y[b][r] = sum_g s[r][g] * d[b][g] *
+ * sum_{j in g} w[r][j] q[b][j], the inner sum an exact integer. l1 = sum_g |s d| sum |w q|. */
+void oracle_gemv_i4g128_i8act(const uint8_t* nib, const uint16_t* scales, int n, int k,
+                              const int8_t* q, const float* d, int batch, const int32_t* rows,
+                              int n_rows, double* y, double* l1) {
+  int ng = k / 128;
+  int nr = rows ? n_rows : n;
+  for (int b = 0; b < batch; ++b) {
+    for (int i = 0; i < nr; ++i) {
+      int r = rows ? rows[i] : i;
+      double acc = 0.0, mag = 0.0;
+      for (int g = 0; g < ng; ++g) {
+        double s = oracle_f16_to_f64(scales[(size_t)r * ng + g]);
+        double dd = (double)d[(size_t)b * ng + g];
+        long long isum = 0, iabs = 0;
+        for (int j = 128 * g; j < 128 * g + 128; ++j) {
+          uint8_t byte = nib[(size_t)r * (k / 2) + j / 2];
+          int u = (j % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+          int w = u >= 8 ? u - 16 : u;
+          int qx = q[(size_t)b * k + j];
+          isum += (long long)w * qx;
+          iabs += (long long)(w * qx < 0 ? -(w * qx) : w * qx);
+        }
+        acc += s * dd * (double)isum;
+        mag += fabs(s) * dd * (double)iabs;
+      }
+      y[(size_t)b * nr + i] = acc;
+      l1[(size_t)b * nr + i] = mag;
+    }
+  }
+}
+
+/* ---------------------------------------------------------------------------------------
  * RMS rescale between GEMVs of the decode-step stream (a reading: the pages name no
  * formula). h = y * y2 (or y), x = bf16_rne(h / sqrt(mean(h^2) + eps)). `exact` receives the
  * unrounded quotient so tests can tell rounding-boundary cases apart. Arrays are [batch][n].
