@@ -12,7 +12,9 @@ by device synchronisation.
 
 With --gemm the bench times the many-row products on the matrix cores instead (prefill and
 large batch: Q1 MLP and INT4 layer shapes at 32, 128 and 512 activation rows) and reports
-TFLOP/s against the bf16 matrix-core peak.
+TFLOP/s against the bf16 matrix-core peak. With --i4-layer it times the seven projections of a
+Qwen3-8B-shaped INT4 g128 layer at B = 1 and 8 through the bf16-activation GEMV and the
+int8-activation GEMV (integer dot products) and reports packed-weight GB/s against HBM.
 
 Printed: one JSON line on stdout (progress goes to stderr).
 """
@@ -72,6 +74,8 @@ def parse():
                     help="layers of the stream the CPU oracle baseline runs (0 = skip)")
     ap.add_argument("--kernel-steps", type=int, default=3,
                     help="instrumented steps timing each GEMV launch with HIP events")
+    ap.add_argument("--i4-layer", action="store_true",
+                    help="time the INT4 layer GEMVs (float and int8-activation paths) instead")
     ap.add_argument("--gemm", action="store_true",
                     help="instead of the decode step, time the many-row products on the matrix "
                          "cores (Q1 MLP and INT4 layer shapes, 32 to 512 activation rows)")
@@ -118,6 +122,8 @@ def main() -> int:
     log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), CUs {props.multi_processor_count}")
     if args.gemm:
         return gemm_bench(args, lbq, synth, torch, np, dev)
+    if args.i4_layer:
+        return i4_layer_bench(args, lbq, synth, torch, np, dev)
 
     L, B = args.layers, args.batch
     hid, kv, ffn = synth.STREAM_HIDDEN, synth.STREAM_KV, synth.STREAM_FFN
@@ -283,6 +289,99 @@ def main() -> int:
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+
+
+def i4_layer_bench(args, lbq, synth, torch, np, dev) -> int:
+    """The seven projections of a Qwen3-8B-shaped INT4 g128 layer (q, o 4096x4096; k, v
+    1024x4096; gate, up 12288x4096; down 4096x12288) through lbq_gemv_i4g128 (bf16 activations)
+    and lbq_gemv_i4g128_act_i8 (int8 activations quantized in the kernel, integer dot products),
+    at B = 1 and 8. Weights rotate through a pool of at least 1 GiB of copies so that every call
+    streams them from HBM; the time per layer is the sum of the projections' HIP-event times on
+    the launch stream (`steps` calls each after `warmup`). Algorithmic bytes: the packed weights
+    (33/64 B per weight) plus bf16 activations in and out."""
+    stream = torch.cuda.current_stream()
+    paths = (("bf16", lbq.lbq_gemv_i4g128), ("i8act", lbq.lbq_gemv_i4g128_act_i8))
+    layer = {(p, b): [0.0, 0] for p, _ in paths for b in (1, 8)}
+    cases = []
+    for name, n, k in synth.I4_SHAPES:
+        mat = synth.i4_matrix(n, k, workload=synth.W_I4_LAYER,
+                              matrix=synth.STREAM_MATRICES.index(name))
+        packed = lbq.lbq_pack_i4g128(mat.nib, mat.scales)
+        host = torch.from_numpy(packed)
+        pool = [host.to(dev) for _ in range(max(2, -(-(1 << 30) // packed.nbytes)))]
+        for batch in (1, 8):
+            x = torch.from_numpy(synth.activations(batch, k, workload=synth.W_I4_LAYER,
+                                                   extra=100 + batch).view(np.int16)).to(dev)
+            y = torch.empty((batch, n), dtype=torch.int16, device=dev)
+            nbytes = packed.nbytes + 2 * batch * (n + k)
+            for pname, fn in paths:
+                it = [0]
+
+                def call():
+                    fn(pool[it[0] % len(pool)], n, k, x, y, stream=stream)
+                    it[0] += 1
+
+                for _ in range(max(1, args.warmup)):
+                    call()
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(args.steps):
+                    call()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / args.steps
+                layer[(pname, batch)][0] += us
+                layer[(pname, batch)][1] += nbytes
+                cases.append({"path": pname, "proj": name, "n": n, "k": k, "batch": batch,
+                              "us_per_call": round(us, 2), "gbs": round(nbytes / us / 1e3, 1)})
+                log(f"i4 {pname} {name} {n}x{k} B={batch}: {us:.1f} us, {nbytes / us / 1e3:.0f} GB/s")
+        del pool
+        torch.cuda.empty_cache()
+    summary = {f"{p}_B{b}": {"us_per_layer": round(v[0], 2), "gbs": round(v[1] / v[0] / 1e3, 1)}
+               for (p, b), v in layer.items()}
+    head_us, head_bytes = layer[("i8act", 1)]
+    gbs = head_bytes / head_us / 1e3
+    # the oracle (one host thread): quantize and multiply 512 rows of each projection, B = 1
+    import oracle
+    t0 = time.perf_counter()
+    sampled = 0
+    for name, n, k in synth.I4_SHAPES:
+        mat = synth.i4_matrix(n, k, workload=synth.W_I4_LAYER,
+                              matrix=synth.STREAM_MATRICES.index(name))
+        xs = synth.activations(1, k, workload=synth.W_I4_LAYER, extra=101)
+        q, d = oracle.quant_act_i8g128(xs)
+        oracle.gemv_i4g128_i8act(mat.nib, mat.scales, q, d, rows=np.arange(512, dtype=np.int32))
+        sampled += 512 * k * 33 // 64
+    dt = time.perf_counter() - t0
+    out = {
+        "metric": "packed-weight HBM GB/s of the INT4 g128 layer GEMVs, int8 activations",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head_us / 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 x int4 -> int32, fp32 group scaling",
+        "data": "synthetic",
+        "config": {"workload": "Qwen3-8B-shaped INT4 g128 layer (7 projections), B = 1, int8 "
+                               "activations; bf16 path and B = 8 in cases",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "i4_i8act_gemv_kernel<1>"},
+        "cpu_baseline": {"value": round(sampled / dt / 1e9, 5), "unit": "GB/s", "cores": 1,
+                         "kind": "oracle",
+                         "sample": "quantize + 512 output rows of each of the 7 projections, B = 1"},
+        "summary": summary,
+        "cases": cases,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
 
 
 def gemm_bench(args, lbq, synth, torch, np, dev) -> int:

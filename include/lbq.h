@@ -183,6 +183,34 @@ lbq_status lbq_gemm_i4g128(const void* d_w, int32_t n, int32_t k, const uint16_t
                            uint16_t* d_y, int32_t m, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * INT4 weights x int8 activations with integer dot products (the Acorn page, its analysis of
+ * the speed gap to llama.cpp: int4 weights, int8 activations and integer dot products, with a
+ * logit deviation of about 1e-3 against the float path; also its list of known limitations).
+ * The page does not give the activation quantizer; the library's reading is symmetric absmax
+ * per activation row and per 128-group along k, every step an fp32 operation rounded to
+ * nearest even:
+ *   d[b][g] = max_{j in g} |x[b][j]| / 127          q[b][j] = clamp(rint(x[b][j] / d), -127, 127)
+ * with d = 0 and q = 0 for a group of zeros (a group holding an infinity or NaN has undefined
+ * codes).
+ * ------------------------------------------------------------------------------------------ */
+
+/* Quantizes activations: d_x bf16 [batch][k] -> d_q int8 [batch][k] and d_scale fp32
+ * [batch][k/128], bit-exact to the rule above. Requires k % 128 == 0, 128 <= k <= 2^24,
+ * 0 <= batch <= 65535 (0 is a no-op); d_x 4-byte, d_q 2-byte, d_scale 4-byte aligned; outputs
+ * must not overlap the input or each other. Caller owns all buffers. */
+lbq_status lbq_quant_act_i8g128(const uint16_t* d_x, int32_t k, int32_t batch, int8_t* d_q,
+                                float* d_scale, void* stream);
+
+/* y[b][row] = bf16_rne( sum_g f32(scale[row][g]) * d[b][g] * S[b][row][g] ), fp32 accumulation
+ * over the groups, where S = sum_{j in g} w[row][j] * q[b][j] is an exact integer and q, d are
+ * the quantized activations of x as lbq_quant_act_i8g128 defines them (quantized inside the
+ * kernel; no buffer is written besides d_y). The product scale * d is taken in fp32 before
+ * S joins it. Weights d_w in the INT4 device layout; shape, pointer, alignment, batch and
+ * workspace rules as lbq_gemv_i4g128. */
+lbq_status lbq_gemv_i4g128_act_i8(const void* d_w, int32_t n, int32_t k, const uint16_t* d_x,
+                                  uint16_t* d_y, int32_t batch, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * RMS rescale: the glue that carries bf16 activations from one GEMV to the next in a decode
  * step of the 27B-shaped 1-bit stream (64 layers, Bonsai digest, "262K context window").
  * The pages name no normalisation formula; the library's reading is

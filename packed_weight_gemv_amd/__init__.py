@@ -62,6 +62,8 @@ def load():
         "lbq_gemv_i4g128": ([P, i32, i32, P, P, i32, P], i32),
         "lbq_gemm_q1g128": ([P, i32, i32, P, P, i32, P], i32),
         "lbq_gemm_i4g128": ([P, i32, i32, P, P, i32, P], i32),
+        "lbq_quant_act_i8g128": ([P, i32, i32, P, P, P], i32),
+        "lbq_gemv_i4g128_act_i8": ([P, i32, i32, P, P, i32, P], i32),
         "lbq_rms_rescale_bf16": ([P, P, P, i32, i32, ctypes.c_float, P], i32),
         "lbq_decode_act_elems": ([i32, i32, i32, i32, i32], sz),
         "lbq_decode_act_offset": ([i32, i32, i32, i32, i32, i32, i32], i64),
@@ -224,6 +226,20 @@ def lbq_gemm_i4g128(w, n: int, k: int, x, y, stream=None) -> None:
     m = x.shape[0] if x.dim() == 2 else 1
     _check("lbq_gemm_i4g128", load().lbq_gemm_i4g128(_dptr(w), n, k, _dptr(x), _dptr(y), m,
                                                      _stream(stream)))
+
+
+def lbq_quant_act_i8g128(x, q, scale, stream=None) -> None:
+    """x: bf16/int16 [B][k] -> q: int8 [B][k], scale: float32 [B][k/128] (all device tensors)."""
+    B, k = (x.shape[0], x.shape[1]) if x.dim() == 2 else (1, x.shape[0])
+    _check("lbq_quant_act_i8g128", load().lbq_quant_act_i8g128(
+        _dptr(x), k, B, _dptr(q), _dptr(scale), _stream(stream)))
+
+
+def lbq_gemv_i4g128_act_i8(w, n: int, k: int, x, y, stream=None) -> None:
+    """INT4 weights x int8-quantized activations (quantized in the kernel). x: bf16 [B][k]."""
+    B = x.shape[0] if x.dim() == 2 else 1
+    _check("lbq_gemv_i4g128_act_i8", load().lbq_gemv_i4g128_act_i8(
+        _dptr(w), n, k, _dptr(x), _dptr(y), B, _stream(stream)))
 
 
 def lbq_rms_rescale_bf16(y, x, y2=None, eps: float = 1e-6, stream=None) -> None:

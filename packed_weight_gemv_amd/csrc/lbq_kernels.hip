@@ -135,9 +135,10 @@ __device__ __forceinline__ void wait_stores_complete() { asm volatile("s_waitcnt
 // Split-K epilogue shared by the GEMV kernels: every workgroup of a tile has stored its fp32
 // partial sums (st_coherent); the last one to arrive adds them in super-group order
 // (deterministic), rounds to bf16 and re-arms the tile counter for the next call.
+// Every thread of the workgroup calls it; only those with `owner` set (one per row) finish.
 __device__ __forceinline__ void splitk_finish(const float* partial, unsigned* counter,
                                               uint16_t* y, int n, int np, int supers, int batch,
-                                              int row) {
+                                              int row, bool owner = true) {
   __shared__ unsigned s_last;
   wait_stores_complete();
   __syncthreads();
@@ -146,11 +147,29 @@ __device__ __forceinline__ void splitk_finish(const float* partial, unsigned* co
     s_last = (prev == (unsigned)supers - 1u) ? 1u : 0u;
   }
   __syncthreads();
-  if (!s_last) return;
-  for (int b = 0; b < batch; ++b) {
-    float sum = 0.f;
-    for (int j = 0; j < supers; ++j) sum += ld_coherent(&partial[((size_t)b * supers + j) * np + row]);
-    if (row < n) y[(size_t)b * n + row] = f32_to_bf16(sum);
+  if (!s_last || !owner) return;
+  // partial (b, j) sits at index b * supers + j; they are loaded 16 at a time (one round trip
+  // per 16, not per partial) and added in that index order, so each row's sum runs over j in order
+  const int total = batch * supers;
+  float sum = 0.f;
+  int b = 0, j = 0;
+  for (int t0 = 0; t0 < total; t0 += 16) {
+    float t[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      t[u] = t0 + u < total ? ld_coherent(&partial[(size_t)(t0 + u) * np + row]) : 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      if (t0 + u < total) {
+        sum += t[u];
+        if (++j == supers) {
+          if (row < n) y[(size_t)b * n + row] = f32_to_bf16(sum);
+          sum = 0.f;
+          j = 0;
+          ++b;
+        }
+      }
+    }
   }
   if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -465,6 +484,201 @@ __global__ __launch_bounds__(256) void rms_kernel(const uint16_t* __restrict__ y
 }
 
 // ---------------------------------------------------------------------------------------------
+// INT4 weights x int8 activations with integer dot products.
+//
+// Activations are quantized per row and per 128-group: d = max|x| / 127 and q = rint(x / d),
+// both fp32 operations rounded to nearest even (the same decision the CPU oracle takes), q
+// clamped to +-127, an all-zero group giving d = 0 and q = 0. A group's dot product is then an
+// exact integer sum, 4 products per v_dot4_i32_i8.
+//
+// The weights stay in the INT4 device layout (offset-binary nibbles, even codes in the low
+// half-word). For a dword d of eight codes, ((d << 4) & 0xF0F0F0F0) ^ 0x80808080 holds codes
+// 0, 4, 1, 5 and (d & 0xF0F0F0F0) ^ 0x80808080 codes 2, 6, 3, 7 as signed bytes 16 q (a nibble
+// n = q + 8 in the top half of a byte, its top bit flipped, is the byte 16 q), so the integer
+// sums come out 16 times too large, exactly. The activation codes are stored in LDS in that
+// byte order.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max64(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+// Quantizes the 128-group whose 128 bf16 values lane l holds two of (positions 2l, 2l + 1):
+// returns the two codes and the group scale.
+__device__ __forceinline__ float quant_group(uint32_t pair, int& q0, int& q1) {
+  const float x0 = bf16_lo(pair), x1 = bf16_hi(pair);
+  const float a = wave_max64(fmaxf(fabsf(x0), fabsf(x1)));
+  const float d = a / 127.0f;
+  q0 = q1 = 0;
+  if (d != 0.0f) {
+    q0 = (int)fminf(fmaxf(__builtin_rintf(x0 / d), -127.0f), 127.0f);
+    q1 = (int)fminf(fmaxf(__builtin_rintf(x1 / d), -127.0f), 127.0f);
+  }
+  return d;
+}
+
+// One wave per (row b, group g): codes to q[b][k], scale to d[b][k / 128].
+__global__ __launch_bounds__(64) void quant_act_kernel(const uint16_t* __restrict__ x,
+                                                       int8_t* __restrict__ q,
+                                                       float* __restrict__ dsc, int k) {
+  const int g = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const size_t base = (size_t)b * k + (size_t)g * kGroup;
+  const uint32_t pair = *(const uint32_t*)(x + base + 2 * lane);
+  int q0, q1;
+  const float d = quant_group(pair, q0, q1);
+  *(uint16_t*)(q + base + 2 * lane) = (uint16_t)((q0 & 0xFF) | ((q1 & 0xFF) << 8));
+  if (lane == 0) dsc[(size_t)b * (k / kGroup) + g] = d;
+}
+
+__device__ __forceinline__ int clamp_code(float v) {
+  return (int)fminf(fmaxf(__builtin_rintf(v), -127.0f), 127.0f);
+}
+
+// Quantizes eight consecutive values x[8p .. 8p + 7] of a group held by one of the 16 lanes that
+// share it (lanes 16c .. 16c + 15 of a wave hold one group, piece p = lane % 16). Returns the
+// group scale; `codes` receives the eight codes as bytes in weight order 0, 4, 1, 5 | 2, 6, 3, 7.
+__device__ __forceinline__ float quant_piece(const uint32_t (&xv)[4], uint2& codes) {
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[2 * i] = bf16_lo(xv[i]); v[2 * i + 1] = bf16_hi(xv[i]); }
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
+  const float d = a / 127.0f;
+  int c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = d != 0.0f ? clamp_code(v[i] / d) : 0;
+  codes.x = (c[0] & 0xFF) | ((c[4] & 0xFF) << 8) | ((c[1] & 0xFF) << 16) | ((uint32_t)(c[5] & 0xFF) << 24);
+  codes.y = (c[2] & 0xFF) | ((c[6] & 0xFF) << 8) | ((c[3] & 0xFF) << 16) | ((uint32_t)(c[7] & 0xFF) << 24);
+  return d;
+}
+
+// Four waves per (64-row tile, super-group): wave w takes groups 2w and 2w + 1. Every weight
+// load of the workgroup is issued before anything else, then each wave quantizes the activations
+// of its two groups into LDS (two batch rows at a time: lanes 0-15 / 16-31 the two groups of one
+// row, lanes 32-63 the next row), takes the integer sums with dot4, and the four waves' partial
+// sums are added in wave order through LDS.
+constexpr int kI8Waves = 4;
+constexpr int kI8GroupsPerWave = kSuper / kI8Waves;   // 2
+
+template <int NB>
+__global__ __launch_bounds__(64 * kI8Waves) void i4_i8act_gemv_kernel(
+    const uint8_t* __restrict__ w, const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
+    float* __restrict__ partial, unsigned* __restrict__ counters, int n, int k, int np,
+    int groups, int supers, long long tile_bytes, int batch) {
+  __shared__ __attribute__((aligned(16))) uint8_t q8[NB][kSuper][kGroup];   // codes, block order
+  __shared__ float dsm[NB][kSuper];
+  __shared__ float red[kI8Waves][NB][64];
+  const int tile = blockIdx.x, sg = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g0 = sg * kSuper;
+  const int gcount = min(kSuper, groups - g0);
+  const int gw = kI8GroupsPerWave * wave;   // first group of this wave within the super-group
+  const uint8_t* base = w + (size_t)tile * tile_bytes + (size_t)sg * (kBlock * (1 + kSuper * kI4GroupBlocks));
+
+  u32x4 wv[kI8GroupsPerWave][4];
+#pragma unroll
+  for (int i = 0; i < kI8GroupsPerWave; ++i) {
+    if (gw + i < gcount) {
+      const uint8_t* gp = base + kBlock + (size_t)(gw + i) * (kI4GroupBlocks * kBlock) + lane * 16;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) wv[i][m] = ld_stream16(gp + m * kBlock);
+    }
+  }
+  // fp16 scales of groups gw, gw + 1 of this lane's row: one dword of the row's 16-byte record
+  const uint32_t scw = *(const uint32_t*)(base + lane * 16 + 4 * wave);
+  const float scale[2] = {f16_to_f32(scw & 0xFFFF), f16_to_f32(scw >> 16)};
+  const int row = tile * kTileRows + lane;
+  // quantization lane map
+  const int qg = gw + ((lane >> 4) & 1), qpiece = lane & 15, qrow = lane >> 5;
+
+  for (int b0 = 0; b0 < batch; b0 += NB) {
+    const int nb = min(NB, batch - b0);
+    uint32_t xv[(NB + 1) / 2][4];
+#pragma unroll
+    for (int h = 0; h < (NB + 1) / 2; ++h) {
+      const int bb = 2 * h + qrow;
+      if (bb < nb && qg < gcount) {
+        const uint32_t* xp = (const uint32_t*)(x + (size_t)(b0 + bb) * k + (size_t)(g0 + qg) * kGroup + 8 * qpiece);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xv[h][i] = xp[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xv[h][i] = 0u;
+      }
+    }
+    __syncthreads();   // the previous pass has finished reading q8, dsm and red
+#pragma unroll
+    for (int h = 0; h < (NB + 1) / 2; ++h) {
+      const int bb = 2 * h + qrow;
+      uint2 codes;
+      const float d = quant_piece(xv[h], codes);
+      if (bb < nb && qg < gcount) {
+        *(uint2*)&q8[bb][qg][8 * qpiece] = codes;
+        if (qpiece == 0) dsm[bb][qg] = d;
+      }
+    }
+    __syncthreads();
+
+    float acc[NB];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) acc[bb] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kI8GroupsPerWave; ++i) {
+      const int gi = gw + i;
+      if (gi >= gcount) break;
+      int isum[NB];
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) isum[bb] = 0;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t s4[4] = {wv[i][m].x, wv[i][m].y, wv[i][m].z, wv[i][m].w};
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+          const uint32_t dw = s4[ww];
+          const int wlo = (int)(((dw << 4) & 0xF0F0F0F0u) ^ 0x80808080u);
+          const int whi = (int)((dw & 0xF0F0F0F0u) ^ 0x80808080u);
+          const int blk = 4 * m + ww;   // codes 32m + 8ww .. 32m + 8ww + 7 of the group
+#pragma unroll
+          for (int bb = 0; bb < NB; ++bb) {
+            if (bb < nb) {
+              const uint2 qv = *(const uint2*)&q8[bb][gi][8 * blk];
+              isum[bb] = __builtin_amdgcn_sdot4(wlo, (int)qv.x, isum[bb], false);
+              isum[bb] = __builtin_amdgcn_sdot4(whi, (int)qv.y, isum[bb], false);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb)
+        if (bb < nb) acc[bb] = fmaf((float)(isum[bb] >> 4), scale[i] * dsm[bb][gi], acc[bb]);
+    }
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) red[wave][bb][lane] = acc[bb];
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        if (bb < nb) {
+          float sum = red[0][bb][lane];
+#pragma unroll
+          for (int v = 1; v < kI8Waves; ++v) sum += red[v][bb][lane];
+          if (supers == 1) {
+            if (row < n) y[(size_t)(b0 + bb) * n + row] = f32_to_bf16(sum);
+          } else {
+            st_coherent(&partial[((size_t)(b0 + bb) * supers + sg) * np + row], sum);
+          }
+        }
+      }
+    }
+  }
+  if (supers > 1) splitk_finish(partial, counters + tile, y, n, np, supers, batch, row, wave == 0);
+}
+
+// ---------------------------------------------------------------------------------------------
 // device entry points
 // ---------------------------------------------------------------------------------------------
 static lbq_status launch_status() {
@@ -576,6 +790,55 @@ extern "C" lbq_status lbq_gemv_q1g128(const void* d_w, int32_t n, int32_t k, con
 extern "C" lbq_status lbq_gemv_i4g128(const void* d_w, int32_t n, int32_t k, const uint16_t* d_x,
                                       uint16_t* d_y, int32_t batch, void* stream) {
   return gemv_common(Fmt::I4, d_w, n, k, d_x, d_y, batch, stream);
+}
+
+extern "C" lbq_status lbq_quant_act_i8g128(const uint16_t* d_x, int32_t k, int32_t batch,
+                                           int8_t* d_q, float* d_scale, void* stream) {
+  if (k < kGroup || k % kGroup != 0 || k > (1 << 24) || batch < 0 || batch > 65535)
+    return LBQ_E_SHAPE;
+  if (batch == 0) return LBQ_OK;
+  if (!d_x || !d_q || !d_scale) return LBQ_E_NULL;
+  if ((uintptr_t)d_x % 4 || (uintptr_t)d_q % 2 || (uintptr_t)d_scale % 4) return LBQ_E_ALIGN;
+  const size_t xb = (size_t)batch * k * 2, qb = (size_t)batch * k, sb = (size_t)batch * (k / kGroup) * 4;
+  if (overlaps(d_q, qb, d_x, xb) || overlaps(d_scale, sb, d_x, xb) || overlaps(d_scale, sb, d_q, qb))
+    return LBQ_E_ALIAS;
+  hipLaunchKernelGGL(quant_act_kernel, dim3(k / kGroup, batch), dim3(64), 0, (hipStream_t)stream,
+                     d_x, d_q, d_scale, k);
+  return launch_status();
+}
+
+extern "C" lbq_status lbq_gemv_i4g128_act_i8(const void* d_w, int32_t n, int32_t k,
+                                             const uint16_t* d_x, uint16_t* d_y, int32_t batch,
+                                             void* stream) {
+  Geometry g;
+  if (!make_geometry(n, k, kI4GroupBlocks, &g)) return LBQ_E_SHAPE;
+  if (batch < 0 || batch > LBQ_MAX_BATCH) return LBQ_E_SHAPE;
+  if (batch == 0) return LBQ_OK;
+  if (!d_w || !d_x || !d_y) return LBQ_E_NULL;
+  if ((uintptr_t)d_w % 16 || (uintptr_t)d_x % 4 || (uintptr_t)d_y % 4) return LBQ_E_ALIGN;
+  const size_t yb = (size_t)batch * n * 2;
+  if (overlaps(d_y, yb, d_x, (size_t)batch * k * 2) || overlaps(d_y, yb, d_w, layout_bytes(g)))
+    return LBQ_E_ALIAS;
+  hipStream_t s = (hipStream_t)stream;
+  unsigned* counters = nullptr;
+  float* partials = nullptr;
+  if (g.supers > 1) {
+    if (g.tiles * sizeof(unsigned) > kCounterBytes) return LBQ_E_SHAPE;
+    const lbq_status st = get_workspace((size_t)batch * g.supers * g.np * sizeof(float), s,
+                                        &counters, &partials);
+    if (st != LBQ_OK) return st;
+  }
+  const dim3 grid((unsigned)g.tiles, (unsigned)g.supers);
+  const int nbp = batch <= 1 ? 1 : (batch <= 2 ? 2 : (batch <= 4 ? 4 : 8));
+#define LAUNCH_I8(NB)                                                                            \
+  hipLaunchKernelGGL(i4_i8act_gemv_kernel<NB>, grid, dim3(64 * kI8Waves), 0, s,                 \
+                     (const uint8_t*)d_w, d_x,                                                   \
+                     d_y, partials, counters, n, k, (int)g.np, (int)g.groups, (int)g.supers,    \
+                     (long long)g.tile_bytes, batch)
+  if (nbp == 1) LAUNCH_I8(1); else if (nbp == 2) LAUNCH_I8(2);
+  else if (nbp == 4) LAUNCH_I8(4); else LAUNCH_I8(8);
+#undef LAUNCH_I8
+  return launch_status();
 }
 
 extern "C" lbq_status lbq_rms_rescale_bf16(const uint16_t* d_y, const uint16_t* d_y2,
