@@ -32,6 +32,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "q1_engine_decode_64L.md")
+I4_PROFILE = os.path.join(ROOT, "profiles", "i4_layer_gemv.md")
+I4_KERNELS = os.path.join(ROOT, "packed_weight_gemv_amd", "csrc", "lbq_kernels.hip")
 ENGINE_SOURCES = [os.path.join(ROOT, "packed_weight_gemv_amd", "csrc", f)
                   for f in ("lbq_engine.hip", "lbq_engine.h")]
 
@@ -56,6 +58,25 @@ def measured_traffic(layers: int, batch: int):
             elif line.startswith("traffic-bytes-per-launch:"):
                 traffic = int(line.split(":", 1)[1].strip())
     return traffic if sha == h.hexdigest() else None
+
+
+def i4_layer_traffic(key: str):
+    """HBM bytes per layer of the INT4 layer GEMVs (`key` like "i8act-B1") from the committed PMC
+    summary, or None when the kernel sources changed since it was taken."""
+    import hashlib
+    if not os.path.exists(I4_PROFILE):
+        return None
+    with open(I4_KERNELS, "rb") as fh:
+        cur = hashlib.sha256(fh.read()).hexdigest()
+    sha, traffic = None, None
+    with open(I4_PROFILE) as fh:
+        for line in fh:
+            line = line.strip()
+            if line.startswith("kernels-source-sha256:"):
+                sha = line.split(":", 1)[1].strip()
+            elif line.startswith(f"traffic-bytes-per-layer-{key}:"):
+                traffic = int(line.split(":", 1)[1].strip())
+    return traffic if sha == cur else None
 
 
 def log(msg: str) -> None:
@@ -296,10 +317,13 @@ def i4_layer_bench(args, lbq, synth, torch, np, dev) -> int:
     1024x4096; gate, up 12288x4096; down 4096x12288) through lbq_gemv_i4g128 (bf16 activations)
     and lbq_gemv_i4g128_act_i8 (int8 activations quantized in the kernel, integer dot products),
     at B = 1 and 8. Weights rotate through a pool of at least 1 GiB of copies so that every call
-    streams them from HBM; the time per layer is the sum of the projections' HIP-event times on
-    the launch stream (`steps` calls each after `warmup`). Algorithmic bytes: the packed weights
-    (33/64 B per weight) plus bf16 activations in and out."""
+    streams them from HBM. Each projection's calls are captured in one HIP graph (64 or more
+    launches) so that host launch cost stays out of the figure; the graph is replayed `steps`
+    times between HIP events on the replay stream, and the time per layer is the sum of the
+    projections' times per call. Algorithmic bytes: the packed weights (33/64 B per weight) plus
+    bf16 activations in and out."""
     stream = torch.cuda.current_stream()
+    cap = torch.cuda.Stream()
     paths = (("bf16", lbq.lbq_gemv_i4g128), ("i8act", lbq.lbq_gemv_i4g128_act_i8))
     layer = {(p, b): [0.0, 0] for p, _ in paths for b in (1, 8)}
     cases = []
@@ -315,23 +339,28 @@ def i4_layer_bench(args, lbq, synth, torch, np, dev) -> int:
             y = torch.empty((batch, n), dtype=torch.int16, device=dev)
             nbytes = packed.nbytes + 2 * batch * (n + k)
             for pname, fn in paths:
-                it = [0]
-
-                def call():
-                    fn(pool[it[0] % len(pool)], n, k, x, y, stream=stream)
-                    it[0] += 1
-
-                for _ in range(max(1, args.warmup)):
-                    call()
+                # eager warm-up on the capture stream (creates the split-K workspace), then one
+                # graph of `calls` launches rotating through the pool
+                calls = len(pool) * max(1, 64 // len(pool))
+                with torch.cuda.stream(cap):
+                    for i in range(max(len(pool), args.warmup)):
+                        fn(pool[i % len(pool)], n, k, x, y, stream=cap)
+                torch.cuda.synchronize()
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph, stream=cap):
+                    for i in range(calls):
+                        fn(pool[i % len(pool)], n, k, x, y, stream=cap)
+                graph.replay()
                 torch.cuda.synchronize()
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
                 for _ in range(args.steps):
-                    call()
+                    graph.replay()
                 e1.record(stream)
                 torch.cuda.synchronize()
-                us = e0.elapsed_time(e1) * 1e3 / args.steps
+                del graph
+                us = e0.elapsed_time(e1) * 1e3 / (args.steps * calls)
                 layer[(pname, batch)][0] += us
                 layer[(pname, batch)][1] += nbytes
                 cases.append({"path": pname, "proj": name, "n": n, "k": k, "batch": batch,
@@ -372,8 +401,12 @@ def i4_layer_bench(args, lbq, synth, torch, np, dev) -> int:
                                "activations; bf16 path and B = 8 in cases",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "i4_i8act_gemv_kernel<1>"},
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": i4_layer_traffic("i8act-B1"),
+                     "traffic_unit": "HBM bytes per layer (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                     "copy-scaled)",
+                     "bytes_per_layer": head_bytes,
+                     "kernel": "i4_i8act_gemv_kernel<1> (7 launches per layer)"},
         "cpu_baseline": {"value": round(sampled / dt / 1e9, 5), "unit": "GB/s", "cores": 1,
                          "kind": "oracle",
                          "sample": "quantize + 512 output rows of each of the 7 projections, B = 1"},

@@ -279,49 +279,109 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8))) void
 // ---------------------------------------------------------------------------------------------
 // INT4 g128 GEMV.
 //
-// One wave per (64-row tile, super-group). x of the super-group sits in LDS as bf16 and is read
-// by broadcast. Codes are stored offset-binary (n = q + 8); two codes at a time are placed in
-// the top four mantissa bits of a pair of bf16 ones, giving 1 + n/16, and multiplied into the
-// matching x pair with one dot2: sum (1 + n/16) x = S + sum(n x)/16, so per group
-// sum q x = 16 * acc - 24 * S with S the group's sum of x (kept in LDS).
+// Four waves per (64-row tile, super-group of eight groups); wave w takes groups 2w and 2w + 1,
+// one row per lane. Every weight load of the workgroup is issued first (one HBM round trip),
+// then each wave stages the activations of its own two groups in LDS, where they are read by
+// broadcast, and the four waves' partial sums are added in wave order through LDS.
+//
+// Codes are stored offset-binary (n = q + 8); two codes at a time are placed in the top four
+// mantissa bits of a pair of bf16 ones, giving 1 + n/16, and multiplied into the matching x
+// pair with one dot2: sum (1 + n/16) x = S + sum(n x)/16, so per group sum q x = 16 acc - 24 S
+// with S the group's sum of x.
 // ---------------------------------------------------------------------------------------------
+constexpr int kI4Waves = 4;
+constexpr int kI4GroupsPerWave = kSuper / kI4Waves;   // 2
+
+// The 16-byte records of groups gw, gw + 1 (those below gcount) of this lane's row.
+__device__ __forceinline__ void i4_load_wave_groups(const uint8_t* base, int gw, int gcount,
+                                                    int lane, u32x4 (&wv)[kI4GroupsPerWave][4]) {
+#pragma unroll
+  for (int i = 0; i < kI4GroupsPerWave; ++i) {
+    if (gw + i < gcount) {
+      const uint8_t* gp = base + kBlock + (size_t)(gw + i) * (kI4GroupBlocks * kBlock) + lane * 16;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) wv[i][m] = ld_stream16(gp + m * kBlock);
+    }
+  }
+}
+
+// Adds the waves' per-row sums (red[wave][bb][lane], written by every wave before the barrier)
+// in wave order and stores them: bf16 outputs when the tile has one super-group, fp32 partials
+// for the split-K finish otherwise. Called by every thread; wave 0 stores.
+template <int NB, int W>
+__device__ __forceinline__ void store_wave_sums(const float (&red)[W][NB][64], int wave, int lane,
+                                                int nb, int b0, int sg, int supers, int row,
+                                                int n, int np, uint16_t* y, float* partial) {
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+    if (bb < nb) {
+      float sum = red[0][bb][lane];
+#pragma unroll
+      for (int v = 1; v < W; ++v) sum += red[v][bb][lane];
+      if (supers == 1) {
+        if (row < n) y[(size_t)(b0 + bb) * n + row] = f32_to_bf16(sum);
+      } else {
+        st_coherent(&partial[((size_t)(b0 + bb) * supers + sg) * np + row], sum);
+      }
+    }
+  }
+}
+
 template <int NB>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8))) void i4_gemv_kernel(
+__global__ __launch_bounds__(64 * kI4Waves) void i4_gemv_kernel(
     const uint8_t* __restrict__ w, const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
     float* __restrict__ partial, unsigned* __restrict__ counters, int n, int k, int np,
     int groups, int supers, long long tile_bytes, int batch) {
-  __shared__ __attribute__((aligned(16))) uint32_t xs[NB][kSuper * kGroup / 2];  // bf16 pairs
+  __shared__ __attribute__((aligned(16))) uint32_t xs[NB][kSuper][kGroup / 2];   // bf16 pairs
   __shared__ float gsum[NB][kSuper];
-  const int tile = blockIdx.x, sg = blockIdx.y, lane = threadIdx.x;
+  __shared__ float red[kI4Waves][NB][64];
+  const int tile = blockIdx.x, sg = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g0 = sg * kSuper;
   const int gcount = min(kSuper, groups - g0);
+  const int gw = kI4GroupsPerWave * wave;
   const uint8_t* base = w + (size_t)tile * tile_bytes + (size_t)sg * (kBlock * (1 + kSuper * kI4GroupBlocks));
-  const u32x4 sc = *(const u32x4*)(base + lane * 16);
-  float scale[kSuper];
-  scale[0] = f16_to_f32(sc.x & 0xFFFF); scale[1] = f16_to_f32(sc.x >> 16);
-  scale[2] = f16_to_f32(sc.y & 0xFFFF); scale[3] = f16_to_f32(sc.y >> 16);
-  scale[4] = f16_to_f32(sc.z & 0xFFFF); scale[5] = f16_to_f32(sc.z >> 16);
-  scale[6] = f16_to_f32(sc.w & 0xFFFF); scale[7] = f16_to_f32(sc.w >> 16);
+  u32x4 wv[kI4GroupsPerWave][4];
+  i4_load_wave_groups(base, gw, gcount, lane, wv);
+  const uint32_t scw = *(const uint32_t*)(base + lane * 16 + 4 * wave);
+  const float scale[2] = {f16_to_f32(scw & 0xFFFF), f16_to_f32(scw >> 16)};
   const int row = tile * kTileRows + lane;
+  // staging lane map: lanes 0-15 / 16-31 hold 8 values each of groups gw / gw + 1 of one batch
+  // row, lanes 32-63 the same for the next batch row
+  const int qg = gw + ((lane >> 4) & 1), qpiece = lane & 15, qrow = lane >> 5;
 
   for (int b0 = 0; b0 < batch; b0 += NB) {
     const int nb = min(NB, batch - b0);
-    __syncthreads();
-    // stage x pairs of this super-group and the per-group sums
-    for (int bb = 0; bb < nb; ++bb) {
-      const uint32_t* xp = (const uint32_t*)(x + (size_t)(b0 + bb) * k + kGroup * g0);
-      for (int p = lane; p < gcount * kGroup / 2; p += 64) xs[bb][p] = xp[p];
+    uint32_t xv[(NB + 1) / 2][4];
+#pragma unroll
+    for (int h = 0; h < (NB + 1) / 2; ++h) {
+      const int bb = 2 * h + qrow;
+      if (bb < nb && qg < gcount) {
+        const uint32_t* xp = (const uint32_t*)(x + (size_t)(b0 + bb) * k + (size_t)(g0 + qg) * kGroup + 8 * qpiece);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xv[h][i] = xp[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xv[h][i] = 0u;
+      }
     }
-    __syncthreads();
-    if (lane < nb * kSuper) {
-      const int bb = lane / kSuper, i = lane % kSuper;
-      float s = 0.f;
-      if (i < gcount)
-        for (int p = 0; p < kGroup / 2; ++p) {
-          const uint32_t v = xs[bb][i * (kGroup / 2) + p];
-          s += bf16_lo(v) + bf16_hi(v);
-        }
-      gsum[bb][i] = s;
+    __syncthreads();   // the previous pass has finished reading xs, gsum and red
+#pragma unroll
+    for (int h = 0; h < (NB + 1) / 2; ++h) {
+      const int bb = 2 * h + qrow;
+      float sx = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sx += bf16_lo(xv[h][i]) + bf16_hi(xv[h][i]);
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) sx += __shfl_xor(sx, off);
+      if (bb < nb && qg < gcount) {
+        u32x4 v;
+        v.x = xv[h][0]; v.y = xv[h][1]; v.z = xv[h][2]; v.w = xv[h][3];
+        *(u32x4*)&xs[bb][qg][4 * qpiece] = v;
+        if (qpiece == 0) gsum[bb][qg] = sx;
+      }
     }
     __syncthreads();
 
@@ -329,18 +389,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8))) void
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) acc[bb] = 0.f;
 #pragma unroll
-    for (int i = 0; i < kSuper; ++i) {
-      if (i >= gcount) break;
-      const uint8_t* gp = base + kBlock + (size_t)i * (kI4GroupBlocks * kBlock) + lane * 16;
-      u32x4 wv[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) wv[m] = ld_stream16(gp + m * kBlock);
+    for (int i = 0; i < kI4GroupsPerWave; ++i) {
+      const int gi = gw + i;
+      if (gi >= gcount) break;
       float ga[NB];
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb) ga[bb] = 0.f;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const uint32_t s4[4] = {wv[m].x, wv[m].y, wv[m].z, wv[m].w};
+        const uint32_t s4[4] = {wv[i][m].x, wv[i][m].y, wv[i][m].z, wv[i][m].w};
 #pragma unroll
         for (int ww = 0; ww < 4; ++ww) {
           const uint32_t s = s4[ww];
@@ -351,37 +408,26 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8))) void
 #pragma unroll
           for (int bb = 0; bb < NB; ++bb) {
             if (bb < nb) {
-              const u32x4 xv = *(const u32x4*)&xs[bb][i * (kGroup / 2) + 16 * m + 4 * ww];
+              const u32x4 xq = *(const u32x4*)&xs[bb][gi][16 * m + 4 * ww];
               float a = ga[bb];
-              a = dot2_bf16(t0, xv.x, a);
-              a = dot2_bf16(t1, xv.y, a);
-              a = dot2_bf16(t2, xv.z, a);
-              a = dot2_bf16(t3, xv.w, a);
+              a = dot2_bf16(t0, xq.x, a);
+              a = dot2_bf16(t1, xq.y, a);
+              a = dot2_bf16(t2, xq.z, a);
+              a = dot2_bf16(t3, xq.w, a);
               ga[bb] = a;
             }
           }
         }
       }
 #pragma unroll
-      for (int bb = 0; bb < NB; ++bb) {
-        if (bb < nb) {
-          const float sx = gsum[bb][i];
-          acc[bb] = fmaf(scale[i], fmaf(16.f, ga[bb], -24.f * sx), acc[bb]);
-        }
-      }
+      for (int bb = 0; bb < NB; ++bb)
+        if (bb < nb) acc[bb] = fmaf(scale[i], fmaf(16.f, ga[bb], -24.f * gsum[bb][gi]), acc[bb]);
     }
 #pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-      if (bb < nb) {
-        if (supers == 1) {
-          if (row < n) y[(size_t)(b0 + bb) * n + row] = f32_to_bf16(acc[bb]);
-        } else {
-          st_coherent(&partial[((size_t)(b0 + bb) * supers + sg) * np + row], acc[bb]);
-        }
-      }
-    }
+    for (int bb = 0; bb < NB; ++bb) red[wave][bb][lane] = acc[bb];
+    store_wave_sums<NB, kI4Waves>(red, wave, lane, nb, b0, sg, supers, row, n, np, y, partial);
   }
-  if (supers > 1) splitk_finish(partial, counters + tile, y, n, np, supers, batch, row);
+  if (supers > 1) splitk_finish(partial, counters + tile, y, n, np, supers, batch, row, wave == 0);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -561,33 +607,23 @@ __device__ __forceinline__ float quant_piece(const uint32_t (&xv)[4], uint2& cod
 // of its two groups into LDS (two batch rows at a time: lanes 0-15 / 16-31 the two groups of one
 // row, lanes 32-63 the next row), takes the integer sums with dot4, and the four waves' partial
 // sums are added in wave order through LDS.
-constexpr int kI8Waves = 4;
-constexpr int kI8GroupsPerWave = kSuper / kI8Waves;   // 2
-
 template <int NB>
-__global__ __launch_bounds__(64 * kI8Waves) void i4_i8act_gemv_kernel(
+__global__ __launch_bounds__(64 * kI4Waves) void i4_i8act_gemv_kernel(
     const uint8_t* __restrict__ w, const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
     float* __restrict__ partial, unsigned* __restrict__ counters, int n, int k, int np,
     int groups, int supers, long long tile_bytes, int batch) {
   __shared__ __attribute__((aligned(16))) uint8_t q8[NB][kSuper][kGroup];   // codes, block order
   __shared__ float dsm[NB][kSuper];
-  __shared__ float red[kI8Waves][NB][64];
+  __shared__ float red[kI4Waves][NB][64];
   const int tile = blockIdx.x, sg = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g0 = sg * kSuper;
   const int gcount = min(kSuper, groups - g0);
-  const int gw = kI8GroupsPerWave * wave;   // first group of this wave within the super-group
+  const int gw = kI4GroupsPerWave * wave;   // first group of this wave within the super-group
   const uint8_t* base = w + (size_t)tile * tile_bytes + (size_t)sg * (kBlock * (1 + kSuper * kI4GroupBlocks));
 
-  u32x4 wv[kI8GroupsPerWave][4];
-#pragma unroll
-  for (int i = 0; i < kI8GroupsPerWave; ++i) {
-    if (gw + i < gcount) {
-      const uint8_t* gp = base + kBlock + (size_t)(gw + i) * (kI4GroupBlocks * kBlock) + lane * 16;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) wv[i][m] = ld_stream16(gp + m * kBlock);
-    }
-  }
+  u32x4 wv[kI4GroupsPerWave][4];
+  i4_load_wave_groups(base, gw, gcount, lane, wv);
   // fp16 scales of groups gw, gw + 1 of this lane's row: one dword of the row's 16-byte record
   const uint32_t scw = *(const uint32_t*)(base + lane * 16 + 4 * wave);
   const float scale[2] = {f16_to_f32(scw & 0xFFFF), f16_to_f32(scw >> 16)};
@@ -627,7 +663,7 @@ __global__ __launch_bounds__(64 * kI8Waves) void i4_i8act_gemv_kernel(
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) acc[bb] = 0.f;
 #pragma unroll
-    for (int i = 0; i < kI8GroupsPerWave; ++i) {
+    for (int i = 0; i < kI4GroupsPerWave; ++i) {
       const int gi = gw + i;
       if (gi >= gcount) break;
       int isum[NB];
@@ -658,22 +694,7 @@ __global__ __launch_bounds__(64 * kI8Waves) void i4_i8act_gemv_kernel(
     }
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) red[wave][bb][lane] = acc[bb];
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-      for (int bb = 0; bb < NB; ++bb) {
-        if (bb < nb) {
-          float sum = red[0][bb][lane];
-#pragma unroll
-          for (int v = 1; v < kI8Waves; ++v) sum += red[v][bb][lane];
-          if (supers == 1) {
-            if (row < n) y[(size_t)(b0 + bb) * n + row] = f32_to_bf16(sum);
-          } else {
-            st_coherent(&partial[((size_t)(b0 + bb) * supers + sg) * np + row], sum);
-          }
-        }
-      }
-    }
+    store_wave_sums<NB, kI4Waves>(red, wave, lane, nb, b0, sg, supers, row, n, np, y, partial);
   }
   if (supers > 1) splitk_finish(partial, counters + tile, y, n, np, supers, batch, row, wave == 0);
 }
@@ -773,7 +794,8 @@ static lbq_status gemv_common(Fmt fmt, const void* d_w, int32_t n, int32_t k,
 #undef LAUNCH_Q1
   } else {
 #define LAUNCH_I4(NB)                                                                            \
-  hipLaunchKernelGGL(i4_gemv_kernel<NB>, grid, dim3(64), 0, s, (const uint8_t*)d_w, d_x, d_y,   \
+  hipLaunchKernelGGL(i4_gemv_kernel<NB>, grid, dim3(64 * kI4Waves), 0, s, (const uint8_t*)d_w,    \
+                     d_x, d_y,                                                                   \
                      partials, counters, n, k, (int)g.np, (int)g.groups, (int)g.supers,         \
                      (long long)g.tile_bytes, batch)
     if (nbp == 1) LAUNCH_I4(1); else if (nbp == 2) LAUNCH_I4(2); else LAUNCH_I4(4);
@@ -831,7 +853,7 @@ extern "C" lbq_status lbq_gemv_i4g128_act_i8(const void* d_w, int32_t n, int32_t
   const dim3 grid((unsigned)g.tiles, (unsigned)g.supers);
   const int nbp = batch <= 1 ? 1 : (batch <= 2 ? 2 : (batch <= 4 ? 4 : 8));
 #define LAUNCH_I8(NB)                                                                            \
-  hipLaunchKernelGGL(i4_i8act_gemv_kernel<NB>, grid, dim3(64 * kI8Waves), 0, s,                 \
+  hipLaunchKernelGGL(i4_i8act_gemv_kernel<NB>, grid, dim3(64 * kI4Waves), 0, s,                 \
                      (const uint8_t*)d_w, d_x,                                                   \
                      d_y, partials, counters, n, k, (int)g.np, (int)g.groups, (int)g.supers,    \
                      (long long)g.tile_bytes, batch)
