@@ -68,6 +68,14 @@ def _load():
     lib.oracle_rms_rescale.restype = None
     lib.oracle_round_bf16.argtypes = [P, ctypes.c_size_t, P]
     lib.oracle_round_bf16.restype = None
+    lib.oracle_fnv1a32.argtypes = [P, i32]
+    lib.oracle_fnv1a32.restype = ctypes.c_uint32
+    lib.oracle_z80_normalize.argtypes = [ctypes.c_uint8]
+    lib.oracle_z80_normalize.restype = ctypes.c_uint8
+    lib.oracle_z80_encode.argtypes = [P, i32, P]
+    lib.oracle_z80_encode.restype = None
+    lib.oracle_z80_chat.argtypes = [P, P, i32, P, P, i32, i32, i32, P, P]
+    lib.oracle_z80_chat.restype = i32
     _lib = lib
     return lib
 
@@ -252,6 +260,55 @@ def rms_rescale(y, y2=None, eps: float = 1e-6):
     ex = np.zeros((B, n), dtype=np.float64)
     lib.oracle_rms_rescale(_ptr(ya), y2p, n, B, float(eps), _ptr(out), _ptr(ex))
     return out, ex
+
+
+# ----------------------------------------------------------------------------------------
+# Z80-uLM character loop (readings of the open points are in oracle/lbq_oracle.c)
+# ----------------------------------------------------------------------------------------
+
+Z80_CHARSET = b"\0 ABCDEFGHIJKLMNOPQRSTUVWXYZ0123456789?!"
+
+
+def fnv1a32(data: bytes) -> int:
+    buf = np.frombuffer(bytes(data) or b"\0", dtype=np.uint8).copy()
+    return int(_load().oracle_fnv1a32(_ptr(buf), len(data)))
+
+
+def z80_normalize(c: int) -> int:
+    return int(_load().oracle_z80_normalize(c))
+
+
+def z80_encode(text: bytes) -> np.ndarray:
+    """128 trigram buckets (int16) of a text."""
+    buf = np.frombuffer(bytes(text) or b"\0", dtype=np.uint8).copy()
+    out = np.zeros(128, dtype=np.int16)
+    _load().oracle_z80_encode(_ptr(buf), len(text), _ptr(out))
+    return out
+
+
+def z80_chat(layer_codes, dims, prompts, max_reply: int):
+    """Generates a reply per prompt (list of bytes). Returns (replies: list of bytes,
+    reply bytes uint8 [B][max_reply] zero-padded, lengths int32 [B])."""
+    lib = _load()
+    L = len(layer_codes)
+    dims_a = _c(dims, np.int32)
+    codes = [_c(c, np.uint8) for c in layer_codes]
+    ptrs = (ctypes.c_void_p * L)(*[_ptr(c) for c in codes])
+    B = len(prompts)
+    stride = max(1, max((len(p) for p in prompts), default=1))
+    pr = np.zeros((B, stride), dtype=np.uint8)
+    lens = np.zeros(B, dtype=np.int32)
+    for b, p in enumerate(prompts):
+        pr[b, :len(p)] = np.frombuffer(bytes(p), dtype=np.uint8)
+        lens[b] = len(p)
+    rep = np.zeros((B, max(1, max_reply)), dtype=np.uint8)
+    rl = np.zeros(B, dtype=np.int32)
+    rc = lib.oracle_z80_chat(ctypes.cast(ptrs, ctypes.c_void_p), _ptr(dims_a), L, _ptr(pr),
+                             _ptr(lens), stride, B, max_reply, _ptr(rep), _ptr(rl))
+    if rc != 0:
+        raise ValueError("oracle_z80_chat: bad shape")
+    rep = rep[:, :max_reply]
+    return [bytes(rep[b, :rl[b]]) for b in range(B)], rep, rl
 
 
 def argmax_lowest(logits) -> np.ndarray:

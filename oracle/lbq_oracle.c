@@ -142,6 +142,99 @@ int oracle_mlp_2bit(const uint8_t* const* layer_codes, const int32_t* dims, int 
 }
 
 /* ---------------------------------------------------------------------------------------
+ * Z80-uLM character loop (Z80-uLM page: the trigram-hash encoding of the input into 128
+ * buckets, typo-tolerant and word-order invariant; 128 query buckets + 128 context buckets
+ * in; one output neuron per charset character; characters generated one at a time).
+ *
+ * The page fixes none of the hash, the charset, the bucket increment, the context rule or the
+ * stop rule; the readings used here:
+ *  - charset of 40: index 0 = end of reply, 1 = space, 2..27 = 'A'..'Z', 28..37 = '0'..'9',
+ *    38 = '?', 39 = '!';
+ *  - input bytes: 'a'..'z' upper-cased, other charset characters kept, every other byte a
+ *    space (a word separator);
+ *  - one trigram per non-space character: (previous, itself, next), with a space standing in
+ *    beyond either end of the text, so a word of L letters gives L trigrams padded by spaces;
+ *  - bucket = FNV-1a (32-bit) of the trigram's three bytes, modulo 128; each trigram adds 32
+ *    to its bucket, the value saturating at 32767;
+ *  - context buckets = the same encoding of the reply generated so far;
+ *  - each step: logits = MLP([query | context]); c = argmax (lowest index among ties);
+ *    c == 0 ends the reply, otherwise charset[c] is appended; at most max_reply characters.
+ * ------------------------------------------------------------------------------------- */
+
+/* FNV-1a, 32-bit, from its published definition: start from the offset basis 2166136261; for
+ * each byte, xor it in, then multiply by the FNV prime 16777619 modulo 2^32. */
+uint32_t oracle_fnv1a32(const uint8_t* bytes, int n) {
+  uint32_t h = 2166136261u;
+  for (int i = 0; i < n; ++i) {
+    h ^= bytes[i];
+    h *= 16777619u;
+  }
+  return h;
+}
+
+static const char z80_charset[40] = {
+    0,   ' ', 'A', 'B', 'C', 'D', 'E', 'F', 'G', 'H', 'I', 'J', 'K', 'L',
+    'M', 'N', 'O', 'P', 'Q', 'R', 'S', 'T', 'U', 'V', 'W', 'X', 'Y', 'Z',
+    '0', '1', '2', '3', '4', '5', '6', '7', '8', '9', '?', '!'};
+
+uint8_t oracle_z80_normalize(uint8_t c) {
+  if (c >= 'a' && c <= 'z') c = (uint8_t)(c - 'a' + 'A');
+  for (int i = 1; i < 40; ++i)
+    if ((uint8_t)z80_charset[i] == c) return c;
+  return ' ';
+}
+
+/* buckets: int16 [128]. */
+void oracle_z80_encode(const uint8_t* text, int n, int16_t* buckets) {
+  int count[128];
+  for (int i = 0; i < 128; ++i) count[i] = 0;
+  for (int i = 0; i < n; ++i) {
+    uint8_t mid = oracle_z80_normalize(text[i]);
+    if (mid == ' ') continue;
+    uint8_t tri[3];
+    tri[0] = i > 0 ? oracle_z80_normalize(text[i - 1]) : ' ';
+    tri[1] = mid;
+    tri[2] = i + 1 < n ? oracle_z80_normalize(text[i + 1]) : ' ';
+    count[oracle_fnv1a32(tri, 3) % 128] += 1;
+  }
+  for (int i = 0; i < 128; ++i) {
+    long v = 32L * count[i];
+    buckets[i] = (int16_t)(v > 32767 ? 32767 : v);
+  }
+}
+
+/* prompts: [batch][stride] bytes, the first prompt_len[b] of row b used. reply: [batch]
+ * [max_reply] ASCII characters, zero after the end; reply_len: [batch]. Layer dims must be
+ * 256 in (128 + 128) and 40 out. Returns 0, or -1 on a bad shape. */
+int oracle_z80_chat(const uint8_t* const* layer_codes, const int32_t* dims, int n_layers,
+                    const uint8_t* prompts, const int32_t* prompt_len, int stride, int batch,
+                    int max_reply, uint8_t* reply, int32_t* reply_len) {
+  if (n_layers < 1 || dims[0] != 256 || dims[n_layers] != 40 || max_reply < 0) return -1;
+  int16_t input[256];
+  int16_t logits[40];
+  uint8_t* text = (uint8_t*)malloc((size_t)(max_reply > 0 ? max_reply : 1));
+  if (!text) return -1;
+  for (int b = 0; b < batch; ++b) {
+    oracle_z80_encode(prompts + (size_t)b * stride, prompt_len[b], input);
+    int len = 0;
+    for (int t = 0; t < max_reply; ++t) {
+      oracle_z80_encode(text, len, input + 128);
+      int32_t c = 0;
+      if (oracle_mlp_2bit(layer_codes, dims, n_layers, input, 1, logits, &c) != 0) {
+        free(text);
+        return -1;
+      }
+      if (c == 0) break;
+      text[len++] = (uint8_t)z80_charset[c];
+    }
+    for (int t = 0; t < max_reply; ++t) reply[(size_t)b * max_reply + t] = t < len ? text[t] : 0;
+    reply_len[b] = len;
+  }
+  free(text);
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------------------
  * Q1_0_g128 GEMV (Bonsai digest, "technical architecture highlights": one sign bit per
  * weight, -1 or +1; one FP16 scale per 128 weights). Sign map bit 1 -> +1, bit 0 -> -1; the
  * 128-weight groups run along k inside a row.
