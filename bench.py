@@ -14,7 +14,9 @@ With --gemm the bench times the many-row products on the matrix cores instead (p
 large batch: Q1 MLP and INT4 layer shapes at 32, 128 and 512 activation rows) and reports
 TFLOP/s against the bf16 matrix-core peak. With --i4-layer it times the seven projections of a
 Qwen3-8B-shaped INT4 g128 layer at B = 1 and 8 through the bf16-activation GEMV and the
-int8-activation GEMV (integer dot products) and reports packed-weight GB/s against HBM.
+int8-activation GEMV (integer dot products) and reports packed-weight GB/s against HBM. With
+--z80-chat it times the Z80-uLM character loop (1024 prompts, replies of up to 32 characters,
+one launch) and reports generated characters per second.
 
 Printed: one JSON line on stdout (progress goes to stderr).
 """
@@ -95,6 +97,8 @@ def parse():
                     help="layers of the stream the CPU oracle baseline runs (0 = skip)")
     ap.add_argument("--kernel-steps", type=int, default=3,
                     help="instrumented steps timing each GEMV launch with HIP events")
+    ap.add_argument("--z80-chat", action="store_true",
+                    help="time the Z80-uLM character loop (1024 prompts, replies up to 32) instead")
     ap.add_argument("--i4-layer", action="store_true",
                     help="time the INT4 layer GEMVs (float and int8-activation paths) instead")
     ap.add_argument("--gemm", action="store_true",
@@ -145,6 +149,8 @@ def main() -> int:
         return gemm_bench(args, lbq, synth, torch, np, dev)
     if args.i4_layer:
         return i4_layer_bench(args, lbq, synth, torch, np, dev)
+    if args.z80_chat:
+        return chat_bench(args, lbq, synth, torch, np, dev)
 
     L, B = args.layers, args.batch
     hid, kv, ffn = synth.STREAM_HIDDEN, synth.STREAM_KV, synth.STREAM_FFN
@@ -310,6 +316,76 @@ def main() -> int:
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+
+
+# 2-bit MACs per evaluation of the 256-192-128-40 network
+Z80_MACS_PER_EVAL = 256 * 192 + 192 * 128 + 128 * 40
+# int16 dot2 issue rate of the chip: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz x 2 MACs
+ALU_DOT2_PEAK_TMACS = 256 * 4 * 16 * 2.4e9 * 2 / 1e12
+
+
+def chat_bench(args, lbq, synth, torch, np, dev) -> int:
+    """The Z80-uLM character loop (lbq_z80_chat_2bit): 1024 synthetic prompts of a few words,
+    replies of up to 32 characters, random 2-bit weights of the 256-192-128-40 network. A step
+    is one launch that generates every reply. Characters per second count the characters
+    emitted; evaluations per second count one network evaluation per emitted character plus
+    one per reply that ended before the cap."""
+    layers = synth.mlp2bit_layers()
+    arr, lens = synth.chat_prompts(synth.MLP_BATCH)
+    B, R = arr.shape[0], synth.Z80_REPLY
+    lw = [torch.from_numpy(lbq.lbq_pack_2bit(c)).to(dev) for c in layers]
+    pr = torch.from_numpy(arr).to(dev)
+    ln = torch.from_numpy(lens).to(dev)
+    reply = torch.empty((B, R), dtype=torch.uint8, device=dev)
+    rl = torch.empty((B,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(max(1, args.warmup)):
+        lbq.lbq_z80_chat_2bit(lw, synth.MLP_DIMS, pr, ln, reply, rl, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        lbq.lbq_z80_chat_2bit(lw, synth.MLP_DIMS, pr, ln, reply, rl, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    lengths = rl.cpu().numpy()
+    chars = int(lengths.sum())
+    evals = chars + int((lengths < R).sum())
+    tmacs = evals * Z80_MACS_PER_EVAL / (us * 1e-6) / 1e12
+    log(f"z80 chat: {us:.1f} us per launch, {chars} characters, {evals} evaluations")
+    # the oracle (one host thread) on the first 256 prompts
+    import oracle
+    nb = 256
+    t0 = time.perf_counter()
+    _, _, orl = oracle.z80_chat(layers, list(synth.MLP_DIMS),
+                                [bytes(arr[b, :lens[b]]) for b in range(nb)], R)
+    dt = time.perf_counter() - t0
+    out = {
+        "metric": "Z80-uLM generated characters per second (whole character loop on the GPU)",
+        "value": round(chars / (us * 1e-6), 1),
+        "unit": "chars/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int16 x 2-bit -> int32 (mod 2^16)",
+        "data": "synthetic",
+        "config": {"workload": f"Z80-uLM chat loop, 256-192-128-40 2-bit network, {B} prompts, "
+                               f"replies up to {R} characters",
+                   "parallelism": "single GPU", "characters": chars, "evaluations": evals},
+        "roofline": {"bound": "alu", "achieved": round(tmacs, 3), "peak": ALU_DOT2_PEAK_TMACS,
+                     "unit": "T 2-bit MAC/s (v_dot2_i32_i16 issue rate)",
+                     "frac": round(tmacs / ALU_DOT2_PEAK_TMACS, 4), "traffic": None,
+                     "kernel": "z80_chat_kernel"},
+        "cpu_baseline": {"value": round(float(orl.sum()) / dt, 1), "unit": "chars/s", "cores": 1,
+                         "kind": "oracle", "sample": f"the first {nb} prompts of the workload"},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
 
 
 def i4_layer_bench(args, lbq, synth, torch, np, dev) -> int:

@@ -45,6 +45,7 @@ extern "C" {
 #define LBQ_MAX_GEMM_ROWS 65536
 #define LBQ_MLP_MAX_LAYERS 8
 #define LBQ_MLP_MAX_DIM 1024
+#define LBQ_Z80_MAX_REPLY 256
 
 typedef int32_t lbq_status;
 enum {
@@ -100,6 +101,46 @@ lbq_status lbq_unpack_2bit(const void* src, int32_t n, int32_t k, uint8_t* codes
 lbq_status lbq_mlp_2bit_i16(const void* const* d_layer_w, const int32_t* dims, int32_t n_layers,
                             const int16_t* d_x, int16_t* d_logits, int32_t* d_argmax,
                             int32_t batch, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Z80-uLM character loop (Z80-uLM page: input hashed by trigrams into 128 buckets, tolerant of
+ * typos and word order; 128 query + 128 context buckets in, one output per charset character,
+ * text generated one character at a time). The page leaves the hash, the charset and the
+ * context rule open; the library's reading:
+ *  - normalization: 'a'..'z' -> 'A'..'Z'; 'A'..'Z', '0'..'9', '?', '!' kept; any other byte is
+ *    a space (word separator);
+ *  - every non-space character i contributes the trigram (text[i-1], text[i], text[i+1]) of
+ *    normalized bytes, a space standing in beyond either end; its bucket is FNV-1a-32 of the
+ *    three bytes modulo 128; each trigram adds 32 to its bucket, saturating at 32767;
+ *  - charset (40): 0 = end of reply, 1 = ' ', 2..27 = 'A'..'Z', 28..37 = '0'..'9', 38 = '?',
+ *    39 = '!';
+ *  - step t: input = [buckets(prompt) | buckets(reply[0..t))], the MLP of lbq_mlp_2bit_i16,
+ *    c = argmax (lowest index among ties); c = 0 ends the reply, otherwise charset[c] is
+ *    appended; at most max_reply characters.
+ * ------------------------------------------------------------------------------------------ */
+
+/* Trigram buckets of `batch` texts: d_text uint8 [batch][stride], the first d_len[b] bytes of
+ * row b (lengths are clamped to [0, stride]); d_buckets int16 [batch][128] (output). Requires
+ * stride >= 1, 0 <= batch <= 2^24; d_len 4-byte and d_buckets 2-byte aligned; the output must
+ * not overlap the inputs. */
+lbq_status lbq_z80_encode(const uint8_t* d_text, const int32_t* d_len, int32_t stride,
+                          int32_t batch, int16_t* d_buckets, void* stream);
+
+/* Generates one reply per prompt, all on the device (one launch for the whole loop).
+ *   d_layer_w, dims, n_layers : the 2-bit MLP as for lbq_mlp_2bit_i16, with dims[0] = 256,
+ *               dims[n_layers] = 40, every input width dims[l] (l < n_layers) a multiple of 16,
+ *               layer pointers 4-byte aligned, and all layers together at most 48 KiB
+ *               (LBQ_E_UNSUPPORTED beyond; the Z80-uLM shape 256-192-128-40 takes 19,712 B);
+ *   d_prompts : uint8 [batch][prompt_stride]; d_prompt_len : int32 [batch], clamped to
+ *               [0, prompt_stride];
+ *   d_reply   : uint8 [batch][max_reply] (output): the reply's characters, zero after its end
+ *               (may be NULL when max_reply == 0); d_reply_len : int32 [batch] (output).
+ * Requires 0 <= max_reply <= LBQ_Z80_MAX_REPLY, 0 <= batch <= 2^24, prompt_stride >= 1;
+ * outputs must not overlap the inputs or each other. */
+lbq_status lbq_z80_chat_2bit(const void* const* d_layer_w, const int32_t* dims, int32_t n_layers,
+                             const uint8_t* d_prompts, const int32_t* d_prompt_len,
+                             int32_t prompt_stride, int32_t batch, int32_t max_reply,
+                             uint8_t* d_reply, int32_t* d_reply_len, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Q1_0_g128 (Bonsai digest, "technical architecture highlights").

@@ -21,6 +21,7 @@ LBQ_OK = 0
 STATUS = {0: "LBQ_OK", -1: "LBQ_E_NULL", -2: "LBQ_E_SHAPE", -3: "LBQ_E_ALIGN",
           -4: "LBQ_E_UNSUPPORTED", -5: "LBQ_E_ALIAS", -6: "LBQ_E_DEVICE", -7: "LBQ_E_NOMEM"}
 MAX_BATCH = 16
+Z80_MAX_REPLY = 256
 ACT_SLOTS = ("x", "q", "k", "v", "gate", "up", "xo", "o", "xd", "down")
 
 _lib = None
@@ -64,6 +65,8 @@ def load():
         "lbq_gemm_i4g128": ([P, i32, i32, P, P, i32, P], i32),
         "lbq_quant_act_i8g128": ([P, i32, i32, P, P, P], i32),
         "lbq_gemv_i4g128_act_i8": ([P, i32, i32, P, P, i32, P], i32),
+        "lbq_z80_encode": ([P, P, i32, i32, P, P], i32),
+        "lbq_z80_chat_2bit": ([P, P, i32, P, P, i32, i32, i32, P, P, P], i32),
         "lbq_rms_rescale_bf16": ([P, P, P, i32, i32, ctypes.c_float, P], i32),
         "lbq_decode_act_elems": ([i32, i32, i32, i32, i32], sz),
         "lbq_decode_act_offset": ([i32, i32, i32, i32, i32, i32, i32], i64),
@@ -199,6 +202,26 @@ def lbq_mlp_2bit_i16(layer_w, dims, x, logits, argmax=None, stream=None) -> None
     _check("lbq_mlp_2bit_i16", load().lbq_mlp_2bit_i16(
         ctypes.cast(ptrs, ctypes.c_void_p), ctypes.cast(d, ctypes.c_void_p), L, _dptr(x),
         _dptr(logits), _dptr(argmax), x.shape[0], _stream(stream)))
+
+
+def lbq_z80_encode(text, lengths, buckets, stream=None) -> None:
+    """text: uint8 device tensor [B][stride]; lengths: int32 [B]; buckets: int16 [B][128]."""
+    B, stride = text.shape
+    _check("lbq_z80_encode", load().lbq_z80_encode(_dptr(text), _dptr(lengths), stride, B,
+                                                   _dptr(buckets), _stream(stream)))
+
+
+def lbq_z80_chat_2bit(layer_w, dims, prompts, lengths, reply, reply_len, stream=None) -> None:
+    """layer_w: list of packed 2-bit layers (device); prompts: uint8 [B][stride]; lengths: int32
+    [B]; reply: uint8 [B][max_reply] (output); reply_len: int32 [B] (output)."""
+    L = len(layer_w)
+    ptrs = (ctypes.c_void_p * L)(*[_dptr(w) for w in layer_w])
+    d = (ctypes.c_int32 * (L + 1))(*[int(v) for v in dims])
+    B, stride = prompts.shape
+    _check("lbq_z80_chat_2bit", load().lbq_z80_chat_2bit(
+        ctypes.cast(ptrs, ctypes.c_void_p), ctypes.cast(d, ctypes.c_void_p), L, _dptr(prompts),
+        _dptr(lengths), stride, B, reply.shape[1], _dptr(reply) if reply.numel() else None,
+        _dptr(reply_len), _stream(stream)))
 
 
 def lbq_gemv_q1g128(w, n: int, k: int, x, y, stream=None) -> None:

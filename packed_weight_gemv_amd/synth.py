@@ -24,6 +24,8 @@ KIND_CODES, KIND_SCALES, KIND_ACT, KIND_STRESS = 0, 1, 2, 3
 
 # workload ids
 W_MLP2BIT, W_Q1_SQUARE, W_Q1_MLP, W_I4_LAYER, W_Q1_STREAM = 1, 2, 3, 4, 5
+W_Z80_CHAT = 6
+Z80_REPLY = 32                          # reply cap of the chat-loop workload
 
 MLP_DIMS = (256, 192, 128, 40)          # 128 query + 128 context buckets -> ... -> 40 chars
 MLP_BATCH = 1024
@@ -145,3 +147,31 @@ def stream_bytes_per_layer(hidden=STREAM_HIDDEN, kv=STREAM_KV, ffn=STREAM_FFN) -
         n, k = stream_shape(name, hidden, kv, ffn)
         total += n * k * 9 // 64
     return total
+
+
+def chat_prompts(batch: int, workload: int = W_Z80_CHAT, extra: int = 0, max_words: int = 5,
+                 max_word: int = 8):
+    """Short, varied chat inputs (the Z80-uLM page's regime: a few words): 1..max_words words of
+    1..max_word characters, mostly lower-case letters with some upper case, digits and '?',
+    joined by a space or ", ". Returns (uint8 [batch][stride] zero-padded, int32 lengths)."""
+    r = rng(workload, 0, 0, KIND_ACT, extra)
+    pool = np.frombuffer(b"abcdefghijklmnopqrstuvwxyz" * 3 + b"ABCDEFGHIJKLMNOPQRSTUVWXYZ"
+                         + b"0123456789?", dtype=np.uint8)
+    texts = []
+    for _ in range(batch):
+        words = []
+        for _ in range(int(r.integers(1, max_words + 1))):
+            words.append(bytes(pool[r.integers(0, pool.size, size=int(r.integers(1, max_word + 1)))]))
+        sep = [b" ", b", "]
+        t = words[0]
+        for w in words[1:]:
+            t += sep[int(r.integers(0, 2))] + w
+        texts.append(t)
+    stride = max(1, max(len(t) for t in texts))
+    arr = np.zeros((batch, stride), dtype=np.uint8)
+    lens = np.zeros(batch, dtype=np.int32)
+    for b, t in enumerate(texts):
+        arr[b, :len(t)] = np.frombuffer(t, dtype=np.uint8)
+        lens[b] = len(t)
+    return arr, lens
+
