@@ -68,6 +68,8 @@ def _load():
     lib.oracle_rms_rescale.restype = None
     lib.oracle_round_bf16.argtypes = [P, ctypes.c_size_t, P]
     lib.oracle_round_bf16.restype = None
+    lib.oracle_gemv_tern_g160.argtypes = [P, P, i32, i32, P, i32, P, i32, P, P]
+    lib.oracle_gemv_tern_g160.restype = None
     lib.oracle_fnv1a32.argtypes = [P, i32]
     lib.oracle_fnv1a32.restype = ctypes.c_uint32
     lib.oracle_z80_normalize.argtypes = [ctypes.c_uint8]
@@ -190,6 +192,16 @@ def gemv_i4g128(nib, scales, x, rows=None):
     sc = _c(scales, np.uint16)
     assert sc.shape == (n, k // 128)
     return _gemv("oracle_gemv_i4g128", q, sc, n, k, x, rows)
+
+
+def gemv_tern_g160(codes, scales, x, rows=None):
+    """Ternary GEMV: codes uint8 [n][k] in {0, 1, 2} (w = t - 1), scales fp16 bits
+    [n][ceil(k/160)], x bf16 bits [B][k]. Returns (y [B][rows], l1 [B][rows]) in float64."""
+    c = _c(codes, np.uint8)
+    n, k = c.shape
+    sc = _c(scales, np.uint16)
+    assert sc.shape == (n, (k + 159) // 160)
+    return _gemv("oracle_gemv_tern_g160", c, sc, n, k, x, rows)
 
 
 def quant_act_i8g128(x):

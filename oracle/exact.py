@@ -147,3 +147,26 @@ def gemv_i4g128(nib, scales, x):
             row_vals.append(total)
         out.append(row_vals)
     return out
+
+
+def gemv_tern_g160(codes, scales, x):
+    """Exact ternary g160 GEMV: codes [n][k] in {0, 1, 2} (w = t - 1), one fp16 scale per 160
+    weights along k (the last group may be shorter); returns y[b][r] as Fractions."""
+    n = len(codes)
+    k = len(codes[0])
+    ng = (k + 159) // 160
+    out = []
+    for xb in x:
+        xv = [bf16_value(int(v)) for v in xb]
+        row_vals = []
+        for r in range(n):
+            total = Fraction(0)
+            for g in range(ng):
+                s = f16_value(int(scales[r][g]))
+                part = Fraction(0)
+                for j in range(160 * g, min(k, 160 * g + 160)):
+                    part += (int(codes[r][j]) - 1) * xv[j]
+                total += s * part
+            row_vals.append(total)
+        out.append(row_vals)
+    return out

@@ -142,6 +142,44 @@ int oracle_mlp_2bit(const uint8_t* const* layer_codes, const int32_t* dims, int 
 }
 
 /* ---------------------------------------------------------------------------------------
+ * Ternary GEMV (Bonsai digest, the intelligence-density table: a ternary variant of the 27B
+ * model next to the 1-bit one). Weights are -1, 0 or +1, given as codes t in {0, 1, 2} with
+ * w = t - 1, and one fp16 scale per group of 160 consecutive weights along k (the last group
+ * of a row may be shorter). The group size is a reading: it is what makes the page's 5.9 GB
+ * for the ternary model (against 3.9 GB at 1.125 bits per weight) come out, with five
+ * ternary digits per byte.
+ *
+ * y = sum_g s_g * sum_{j in g} (t_j - 1) x_j and l1 = sum_g |s_g| sum_{j in g} |t_j - 1| |x_j|.
+ * codes: [n][k] uint8, scales: [n][ceil(k / 160)] fp16, outputs [batch][n_rows].
+ * ------------------------------------------------------------------------------------- */
+void oracle_gemv_tern_g160(const uint8_t* codes, const uint16_t* scales, int n, int k,
+                           const uint16_t* x, int batch, const int32_t* rows, int n_rows,
+                           double* y, double* l1) {
+  int ng = (k + 159) / 160;
+  int nr = rows ? n_rows : n;
+  for (int b = 0; b < batch; ++b) {
+    for (int i = 0; i < nr; ++i) {
+      int r = rows ? rows[i] : i;
+      double acc = 0.0, mag = 0.0;
+      for (int g = 0; g < ng; ++g) {
+        double s = oracle_f16_to_f64(scales[(size_t)r * ng + g]);
+        double part = 0.0, pabs = 0.0;
+        for (int j = 160 * g; j < 160 * g + 160 && j < k; ++j) {
+          int w = (int)codes[(size_t)r * k + j] - 1;
+          double xv = oracle_bf16_to_f64(x[(size_t)b * k + j]);
+          part += w * xv;
+          pabs += (w != 0) ? fabs(xv) : 0.0;
+        }
+        acc += s * part;
+        mag += fabs(s) * pabs;
+      }
+      y[(size_t)b * nr + i] = acc;
+      l1[(size_t)b * nr + i] = mag;
+    }
+  }
+}
+
+/* ---------------------------------------------------------------------------------------
  * Z80-uLM character loop (Z80-uLM page: the trigram-hash encoding of the input into 128
  * buckets, typo-tolerant and word-order invariant; 128 query buckets + 128 context buckets
  * in; one output neuron per charset character; characters generated one at a time).
