@@ -16,7 +16,9 @@ TFLOP/s against the bf16 matrix-core peak. With --i4-layer it times the seven pr
 Qwen3-8B-shaped INT4 g128 layer at B = 1 and 8 through the bf16-activation GEMV and the
 int8-activation GEMV (integer dot products) and reports packed-weight GB/s against HBM. With
 --z80-chat it times the Z80-uLM character loop (1024 prompts, replies of up to 32 characters,
-one launch) and reports generated characters per second.
+one launch) and reports generated characters per second. With --tern-layer it times the seven
+projections of one 27B-shaped layer with ternary g160 weights (1.7 bits per weight) at B = 1
+and 8 and reports packed-weight GB/s against HBM.
 
 Printed: one JSON line on stdout (progress goes to stderr).
 """
@@ -35,6 +37,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "q1_engine_decode_64L.md")
 I4_PROFILE = os.path.join(ROOT, "profiles", "i4_layer_gemv.md")
+TERN_PROFILE = os.path.join(ROOT, "profiles", "tern_layer_gemv.md")
 I4_KERNELS = os.path.join(ROOT, "packed_weight_gemv_amd", "csrc", "lbq_kernels.hip")
 ENGINE_SOURCES = [os.path.join(ROOT, "packed_weight_gemv_amd", "csrc", f)
                   for f in ("lbq_engine.hip", "lbq_engine.h")]
@@ -62,16 +65,17 @@ def measured_traffic(layers: int, batch: int):
     return traffic if sha == h.hexdigest() else None
 
 
-def i4_layer_traffic(key: str):
-    """HBM bytes per layer of the INT4 layer GEMVs (`key` like "i8act-B1") from the committed PMC
+def i4_layer_traffic(key: str, profile: str = None):
+    """HBM bytes per layer of the layer GEMVs (`key` like "i8act-B1") from a committed PMC
     summary, or None when the kernel sources changed since it was taken."""
     import hashlib
-    if not os.path.exists(I4_PROFILE):
+    profile = profile or I4_PROFILE
+    if not os.path.exists(profile):
         return None
     with open(I4_KERNELS, "rb") as fh:
         cur = hashlib.sha256(fh.read()).hexdigest()
     sha, traffic = None, None
-    with open(I4_PROFILE) as fh:
+    with open(profile) as fh:
         for line in fh:
             line = line.strip()
             if line.startswith("kernels-source-sha256:"):
@@ -97,6 +101,8 @@ def parse():
                     help="layers of the stream the CPU oracle baseline runs (0 = skip)")
     ap.add_argument("--kernel-steps", type=int, default=3,
                     help="instrumented steps timing each GEMV launch with HIP events")
+    ap.add_argument("--tern-layer", action="store_true",
+                    help="time the ternary g160 GEMVs of one 27B-shaped layer instead")
     ap.add_argument("--z80-chat", action="store_true",
                     help="time the Z80-uLM character loop (1024 prompts, replies up to 32) instead")
     ap.add_argument("--i4-layer", action="store_true",
@@ -151,6 +157,8 @@ def main() -> int:
         return i4_layer_bench(args, lbq, synth, torch, np, dev)
     if args.z80_chat:
         return chat_bench(args, lbq, synth, torch, np, dev)
+    if args.tern_layer:
+        return tern_layer_bench(args, lbq, synth, torch, np, dev)
 
     L, B = args.layers, args.batch
     hid, kv, ffn = synth.STREAM_HIDDEN, synth.STREAM_KV, synth.STREAM_FFN
@@ -322,6 +330,106 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 Z80_MACS_PER_EVAL = 256 * 192 + 192 * 128 + 128 * 40
 # int16 dot2 issue rate of the chip: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz x 2 MACs
 ALU_DOT2_PEAK_TMACS = 256 * 4 * 16 * 2.4e9 * 2 / 1e12
+
+
+def graph_time_us(torch, fn, pool, args, cap, stream):
+    """Per-call time of fn(w) over a HIP graph of >= 64 launches rotating through `pool`."""
+    calls = len(pool) * max(1, 64 // len(pool))
+    with torch.cuda.stream(cap):
+        for i in range(max(len(pool), args.warmup)):
+            fn(pool[i % len(pool)])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        for i in range(calls):
+            fn(pool[i % len(pool)])
+    graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del graph
+    return e0.elapsed_time(e1) * 1e3 / (args.steps * calls)
+
+
+def tern_layer_bench(args, lbq, synth, torch, np, dev) -> int:
+    """The seven projections of one 27B-shaped layer (q, o 5120x5120; k, v 1024x5120; gate, up
+    17408x5120; down 5120x17408) with ternary g160 weights through lbq_gemv_tern_g160 at B = 1
+    and 8. Weights rotate through >= 1 GiB of copies; each projection's calls are replayed from
+    one HIP graph; the time per layer is the sum of the projections' times per call. Algorithmic
+    bytes: packed weights (34 bytes per 160 weights) plus bf16 activations in and out."""
+    stream = torch.cuda.current_stream()
+    cap = torch.cuda.Stream()
+    layer = {1: [0.0, 0], 8: [0.0, 0]}
+    cases = []
+    for name in synth.STREAM_MATRICES:
+        n, k = synth.stream_shape(name)
+        m = synth.tern_matrix(n, k, matrix=synth.STREAM_MATRICES.index(name))
+        packed = lbq.lbq_pack_tern_g160(m.codes, m.scales)
+        host = torch.from_numpy(packed)
+        pool = [host.to(dev) for _ in range(max(2, -(-(1 << 30) // packed.nbytes)))]
+        for batch in (1, 8):
+            x = torch.from_numpy(synth.activations(batch, k, workload=synth.W_TERN,
+                                                   extra=100 + batch).view(np.int16)).to(dev)
+            y = torch.empty((batch, n), dtype=torch.int16, device=dev)
+            us = graph_time_us(torch, lambda w: lbq.lbq_gemv_tern_g160(w, n, k, x, y, stream=cap),
+                               pool, args, cap, stream)
+            nbytes = packed.nbytes + 2 * batch * (n + k)
+            layer[batch][0] += us
+            layer[batch][1] += nbytes
+            cases.append({"proj": name, "n": n, "k": k, "batch": batch, "us_per_call": round(us, 2),
+                          "gbs": round(nbytes / us / 1e3, 1)})
+            log(f"tern {name} {n}x{k} B={batch}: {us:.1f} us, {nbytes / us / 1e3:.0f} GB/s")
+        del pool
+        torch.cuda.empty_cache()
+    head_us, head_bytes = layer[1]
+    gbs = head_bytes / head_us / 1e3
+    import oracle
+    t0 = time.perf_counter()
+    sampled = 0
+    for name in synth.STREAM_MATRICES:
+        n, k = synth.stream_shape(name)
+        m = synth.tern_matrix(n, k, matrix=synth.STREAM_MATRICES.index(name))
+        xs = synth.activations(1, k, workload=synth.W_TERN, extra=101)
+        oracle.gemv_tern_g160(m.codes, m.scales, xs, rows=np.arange(512, dtype=np.int32))
+        sampled += 512 * ((k + 159) // 160) * 34
+    dt = time.perf_counter() - t0
+    out = {
+        "metric": "packed-weight HBM GB/s of the ternary g160 GEMVs of a 27B-shaped layer",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head_us / 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 (ternary weights, bf16 activations)",
+        "data": "synthetic",
+        "config": {"workload": "27B-shaped layer (7 projections), ternary g160 weights, B = 1; "
+                               "B = 8 in cases",
+                   "parallelism": "single GPU",
+                   "us_per_layer_b8": round(layer[8][0], 2),
+                   "gbs_b8": round(layer[8][1] / layer[8][0] / 1e3, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": i4_layer_traffic("B1", TERN_PROFILE),
+                     "traffic_unit": "HBM bytes per layer (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                     "copy-scaled)",
+                     "bytes_per_layer": head_bytes,
+                     "kernel": "tern_gemv_kernel<1> (7 launches per layer)"},
+        "cpu_baseline": {"value": round(sampled / dt / 1e9, 5), "unit": "GB/s", "cores": 1,
+                         "kind": "oracle",
+                         "sample": "512 output rows of each of the 7 projections, B = 1"},
+        "cases": cases,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
 
 
 def chat_bench(args, lbq, synth, torch, np, dev) -> int:

@@ -56,7 +56,8 @@ enum {
   LBQ_E_UNSUPPORTED = -4, /* valid request the library does not implement (e.g. batch)   */
   LBQ_E_ALIAS = -5,       /* an output overlaps an input                                 */
   LBQ_E_DEVICE = -6,      /* a HIP runtime call or kernel launch failed                  */
-  LBQ_E_NOMEM = -7        /* the library could not obtain its device workspace           */
+  LBQ_E_NOMEM = -7,       /* the library could not obtain its device workspace           */
+  LBQ_E_VALUE = -8        /* an input value is outside the range its format allows       */
 };
 
 /* Returns LBQ_ABI_VERSION of the built library. */
@@ -222,6 +223,35 @@ lbq_status lbq_gemv_i4g128(const void* d_w, int32_t n, int32_t k, const uint16_t
  * and error rules as lbq_gemm_q1g128. */
 lbq_status lbq_gemm_i4g128(const void* d_w, int32_t n, int32_t k, const uint16_t* d_x,
                            uint16_t* d_y, int32_t m, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Ternary g160 (Bonsai digest, intelligence-density table: a ternary build of the 27B model
+ * at 5.9 GB next to the 1-bit build at 3.9 GB). Weights are -1, 0 or +1; the packing is not
+ * given, and the library's reading is five base-3 digits per byte with one fp16 scale per 160
+ * consecutive weights along k: (32 * 8 + 16) / 160 = 1.7 bits per weight, which turns the
+ * 1-bit build's 3.9 GB at 1.125 bits into the page's 5.9 GB.
+ *
+ * Canonical layout: codes[n][k] uint8 in {0, 1, 2}, weight = code - 1; scales[n][ceil(k/160)]
+ * fp16, the scale of weights [160g, 160g + 160) of the row (the last group may be shorter).
+ * Device layout (owned by the packer): rows in tiles of 64 (padded with zero bytes); per tile
+ * and per block of eight groups, 1 KiB of scales (eight fp16 per row) followed by 2 KiB per
+ * group: byte b of a row's 32-byte group record holds weights 5b .. 5b + 4 of the group as
+ * base-3 digits of (weight + 1), least significant first; weights past k are stored as zero.
+ * Bytes = n * ceil(k/160) * 34 when n % 64 == 0 and ceil(k/160) % 8 == 0.
+ * ------------------------------------------------------------------------------------------ */
+
+size_t lbq_tern_g160_bytes(int32_t n, int32_t k);
+/* Returns LBQ_E_VALUE (nothing written past the check) if a code exceeds 2. */
+lbq_status lbq_pack_tern_g160(const uint8_t* codes, const uint16_t* scales, int32_t n, int32_t k,
+                              void* dst);
+lbq_status lbq_unpack_tern_g160(const void* src, int32_t n, int32_t k, uint8_t* codes,
+                                uint16_t* scales);
+
+/* y[b][row] = bf16_rne( sum_g f32(scale[row][g]) * sum_{j in g} (code[row][j] - 1) * x[b][j] ),
+ * fp32 accumulation. Any k >= 1 (no multiple required); otherwise the pointer, alignment,
+ * batch and workspace rules of lbq_gemv_q1g128. */
+lbq_status lbq_gemv_tern_g160(const void* d_w, int32_t n, int32_t k, const uint16_t* d_x,
+                              uint16_t* d_y, int32_t batch, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * INT4 weights x int8 activations with integer dot products (the Acorn page, its analysis of

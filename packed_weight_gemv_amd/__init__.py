@@ -19,7 +19,8 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "lbq.h")
 
 LBQ_OK = 0
 STATUS = {0: "LBQ_OK", -1: "LBQ_E_NULL", -2: "LBQ_E_SHAPE", -3: "LBQ_E_ALIGN",
-          -4: "LBQ_E_UNSUPPORTED", -5: "LBQ_E_ALIAS", -6: "LBQ_E_DEVICE", -7: "LBQ_E_NOMEM"}
+          -4: "LBQ_E_UNSUPPORTED", -5: "LBQ_E_ALIAS", -6: "LBQ_E_DEVICE", -7: "LBQ_E_NOMEM",
+          -8: "LBQ_E_VALUE"}
 MAX_BATCH = 16
 Z80_MAX_REPLY = 256
 ACT_SLOTS = ("x", "q", "k", "v", "gate", "up", "xo", "o", "xd", "down")
@@ -66,6 +67,10 @@ def load():
         "lbq_quant_act_i8g128": ([P, i32, i32, P, P, P], i32),
         "lbq_gemv_i4g128_act_i8": ([P, i32, i32, P, P, i32, P], i32),
         "lbq_z80_encode": ([P, P, i32, i32, P, P], i32),
+        "lbq_tern_g160_bytes": ([i32, i32], sz),
+        "lbq_pack_tern_g160": ([P, P, i32, i32, P], i32),
+        "lbq_unpack_tern_g160": ([P, i32, i32, P, P], i32),
+        "lbq_gemv_tern_g160": ([P, i32, i32, P, P, i32, P], i32),
         "lbq_z80_chat_2bit": ([P, P, i32, P, P, i32, i32, i32, P, P, P], i32),
         "lbq_rms_rescale_bf16": ([P, P, P, i32, i32, ctypes.c_float, P], i32),
         "lbq_decode_act_elems": ([i32, i32, i32, i32, i32], sz),
@@ -202,6 +207,36 @@ def lbq_mlp_2bit_i16(layer_w, dims, x, logits, argmax=None, stream=None) -> None
     _check("lbq_mlp_2bit_i16", load().lbq_mlp_2bit_i16(
         ctypes.cast(ptrs, ctypes.c_void_p), ctypes.cast(d, ctypes.c_void_p), L, _dptr(x),
         _dptr(logits), _dptr(argmax), x.shape[0], _stream(stream)))
+
+
+def lbq_tern_g160_bytes(n: int, k: int) -> int:
+    return load().lbq_tern_g160_bytes(n, k)
+
+
+def lbq_pack_tern_g160(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """codes uint8 [n][k] in {0, 1, 2}; scales fp16 bits [n][ceil(k/160)] -> device bytes."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    n, k = codes.shape
+    out = np.zeros(lbq_tern_g160_bytes(n, k), dtype=np.uint8)
+    _check("lbq_pack_tern_g160", load().lbq_pack_tern_g160(_np_ptr(codes), _np_ptr(scales), n, k,
+                                                           _np_ptr(out)))
+    return out
+
+
+def lbq_unpack_tern_g160(dev: np.ndarray, n: int, k: int):
+    dev = np.ascontiguousarray(dev, dtype=np.uint8)
+    codes = np.zeros((n, k), dtype=np.uint8)
+    scales = np.zeros((n, (k + 159) // 160), dtype=np.uint16)
+    _check("lbq_unpack_tern_g160", load().lbq_unpack_tern_g160(_np_ptr(dev), n, k, _np_ptr(codes),
+                                                               _np_ptr(scales)))
+    return codes, scales
+
+
+def lbq_gemv_tern_g160(w, n: int, k: int, x, y, stream=None) -> None:
+    B = x.shape[0] if x.dim() == 2 else 1
+    _check("lbq_gemv_tern_g160", load().lbq_gemv_tern_g160(_dptr(w), n, k, _dptr(x), _dptr(y), B,
+                                                           _stream(stream)))
 
 
 def lbq_z80_encode(text, lengths, buckets, stream=None) -> None:

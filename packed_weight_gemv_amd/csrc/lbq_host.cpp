@@ -18,6 +18,7 @@ extern "C" const char* lbq_status_string(lbq_status s) {
     case LBQ_E_ALIAS: return "output overlaps an input";
     case LBQ_E_DEVICE: return "HIP runtime or launch failure";
     case LBQ_E_NOMEM: return "device workspace unavailable";
+    case LBQ_E_VALUE: return "input value out of range";
     default: return "unknown status";
   }
 }
@@ -233,4 +234,72 @@ extern "C" int64_t lbq_decode_act_offset(int32_t layer, int32_t slot, int32_t n_
   int64_t off = per_layer * layer;
   for (int i = 0; i < slot; ++i) off += dims[i] * batch;
   return off;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Ternary g160. Per row and group: 32 bytes, byte b holding the five weights 5b .. 5b + 4 of the
+// group as base-3 digits, least significant first (value = sum_i t_i 3^i, t = w + 1 in 0..2);
+// weights past k are zero (digit 1). Bytes 0..15 and 16..31 form two 16-byte records placed
+// 1 KiB apart, one 16-byte load per lane reading 1 KiB contiguously across a wave.
+// ---------------------------------------------------------------------------------------------
+extern "C" size_t lbq_tern_g160_bytes(int32_t n, int32_t k) {
+  Geometry g;
+  if (!make_geometry_tern(n, k, &g)) return 0;
+  return layout_bytes(g);
+}
+
+extern "C" lbq_status lbq_pack_tern_g160(const uint8_t* codes, const uint16_t* scales, int32_t n,
+                                         int32_t k, void* dst) {
+  if (!codes || !scales || !dst) return LBQ_E_NULL;
+  Geometry g;
+  if (!make_geometry_tern(n, k, &g)) return LBQ_E_SHAPE;
+  for (int64_t i = 0; i < (int64_t)n * k; ++i)
+    if (codes[i] > 2) return LBQ_E_VALUE;
+  uint8_t* out = (uint8_t*)dst;
+  memset(out, 0, layout_bytes(g));
+  for (int64_t r = 0; r < n; ++r) {
+    const int64_t t = r / kTileRows, lane = r % kTileRows;
+    const uint8_t* crow = codes + r * k;
+    const uint16_t* srow = scales + r * g.groups;
+    for (int64_t gi = 0; gi < g.groups; ++gi) {
+      uint8_t* sc = out + scale_offset(g, t, gi / kSuper) + lane * 16 + (gi % kSuper) * 2;
+      sc[0] = (uint8_t)srow[gi];
+      sc[1] = (uint8_t)(srow[gi] >> 8);
+      for (int b = 0; b < 32; ++b) {
+        uint32_t v = 0;
+        for (int i = 4; i >= 0; --i) {
+          const int64_t j = gi * kTernGroup + 5 * b + i;
+          v = 3 * v + (j < k ? crow[j] : 1u);
+        }
+        out[group_offset(g, t, gi) + (int64_t)(b / 16) * kBlock + lane * 16 + b % 16] = (uint8_t)v;
+      }
+    }
+  }
+  return LBQ_OK;
+}
+
+extern "C" lbq_status lbq_unpack_tern_g160(const void* src, int32_t n, int32_t k, uint8_t* codes,
+                                           uint16_t* scales) {
+  if (!codes || !scales || !src) return LBQ_E_NULL;
+  Geometry g;
+  if (!make_geometry_tern(n, k, &g)) return LBQ_E_SHAPE;
+  const uint8_t* in = (const uint8_t*)src;
+  for (int64_t r = 0; r < n; ++r) {
+    const int64_t t = r / kTileRows, lane = r % kTileRows;
+    uint8_t* crow = codes + r * k;
+    uint16_t* srow = scales + r * g.groups;
+    for (int64_t gi = 0; gi < g.groups; ++gi) {
+      const uint8_t* sc = in + scale_offset(g, t, gi / kSuper) + lane * 16 + (gi % kSuper) * 2;
+      srow[gi] = (uint16_t)(sc[0] | (sc[1] << 8));
+      for (int b = 0; b < 32; ++b) {
+        uint32_t v = in[group_offset(g, t, gi) + (int64_t)(b / 16) * kBlock + lane * 16 + b % 16];
+        for (int i = 0; i < 5; ++i) {
+          const int64_t j = gi * kTernGroup + 5 * b + i;
+          if (j < k) crow[j] = (uint8_t)(v % 3);
+          v /= 3;
+        }
+      }
+    }
+  }
+  return LBQ_OK;
 }

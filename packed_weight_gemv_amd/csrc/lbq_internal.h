@@ -45,6 +45,25 @@ inline bool make_geometry(int64_t n, int64_t k, int group_blocks, Geometry* g) {
   return true;
 }
 
+// Ternary g160: groups of 160 weights (five base-3 digits per byte, 32 bytes per row and group,
+// two 16-byte records 1 KiB apart), any k >= 1 (the last group is padded with zero weights).
+constexpr int kTernGroup = 160;
+constexpr int kTernGroupBlocks = 2;
+
+inline bool make_geometry_tern(int64_t n, int64_t k, Geometry* g) {
+  if (n < 1 || k < 1 || n > (int64_t)1 << 24 || k > (int64_t)1 << 24) return false;
+  g->n = n;
+  g->k = k;
+  g->np = (n + kTileRows - 1) / kTileRows * kTileRows;
+  g->tiles = g->np / kTileRows;
+  g->groups = (k + kTernGroup - 1) / kTernGroup;
+  g->supers = (g->groups + kSuper - 1) / kSuper;
+  g->group_bytes = (int64_t)kTernGroupBlocks * kBlock;
+  g->super_bytes = kBlock + kSuper * g->group_bytes;
+  g->tile_bytes = g->supers * kBlock + g->groups * g->group_bytes;
+  return true;
+}
+
 inline size_t layout_bytes(const Geometry& g) { return (size_t)(g.tiles * g.tile_bytes); }
 
 // Byte offset of the scale record of (tile t, super-group j) and of the code block of group gi.

@@ -700,6 +700,119 @@ __global__ __launch_bounds__(64 * kI4Waves) void i4_i8act_gemv_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
+// Ternary g160 GEMV.
+//
+// A row's group is 32 bytes, byte b holding weights 5b .. 5b + 4 as base-3 digits t = w + 1
+// (least significant first). Per chunk of five activations the kernel keeps two tables in LDS:
+// the 9 sums over digits 0-1, T2[lo] = sum_{i<2} (t_i - 1) x_i for lo = t_0 + 3 t_1, and the 27
+// sums over digits 2-4, T3[hi] = sum_{2<=i<5} (t_i - 1) x_i for hi = t_2 + 3 t_3 + 9 t_4. A
+// byte v contributes T2[v mod 9] + T3[v div 9], with v div 9 = (57 v) >> 9 exactly for v < 243.
+// Every lane of a wave reads the tables of the same chunk at the same time, so the lookups
+// are free of bank conflicts. Grid, wave split, up-front weight loads, wave-order reduction
+// and split-K finish as for the INT4 kernels; wave w builds the tables of its own two groups,
+// one chunk per lane.
+// ---------------------------------------------------------------------------------------------
+constexpr int kTernChunks = kTernGroup / 5;   // 32 bytes per row and group
+constexpr int kTernTab = 9 + 27;
+
+template <int NB>
+__global__ __launch_bounds__(64 * kI4Waves) void tern_gemv_kernel(
+    const uint8_t* __restrict__ w, const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
+    float* __restrict__ partial, unsigned* __restrict__ counters, int n, int k, int np,
+    int groups, int supers, long long tile_bytes, int batch) {
+  __shared__ float tab[NB][kSuper][kTernChunks][kTernTab];
+  __shared__ float red[kI4Waves][NB][64];
+  const int tile = blockIdx.x, sg = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g0 = sg * kSuper;
+  const int gcount = min(kSuper, groups - g0);
+  const int gw = kI4GroupsPerWave * wave;
+  const uint8_t* base = w + (size_t)tile * tile_bytes + (size_t)sg * (kBlock * (1 + kSuper * kTernGroupBlocks));
+  u32x4 wv[kI4GroupsPerWave][kTernGroupBlocks];
+#pragma unroll
+  for (int i = 0; i < kI4GroupsPerWave; ++i) {
+    if (gw + i < gcount) {
+      const uint8_t* gp = base + kBlock + (size_t)(gw + i) * (kTernGroupBlocks * kBlock) + lane * 16;
+#pragma unroll
+      for (int m = 0; m < kTernGroupBlocks; ++m) wv[i][m] = ld_stream16(gp + m * kBlock);
+    }
+  }
+  const uint32_t scw = *(const uint32_t*)(base + lane * 16 + 4 * wave);
+  const float scale[2] = {f16_to_f32(scw & 0xFFFF), f16_to_f32(scw >> 16)};
+  const int row = tile * kTileRows + lane;
+  // table lane map: lanes 0-31 chunks of group gw, lanes 32-63 chunks of group gw + 1
+  const int tg = gw + (lane >> 5), tc = lane & 31;
+  const int j0 = (g0 + tg) * kTernGroup + 5 * tc;   // first input of the lane's chunk
+
+  for (int b0 = 0; b0 < batch; b0 += NB) {
+    const int nb = min(NB, batch - b0);
+    float xv[NB][5];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+      for (int i = 0; i < 5; ++i)
+        xv[bb][i] = (bb < nb && tg < gcount && j0 + i < k) ? bf16_to_f32(x[(size_t)(b0 + bb) * k + j0 + i]) : 0.f;
+    __syncthreads();   // the previous pass has finished reading tab and red
+    if (tg < gcount) {
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        if (bb < nb) {
+          float* T = tab[bb][tg][tc];
+#pragma unroll
+          for (int lo = 0; lo < 9; ++lo)
+            T[lo] = (float)(lo % 3 - 1) * xv[bb][0] + (float)(lo / 3 - 1) * xv[bb][1];
+#pragma unroll
+          for (int hi = 0; hi < 27; ++hi)
+            T[9 + hi] = (float)(hi % 3 - 1) * xv[bb][2] + (float)(hi / 3 % 3 - 1) * xv[bb][3] +
+                        (float)(hi / 9 - 1) * xv[bb][4];
+        }
+      }
+    }
+    __syncthreads();
+
+    float acc[NB];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) acc[bb] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kI4GroupsPerWave; ++i) {
+      const int gi = gw + i;
+      if (gi >= gcount) break;
+      float ga[NB];
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) ga[bb] = 0.f;
+#pragma unroll
+      for (int m = 0; m < kTernGroupBlocks; ++m) {
+        const uint32_t s4[4] = {wv[i][m].x, wv[i][m].y, wv[i][m].z, wv[i][m].w};
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+          // an empty asm step per dword keeps the compiler from computing the table addresses
+          // of all 64 bytes up front (196 live registers instead of about 50)
+          uint32_t dw = s4[ww];
+          asm volatile("" : "+v"(dw));
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = 16 * m + 4 * ww + q;   // chunk (byte) of the group
+            const uint32_t v = (dw >> (8 * q)) & 0xFFu;
+            const uint32_t hi = (v * 57u) >> 9;
+            const uint32_t lo = v - 9u * hi;
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb)
+              if (bb < nb) ga[bb] += tab[bb][gi][c][lo] + tab[bb][gi][c][9 + hi];
+          }
+        }
+      }
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb)
+        if (bb < nb) acc[bb] = fmaf(scale[i], ga[bb], acc[bb]);
+    }
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) red[wave][bb][lane] = acc[bb];
+    store_wave_sums<NB, kI4Waves>(red, wave, lane, nb, b0, sg, supers, row, n, np, y, partial);
+  }
+  if (supers > 1) splitk_finish(partial, counters + tile, y, n, np, supers, batch, row, wave == 0);
+}
+
+// ---------------------------------------------------------------------------------------------
 // device entry points
 // ---------------------------------------------------------------------------------------------
 static lbq_status launch_status() {
@@ -860,6 +973,37 @@ extern "C" lbq_status lbq_gemv_i4g128_act_i8(const void* d_w, int32_t n, int32_t
   if (nbp == 1) LAUNCH_I8(1); else if (nbp == 2) LAUNCH_I8(2);
   else if (nbp == 4) LAUNCH_I8(4); else LAUNCH_I8(8);
 #undef LAUNCH_I8
+  return launch_status();
+}
+
+extern "C" lbq_status lbq_gemv_tern_g160(const void* d_w, int32_t n, int32_t k,
+                                         const uint16_t* d_x, uint16_t* d_y, int32_t batch,
+                                         void* stream) {
+  Geometry g;
+  if (!make_geometry_tern(n, k, &g)) return LBQ_E_SHAPE;
+  if (batch < 0 || batch > LBQ_MAX_BATCH) return LBQ_E_SHAPE;
+  if (batch == 0) return LBQ_OK;
+  if (!d_w || !d_x || !d_y) return LBQ_E_NULL;
+  if ((uintptr_t)d_w % 16 || (uintptr_t)d_x % 4 || (uintptr_t)d_y % 4) return LBQ_E_ALIGN;
+  const size_t yb = (size_t)batch * n * 2;
+  if (overlaps(d_y, yb, d_x, (size_t)batch * k * 2) || overlaps(d_y, yb, d_w, layout_bytes(g)))
+    return LBQ_E_ALIAS;
+  hipStream_t s = (hipStream_t)stream;
+  unsigned* counters = nullptr;
+  float* partials = nullptr;
+  if (g.supers > 1) {
+    if (g.tiles * sizeof(unsigned) > kCounterBytes) return LBQ_E_SHAPE;
+    const lbq_status st = get_workspace((size_t)batch * g.supers * g.np * sizeof(float), s,
+                                        &counters, &partials);
+    if (st != LBQ_OK) return st;
+  }
+  const dim3 grid((unsigned)g.tiles, (unsigned)g.supers);
+#define LAUNCH_TERN(NB)                                                                          \
+  hipLaunchKernelGGL(tern_gemv_kernel<NB>, grid, dim3(64 * kI4Waves), 0, s, (const uint8_t*)d_w, \
+                     d_x, d_y, partials, counters, n, k, (int)g.np, (int)g.groups,              \
+                     (int)g.supers, (long long)g.tile_bytes, batch)
+  if (batch == 1) LAUNCH_TERN(1); else LAUNCH_TERN(2);
+#undef LAUNCH_TERN
   return launch_status();
 }
 

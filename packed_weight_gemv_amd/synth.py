@@ -25,6 +25,7 @@ KIND_CODES, KIND_SCALES, KIND_ACT, KIND_STRESS = 0, 1, 2, 3
 # workload ids
 W_MLP2BIT, W_Q1_SQUARE, W_Q1_MLP, W_I4_LAYER, W_Q1_STREAM = 1, 2, 3, 4, 5
 W_Z80_CHAT = 6
+W_TERN = 7
 Z80_REPLY = 32                          # reply cap of the chat-loop workload
 
 MLP_DIMS = (256, 192, 128, 40)          # 128 query + 128 context buckets -> ... -> 40 chars
@@ -109,6 +110,24 @@ def i4_matrix(n: int, k: int, workload: int, layer: int = 0, matrix: int = 0,
     nib = random_bytes(rng(workload, layer, matrix, KIND_CODES), (n, k // 2))
     scales = fp16_abs_normal(rng(workload, layer, matrix, KIND_SCALES), (n, k // 128), sigma)
     return I4Matrix(nib, scales)
+
+
+@dataclass
+class TernMatrix:
+    codes: np.ndarray    # uint8 [n][k] in {0, 1, 2}, weight = code - 1
+    scales: np.ndarray   # fp16 bits [n][ceil(k/160)]
+
+    @property
+    def shape(self):
+        return self.codes.shape
+
+
+def tern_matrix(n: int, k: int, workload: int = W_TERN, layer: int = 0, matrix: int = 0,
+                sigma: float = Q1_SIGMA) -> TernMatrix:
+    """Ternary weights uniform over {-1, 0, +1}, fp16 scales |N(0, sigma)| per 160 weights."""
+    codes = rng(workload, layer, matrix, KIND_CODES).integers(0, 3, size=(n, k), dtype=np.uint8)
+    scales = fp16_abs_normal(rng(workload, layer, matrix, KIND_SCALES), (n, (k + 159) // 160), sigma)
+    return TernMatrix(codes, scales)
 
 
 def activations(batch: int, k: int, workload: int, layer: int = 0, matrix: int = 0,

@@ -26,7 +26,7 @@ def lib():
 
 def test_library_exports_every_declared_function(lib):
     names = _declared_functions()
-    assert len(names) == 25
+    assert len(names) == 29
     for name in names:
         assert hasattr(lib, name), name
         assert name in dir(lbq) or name in ("lbq_status_string",), f"binding lacks {name}"
@@ -136,3 +136,33 @@ def test_decode_activation_record_geometry():
     assert lbq.lbq_decode_act_offset(L, 10, L, h, kv, f, B) == per_layer * L
     assert lbq.lbq_decode_act_offset(L, 3, L, h, kv, f, B) == -1
     assert lbq.lbq_decode_act_elems(L, 100, kv, f, B) == 0
+
+
+@pytest.mark.parametrize("n,k", [(64, 160), (70, 1000), (1, 37), (130, 17408), (3, 1281)])
+def test_tern_pack_roundtrip(n, k):
+    m = synth.tern_matrix(n, k, matrix=n + k)
+    dev = lbq.lbq_pack_tern_g160(m.codes, m.scales)
+    assert dev.size == lbq.lbq_tern_g160_bytes(n, k)
+    c2, s2 = lbq.lbq_unpack_tern_g160(dev, n, k)
+    assert np.array_equal(c2, m.codes) and np.array_equal(s2, m.scales)
+
+
+def test_tern_sizes_and_digit_order():
+    # 1.7 bits per weight on aligned shapes (34 bytes per 160 weights)
+    for n, k in ((5120, 5120), (1024, 5120), (17408, 5120)):
+        assert lbq.lbq_tern_g160_bytes(n, k) == n * k // 160 * 34
+    n, k = 64, 160
+    codes = np.ones((n, k), dtype=np.uint8)
+    codes[0, :5] = [2, 0, 1, 1, 2]            # byte 0 of row 0: 2 + 0*3 + 1*9 + 1*27 + 2*81
+    codes[1, 5:10] = [0, 0, 0, 0, 0]          # byte 1 of row 1: 0
+    scales = np.arange(n, dtype=np.uint16)[:, None]
+    dev = lbq.lbq_pack_tern_g160(codes, scales)
+    assert np.array_equal(dev[:1024].view(np.uint16).reshape(64, 8)[:, 0], scales[:, 0])
+    rec = dev[1024:2048].reshape(64, 16)      # bytes 0..15 of every row's group record
+    assert rec[0, 0] == 2 + 9 + 27 + 162 and rec[1, 1] == 0 and rec[2, 0] == 121
+    # a code above 2 is rejected
+    bad = codes.copy()
+    bad[5, 7] = 3
+    with pytest.raises(lbq.LbqError) as e:
+        lbq.lbq_pack_tern_g160(bad, scales)
+    assert e.value.status == -8
