@@ -6,9 +6,10 @@ A step is one decode step of the whole stream: 64 layers x (q, o 5120x5120; k, v
 gate, up 17408x5120; down 5120x17408) Q1_0_g128 GEMVs with the RMS rescales between them
 (lbq_decode_step_q1g128), over seeded synthetic weights (sign bits Bernoulli(0.5), fp16 scales
 |N(0, 0.02)|) and a bf16 N(0, 1) input, all resident in HBM before timing starts. At batch 1 a
-step is one launch of the persistent engine; larger batches replay a HIP graph of
-the per-projection launches. W untimed warm-up steps precede exactly K timed steps bracketed
-by device synchronisation.
+step is two stage-kernel launches per layer and a final one; larger batches run the
+per-projection launches. Either is captured once in a HIP graph and replayed (--no-graph runs it
+eagerly). W untimed warm-up steps precede exactly K timed steps bracketed by device
+synchronisation.
 
 With --gemm the bench times the many-row products on the matrix cores instead (prefill and
 large batch: Q1 MLP and INT4 layer shapes at 32, 128 and 512 activation rows) and reports
@@ -35,32 +36,33 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "q1_engine_decode_64L.md")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "q1_stage_decode_64L.md")
 I4_PROFILE = os.path.join(ROOT, "profiles", "i4_layer_gemv.md")
 TERN_PROFILE = os.path.join(ROOT, "profiles", "tern_layer_gemv.md")
 I4_KERNELS = os.path.join(ROOT, "packed_weight_gemv_amd", "csrc", "lbq_kernels.hip")
-ENGINE_SOURCES = [os.path.join(ROOT, "packed_weight_gemv_amd", "csrc", f)
-                  for f in ("lbq_engine.hip", "lbq_engine.h")]
+STEP_SOURCES = [os.path.join(ROOT, "packed_weight_gemv_amd", "csrc", f)
+                for f in ("lbq_stage.hip", "lbq_internal.h")]
 
 
 def measured_traffic(layers: int, batch: int):
-    """HBM bytes per launch from the committed PMC summary (FETCH_SIZE + WRITE_SIZE, each scaled
-    by a plain copy of known size), or None when the engine sources changed since it was taken
-    or the workload differs from the profiled one (64 layers, batch 1)."""
+    """HBM bytes per decode step from the committed PMC summary (FETCH_SIZE + WRITE_SIZE summed
+    over the step's launches, each scaled by a plain copy of known size), or None when the
+    stage-kernel sources changed since it was taken or the workload differs from the profiled
+    one (64 layers, batch 1)."""
     import hashlib
     if layers != 64 or batch != 1 or not os.path.exists(TRAFFIC_PROFILE):
         return None
     h = hashlib.sha256()
-    for f in ENGINE_SOURCES:
+    for f in STEP_SOURCES:
         with open(f, "rb") as fh:
             h.update(fh.read())
     sha, traffic = None, None
     with open(TRAFFIC_PROFILE) as fh:
         for line in fh:
             line = line.strip()
-            if line.startswith("engine-source-sha256:"):
+            if line.startswith("step-source-sha256:"):
                 sha = line.split(":", 1)[1].strip()
-            elif line.startswith("traffic-bytes-per-launch:"):
+            elif line.startswith("traffic-bytes-per-step:"):
                 traffic = int(line.split(":", 1)[1].strip())
     return traffic if sha == h.hexdigest() else None
 
@@ -190,7 +192,7 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
     graph = None
-    if not args.no_graph and B > 1:   # batch 1 is a single persistent launch per step
+    if not args.no_graph:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             step()
@@ -200,8 +202,8 @@ def main() -> int:
     run = graph.replay if graph is not None else step
     log(f"timing {args.steps} steps ({'graph' if graph is not None else 'eager'})")
     # every step is bracketed by its own event pair on the launch stream, inside the timed
-    # region: at batch 1 a step is exactly one launch of the persistent kernel, so these give
-    # that kernel's average duration
+    # region: at batch 1 a step is the 2 x layers + 1 stage-kernel launches and nothing else, so
+    # these give the step's kernel time
     stream = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
@@ -222,7 +224,8 @@ def main() -> int:
 
     # ---- dominant kernel ---------------------------------------------------------------------
     if B == 1:
-        kern_name = "q1_engine_kernel (whole decode step, one persistent launch)"
+        kern_name = ("stage_kernel (whole decode step: two launches per layer and a final one, "
+                     f"{2 * L + 1} launches)")
         kern_avg_ms, kern_bytes = step_kernel_ms, bytes_per_step
     else:
         # host-driven step: every Q1 GEMV launch of a step bracketed by events
@@ -312,7 +315,8 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(L, B) if B == 1 else None,
-            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
+            "traffic_unit": ("bytes per step (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)"
+                             if B == 1 else "bytes per launch"),
             "kernel": kern_name,
             "avg_launch_us": round(kern_avg_ms * 1e3, 3),
             "bytes_per_launch": round(kern_bytes),

@@ -343,9 +343,11 @@ lbq_status lbq_decode_step_q1g128(const lbq_q1_layer* layers, int32_t n_layers, 
                                   int32_t kv, int32_t ffn, const uint16_t* d_x0,
                                   uint16_t* d_act, int32_t batch, float eps, void* stream);
 
-/* Batch-1 Q1_0_g128 GEMVs and decode steps run as one persistent launch (one workgroup per
- * compute unit) whose workgroups exchange partial sums through tagged words in a
- * library-owned device workspace; every wait inside such a launch is bounded. Such a launch
+/* Batch-1 decode steps run as two launches per layer that need no communication between
+ * workgroups (an fp32 accumulator of 2 x hidden floats per device is the library's workspace).
+ * Batch-1 Q1_0_g128 GEMVs run as one persistent launch (one workgroup per compute unit) whose
+ * workgroups exchange partial sums through tagged words in a library-owned device workspace;
+ * every wait inside such a launch is bounded. Such a launch
  * expects the device to itself: should another kernel hold compute units meanwhile, its waits
  * time out instead of hanging. This call synchronises `stream` and returns LBQ_E_DEVICE if a
  * launch on the current device gave up waiting (its outputs are then invalid), LBQ_OK

@@ -83,4 +83,9 @@ constexpr size_t kSplitCounterBytes = 1 << 20;
 lbq_status splitk_workspace(size_t partial_bytes, void* stream, unsigned** counters,
                             float** partials);
 
+// Batch-1 decode step as two stage launches per layer (lbq_stage.hip); LBQ_E_UNSUPPORTED for
+// shapes it does not cover.
+lbq_status stage_decode_q1(const lbq_q1_layer* layers, int n_layers, int hidden, int kv, int ffn,
+                           const uint16_t* d_x0, uint16_t* d_act, float eps, void* stream);
+
 }  // namespace lbq

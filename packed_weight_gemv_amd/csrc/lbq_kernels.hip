@@ -1037,7 +1037,9 @@ extern "C" lbq_status lbq_decode_step_q1g128(const lbq_q1_layer* layers, int32_t
   if (overlaps(d_x0, (size_t)batch * hidden * 2, d_act, elems * 2)) return LBQ_E_ALIAS;
   hipStream_t s = (hipStream_t)stream;
   if (batch == 1) {
-    const lbq_status st = lbq_engine_decode_q1(layers, n_layers, hidden, kv, ffn, d_x0, d_act, eps, s);
+    lbq_status st = stage_decode_q1(layers, n_layers, hidden, kv, ffn, d_x0, d_act, eps, s);
+    if (st != LBQ_E_UNSUPPORTED) return st;
+    st = lbq_engine_decode_q1(layers, n_layers, hidden, kv, ffn, d_x0, d_act, eps, s);
     if (st != LBQ_E_UNSUPPORTED) return st;
   }
   auto at = [&](int layer, int slot) {

@@ -1,0 +1,508 @@
+// lbq_stage.hip - batch-1 decode step of a Q1_0_g128 layer stack as two launches per layer,
+// with no communication between workgroups inside a launch (the launch boundary is the only
+// synchronisation).
+//
+//  * Stage 1 of layer l computes q, k, v, gate and up from x_l. Every workgroup first forms x_l
+//    itself: for layer 0 it is the step input; otherwise it is rms(down_{l-1}), where down_{l-1}
+//    is read from the fp32 accumulator that stage 2 of the previous layer filled, rounded to
+//    bf16 and rescaled. It then builds the sign-sum tables of all of x_l in LDS (16 entries per
+//    4 inputs) and walks its share of the 64-row output tiles of the five matrices, each tile
+//    over the whole of k, with the next tile's weights in flight while the current one is
+//    computed.
+//  * Stage 2 of layer l computes o from rms(q) (one workgroup per tile) and down from
+//    rms(gate * up) (two workgroups per tile, each over half of k). The two halves of a down row
+//    are added into a zeroed fp32 accumulator with atomic adds: 0 + a + b is the same in either
+//    order, so the result is deterministic.
+//  * A workgroup has 16 waves; wave w takes groups w, w + 16, ... of a tile, one row per lane,
+//    and adds one table entry per 4 weights (the field extraction of the per-call Q1 kernel);
+//    the 16 waves' sums are added in wave order through LDS.
+//  * The activation slots (x, q, k, v, gate, up, xo, o, xd, down) are written as the per-call
+//    path writes them: stage 1's first workgroup writes x_l and down_{l-1}, stage 2's first o
+//    and down workgroups write xo and xd.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "lbq_internal.h"
+
+using namespace lbq;
+
+namespace {
+
+constexpr int kStWaves = 16;
+constexpr int kStThreads = 64 * kStWaves;
+// per launch kind: stage 1 takes up to 3 tiles of up to 48 groups (3 per wave), stage 2 one tile
+// (or half a down row) of up to 80 groups (5 per wave)
+constexpr int kSt1Items = 3, kSt1G = 3, kSt2G = 5;
+constexpr int kStMaxChunks = 2304;    // table capacity: 9,216 inputs (147,456 B)
+constexpr int kStSuperBytes = kBlock * (1 + kSuper * kQ1GroupBlocks);
+constexpr int kStInIters = 6;        // input chunks (4 inputs) per thread: vectors up to 24,576
+constexpr int kStMaxItems = kSt1Items;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float st_bf16(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ uint16_t st_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float st_f16(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+// byte offset (4-bit field x 4) of table entry q of a sign dword stored rotated left by two:
+// bits [8q+2, 8q+5]. For byte 1 the SDWA source select does it in one op (the compiler emits a
+// shift and a mask there, and one op for bytes 0, 2 and 3 by itself).
+__device__ __forceinline__ uint32_t st_field(uint32_t s, int q) {
+  if (q == 1) {
+    uint32_t r, m = 0x3Cu;
+    asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 "
+        "src1_sel:DWORD"
+        : "=v"(r)
+        : "v"(s), "v"(m));
+    return r;
+  }
+  return (s >> (8 * q)) & 0x3Cu;
+}
+
+struct StMat {
+  const uint8_t* w;        // device layout
+  uint16_t* y;             // bf16 output rows, or nullptr
+  float* acc;              // fp32 accumulator rows (atomic add), or nullptr
+  int n;                   // rows
+  int tiles;               // 64-row tiles
+  int groups;              // 128-weight groups of a full row
+  long long tile_bytes;
+};
+
+// One stage launch. Stage 1: mats[0..4] = q, k, v, gate, up over input x. Stage 2: mats[0] = o
+// over rms(q), mats[1] = down over rms(gate * up), split in two halves of its super-groups.
+struct StArgs {
+  StMat mats[5];
+  int nmats;
+  int stage;               // 1 or 2
+  int hidden, ffn;
+  float eps;
+  // stage 1 input: x0 (layer 0) or the previous layer's down accumulator
+  const uint16_t* x0;
+  const float* acc_in;
+  uint16_t* x_out;         // x_l (bf16), written by workgroup 0
+  uint16_t* down_out;      // down_{l-1} (bf16), written by workgroup 0 when acc_in is set
+  float* acc_zero;         // accumulator cleared by workgroup 0 for this layer's stage 2
+  // stage 2 inputs
+  const uint16_t* q;
+  const uint16_t* gate;
+  const uint16_t* up;
+  uint16_t* xo_out;
+  uint16_t* xd_out;
+  int down_split_sg;       // first super-group of the second half of down
+};
+
+struct StLds {
+  float lut[kStMaxChunks * 16];
+  float red[kStWaves][64];
+  float ssum[kStWaves];
+};
+
+// Input kinds: 0 = bf16 x0; 1 = bf16(fp32 accumulator); 2 = bf16 q; 3 = gate * up (exact in
+// fp32). Thread t owns the chunks c = t + i * kStThreads (inputs 4c .. 4c + 3) of the whole
+// vector: their loads are issued first, the sum of squares runs over them in a fixed order
+// (identical in every workgroup), and the tables of the workgroup's chunk range are built from
+// the same registers.
+struct StIn {
+  uint32_t a[kStInIters][4];   // raw words: bf16 pairs (kinds 0, 2, 3: a[..][0..1]) or fp32 (kind 1)
+  uint32_t b[kStInIters][2];   // up pairs (kind 3)
+};
+
+template <int KIND>
+__device__ __forceinline__ void st_in_load(const StArgs& A, int nch, StIn& I) {
+#pragma unroll
+  for (int it = 0; it < kStInIters; ++it) {
+    const int c = threadIdx.x + it * kStThreads;
+    if (c < nch) {
+      if (KIND == 1) {
+        const u32x4 v = *(const u32x4*)(A.acc_in + 4 * c);
+        I.a[it][0] = v.x; I.a[it][1] = v.y; I.a[it][2] = v.z; I.a[it][3] = v.w;
+      } else {
+        const uint16_t* src = KIND == 0 ? A.x0 : (KIND == 2 ? A.q : A.gate);
+        I.a[it][0] = *(const uint32_t*)(src + 4 * c);
+        I.a[it][1] = *(const uint32_t*)(src + 4 * c + 2);
+        if (KIND == 3) {
+          I.b[it][0] = *(const uint32_t*)(A.up + 4 * c);
+          I.b[it][1] = *(const uint32_t*)(A.up + 4 * c + 2);
+        }
+      }
+    }
+  }
+}
+
+template <int KIND>
+__device__ __forceinline__ float st_in_value(const StIn& I, int it, int i) {
+  if (KIND == 1) return st_bf16(st_to_bf16(__uint_as_float(I.a[it][i])));
+  const uint32_t w = I.a[it][i >> 1];
+  const float v = (i & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+  if (KIND != 3) return v;
+  const uint32_t u = I.b[it][i >> 1];
+  return v * ((i & 1) ? __uint_as_float(u & 0xFFFF0000u) : __uint_as_float(u << 16));
+}
+
+template <int KIND>
+__device__ float st_block_sumsq(const StIn& I, int nch, StLds& L) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float ss = 0.f;
+#pragma unroll
+  for (int it = 0; it < kStInIters; ++it) {
+    if (tid + it * kStThreads < nch) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float h = st_in_value<KIND>(I, it, i);
+        ss = fmaf(h, h, ss);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  if (lane == 0) L.ssum[wave] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int v = 0; v < kStWaves; ++v) tot += L.ssum[v];
+  return tot;
+}
+
+// Tables of chunks [c0, c1) (table entry block c - c0), from the loaded registers; the
+// (rescaled) bf16 inputs of those chunks are also written to `out` when it is set.
+template <int KIND>
+__device__ void st_build_tables(const StIn& I, int c0, int c1, float denom, bool rescale,
+                                uint16_t* out, StLds& L) {
+#pragma unroll
+  for (int it = 0; it < kStInIters; ++it) {
+    const int c = threadIdx.x + it * kStThreads;
+    if (c < c0 || c >= c1) continue;
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float h = st_in_value<KIND>(I, it, i);
+      if (rescale) {
+        const uint16_t b = st_to_bf16(h / denom);
+        if (out) out[4 * c + i] = b;
+        h = st_bf16(b);
+      } else if (out) {
+        out[4 * c + i] = st_to_bf16(h);
+      }
+      v[i] = h;
+    }
+    const float p0 = -v[0] - v[1], p1 = v[0] - v[1], p2 = v[1] - v[0], p3 = v[0] + v[1];
+    const float q0 = -v[2] - v[3], q1 = v[2] - v[3], q2 = v[3] - v[2], q3 = v[2] + v[3];
+    float4* dst = (float4*)(L.lut + (c - c0) * 16);
+    dst[0] = make_float4(p0 + q0, p1 + q0, p2 + q0, p3 + q0);
+    dst[1] = make_float4(p0 + q1, p1 + q1, p2 + q1, p3 + q1);
+    dst[2] = make_float4(p0 + q2, p1 + q2, p2 + q2, p3 + q2);
+    dst[3] = make_float4(p0 + q3, p1 + q3, p2 + q3, p3 + q3);
+  }
+}
+
+// A work item: tile `tile` of matrix `m`, groups [ga, gb) of its rows; table chunk 0 is the
+// first input of group ga.
+struct StItem {
+  int m, tile, ga, gb;
+};
+
+template <int MG>
+struct StRegs {
+  u32x4 rec[MG];
+  uint32_t sc[MG];
+};
+
+template <int MG>
+__device__ __forceinline__ void st_load(const StArgs& A, const StItem& it, int wave, int lane,
+                                        StRegs<MG>& R) {
+  const StMat& M = A.mats[it.m];
+  const uint8_t* tb = M.w + (size_t)it.tile * M.tile_bytes;
+#pragma unroll
+  for (int i = 0; i < MG; ++i) {
+    const int g = it.ga + wave + kStWaves * i;
+    if (g < it.gb) {
+      const uint8_t* sb = tb + (size_t)(g / kSuper) * kStSuperBytes;
+      R.rec[i] = __builtin_nontemporal_load((const u32x4*)(sb + kBlock * (1 + g % kSuper) + lane * 16));
+      R.sc[i] = *(const uint16_t*)(sb + lane * 16 + (g % kSuper) * 2);
+    }
+  }
+}
+
+template <int MG>
+__device__ __forceinline__ float st_compute(const StItem& it, int wave, const StRegs<MG>& R,
+                                            const StLds& L) {
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < MG; ++i) {
+    const int g = it.ga + wave + kStWaves * i;
+    if (g >= it.gb) break;
+    uint32_t s4[4] = {R.rec[i].x, R.rec[i].y, R.rec[i].z, R.rec[i].w};
+    // keep one group's lookups together (hoisting all of them costs many registers)
+    asm volatile("" : "+v"(s4[0]), "+v"(s4[1]), "+v"(s4[2]), "+v"(s4[3]));
+    const char* lb = (const char*)L.lut + (size_t)(g - it.ga) * 32 * 64;
+    float pa = 0.f, pb = 0.f;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t s = s4[d];
+      const uint32_t r = __builtin_amdgcn_alignbit(s, s, 4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        pa += *(const float*)(lb + (8 * d + 2 * q) * 64 + st_field(s, q));
+        pb += *(const float*)(lb + (8 * d + 2 * q + 1) * 64 + st_field(r, q));
+      }
+    }
+    acc = fmaf(st_f16(R.sc[i]), pa + pb, acc);
+  }
+  return acc;
+}
+
+// The idx-th item of this workgroup (stage 1: tiles blockIdx.x + idx * gridDim.x over the five
+// matrices in order; stage 2: one item per workgroup). Returns false past the last.
+__device__ bool st_item(const StArgs& A, int idx, StItem& it) {
+  if (A.stage == 1) {
+    int t = blockIdx.x + idx * gridDim.x;
+    for (int m = 0; m < A.nmats; ++m) {
+      if (t < A.mats[m].tiles) {
+        it.m = m;
+        it.tile = t;
+        it.ga = 0;
+        it.gb = A.mats[m].groups;
+        return true;
+      }
+      t -= A.mats[m].tiles;
+    }
+    return false;
+  }
+  if (idx > 0) return false;
+  const int b = blockIdx.x;
+  if (b < A.mats[0].tiles) {
+    it.m = 0;
+    it.tile = b;
+    it.ga = 0;
+    it.gb = A.mats[0].groups;
+    return true;
+  }
+  const int d = b - A.mats[0].tiles;
+  if (d >= 2 * A.mats[1].tiles) return false;
+  it.m = 1;
+  it.tile = d >> 1;
+  const int split = A.down_split_sg * kSuper;
+  it.ga = (d & 1) ? split : 0;
+  it.gb = (d & 1) ? A.mats[1].groups : split;
+  return true;
+}
+
+// The prologue and every tile of one input kind. Loads are issued in order of need: the input
+// vector first (latency-critical), then the weights of every item of the workgroup.
+template <int KIND, int MI, int MG>
+__device__ void st_run(const StArgs& A, int n_in, int c0, int c1, bool rescale, uint16_t* out,
+                       int nitems, const StItem (&items)[kStMaxItems], StLds& L) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  StIn I;
+  st_in_load<KIND>(A, n_in / 4, I);
+  StRegs<MG> R[MI];
+#pragma unroll
+  for (int t = 0; t < MI; ++t)
+    if (t < nitems) st_load<MG>(A, items[t], wave, lane, R[t]);
+  float denom = 1.f;
+  if (rescale) denom = sqrtf(st_block_sumsq<KIND>(I, n_in / 4, L) / (float)n_in + A.eps);
+  st_build_tables<KIND>(I, c0, c1, denom, rescale, out, L);
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < MI; ++t) {
+    if (t >= nitems) break;
+    const float part = st_compute<MG>(items[t], wave, R[t], L);
+    L.red[wave][lane] = part;
+    __syncthreads();
+    if (wave == 0) {
+      float sum = L.red[0][lane];
+#pragma unroll
+      for (int v = 1; v < kStWaves; ++v) sum += L.red[v][lane];
+      const StMat& M = A.mats[items[t].m];
+      const int row = items[t].tile * kTileRows + lane;
+      if (row < M.n) {
+        if (M.acc) atomicAdd(M.acc + row, sum);
+        else M.y[row] = st_to_bf16(sum);
+      }
+    }
+    __syncthreads();   // red is free again
+  }
+}
+
+template <int MI, int MG>
+__global__ __launch_bounds__(kStThreads) void stage_kernel(StArgs A) {
+  __shared__ StLds L;
+  const int tid = threadIdx.x;
+  StItem items[kStMaxItems];
+  int nitems = 0;
+#pragma unroll
+  for (int t = 0; t < MI; ++t)
+    if (nitems == t && st_item(A, t, items[t])) nitems = t + 1;
+
+  // the input of this workgroup's items and the range of chunks its tables cover
+  int kind, n_in, c0 = 0, c1;
+  uint16_t* out = nullptr;
+  bool rescale = true;
+  if (A.stage == 1) {
+    kind = A.x0 ? 0 : 1;
+    n_in = A.hidden;
+    c1 = A.hidden / 4;
+    rescale = kind == 1;
+    if (blockIdx.x == 0) {
+      out = A.x_out;
+      if (kind == 1)
+        for (int j = tid; j < A.hidden; j += kStThreads) A.down_out[j] = st_to_bf16(A.acc_in[j]);
+      if (A.acc_zero)
+        for (int j = tid; j < A.hidden; j += kStThreads) A.acc_zero[j] = 0.f;
+    }
+  } else if (nitems == 0 || items[0].m == 0) {
+    kind = 2;
+    n_in = A.hidden;
+    c1 = A.hidden / 4;
+    if (blockIdx.x == 0) out = A.xo_out;
+  } else {
+    kind = 3;
+    n_in = A.ffn;
+    c0 = items[0].ga * kGroup / 4;
+    c1 = items[0].gb * kGroup / 4;
+    if (items[0].tile == 0) out = A.xd_out;   // each half writes its own inputs
+  }
+  if (MI > 1) {   // stage 1
+    if (kind == 0) st_run<0, MI, MG>(A, n_in, c0, c1, rescale, out, nitems, items, L);
+    else st_run<1, MI, MG>(A, n_in, c0, c1, rescale, out, nitems, items, L);
+  } else {
+    if (kind == 2) st_run<2, MI, MG>(A, n_in, c0, c1, rescale, out, nitems, items, L);
+    else st_run<3, MI, MG>(A, n_in, c0, c1, rescale, out, nitems, items, L);
+  }
+}
+
+// two fp32 accumulators of `hidden` floats per device, allocated once, never freed
+constexpr int kStMaxDevices = 64;
+struct StWork {
+  float* acc = nullptr;
+  size_t floats = 0;
+};
+StWork g_st_work[kStMaxDevices];
+std::mutex g_st_mu;
+
+lbq_status st_workspace(int hidden, hipStream_t s, float** acc) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kStMaxDevices) return LBQ_E_DEVICE;
+  std::lock_guard<std::mutex> lock(g_st_mu);
+  StWork& W = g_st_work[dev];
+  const size_t need = 2 * (size_t)hidden;
+  if (W.floats < need) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) return LBQ_E_DEVICE;
+    if (cs != hipStreamCaptureStatusNone) return LBQ_E_NOMEM;
+    void* p = nullptr;
+    if (hipMalloc(&p, need * sizeof(float)) != hipSuccess) return LBQ_E_NOMEM;
+    // the previous buffer may still be in use by queued work: it is kept, not freed
+    W.acc = (float*)p;
+    W.floats = need;
+  }
+  *acc = W.acc;
+  return LBQ_OK;
+}
+
+StMat st_mat(const void* w, int n, int k, uint16_t* y, float* acc) {
+  Geometry g;
+  make_geometry(n, k, kQ1GroupBlocks, &g);
+  StMat m;
+  m.w = (const uint8_t*)w;
+  m.y = y;
+  m.acc = acc;
+  m.n = n;
+  m.tiles = (int)g.tiles;
+  m.groups = (int)g.groups;
+  m.tile_bytes = g.tile_bytes;
+  return m;
+}
+
+}  // namespace
+
+// Batch-1 decode step through the stage kernels. Shapes are validated by the caller; returns
+// LBQ_E_UNSUPPORTED where the stage kernels do not apply.
+lbq_status lbq::stage_decode_q1(const lbq_q1_layer* layers, int n_layers, int hidden, int kv,
+                                int ffn, const uint16_t* d_x0, uint16_t* d_act, float eps,
+                                void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (hidden % kGroup || kv % kGroup || ffn % kGroup) return LBQ_E_UNSUPPORTED;
+  const int hg = hidden / kGroup, fg = ffn / kGroup;
+  if (hg > kStWaves * kSt1G || hidden / 4 > kStMaxChunks) return LBQ_E_UNSUPPORTED;
+  if (hidden > 4 * kStInIters * kStThreads || ffn > 4 * kStInIters * kStThreads)
+    return LBQ_E_UNSUPPORTED;
+  const int fsg = (fg + kSuper - 1) / kSuper, split = (fsg + 1) / 2;
+  const int half0 = split * kSuper, half1 = fg - half0;
+  if (half0 > kStWaves * kSt2G || half1 > kStWaves * kSt2G || half0 * kGroup / 4 > kStMaxChunks)
+    return LBQ_E_UNSUPPORTED;
+  float* acc = nullptr;
+  const lbq_status ws = st_workspace(hidden, s, &acc);
+  if (ws != LBQ_OK) return ws;
+  int cus = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return LBQ_E_DEVICE;
+  auto at = [&](int layer, int slot) {
+    return d_act + lbq_decode_act_offset(layer, slot, n_layers, hidden, kv, ffn, 1);
+  };
+  for (int l = 0; l <= n_layers; ++l) {
+    float* acc_prev = acc + (size_t)((l + 1) % 2) * hidden;   // filled by stage 2 of layer l - 1
+    float* acc_cur = acc + (size_t)(l % 2) * hidden;
+    StArgs A;
+    memset(&A, 0, sizeof(A));
+    A.stage = 1;
+    A.hidden = hidden;
+    A.ffn = ffn;
+    A.eps = eps;
+    A.x0 = l == 0 ? d_x0 : nullptr;
+    A.acc_in = l == 0 ? nullptr : acc_prev;
+    A.down_out = l == 0 ? nullptr : at(l - 1, LBQ_ACT_DOWN);
+    A.x_out = l < n_layers ? at(l, LBQ_ACT_X)
+                           : d_act + lbq_decode_act_offset(n_layers, LBQ_ACT_NSLOTS, n_layers,
+                                                           hidden, kv, ffn, 1);
+    int tiles = 0;
+    if (l < n_layers) {
+      const lbq_q1_layer& Ly = layers[l];
+      A.acc_zero = acc_cur;
+      A.mats[0] = st_mat(Ly.q, hidden, hidden, at(l, LBQ_ACT_Q), nullptr);
+      A.mats[1] = st_mat(Ly.k, kv, hidden, at(l, LBQ_ACT_K), nullptr);
+      A.mats[2] = st_mat(Ly.v, kv, hidden, at(l, LBQ_ACT_V), nullptr);
+      A.mats[3] = st_mat(Ly.gate, ffn, hidden, at(l, LBQ_ACT_GATE), nullptr);
+      A.mats[4] = st_mat(Ly.up, ffn, hidden, at(l, LBQ_ACT_UP), nullptr);
+      A.nmats = 5;
+      for (int m = 0; m < 5; ++m) tiles += A.mats[m].tiles;
+    }
+    // at most kStMaxItems tiles per workgroup, at least one workgroup per compute unit
+    int grid1 = (tiles + kStMaxItems - 1) / kStMaxItems;
+    if (grid1 < cus) grid1 = cus;
+    if (grid1 > tiles) grid1 = tiles;
+    if (l == n_layers) grid1 = 1;
+    hipLaunchKernelGGL((stage_kernel<kSt1Items, kSt1G>), dim3(grid1), dim3(kStThreads), 0, s, A);
+    if (l == n_layers) break;
+
+    const lbq_q1_layer& Ly = layers[l];
+    StArgs B;
+    memset(&B, 0, sizeof(B));
+    B.stage = 2;
+    B.hidden = hidden;
+    B.ffn = ffn;
+    B.eps = eps;
+    B.q = at(l, LBQ_ACT_Q);
+    B.gate = at(l, LBQ_ACT_GATE);
+    B.up = at(l, LBQ_ACT_UP);
+    B.xo_out = at(l, LBQ_ACT_XO);
+    B.xd_out = at(l, LBQ_ACT_XD);
+    B.down_split_sg = split;
+    B.mats[0] = st_mat(Ly.o, hidden, hidden, at(l, LBQ_ACT_O), nullptr);
+    B.mats[1] = st_mat(Ly.down, hidden, ffn, nullptr, acc_cur);
+    B.nmats = 2;
+    const int grid2 = B.mats[0].tiles + 2 * B.mats[1].tiles;
+    hipLaunchKernelGGL((stage_kernel<1, kSt2G>), dim3(grid2), dim3(kStThreads), 0, s, B);
+  }
+  return hipGetLastError() == hipSuccess ? LBQ_OK : LBQ_E_DEVICE;
+}
