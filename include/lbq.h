@@ -347,7 +347,9 @@ lbq_status lbq_decode_step_q1g128(const lbq_q1_layer* layers, int32_t n_layers, 
  * workgroups (an fp32 accumulator of 2 x hidden floats per device is the library's workspace).
  * Batch-1 Q1_0_g128 GEMVs run as one persistent launch (one workgroup per compute unit) whose
  * workgroups exchange partial sums through tagged words in a library-owned device workspace;
- * every wait inside such a launch is bounded. Such a launch
+ * every wait inside such a launch is bounded. Such a launch is never recorded into a HIP graph:
+ * while the stream is being captured, batch-1 Q1 GEMVs use the per-call kernels instead (same
+ * results within the float tolerance). Such a launch
  * expects the device to itself: should another kernel hold compute units meanwhile, its waits
  * time out instead of hanging. This call synchronises `stream` and returns LBQ_E_DEVICE if a
  * launch on the current device gave up waiting (its outputs are then invalid), LBQ_OK

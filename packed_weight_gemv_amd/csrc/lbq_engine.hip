@@ -1248,8 +1248,17 @@ using namespace lbq;
 
 // Single batch-1 Q1 GEMV through the engine. Returns LBQ_E_UNSUPPORTED when the shape does not
 // suit it (the caller then uses the per-call kernels).
+// A launch of the engine cannot be captured: its program upload copies from host memory that
+// is reused by later calls, and each launch carries a fresh epoch. While `stream` is being
+// captured the engine declines (the callers then use their per-call kernels).
+static bool eng_capturing(hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone;
+}
+
 lbq_status lbq_engine_gemv_q1(const void* d_w, int32_t n, int32_t k, const uint16_t* d_x,
                               uint16_t* d_y, hipStream_t stream) {
+  if (eng_capturing(stream)) return LBQ_E_UNSUPPORTED;
   std::lock_guard<std::mutex> lock(g_eng_mutex);
   int dev;
   EngDevice* E;
@@ -1290,6 +1299,7 @@ lbq_status lbq_engine_gemv_q1(const void* d_w, int32_t n, int32_t k, const uint1
 lbq_status lbq_engine_decode_q1(const lbq_q1_layer* layers, int32_t L, int32_t hidden, int32_t kv,
                                 int32_t ffn, const uint16_t* d_x0, uint16_t* d_act, float eps,
                                 hipStream_t stream) {
+  if (eng_capturing(stream)) return LBQ_E_UNSUPPORTED;
   std::lock_guard<std::mutex> lock(g_eng_mutex);
   int dev;
   EngDevice* E;

@@ -878,15 +878,14 @@ static lbq_status gemv_common(Fmt fmt, const void* d_w, int32_t n, int32_t k,
   if (overlaps(d_y, yb, d_x, (size_t)batch * k * 2) || overlaps(d_y, yb, d_w, layout_bytes(g)))
     return LBQ_E_ALIAS;
   hipStream_t s = (hipStream_t)stream;
-  if (fmt == Fmt::Q1 && batch == 1) {
-    const lbq_status st = lbq_engine_gemv_q1(d_w, n, k, d_x, d_y, s);
-    if (st != LBQ_E_UNSUPPORTED) return st;
-  }
   // two or more vectors: the matrix-core product (it needs 16-byte aligned rows of x; other
   // alignments take the per-row lookup kernels below)
   if (batch >= 2 && (uintptr_t)d_x % 16 == 0)
     return fmt == Fmt::Q1 ? lbq_gemm_q1g128(d_w, n, k, d_x, d_y, batch, stream)
                           : lbq_gemm_i4g128(d_w, n, k, d_x, d_y, batch, stream);
+  // the per-call kernels' split-K workspace, reserved even when the persistent engine takes a
+  // batch-1 Q1 call: a later captured call of the same shape falls back to these kernels and
+  // cannot allocate
   unsigned* counters = nullptr;
   float* partials = nullptr;
   if (g.supers > 1) {
@@ -894,6 +893,10 @@ static lbq_status gemv_common(Fmt fmt, const void* d_w, int32_t n, int32_t k,
     lbq_status st = get_workspace((size_t)batch * g.supers * g.np * sizeof(float), s, &counters,
                                   &partials);
     if (st != LBQ_OK) return st;
+  }
+  if (fmt == Fmt::Q1 && batch == 1) {
+    const lbq_status st = lbq_engine_gemv_q1(d_w, n, k, d_x, d_y, s);
+    if (st != LBQ_E_UNSUPPORTED) return st;
   }
   const dim3 grid((unsigned)g.tiles, (unsigned)g.supers);
   const int nbp = batch <= 1 ? 1 : (batch <= 2 ? 2 : 4);
