@@ -43,11 +43,17 @@ constexpr int kStMaxItems = kSt1Items;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float st_bf16(uint32_t v) { return __uint_as_float(v << 16); }
+// float -> bf16 bits with the hardware conversion (round to nearest even; the kernels keep fp32
+// denormals, so tiny values round to bf16 subnormals as the software rounding would)
 __device__ __forceinline__ uint16_t st_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+// h / d from y = RN(1 / d) with one residual correction (Markstein): the residual h - q d is
+// exact in an fma, and q + r y rounds to the quotient IEEE division would give.
+__device__ __forceinline__ float st_div(float h, float d, float y) {
+  const float q = h * y;
+  const float r = fmaf(-q, d, h);
+  return fmaf(r, y, q);
 }
 __device__ __forceinline__ float st_f16(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
@@ -177,6 +183,7 @@ __device__ float st_block_sumsq(const StIn& I, int nch, StLds& L) {
 template <int KIND>
 __device__ void st_build_tables(const StIn& I, int c0, int c1, float denom, bool rescale,
                                 uint16_t* out, StLds& L) {
+  const float rden = 1.f / denom;
 #pragma unroll
   for (int it = 0; it < kStInIters; ++it) {
     const int c = threadIdx.x + it * kStThreads;
@@ -186,7 +193,7 @@ __device__ void st_build_tables(const StIn& I, int c0, int c1, float denom, bool
     for (int i = 0; i < 4; ++i) {
       float h = st_in_value<KIND>(I, it, i);
       if (rescale) {
-        const uint16_t b = st_to_bf16(h / denom);
+        const uint16_t b = st_to_bf16(st_div(h, denom, rden));
         if (out) out[4 * c + i] = b;
         h = st_bf16(b);
       } else if (out) {
@@ -221,14 +228,14 @@ __device__ __forceinline__ void st_load(const StArgs& A, const StItem& it, int w
                                         StRegs<MG>& R) {
   const StMat& M = A.mats[it.m];
   const uint8_t* tb = M.w + (size_t)it.tile * M.tile_bytes;
+  // every slot is loaded (a slot past the item's last group reloads that group and is skipped
+  // by the compute): a wave issues exactly 2 * MG loads per item, with no branch around them
 #pragma unroll
   for (int i = 0; i < MG; ++i) {
-    const int g = it.ga + wave + kStWaves * i;
-    if (g < it.gb) {
-      const uint8_t* sb = tb + (size_t)(g / kSuper) * kStSuperBytes;
-      R.rec[i] = __builtin_nontemporal_load((const u32x4*)(sb + kBlock * (1 + g % kSuper) + lane * 16));
-      R.sc[i] = *(const uint16_t*)(sb + lane * 16 + (g % kSuper) * 2);
-    }
+    const int g = min(it.ga + wave + kStWaves * i, it.gb - 1);
+    const uint8_t* sb = tb + (size_t)(g / kSuper) * kStSuperBytes;
+    R.rec[i] = __builtin_nontemporal_load((const u32x4*)(sb + kBlock * (1 + g % kSuper) + lane * 16));
+    R.sc[i] = *(const uint16_t*)(sb + lane * 16 + (g % kSuper) * 2);
   }
 }
 
@@ -241,8 +248,10 @@ __device__ __forceinline__ float st_compute(const StItem& it, int wave, const St
     const int g = it.ga + wave + kStWaves * i;
     if (g >= it.gb) break;
     uint32_t s4[4] = {R.rec[i].x, R.rec[i].y, R.rec[i].z, R.rec[i].w};
-    // keep one group's lookups together (hoisting all of them costs many registers)
-    asm volatile("" : "+v"(s4[0]), "+v"(s4[1]), "+v"(s4[2]), "+v"(s4[3]));
+    uint32_t sc = R.sc[i];
+    // keep one group's lookups together (hoisting all of them costs many registers), and keep
+    // the scale's conversion here: placed beside its load it would wait for the load at once
+    asm volatile("" : "+v"(s4[0]), "+v"(s4[1]), "+v"(s4[2]), "+v"(s4[3]), "+v"(sc));
     const char* lb = (const char*)L.lut + (size_t)(g - it.ga) * 32 * 64;
     float pa = 0.f, pb = 0.f;
 #pragma unroll
@@ -255,14 +264,14 @@ __device__ __forceinline__ float st_compute(const StItem& it, int wave, const St
         pb += *(const float*)(lb + (8 * d + 2 * q + 1) * 64 + st_field(r, q));
       }
     }
-    acc = fmaf(st_f16(R.sc[i]), pa + pb, acc);
+    acc = fmaf(st_f16(sc), pa + pb, acc);
   }
   return acc;
 }
 
 // The idx-th item of this workgroup (stage 1: tiles blockIdx.x + idx * gridDim.x over the five
 // matrices in order; stage 2: one item per workgroup). Returns false past the last.
-__device__ bool st_item(const StArgs& A, int idx, StItem& it) {
+__device__ bool st_item_raw(const StArgs& A, int idx, StItem& it) {
   if (A.stage == 1) {
     int t = blockIdx.x + idx * gridDim.x;
     for (int m = 0; m < A.nmats; ++m) {
@@ -290,7 +299,9 @@ __device__ bool st_item(const StArgs& A, int idx, StItem& it) {
   if (d >= 2 * A.mats[1].tiles) return false;
   it.m = 1;
   it.tile = d >> 1;
-  const int split = A.down_split_sg * kSuper;
+  // the first half ends at a super-group boundary, or at the last group when down has fewer
+  // groups than one super-group (the second half is then empty)
+  const int split = min(A.down_split_sg * kSuper, A.mats[1].groups);
   it.ga = (d & 1) ? split : 0;
   it.gb = (d & 1) ? A.mats[1].groups : split;
   return true;
@@ -298,12 +309,25 @@ __device__ bool st_item(const StArgs& A, int idx, StItem& it) {
 
 // The prologue and every tile of one input kind. Loads are issued in order of need: the input
 // vector first (latency-critical), then the weights of every item of the workgroup.
+// The same with every field pinned to a scalar register (an item is the same for every lane; a
+// per-lane matrix index would turn each read of the matrix record into a vector memory load).
+__device__ __forceinline__ bool st_item(const StArgs& A, int idx, StItem& it) {
+  const bool ok = st_item_raw(A, idx, it);
+  it.m = __builtin_amdgcn_readfirstlane(it.m);
+  it.tile = __builtin_amdgcn_readfirstlane(it.tile);
+  it.ga = __builtin_amdgcn_readfirstlane(it.ga);
+  it.gb = __builtin_amdgcn_readfirstlane(it.gb);
+  return __builtin_amdgcn_readfirstlane((int)ok) != 0;
+}
+
 template <int KIND, int MI, int MG>
 __device__ void st_run(const StArgs& A, int n_in, int c0, int c1, bool rescale, uint16_t* out,
                        int nitems, const StItem (&items)[kStMaxItems], StLds& L) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   StIn I;
   st_in_load<KIND>(A, n_in / 4, I);
+  // the input first (a compiler-visible vmcnt(0)): queued behind the weights it would arrive late
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   StRegs<MG> R[MI];
 #pragma unroll
   for (int t = 0; t < MI; ++t)
@@ -333,6 +357,117 @@ __device__ void st_run(const StArgs& A, int n_in, int c0, int c1, bool rescale, 
   }
 }
 
+// Copies 16 bytes per lane from base + voff straight into LDS at lds + 16 * lane (the copy
+// bypasses the registers; a wave waits for it with s_waitcnt vmcnt, see st_wait_vm).
+__device__ __forceinline__ void st_dma16(const void* base, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved) : "s"(lds), "v"(voff), "s"(base) : "memory");
+}
+// Waits until at most N of this wave's vector memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void st_wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Kinds 1 (stage 1 after layer 0: the fp32 down accumulator) and 2 (stage 2, o: bf16 q), for a
+// workgroup with exactly NI items. A wave issues its loads in order and stalls at issue once the
+// memory pipeline is full, so work placed behind a long run of weight loads waits for the
+// weights. Hence the order: the input vector is copied into LDS (behind the tables, with copies
+// that bypass the registers) and waited for; item 0's weights are issued; the sum of squares,
+// the rescale and the tables are formed from LDS while they stream; then item t + 1's weights
+// are issued just before item t is computed. NI is a template argument so that every load is
+// unconditional: a load under a run-time branch makes the compiler wait for it at the merge.
+template <int KIND, int NI, int MG>
+__device__ void st_run_lds_n(const StArgs& A, int n_in, uint16_t* out, uint16_t* raw_out,
+                             const StItem (&items)[kStMaxItems], StLds& L) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nch = n_in / 4;
+  char* inb = (char*)L.lut + (size_t)nch * 64;   // right after the tables
+  const void* src = KIND == 1 ? (const void*)A.acc_in : (const void*)A.q;
+  const uint32_t nbytes = (uint32_t)n_in * (KIND == 1 ? 4u : 2u);
+  const uint32_t ninst = (nbytes + 1023u) / 1024u;
+  for (uint32_t i = wave; i < ninst; i += kStWaves) {
+    const uint32_t voff = i * 1024u + lane * 16u;
+    const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)inb + i * 1024u);
+    if (voff < nbytes) st_dma16(src, voff, dst);
+  }
+  st_wait_vm<0>();
+  __syncthreads();
+  StRegs<MG> R[NI > 0 ? NI : 1];
+  if (NI > 0) st_load<MG>(A, items[0], wave, lane, R[0]);
+  auto val = [&](int j) -> float {
+    if (KIND == 1) return st_bf16(st_to_bf16(((const float*)inb)[j]));
+    return st_bf16(((const uint16_t*)inb)[j]);
+  };
+  float ss = 0.f;
+  for (int j = tid; j < n_in; j += kStThreads) {
+    const float h = val(j);
+    ss = fmaf(h, h, ss);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  if (lane == 0) L.ssum[wave] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int v = 0; v < kStWaves; ++v) tot += L.ssum[v];
+  const float denom = sqrtf(tot / (float)n_in + A.eps);
+  const float rden = 1.f / denom;
+  for (int c = tid; c < nch; c += kStThreads) {
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float h = val(4 * c + i);
+      if (raw_out) raw_out[4 * c + i] = st_to_bf16(h);   // h is a bf16 value already
+      const uint16_t b = st_to_bf16(st_div(h, denom, rden));
+      if (out) out[4 * c + i] = b;
+      v[i] = st_bf16(b);
+    }
+    const float p0 = -v[0] - v[1], p1 = v[0] - v[1], p2 = v[1] - v[0], p3 = v[0] + v[1];
+    const float q0 = -v[2] - v[3], q1 = v[2] - v[3], q2 = v[3] - v[2], q3 = v[2] + v[3];
+    float4* dst = (float4*)(L.lut + c * 16);
+    dst[0] = make_float4(p0 + q0, p1 + q0, p2 + q0, p3 + q0);
+    dst[1] = make_float4(p0 + q1, p1 + q1, p2 + q1, p3 + q1);
+    dst[2] = make_float4(p0 + q2, p1 + q2, p2 + q2, p3 + q2);
+    dst[3] = make_float4(p0 + q3, p1 + q3, p2 + q3, p3 + q3);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < NI; ++t) {
+    if (t + 1 < NI) st_load<MG>(A, items[t + 1], wave, lane, R[t + 1]);
+    const float part = st_compute<MG>(items[t], wave, R[t], L);
+    L.red[wave][lane] = part;
+    __syncthreads();
+    if (wave == 0) {
+      float sum = L.red[0][lane];
+#pragma unroll
+      for (int v = 1; v < kStWaves; ++v) sum += L.red[v][lane];
+      const StMat& M = A.mats[items[t].m];
+      const int row = items[t].tile * kTileRows + lane;
+      if (row < M.n) {
+        if (M.acc) atomicAdd(M.acc + row, sum);
+        else M.y[row] = st_to_bf16(sum);
+      }
+    }
+    __syncthreads();   // red is free again
+  }
+}
+
+template <int KIND, int MI, int MG>
+__device__ void st_run_lds(const StArgs& A, int n_in, uint16_t* out, uint16_t* raw_out,
+                           int nitems, const StItem (&items)[kStMaxItems], StLds& L) {
+  // vmcnt(0), seen by the compiler: where other code paths merge in front of this one, loads it
+  // believes are still pending would otherwise make it wait for weights issued later
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  if (nitems <= 0) st_run_lds_n<KIND, 0, MG>(A, n_in, out, raw_out, items, L);
+  else if (MI == 1 || nitems == 1) st_run_lds_n<KIND, 1, MG>(A, n_in, out, raw_out, items, L);
+  else if (MI == 2 || nitems == 2) st_run_lds_n<KIND, (MI >= 2 ? 2 : 1), MG>(A, n_in, out, raw_out, items, L);
+  else st_run_lds_n<KIND, (MI >= 3 ? 3 : 1), MG>(A, n_in, out, raw_out, items, L);
+}
+
 template <int MI, int MG>
 __global__ __launch_bounds__(kStThreads) void stage_kernel(StArgs A) {
   __shared__ StLds L;
@@ -340,8 +475,10 @@ __global__ __launch_bounds__(kStThreads) void stage_kernel(StArgs A) {
   StItem items[kStMaxItems];
   int nitems = 0;
 #pragma unroll
-  for (int t = 0; t < MI; ++t)
+  for (int t = 0; t < MI; ++t) {
     if (nitems == t && st_item(A, t, items[t])) nitems = t + 1;
+    else if (t > 0) items[t] = items[t - 1];   // a slot past the last item repeats it
+  }
 
   // the input of this workgroup's items and the range of chunks its tables cover
   int kind, n_in, c0 = 0, c1;
@@ -354,8 +491,6 @@ __global__ __launch_bounds__(kStThreads) void stage_kernel(StArgs A) {
     rescale = kind == 1;
     if (blockIdx.x == 0) {
       out = A.x_out;
-      if (kind == 1)
-        for (int j = tid; j < A.hidden; j += kStThreads) A.down_out[j] = st_to_bf16(A.acc_in[j]);
       if (A.acc_zero)
         for (int j = tid; j < A.hidden; j += kStThreads) A.acc_zero[j] = 0.f;
     }
@@ -373,9 +508,9 @@ __global__ __launch_bounds__(kStThreads) void stage_kernel(StArgs A) {
   }
   if (MI > 1) {   // stage 1
     if (kind == 0) st_run<0, MI, MG>(A, n_in, c0, c1, rescale, out, nitems, items, L);
-    else st_run<1, MI, MG>(A, n_in, c0, c1, rescale, out, nitems, items, L);
+    else st_run_lds<1, MI, MG>(A, n_in, out, blockIdx.x == 0 ? A.down_out : nullptr, nitems, items, L);
   } else {
-    if (kind == 2) st_run<2, MI, MG>(A, n_in, c0, c1, rescale, out, nitems, items, L);
+    if (kind == 2) st_run_lds<2, MI, MG>(A, n_in, out, nullptr, nitems, items, L);
     else st_run<3, MI, MG>(A, n_in, c0, c1, rescale, out, nitems, items, L);
   }
 }
@@ -432,12 +567,16 @@ lbq_status lbq::stage_decode_q1(const lbq_q1_layer* layers, int n_layers, int hi
                                 void* stream) {
   hipStream_t s = (hipStream_t)stream;
   if (hidden % kGroup || kv % kGroup || ffn % kGroup) return LBQ_E_UNSUPPORTED;
+  // the LDS copies of q need its slot 16-byte aligned (slot offsets are multiples of 256 bytes)
+  if ((uintptr_t)d_act % 16) return LBQ_E_UNSUPPORTED;
   const int hg = hidden / kGroup, fg = ffn / kGroup;
   if (hg > kStWaves * kSt1G || hidden / 4 > kStMaxChunks) return LBQ_E_UNSUPPORTED;
+  // tables (64 B per 4 inputs) plus the LDS copy of an fp32 input vector (4 B per input)
+  if ((size_t)hidden * 20 > sizeof(StLds::lut)) return LBQ_E_UNSUPPORTED;
   if (hidden > 4 * kStInIters * kStThreads || ffn > 4 * kStInIters * kStThreads)
     return LBQ_E_UNSUPPORTED;
   const int fsg = (fg + kSuper - 1) / kSuper, split = (fsg + 1) / 2;
-  const int half0 = split * kSuper, half1 = fg - half0;
+  const int half0 = std::min(split * kSuper, fg), half1 = fg - half0;
   if (half0 > kStWaves * kSt2G || half1 > kStWaves * kSt2G || half0 * kGroup / 4 > kStMaxChunks)
     return LBQ_E_UNSUPPORTED;
   float* acc = nullptr;
