@@ -223,49 +223,55 @@ struct StRegs {
   uint32_t sc[MG];
 };
 
+// Slot i of an item: group ga + wave + 16 i (a slot past the item's last group reloads that
+// group, so a wave issues exactly two loads per slot with no branch around them, and the
+// compute skips it).
+template <int MG>
+__device__ __forceinline__ void st_load_slot(const StArgs& A, const StItem& it, int wave, int lane,
+                                             StRegs<MG>& R, int i) {
+  const StMat& M = A.mats[it.m];
+  const uint8_t* tb = M.w + (size_t)it.tile * M.tile_bytes;
+  const int g = min(it.ga + wave + kStWaves * i, it.gb - 1);
+  const uint8_t* sb = tb + (size_t)(g / kSuper) * kStSuperBytes;
+  R.rec[i] = __builtin_nontemporal_load((const u32x4*)(sb + kBlock * (1 + g % kSuper) + lane * 16));
+  R.sc[i] = *(const uint16_t*)(sb + lane * 16 + (g % kSuper) * 2);
+}
 template <int MG>
 __device__ __forceinline__ void st_load(const StArgs& A, const StItem& it, int wave, int lane,
                                         StRegs<MG>& R) {
-  const StMat& M = A.mats[it.m];
-  const uint8_t* tb = M.w + (size_t)it.tile * M.tile_bytes;
-  // every slot is loaded (a slot past the item's last group reloads that group and is skipped
-  // by the compute): a wave issues exactly 2 * MG loads per item, with no branch around them
 #pragma unroll
-  for (int i = 0; i < MG; ++i) {
-    const int g = min(it.ga + wave + kStWaves * i, it.gb - 1);
-    const uint8_t* sb = tb + (size_t)(g / kSuper) * kStSuperBytes;
-    R.rec[i] = __builtin_nontemporal_load((const u32x4*)(sb + kBlock * (1 + g % kSuper) + lane * 16));
-    R.sc[i] = *(const uint16_t*)(sb + lane * 16 + (g % kSuper) * 2);
-  }
+  for (int i = 0; i < MG; ++i) st_load_slot<MG>(A, it, wave, lane, R, i);
 }
-
+template <int MG>
+__device__ __forceinline__ void st_compute_slot(const StItem& it, int wave, const StRegs<MG>& R,
+                                                const StLds& L, int i, float& acc) {
+  const int g = it.ga + wave + kStWaves * i;
+  if (g >= it.gb) return;
+  uint32_t s4[4] = {R.rec[i].x, R.rec[i].y, R.rec[i].z, R.rec[i].w};
+  uint32_t sc = R.sc[i];
+  // keep one group's lookups together (hoisting all of them costs many registers), and keep
+  // the scale's conversion here: placed beside its load it would wait for the load at once
+  asm volatile("" : "+v"(s4[0]), "+v"(s4[1]), "+v"(s4[2]), "+v"(s4[3]), "+v"(sc));
+  const char* lb = (const char*)L.lut + (size_t)(g - it.ga) * 32 * 64;
+  float pa = 0.f, pb = 0.f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t s = s4[d];
+    const uint32_t r = __builtin_amdgcn_alignbit(s, s, 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      pa += *(const float*)(lb + (8 * d + 2 * q) * 64 + st_field(s, q));
+      pb += *(const float*)(lb + (8 * d + 2 * q + 1) * 64 + st_field(r, q));
+    }
+  }
+  acc = fmaf(st_f16(sc), pa + pb, acc);
+}
 template <int MG>
 __device__ __forceinline__ float st_compute(const StItem& it, int wave, const StRegs<MG>& R,
                                             const StLds& L) {
   float acc = 0.f;
 #pragma unroll
-  for (int i = 0; i < MG; ++i) {
-    const int g = it.ga + wave + kStWaves * i;
-    if (g >= it.gb) break;
-    uint32_t s4[4] = {R.rec[i].x, R.rec[i].y, R.rec[i].z, R.rec[i].w};
-    uint32_t sc = R.sc[i];
-    // keep one group's lookups together (hoisting all of them costs many registers), and keep
-    // the scale's conversion here: placed beside its load it would wait for the load at once
-    asm volatile("" : "+v"(s4[0]), "+v"(s4[1]), "+v"(s4[2]), "+v"(s4[3]), "+v"(sc));
-    const char* lb = (const char*)L.lut + (size_t)(g - it.ga) * 32 * 64;
-    float pa = 0.f, pb = 0.f;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const uint32_t s = s4[d];
-      const uint32_t r = __builtin_amdgcn_alignbit(s, s, 4);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        pa += *(const float*)(lb + (8 * d + 2 * q) * 64 + st_field(s, q));
-        pb += *(const float*)(lb + (8 * d + 2 * q + 1) * 64 + st_field(r, q));
-      }
-    }
-    acc = fmaf(st_f16(sc), pa + pb, acc);
-  }
+  for (int i = 0; i < MG; ++i) st_compute_slot<MG>(it, wave, R, L, i, acc);
   return acc;
 }
 
@@ -397,7 +403,12 @@ __device__ void st_run_lds_n(const StArgs& A, int n_in, uint16_t* out, uint16_t*
   st_wait_vm<0>();
   __syncthreads();
   StRegs<MG> R[NI > 0 ? NI : 1];
-  if (NI > 0) st_load<MG>(A, items[0], wave, lane, R[0]);
+  // item 0's slots are issued between pieces of the prologue: a wave stalls at issue while the
+  // memory pipeline is full, and the work between issues keeps its VALU busy meanwhile
+  auto issue0 = [&](int i) {
+    if (NI > 0 && i < MG) st_load_slot<MG>(A, items[0], wave, lane, R[0], i);
+  };
+  issue0(0);
   auto val = [&](int j) -> float {
     if (KIND == 1) return st_bf16(st_to_bf16(((const float*)inb)[j]));
     return st_bf16(((const uint16_t*)inb)[j]);
@@ -409,8 +420,10 @@ __device__ void st_run_lds_n(const StArgs& A, int n_in, uint16_t* out, uint16_t*
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  issue0(1);
   if (lane == 0) L.ssum[wave] = ss;
   __syncthreads();
+  issue0(2);
   float tot = 0.f;
 #pragma unroll
   for (int v = 0; v < kStWaves; ++v) tot += L.ssum[v];
@@ -434,11 +447,18 @@ __device__ void st_run_lds_n(const StArgs& A, int n_in, uint16_t* out, uint16_t*
     dst[2] = make_float4(p0 + q2, p1 + q2, p2 + q2, p3 + q2);
     dst[3] = make_float4(p0 + q3, p1 + q3, p2 + q3, p3 + q3);
   }
+#pragma unroll
+  for (int i = 3; i < MG; ++i) issue0(i);
   __syncthreads();
 #pragma unroll
   for (int t = 0; t < NI; ++t) {
-    if (t + 1 < NI) st_load<MG>(A, items[t + 1], wave, lane, R[t + 1]);
-    const float part = st_compute<MG>(items[t], wave, R[t], L);
+    // item t + 1's slot i is issued after item t's slot i is computed
+    float part = 0.f;
+#pragma unroll
+    for (int i = 0; i < MG; ++i) {
+      st_compute_slot<MG>(items[t], wave, R[t], L, i, part);
+      if (t + 1 < NI) st_load_slot<MG>(A, items[t + 1], wave, lane, R[t + 1], i);
+    }
     L.red[wave][lane] = part;
     __syncthreads();
     if (wave == 0) {
@@ -466,6 +486,106 @@ __device__ void st_run_lds(const StArgs& A, int n_in, uint16_t* out, uint16_t* r
   else if (MI == 1 || nitems == 1) st_run_lds_n<KIND, 1, MG>(A, n_in, out, raw_out, items, L);
   else if (MI == 2 || nitems == 2) st_run_lds_n<KIND, (MI >= 2 ? 2 : 1), MG>(A, n_in, out, raw_out, items, L);
   else st_run_lds_n<KIND, (MI >= 3 ? 3 : 1), MG>(A, n_in, out, raw_out, items, L);
+}
+
+// Kind 3 (stage 2, a half of down; input rms(gate ⊙ up)). gate and up are copied whole into the
+// table area with LDS-direct loads and waited for; then the item's weights are issued. While they
+// stream, the sum of squares of h = gate ⊙ up is taken from LDS, each thread keeps h for the
+// table chunks it will build (at most 3 chunks), and after the barrier that ends every read of the
+// copies the tables of the workgroup's half are written over them.
+template <int MG, int NI>
+__device__ void st_run_down(const StArgs& A, uint16_t* out, const StItem (&items)[kStMaxItems],
+                            StLds& L) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n_in = A.ffn;
+  const uint16_t* gs = (const uint16_t*)L.lut;             // gate copy
+  const uint16_t* us = (const uint16_t*)L.lut + n_in;      // up copy
+  const uint32_t nbytes = (uint32_t)n_in * 2u;
+  const uint32_t ninst = (nbytes + 1023u) / 1024u;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)L.lut;
+  for (uint32_t i = wave; i < ninst; i += kStWaves) {
+    const uint32_t voff = i * 1024u + lane * 16u;
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + i * 1024u);
+    if (voff < nbytes) st_dma16(A.gate, voff, dst);
+  }
+  for (uint32_t i = wave; i < ninst; i += kStWaves) {
+    const uint32_t voff = i * 1024u + lane * 16u;
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + nbytes + i * 1024u);
+    if (voff < nbytes) st_dma16(A.up, voff, dst);
+  }
+  st_wait_vm<0>();
+  __syncthreads();
+  // the weight slots are issued between pieces of the prologue (a wave stalls at issue while the
+  // memory pipeline is full; the work between issues keeps its VALU busy meanwhile)
+  StRegs<MG> R;
+  auto issue = [&](int i) {
+    if (NI > 0 && i < MG) st_load_slot<MG>(A, items[0], wave, lane, R, i);
+  };
+  issue(0);
+  const int c0 = NI > 0 ? items[0].ga * kGroup / 4 : 0;
+  const int c1 = NI > 0 ? items[0].gb * kGroup / 4 : 0;
+  float ss = 0.f;
+  for (int j = tid; j < n_in; j += kStThreads) {
+    const float h = st_bf16(gs[j]) * st_bf16(us[j]);
+    ss = fmaf(h, h, ss);
+  }
+  issue(1);
+  float hv[3][4];
+#pragma unroll
+  for (int it = 0; it < 3; ++it) {
+    const int c = c0 + tid + it * kStThreads;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hv[it][i] = c < c1 ? st_bf16(gs[4 * c + i]) * st_bf16(us[4 * c + i]) : 0.f;
+  }
+  issue(2);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  if (lane == 0) L.ssum[wave] = ss;
+  __syncthreads();   // every read of the copies is done: the tables may overwrite them
+  issue(3);
+  float tot = 0.f;
+#pragma unroll
+  for (int v = 0; v < kStWaves; ++v) tot += L.ssum[v];
+  const float denom = sqrtf(tot / (float)n_in + A.eps);
+  const float rden = 1.f / denom;
+#pragma unroll
+  for (int it = 0; it < 3; ++it) {
+    if (it == 1) issue(4);
+    const int c = c0 + tid + it * kStThreads;
+    if (c >= c1) continue;
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t b = st_to_bf16(st_div(hv[it][i], denom, rden));
+      if (out) out[4 * c + i] = b;
+      v[i] = st_bf16(b);
+    }
+    const float p0 = -v[0] - v[1], p1 = v[0] - v[1], p2 = v[1] - v[0], p3 = v[0] + v[1];
+    const float q0 = -v[2] - v[3], q1 = v[2] - v[3], q2 = v[3] - v[2], q3 = v[2] + v[3];
+    float4* dst = (float4*)(L.lut + (c - c0) * 16);
+    dst[0] = make_float4(p0 + q0, p1 + q0, p2 + q0, p3 + q0);
+    dst[1] = make_float4(p0 + q1, p1 + q1, p2 + q1, p3 + q1);
+    dst[2] = make_float4(p0 + q2, p1 + q2, p2 + q2, p3 + q2);
+    dst[3] = make_float4(p0 + q3, p1 + q3, p2 + q3, p3 + q3);
+  }
+#pragma unroll
+  for (int i = 5; i < MG; ++i) issue(i);
+  __syncthreads();
+  if (NI <= 0) return;
+  const float part = st_compute<MG>(items[0], wave, R, L);
+  L.red[wave][lane] = part;
+  __syncthreads();
+  if (wave == 0) {
+    float sum = L.red[0][lane];
+#pragma unroll
+    for (int v = 1; v < kStWaves; ++v) sum += L.red[v][lane];
+    const StMat& M = A.mats[items[0].m];
+    const int row = items[0].tile * kTileRows + lane;
+    if (row < M.n) {
+      if (M.acc) atomicAdd(M.acc + row, sum);
+      else M.y[row] = st_to_bf16(sum);
+    }
+  }
 }
 
 template <int MI, int MG>
@@ -511,7 +631,8 @@ __global__ __launch_bounds__(kStThreads) void stage_kernel(StArgs A) {
     else st_run_lds<1, MI, MG>(A, n_in, out, blockIdx.x == 0 ? A.down_out : nullptr, nitems, items, L);
   } else {
     if (kind == 2) st_run_lds<2, MI, MG>(A, n_in, out, nullptr, nitems, items, L);
-    else st_run<3, MI, MG>(A, n_in, c0, c1, rescale, out, nitems, items, L);
+    else if (nitems > 0) st_run_down<MG, 1>(A, out, items, L);
+    else st_run_down<MG, 0>(A, out, items, L);
   }
 }
 
@@ -578,6 +699,10 @@ lbq_status lbq::stage_decode_q1(const lbq_q1_layer* layers, int n_layers, int hi
   const int fsg = (fg + kSuper - 1) / kSuper, split = (fsg + 1) / 2;
   const int half0 = std::min(split * kSuper, fg), half1 = fg - half0;
   if (half0 > kStWaves * kSt2G || half1 > kStWaves * kSt2G || half0 * kGroup / 4 > kStMaxChunks)
+    return LBQ_E_UNSUPPORTED;
+  // stage 2 copies gate and up (bf16) into the table area; a thread builds at most 3 chunks
+  if ((size_t)ffn * 4 > sizeof(StLds::lut) || half0 * kGroup / 4 > 3 * kStThreads ||
+      half1 * kGroup / 4 > 3 * kStThreads)
     return LBQ_E_UNSUPPORTED;
   float* acc = nullptr;
   const lbq_status ws = st_workspace(hidden, s, &acc);
