@@ -524,25 +524,49 @@ __device__ void st_run_down(const StArgs& A, uint16_t* out, const StItem (&items
   issue(0);
   const int c0 = NI > 0 ? items[0].ga * kGroup / 4 : 0;
   const int c1 = NI > 0 ? items[0].gb * kGroup / 4 : 0;
+  // sum of squares over chunks (4 inputs) in the order c0 + tid + 1024 k, wrapping at the end;
+  // the first three visits of a thread are the table chunks it builds, whose h it keeps
+  const int nch = n_in / 4;
+  auto hchunk = [&](int c, float (&h)[4]) {
+    const uint2 g = *(const uint2*)(gs + 4 * c);
+    const uint2 u = *(const uint2*)(us + 4 * c);
+    h[0] = __uint_as_float(g.x << 16) * __uint_as_float(u.x << 16);
+    h[1] = __uint_as_float(g.x & 0xFFFF0000u) * __uint_as_float(u.x & 0xFFFF0000u);
+    h[2] = __uint_as_float(g.y << 16) * __uint_as_float(u.y << 16);
+    h[3] = __uint_as_float(g.y & 0xFFFF0000u) * __uint_as_float(u.y & 0xFFFF0000u);
+  };
   float ss = 0.f;
-  for (int j = tid; j < n_in; j += kStThreads) {
-    const float h = st_bf16(gs[j]) * st_bf16(us[j]);
-    ss = fmaf(h, h, ss);
-  }
-  issue(1);
   float hv[3][4];
 #pragma unroll
-  for (int it = 0; it < 3; ++it) {
-    const int c = c0 + tid + it * kStThreads;
+  for (int k = 0; k < 3; ++k) {
+    const int t = tid + k * kStThreads;
+    float h[4] = {0.f, 0.f, 0.f, 0.f};
+    if (t < nch) {
+      const int c = c0 + t < nch ? c0 + t : c0 + t - nch;
+      hchunk(c, h);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) hv[it][i] = c < c1 ? st_bf16(gs[4 * c + i]) * st_bf16(us[4 * c + i]) : 0.f;
+      for (int i = 0; i < 4; ++i) ss = fmaf(h[i], h[i], ss);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hv[k][i] = h[i];
+    if (k == 0) issue(1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int t = tid + 3 * kStThreads; t < nch; t += kStThreads) {
+    const int c = c0 + t < nch ? c0 + t : c0 + t - nch;
+    float h[4];
+    hchunk(c, h);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ss = fmaf(h[i], h[i], ss);
   }
   issue(2);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
   if (lane == 0) L.ssum[wave] = ss;
   __syncthreads();   // every read of the copies is done: the tables may overwrite them
   issue(3);
+  __builtin_amdgcn_sched_barrier(0);
   float tot = 0.f;
 #pragma unroll
   for (int v = 0; v < kStWaves; ++v) tot += L.ssum[v];
@@ -551,6 +575,7 @@ __device__ void st_run_down(const StArgs& A, uint16_t* out, const StItem (&items
 #pragma unroll
   for (int it = 0; it < 3; ++it) {
     if (it == 1) issue(4);
+    __builtin_amdgcn_sched_barrier(0);
     const int c = c0 + tid + it * kStThreads;
     if (c >= c1) continue;
     float v[4];
