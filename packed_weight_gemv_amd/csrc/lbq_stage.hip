@@ -409,31 +409,57 @@ __device__ void st_run_lds_n(const StArgs& A, int n_in, uint16_t* out, uint16_t*
     if (NI > 0 && i < MG) st_load_slot<MG>(A, items[0], wave, lane, R[0], i);
   };
   issue0(0);
-  auto val = [&](int j) -> float {
-    if (KIND == 1) return st_bf16(st_to_bf16(((const float*)inb)[j]));
-    return st_bf16(((const uint16_t*)inb)[j]);
+  // chunks (4 inputs) tid and tid + 1024: read once (16 or 8 bytes per lane) and kept
+  auto chunk = [&](int c, float (&h)[4]) {
+    if (KIND == 1) {
+      const float4 f = *(const float4*)((const float*)inb + 4 * c);
+      h[0] = st_bf16(st_to_bf16(f.x));
+      h[1] = st_bf16(st_to_bf16(f.y));
+      h[2] = st_bf16(st_to_bf16(f.z));
+      h[3] = st_bf16(st_to_bf16(f.w));
+    } else {
+      const uint2 w = *(const uint2*)((const uint16_t*)inb + 4 * c);
+      h[0] = __uint_as_float(w.x << 16);
+      h[1] = __uint_as_float(w.x & 0xFFFF0000u);
+      h[2] = __uint_as_float(w.y << 16);
+      h[3] = __uint_as_float(w.y & 0xFFFF0000u);
+    }
   };
   float ss = 0.f;
-  for (int j = tid; j < n_in; j += kStThreads) {
-    const float h = val(j);
-    ss = fmaf(h, h, ss);
+  float hv[2][4];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int c = tid + k * kStThreads;
+    float h[4] = {0.f, 0.f, 0.f, 0.f};
+    if (c < nch) {
+      chunk(c, h);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ss = fmaf(h[i], h[i], ss);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hv[k][i] = h[i];
+    if (k == 0) issue0(1);
+    __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
-  issue0(1);
   if (lane == 0) L.ssum[wave] = ss;
   __syncthreads();
   issue0(2);
+  __builtin_amdgcn_sched_barrier(0);
   float tot = 0.f;
 #pragma unroll
   for (int v = 0; v < kStWaves; ++v) tot += L.ssum[v];
   const float denom = sqrtf(tot / (float)n_in + A.eps);
   const float rden = 1.f / denom;
-  for (int c = tid; c < nch; c += kStThreads) {
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int c = tid + k * kStThreads;
+    if (c >= nch) continue;
     float v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float h = val(4 * c + i);
+      const float h = hv[k][i];
       if (raw_out) raw_out[4 * c + i] = st_to_bf16(h);   // h is a bf16 value already
       const uint16_t b = st_to_bf16(st_div(h, denom, rden));
       if (out) out[4 * c + i] = b;
@@ -719,6 +745,7 @@ lbq_status lbq::stage_decode_q1(const lbq_q1_layer* layers, int n_layers, int hi
   if (hg > kStWaves * kSt1G || hidden / 4 > kStMaxChunks) return LBQ_E_UNSUPPORTED;
   // tables (64 B per 4 inputs) plus the LDS copy of an fp32 input vector (4 B per input)
   if ((size_t)hidden * 20 > sizeof(StLds::lut)) return LBQ_E_UNSUPPORTED;
+  if (hidden / 4 > 2 * kStThreads) return LBQ_E_UNSUPPORTED;   // two table chunks per thread
   if (hidden > 4 * kStInIters * kStThreads || ffn > 4 * kStInIters * kStThreads)
     return LBQ_E_UNSUPPORTED;
   const int fsg = (fg + kSuper - 1) / kSuper, split = (fsg + 1) / 2;
