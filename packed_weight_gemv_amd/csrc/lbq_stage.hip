@@ -84,7 +84,7 @@ struct StMat {
 };
 
 // One stage launch. Stage 1: mats[0..4] = q, k, v, gate, up over input x. Stage 2: mats[0] = o
-// over rms(q), mats[1] = down over rms(gate * up), split in two halves of its super-groups.
+// over rms(q), mats[1] = down over rms(gate * up), split in two halves of its groups.
 struct StArgs {
   StMat mats[5];
   int nmats;
@@ -103,7 +103,7 @@ struct StArgs {
   const uint16_t* up;
   uint16_t* xo_out;
   uint16_t* xd_out;
-  int down_split_sg;       // first super-group of the second half of down
+  int down_split_g;        // first group of the second half of down
 };
 
 struct StLds {
@@ -305,9 +305,7 @@ __device__ bool st_item_raw(const StArgs& A, int idx, StItem& it) {
   if (d >= 2 * A.mats[1].tiles) return false;
   it.m = 1;
   it.tile = d >> 1;
-  // the first half ends at a super-group boundary, or at the last group when down has fewer
-  // groups than one super-group (the second half is then empty)
-  const int split = min(A.down_split_sg * kSuper, A.mats[1].groups);
+  const int split = A.down_split_g;   // half of the groups, rounded up
   it.ga = (d & 1) ? split : 0;
   it.gb = (d & 1) ? A.mats[1].groups : split;
   return true;
@@ -748,8 +746,8 @@ lbq_status lbq::stage_decode_q1(const lbq_q1_layer* layers, int n_layers, int hi
   if (hidden / 4 > 2 * kStThreads) return LBQ_E_UNSUPPORTED;   // two table chunks per thread
   if (hidden > 4 * kStInIters * kStThreads || ffn > 4 * kStInIters * kStThreads)
     return LBQ_E_UNSUPPORTED;
-  const int fsg = (fg + kSuper - 1) / kSuper, split = (fsg + 1) / 2;
-  const int half0 = std::min(split * kSuper, fg), half1 = fg - half0;
+  const int split = (fg + 1) / 2;   // the halves may share a super-group's scale record
+  const int half0 = split, half1 = fg - half0;
   if (half0 > kStWaves * kSt2G || half1 > kStWaves * kSt2G || half0 * kGroup / 4 > kStMaxChunks)
     return LBQ_E_UNSUPPORTED;
   // stage 2 copies gate and up (bf16) into the table area; a thread builds at most 3 chunks
@@ -813,7 +811,7 @@ lbq_status lbq::stage_decode_q1(const lbq_q1_layer* layers, int n_layers, int hi
     B.up = at(l, LBQ_ACT_UP);
     B.xo_out = at(l, LBQ_ACT_XO);
     B.xd_out = at(l, LBQ_ACT_XD);
-    B.down_split_sg = split;
+    B.down_split_g = split;
     B.mats[0] = st_mat(Ly.o, hidden, hidden, at(l, LBQ_ACT_O), nullptr);
     B.mats[1] = st_mat(Ly.down, hidden, ffn, nullptr, acc_cur);
     B.nmats = 2;
