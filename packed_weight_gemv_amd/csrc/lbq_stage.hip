@@ -37,7 +37,6 @@ constexpr int kStThreads = 64 * kStWaves;
 constexpr int kSt1Items = 3, kSt1G = 3, kSt2G = 5;
 constexpr int kStMaxChunks = 2304;    // table capacity: 9,216 inputs (147,456 B)
 constexpr int kStSuperBytes = kBlock * (1 + kSuper * kQ1GroupBlocks);
-constexpr int kStInIters = 6;        // input chunks (4 inputs) per thread: vectors up to 24,576
 constexpr int kStMaxItems = kSt1Items;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -111,105 +110,6 @@ struct StLds {
   float red[kStWaves][64];
   float ssum[kStWaves];
 };
-
-// Input kinds: 0 = bf16 x0; 1 = bf16(fp32 accumulator); 2 = bf16 q; 3 = gate * up (exact in
-// fp32). Thread t owns the chunks c = t + i * kStThreads (inputs 4c .. 4c + 3) of the whole
-// vector: their loads are issued first, the sum of squares runs over them in a fixed order
-// (identical in every workgroup), and the tables of the workgroup's chunk range are built from
-// the same registers.
-struct StIn {
-  uint32_t a[kStInIters][4];   // raw words: bf16 pairs (kinds 0, 2, 3: a[..][0..1]) or fp32 (kind 1)
-  uint32_t b[kStInIters][2];   // up pairs (kind 3)
-};
-
-template <int KIND>
-__device__ __forceinline__ void st_in_load(const StArgs& A, int nch, StIn& I) {
-#pragma unroll
-  for (int it = 0; it < kStInIters; ++it) {
-    const int c = threadIdx.x + it * kStThreads;
-    if (c < nch) {
-      if (KIND == 1) {
-        const u32x4 v = *(const u32x4*)(A.acc_in + 4 * c);
-        I.a[it][0] = v.x; I.a[it][1] = v.y; I.a[it][2] = v.z; I.a[it][3] = v.w;
-      } else {
-        const uint16_t* src = KIND == 0 ? A.x0 : (KIND == 2 ? A.q : A.gate);
-        I.a[it][0] = *(const uint32_t*)(src + 4 * c);
-        I.a[it][1] = *(const uint32_t*)(src + 4 * c + 2);
-        if (KIND == 3) {
-          I.b[it][0] = *(const uint32_t*)(A.up + 4 * c);
-          I.b[it][1] = *(const uint32_t*)(A.up + 4 * c + 2);
-        }
-      }
-    }
-  }
-}
-
-template <int KIND>
-__device__ __forceinline__ float st_in_value(const StIn& I, int it, int i) {
-  if (KIND == 1) return st_bf16(st_to_bf16(__uint_as_float(I.a[it][i])));
-  const uint32_t w = I.a[it][i >> 1];
-  const float v = (i & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
-  if (KIND != 3) return v;
-  const uint32_t u = I.b[it][i >> 1];
-  return v * ((i & 1) ? __uint_as_float(u & 0xFFFF0000u) : __uint_as_float(u << 16));
-}
-
-template <int KIND>
-__device__ float st_block_sumsq(const StIn& I, int nch, StLds& L) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float ss = 0.f;
-#pragma unroll
-  for (int it = 0; it < kStInIters; ++it) {
-    if (tid + it * kStThreads < nch) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float h = st_in_value<KIND>(I, it, i);
-        ss = fmaf(h, h, ss);
-      }
-    }
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
-  if (lane == 0) L.ssum[wave] = ss;
-  __syncthreads();
-  float tot = 0.f;
-#pragma unroll
-  for (int v = 0; v < kStWaves; ++v) tot += L.ssum[v];
-  return tot;
-}
-
-// Tables of chunks [c0, c1) (table entry block c - c0), from the loaded registers; the
-// (rescaled) bf16 inputs of those chunks are also written to `out` when it is set.
-template <int KIND>
-__device__ void st_build_tables(const StIn& I, int c0, int c1, float denom, bool rescale,
-                                uint16_t* out, StLds& L) {
-  const float rden = 1.f / denom;
-#pragma unroll
-  for (int it = 0; it < kStInIters; ++it) {
-    const int c = threadIdx.x + it * kStThreads;
-    if (c < c0 || c >= c1) continue;
-    float v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float h = st_in_value<KIND>(I, it, i);
-      if (rescale) {
-        const uint16_t b = st_to_bf16(st_div(h, denom, rden));
-        if (out) out[4 * c + i] = b;
-        h = st_bf16(b);
-      } else if (out) {
-        out[4 * c + i] = st_to_bf16(h);
-      }
-      v[i] = h;
-    }
-    const float p0 = -v[0] - v[1], p1 = v[0] - v[1], p2 = v[1] - v[0], p3 = v[0] + v[1];
-    const float q0 = -v[2] - v[3], q1 = v[2] - v[3], q2 = v[3] - v[2], q3 = v[2] + v[3];
-    float4* dst = (float4*)(L.lut + (c - c0) * 16);
-    dst[0] = make_float4(p0 + q0, p1 + q0, p2 + q0, p3 + q0);
-    dst[1] = make_float4(p0 + q1, p1 + q1, p2 + q1, p3 + q1);
-    dst[2] = make_float4(p0 + q2, p1 + q2, p2 + q2, p3 + q2);
-    dst[3] = make_float4(p0 + q3, p1 + q3, p2 + q3, p3 + q3);
-  }
-}
 
 // A work item: tile `tile` of matrix `m`, groups [ga, gb) of its rows; table chunk 0 is the
 // first input of group ga.
@@ -324,43 +224,6 @@ __device__ __forceinline__ bool st_item(const StArgs& A, int idx, StItem& it) {
   return __builtin_amdgcn_readfirstlane((int)ok) != 0;
 }
 
-template <int KIND, int MI, int MG>
-__device__ void st_run(const StArgs& A, int n_in, int c0, int c1, bool rescale, uint16_t* out,
-                       int nitems, const StItem (&items)[kStMaxItems], StLds& L) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  StIn I;
-  st_in_load<KIND>(A, n_in / 4, I);
-  // the input first (a compiler-visible vmcnt(0)): queued behind the weights it would arrive late
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  StRegs<MG> R[MI];
-#pragma unroll
-  for (int t = 0; t < MI; ++t)
-    if (t < nitems) st_load<MG>(A, items[t], wave, lane, R[t]);
-  float denom = 1.f;
-  if (rescale) denom = sqrtf(st_block_sumsq<KIND>(I, n_in / 4, L) / (float)n_in + A.eps);
-  st_build_tables<KIND>(I, c0, c1, denom, rescale, out, L);
-  __syncthreads();
-#pragma unroll
-  for (int t = 0; t < MI; ++t) {
-    if (t >= nitems) break;
-    const float part = st_compute<MG>(items[t], wave, R[t], L);
-    L.red[wave][lane] = part;
-    __syncthreads();
-    if (wave == 0) {
-      float sum = L.red[0][lane];
-#pragma unroll
-      for (int v = 1; v < kStWaves; ++v) sum += L.red[v][lane];
-      const StMat& M = A.mats[items[t].m];
-      const int row = items[t].tile * kTileRows + lane;
-      if (row < M.n) {
-        if (M.acc) atomicAdd(M.acc + row, sum);
-        else M.y[row] = st_to_bf16(sum);
-      }
-    }
-    __syncthreads();   // red is free again
-  }
-}
-
 // Copies 16 bytes per lane from base + voff straight into LDS at lds + 16 * lane (the copy
 // bypasses the registers; a wave waits for it with s_waitcnt vmcnt, see st_wait_vm).
 __device__ __forceinline__ void st_dma16(const void* base, uint32_t voff, uint32_t lds) {
@@ -376,7 +239,8 @@ __device__ __forceinline__ void st_wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Kinds 1 (stage 1 after layer 0: the fp32 down accumulator) and 2 (stage 2, o: bf16 q), for a
+// Kinds 0 (stage 1 of layer 0: the bf16 step input, used as it is), 1 (stage 1 after layer 0:
+// rms of the fp32 down accumulator rounded to bf16) and 2 (stage 2, o: rms of bf16 q), for a
 // workgroup with exactly NI items. A wave issues its loads in order and stalls at issue once the
 // memory pipeline is full, so work placed behind a long run of weight loads waits for the
 // weights. Hence the order: the input vector is copied into LDS (behind the tables, with copies
@@ -390,7 +254,7 @@ __device__ void st_run_lds_n(const StArgs& A, int n_in, uint16_t* out, uint16_t*
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nch = n_in / 4;
   char* inb = (char*)L.lut + (size_t)nch * 64;   // right after the tables
-  const void* src = KIND == 1 ? (const void*)A.acc_in : (const void*)A.q;
+  const void* src = KIND == 1 ? (const void*)A.acc_in : KIND == 0 ? (const void*)A.x0 : (const void*)A.q;
   const uint32_t nbytes = (uint32_t)n_in * (KIND == 1 ? 4u : 2u);
   const uint32_t ninst = (nbytes + 1023u) / 1024u;
   for (uint32_t i = wave; i < ninst; i += kStWaves) {
@@ -448,7 +312,8 @@ __device__ void st_run_lds_n(const StArgs& A, int n_in, uint16_t* out, uint16_t*
   float tot = 0.f;
 #pragma unroll
   for (int v = 0; v < kStWaves; ++v) tot += L.ssum[v];
-  const float denom = sqrtf(tot / (float)n_in + A.eps);
+  // kind 0 is not rescaled: with d = y = 1 the division below returns h unchanged
+  const float denom = KIND == 0 ? 1.f : sqrtf(tot / (float)n_in + A.eps);
   const float rden = 1.f / denom;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
@@ -649,15 +514,12 @@ __global__ __launch_bounds__(kStThreads) void stage_kernel(StArgs A) {
     else if (t > 0) items[t] = items[t - 1];   // a slot past the last item repeats it
   }
 
-  // the input of this workgroup's items and the range of chunks its tables cover
-  int kind, n_in, c0 = 0, c1;
+  // the input kind of this workgroup's items and the activation slot it writes, if any
+  int kind, n_in;
   uint16_t* out = nullptr;
-  bool rescale = true;
   if (A.stage == 1) {
     kind = A.x0 ? 0 : 1;
     n_in = A.hidden;
-    c1 = A.hidden / 4;
-    rescale = kind == 1;
     if (blockIdx.x == 0) {
       out = A.x_out;
       if (A.acc_zero)
@@ -666,17 +528,14 @@ __global__ __launch_bounds__(kStThreads) void stage_kernel(StArgs A) {
   } else if (nitems == 0 || items[0].m == 0) {
     kind = 2;
     n_in = A.hidden;
-    c1 = A.hidden / 4;
     if (blockIdx.x == 0) out = A.xo_out;
   } else {
     kind = 3;
     n_in = A.ffn;
-    c0 = items[0].ga * kGroup / 4;
-    c1 = items[0].gb * kGroup / 4;
     if (items[0].tile == 0) out = A.xd_out;   // each half writes its own inputs
   }
   if (MI > 1) {   // stage 1
-    if (kind == 0) st_run<0, MI, MG>(A, n_in, c0, c1, rescale, out, nitems, items, L);
+    if (kind == 0) st_run_lds<0, MI, MG>(A, n_in, out, nullptr, nitems, items, L);
     else st_run_lds<1, MI, MG>(A, n_in, out, blockIdx.x == 0 ? A.down_out : nullptr, nitems, items, L);
   } else {
     if (kind == 2) st_run_lds<2, MI, MG>(A, n_in, out, nullptr, nitems, items, L);
@@ -738,14 +597,12 @@ lbq_status lbq::stage_decode_q1(const lbq_q1_layer* layers, int n_layers, int hi
   hipStream_t s = (hipStream_t)stream;
   if (hidden % kGroup || kv % kGroup || ffn % kGroup) return LBQ_E_UNSUPPORTED;
   // the LDS copies of q need its slot 16-byte aligned (slot offsets are multiples of 256 bytes)
-  if ((uintptr_t)d_act % 16) return LBQ_E_UNSUPPORTED;
+  if ((uintptr_t)d_act % 16 || (uintptr_t)d_x0 % 16) return LBQ_E_UNSUPPORTED;
   const int hg = hidden / kGroup, fg = ffn / kGroup;
   if (hg > kStWaves * kSt1G || hidden / 4 > kStMaxChunks) return LBQ_E_UNSUPPORTED;
   // tables (64 B per 4 inputs) plus the LDS copy of an fp32 input vector (4 B per input)
   if ((size_t)hidden * 20 > sizeof(StLds::lut)) return LBQ_E_UNSUPPORTED;
   if (hidden / 4 > 2 * kStThreads) return LBQ_E_UNSUPPORTED;   // two table chunks per thread
-  if (hidden > 4 * kStInIters * kStThreads || ffn > 4 * kStInIters * kStThreads)
-    return LBQ_E_UNSUPPORTED;
   const int split = (fg + 1) / 2;   // the halves may share a super-group's scale record
   const int half0 = split, half1 = fg - half0;
   if (half0 > kStWaves * kSt2G || half1 > kStWaves * kSt2G || half0 * kGroup / 4 > kStMaxChunks)
