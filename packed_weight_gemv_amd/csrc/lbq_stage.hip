@@ -107,7 +107,9 @@ struct StArgs {
 
 struct StLds {
   float lut[kStMaxChunks * 16];
-  float red[kStWaves][64];
+  // per-tile partial sums, double-buffered: tile t uses red[t & 1], and the barrier after tile
+  // t + 1's writes orders wave 0's reads of tile t before anyone writes red[t & 1] again
+  float red[2][kStWaves][64];
   float ssum[kStWaves];
 };
 
@@ -348,12 +350,12 @@ __device__ void st_run_lds_n(const StArgs& A, int n_in, uint16_t* out, uint16_t*
       st_compute_slot<MG>(items[t], wave, R[t], L, i, part);
       if (t + 1 < NI) st_load_slot<MG>(A, items[t + 1], wave, lane, R[t + 1], i);
     }
-    L.red[wave][lane] = part;
+    L.red[t & 1][wave][lane] = part;
     __syncthreads();
     if (wave == 0) {
-      float sum = L.red[0][lane];
+      float sum = L.red[t & 1][0][lane];
 #pragma unroll
-      for (int v = 1; v < kStWaves; ++v) sum += L.red[v][lane];
+      for (int v = 1; v < kStWaves; ++v) sum += L.red[t & 1][v][lane];
       const StMat& M = A.mats[items[t].m];
       const int row = items[t].tile * kTileRows + lane;
       if (row < M.n) {
@@ -361,7 +363,6 @@ __device__ void st_run_lds_n(const StArgs& A, int n_in, uint16_t* out, uint16_t*
         else M.y[row] = st_to_bf16(sum);
       }
     }
-    __syncthreads();   // red is free again
   }
 }
 
@@ -487,12 +488,12 @@ __device__ void st_run_down(const StArgs& A, uint16_t* out, const StItem (&items
   __syncthreads();
   if (NI <= 0) return;
   const float part = st_compute<MG>(items[0], wave, R, L);
-  L.red[wave][lane] = part;
+  L.red[0][wave][lane] = part;
   __syncthreads();
   if (wave == 0) {
-    float sum = L.red[0][lane];
+    float sum = L.red[0][0][lane];
 #pragma unroll
-    for (int v = 1; v < kStWaves; ++v) sum += L.red[v][lane];
+    for (int v = 1; v < kStWaves; ++v) sum += L.red[0][v][lane];
     const StMat& M = A.mats[items[0].m];
     const int row = items[0].tile * kTileRows + lane;
     if (row < M.n) {
@@ -538,7 +539,9 @@ __global__ __launch_bounds__(kStThreads) void stage_kernel(StArgs A) {
     if (kind == 0) st_run_lds<0, MI, MG>(A, n_in, out, nullptr, nitems, items, L);
     else st_run_lds<1, MI, MG>(A, n_in, out, blockIdx.x == 0 ? A.down_out : nullptr, nitems, items, L);
   } else {
-    if (kind == 2) st_run_lds<2, MI, MG>(A, n_in, out, nullptr, nitems, items, L);
+    // o tiles span hidden / 128 <= 48 groups: three slots per wave cover them (the down
+    // halves need MG)
+    if (kind == 2) st_run_lds<2, MI, kSt1G>(A, n_in, out, nullptr, nitems, items, L);
     else if (nitems > 0) st_run_down<MG, 1>(A, out, items, L);
     else st_run_down<MG, 0>(A, out, items, L);
   }
