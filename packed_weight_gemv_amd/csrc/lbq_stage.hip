@@ -17,8 +17,8 @@
 //    and adds one table entry per 4 weights (the field extraction of the per-call Q1 kernel);
 //    the 16 waves' sums are added in wave order through LDS.
 //  * The activation slots (x, q, k, v, gate, up, xo, o, xd, down) are written as the per-call
-//    path writes them: stage 1's first workgroup writes x_l and down_{l-1}, stage 2's first o
-//    and down workgroups write xo and xd.
+//    path writes them: stage 1's last workgroup (the one with the fewest tiles) writes x_l and
+//    down_{l-1}, stage 2's first o and down workgroups write xo and xd.
 #include <hip/hip_runtime.h>
 #include <string.h>
 
@@ -322,14 +322,17 @@ __device__ void st_run_lds_n(const StArgs& A, int n_in, uint16_t* out, uint16_t*
     const int c = tid + k * kStThreads;
     if (c >= nch) continue;
     float v[4];
+    uint32_t rb[4], ob[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float h = hv[k][i];
-      if (raw_out) raw_out[4 * c + i] = st_to_bf16(h);   // h is a bf16 value already
-      const uint16_t b = st_to_bf16(st_div(h, denom, rden));
-      if (out) out[4 * c + i] = b;
-      v[i] = st_bf16(b);
+      rb[i] = st_to_bf16(h);   // h is a bf16 value already
+      ob[i] = st_to_bf16(st_div(h, denom, rden));
+      v[i] = st_bf16(ob[i]);
     }
+    // one 8-byte store per chunk (the activation slots are 16-byte aligned)
+    if (raw_out) *(uint2*)(raw_out + 4 * c) = make_uint2(rb[0] | rb[1] << 16, rb[2] | rb[3] << 16);
+    if (out) *(uint2*)(out + 4 * c) = make_uint2(ob[0] | ob[1] << 16, ob[2] | ob[3] << 16);
     const float p0 = -v[0] - v[1], p1 = v[0] - v[1], p2 = v[1] - v[0], p3 = v[0] + v[1];
     const float q0 = -v[2] - v[3], q1 = v[2] - v[3], q2 = v[3] - v[2], q3 = v[2] + v[3];
     float4* dst = (float4*)(L.lut + c * 16);
@@ -469,12 +472,13 @@ __device__ void st_run_down(const StArgs& A, uint16_t* out, const StItem (&items
     const int c = c0 + tid + it * kStThreads;
     if (c >= c1) continue;
     float v[4];
+    uint32_t ob[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint16_t b = st_to_bf16(st_div(hv[it][i], denom, rden));
-      if (out) out[4 * c + i] = b;
-      v[i] = st_bf16(b);
+      ob[i] = st_to_bf16(st_div(hv[it][i], denom, rden));
+      v[i] = st_bf16(ob[i]);
     }
+    if (out) *(uint2*)(out + 4 * c) = make_uint2(ob[0] | ob[1] << 16, ob[2] | ob[3] << 16);
     const float p0 = -v[0] - v[1], p1 = v[0] - v[1], p2 = v[1] - v[0], p3 = v[0] + v[1];
     const float q0 = -v[2] - v[3], q1 = v[2] - v[3], q2 = v[3] - v[2], q3 = v[2] + v[3];
     float4* dst = (float4*)(L.lut + (c - c0) * 16);
@@ -521,7 +525,7 @@ __global__ __launch_bounds__(kStThreads) void stage_kernel(StArgs A) {
   if (A.stage == 1) {
     kind = A.x0 ? 0 : 1;
     n_in = A.hidden;
-    if (blockIdx.x == 0) {
+    if (blockIdx.x == gridDim.x - 1) {   // holds the fewest tiles
       out = A.x_out;
       if (A.acc_zero)
         for (int j = tid; j < A.hidden; j += kStThreads) A.acc_zero[j] = 0.f;
@@ -537,7 +541,7 @@ __global__ __launch_bounds__(kStThreads) void stage_kernel(StArgs A) {
   }
   if (MI > 1) {   // stage 1
     if (kind == 0) st_run_lds<0, MI, MG>(A, n_in, out, nullptr, nitems, items, L);
-    else st_run_lds<1, MI, MG>(A, n_in, out, blockIdx.x == 0 ? A.down_out : nullptr, nitems, items, L);
+    else st_run_lds<1, MI, MG>(A, n_in, out, blockIdx.x == gridDim.x - 1 ? A.down_out : nullptr, nitems, items, L);
   } else {
     // o tiles span hidden / 128 <= 48 groups: three slots per wave cover them (the down
     // halves need MG)
