@@ -82,3 +82,29 @@ def test_decode_step_27b_shapes_two_layers_sampled(lbq):
     lbq.lbq_decode_step_q1g128(arr, L, hid, kv, ffn, to_dev(x0), act)
     torch.cuda.synchronize()
     _check_step(lbq, mats, act, L, hid, kv, ffn, batch, range(L), rows=61)
+
+
+def test_decode_step_unaligned_input(lbq):
+    """A step input 4-byte but not 16-byte aligned is refused by the stage kernels (their LDS
+    copies need 16 bytes) and served by another path, still in teacher-forced parity; one that
+    is not 4-byte aligned is rejected with LBQ_E_ALIGN and leaves the record untouched."""
+    L, hid, kv, ffn, batch = 2, 384, 128, 640, 1
+    mats, layers = _build_stream(lbq, L, hid, kv, ffn)
+    arr = lbq.make_layers(layers)
+    x0 = synth.activations(batch, hid, workload=synth.W_Q1_STREAM, extra=7)
+    buf = torch.zeros(hid + 8, dtype=torch.int16, device="cuda:0")
+    n = lbq.lbq_decode_act_elems(L, hid, kv, ffn, batch)
+    act = torch.zeros(n, dtype=torch.int16, device="cuda:0")
+    odd = buf[1:1 + hid].view(batch, hid)      # 2 bytes past a 256-byte aligned allocation
+    odd.copy_(to_dev(x0))
+    with pytest.raises(lbq.LbqError, match="LBQ_E_ALIGN"):
+        lbq.lbq_decode_step_q1g128(arr, L, hid, kv, ffn, odd, act)
+    torch.cuda.synchronize()
+    assert not act.any()
+    view = buf[2:2 + hid].view(batch, hid)     # 4 bytes past it
+    view.copy_(to_dev(x0))
+    assert view.data_ptr() % 16 == 4
+    lbq.lbq_decode_step_q1g128(arr, L, hid, kv, ffn, view, act)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(lbq.act_view(act, "x", 0, L, hid, kv, ffn, batch)), x0)
+    _check_step(lbq, mats, act, L, hid, kv, ffn, batch, range(L))
