@@ -336,10 +336,14 @@ __device__ void st_run_lds_n(const StArgs& A, int n_in, uint16_t* out, uint16_t*
     const float p0 = -v[0] - v[1], p1 = v[0] - v[1], p2 = v[1] - v[0], p3 = v[0] + v[1];
     const float q0 = -v[2] - v[3], q1 = v[2] - v[3], q2 = v[3] - v[2], q3 = v[2] + v[3];
     float4* dst = (float4*)(L.lut + c * 16);
-    dst[0] = make_float4(p0 + q0, p1 + q0, p2 + q0, p3 + q0);
-    dst[1] = make_float4(p0 + q1, p1 + q1, p2 + q1, p3 + q1);
-    dst[2] = make_float4(p0 + q2, p1 + q2, p2 + q2, p3 + q2);
-    dst[3] = make_float4(p0 + q3, p1 + q3, p2 + q3, p3 + q3);
+    // lane l writes row (r + l) mod 4 at step r: with one chunk (64 bytes) per lane, writing
+    // the same row in every lane would put the 16-byte stores on few LDS banks
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = (r + lane) & 3;
+      const float qj = j == 0 ? q0 : j == 1 ? q1 : j == 2 ? q2 : q3;
+      dst[j] = make_float4(p0 + qj, p1 + qj, p2 + qj, p3 + qj);
+    }
   }
 #pragma unroll
   for (int i = 3; i < MG; ++i) issue0(i);
@@ -482,10 +486,14 @@ __device__ void st_run_down(const StArgs& A, uint16_t* out, const StItem (&items
     const float p0 = -v[0] - v[1], p1 = v[0] - v[1], p2 = v[1] - v[0], p3 = v[0] + v[1];
     const float q0 = -v[2] - v[3], q1 = v[2] - v[3], q2 = v[3] - v[2], q3 = v[2] + v[3];
     float4* dst = (float4*)(L.lut + (c - c0) * 16);
-    dst[0] = make_float4(p0 + q0, p1 + q0, p2 + q0, p3 + q0);
-    dst[1] = make_float4(p0 + q1, p1 + q1, p2 + q1, p3 + q1);
-    dst[2] = make_float4(p0 + q2, p1 + q2, p2 + q2, p3 + q2);
-    dst[3] = make_float4(p0 + q3, p1 + q3, p2 + q3, p3 + q3);
+    // lane l writes row (r + l) mod 4 at step r: with one chunk (64 bytes) per lane, writing
+    // the same row in every lane would put the 16-byte stores on few LDS banks
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = (r + lane) & 3;
+      const float qj = j == 0 ? q0 : j == 1 ? q1 : j == 2 ? q2 : q3;
+      dst[j] = make_float4(p0 + qj, p1 + qj, p2 + qj, p3 + qj);
+    }
   }
 #pragma unroll
   for (int i = 5; i < MG; ++i) issue(i);
