@@ -72,11 +72,12 @@ def test_decode_step_small_stream_teacher_forced(lbq, batch):
     _check_step(lbq, mats, act, L, hid, kv, ffn, batch, range(L))
 
 
-def test_decode_step_27b_shapes_two_layers_sampled(lbq):
-    L, hid, kv, ffn, batch = 2, synth.STREAM_HIDDEN, synth.STREAM_KV, synth.STREAM_FFN, 1
+@pytest.mark.parametrize("batch", [1, 8])
+def test_decode_step_27b_shapes_two_layers_sampled(lbq, batch):
+    L, hid, kv, ffn = 2, synth.STREAM_HIDDEN, synth.STREAM_KV, synth.STREAM_FFN
     mats, layers = _build_stream(lbq, L, hid, kv, ffn)
     arr = lbq.make_layers(layers)
-    x0 = synth.activations(batch, hid, workload=synth.W_Q1_STREAM)
+    x0 = synth.activations(batch, hid, workload=synth.W_Q1_STREAM, extra=batch - 1)
     act = torch.zeros(lbq.lbq_decode_act_elems(L, hid, kv, ffn, batch), dtype=torch.int16,
                       device="cuda:0")
     lbq.lbq_decode_step_q1g128(arr, L, hid, kv, ffn, to_dev(x0), act)

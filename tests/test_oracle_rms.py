@@ -48,3 +48,52 @@ def test_zero_vector_stays_zero():
     y = np.zeros((1, 256), dtype=np.uint16)
     x, q = oracle.rms_rescale(y, eps=1e-6)
     assert not x.any() and not q.any()
+
+
+# ---- the product branch h = y * y2 (feeds every down GEMV of the decode step) --------------
+# These fix h by mathematics rather than by restating the formula: a unit second factor, the
+# symmetry of the product, power-of-two factors, and a closed form whose output is known exactly.
+
+BF16_ONE, BF16_FOUR, BF16_QUARTER = 0x3F80, 0x4080, 0x3E80
+
+
+def test_product_with_unit_factor_is_the_single_input_rescale():
+    y = synth.activations(2, 1536, workload=84)
+    ones = np.full_like(y, BF16_ONE)
+    a, qa = oracle.rms_rescale(y, eps=1e-6)
+    b, qb = oracle.rms_rescale(y, ones, eps=1e-6)
+    assert np.array_equal(a, b) and np.array_equal(qa, qb)
+
+
+def test_product_is_symmetric_in_its_factors():
+    g = synth.activations(2, 1024, workload=85)
+    u = synth.activations(2, 1024, workload=86)
+    a, qa = oracle.rms_rescale(g, u, eps=1e-6)
+    b, qb = oracle.rms_rescale(u, g, eps=1e-6)
+    assert np.array_equal(a, b) and np.array_equal(qa, qb)
+
+
+def test_power_of_two_second_factor_leaves_output_unchanged():
+    y = synth.activations(2, 640, workload=87)
+    a, _ = oracle.rms_rescale(y, eps=0.0)
+    for c in (BF16_FOUR, BF16_QUARTER):
+        b, _ = oracle.rms_rescale(y, np.full_like(y, c), eps=0.0)
+        assert np.array_equal(a, b)
+
+
+def test_product_closed_form_signs():
+    # |y| = 3 and |y2| = 2 everywhere with independent signs: h = +-6, mean(h^2) = 36, so with
+    # eps = 0 every output is exactly sign(y) * sign(y2). Dropping either factor, or using one in
+    # place of the other, flips the outputs where that factor is negative.
+    r = np.random.default_rng([0x1B0, 88])
+    sy = r.integers(0, 2, size=(2, 512)).astype(np.uint16)
+    s2 = r.integers(0, 2, size=(2, 512)).astype(np.uint16)
+    y = (0x4040 | (sy << 15)).astype(np.uint16)        # +-3.0
+    y2 = (0x4000 | (s2 << 15)).astype(np.uint16)       # +-2.0
+    x, q = oracle.rms_rescale(y, y2, eps=0.0)
+    want = np.where(sy ^ s2, -1.0, 1.0)
+    assert np.array_equal(q, want)
+    assert np.array_equal(x, np.where(sy ^ s2, 0xBF80, 0x3F80).astype(np.uint16))
+    # with eps > 0 the closed form is h / sqrt(36 + eps)
+    x, q = oracle.rms_rescale(y, y2, eps=0.25)
+    assert np.allclose(q, want * 6.0 / np.sqrt(36.25), rtol=1e-15, atol=0)
