@@ -188,13 +188,18 @@ def main() -> int:
         lbq.lbq_decode_step_q1g128(arr, L, hid, kv, ffn, x0, act)
 
     # ---- warm-up, graph capture, timed steps -------------------------------------------------
-    for _ in range(max(1, args.warmup)):
-        step()
+    # warm-up runs on the stream the graph is captured on: the library's per-stream workspace
+    # is allocated by the first call on a stream, which cannot happen inside a capture
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        for _ in range(max(1, args.warmup)):
+            step()
     torch.cuda.synchronize()
     graph = None
     if not args.no_graph:
         graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
+        with torch.cuda.graph(graph, stream=cap):
             step()
         for _ in range(2):
             graph.replay()

@@ -1033,9 +1033,23 @@ extern "C" lbq_status lbq_decode_step_q1g128(const lbq_q1_layer* layers, int32_t
   const size_t elems = lbq_decode_act_elems(n_layers, hidden, kv, ffn, batch);
   if (!elems || !(eps >= 0.f)) return LBQ_E_SHAPE;
   if ((uintptr_t)d_x0 % 4 || (uintptr_t)d_act % 4) return LBQ_E_ALIGN;
+  // every layer's seven matrices are validated before anything is launched: present, 16-byte
+  // aligned, and not overlapping the activation record the step writes
+  Geometry gq, gk, gf, gd;
+  make_geometry(hidden, hidden, kQ1GroupBlocks, &gq);
+  make_geometry(kv, hidden, kQ1GroupBlocks, &gk);
+  make_geometry(ffn, hidden, kQ1GroupBlocks, &gf);
+  make_geometry(hidden, ffn, kQ1GroupBlocks, &gd);
   for (int l = 0; l < n_layers; ++l) {
     const lbq_q1_layer& L = layers[l];
-    if (!L.q || !L.k || !L.v || !L.o || !L.gate || !L.up || !L.down) return LBQ_E_NULL;
+    const void* w[7] = {L.q, L.k, L.v, L.o, L.gate, L.up, L.down};
+    const size_t wb[7] = {layout_bytes(gq), layout_bytes(gk), layout_bytes(gk), layout_bytes(gq),
+                          layout_bytes(gf), layout_bytes(gf), layout_bytes(gd)};
+    for (int m = 0; m < 7; ++m) {
+      if (!w[m]) return LBQ_E_NULL;
+      if ((uintptr_t)w[m] % 16) return LBQ_E_ALIGN;
+      if (overlaps(w[m], wb[m], d_act, elems * 2)) return LBQ_E_ALIAS;
+    }
   }
   if (overlaps(d_x0, (size_t)batch * hidden * 2, d_act, elems * 2)) return LBQ_E_ALIAS;
   hipStream_t s = (hipStream_t)stream;

@@ -1,28 +1,47 @@
-// lbq_stage.hip - batch-1 decode step of a Q1_0_g128 layer stack as two launches per layer,
-// with no communication between workgroups inside a launch (the launch boundary is the only
-// synchronisation).
+// lbq_stage.hip - batch-1 decode step of a stack of Q1_0_g128 layers (the 64-layer 1-bit model
+// of the Bonsai-27B-gguf digest, "technical architecture highlights") as two launches per layer.
+// Workgroups of one launch never wait for each other: the launch boundary is the only
+// synchronisation.
 //
-//  * Stage 1 of layer l computes q, k, v, gate and up from x_l. Every workgroup first forms x_l
-//    itself: for layer 0 it is the step input; otherwise it is rms(down_{l-1}), where down_{l-1}
-//    is read from the fp32 accumulator that stage 2 of the previous layer filled, rounded to
-//    bf16 and rescaled. It then builds the sign-sum tables of all of x_l in LDS (16 entries per
-//    4 inputs) and walks its share of the 64-row output tiles of the five matrices, each tile
-//    over the whole of k, with the next tile's weights in flight while the current one is
-//    computed.
-//  * Stage 2 of layer l computes o from rms(q) (one workgroup per tile) and down from
-//    rms(gate * up) (two workgroups per tile, each over half of k). The two halves of a down row
-//    are added into a zeroed fp32 accumulator with atomic adds: 0 + a + b is the same in either
-//    order, so the result is deterministic.
-//  * A workgroup has 16 waves; wave w takes groups w, w + 16, ... of a tile, one row per lane,
-//    and adds one table entry per 4 weights (the field extraction of the per-call Q1 kernel);
-//    the 16 waves' sums are added in wave order through LDS.
-//  * The activation slots (x, q, k, v, gate, up, xo, o, xd, down) are written as the per-call
-//    path writes them: stage 1's last workgroup (the one with the fewest tiles) writes x_l and
-//    down_{l-1}, stage 2's first o and down workgroups write xo and xd.
+//  * Stage 1 of layer l: q, k, v, gate and up from x_l, and o of layer l - 1 from
+//    rms(q_{l-1}) (o is a leaf of the step, so it rides along with the next layer). A workgroup
+//    either owns up to three 64-row tiles of q..up over the whole of k, or up to three tiles of o.
+//    x_l is the step input for layer 0, else rms(down_{l-1}) with down_{l-1} the sum of the
+//    partial sums left by stage 2 (in a fixed order, then rounded to bf16).
+//  * gate and up are computed in pair tiles: 32 rows of gate and the same 32 rows of up in one
+//    wave's 64 lanes, so the workgroup that produces them also forms gate * up of those rows
+//    and leaves the sum of its squares for the rescale of stage 2 (which then reads 2 KiB of
+//    sums instead of all of gate and up).
+//  * Stage 2 of layer l: down from rms(gate * up). Every 64-row tile is split along k into P
+//    pieces (P <= 4); the workgroup of piece p writes its fp32 partial sums to slot p, and the
+//    next stage 1 adds the slots in slot order.
+//  * Load order inside a workgroup: the input vector first, then the scale blocks of its tiles
+//    (1 KiB each, copied straight into LDS), then the first units of every wave (a unit is one
+//    128-weight group of one 64-row tile: 16 bytes per lane). While those stream, the workgroup
+//    forms its input and builds its tables; every later unit is requested a fixed number of
+//    units ahead of its use. A wave issues its memory instructions in order and stalls at issue
+//    once the compute unit's memory pipeline is full, so requesting every unit up front would
+//    hold the prologue back behind the weights.
+//  * Tables: for every 4 consecutive inputs, the 16 signed sums +-x0 +-x1 +-x2 +-x3, as exact
+//    int32 fixed-point values. Within a 128-input group every input is put on the fixed point
+//    2^(E - 22), where 2^E is above the group's largest magnitude: a bf16 input is represented
+//    exactly unless it is 2^15 times smaller than that largest, and the error of the others is
+//    at most 2^(E - 23). A row's group sum (32 lookups) stays below 2^29 and is exact; it goes
+//    back to fp32 (one conversion, then the exact factor 2^(E - 22)) before it is weighted by
+//    the fp16 scale, so the accumulation over groups is fp32.
+//  * Lookups: a row's 16 bytes of sign bits hold 32 four-bit fields; one mask gives four byte-
+//    aligned fields (x4, the table's byte stride), an SDWA add places one on the group's table
+//    base, and one LDS read fetches the entry; two entries join the int32 sum per add3.
+//  * Sums that every workgroup must agree on (the sum of squares of a rescale) are taken in one
+//    fixed order: DPP steps inside a wave, then the waves in order.
+//  * The activation slots (x, q, k, v, gate, up, xo, o, xd, down) are written as the
+//    per-projection path writes them.
 #include <hip/hip_runtime.h>
 #include <string.h>
 
+#include <map>
 #include <mutex>
+#include <utility>
 
 #include "lbq_internal.h"
 
@@ -30,665 +49,828 @@ using namespace lbq;
 
 namespace {
 
-constexpr int kStWaves = 16;
-constexpr int kStThreads = 64 * kStWaves;
-// per launch kind: stage 1 takes up to 3 tiles of up to 48 groups (3 per wave), stage 2 one tile
-// (or half a down row) of up to 80 groups (5 per wave)
-constexpr int kSt1Items = 3, kSt1G = 3, kSt2G = 5;
-constexpr int kStMaxChunks = 2304;    // table capacity: 9,216 inputs (147,456 B)
-constexpr int kStSuperBytes = kBlock * (1 + kSuper * kQ1GroupBlocks);
-constexpr int kStMaxItems = kSt1Items;
+constexpr int kWaves = 16;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kPWaves = 8;             // prologue waves (0-7); waves 8-15 stream weights at once
+constexpr int kPThreads = 64 * kPWaves;
+constexpr int kUnitsS1 = 10;           // stage 1: units per stream wave
+constexpr int kUnitsP1 = 5;            //          units per prologue wave
+constexpr int kUnitsS2 = 4;            // stage 2: units per stream wave
+constexpr int kUnitsP2 = 3;            //          units per prologue wave
+constexpr int kMaxTiles = 3;           // tiles per stage-1 workgroup
+constexpr int kTabGroups = 56;         // table capacity: 56 groups = 7,168 inputs (112 KiB)
+constexpr int kMaxBlocks = 16;         // scale blocks staged in LDS (two per prologue wave)
+constexpr int kMaxSlots = 3;           // pieces per down tile
+constexpr int kGroupTabBytes = 32 * 64;// 32 tables of 16 int32 entries per 128-input group
+constexpr int kSuperBytes = kBlock * (1 + kSuper);   // Q1 super-group: scales + 8 sign blocks
+constexpr int kPRounds = 3;            // stage-1 input: 4-input chunks pt + 512 r
+constexpr int kPRounds2 = 2;           // stage-2 input: pair sums and 8-input chunks pt + 512 r
+constexpr size_t kPartFloats = (size_t)kMaxSlots * kTabGroups * kGroup;   // 28,672 floats
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const int lds_cint;
+typedef __attribute__((address_space(3))) const uint16_t lds_cu16;
+typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ float st_bf16(uint32_t v) { return __uint_as_float(v << 16); }
-// float -> bf16 bits with the hardware conversion (round to nearest even; the kernels keep fp32
-// denormals, so tiny values round to bf16 subnormals as the software rounding would)
-__device__ __forceinline__ uint16_t st_to_bf16(float f) {
+__device__ __forceinline__ float bf(uint32_t b16) { return __uint_as_float(b16 << 16); }
+// float -> bf16 bits, round to nearest even (the gfx950 conversion; fp32 denormals are kept)
+__device__ __forceinline__ uint32_t to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
+__device__ __forceinline__ float f16(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
 // h / d from y = RN(1 / d) with one residual correction (Markstein): the residual h - q d is
-// exact in an fma, and q + r y rounds to the quotient IEEE division would give.
-__device__ __forceinline__ float st_div(float h, float d, float y) {
+// exact in an fma, and q + r y rounds to the quotient IEEE division gives.
+__device__ __forceinline__ float div_corr(float h, float d, float y) {
   const float q = h * y;
   const float r = fmaf(-q, d, h);
   return fmaf(r, y, q);
 }
-__device__ __forceinline__ float st_f16(uint32_t h) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+
+// DPP move of v (as bits) with the given control; lanes outside row_mask keep `old`.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp(float old, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                               __builtin_bit_cast(int, v), CTRL,
+                                                               ROWS, 0xF, false));
 }
-// byte offset (4-bit field x 4) of table entry q of a sign dword stored rotated left by two:
-// bits [8q+2, 8q+5]. For byte 1 the SDWA source select does it in one op (the compiler emits a
-// shift and a mask there, and one op for bytes 0, 2 and 3 by itself).
-__device__ __forceinline__ uint32_t st_field(uint32_t s, int q) {
-  if (q == 1) {
-    uint32_t r, m = 0x3Cu;
-    asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 "
-        "src1_sel:DWORD"
-        : "=v"(r)
-        : "v"(s), "v"(m));
-    return r;
-  }
-  return (s >> (8 * q)) & 0x3Cu;
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+
+// Sum over the wave in a fixed order; the total is returned in every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp<kDppXor1>(0.f, v);
+  v += dpp<kDppXor2>(0.f, v);
+  v += dpp<kDppHalfMirror>(0.f, v);
+  v += dpp<kDppMirror>(0.f, v);           // every lane holds its row's sum
+  v += dpp<kDppBcast15, 0xA>(0.f, v);     // rows 1, 3 add rows 0, 2
+  v += dpp<kDppBcast31, 0xC>(0.f, v);     // rows 2, 3 add the sum of rows 0, 1
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+// Maximum over each row of 16 lanes, in every lane of the row.
+__device__ __forceinline__ float row_max(float m) {
+  m = fmaxf(m, dpp<kDppXor1>(m, m));
+  m = fmaxf(m, dpp<kDppXor2>(m, m));
+  m = fmaxf(m, dpp<kDppHalfMirror>(m, m));
+  return fmaxf(m, dpp<kDppMirror>(m, m));
+}
+// Maximum over each half wave (32 lanes), in every lane of the half.
+__device__ __forceinline__ float half_max(float m) {
+  m = row_max(m);
+  m = fmaxf(m, dpp<kDppBcast15, 0xA>(m, m));   // lanes 16..31 and 48..63 hold their half's max
+  const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 31));
+  const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 63));
+  return (threadIdx.x & 32) ? hi : lo;
+}
+// Exponent E with 2^E above the magnitude m (E = -126 covers zero and subnormal magnitudes).
+__device__ __forceinline__ int exponent_above(float m) {
+  const uint32_t eb = (__float_as_uint(m) >> 23) & 0xFFu;
+  return (int)(eb > 1u ? eb : 1u) - 126;
 }
 
-struct StMat {
-  const uint8_t* w;        // device layout
-  uint16_t* y;             // bf16 output rows, or nullptr
-  float* acc;              // fp32 accumulator rows (atomic add), or nullptr
-  int n;                   // rows
-  int tiles;               // 64-row tiles
-  int groups;              // 128-weight groups of a full row
-  long long tile_bytes;
-};
-
-// One stage launch. Stage 1: mats[0..4] = q, k, v, gate, up over input x. Stage 2: mats[0] = o
-// over rms(q), mats[1] = down over rms(gate * up), split in two halves of its groups.
-struct StArgs {
-  StMat mats[5];
-  int nmats;
-  int stage;               // 1 or 2
-  int hidden, ffn;
-  float eps;
-  // stage 1 input: x0 (layer 0) or the previous layer's down accumulator
-  const uint16_t* x0;
-  const float* acc_in;
-  uint16_t* x_out;         // x_l (bf16), written by workgroup 0
-  uint16_t* down_out;      // down_{l-1} (bf16), written by workgroup 0 when acc_in is set
-  float* acc_zero;         // accumulator cleared by workgroup 0 for this layer's stage 2
-  // stage 2 inputs
-  const uint16_t* q;
-  const uint16_t* gate;
-  const uint16_t* up;
-  uint16_t* xo_out;
-  uint16_t* xd_out;
-  int down_split_g;        // first group of the second half of down
-};
-
-struct StLds {
-  float lut[kStMaxChunks * 16];
-  // per-tile partial sums, double-buffered: tile t uses red[t & 1], and the barrier after tile
-  // t + 1's writes orders wave 0's reads of tile t before anyone writes red[t & 1] again
-  float red[2][kStWaves][64];
-  float ssum[kStWaves];
-};
-
-// A work item: tile `tile` of matrix `m`, groups [ga, gb) of its rows; table chunk 0 is the
-// first input of group ga.
-struct StItem {
-  int m, tile, ga, gb;
-};
-
-template <int MG>
-struct StRegs {
-  u32x4 rec[MG];
-  uint32_t sc[MG];
-};
-
-// Slot i of an item: group ga + wave + 16 i (a slot past the item's last group reloads that
-// group, so a wave issues exactly two loads per slot with no branch around them, and the
-// compute skips it).
-template <int MG>
-__device__ __forceinline__ void st_load_slot(const StArgs& A, const StItem& it, int wave, int lane,
-                                             StRegs<MG>& R, int i) {
-  const StMat& M = A.mats[it.m];
-  const uint8_t* tb = M.w + (size_t)it.tile * M.tile_bytes;
-  const int g = min(it.ga + wave + kStWaves * i, it.gb - 1);
-  const uint8_t* sb = tb + (size_t)(g / kSuper) * kStSuperBytes;
-  R.rec[i] = __builtin_nontemporal_load((const u32x4*)(sb + kBlock * (1 + g % kSuper) + lane * 16));
-  R.sc[i] = *(const uint16_t*)(sb + lane * 16 + (g % kSuper) * 2);
+// LDS byte address of byte q of `masked` (a field x4 at bits [8q+2, 8q+5], zeros elsewhere)
+// plus the table base: one SDWA add.
+__device__ __forceinline__ uint32_t field_addr(uint32_t masked, uint32_t base, int q) {
+  uint32_t r;
+  if (q == 0)
+    asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0 src1_sel:DWORD"
+        : "=v"(r) : "v"(masked), "v"(base));
+  else if (q == 1)
+    asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:DWORD"
+        : "=v"(r) : "v"(masked), "v"(base));
+  else if (q == 2)
+    asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2 src1_sel:DWORD"
+        : "=v"(r) : "v"(masked), "v"(base));
+  else
+    asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3 src1_sel:DWORD"
+        : "=v"(r) : "v"(masked), "v"(base));
+  return r;
 }
-template <int MG>
-__device__ __forceinline__ void st_load(const StArgs& A, const StItem& it, int wave, int lane,
-                                        StRegs<MG>& R) {
-#pragma unroll
-  for (int i = 0; i < MG; ++i) st_load_slot<MG>(A, it, wave, lane, R, i);
+__device__ __forceinline__ int lds_ld(uint32_t addr, uint32_t off) {
+  return *(lds_cint*)(uintptr_t)(addr + off);
 }
-template <int MG>
-__device__ __forceinline__ void st_compute_slot(const StItem& it, int wave, const StRegs<MG>& R,
-                                                const StLds& L, int i, float& acc) {
-  const int g = it.ga + wave + kStWaves * i;
-  if (g >= it.gb) return;
-  uint32_t s4[4] = {R.rec[i].x, R.rec[i].y, R.rec[i].z, R.rec[i].w};
-  uint32_t sc = R.sc[i];
-  // keep one group's lookups together (hoisting all of them costs many registers), and keep
-  // the scale's conversion here: placed beside its load it would wait for the load at once
-  asm volatile("" : "+v"(s4[0]), "+v"(s4[1]), "+v"(s4[2]), "+v"(s4[3]), "+v"(sc));
-  const char* lb = (const char*)L.lut + (size_t)(g - it.ga) * 32 * 64;
-  float pa = 0.f, pb = 0.f;
+
+// Exact signed sum of one row's 128 weights against the group's tables at LDS byte address
+// `base`. The row's 16 bytes: dword d holds weights 32d..32d+31 (bit b = weight 32d + b), rotated
+// left by two, so the field of weights 32d + 4n .. +3 sits at bits [4n+2, 4n+5]: n even at
+// [8i+2, 8i+5], n odd at the same place after a rotation right by four.
+__device__ __forceinline__ int group_sum(const u32x4 rec, uint32_t base) {
+  int acc = 0;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    const uint32_t s = s4[d];
-    const uint32_t r = __builtin_amdgcn_alignbit(s, s, 4);
+    const uint32_t s = rec[d];
+    const uint32_t me = s & 0x3C3C3C3Cu;
+    const uint32_t mo = __builtin_amdgcn_alignbit(s, s, 4) & 0x3C3C3C3Cu;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      pa += *(const float*)(lb + (8 * d + 2 * q) * 64 + st_field(s, q));
-      pb += *(const float*)(lb + (8 * d + 2 * q + 1) * 64 + st_field(r, q));
+      const uint32_t a0 = field_addr(me, base, q), a1 = field_addr(mo, base, q);
+      acc = lds_ld(a0, (8 * d + 2 * q) * 64) + lds_ld(a1, (8 * d + 2 * q + 1) * 64) + acc;
     }
   }
-  acc = fmaf(st_f16(sc), pa + pb, acc);
-}
-template <int MG>
-__device__ __forceinline__ float st_compute(const StItem& it, int wave, const StRegs<MG>& R,
-                                            const StLds& L) {
-  float acc = 0.f;
-#pragma unroll
-  for (int i = 0; i < MG; ++i) st_compute_slot<MG>(it, wave, R, L, i, acc);
   return acc;
 }
 
-// The idx-th item of this workgroup (stage 1: tiles blockIdx.x + idx * gridDim.x over the five
-// matrices in order; stage 2: one item per workgroup). Returns false past the last.
-__device__ bool st_item_raw(const StArgs& A, int idx, StItem& it) {
-  if (A.stage == 1) {
-    int t = blockIdx.x + idx * gridDim.x;
-    for (int m = 0; m < A.nmats; ++m) {
-      if (t < A.mats[m].tiles) {
-        it.m = m;
-        it.tile = t;
-        it.ga = 0;
-        it.gb = A.mats[m].groups;
-        return true;
-      }
-      t -= A.mats[m].tiles;
-    }
-    return false;
+// The 16-entry table of 4 inputs v (bf16 values) on the fixed point 2^(E - 22), sh = 22 - E:
+// entry i = sum_j (bit j of i ? +q_j : -q_j), written as four 16-byte rows at byte offset `off`.
+// Lanes hold consecutive tables (64 bytes apart), so the same row in every lane would put the
+// 16-byte stores of lanes l, l + 4, l + 8, ... on the same banks: lane l writes row
+// (r + l / 4) mod 4 at step r instead (a select, not a branch).
+__device__ __forceinline__ void put_table(char* tab, uint32_t off, const float (&v)[4], int sh,
+                                          int lane) {
+  int q[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = (int)__builtin_rintf(__builtin_ldexpf(v[i], sh));
+  const int p0 = -q[0] - q[1], p1 = q[0] - q[1], p2 = q[1] - q[0], p3 = q[0] + q[1];
+  const int r0 = -q[2] - q[3], r1 = q[2] - q[3], r2 = q[3] - q[2], r3 = q[2] + q[3];
+  const int rot = (lane >> 2) & 3;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int j = (r + rot) & 3;
+    const int a = (j & 1) ? r1 : r0;
+    const int b = (j & 1) ? r3 : r2;
+    const int rj = (j & 2) ? b : a;
+    i32x4 row = {p0 + rj, p1 + rj, p2 + rj, p3 + rj};
+    *(i32x4*)(tab + off + 16 * j) = row;
   }
-  if (idx > 0) return false;
-  const int b = blockIdx.x;
-  if (b < A.mats[0].tiles) {
-    it.m = 0;
-    it.tile = b;
-    it.ga = 0;
-    it.gb = A.mats[0].groups;
-    return true;
-  }
-  const int d = b - A.mats[0].tiles;
-  if (d >= 2 * A.mats[1].tiles) return false;
-  it.m = 1;
-  it.tile = d >> 1;
-  const int split = A.down_split_g;   // half of the groups, rounded up
-  it.ga = (d & 1) ? split : 0;
-  it.gb = (d & 1) ? A.mats[1].groups : split;
-  return true;
 }
 
-// The prologue and every tile of one input kind. Loads are issued in order of need: the input
-// vector first (latency-critical), then the weights of every item of the workgroup.
-// The same with every field pinned to a scalar register (an item is the same for every lane; a
-// per-lane matrix index would turn each read of the matrix record into a vector memory load).
-__device__ __forceinline__ bool st_item(const StArgs& A, int idx, StItem& it) {
-  const bool ok = st_item_raw(A, idx, it);
-  it.m = __builtin_amdgcn_readfirstlane(it.m);
-  it.tile = __builtin_amdgcn_readfirstlane(it.tile);
-  it.ga = __builtin_amdgcn_readfirstlane(it.ga);
-  it.gb = __builtin_amdgcn_readfirstlane(it.gb);
-  return __builtin_amdgcn_readfirstlane((int)ok) != 0;
+struct StLds {
+  int tab[kTabGroups * kGroupTabBytes / 4];   // 112 KiB of tables
+  uint8_t sblk[kMaxBlocks][kBlock];           // scale blocks of the workgroup's units
+  float red[kMaxTiles][kWaves][64];           // per-wave partial sums of each tile
+  float fac[kTabGroups];                      // 2^(E_g - 22)
+  float ssum[kPWaves];                        // per-wave sums of squares of the prologue waves
+  unsigned arrived_sum, arrived_tab;          // prologue waves done with their sums / tables
+};
+
+// Counters in LDS through which the prologue waves hand their results to the other waves of
+// the workgroup (all of them resident, so every wait ends): one lane per wave arrives once its
+// earlier LDS writes (and, where stated, its copies into LDS) are complete; waiters spin.
+__device__ __forceinline__ void arrive(unsigned* c) {
+  if ((threadIdx.x & 63) == 0)
+    __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void wait_count(unsigned* c, unsigned n) {
+  while (__hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < n)
+    __builtin_amdgcn_s_sleep(1);
+}
+// Sum over the prologue waves of one value per thread, in a fixed order (the same bits in every
+// workgroup): wave sums in LDS, then the waves in order once all have arrived.
+__device__ __forceinline__ float prologue_sum(float v, StLds& L) {
+  const float w = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) L.ssum[threadIdx.x >> 6] = w;
+  arrive(&L.arrived_sum);
+  wait_count(&L.arrived_sum, kPWaves);
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < kPWaves; ++i) t += L.ssum[i];
+  return t;
 }
 
-// Copies 16 bytes per lane from base + voff straight into LDS at lds + 16 * lane (the copy
-// bypasses the registers; a wave waits for it with s_waitcnt vmcnt, see st_wait_vm).
-__device__ __forceinline__ void st_dma16(const void* base, uint32_t voff, uint32_t lds) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved) : "s"(lds), "v"(voff), "s"(base) : "memory");
+struct StMat {
+  const uint8_t* w;      // device layout
+  uint16_t* y;           // bf16 output rows
+  int n, tiles;
+  long long tile_bytes;
+};
+
+// Stage 1. The tiles of q, k and v (mats[0..2]) come first, then the gate/up pair tiles: pair
+// tile p holds rows 32p .. 32p + 31 of gate (lanes 0-31) and of up (lanes 32-63), so the
+// workgroup that computes it also forms gate * up of those rows and leaves the sum of its
+// squares in stat[p] for the rescale of stage 2. Workgroup b < x_wgs gets x_q tiles of that list
+// (one more when b < x_r); the o workgroups that follow share the o tiles (of layer l - 1) the
+// same way.
+struct S1Args {
+  StMat mats[3];
+  StMat gate, up;
+  int nsingle, npair;
+  int x_wgs, x_q, x_r;
+  StMat o;
+  int o_wgs, o_q, o_r;
+  int hidden;
+  float eps;
+  const uint16_t* x0;    // layer 0: the step input, used as it is
+  const float* part;     // otherwise: down partial slots of layer l - 1, [nslots][hidden]
+  int nslots;
+  uint16_t* x_out;       // record slot x_l (written by workgroup x_wgs - 1)
+  uint16_t* down_out;    // record slot down_{l-1} (same workgroup, when part is set)
+  const uint16_t* q_prev;// q_{l-1} (o workgroups)
+  uint16_t* xo_out;      // record slot xo_{l-1} (written by the last o workgroup)
+  float* stat;           // [npair] sums of squares of gate * up (output)
+};
+
+// Stage 2: piece p of tile t is workgroup t * pieces + p, groups [pg[p], pg[p + 1]).
+struct S2Args {
+  StMat down;
+  int pieces;
+  int pg[kMaxSlots + 1];
+  int hidden, ffn;
+  float eps;
+  const uint16_t* gate;
+  const uint16_t* up;
+  const float* stat;     // [ffn / 32] sums of squares of gate * up, from stage 1
+  uint16_t* xd_out;      // record slot xd_l (written by the pieces of tile 0)
+  float* part;           // [pieces][hidden] fp32 partial sums (output)
+};
+
+// A tile as one lane sees it: `w` points at this lane's 16 bytes of the first super-group's
+// scale block (the row's records follow at fixed offsets), and the lane's output is y[row].
+struct LaneTile {
+  const uint8_t* w;
+  uint16_t* y;
+  int row, n;
+};
+
+__device__ __forceinline__ LaneTile lane_tile(const StMat& M, int t, int lane) {
+  LaneTile r;
+  r.w = M.w + (size_t)t * M.tile_bytes + lane * 16;
+  r.y = M.y;
+  r.row = t * kTileRows + lane;
+  r.n = M.n;
+  return r;
 }
+
+// Tile t of stage 1's x list (q, k, v tiles, then pair tiles); `pair` is set for a pair tile.
+__device__ __forceinline__ LaneTile lane_tile_x(const S1Args& A, int t, int lane, bool& pair) {
+  const int tq = A.mats[0].tiles, tk = A.mats[1].tiles;
+  if (t < A.nsingle) {
+    pair = false;
+    const int m = (t >= tq) + (t >= tq + tk);
+    const int lt = t - (m == 0 ? 0 : (m == 1 ? tq : tq + tk));
+    StMat M;   // field-wise selects: no dynamic index into the argument block
+    M.w = m == 0 ? A.mats[0].w : (m == 1 ? A.mats[1].w : A.mats[2].w);
+    M.y = m == 0 ? A.mats[0].y : (m == 1 ? A.mats[1].y : A.mats[2].y);
+    M.n = m == 0 ? A.mats[0].n : (m == 1 ? A.mats[1].n : A.mats[2].n);
+    M.tile_bytes = m == 0 ? A.mats[0].tile_bytes
+                          : (m == 1 ? A.mats[1].tile_bytes : A.mats[2].tile_bytes);
+    return lane_tile(M, lt, lane);
+  }
+  pair = true;
+  const int p = t - A.nsingle;
+  const int gt = p >> 1, rr = 32 * (p & 1) + (lane & 31);   // device tile, row within it
+  const bool up = lane >= 32;
+  LaneTile r;
+  r.w = (up ? A.up.w : A.gate.w) + (size_t)gt * A.gate.tile_bytes + rr * 16;
+  r.y = up ? A.up.y : A.gate.y;
+  r.row = gt * kTileRows + rr;
+  r.n = A.gate.n;
+  return r;
+}
+
+// Copies 1 KiB to LDS at dst, 16 bytes per lane from this lane's own source address.
+__device__ __forceinline__ void copy_block(const uint8_t* src_lane, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds((const void*)src_lane, (lds_void*)dst, 16, 0, 0);
+}
+// A workgroup barrier that orders the issue of memory requests only: __syncthreads() also
+// carries a release fence, which waits for every outstanding load of the wave first.
+__device__ __forceinline__ void issue_barrier() { __builtin_amdgcn_s_barrier(); }
 // Waits until at most N of this wave's vector memory operations are outstanding.
 template <int N>
-__device__ __forceinline__ void st_wait_vm() {
+__device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N <= 63, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Kinds 0 (stage 1 of layer 0: the bf16 step input, used as it is), 1 (stage 1 after layer 0:
-// rms of the fp32 down accumulator rounded to bf16) and 2 (stage 2, o: rms of bf16 q), for a
-// workgroup with exactly NI items. A wave issues its loads in order and stalls at issue once the
-// memory pipeline is full, so work placed behind a long run of weight loads waits for the
-// weights. Hence the order: the input vector is copied into LDS (behind the tables, with copies
-// that bypass the registers) and waited for; item 0's weights are issued; the sum of squares,
-// the rescale and the tables are formed from LDS while they stream; then item t + 1's weights
-// are issued just before item t is computed. NI is a template argument so that every load is
-// unconditional: a load under a run-time branch makes the compiler wait for it at the merge.
-template <int KIND, int NI, int MG>
-__device__ void st_run_lds_n(const StArgs& A, int n_in, uint16_t* out, uint16_t* raw_out,
-                             const StItem (&items)[kStMaxItems], StLds& L) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nch = n_in / 4;
-  char* inb = (char*)L.lut + (size_t)nch * 64;   // right after the tables
-  const void* src = KIND == 1 ? (const void*)A.acc_in : KIND == 0 ? (const void*)A.x0 : (const void*)A.q;
-  const uint32_t nbytes = (uint32_t)n_in * (KIND == 1 ? 4u : 2u);
-  const uint32_t ninst = (nbytes + 1023u) / 1024u;
-  for (uint32_t i = wave; i < ninst; i += kStWaves) {
-    const uint32_t voff = i * 1024u + lane * 16u;
-    const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)inb + i * 1024u);
-    if (voff < nbytes) st_dma16(src, voff, dst);
+// The units of a wave: slot j is unit u0 + 8 j while below u1. A slot past the wave's last unit
+// loads `spare` (a cached scale block) instead, so that every load is unconditional.
+template <int MU>
+struct WaveUnits {
+  u32x4 rec[MU];
+  int u0, u1;
+};
+
+// Unit u of a workgroup with tiles of G groups (stage 1): the record of group g of tile ti.
+struct UnitAddr1 {
+  const uint8_t *w0, *w1, *w2;
+  int G;
+  __device__ __forceinline__ const uint8_t* operator()(int u) const {
+    const int ti = (u >= G) + (u >= 2 * G);
+    const int g = u - ti * G;
+    // pointer select as integer arithmetic on the uniform tile index (a select between struct
+    // fields is otherwise lowered through scratch memory)
+    const uintptr_t a0 = (uintptr_t)w0, a1 = (uintptr_t)w1, a2 = (uintptr_t)w2;
+    const uintptr_t w = ti == 0 ? a0 : (ti == 1 ? a1 : a2);
+    return (const uint8_t*)w + (size_t)(g >> 3) * kSuperBytes + kBlock * (1 + (g & 7));
   }
-  st_wait_vm<0>();
-  __syncthreads();
-  StRegs<MG> R[NI > 0 ? NI : 1];
-  // item 0's slots are issued between pieces of the prologue: a wave stalls at issue while the
-  // memory pipeline is full, and the work between issues keeps its VALU busy meanwhile
-  auto issue0 = [&](int i) {
-    if (NI > 0 && i < MG) st_load_slot<MG>(A, items[0], wave, lane, R[0], i);
-  };
-  issue0(0);
-  // chunks (4 inputs) tid and tid + 1024: read once (16 or 8 bytes per lane) and kept
-  auto chunk = [&](int c, float (&h)[4]) {
-    if (KIND == 1) {
-      const float4 f = *(const float4*)((const float*)inb + 4 * c);
-      h[0] = st_bf16(st_to_bf16(f.x));
-      h[1] = st_bf16(st_to_bf16(f.y));
-      h[2] = st_bf16(st_to_bf16(f.z));
-      h[3] = st_bf16(st_to_bf16(f.w));
+};
+// Unit u of a down piece (stage 2): group ga + u of the tile.
+struct UnitAddr2 {
+  const uint8_t* w;
+  int ga;
+  __device__ __forceinline__ const uint8_t* operator()(int u) const {
+    const int g = ga + u;
+    return w + (size_t)(g >> 3) * kSuperBytes + kBlock * (1 + (g & 7));
+  }
+};
+
+template <int MU, typename Addr>
+__device__ __forceinline__ void issue_units(WaveUnits<MU>& W, const Addr addr,
+                                            const uint8_t* spare) {
+#pragma unroll
+  for (int j = 0; j < MU; ++j) {
+    const int u = W.u0 + kPWaves * j;
+    W.rec[j] = __builtin_nontemporal_load((const u32x4*)(u < W.u1 ? addr(u) : spare));
+  }
+}
+
+// One unit: the row's group sum from the tables at `tab`, times the group's fixed-point factor
+// (LDS `fac`) and fp16 scale (LDS `sc`). Not inlined: one copy serves every unit of every
+// kernel variant, which keeps the kernels' code small.
+__device__ __attribute__((noinline)) float unit_value(u32x4 rec, uint32_t tab, uint32_t fac,
+                                                      uint32_t sc) {
+  const int isum = group_sum(rec, tab);
+  const float f = *(__attribute__((address_space(3))) const float*)(uintptr_t)fac;
+  return (float)isum * f * f16(*(lds_cu16*)(uintptr_t)sc);
+}
+
+// The lookups of a wave's units. Stage 1: tile ti = u / G, group u mod G, table group = group,
+// scale block ti * S + group / 8. Stage 2 (G = units of the piece, S unused): table group u,
+// scale block (ga + u) / 8 - j0.
+template <int MU, bool STAGE1>
+__device__ __forceinline__ void lookup_units(const WaveUnits<MU>& W, int G, int S, int ga, int j0,
+                                             const StLds& L, float (&acc)[kMaxTiles]) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t tab0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)L.tab;
+  const uint32_t sbl0 =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)L.sblk;
+  const uint32_t fac0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const float*)L.fac;
+#pragma unroll
+  for (int j = 0; j < MU; ++j) {
+    const int u = W.u0 + kPWaves * j;
+    if (u >= W.u1) break;
+    int ti = 0, gt = u, blk;
+    if (STAGE1) {
+      ti = (u >= G) + (u >= 2 * G);
+      gt = u - ti * G;
+      blk = ti * S + (gt >> 3);
     } else {
-      const uint2 w = *(const uint2*)((const uint16_t*)inb + 4 * c);
-      h[0] = __uint_as_float(w.x << 16);
-      h[1] = __uint_as_float(w.x & 0xFFFF0000u);
-      h[2] = __uint_as_float(w.y << 16);
-      h[3] = __uint_as_float(w.y & 0xFFFF0000u);
+      blk = ((ga + u) >> 3) - j0;
     }
-  };
-  float ss = 0.f;
-  float hv[2][4];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int c = tid + k * kStThreads;
-    float h[4] = {0.f, 0.f, 0.f, 0.f};
-    if (c < nch) {
-      chunk(c, h);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ss = fmaf(h[i], h[i], ss);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) hv[k][i] = h[i];
-    if (k == 0) issue0(1);
-    __builtin_amdgcn_sched_barrier(0);
+    const int gs = STAGE1 ? gt : ga + u;   // group within the row (for the scale)
+    const uint32_t sb = sbl0 + (uint32_t)blk * kBlock + lane * 16 + (gs & 7) * 2;
+    const float v = unit_value(W.rec[j], tab0 + (uint32_t)gt * kGroupTabBytes,
+                               fac0 + (uint32_t)gt * 4, sb);
+    if (ti == 0) acc[0] += v;
+    else if (ti == 1) acc[1] += v;
+    else acc[2] += v;
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
-  if (lane == 0) L.ssum[wave] = ss;
-  __syncthreads();
-  issue0(2);
-  __builtin_amdgcn_sched_barrier(0);
-  float tot = 0.f;
-#pragma unroll
-  for (int v = 0; v < kStWaves; ++v) tot += L.ssum[v];
-  // kind 0 is not rescaled: with d = y = 1 the division below returns h unchanged
-  const float denom = KIND == 0 ? 1.f : sqrtf(tot / (float)n_in + A.eps);
-  const float rden = 1.f / denom;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int c = tid + k * kStThreads;
-    if (c >= nch) continue;
-    float v[4];
-    uint32_t rb[4], ob[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float h = hv[k][i];
-      rb[i] = st_to_bf16(h);   // h is a bf16 value already
-      ob[i] = st_to_bf16(st_div(h, denom, rden));
-      v[i] = st_bf16(ob[i]);
+}
+
+// KIND 0: x = the step input as it is; 1: x = rms(bf16(sum of the down slots)); 2: x = rms(q).
+// UNITS is false only for the workgroup of the final launch that forms the last x (no tiles).
+//
+// Waves 0-7 (prologue waves) load the input and the scale blocks, form x, build the tables and
+// only then request their own units; waves 8-15 (stream waves) request their units at once
+// (stalling at issue while the memory pipeline is full, which is all they have to do) and start
+// their lookups when the tables are published.
+template <int KIND, bool UNITS>
+__device__ void stage1_run(const S1Args& A, StLds& L, int T, const LaneTile (&lt)[kMaxTiles],
+                           const bool (&pair)[kMaxTiles], int t0, uint16_t* rec_x,
+                           uint16_t* rec_raw) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool prologue = wave < kPWaves;
+  const int n_in = A.hidden;
+  const int nch = n_in / 4;
+  const int G = n_in / kGroup;
+  const int S = (G + kSuper - 1) / kSuper;
+  const int nunits = T * G;
+  const int us = nunits < kPWaves * kUnitsS1 ? nunits : kPWaves * kUnitsS1;   // stream units
+  const UnitAddr1 addr{lt[0].w, lt[1].w, lt[2].w, G};
+  float acc[kMaxTiles] = {0.f, 0.f, 0.f};
+  if (!prologue) {
+    // ---- stream waves ----------------------------------------------------------------------
+    issue_barrier();   // the prologue waves' requests are queued first
+    if (UNITS) {
+      WaveUnits<kUnitsS1> W;
+      W.u0 = wave - kPWaves;
+      W.u1 = us;
+      issue_units(W, addr, lt[0].w);
+      wait_count(&L.arrived_tab, kPWaves);
+      lookup_units<kUnitsS1, true>(W, G, S, 0, 0, L, acc);
     }
-    // one 8-byte store per chunk (the activation slots are 16-byte aligned)
-    if (raw_out) *(uint2*)(raw_out + 4 * c) = make_uint2(rb[0] | rb[1] << 16, rb[2] | rb[3] << 16);
-    if (out) *(uint2*)(out + 4 * c) = make_uint2(ob[0] | ob[1] << 16, ob[2] | ob[3] << 16);
-    const float p0 = -v[0] - v[1], p1 = v[0] - v[1], p2 = v[1] - v[0], p3 = v[0] + v[1];
-    const float q0 = -v[2] - v[3], q1 = v[2] - v[3], q2 = v[3] - v[2], q3 = v[2] + v[3];
-    float4* dst = (float4*)(L.lut + c * 16);
-    // lane l writes row (r + l) mod 4 at step r: with one chunk (64 bytes) per lane, writing
-    // the same row in every lane would put the 16-byte stores on few LDS banks
+  } else {
+    // ---- prologue waves: the input vector and the scale blocks -----------------------------
+    const int pt = tid;   // 0 .. 511
+    uint2 xb[kPRounds];
+    f32x4 pv[kPRounds][kMaxSlots];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int j = (r + lane) & 3;
-      const float qj = j == 0 ? q0 : j == 1 ? q1 : j == 2 ? q2 : q3;
-      dst[j] = make_float4(p0 + qj, p1 + qj, p2 + qj, p3 + qj);
-    }
-  }
+    for (int r = 0; r < kPRounds; ++r) {
+      int c = pt + kPThreads * r;
+      c = c < nch ? c : nch - 1;
+      if (KIND == 1) {
 #pragma unroll
-  for (int i = 3; i < MG; ++i) issue0(i);
-  __syncthreads();
-#pragma unroll
-  for (int t = 0; t < NI; ++t) {
-    // item t + 1's slot i is issued after item t's slot i is computed
-    float part = 0.f;
-#pragma unroll
-    for (int i = 0; i < MG; ++i) {
-      st_compute_slot<MG>(items[t], wave, R[t], L, i, part);
-      if (t + 1 < NI) st_load_slot<MG>(A, items[t + 1], wave, lane, R[t + 1], i);
-    }
-    L.red[t & 1][wave][lane] = part;
-    __syncthreads();
-    if (wave == 0) {
-      float sum = L.red[t & 1][0][lane];
-#pragma unroll
-      for (int v = 1; v < kStWaves; ++v) sum += L.red[t & 1][v][lane];
-      const StMat& M = A.mats[items[t].m];
-      const int row = items[t].tile * kTileRows + lane;
-      if (row < M.n) {
-        if (M.acc) atomicAdd(M.acc + row, sum);
-        else M.y[row] = st_to_bf16(sum);
+        for (int s = 0; s < kMaxSlots; ++s) {
+          const int ss = s < A.nslots ? s : A.nslots - 1;
+          pv[r][s] = *(const f32x4*)(A.part + (size_t)ss * n_in + 4 * c);
+        }
+      } else {
+        xb[r] = *(const uint2*)((KIND == 0 ? A.x0 : A.q_prev) + 4 * c);
       }
     }
+    if (UNITS) {
+#pragma unroll
+      for (int k = 0; k < kMaxBlocks / kPWaves; ++k) {
+        int b = wave + kPWaves * k;
+        b = b < T * S ? b : T * S - 1;
+        const int ti = (b >= S) + (b >= 2 * S);
+        const uint8_t* w = ti == 0 ? lt[0].w : (ti == 1 ? lt[1].w : lt[2].w);
+        copy_block(w + (size_t)(b - ti * S) * kSuperBytes, L.sblk[b]);
+      }
+    }
+    issue_barrier();
+    // ---- input values, sum of squares, rescale ---------------------------------------------
+    float h[kPRounds][4];
+    uint32_t raw[kPRounds][4];
+    float ss = 0.f;
+#pragma unroll
+    for (int r = 0; r < kPRounds; ++r) {
+      const bool ok = pt + kPThreads * r < nch;
+      if (KIND == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float sum = pv[r][0][i];
+#pragma unroll
+          for (int s = 1; s < kMaxSlots; ++s) sum += s < A.nslots ? pv[r][s][i] : -0.f;
+          raw[r][i] = to_bf16(sum);            // down_{l-1} as the record holds it
+          h[r][i] = ok ? bf(raw[r][i]) : 0.f;
+        }
+      } else {
+        raw[r][0] = xb[r].x & 0xFFFFu;
+        raw[r][1] = xb[r].x >> 16;
+        raw[r][2] = xb[r].y & 0xFFFFu;
+        raw[r][3] = xb[r].y >> 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[r][i] = ok ? bf(raw[r][i]) : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ss = fmaf(h[r][i], h[r][i], ss);
+    }
+    float denom = 1.f, rden = 1.f;
+    if (KIND != 0) {
+      const float tot = prologue_sum(ss, L);
+      denom = sqrtf(tot / (float)n_in + A.eps);
+      rden = 1.f / denom;
+    }
+    // ---- bf16 inputs, record slots, fixed point, tables ------------------------------------
+    char* tab = (char*)L.tab;
+#pragma unroll
+    for (int r = 0; r < kPRounds; ++r) {
+      const int c = pt + kPThreads * r;
+      if (r > 0 && (kPThreads * r >= nch)) break;   // uniform: no chunk of this round exists
+      const bool ok = c < nch;
+      float v[4];
+      uint32_t ob[4];
+      float m = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ob[i] = KIND == 0 ? raw[r][i] : to_bf16(div_corr(h[r][i], denom, rden));
+        v[i] = bf(ob[i]);
+        m = fmaxf(m, fabsf(v[i]));
+      }
+      // a group is 32 chunks: 32 consecutive threads, half a wave
+      const int E = exponent_above(half_max(ok ? m : 0.f));
+      if (ok) {
+        if (rec_x) *(uint2*)(rec_x + 4 * c) = make_uint2(ob[0] | ob[1] << 16, ob[2] | ob[3] << 16);
+        if (rec_raw)
+          *(uint2*)(rec_raw + 4 * c) = make_uint2(raw[r][0] | raw[r][1] << 16,
+                                                  raw[r][2] | raw[r][3] << 16);
+        put_table(tab, (uint32_t)c * 64, v, 22 - E, lane);
+        if ((c & 31) == 0) L.fac[c >> 5] = __builtin_ldexpf(1.f, E - 22);
+      }
+    }
+    wait_vm<0>();   // this wave's scale blocks are in LDS
+    arrive(&L.arrived_tab);
+    if (UNITS) {
+      WaveUnits<kUnitsP1> W;
+      W.u0 = us + wave;
+      W.u1 = nunits;
+      issue_units(W, addr, lt[0].w);
+      wait_count(&L.arrived_tab, kPWaves);
+      lookup_units<kUnitsP1, true>(W, G, S, 0, 0, L, acc);
+    }
+  }
+  if (!UNITS) return;
+  // ---- per-tile sums (waves in order), outputs, pair statistics ----------------------------
+  L.red[0][wave][lane] = acc[0];
+  if (T > 1) L.red[1][wave][lane] = acc[1];
+  if (T > 2) L.red[2][wave][lane] = acc[2];
+  __syncthreads();
+  if (wave < T) {
+    float y = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) y += L.red[wave][w][lane];
+    const int i = wave;
+    const uint32_t yb = to_bf16(y);
+    uint16_t* yp = i == 0 ? lt[0].y : (i == 1 ? lt[1].y : lt[2].y);
+    const int row = i == 0 ? lt[0].row : (i == 1 ? lt[1].row : lt[2].row);
+    const int n = i == 0 ? lt[0].n : (i == 1 ? lt[1].n : lt[2].n);
+    if (row < n) yp[row] = (uint16_t)yb;
+    const bool pr = i == 0 ? pair[0] : (i == 1 ? pair[1] : pair[2]);
+    if (pr) {   // uniform: gate (lanes 0-31) times up (lanes 32-63) of the same rows
+      const float other = bf((uint32_t)__shfl_xor((int)yb, 32, 64));
+      const float hv = bf(yb) * other;
+      const float sq = wave_sum(lane < 32 ? hv * hv : 0.f);
+      if (lane == 0) A.stat[t0 + i - A.nsingle] = sq;
+    }
   }
 }
 
-template <int KIND, int MI, int MG>
-__device__ void st_run_lds(const StArgs& A, int n_in, uint16_t* out, uint16_t* raw_out,
-                           int nitems, const StItem (&items)[kStMaxItems], StLds& L) {
-  // vmcnt(0), seen by the compiler: where other code paths merge in front of this one, loads it
-  // believes are still pending would otherwise make it wait for weights issued later
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  if (nitems <= 0) st_run_lds_n<KIND, 0, MG>(A, n_in, out, raw_out, items, L);
-  else if (MI == 1 || nitems == 1) st_run_lds_n<KIND, 1, MG>(A, n_in, out, raw_out, items, L);
-  else if (MI == 2 || nitems == 2) st_run_lds_n<KIND, (MI >= 2 ? 2 : 1), MG>(A, n_in, out, raw_out, items, L);
-  else st_run_lds_n<KIND, (MI >= 3 ? 3 : 1), MG>(A, n_in, out, raw_out, items, L);
+__global__ __launch_bounds__(kThreads) void stage1_kernel(S1Args A) {
+  __shared__ StLds L;
+  const int b = blockIdx.x, lane = threadIdx.x & 63;
+  if (threadIdx.x == 0) {
+    L.arrived_sum = 0;
+    L.arrived_tab = 0;
+  }
+  const bool is_x = b < A.x_wgs;
+  const int i = is_x ? b : b - A.x_wgs;
+  const int q = is_x ? A.x_q : A.o_q, r = is_x ? A.x_r : A.o_r;
+  const int t0 = i * q + (i < r ? i : r);
+  const int T = q + (i < r ? 1 : 0);
+  // a tile index past the workgroup's run repeats its first tile (loaded, never used)
+  LaneTile lt[kMaxTiles];
+  bool pair[kMaxTiles] = {false, false, false};
+  if (is_x) {
+#pragma unroll
+    for (int k = 0; k < kMaxTiles; ++k) lt[k] = lane_tile_x(A, t0 + (k < T ? k : 0), lane, pair[k]);
+    const bool writer = b == A.x_wgs - 1;   // holds the fewest tiles
+    uint16_t* rx = writer ? A.x_out : nullptr;
+    if (A.x0) stage1_run<0, true>(A, L, T, lt, pair, t0, rx, nullptr);
+    else if (T > 0) stage1_run<1, true>(A, L, T, lt, pair, t0, rx, writer ? A.down_out : nullptr);
+    else stage1_run<1, false>(A, L, T, lt, pair, t0, rx, writer ? A.down_out : nullptr);
+  } else {
+#pragma unroll
+    for (int k = 0; k < kMaxTiles; ++k) lt[k] = lane_tile(A.o, t0 + (k < T ? k : 0), lane);
+    const bool writer = b == A.x_wgs + A.o_wgs - 1;
+    stage1_run<2, true>(A, L, T, lt, pair, t0, writer ? A.xo_out : nullptr, nullptr);
+  }
 }
 
-// Kind 3 (stage 2, a half of down; input rms(gate ⊙ up)). gate and up are copied whole into the
-// table area with LDS-direct loads and waited for; then the item's weights are issued. While they
-// stream, the sum of squares of h = gate ⊙ up is taken from LDS, each thread keeps h for the
-// table chunks it will build (at most 3 chunks), and after the barrier that ends every read of the
-// copies the tables of the workgroup's half are written over them.
-template <int MG, int NI>
-__device__ void st_run_down(const StArgs& A, uint16_t* out, const StItem (&items)[kStMaxItems],
-                            StLds& L) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n_in = A.ffn;
-  const uint16_t* gs = (const uint16_t*)L.lut;             // gate copy
-  const uint16_t* us = (const uint16_t*)L.lut + n_in;      // up copy
-  const uint32_t nbytes = (uint32_t)n_in * 2u;
-  const uint32_t ninst = (nbytes + 1023u) / 1024u;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)L.lut;
-  for (uint32_t i = wave; i < ninst; i += kStWaves) {
-    const uint32_t voff = i * 1024u + lane * 16u;
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + i * 1024u);
-    if (voff < nbytes) st_dma16(A.gate, voff, dst);
+__global__ __launch_bounds__(kThreads) void stage2_kernel(S2Args A) {
+  __shared__ StLds L;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (tid == 0) {
+    L.arrived_sum = 0;
+    L.arrived_tab = 0;
   }
-  for (uint32_t i = wave; i < ninst; i += kStWaves) {
-    const uint32_t voff = i * 1024u + lane * 16u;
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + nbytes + i * 1024u);
-    if (voff < nbytes) st_dma16(A.up, voff, dst);
-  }
-  st_wait_vm<0>();
-  __syncthreads();
-  // the weight slots are issued between pieces of the prologue (a wave stalls at issue while the
-  // memory pipeline is full; the work between issues keeps its VALU busy meanwhile)
-  StRegs<MG> R;
-  auto issue = [&](int i) {
-    if (NI > 0 && i < MG) st_load_slot<MG>(A, items[0], wave, lane, R, i);
-  };
-  issue(0);
-  const int c0 = NI > 0 ? items[0].ga * kGroup / 4 : 0;
-  const int c1 = NI > 0 ? items[0].gb * kGroup / 4 : 0;
-  // sum of squares over chunks (4 inputs) in the order c0 + tid + 1024 k, wrapping at the end;
-  // the first three visits of a thread are the table chunks it builds, whose h it keeps
-  const int nch = n_in / 4;
-  auto hchunk = [&](int c, float (&h)[4]) {
-    const uint2 g = *(const uint2*)(gs + 4 * c);
-    const uint2 u = *(const uint2*)(us + 4 * c);
-    h[0] = __uint_as_float(g.x << 16) * __uint_as_float(u.x << 16);
-    h[1] = __uint_as_float(g.x & 0xFFFF0000u) * __uint_as_float(u.x & 0xFFFF0000u);
-    h[2] = __uint_as_float(g.y << 16) * __uint_as_float(u.y << 16);
-    h[3] = __uint_as_float(g.y & 0xFFFF0000u) * __uint_as_float(u.y & 0xFFFF0000u);
-  };
-  float ss = 0.f;
-  float hv[3][4];
+  const int t = blockIdx.x / A.pieces, p = blockIdx.x - t * A.pieces;
+  const int ga = A.pg[p], gb = A.pg[p + 1];
+  const int nunits = gb - ga;
+  const int us = nunits < kPWaves * kUnitsS2 ? nunits : kPWaves * kUnitsS2;   // stream units
+  const uint8_t* tw = A.down.w + (size_t)t * A.down.tile_bytes + lane * 16;
+  const int j0 = ga >> 3;
+  const UnitAddr2 addr{tw, ga};
+  const uint8_t* spare = tw + (size_t)j0 * kSuperBytes;
+  float acc[kMaxTiles] = {0.f, 0.f, 0.f};
+  if (wave >= kPWaves) {
+    // ---- stream waves ----------------------------------------------------------------------
+    issue_barrier();   // the prologue waves' requests are queued first
+    WaveUnits<kUnitsS2> W;
+    W.u0 = wave - kPWaves;
+    W.u1 = us;
+    issue_units(W, addr, spare);
+    wait_count(&L.arrived_tab, kPWaves);
+    lookup_units<kUnitsS2, false>(W, nunits, 0, ga, j0, L, acc);
+  } else {
+    // ---- prologue waves: the pair tiles' sums of squares, this piece's gate and up, and the
+    //      scale blocks ------------------------------------------------------------------------
+    const int pt = tid;   // 0 .. 511
+    const int npair = A.ffn / 32;
+    const int c8a = ga * (kGroup / 8), n8 = nunits * (kGroup / 8);
+    float st[kPRounds2];
+    u32x4 go[kPRounds2], uo[kPRounds2];
 #pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    const int t = tid + k * kStThreads;
-    float h[4] = {0.f, 0.f, 0.f, 0.f};
-    if (t < nch) {
-      const int c = c0 + t < nch ? c0 + t : c0 + t - nch;
-      hchunk(c, h);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ss = fmaf(h[i], h[i], ss);
+    for (int r = 0; r < kPRounds2; ++r) {
+      const int i = pt + kPThreads * r;
+      st[r] = A.stat[i < npair ? i : npair - 1];
+      const int c = c8a + (i < n8 ? i : n8 - 1);
+      go[r] = *(const u32x4*)(A.gate + 8 * c);
+      uo[r] = *(const u32x4*)(A.up + 8 * c);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) hv[k][i] = h[i];
-    if (k == 0) issue(1);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  for (int t = tid + 3 * kStThreads; t < nch; t += kStThreads) {
-    const int c = c0 + t < nch ? c0 + t : c0 + t - nch;
-    float h[4];
-    hchunk(c, h);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ss = fmaf(h[i], h[i], ss);
-  }
-  issue(2);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
-  if (lane == 0) L.ssum[wave] = ss;
-  __syncthreads();   // every read of the copies is done: the tables may overwrite them
-  issue(3);
-  __builtin_amdgcn_sched_barrier(0);
-  float tot = 0.f;
-#pragma unroll
-  for (int v = 0; v < kStWaves; ++v) tot += L.ssum[v];
-  const float denom = sqrtf(tot / (float)n_in + A.eps);
-  const float rden = 1.f / denom;
-#pragma unroll
-  for (int it = 0; it < 3; ++it) {
-    if (it == 1) issue(4);
-    __builtin_amdgcn_sched_barrier(0);
-    const int c = c0 + tid + it * kStThreads;
-    if (c >= c1) continue;
-    float v[4];
-    uint32_t ob[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ob[i] = st_to_bf16(st_div(hv[it][i], denom, rden));
-      v[i] = st_bf16(ob[i]);
+    {
+      const int nblk = ((gb - 1) >> 3) - j0 + 1;
+      const int b = wave < nblk ? wave : nblk - 1;
+      copy_block(tw + (size_t)(j0 + b) * kSuperBytes, L.sblk[b]);
     }
-    if (out) *(uint2*)(out + 4 * c) = make_uint2(ob[0] | ob[1] << 16, ob[2] | ob[3] << 16);
-    const float p0 = -v[0] - v[1], p1 = v[0] - v[1], p2 = v[1] - v[0], p3 = v[0] + v[1];
-    const float q0 = -v[2] - v[3], q1 = v[2] - v[3], q2 = v[3] - v[2], q3 = v[2] + v[3];
-    float4* dst = (float4*)(L.lut + (c - c0) * 16);
-    // lane l writes row (r + l) mod 4 at step r: with one chunk (64 bytes) per lane, writing
-    // the same row in every lane would put the 16-byte stores on few LDS banks
+    issue_barrier();
+    // ---- the rescale of h = gate * up (the pair tiles' sums in a fixed order) --------------
+    float ss = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int j = (r + lane) & 3;
-      const float qj = j == 0 ? q0 : j == 1 ? q1 : j == 2 ? q2 : q3;
-      dst[j] = make_float4(p0 + qj, p1 + qj, p2 + qj, p3 + qj);
+    for (int r = 0; r < kPRounds2; ++r) ss += pt + kPThreads * r < npair ? st[r] : 0.f;
+    const float tot = prologue_sum(ss, L);
+    const float denom = sqrtf(tot / (float)A.ffn + A.eps);
+    const float rden = 1.f / denom;
+    // ---- xd over the piece: record (pieces of tile 0), fixed point, tables -----------------
+    char* tab = (char*)L.tab;
+#pragma unroll
+    for (int r = 0; r < kPRounds2; ++r) {
+      const int i = pt + kPThreads * r;
+      if (r > 0 && kPThreads * r >= n8) break;   // uniform
+      const bool own = i < n8;
+      float v[8];
+      uint32_t ob[8];
+      float m = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t gw = go[r][k >> 1], uw = uo[r][k >> 1];
+        const float gf = (k & 1) ? __uint_as_float(gw & 0xFFFF0000u) : bf(gw & 0xFFFFu);
+        const float uf = (k & 1) ? __uint_as_float(uw & 0xFFFF0000u) : bf(uw & 0xFFFFu);
+        ob[k] = to_bf16(div_corr(gf * uf, denom, rden));   // gate * up is exact in fp32
+        v[k] = bf(ob[k]);
+        m = fmaxf(m, fabsf(v[k]));
+      }
+      // a group is 16 chunks of 8: one row of 16 lanes
+      const int E = exponent_above(row_max(own ? m : 0.f));
+      if (own) {
+        if (t == 0)
+          *(u32x4*)(A.xd_out + 8 * (c8a + i)) =
+              u32x4{ob[0] | ob[1] << 16, ob[2] | ob[3] << 16, ob[4] | ob[5] << 16,
+                    ob[6] | ob[7] << 16};
+        const float v0[4] = {v[0], v[1], v[2], v[3]}, v1[4] = {v[4], v[5], v[6], v[7]};
+        put_table(tab, (uint32_t)i * 128, v0, 22 - E, lane);
+        put_table(tab, (uint32_t)i * 128 + 64, v1, 22 - E, lane);
+        if ((i & 15) == 0) L.fac[i >> 4] = __builtin_ldexpf(1.f, E - 22);
+      }
     }
+    wait_vm<0>();   // this wave's scale block is in LDS
+    arrive(&L.arrived_tab);
+    WaveUnits<kUnitsP2> W;
+    W.u0 = us + wave;
+    W.u1 = nunits;
+    issue_units(W, addr, spare);
+    wait_count(&L.arrived_tab, kPWaves);
+    lookup_units<kUnitsP2, false>(W, nunits, 0, ga, j0, L, acc);
   }
-#pragma unroll
-  for (int i = 5; i < MG; ++i) issue(i);
-  __syncthreads();
-  if (NI <= 0) return;
-  const float part = st_compute<MG>(items[0], wave, R, L);
-  L.red[0][wave][lane] = part;
+  L.red[0][wave][lane] = acc[0];
   __syncthreads();
   if (wave == 0) {
-    float sum = L.red[0][0][lane];
+    float y = 0.f;
 #pragma unroll
-    for (int v = 1; v < kStWaves; ++v) sum += L.red[0][v][lane];
-    const StMat& M = A.mats[items[0].m];
-    const int row = items[0].tile * kTileRows + lane;
-    if (row < M.n) {
-      if (M.acc) atomicAdd(M.acc + row, sum);
-      else M.y[row] = st_to_bf16(sum);
-    }
+    for (int w = 0; w < kWaves; ++w) y += L.red[0][w][lane];
+    const int row = t * kTileRows + lane;
+    if (row < A.hidden) A.part[(size_t)p * A.hidden + row] = y;
   }
 }
 
-template <int MI, int MG>
-__global__ __launch_bounds__(kStThreads) void stage_kernel(StArgs A) {
-  __shared__ StLds L;
-  const int tid = threadIdx.x;
-  StItem items[kStMaxItems];
-  int nitems = 0;
-#pragma unroll
-  for (int t = 0; t < MI; ++t) {
-    if (nitems == t && st_item(A, t, items[t])) nitems = t + 1;
-    else if (t > 0) items[t] = items[t - 1];   // a slot past the last item repeats it
-  }
-
-  // the input kind of this workgroup's items and the activation slot it writes, if any
-  int kind, n_in;
-  uint16_t* out = nullptr;
-  if (A.stage == 1) {
-    kind = A.x0 ? 0 : 1;
-    n_in = A.hidden;
-    if (blockIdx.x == gridDim.x - 1) {   // holds the fewest tiles
-      out = A.x_out;
-      if (A.acc_zero)
-        for (int j = tid; j < A.hidden; j += kStThreads) A.acc_zero[j] = 0.f;
-    }
-  } else if (nitems == 0 || items[0].m == 0) {
-    kind = 2;
-    n_in = A.hidden;
-    if (blockIdx.x == 0) out = A.xo_out;
-  } else {
-    kind = 3;
-    n_in = A.ffn;
-    if (items[0].tile == 0) out = A.xd_out;   // each half writes its own inputs
-  }
-  if (MI > 1) {   // stage 1
-    if (kind == 0) st_run_lds<0, MI, MG>(A, n_in, out, nullptr, nitems, items, L);
-    else st_run_lds<1, MI, MG>(A, n_in, out, blockIdx.x == gridDim.x - 1 ? A.down_out : nullptr, nitems, items, L);
-  } else {
-    // o tiles span hidden / 128 <= 48 groups: three slots per wave cover them (the down
-    // halves need MG)
-    if (kind == 2) st_run_lds<2, MI, kSt1G>(A, n_in, out, nullptr, nitems, items, L);
-    else if (nitems > 0) st_run_down<MG, 1>(A, out, items, L);
-    else st_run_down<MG, 0>(A, out, items, L);
-  }
-}
-
-// two fp32 accumulators of `hidden` floats per device, allocated once, never freed
-constexpr int kStMaxDevices = 64;
-struct StWork {
-  float* acc = nullptr;
-  size_t floats = 0;
-};
-StWork g_st_work[kStMaxDevices];
+// One workspace per device and stream, allocated on first use and kept until the process exits:
+// the down partial slots (kPartFloats) and the pair-tile sums of squares (kStatFloats). Its size
+// never changes, so nothing is ever freed or replaced under a queued launch or a captured graph.
+constexpr size_t kStatFloats = 1024;   // ffn / 32 <= 1024
+std::map<std::pair<int, uintptr_t>, float*> g_st_ws;
 std::mutex g_st_mu;
 
-lbq_status st_workspace(int hidden, hipStream_t s, float** acc) {
+lbq_status st_workspace(hipStream_t s, float** out) {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kStMaxDevices) return LBQ_E_DEVICE;
+  if (hipGetDevice(&dev) != hipSuccess) return LBQ_E_DEVICE;
   std::lock_guard<std::mutex> lock(g_st_mu);
-  StWork& W = g_st_work[dev];
-  const size_t need = 2 * (size_t)hidden;
-  if (W.floats < need) {
+  float*& p = g_st_ws[{dev, (uintptr_t)s}];
+  if (!p) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(s, &cs) != hipSuccess) return LBQ_E_DEVICE;
     if (cs != hipStreamCaptureStatusNone) return LBQ_E_NOMEM;
-    void* p = nullptr;
-    if (hipMalloc(&p, need * sizeof(float)) != hipSuccess) return LBQ_E_NOMEM;
-    // the previous buffer may still be in use by queued work: it is kept, not freed
-    W.acc = (float*)p;
-    W.floats = need;
+    void* q = nullptr;
+    if (hipMalloc(&q, (kPartFloats + kStatFloats) * sizeof(float)) != hipSuccess)
+      return LBQ_E_NOMEM;
+    p = (float*)q;
   }
-  *acc = W.acc;
+  *out = p;
   return LBQ_OK;
 }
 
-StMat st_mat(const void* w, int n, int k, uint16_t* y, float* acc) {
+StMat st_mat(const void* w, int n, int k, uint16_t* y) {
   Geometry g;
   make_geometry(n, k, kQ1GroupBlocks, &g);
   StMat m;
   m.w = (const uint8_t*)w;
   m.y = y;
-  m.acc = acc;
   m.n = n;
   m.tiles = (int)g.tiles;
-  m.groups = (int)g.groups;
   m.tile_bytes = g.tile_bytes;
   return m;
 }
 
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
 }  // namespace
 
-// Batch-1 decode step through the stage kernels. Shapes are validated by the caller; returns
-// LBQ_E_UNSUPPORTED where the stage kernels do not apply.
+// Batch-1 decode step through the stage kernels. Shapes and pointers are validated by the
+// caller; returns LBQ_E_UNSUPPORTED (having launched nothing) where the stage kernels do not
+// apply.
 lbq_status lbq::stage_decode_q1(const lbq_q1_layer* layers, int n_layers, int hidden, int kv,
                                 int ffn, const uint16_t* d_x0, uint16_t* d_act, float eps,
                                 void* stream) {
   hipStream_t s = (hipStream_t)stream;
   if (hidden % kGroup || kv % kGroup || ffn % kGroup) return LBQ_E_UNSUPPORTED;
-  // the LDS copies of q need its slot 16-byte aligned (slot offsets are multiples of 256 bytes)
-  if ((uintptr_t)d_act % 16 || (uintptr_t)d_x0 % 16) return LBQ_E_UNSUPPORTED;
-  const int hg = hidden / kGroup, fg = ffn / kGroup;
-  if (hg > kStWaves * kSt1G || hidden / 4 > kStMaxChunks) return LBQ_E_UNSUPPORTED;
-  // tables (64 B per 4 inputs) plus the LDS copy of an fp32 input vector (4 B per input)
-  if ((size_t)hidden * 20 > sizeof(StLds::lut)) return LBQ_E_UNSUPPORTED;
-  if (hidden / 4 > 2 * kStThreads) return LBQ_E_UNSUPPORTED;   // two table chunks per thread
-  const int split = (fg + 1) / 2;   // the halves may share a super-group's scale record
-  const int half0 = split, half1 = fg - half0;
-  if (half0 > kStWaves * kSt2G || half1 > kStWaves * kSt2G || half0 * kGroup / 4 > kStMaxChunks)
-    return LBQ_E_UNSUPPORTED;
-  // stage 2 copies gate and up (bf16) into the table area; a thread builds at most 3 chunks
-  if ((size_t)ffn * 4 > sizeof(StLds::lut) || half0 * kGroup / 4 > 3 * kStThreads ||
-      half1 * kGroup / 4 > 3 * kStThreads)
-    return LBQ_E_UNSUPPORTED;
-  float* acc = nullptr;
-  const lbq_status ws = st_workspace(hidden, s, &acc);
-  if (ws != LBQ_OK) return ws;
+  if ((uintptr_t)d_act % 16 || (uintptr_t)d_x0 % 8) return LBQ_E_UNSUPPORTED;
+  const int G = hidden / kGroup, FG = ffn / kGroup;
+  const int S = ceil_div(G, kSuper);
+  if (G > kTabGroups || hidden / 4 > kPRounds * kPThreads) return LBQ_E_UNSUPPORTED;
+  if ((size_t)ffn / 32 > kStatFloats || ffn / 32 > kPRounds2 * kPThreads) return LBQ_E_UNSUPPORTED;
+  // tiles per stage-1 workgroup: within the units of its waves and the scale blocks it stages
+  const int wg_units1 = kPWaves * (kUnitsS1 + kUnitsP1);
+  int tmax = kMaxTiles;
+  if (tmax > wg_units1 / G) tmax = wg_units1 / G;
+  if (tmax > kMaxBlocks / S) tmax = kMaxBlocks / S;
+  if (tmax < 1) return LBQ_E_UNSUPPORTED;
   int cus = 0, dev = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return LBQ_E_DEVICE;
+  // down pieces: as many as the compute units allow (at most kMaxSlots), each within the table
+  // capacity, the units of one piece per wave and its scale blocks per workgroup
+  const int down_tiles = hidden / kTileRows;
+  const int wg_units2 = kPWaves * (kUnitsS2 + kUnitsP2);
+  const int piece_cap = wg_units2 < kTabGroups ? wg_units2 : kTabGroups;
+  int P = cus / down_tiles;
+  if (P > kMaxSlots) P = kMaxSlots;
+  if (P < ceil_div(FG, piece_cap)) P = ceil_div(FG, piece_cap);
+  if (P > FG) P = FG;
+  if (P < 1) P = 1;
+  if (P > kMaxSlots || ceil_div(FG, P) > piece_cap) return LBQ_E_UNSUPPORTED;
+  int pg[kMaxSlots + 1];
+  for (int p = 0; p <= P; ++p) pg[p] = (int)((long long)p * FG / P);
+  for (int p = 0; p < P; ++p)
+    if (((pg[p + 1] - 1) >> 3) - (pg[p] >> 3) + 1 > kPWaves) return LBQ_E_UNSUPPORTED;
+  if ((size_t)P * hidden > kPartFloats) return LBQ_E_UNSUPPORTED;
+  float* ws = nullptr;
+  const lbq_status wst = st_workspace(s, &ws);
+  if (wst != LBQ_OK) return wst;
+  float* part = ws;
+  float* stat = ws + kPartFloats;
   auto at = [&](int layer, int slot) {
     return d_act + lbq_decode_act_offset(layer, slot, n_layers, hidden, kv, ffn, 1);
   };
+  const int o_tiles = hidden / kTileRows;
   for (int l = 0; l <= n_layers; ++l) {
-    float* acc_prev = acc + (size_t)((l + 1) % 2) * hidden;   // filled by stage 2 of layer l - 1
-    float* acc_cur = acc + (size_t)(l % 2) * hidden;
-    StArgs A;
+    S1Args A;
     memset(&A, 0, sizeof(A));
-    A.stage = 1;
     A.hidden = hidden;
-    A.ffn = ffn;
     A.eps = eps;
     A.x0 = l == 0 ? d_x0 : nullptr;
-    A.acc_in = l == 0 ? nullptr : acc_prev;
+    A.part = l == 0 ? nullptr : part;
+    A.nslots = P;
     A.down_out = l == 0 ? nullptr : at(l - 1, LBQ_ACT_DOWN);
     A.x_out = l < n_layers ? at(l, LBQ_ACT_X)
                            : d_act + lbq_decode_act_offset(n_layers, LBQ_ACT_NSLOTS, n_layers,
                                                            hidden, kv, ffn, 1);
-    int tiles = 0;
+    A.stat = stat;
+    int x_tiles = 0;
     if (l < n_layers) {
       const lbq_q1_layer& Ly = layers[l];
-      A.acc_zero = acc_cur;
-      A.mats[0] = st_mat(Ly.q, hidden, hidden, at(l, LBQ_ACT_Q), nullptr);
-      A.mats[1] = st_mat(Ly.k, kv, hidden, at(l, LBQ_ACT_K), nullptr);
-      A.mats[2] = st_mat(Ly.v, kv, hidden, at(l, LBQ_ACT_V), nullptr);
-      A.mats[3] = st_mat(Ly.gate, ffn, hidden, at(l, LBQ_ACT_GATE), nullptr);
-      A.mats[4] = st_mat(Ly.up, ffn, hidden, at(l, LBQ_ACT_UP), nullptr);
-      A.nmats = 5;
-      for (int m = 0; m < 5; ++m) tiles += A.mats[m].tiles;
+      A.mats[0] = st_mat(Ly.q, hidden, hidden, at(l, LBQ_ACT_Q));
+      A.mats[1] = st_mat(Ly.k, kv, hidden, at(l, LBQ_ACT_K));
+      A.mats[2] = st_mat(Ly.v, kv, hidden, at(l, LBQ_ACT_V));
+      A.gate = st_mat(Ly.gate, ffn, hidden, at(l, LBQ_ACT_GATE));
+      A.up = st_mat(Ly.up, ffn, hidden, at(l, LBQ_ACT_UP));
+      A.nsingle = A.mats[0].tiles + A.mats[1].tiles + A.mats[2].tiles;
+      A.npair = 2 * A.gate.tiles;
+      x_tiles = A.nsingle + A.npair;
     }
-    // at most kStMaxItems tiles per workgroup, at least one workgroup per compute unit
-    int grid1 = (tiles + kStMaxItems - 1) / kStMaxItems;
-    if (grid1 < cus) grid1 = cus;
-    if (grid1 > tiles) grid1 = tiles;
-    if (l == n_layers) grid1 = 1;
-    hipLaunchKernelGGL((stage_kernel<kSt1Items, kSt1G>), dim3(grid1), dim3(kStThreads), 0, s, A);
+    if (l > 0) {
+      A.o = st_mat(layers[l - 1].o, hidden, hidden, at(l - 1, LBQ_ACT_O));
+      A.q_prev = at(l - 1, LBQ_ACT_Q);
+      A.xo_out = at(l - 1, LBQ_ACT_XO);
+      // o workgroups in proportion to their tiles, at most tmax tiles each
+      int ow = (int)((long long)cus * o_tiles / (o_tiles + x_tiles));
+      if (ow < ceil_div(o_tiles, tmax)) ow = ceil_div(o_tiles, tmax);
+      if (ow > o_tiles) ow = o_tiles;
+      A.o_wgs = ow;
+      A.o_q = o_tiles / ow;
+      A.o_r = o_tiles % ow;
+    }
+    if (x_tiles > 0) {
+      int xw = cus - A.o_wgs;
+      if (xw > x_tiles) xw = x_tiles;
+      if (xw < ceil_div(x_tiles, tmax)) xw = ceil_div(x_tiles, tmax);
+      A.x_wgs = xw;
+      A.x_q = x_tiles / xw;
+      A.x_r = x_tiles % xw;
+    } else {
+      A.x_wgs = 1;   // the final launch: one workgroup forms x_{n_layers}, with no tiles
+    }
+    hipLaunchKernelGGL(stage1_kernel, dim3(A.x_wgs + A.o_wgs), dim3(kThreads), 0, s, A);
     if (l == n_layers) break;
 
     const lbq_q1_layer& Ly = layers[l];
-    StArgs B;
+    S2Args B;
     memset(&B, 0, sizeof(B));
-    B.stage = 2;
+    B.down = st_mat(Ly.down, hidden, ffn, nullptr);
+    B.pieces = P;
+    for (int p = 0; p <= P; ++p) B.pg[p] = pg[p];
     B.hidden = hidden;
     B.ffn = ffn;
     B.eps = eps;
-    B.q = at(l, LBQ_ACT_Q);
     B.gate = at(l, LBQ_ACT_GATE);
     B.up = at(l, LBQ_ACT_UP);
-    B.xo_out = at(l, LBQ_ACT_XO);
+    B.stat = stat;
     B.xd_out = at(l, LBQ_ACT_XD);
-    B.down_split_g = split;
-    B.mats[0] = st_mat(Ly.o, hidden, hidden, at(l, LBQ_ACT_O), nullptr);
-    B.mats[1] = st_mat(Ly.down, hidden, ffn, nullptr, acc_cur);
-    B.nmats = 2;
-    const int grid2 = B.mats[0].tiles + 2 * B.mats[1].tiles;
-    hipLaunchKernelGGL((stage_kernel<1, kSt2G>), dim3(grid2), dim3(kStThreads), 0, s, B);
+    B.part = part;
+    hipLaunchKernelGGL(stage2_kernel, dim3(down_tiles * P), dim3(kThreads), 0, s, B);
   }
   return hipGetLastError() == hipSuccess ? LBQ_OK : LBQ_E_DEVICE;
 }
