@@ -13,15 +13,20 @@
 //    and leaves the sum of its squares for the rescale of stage 2 (which then reads 2 KiB of
 //    sums instead of all of gate and up).
 //  * Stage 2 of layer l: down from rms(gate * up). Every 64-row tile is split along k into P
-//    pieces (P <= 4); the workgroup of piece p writes its fp32 partial sums to slot p, and the
+//    pieces (P <= 3); the workgroup of piece p writes its fp32 partial sums to slot p, and the
 //    next stage 1 adds the slots in slot order.
-//  * Load order inside a workgroup: the input vector first, then the scale blocks of its tiles
-//    (1 KiB each, copied straight into LDS), then the first units of every wave (a unit is one
-//    128-weight group of one 64-row tile: 16 bytes per lane). While those stream, the workgroup
-//    forms its input and builds its tables; every later unit is requested a fixed number of
-//    units ahead of its use. A wave issues its memory instructions in order and stalls at issue
-//    once the compute unit's memory pipeline is full, so requesting every unit up front would
-//    hold the prologue back behind the weights.
+//  * Wave roles inside a workgroup of 16 waves. Waves 8-15 (stream waves) request all of their
+//    units at once (a unit is one 128-weight group of one 64-row tile: 16 bytes per lane) and
+//    wait for the tables. Waves 0-7 (prologue waves) first request the input vector and the scale
+//    blocks of the workgroup's tiles (1 KiB each, staged in LDS through registers), form the
+//    input, build the tables and publish them, and only then request their own units. A wave
+//    issues its memory instructions in order and stalls at issue while the compute unit's
+//    memory pipeline is full, so a wave that requested weights up front could do nothing else
+//    until they arrive; the split keeps the weights streaming while the tables are built. The
+//    prologue waves hold more units than the stream waves, so that all 16 finish their lookups
+//    at about the same time.
+//  * Hand-offs between the waves go through counters in LDS (the LDS serves a compute unit's
+//    requests in order); no wave ever waits on a global-memory fence.
 //  * Tables: for every 4 consecutive inputs, the 16 signed sums +-x0 +-x1 +-x2 +-x3, as exact
 //    int32 fixed-point values. Within a 128-input group every input is put on the fixed point
 //    2^(E - 22), where 2^E is above the group's largest magnitude: a bf16 input is represented
@@ -51,20 +56,23 @@ namespace {
 
 constexpr int kWaves = 16;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kPWaves = 8;             // prologue waves (0-7); waves 8-15 stream weights at once
+constexpr int kPWaves = 8;             // prologue waves 0 .. kPWaves - 1; the others stream
+constexpr int kSWaves = kWaves - kPWaves;   // weights at once
 constexpr int kPThreads = 64 * kPWaves;
-constexpr int kUnitsS1 = 10;           // stage 1: units per stream wave
-constexpr int kUnitsP1 = 5;            //          units per prologue wave
-constexpr int kUnitsS2 = 4;            // stage 2: units per stream wave
-constexpr int kUnitsP2 = 3;            //          units per prologue wave
+constexpr int kUnitsS1 = 7;            // stage 1: units per stream wave
+constexpr int kUnitsP1 = 8;            //          units per prologue wave
+constexpr int kUnitsS2 = 3;            // stage 2: units per stream wave
+constexpr int kUnitsP2 = 4;            //          units per prologue wave
 constexpr int kMaxTiles = 3;           // tiles per stage-1 workgroup
 constexpr int kTabGroups = 56;         // table capacity: 56 groups = 7,168 inputs (112 KiB)
 constexpr int kMaxBlocks = 16;         // scale blocks staged in LDS (two per prologue wave)
 constexpr int kMaxSlots = 3;           // pieces per down tile
 constexpr int kGroupTabBytes = 32 * 64;// 32 tables of 16 int32 entries per 128-input group
 constexpr int kSuperBytes = kBlock * (1 + kSuper);   // Q1 super-group: scales + 8 sign blocks
-constexpr int kPRounds = 3;            // stage-1 input: 4-input chunks pt + 512 r
-constexpr int kPRounds2 = 2;           // stage-2 input: pair sums and 8-input chunks pt + 512 r
+constexpr int kPRounds = (1280 + kPThreads - 1) / kPThreads;   // stage-1 input: 4-input chunks
+                                                              // pt + kPThreads r
+constexpr int kPRounds2 = (1024 + kPThreads - 1) / kPThreads;  // stage-2 input: pair sums and
+                                                              // 8-input chunks pt + kPThreads r
 constexpr size_t kPartFloats = (size_t)kMaxSlots * kTabGroups * kGroup;   // 28,672 floats
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -72,7 +80,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) const int lds_cint;
 typedef __attribute__((address_space(3))) const uint16_t lds_cu16;
-typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ float bf(uint32_t b16) { return __uint_as_float(b16 << 16); }
 // float -> bf16 bits, round to nearest even (the gfx950 conversion; fp32 denormals are kept)
@@ -203,25 +210,38 @@ struct StLds {
   float red[kMaxTiles][kWaves][64];           // per-wave partial sums of each tile
   float fac[kTabGroups];                      // 2^(E_g - 22)
   float ssum[kPWaves];                        // per-wave sums of squares of the prologue waves
-  unsigned arrived_sum, arrived_tab;          // prologue waves done with their sums / tables
+  unsigned arrived_sum, arrived_tab, arrived_scl;   // prologue waves done with their sums /
+                                                    // tables / scale-block copies
 };
 
-// Counters in LDS through which the prologue waves hand their results to the other waves of
-// the workgroup (all of them resident, so every wait ends): one lane per wave arrives once its
-// earlier LDS writes (and, where stated, its copies into LDS) are complete; waiters spin.
+// Counters in LDS through which the prologue waves hand their LDS results to the other waves
+// of the workgroup (all of them resident, so every wait ends). A wave arrives once its earlier
+// LDS writes are complete (the LDS serves a compute unit's requests in order, so a later read
+// by any wave sees them); waiters spin. Only LDS is ordered: a release fence would also wait
+// for every outstanding global load of the wave, which here are the weights in flight.
 __device__ __forceinline__ void arrive(unsigned* c) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   if ((threadIdx.x & 63) == 0)
-    __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 __device__ __forceinline__ void wait_count(unsigned* c, unsigned n) {
-  while (__hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < n)
+  while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < n)
     __builtin_amdgcn_s_sleep(1);
+  asm volatile("" ::: "memory");   // later LDS reads stay after the wait
 }
+// Roles of the 16 waves: waves 0 .. kPWaves - 1 are the prologue waves, the others the stream
+// waves; rw numbers the waves of each role from 0.
+__device__ __forceinline__ bool is_prologue(int wave) { return wave < kPWaves; }
+__device__ __forceinline__ int role_index(int wave) {
+  return wave < kPWaves ? wave : wave - kPWaves;
+}
+
 // Sum over the prologue waves of one value per thread, in a fixed order (the same bits in every
-// workgroup): wave sums in LDS, then the waves in order once all have arrived.
-__device__ __forceinline__ float prologue_sum(float v, StLds& L) {
+// workgroup): wave sums in LDS, then the waves in order once all have arrived. rw: the wave's
+// prologue index.
+__device__ __forceinline__ float prologue_sum(float v, StLds& L, int rw) {
   const float w = wave_sum(v);
-  if ((threadIdx.x & 63) == 0) L.ssum[threadIdx.x >> 6] = w;
+  if ((threadIdx.x & 63) == 0) L.ssum[rw] = w;
   arrive(&L.arrived_sum);
   wait_count(&L.arrived_sum, kPWaves);
   float t = 0.f;
@@ -320,40 +340,41 @@ __device__ __forceinline__ LaneTile lane_tile_x(const S1Args& A, int t, int lane
   return r;
 }
 
-// Copies 1 KiB to LDS at dst, 16 bytes per lane from this lane's own source address.
-__device__ __forceinline__ void copy_block(const uint8_t* src_lane, uint8_t* dst) {
-  __builtin_amdgcn_global_load_lds((const void*)src_lane, (lds_void*)dst, 16, 0, 0);
+// A 1 KiB scale block is staged in LDS through registers: 16 bytes per lane are loaded early
+// and stored to LDS once the tables are written. (A direct global-to-LDS copy would make the
+// compiler wait for every outstanding load of the wave before each later LDS access.)
+__device__ __forceinline__ u32x4 load_block(const uint8_t* src_lane) {
+  return *(const u32x4*)src_lane;
+}
+__device__ __forceinline__ void store_block(uint8_t* dst, u32x4 v) {
+  *(u32x4*)(dst + (threadIdx.x & 63) * 16) = v;
 }
 // A workgroup barrier that orders the issue of memory requests only: __syncthreads() also
 // carries a release fence, which waits for every outstanding load of the wave first.
 __device__ __forceinline__ void issue_barrier() { __builtin_amdgcn_s_barrier(); }
-// Waits until at most N of this wave's vector memory operations are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N <= 63, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 // The units of a wave: slot j is unit u0 + 8 j while below u1. A slot past the wave's last unit
 // loads `spare` (a cached scale block) instead, so that every load is unconditional.
 template <int MU>
 struct WaveUnits {
   u32x4 rec[MU];
-  int u0, u1;
+  int u0, u1, stride;
 };
 
 // Unit u of a workgroup with tiles of G groups (stage 1): the record of group g of tile ti.
 struct UnitAddr1 {
   const uint8_t *w0, *w1, *w2;
   int G;
+  // tile ti's base, selected as integer arithmetic on the uniform tile index (a select between
+  // struct fields or array elements is otherwise lowered through scratch memory, and the
+  // pointer read back from there is a generic one, whose loads also hold up LDS waits)
+  __device__ __forceinline__ const uint8_t* tile(int ti) const {
+    const uintptr_t a0 = (uintptr_t)w0, a1 = (uintptr_t)w1, a2 = (uintptr_t)w2;
+    return (const uint8_t*)(ti == 0 ? a0 : (ti == 1 ? a1 : a2));
+  }
   __device__ __forceinline__ const uint8_t* operator()(int u) const {
     const int ti = (u >= G) + (u >= 2 * G);
     const int g = u - ti * G;
-    // pointer select as integer arithmetic on the uniform tile index (a select between struct
-    // fields is otherwise lowered through scratch memory)
-    const uintptr_t a0 = (uintptr_t)w0, a1 = (uintptr_t)w1, a2 = (uintptr_t)w2;
-    const uintptr_t w = ti == 0 ? a0 : (ti == 1 ? a1 : a2);
-    return (const uint8_t*)w + (size_t)(g >> 3) * kSuperBytes + kBlock * (1 + (g & 7));
+    return tile(ti) + (size_t)(g >> 3) * kSuperBytes + kBlock * (1 + (g & 7));
   }
 };
 // Unit u of a down piece (stage 2): group ga + u of the tile.
@@ -366,29 +387,31 @@ struct UnitAddr2 {
   }
 };
 
+// Requests slot j of the wave's units (j a constant once the callers' loops are unrolled).
 template <int MU, typename Addr>
+__device__ __forceinline__ void issue_unit(WaveUnits<MU>& W, const Addr& addr,
+                                           const uint8_t* spare, int j) {
+  const int u = W.u0 + W.stride * j;
+  W.rec[j] = __builtin_nontemporal_load((const u32x4*)(u < W.u1 ? addr(u) : spare));
+}
+// Requests slots 0 .. N - 1.
+template <int N, int MU, typename Addr>
 __device__ __forceinline__ void issue_units(WaveUnits<MU>& W, const Addr addr,
                                             const uint8_t* spare) {
 #pragma unroll
-  for (int j = 0; j < MU; ++j) {
-    const int u = W.u0 + kPWaves * j;
-    W.rec[j] = __builtin_nontemporal_load((const u32x4*)(u < W.u1 ? addr(u) : spare));
-  }
+  for (int j = 0; j < N; ++j) issue_unit(W, addr, spare, j);
 }
 
-// One unit: the row's group sum from the tables at `tab`, times the group's fixed-point factor
-// (LDS `fac`) and fp16 scale (LDS `sc`). Not inlined: one copy serves every unit of every
-// kernel variant, which keeps the kernels' code small.
-__device__ __attribute__((noinline)) float unit_value(u32x4 rec, uint32_t tab, uint32_t fac,
-                                                      uint32_t sc) {
-  const int isum = group_sum(rec, tab);
-  const float f = *(__attribute__((address_space(3))) const float*)(uintptr_t)fac;
-  return (float)isum * f * f16(*(lds_cu16*)(uintptr_t)sc);
+// One unit's group sum from the tables at `tab`.
+__device__ __forceinline__ int unit_isum(u32x4 rec, uint32_t tab) {
+  return group_sum(rec, tab);
 }
 
-// The lookups of a wave's units. Stage 1: tile ti = u / G, group u mod G, table group = group,
-// scale block ti * S + group / 8. Stage 2 (G = units of the piece, S unused): table group u,
-// scale block (ga + u) / 8 - j0.
+// The lookups of a wave's units: each unit's group sum times the group's fixed-point factor
+// (LDS `fac`) and the row's fp16 scale (the staged scale blocks, awaited once the first group
+// sum is formed). Stage 1: tile ti = u / G, group u mod G, table group = group, scale block
+// ti * S + group / 8. Stage 2 (G = units of the piece, S unused): table group u, scale block
+// (ga + u) / 8 - j0.
 template <int MU, bool STAGE1>
 __device__ __forceinline__ void lookup_units(const WaveUnits<MU>& W, int G, int S, int ga, int j0,
                                              const StLds& L, float (&acc)[kMaxTiles]) {
@@ -399,7 +422,7 @@ __device__ __forceinline__ void lookup_units(const WaveUnits<MU>& W, int G, int 
   const uint32_t fac0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const float*)L.fac;
 #pragma unroll
   for (int j = 0; j < MU; ++j) {
-    const int u = W.u0 + kPWaves * j;
+    const int u = W.u0 + W.stride * j;
     if (u >= W.u1) break;
     int ti = 0, gt = u, blk;
     if (STAGE1) {
@@ -411,8 +434,10 @@ __device__ __forceinline__ void lookup_units(const WaveUnits<MU>& W, int G, int 
     }
     const int gs = STAGE1 ? gt : ga + u;   // group within the row (for the scale)
     const uint32_t sb = sbl0 + (uint32_t)blk * kBlock + lane * 16 + (gs & 7) * 2;
-    const float v = unit_value(W.rec[j], tab0 + (uint32_t)gt * kGroupTabBytes,
-                               fac0 + (uint32_t)gt * 4, sb);
+    const int isum = unit_isum(W.rec[j], tab0 + (uint32_t)gt * kGroupTabBytes);
+    if (j == 0) wait_count(const_cast<unsigned*>(&L.arrived_scl), kPWaves);
+    const float f = *(__attribute__((address_space(3))) const float*)(uintptr_t)(fac0 + gt * 4);
+    const float v = (float)isum * f * f16(*(lds_cu16*)(uintptr_t)sb);
     if (ti == 0) acc[0] += v;
     else if (ti == 1) acc[1] += v;
     else acc[2] += v;
@@ -432,13 +457,14 @@ __device__ void stage1_run(const S1Args& A, StLds& L, int T, const LaneTile (&lt
                            uint16_t* rec_raw) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool prologue = wave < kPWaves;
+  const bool prologue = is_prologue(wave);
+  const int rw = role_index(wave);
   const int n_in = A.hidden;
   const int nch = n_in / 4;
   const int G = n_in / kGroup;
   const int S = (G + kSuper - 1) / kSuper;
   const int nunits = T * G;
-  const int us = nunits < kPWaves * kUnitsS1 ? nunits : kPWaves * kUnitsS1;   // stream units
+  const int us = nunits < kSWaves * kUnitsS1 ? nunits : kSWaves * kUnitsS1;   // stream units
   const UnitAddr1 addr{lt[0].w, lt[1].w, lt[2].w, G};
   float acc[kMaxTiles] = {0.f, 0.f, 0.f};
   if (!prologue) {
@@ -446,15 +472,16 @@ __device__ void stage1_run(const S1Args& A, StLds& L, int T, const LaneTile (&lt
     issue_barrier();   // the prologue waves' requests are queued first
     if (UNITS) {
       WaveUnits<kUnitsS1> W;
-      W.u0 = wave - kPWaves;
+      W.u0 = rw;
+      W.stride = kSWaves;
       W.u1 = us;
-      issue_units(W, addr, lt[0].w);
+      issue_units<kUnitsS1>(W, addr, lt[0].w);
       wait_count(&L.arrived_tab, kPWaves);
       lookup_units<kUnitsS1, true>(W, G, S, 0, 0, L, acc);
     }
   } else {
     // ---- prologue waves: the input vector and the scale blocks -----------------------------
-    const int pt = tid;   // 0 .. 511
+    const int pt = rw * 64 + lane;   // 0 .. 511
     uint2 xb[kPRounds];
     f32x4 pv[kPRounds][kMaxSlots];
 #pragma unroll
@@ -471,14 +498,17 @@ __device__ void stage1_run(const S1Args& A, StLds& L, int T, const LaneTile (&lt
         xb[r] = *(const uint2*)((KIND == 0 ? A.x0 : A.q_prev) + 4 * c);
       }
     }
+    constexpr int kB = (kMaxBlocks + kPWaves - 1) / kPWaves;   // scale blocks per prologue wave
+    u32x4 sreg[kB];
+    int sblk[kB];
     if (UNITS) {
 #pragma unroll
-      for (int k = 0; k < kMaxBlocks / kPWaves; ++k) {
-        int b = wave + kPWaves * k;
-        b = b < T * S ? b : T * S - 1;
+      for (int k = 0; k < kB; ++k) {
+        int b = rw + kPWaves * k;
+        b = b < T * S ? b : T * S - 1;   // a repeated block is stored twice with the same bytes
         const int ti = (b >= S) + (b >= 2 * S);
-        const uint8_t* w = ti == 0 ? lt[0].w : (ti == 1 ? lt[1].w : lt[2].w);
-        copy_block(w + (size_t)(b - ti * S) * kSuperBytes, L.sblk[b]);
+        sreg[k] = load_block(addr.tile(ti) + (size_t)(b - ti * S) * kSuperBytes);
+        sblk[k] = b;
       }
     }
     issue_barrier();
@@ -511,7 +541,7 @@ __device__ void stage1_run(const S1Args& A, StLds& L, int T, const LaneTile (&lt
     }
     float denom = 1.f, rden = 1.f;
     if (KIND != 0) {
-      const float tot = prologue_sum(ss, L);
+      const float tot = prologue_sum(ss, L, rw);
       denom = sqrtf(tot / (float)n_in + A.eps);
       rden = 1.f / denom;
     }
@@ -542,13 +572,18 @@ __device__ void stage1_run(const S1Args& A, StLds& L, int T, const LaneTile (&lt
         if ((c & 31) == 0) L.fac[c >> 5] = __builtin_ldexpf(1.f, E - 22);
       }
     }
-    wait_vm<0>();   // this wave's scale blocks are in LDS
     arrive(&L.arrived_tab);
     if (UNITS) {
+#pragma unroll
+      for (int k = 0; k < kB; ++k) store_block(L.sblk[sblk[k]], sreg[k]);
+    }
+    arrive(&L.arrived_scl);
+    if (UNITS) {
       WaveUnits<kUnitsP1> W;
-      W.u0 = us + wave;
+      W.u0 = us + rw;
+      W.stride = kPWaves;
       W.u1 = nunits;
-      issue_units(W, addr, lt[0].w);
+      issue_units<kUnitsP1>(W, addr, lt[0].w);
       wait_count(&L.arrived_tab, kPWaves);
       lookup_units<kUnitsP1, true>(W, G, S, 0, 0, L, acc);
     }
@@ -565,12 +600,14 @@ __device__ void stage1_run(const S1Args& A, StLds& L, int T, const LaneTile (&lt
     for (int w = 0; w < kWaves; ++w) y += L.red[wave][w][lane];
     const int i = wave;
     const uint32_t yb = to_bf16(y);
-    uint16_t* yp = i == 0 ? lt[0].y : (i == 1 ? lt[1].y : lt[2].y);
-    const int row = i == 0 ? lt[0].row : (i == 1 ? lt[1].row : lt[2].row);
-    const int n = i == 0 ? lt[0].n : (i == 1 ? lt[1].n : lt[2].n);
+    // integer selects on the uniform tile index, as in UnitAddr1::tile
+    const uintptr_t y0 = (uintptr_t)lt[0].y, y1 = (uintptr_t)lt[1].y, y2 = (uintptr_t)lt[2].y;
+    uint16_t* yp = (uint16_t*)(i == 0 ? y0 : (i == 1 ? y1 : y2));
+    const int row = lt[0].row * (i == 0) + lt[1].row * (i == 1) + lt[2].row * (i == 2);
+    const int n = lt[0].n * (i == 0) + lt[1].n * (i == 1) + lt[2].n * (i == 2);
     if (row < n) yp[row] = (uint16_t)yb;
-    const bool pr = i == 0 ? pair[0] : (i == 1 ? pair[1] : pair[2]);
-    if (pr) {   // uniform: gate (lanes 0-31) times up (lanes 32-63) of the same rows
+    const int pmask = (pair[0] ? 1 : 0) | (pair[1] ? 2 : 0) | (pair[2] ? 4 : 0);
+    if ((pmask >> i) & 1) {   // uniform: gate (lanes 0-31) times up (lanes 32-63) of the same rows
       const float other = bf((uint32_t)__shfl_xor((int)yb, 32, 64));
       const float hv = bf(yb) * other;
       const float sq = wave_sum(lane < 32 ? hv * hv : 0.f);
@@ -585,6 +622,8 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(S1Args A) {
   if (threadIdx.x == 0) {
     L.arrived_sum = 0;
     L.arrived_tab = 0;
+    L.arrived_scl = 0;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // zeros land before any arrival
   }
   const bool is_x = b < A.x_wgs;
   const int i = is_x ? b : b - A.x_wgs;
@@ -614,32 +653,36 @@ __global__ __launch_bounds__(kThreads) void stage2_kernel(S2Args A) {
   __shared__ StLds L;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rw = role_index(wave);
   if (tid == 0) {
     L.arrived_sum = 0;
     L.arrived_tab = 0;
+    L.arrived_scl = 0;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // zeros land before any arrival
   }
   const int t = blockIdx.x / A.pieces, p = blockIdx.x - t * A.pieces;
   const int ga = A.pg[p], gb = A.pg[p + 1];
   const int nunits = gb - ga;
-  const int us = nunits < kPWaves * kUnitsS2 ? nunits : kPWaves * kUnitsS2;   // stream units
+  const int us = nunits < kSWaves * kUnitsS2 ? nunits : kSWaves * kUnitsS2;   // stream units
   const uint8_t* tw = A.down.w + (size_t)t * A.down.tile_bytes + lane * 16;
   const int j0 = ga >> 3;
   const UnitAddr2 addr{tw, ga};
   const uint8_t* spare = tw + (size_t)j0 * kSuperBytes;
   float acc[kMaxTiles] = {0.f, 0.f, 0.f};
-  if (wave >= kPWaves) {
+  if (!is_prologue(wave)) {
     // ---- stream waves ----------------------------------------------------------------------
     issue_barrier();   // the prologue waves' requests are queued first
     WaveUnits<kUnitsS2> W;
-    W.u0 = wave - kPWaves;
+    W.u0 = rw;
+    W.stride = kSWaves;
     W.u1 = us;
-    issue_units(W, addr, spare);
+    issue_units<kUnitsS2>(W, addr, spare);
     wait_count(&L.arrived_tab, kPWaves);
     lookup_units<kUnitsS2, false>(W, nunits, 0, ga, j0, L, acc);
   } else {
     // ---- prologue waves: the pair tiles' sums of squares, this piece's gate and up, and the
     //      scale blocks ------------------------------------------------------------------------
-    const int pt = tid;   // 0 .. 511
+    const int pt = rw * 64 + lane;   // 0 .. 511
     const int npair = A.ffn / 32;
     const int c8a = ga * (kGroup / 8), n8 = nunits * (kGroup / 8);
     float st[kPRounds2];
@@ -652,17 +695,15 @@ __global__ __launch_bounds__(kThreads) void stage2_kernel(S2Args A) {
       go[r] = *(const u32x4*)(A.gate + 8 * c);
       uo[r] = *(const u32x4*)(A.up + 8 * c);
     }
-    {
-      const int nblk = ((gb - 1) >> 3) - j0 + 1;
-      const int b = wave < nblk ? wave : nblk - 1;
-      copy_block(tw + (size_t)(j0 + b) * kSuperBytes, L.sblk[b]);
-    }
+    const int nblk = ((gb - 1) >> 3) - j0 + 1;
+    const int sb = rw < nblk ? rw : nblk - 1;   // a repeated block: same bytes twice
+    const u32x4 sreg = load_block(tw + (size_t)(j0 + sb) * kSuperBytes);
     issue_barrier();
     // ---- the rescale of h = gate * up (the pair tiles' sums in a fixed order) --------------
     float ss = 0.f;
 #pragma unroll
     for (int r = 0; r < kPRounds2; ++r) ss += pt + kPThreads * r < npair ? st[r] : 0.f;
-    const float tot = prologue_sum(ss, L);
+    const float tot = prologue_sum(ss, L, rw);
     const float denom = sqrtf(tot / (float)A.ffn + A.eps);
     const float rden = 1.f / denom;
     // ---- xd over the piece: record (pieces of tile 0), fixed point, tables -----------------
@@ -697,12 +738,14 @@ __global__ __launch_bounds__(kThreads) void stage2_kernel(S2Args A) {
         if ((i & 15) == 0) L.fac[i >> 4] = __builtin_ldexpf(1.f, E - 22);
       }
     }
-    wait_vm<0>();   // this wave's scale block is in LDS
     arrive(&L.arrived_tab);
+    store_block(L.sblk[sb], sreg);
+    arrive(&L.arrived_scl);
     WaveUnits<kUnitsP2> W;
-    W.u0 = us + wave;
+    W.u0 = us + rw;
+    W.stride = kPWaves;
     W.u1 = nunits;
-    issue_units(W, addr, spare);
+    issue_units<kUnitsP2>(W, addr, spare);
     wait_count(&L.arrived_tab, kPWaves);
     lookup_units<kUnitsP2, false>(W, nunits, 0, ga, j0, L, acc);
   }
@@ -772,7 +815,7 @@ lbq_status lbq::stage_decode_q1(const lbq_q1_layer* layers, int n_layers, int hi
   if (G > kTabGroups || hidden / 4 > kPRounds * kPThreads) return LBQ_E_UNSUPPORTED;
   if ((size_t)ffn / 32 > kStatFloats || ffn / 32 > kPRounds2 * kPThreads) return LBQ_E_UNSUPPORTED;
   // tiles per stage-1 workgroup: within the units of its waves and the scale blocks it stages
-  const int wg_units1 = kPWaves * (kUnitsS1 + kUnitsP1);
+  const int wg_units1 = kSWaves * kUnitsS1 + kPWaves * kUnitsP1;
   int tmax = kMaxTiles;
   if (tmax > wg_units1 / G) tmax = wg_units1 / G;
   if (tmax > kMaxBlocks / S) tmax = kMaxBlocks / S;
@@ -784,7 +827,7 @@ lbq_status lbq::stage_decode_q1(const lbq_q1_layer* layers, int n_layers, int hi
   // down pieces: as many as the compute units allow (at most kMaxSlots), each within the table
   // capacity, the units of one piece per wave and its scale blocks per workgroup
   const int down_tiles = hidden / kTileRows;
-  const int wg_units2 = kPWaves * (kUnitsS2 + kUnitsP2);
+  const int wg_units2 = kSWaves * kUnitsS2 + kPWaves * kUnitsP2;
   const int piece_cap = wg_units2 < kTabGroups ? wg_units2 : kTabGroups;
   int P = cus / down_tiles;
   if (P > kMaxSlots) P = kMaxSlots;
@@ -795,7 +838,9 @@ lbq_status lbq::stage_decode_q1(const lbq_q1_layer* layers, int n_layers, int hi
   int pg[kMaxSlots + 1];
   for (int p = 0; p <= P; ++p) pg[p] = (int)((long long)p * FG / P);
   for (int p = 0; p < P; ++p)
-    if (((pg[p + 1] - 1) >> 3) - (pg[p] >> 3) + 1 > kPWaves) return LBQ_E_UNSUPPORTED;
+    if (((pg[p + 1] - 1) >> 3) - (pg[p] >> 3) + 1 > kPWaves ||
+        (pg[p + 1] - pg[p]) * (kGroup / 8) > kPRounds2 * kPThreads)
+      return LBQ_E_UNSUPPORTED;
   if ((size_t)P * hidden > kPartFloats) return LBQ_E_UNSUPPORTED;
   float* ws = nullptr;
   const lbq_status wst = st_workspace(s, &ws);
