@@ -71,8 +71,9 @@ constexpr int kGroupTabBytes = 32 * 64;// 32 tables of 16 int32 entries per 128-
 constexpr int kSuperBytes = kBlock * (1 + kSuper);   // Q1 super-group: scales + 8 sign blocks
 constexpr int kPRounds = (1280 + kPThreads - 1) / kPThreads;   // stage-1 input: 4-input chunks
                                                               // pt + kPThreads r
-constexpr int kPRounds2 = (1024 + kPThreads - 1) / kPThreads;  // stage-2 input: pair sums and
-                                                              // 8-input chunks pt + kPThreads r
+constexpr int kPRounds2 = (1536 + kPThreads - 1) / kPThreads;  // stage-2 input: 4-input chunks
+                                                              // pt + kPThreads r (48 groups)
+constexpr int kStRounds = (1024 + kPThreads - 1) / kPThreads;  // the pair sums, pt + kPThreads r
 constexpr size_t kPartFloats = (size_t)kMaxSlots * kTabGroups * kGroup;   // 28,672 floats
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -118,23 +119,28 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 // Maximum over each row of 16 lanes, in every lane of the row.
-__device__ __forceinline__ float row_max(float m) {
-  m = fmaxf(m, dpp<kDppXor1>(m, m));
-  m = fmaxf(m, dpp<kDppXor2>(m, m));
-  m = fmaxf(m, dpp<kDppHalfMirror>(m, m));
-  return fmaxf(m, dpp<kDppMirror>(m, m));
+// Magnitudes are compared as the bits of non-negative floats (which order like unsigned
+// integers), so the DPP steps are integer maxima.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dppu(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROWS, 0xF, false);
 }
-// Maximum over each half wave (32 lanes), in every lane of the half.
-__device__ __forceinline__ float half_max(float m) {
-  m = row_max(m);
-  m = fmaxf(m, dpp<kDppBcast15, 0xA>(m, m));   // lanes 16..31 and 48..63 hold their half's max
-  const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 31));
-  const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 63));
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+// Maximum over each half wave (32 lanes) of the magnitude bits m, in every lane of the half.
+__device__ __forceinline__ uint32_t half_max_bits(uint32_t m) {
+  m = umax(m, dppu<kDppXor1>(m, m));
+  m = umax(m, dppu<kDppXor2>(m, m));
+  m = umax(m, dppu<kDppHalfMirror>(m, m));
+  m = umax(m, dppu<kDppMirror>(m, m));
+  m = umax(m, dppu<kDppBcast15, 0xA>(m, m));   // lanes 16..31 and 48..63 hold their half's max
+  const uint32_t lo = __builtin_amdgcn_readlane((int)m, 31);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)m, 63);
   return (threadIdx.x & 32) ? hi : lo;
 }
-// Exponent E with 2^E above the magnitude m (E = -126 covers zero and subnormal magnitudes).
-__device__ __forceinline__ int exponent_above(float m) {
-  const uint32_t eb = (__float_as_uint(m) >> 23) & 0xFFu;
+// Exponent E with 2^E above the magnitude with bits m (E = -126 covers zero and subnormal
+// magnitudes).
+__device__ __forceinline__ int exponent_above(uint32_t m) {
+  const uint32_t eb = (m >> 23) & 0xFFu;
   return (int)(eb > 1u ? eb : 1u) - 126;
 }
 
@@ -346,8 +352,12 @@ __device__ __forceinline__ LaneTile lane_tile_x(const S1Args& A, int t, int lane
 __device__ __forceinline__ u32x4 load_block(const uint8_t* src_lane) {
   return *(const u32x4*)src_lane;
 }
+// The block is stored transposed, [group][row], so that the scale reads of a unit (one group,
+// the 64 rows of the lanes) fall on consecutive banks.
 __device__ __forceinline__ void store_block(uint8_t* dst, u32x4 v) {
-  *(u32x4*)(dst + (threadIdx.x & 63) * 16) = v;
+  uint16_t* d = (uint16_t*)dst + (threadIdx.x & 63);
+#pragma unroll
+  for (int g = 0; g < kSuper; ++g) d[g * kTileRows] = (uint16_t)(v[g >> 1] >> (16 * (g & 1)));
 }
 // A workgroup barrier that orders the issue of memory requests only: __syncthreads() also
 // carries a release fence, which waits for every outstanding load of the wave first.
@@ -433,7 +443,7 @@ __device__ __forceinline__ void lookup_units(const WaveUnits<MU>& W, int G, int 
       blk = ((ga + u) >> 3) - j0;
     }
     const int gs = STAGE1 ? gt : ga + u;   // group within the row (for the scale)
-    const uint32_t sb = sbl0 + (uint32_t)blk * kBlock + lane * 16 + (gs & 7) * 2;
+    const uint32_t sb = sbl0 + (uint32_t)blk * kBlock + (gs & 7) * (2 * kTileRows) + lane * 2;
     const int isum = unit_isum(W.rec[j], tab0 + (uint32_t)gt * kGroupTabBytes);
     if (j == 0) wait_count(const_cast<unsigned*>(&L.arrived_scl), kPWaves);
     const float f = *(__attribute__((address_space(3))) const float*)(uintptr_t)(fac0 + gt * 4);
@@ -554,15 +564,15 @@ __device__ void stage1_run(const S1Args& A, StLds& L, int T, const LaneTile (&lt
       const bool ok = c < nch;
       float v[4];
       uint32_t ob[4];
-      float m = 0.f;
+      uint32_t m = 0u;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         ob[i] = KIND == 0 ? raw[r][i] : to_bf16(div_corr(h[r][i], denom, rden));
         v[i] = bf(ob[i]);
-        m = fmaxf(m, fabsf(v[i]));
+        m = umax(m, (ob[i] & 0x7FFFu) << 16);
       }
       // a group is 32 chunks: 32 consecutive threads, half a wave
-      const int E = exponent_above(half_max(ok ? m : 0.f));
+      const int E = exponent_above(half_max_bits(ok ? m : 0u));
       if (ok) {
         if (rec_x) *(uint2*)(rec_x + 4 * c) = make_uint2(ob[0] | ob[1] << 16, ob[2] | ob[3] << 16);
         if (rec_raw)
@@ -684,16 +694,20 @@ __global__ __launch_bounds__(kThreads) void stage2_kernel(S2Args A) {
     //      scale blocks ------------------------------------------------------------------------
     const int pt = rw * 64 + lane;   // 0 .. 511
     const int npair = A.ffn / 32;
-    const int c8a = ga * (kGroup / 8), n8 = nunits * (kGroup / 8);
-    float st[kPRounds2];
-    u32x4 go[kPRounds2], uo[kPRounds2];
+    const int c4a = ga * (kGroup / 4), n4 = nunits * (kGroup / 4);
+    float st[kStRounds];
+#pragma unroll
+    for (int r = 0; r < kStRounds; ++r) {
+      const int i = pt + kPThreads * r;
+      st[r] = A.stat[i < npair ? i : npair - 1];
+    }
+    uint2 go[kPRounds2], uo[kPRounds2];
 #pragma unroll
     for (int r = 0; r < kPRounds2; ++r) {
       const int i = pt + kPThreads * r;
-      st[r] = A.stat[i < npair ? i : npair - 1];
-      const int c = c8a + (i < n8 ? i : n8 - 1);
-      go[r] = *(const u32x4*)(A.gate + 8 * c);
-      uo[r] = *(const u32x4*)(A.up + 8 * c);
+      const int c = c4a + (i < n4 ? i : n4 - 1);
+      go[r] = *(const uint2*)(A.gate + 4 * c);
+      uo[r] = *(const uint2*)(A.up + 4 * c);
     }
     const int nblk = ((gb - 1) >> 3) - j0 + 1;
     const int sb = rw < nblk ? rw : nblk - 1;   // a repeated block: same bytes twice
@@ -702,7 +716,7 @@ __global__ __launch_bounds__(kThreads) void stage2_kernel(S2Args A) {
     // ---- the rescale of h = gate * up (the pair tiles' sums in a fixed order) --------------
     float ss = 0.f;
 #pragma unroll
-    for (int r = 0; r < kPRounds2; ++r) ss += pt + kPThreads * r < npair ? st[r] : 0.f;
+    for (int r = 0; r < kStRounds; ++r) ss += pt + kPThreads * r < npair ? st[r] : 0.f;
     const float tot = prologue_sum(ss, L, rw);
     const float denom = sqrtf(tot / (float)A.ffn + A.eps);
     const float rden = 1.f / denom;
@@ -711,31 +725,28 @@ __global__ __launch_bounds__(kThreads) void stage2_kernel(S2Args A) {
 #pragma unroll
     for (int r = 0; r < kPRounds2; ++r) {
       const int i = pt + kPThreads * r;
-      if (r > 0 && kPThreads * r >= n8) break;   // uniform
-      const bool own = i < n8;
-      float v[8];
-      uint32_t ob[8];
-      float m = 0.f;
+      if (r > 0 && kPThreads * r >= n4) break;   // uniform
+      const bool own = i < n4;
+      float v[4];
+      uint32_t ob[4];
+      uint32_t m = 0u;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const uint32_t gw = go[r][k >> 1], uw = uo[r][k >> 1];
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t gw = k < 2 ? go[r].x : go[r].y, uw = k < 2 ? uo[r].x : uo[r].y;
         const float gf = (k & 1) ? __uint_as_float(gw & 0xFFFF0000u) : bf(gw & 0xFFFFu);
         const float uf = (k & 1) ? __uint_as_float(uw & 0xFFFF0000u) : bf(uw & 0xFFFFu);
         ob[k] = to_bf16(div_corr(gf * uf, denom, rden));   // gate * up is exact in fp32
         v[k] = bf(ob[k]);
-        m = fmaxf(m, fabsf(v[k]));
+        m = umax(m, (ob[k] & 0x7FFFu) << 16);
       }
-      // a group is 16 chunks of 8: one row of 16 lanes
-      const int E = exponent_above(row_max(own ? m : 0.f));
+      // a group is 32 chunks: 32 consecutive threads, half a wave
+      const int E = exponent_above(half_max_bits(own ? m : 0u));
       if (own) {
         if (t == 0)
-          *(u32x4*)(A.xd_out + 8 * (c8a + i)) =
-              u32x4{ob[0] | ob[1] << 16, ob[2] | ob[3] << 16, ob[4] | ob[5] << 16,
-                    ob[6] | ob[7] << 16};
-        const float v0[4] = {v[0], v[1], v[2], v[3]}, v1[4] = {v[4], v[5], v[6], v[7]};
-        put_table(tab, (uint32_t)i * 128, v0, 22 - E, lane);
-        put_table(tab, (uint32_t)i * 128 + 64, v1, 22 - E, lane);
-        if ((i & 15) == 0) L.fac[i >> 4] = __builtin_ldexpf(1.f, E - 22);
+          *(uint2*)(A.xd_out + 4 * (c4a + i)) =
+              make_uint2(ob[0] | ob[1] << 16, ob[2] | ob[3] << 16);
+        put_table(tab, (uint32_t)i * 64, v, 22 - E, lane);
+        if ((i & 31) == 0) L.fac[i >> 5] = __builtin_ldexpf(1.f, E - 22);
       }
     }
     arrive(&L.arrived_tab);
@@ -813,7 +824,7 @@ lbq_status lbq::stage_decode_q1(const lbq_q1_layer* layers, int n_layers, int hi
   const int G = hidden / kGroup, FG = ffn / kGroup;
   const int S = ceil_div(G, kSuper);
   if (G > kTabGroups || hidden / 4 > kPRounds * kPThreads) return LBQ_E_UNSUPPORTED;
-  if ((size_t)ffn / 32 > kStatFloats || ffn / 32 > kPRounds2 * kPThreads) return LBQ_E_UNSUPPORTED;
+  if ((size_t)ffn / 32 > kStatFloats || ffn / 32 > kStRounds * kPThreads) return LBQ_E_UNSUPPORTED;
   // tiles per stage-1 workgroup: within the units of its waves and the scale blocks it stages
   const int wg_units1 = kSWaves * kUnitsS1 + kPWaves * kUnitsP1;
   int tmax = kMaxTiles;
@@ -828,7 +839,8 @@ lbq_status lbq::stage_decode_q1(const lbq_q1_layer* layers, int n_layers, int hi
   // capacity, the units of one piece per wave and its scale blocks per workgroup
   const int down_tiles = hidden / kTileRows;
   const int wg_units2 = kSWaves * kUnitsS2 + kPWaves * kUnitsP2;
-  const int piece_cap = wg_units2 < kTabGroups ? wg_units2 : kTabGroups;
+  int piece_cap = wg_units2 < kTabGroups ? wg_units2 : kTabGroups;
+  if (piece_cap > kPRounds2 * kPThreads / (kGroup / 4)) piece_cap = kPRounds2 * kPThreads / (kGroup / 4);
   int P = cus / down_tiles;
   if (P > kMaxSlots) P = kMaxSlots;
   if (P < ceil_div(FG, piece_cap)) P = ceil_div(FG, piece_cap);
@@ -839,7 +851,7 @@ lbq_status lbq::stage_decode_q1(const lbq_q1_layer* layers, int n_layers, int hi
   for (int p = 0; p <= P; ++p) pg[p] = (int)((long long)p * FG / P);
   for (int p = 0; p < P; ++p)
     if (((pg[p + 1] - 1) >> 3) - (pg[p] >> 3) + 1 > kPWaves ||
-        (pg[p + 1] - pg[p]) * (kGroup / 8) > kPRounds2 * kPThreads)
+        (pg[p + 1] - pg[p]) * (kGroup / 4) > kPRounds2 * kPThreads)
       return LBQ_E_UNSUPPORTED;
   if ((size_t)P * hidden > kPartFloats) return LBQ_E_UNSUPPORTED;
   float* ws = nullptr;
