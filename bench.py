@@ -222,7 +222,6 @@ def main() -> int:
         evs[i][1].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
-    lbq.lbq_device_check()
     ms = start.elapsed_time(end) / args.steps
     gbs = bytes_per_step / (ms * 1e-3) / 1e9
     step_kernel_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps

@@ -28,7 +28,15 @@
  *     LBQ_OK without looking at the data pointers (an empty tensor may have a NULL pointer).
  *   - Matrices are [n][k]: n output rows, k inputs (the reduction dimension).
  *   - Every device entry point may be called concurrently from several host threads on
- *     different streams, except where noted (split-K workspace, see lbq_gemv_q1g128).
+ *     different streams. Device memory the library owns (the split-K workspace of the GEMV
+ *     entry points, the stage workspace of the decode step) is kept per (device, stream):
+ *     work on one stream never touches another stream's workspace. A workspace is allocated
+ *     on a stream's first call that needs it (LBQ_E_NOMEM if that call is being captured into
+ *     a HIP graph: make one eager call on the stream first), may be replaced by a larger one
+ *     later, and is never freed while the process runs, so graphs captured earlier stay valid.
+ *     A captured graph uses the workspace of the stream it was captured on: do not replay it
+ *     concurrently with other work that uses that stream's workspace. No entry point
+ *     synchronises the device or a stream.
  */
 #ifndef LBQ_H
 #define LBQ_H
@@ -40,7 +48,7 @@
 extern "C" {
 #endif
 
-#define LBQ_ABI_VERSION 1
+#define LBQ_ABI_VERSION 2
 #define LBQ_MAX_BATCH 16
 #define LBQ_MAX_GEMM_ROWS 65536
 #define LBQ_MLP_MAX_LAYERS 8
@@ -175,10 +183,9 @@ lbq_status lbq_unpack_q1g128(const void* src, int32_t n, int32_t k, uint8_t* sig
  * Requires k % 128 == 0, 1 <= n, 0 <= batch <= LBQ_MAX_BATCH (0 = no-op). d_y must not
  * overlap d_x or the weights. With batch >= 2 and d_x 16-byte aligned the call is the
  * matrix-core product lbq_gemm_q1g128 (same result rule; within each group the matrix cores sum
- * the exact products in their own order). Large-k calls may split the reduction over
- * workgroups through a library-owned device workspace (allocated once per device on first need, kept until the
- * process exits); calls that split share it, so concurrent split calls on one device must be
- * ordered on one stream. LBQ_E_NOMEM if it cannot be allocated (e.g. inside graph capture). */
+ * the exact products in their own order). Large-k calls split the reduction over workgroups
+ * through the stream's split-K workspace (see the conventions above). LBQ_E_NOMEM if it cannot
+ * be allocated (e.g. on a stream's first such call inside graph capture). */
 lbq_status lbq_gemv_q1g128(const void* d_w, int32_t n, int32_t k, const uint16_t* d_x,
                            uint16_t* d_y, int32_t batch, void* stream);
 
@@ -339,22 +346,17 @@ size_t lbq_decode_act_elems(int32_t n_layers, int32_t hidden, int32_t kv, int32_
 int64_t lbq_decode_act_offset(int32_t layer, int32_t slot, int32_t n_layers, int32_t hidden,
                               int32_t kv, int32_t ffn, int32_t batch);
 
+/* Runs the step on `stream`. Batch 1 with hidden and ffn within the stage kernels' limits
+ * (hidden <= 7168, ffn <= 32768, d_act 16-byte aligned, d_x0 8-byte aligned) takes two
+ * launches per layer and one final launch; their workgroups never wait for each other, and the
+ * down projection's partial sums go through the stream's stage workspace (3 x hidden floats,
+ * plus ffn / 32 floats of gate * up sums of squares). Other cases run every GEMV and rescale of
+ * the step as separate calls of the entry points above. Every layer pointer is validated
+ * (non-NULL, 16-byte aligned, no overlap with d_act) before anything is launched. */
 lbq_status lbq_decode_step_q1g128(const lbq_q1_layer* layers, int32_t n_layers, int32_t hidden,
                                   int32_t kv, int32_t ffn, const uint16_t* d_x0,
                                   uint16_t* d_act, int32_t batch, float eps, void* stream);
 
-/* Batch-1 decode steps run as two launches per layer that need no communication between
- * workgroups (an fp32 accumulator of 2 x hidden floats per device is the library's workspace).
- * Batch-1 Q1_0_g128 GEMVs run as one persistent launch (one workgroup per compute unit) whose
- * workgroups exchange partial sums through tagged words in a library-owned device workspace;
- * every wait inside such a launch is bounded. Such a launch is never recorded into a HIP graph:
- * while the stream is being captured, batch-1 Q1 GEMVs use the per-call kernels instead (same
- * results within the float tolerance). Such a launch
- * expects the device to itself: should another kernel hold compute units meanwhile, its waits
- * time out instead of hanging. This call synchronises `stream` and returns LBQ_E_DEVICE if a
- * launch on the current device gave up waiting (its outputs are then invalid), LBQ_OK
- * otherwise. */
-lbq_status lbq_device_check(void* stream);
 
 #ifdef __cplusplus
 }

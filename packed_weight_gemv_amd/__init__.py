@@ -76,7 +76,6 @@ def load():
         "lbq_decode_act_elems": ([i32, i32, i32, i32, i32], sz),
         "lbq_decode_act_offset": ([i32, i32, i32, i32, i32, i32, i32], i64),
         "lbq_decode_step_q1g128": ([P, i32, i32, i32, i32, P, P, i32, ctypes.c_float, P], i32),
-        "lbq_device_check": ([P], i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -315,12 +314,13 @@ def lbq_decode_act_offset(layer, slot, n_layers, hidden, kv, ffn, batch) -> int:
 
 
 def make_layers(layers) -> ctypes.Array:
-    """layers: list of dicts {name: uint8 device tensor} -> lbq_q1_layer array (keep the
-    tensors alive while the array is used)."""
+    """layers: list of dicts {name: uint8 device tensor} -> lbq_q1_layer array. The array holds
+    references to the tensors, so their memory stays allocated while the array is in use."""
     arr = (Q1Layer * len(layers))()
     for i, L in enumerate(layers):
         for name in ("q", "k", "v", "o", "gate", "up", "down"):
             setattr(arr[i], name, _dptr(L[name]))
+    arr._tensors = [dict(L) for L in layers]
     return arr
 
 
@@ -330,11 +330,6 @@ def lbq_decode_step_q1g128(layer_array, n_layers, hidden, kv, ffn, x0, act, eps=
     _check("lbq_decode_step_q1g128", load().lbq_decode_step_q1g128(
         ctypes.cast(layer_array, ctypes.c_void_p), n_layers, hidden, kv, ffn, _dptr(x0),
         _dptr(act), B, float(eps), _stream(stream)))
-
-
-def lbq_device_check(stream=None) -> None:
-    """Synchronises the stream; raises if a persistent launch gave up waiting."""
-    _check("lbq_device_check", load().lbq_device_check(_stream(stream)))
 
 
 def act_view(act, slot: str, layer: int, n_layers, hidden, kv, ffn, batch):

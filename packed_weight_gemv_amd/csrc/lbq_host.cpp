@@ -36,7 +36,7 @@ static inline uint32_t rotl32(uint32_t v, int s) { return (v << s) | (v >> (32 -
 static inline uint32_t rotr32(uint32_t v, int s) { return (v >> s) | (v << (32 - s)); }
 
 // ---------------------------------------------------------------------------------------------
-// 2-bit: the device layout is the canonical one (the MLP kernel stages whole layers on chip).
+// 2-bit: the device layout is the canonical one (four codes per byte, row-major).
 // ---------------------------------------------------------------------------------------------
 extern "C" size_t lbq_2bit_bytes(int32_t n, int32_t k) {
   if (n < 1 || k < 4 || k % 4 != 0) return 0;

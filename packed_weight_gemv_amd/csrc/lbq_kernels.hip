@@ -4,7 +4,10 @@
 #include <hip/hip_runtime.h>
 #include <string.h>
 
+#include <map>
 #include <mutex>
+#include <utility>
+#include <vector>
 
 #include "lbq_internal.h"
 
@@ -60,40 +63,46 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// library-owned split-K workspace (one per device, grown on demand, never freed)
+// library-owned split-K workspace: one per (device, stream), grown on demand, never freed
 // ---------------------------------------------------------------------------------------------
 namespace {
-constexpr int kMaxDevices = 64;
 constexpr size_t kCounterBytes = kSplitCounterBytes;   // 256 Ki tile counters, self-resetting
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
 };
-Workspace g_ws[kMaxDevices];
+// Work queued on one stream uses that stream's workspace only, so calls on different streams
+// never share partial sums or tile counters. A workspace that has to grow is replaced by a
+// larger one and the old one is kept (never freed): kernels already queued, and HIP graphs
+// captured with its address, may still use it. Each replacement at least doubles the size,
+// so the retired buffers of a stream take at most as much memory as its current one.
+std::map<std::pair<int, uintptr_t>, Workspace> g_ws;
+std::vector<void*> g_retired;
 std::mutex g_ws_mutex;
 
-// Returns device memory of at least kCounterBytes + partial_bytes; the first kCounterBytes are
-// zero-initialised tile counters that every kernel leaves at zero.
+// Returns device memory of at least kCounterBytes + partial_bytes for `stream`; the first
+// kCounterBytes are tile counters that start at zero and that every kernel leaves at zero.
 lbq_status get_workspace(size_t partial_bytes, hipStream_t stream, unsigned** counters,
                          float** partials) {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LBQ_E_DEVICE;
+  if (hipGetDevice(&dev) != hipSuccess) return LBQ_E_DEVICE;
   std::lock_guard<std::mutex> lock(g_ws_mutex);
-  Workspace& w = g_ws[dev];
-  size_t need = kCounterBytes + partial_bytes;
+  Workspace& w = g_ws[{dev, (uintptr_t)stream}];
+  const size_t need = kCounterBytes + partial_bytes;
   if (w.bytes < need) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
       return LBQ_E_NOMEM;
     size_t grow = need < ((size_t)64 << 20) ? ((size_t)64 << 20) : need;
+    if (grow < 2 * w.bytes) grow = 2 * w.bytes;
     void* p = nullptr;
     if (hipMalloc(&p, grow) != hipSuccess) return LBQ_E_NOMEM;
-    if (hipMemset(p, 0, kCounterBytes) != hipSuccess) return LBQ_E_DEVICE;
-    if (w.ptr) {
-      // the old buffer may still be in use by queued kernels: wait before releasing it
-      (void)hipDeviceSynchronize();
-      (void)hipFree(w.ptr);
+    // ordered before every later use on this stream (the stream is not being captured)
+    if (hipMemsetAsync(p, 0, kCounterBytes, stream) != hipSuccess) {
+      (void)hipFree(p);
+      return LBQ_E_DEVICE;
     }
+    if (w.ptr) g_retired.push_back(w.ptr);
     w.ptr = p;
     w.bytes = grow;
   }
@@ -859,13 +868,6 @@ extern "C" lbq_status lbq_mlp_2bit_i16(const void* const* d_layer_w, const int32
 
 enum class Fmt { Q1, I4 };
 
-// persistent engine (lbq_engine.hip)
-lbq_status lbq_engine_gemv_q1(const void* d_w, int32_t n, int32_t k, const uint16_t* d_x,
-                              uint16_t* d_y, hipStream_t stream);
-lbq_status lbq_engine_decode_q1(const lbq_q1_layer* layers, int32_t L, int32_t hidden, int32_t kv,
-                                int32_t ffn, const uint16_t* d_x0, uint16_t* d_act, float eps,
-                                hipStream_t stream);
-
 static lbq_status gemv_common(Fmt fmt, const void* d_w, int32_t n, int32_t k,
                               const uint16_t* d_x, uint16_t* d_y, int32_t batch, void* stream) {
   Geometry g;
@@ -883,9 +885,7 @@ static lbq_status gemv_common(Fmt fmt, const void* d_w, int32_t n, int32_t k,
   if (batch >= 2 && (uintptr_t)d_x % 16 == 0)
     return fmt == Fmt::Q1 ? lbq_gemm_q1g128(d_w, n, k, d_x, d_y, batch, stream)
                           : lbq_gemm_i4g128(d_w, n, k, d_x, d_y, batch, stream);
-  // the per-call kernels' split-K workspace, reserved even when the persistent engine takes a
-  // batch-1 Q1 call: a later captured call of the same shape falls back to these kernels and
-  // cannot allocate
+  // the split-K workspace of this stream
   unsigned* counters = nullptr;
   float* partials = nullptr;
   if (g.supers > 1) {
@@ -893,10 +893,6 @@ static lbq_status gemv_common(Fmt fmt, const void* d_w, int32_t n, int32_t k,
     lbq_status st = get_workspace((size_t)batch * g.supers * g.np * sizeof(float), s, &counters,
                                   &partials);
     if (st != LBQ_OK) return st;
-  }
-  if (fmt == Fmt::Q1 && batch == 1) {
-    const lbq_status st = lbq_engine_gemv_q1(d_w, n, k, d_x, d_y, s);
-    if (st != LBQ_E_UNSUPPORTED) return st;
   }
   const dim3 grid((unsigned)g.tiles, (unsigned)g.supers);
   const int nbp = batch <= 1 ? 1 : (batch <= 2 ? 2 : 4);
@@ -1054,9 +1050,8 @@ extern "C" lbq_status lbq_decode_step_q1g128(const lbq_q1_layer* layers, int32_t
   if (overlaps(d_x0, (size_t)batch * hidden * 2, d_act, elems * 2)) return LBQ_E_ALIAS;
   hipStream_t s = (hipStream_t)stream;
   if (batch == 1) {
-    lbq_status st = stage_decode_q1(layers, n_layers, hidden, kv, ffn, d_x0, d_act, eps, s);
-    if (st != LBQ_E_UNSUPPORTED) return st;
-    st = lbq_engine_decode_q1(layers, n_layers, hidden, kv, ffn, d_x0, d_act, eps, s);
+    const lbq_status st =
+        stage_decode_q1(layers, n_layers, hidden, kv, ffn, d_x0, d_act, eps, s);
     if (st != LBQ_E_UNSUPPORTED) return st;
   }
   auto at = [&](int layer, int slot) {

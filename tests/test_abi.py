@@ -26,14 +26,14 @@ def lib():
 
 def test_library_exports_every_declared_function(lib):
     names = _declared_functions()
-    assert len(names) == 29
+    assert len(names) == 28
     for name in names:
         assert hasattr(lib, name), name
         assert name in dir(lbq) or name in ("lbq_status_string",), f"binding lacks {name}"
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lbq.lbq_abi_version() == 1
+    assert lbq.lbq_abi_version() == 2
     for code in lbq.STATUS:
         assert lbq.lbq_status_string(code)
     assert lbq.lbq_status_string(12345) == "unknown status"

@@ -1,8 +1,6 @@
 """Calls captured in a HIP graph and replayed: every replay (with eager work and synchronisation
-between replays) must match the eager result. Batch-1 Q1 GEMVs are captured through the per-call
-kernels (the persistent engine declines capture), so they are held to the oracle's tolerance and
-to bitwise agreement between replays; the other paths run the same kernels eagerly and captured,
-so they must agree bitwise."""
+between replays) must match the eager result. Eager and captured calls run the same kernels, so
+they must agree bitwise; batch-1 Q1 GEMVs are also held to the oracle's tolerance."""
 import numpy as np
 import pytest
 import torch
@@ -42,7 +40,7 @@ def test_batch1_q1_gemvs_in_a_graph(lbq):
             lbq.lbq_gemv_q1g128(w, n, k, x, y)
     junk = empty_bf16(1, 320)
 
-    def eager():   # an eager engine call between replays, writing elsewhere
+    def eager():   # an eager call between replays, writing elsewhere
         lbq.lbq_gemv_q1g128(ws[0], 320, 1024, xs[0], junk)
 
     reps = _replays(g, ys, eager)
