@@ -358,6 +358,21 @@ lbq_status lbq_decode_step_q1g128(const lbq_q1_layer* layers, int32_t n_layers, 
                                   uint16_t* d_act, int32_t batch, float eps, void* stream);
 
 
+/* The batch-1 decode step of lbq_decode_step_q1g128 for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and the same results, bit for bit, with the stage workspace taken from a
+ * static device array of 116 KiB that each GPU the library runs on holds until the process
+ * ends. It calls no hipMalloc, hipFree or other allocating routine. Every call on one GPU
+ * shares that array and leaves its contents behind (nothing in it needs clearing between
+ * calls): calls that overlap on one GPU, on any streams, race and corrupt each other's
+ * results, so order them. Arguments and validation as lbq_decode_step_q1g128, plus:
+ * batch == 1, hidden <= 7168, ffn <= 32768, d_act 16-byte aligned and d_x0 8-byte aligned;
+ * other requests return LBQ_E_UNSUPPORTED having launched nothing. */
+lbq_status lbq_decode_step_q1g128_noalloc(const lbq_q1_layer* layers, int32_t n_layers,
+                                          int32_t hidden, int32_t kv, int32_t ffn,
+                                          const uint16_t* d_x0, uint16_t* d_act, int32_t batch,
+                                          float eps, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

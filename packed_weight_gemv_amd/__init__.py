@@ -76,6 +76,8 @@ def load():
         "lbq_decode_act_elems": ([i32, i32, i32, i32, i32], sz),
         "lbq_decode_act_offset": ([i32, i32, i32, i32, i32, i32, i32], i64),
         "lbq_decode_step_q1g128": ([P, i32, i32, i32, i32, P, P, i32, ctypes.c_float, P], i32),
+        "lbq_decode_step_q1g128_noalloc": ([P, i32, i32, i32, i32, P, P, i32, ctypes.c_float,
+                                            P], i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -328,6 +330,14 @@ def lbq_decode_step_q1g128(layer_array, n_layers, hidden, kv, ffn, x0, act, eps=
                            stream=None) -> None:
     B = x0.shape[0]
     _check("lbq_decode_step_q1g128", load().lbq_decode_step_q1g128(
+        ctypes.cast(layer_array, ctypes.c_void_p), n_layers, hidden, kv, ffn, _dptr(x0),
+        _dptr(act), B, float(eps), _stream(stream)))
+
+
+def lbq_decode_step_q1g128_noalloc(layer_array, n_layers, hidden, kv, ffn, x0, act, eps=1e-6,
+                                   stream=None) -> None:
+    B = x0.shape[0]
+    _check("lbq_decode_step_q1g128_noalloc", load().lbq_decode_step_q1g128_noalloc(
         ctypes.cast(layer_array, ctypes.c_void_p), n_layers, hidden, kv, ffn, _dptr(x0),
         _dptr(act), B, float(eps), _stream(stream)))
 

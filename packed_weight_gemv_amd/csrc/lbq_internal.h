@@ -84,8 +84,10 @@ lbq_status splitk_workspace(size_t partial_bytes, void* stream, unsigned** count
                             float** partials);
 
 // Batch-1 decode step as two stage launches per layer (lbq_stage.hip); LBQ_E_UNSUPPORTED for
-// shapes it does not cover.
+// shapes it does not cover. Its workspace is the stream's (allocated on first use) or, with
+// no_alloc, the device's static scratch array (nothing is allocated).
 lbq_status stage_decode_q1(const lbq_q1_layer* layers, int n_layers, int hidden, int kv, int ffn,
-                           const uint16_t* d_x0, uint16_t* d_act, float eps, void* stream);
+                           const uint16_t* d_x0, uint16_t* d_act, float eps, void* stream,
+                           bool no_alloc);
 
 }  // namespace lbq

@@ -1021,10 +1021,11 @@ extern "C" lbq_status lbq_rms_rescale_bf16(const uint16_t* d_y, const uint16_t* 
   return launch_status();
 }
 
-extern "C" lbq_status lbq_decode_step_q1g128(const lbq_q1_layer* layers, int32_t n_layers,
-                                             int32_t hidden, int32_t kv, int32_t ffn,
-                                             const uint16_t* d_x0, uint16_t* d_act,
-                                             int32_t batch, float eps, void* stream) {
+// Validation shared by the decode-step entry points: every pointer the step uses, before
+// anything is launched.
+static lbq_status validate_decode(const lbq_q1_layer* layers, int32_t n_layers, int32_t hidden,
+                                  int32_t kv, int32_t ffn, const uint16_t* d_x0,
+                                  uint16_t* d_act, int32_t batch, float eps) {
   if (!layers || !d_x0 || !d_act) return LBQ_E_NULL;
   const size_t elems = lbq_decode_act_elems(n_layers, hidden, kv, ffn, batch);
   if (!elems || !(eps >= 0.f)) return LBQ_E_SHAPE;
@@ -1048,10 +1049,19 @@ extern "C" lbq_status lbq_decode_step_q1g128(const lbq_q1_layer* layers, int32_t
     }
   }
   if (overlaps(d_x0, (size_t)batch * hidden * 2, d_act, elems * 2)) return LBQ_E_ALIAS;
+  return LBQ_OK;
+}
+
+extern "C" lbq_status lbq_decode_step_q1g128(const lbq_q1_layer* layers, int32_t n_layers,
+                                             int32_t hidden, int32_t kv, int32_t ffn,
+                                             const uint16_t* d_x0, uint16_t* d_act,
+                                             int32_t batch, float eps, void* stream) {
+  const lbq_status vst = validate_decode(layers, n_layers, hidden, kv, ffn, d_x0, d_act, batch, eps);
+  if (vst != LBQ_OK) return vst;
   hipStream_t s = (hipStream_t)stream;
   if (batch == 1) {
     const lbq_status st =
-        stage_decode_q1(layers, n_layers, hidden, kv, ffn, d_x0, d_act, eps, s);
+        stage_decode_q1(layers, n_layers, hidden, kv, ffn, d_x0, d_act, eps, s, false);
     if (st != LBQ_E_UNSUPPORTED) return st;
   }
   auto at = [&](int layer, int slot) {
@@ -1082,4 +1092,14 @@ extern "C" lbq_status lbq_decode_step_q1g128(const lbq_q1_layer* layers, int32_t
   }
 #undef CHECK
   return LBQ_OK;
+}
+
+extern "C" lbq_status lbq_decode_step_q1g128_noalloc(const lbq_q1_layer* layers, int32_t n_layers,
+                                                     int32_t hidden, int32_t kv, int32_t ffn,
+                                                     const uint16_t* d_x0, uint16_t* d_act,
+                                                     int32_t batch, float eps, void* stream) {
+  const lbq_status vst = validate_decode(layers, n_layers, hidden, kv, ffn, d_x0, d_act, batch, eps);
+  if (vst != LBQ_OK) return vst;
+  if (batch != 1) return LBQ_E_UNSUPPORTED;
+  return stage_decode_q1(layers, n_layers, hidden, kv, ffn, d_x0, d_act, eps, stream, true);
 }

@@ -796,6 +796,29 @@ lbq_status st_workspace(hipStream_t s, float** out) {
   return LBQ_OK;
 }
 
+// The allocation-free variant's workspace: a static device array of the same layout, which
+// every GPU the library runs on holds until the process ends. Host code never uses the array's
+// name as an address: its device address is looked up once per device (with that device
+// current) and kept in g_scratch_ptr. All allocation-free steps on one GPU share it.
+constexpr size_t kScratchFloats = kPartFloats + kStatFloats;   // 29,696 floats (116 KiB)
+__device__ __align__(256) float scratch[kScratchFloats];
+constexpr int kMaxDevices = 64;
+float* g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+lbq_status scratch_workspace(float** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LBQ_E_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LBQ_E_DEVICE;
+    g_scratch_ptr[dev] = (float*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LBQ_OK;
+}
+
 StMat st_mat(const void* w, int n, int k, uint16_t* y) {
   Geometry g;
   make_geometry(n, k, kQ1GroupBlocks, &g);
@@ -817,7 +840,7 @@ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 // apply.
 lbq_status lbq::stage_decode_q1(const lbq_q1_layer* layers, int n_layers, int hidden, int kv,
                                 int ffn, const uint16_t* d_x0, uint16_t* d_act, float eps,
-                                void* stream) {
+                                void* stream, bool no_alloc) {
   hipStream_t s = (hipStream_t)stream;
   if (hidden % kGroup || kv % kGroup || ffn % kGroup) return LBQ_E_UNSUPPORTED;
   if ((uintptr_t)d_act % 16 || (uintptr_t)d_x0 % 8) return LBQ_E_UNSUPPORTED;
@@ -854,8 +877,10 @@ lbq_status lbq::stage_decode_q1(const lbq_q1_layer* layers, int n_layers, int hi
         (pg[p + 1] - pg[p]) * (kGroup / 4) > kPRounds2 * kPThreads)
       return LBQ_E_UNSUPPORTED;
   if ((size_t)P * hidden > kPartFloats) return LBQ_E_UNSUPPORTED;
+  // nothing in the workspace needs clearing: every partial slot and pair sum a launch reads
+  // is written earlier in the same step
   float* ws = nullptr;
-  const lbq_status wst = st_workspace(s, &ws);
+  const lbq_status wst = no_alloc ? scratch_workspace(&ws) : st_workspace(s, &ws);
   if (wst != LBQ_OK) return wst;
   float* part = ws;
   float* stat = ws + kPartFloats;
