@@ -91,6 +91,61 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def host_cpu():
+    """(cores this process may run on, CPU model name from /proc/cpuinfo)."""
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return cores, model
+
+
+def oracle_rows(fn, signs, scales, x, n, threads, rows=None):
+    """The oracle GEMV `fn` over `rows` (default: all n) split across `threads` host threads (the
+    oracle is a plain C function; ctypes releases the interpreter lock while it runs). Returns
+    (y, l1) as the oracle does."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+    rows = np.arange(n, dtype=np.int32) if rows is None else np.asarray(rows, dtype=np.int32)
+    chunks = [c for c in np.array_split(rows, max(1, min(threads, rows.size))) if c.size]
+    with ThreadPoolExecutor(len(chunks)) as ex:
+        res = list(ex.map(lambda r: fn(signs, scales, x, rows=r), chunks))
+    return (np.concatenate([r[0] for r in res], axis=1),
+            np.concatenate([r[1] for r in res], axis=1))
+
+
+def hbm_achievable(torch, lbq, dev, gib: int = 4):
+    """Best read bandwidth (GB/s) of the streaming-read probe over a `gib` GiB buffer (best of
+    several workgroup counts, three passes each), the reference for "% of achievable HBM"."""
+    nbytes = gib << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.empty(65536, dtype=torch.int32, device=dev)
+    best = 0.0
+    for wgs in (1024, 2048, 4096, 8192):
+        lbq.lbq_hbm_read_probe(buf, sink, wgs)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            lbq.lbq_hbm_read_probe(buf, sink, wgs)
+            e1.record()
+            torch.cuda.synchronize()
+            best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return best
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,9 +155,21 @@ def parse():
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly")
     ap.add_argument("--cpu-layers", type=int, default=2,
-                    help="layers of the stream the CPU oracle baseline runs (0 = skip)")
+                    help="layers of the stream the CPU oracle baseline runs on all host cores "
+                         "(0 = skip the baseline, the sampled parity and the chain check)")
+    ap.add_argument("--rounds", type=int, default=3,
+                    help="extra timed rounds of --steps steps each (min and median reported)")
+    ap.add_argument("--no-chain", action="store_true",
+                    help="skip the oracle chain over all layers (batch 1) and its cosine")
+    ap.add_argument("--no-hbm-probe", action="store_true",
+                    help="skip the 4 GiB streaming-read reference of achievable bandwidth")
     ap.add_argument("--kernel-steps", type=int, default=3,
                     help="instrumented steps timing each GEMV launch with HIP events")
+    ap.add_argument("--q1-gemv", action="store_true",
+                    help="time single Q1_0_g128 GEMVs instead: 5120x5120 at batch 1, and gate/up "
+                         "17408x5120 and down 5120x17408 at batch 1, 4 and 16")
+    ap.add_argument("--mlp2bit", action="store_true",
+                    help="time the 2-bit integer MLP (1024 vectors through 256-192-128-40) instead")
     ap.add_argument("--tern-layer", action="store_true",
                     help="time the ternary g160 GEMVs of one 27B-shaped layer instead")
     ap.add_argument("--z80-chat", action="store_true",
@@ -161,6 +228,10 @@ def main() -> int:
         return chat_bench(args, lbq, synth, torch, np, dev)
     if args.tern_layer:
         return tern_layer_bench(args, lbq, synth, torch, np, dev)
+    if args.q1_gemv:
+        return q1_gemv_bench(args, lbq, synth, torch, np, dev)
+    if args.mlp2bit:
+        return mlp2bit_bench(args, lbq, synth, torch, np, dev)
 
     L, B = args.layers, args.batch
     hid, kv, ffn = synth.STREAM_HIDDEN, synth.STREAM_KV, synth.STREAM_FFN
@@ -225,6 +296,21 @@ def main() -> int:
     ms = start.elapsed_time(end) / args.steps
     gbs = bytes_per_step / (ms * 1e-3) / 1e9
     step_kernel_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    # further rounds of K steps each, after the timed region (run-to-run spread)
+    round_ms = []
+    for _ in range(max(0, args.rounds)):
+        r0 = torch.cuda.Event(enable_timing=True)
+        r1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        r0.record(stream)
+        for _ in range(args.steps):
+            run()
+        r1.record(stream)
+        torch.cuda.synchronize()
+        round_ms.append(r0.elapsed_time(r1) / args.steps)
+    achievable = None if args.no_hbm_probe else hbm_achievable(torch, lbq, dev)
+    if achievable:
+        log(f"achievable HBM read bandwidth (4 GiB streaming read): {achievable:.0f} GB/s")
 
     # ---- dominant kernel ---------------------------------------------------------------------
     if B == 1:
@@ -233,7 +319,8 @@ def main() -> int:
         kern_avg_ms, kern_bytes = step_kernel_ms, bytes_per_step
     else:
         # host-driven step: every Q1 GEMV launch of a step bracketed by events
-        kern_name = "q1_gemv_kernel (per-projection launches)"
+        kern_name = ("per-projection Q1 launches (the matrix-core product gemm_kernel for "
+                     "batch >= 2)")
         gemv_ms, gemv_bytes, launches = 0.0, 0, 0
         src = {"q": "x", "k": "x", "v": "x", "gate": "x", "up": "x", "o": "xo", "down": "xd"}
         for _ in range(max(1, args.kernel_steps)):
@@ -260,34 +347,93 @@ def main() -> int:
         torch.cuda.synchronize()
     kern_gbs = kern_bytes / (kern_avg_ms * 1e-3) / 1e9
 
-    # ---- CPU oracle baseline (bounded sample) + teacher-forced parity of that sample ----------
-    cpu = None
+    # ---- oracle legs: sampled teacher-forced parity, all-core baseline, chain cosine ---------
+    cpu, parity, chain = None, None, None
     if args.cpu_layers > 0:
         import oracle
         from tests._gpu import check_within  # the tolerance rule shared with the tests
-        cpu_s, cpu_bytes, worst = 0.0, 0, 0.0
+        cores, cpu_model = host_cpu()
         src = {"q": "x", "k": "x", "v": "x", "gate": "x", "up": "x", "o": "xo", "down": "xd"}
+        view = lambda slot, l: lbq.act_view(act, slot, l, L, hid, kv, ffn, B).cpu().numpy().view(np.uint16)
+        # (1) teacher-forced parity on sampled rows of every GEMV of layers 0, 1, L/2 - 1, L - 1
+        #     (each GEMV fed the GPU's own input), and the rescales of those layers
+        check_layers = sorted({l for l in (0, 1, L // 2 - 1, L - 1) if 0 <= l < L})
+        worst, checked = 0.0, 0
+        for l in check_layers:
+            for nm in synth.STREAM_MATRICES:
+                m = synth.stream_matrix(l, nm)
+                n = m.shape[0]
+                rows = np.unique(np.concatenate([np.linspace(0, n - 1, 384).astype(np.int32),
+                                                 [n - 1]])).astype(np.int32)
+                ref, l1 = oracle_rows(oracle.gemv_q1g128, m.signs, m.scales, view(src[nm], l), n,
+                                      cores, rows)
+                worst = max(worst, check_within(view(nm, l)[:, rows], ref, l1,
+                                                f"bench layer {l} {nm}"))
+                checked += rows.size * B
+            from tests._gpu import bf16_ordinal
+            nxt = (view("x", l + 1) if l + 1 < L else lbq.act_view(
+                act, "final", L, L, hid, kv, ffn, B).cpu().numpy().view(np.uint16))
+            for yname, y2name, got in (("q", None, view("xo", l)), ("gate", "up", view("xd", l)),
+                                       ("down", None, nxt)):
+                xr, _ = oracle.rms_rescale(view(yname, l),
+                                           None if y2name is None else view(y2name, l))
+                dd = np.abs(bf16_ordinal(xr) - bf16_ordinal(got))
+                assert dd.max() <= 1, f"bench layer {l} rescale of {yname}: {dd.max()} ulp"
+        parity = {"layers": check_layers, "gemv_rows_checked": int(checked),
+                  "worst_err_over_l1": float(f"{worst:.3e}"), "tolerance": "2e-3 * sum|s*w*x|",
+                  "rescales": "within 1 bf16 ulp"}
+        log(f"parity: layers {check_layers}, sampled rows of all 7 GEMVs within 2e-3*L1 "
+            f"(worst |err|/L1 = {worst:.2e}); rescales within 1 ulp")
+        # (2) the oracle as it stands on all host cores (rows split across threads), on every
+        #     row of every GEMV of the first --cpu-layers layers
+        cpu_s, cpu_bytes = 0.0, 0
         sample_layers = list(range(min(args.cpu_layers, L)))
         for l in sample_layers:
             for nm in synth.STREAM_MATRICES:
                 m = synth.stream_matrix(l, nm)
-                xin = lbq.act_view(act, src[nm], l, L, hid, kv, ffn, B).cpu().view(torch.int16)
-                xin = xin.numpy().view(np.uint16)
+                xin = view(src[nm], l)
                 t = time.perf_counter()
-                ref, l1 = oracle.gemv_q1g128(m.signs, m.scales, xin)
+                oracle_rows(oracle.gemv_q1g128, m.signs, m.scales, xin, m.shape[0], cores)
                 cpu_s += time.perf_counter() - t
                 cpu_bytes += m.shape[0] * m.shape[1] * 9 // 64 * B
-                y = lbq.act_view(act, nm, l, L, hid, kv, ffn, B).cpu().view(torch.int16)
-                worst = max(worst, check_within(y.numpy().view(np.uint16), ref, l1,
-                                                f"bench layer {l} {nm}"))
-        log(f"parity: layers {sample_layers} all 7 GEMVs within 2e-3*L1 "
-            f"(worst |err|/L1 = {worst:.2e}); oracle {cpu_s:.1f} s")
-        cpu = {"value": round(cpu_bytes / cpu_s / 1e9, 6), "unit": "GB/s", "cores": 1,
-               "kind": "oracle",
+        log(f"oracle baseline: {cpu_bytes / 1e6:.0f} MB in {cpu_s:.1f} s on {cores} cores ({cpu_model})")
+        cpu = {"value": round(cpu_bytes / cpu_s / 1e9, 6), "unit": "GB/s", "cores": cores,
+               "kind": "oracle", "cpu_model": cpu_model,
                "sample": f"{len(sample_layers)} of {L} layers (all 7 GEMVs of each, every row, "
-                         f"batch {B}), plain scalar C oracle in float64, one thread; "
-                         f"{cpu_bytes / 1e6:.1f} MB of packed weights in {cpu_s:.1f} s",
+                         f"batch {B}), plain scalar C oracle in float64, rows split over "
+                         f"{cores} threads; {cpu_bytes / 1e6:.1f} MB of packed weights in "
+                         f"{cpu_s:.1f} s",
                "tok_s_equiv": round(B * cpu_bytes / bytes_per_step / cpu_s, 6)}
+        # (3) the whole chain in the oracle (batch 1): x_{l+1} = rms(down(rms(gate * up))) from
+        #     the same x0, every row, compared with the GPU's chain by cosine similarity
+        #     (reported, not gated: the two chains drift apart by rounding)
+        if B == 1 and not args.no_chain:
+            t = time.perf_counter()
+            x = x0_np.reshape(1, hid)
+            cos = []
+            for l in range(L):
+                g = synth.stream_matrix(l, "gate")
+                u = synth.stream_matrix(l, "up")
+                dn = synth.stream_matrix(l, "down")
+                yg, _ = oracle_rows(oracle.gemv_q1g128, g.signs, g.scales, x, ffn, cores)
+                yu, _ = oracle_rows(oracle.gemv_q1g128, u.signs, u.scales, x, ffn, cores)
+                xd, _ = oracle.rms_rescale(oracle.round_bf16(yg), oracle.round_bf16(yu))
+                yd, _ = oracle_rows(oracle.gemv_q1g128, dn.signs, dn.scales, xd, hid, cores)
+                x, _ = oracle.rms_rescale(oracle.round_bf16(yd))
+                gpu_x = (view("x", l + 1) if l + 1 < L else lbq.act_view(
+                    act, "final", L, L, hid, kv, ffn, B).cpu().numpy().view(np.uint16))
+                a = oracle.bf16_to_f64(x).ravel()
+                b = oracle.bf16_to_f64(gpu_x).ravel()
+                cos.append(float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b))))
+            marks = [m for m in (1, 2, 4, 8, 16, 32, 64) if m <= L]
+            chain = {"layers": L, "cosine_final_x": round(cos[-1], 6),
+                     "cosine_by_layer": {str(m): round(cos[m - 1], 6) for m in marks},
+                     "note": "x_l of the GPU chain vs x_l of the oracle chain from the same x0; "
+                             "random 1-bit layers amplify rounding differences, so the chains "
+                             "decorrelate with depth (reported, not gated)",
+                     "oracle_seconds": round(time.perf_counter() - t, 1), "threads": cores}
+            log(f"chain: cosine of x_l (GPU vs oracle chain) by layer: {chain['cosine_by_layer']} "
+                f"({chain['oracle_seconds']} s)")
 
     out = {
         "metric": "packed-weight HBM GB/s (% of peak) + decode tok/s-equiv, batch 1, 27B-shape",
@@ -326,6 +472,16 @@ def main() -> int:
             "bytes_per_launch": round(kern_bytes),
         },
         "cpu_baseline": cpu,
+        "rounds": {"count": len(round_ms), "steps_each": args.steps,
+                   "ms_per_step_min": round(min(round_ms), 4) if round_ms else None,
+                   "ms_per_step_median": round(sorted(round_ms)[len(round_ms) // 2], 4)
+                   if round_ms else None},
+        "hbm_achievable": None if achievable is None else {
+            "gbs": round(achievable, 1), "pct_of_peak": round(100.0 * achievable / HBM_PEAK_GBS, 2),
+            "probe": "4 GiB streaming read, 16-byte nontemporal loads (lbq_hbm_read_probe)",
+            "value_pct_of_achievable": round(100.0 * gbs / achievable, 2)},
+        "parity": parity,
+        "chain": chain,
     }
     print(json.dumps(out), flush=True)
     return 0
@@ -362,6 +518,150 @@ def graph_time_us(torch, fn, pool, args, cap, stream):
     torch.cuda.synchronize()
     del graph
     return e0.elapsed_time(e1) * 1e3 / (args.steps * calls)
+
+
+def q1_gemv_bench(args, lbq, synth, torch, np, dev) -> int:
+    """Single Q1_0_g128 GEMVs through lbq_gemv_q1g128: 5120x5120 at batch 1, and the MLP
+    projections gate/up 17408x5120 and down 5120x17408 at batch 1, 4 and 16. Weights rotate
+    through >= 1 GiB of copies (no reuse from the 256 MB last-level cache); the calls are
+    replayed from one HIP graph. Algorithmic bytes per call: packed weights (1.125 bits per
+    weight) plus bf16 activations in and out. The headline value is 5120x5120 at batch 1."""
+    stream = torch.cuda.current_stream()
+    cap = torch.cuda.Stream()
+    import oracle
+    from tests._gpu import check_within
+    cores, cpu_model = host_cpu()
+    cases, head = [], None
+    worst = 0.0
+    for name, n, k, batches in (("square", 5120, 5120, (1,)), ("gate", 17408, 5120, (1, 4, 16)),
+                                ("down", 5120, 17408, (1, 4, 16))):
+        m = synth.q1_matrix(n, k, workload=synth.W_Q1_SQUARE if name == "square"
+                            else synth.W_Q1_MLP, matrix={"square": 0, "gate": 4, "down": 6}[name])
+        packed = lbq.lbq_pack_q1g128(m.signs, m.scales)
+        host = torch.from_numpy(packed)
+        pool = [host.to(dev) for _ in range(max(2, -(-(1 << 30) // packed.nbytes)))]
+        for batch in batches:
+            xh = synth.activations(batch, k, workload=synth.W_Q1_MLP, extra=200 + batch)
+            x = torch.from_numpy(xh.view(np.int16)).to(dev)
+            y = torch.empty((batch, n), dtype=torch.int16, device=dev)
+            us = graph_time_us(torch, lambda w: lbq.lbq_gemv_q1g128(w, n, k, x, y, stream=cap),
+                               pool, args, cap, stream)
+            nbytes = packed.nbytes + 2 * batch * (n + k)
+            rows = np.unique(np.linspace(0, n - 1, 256).astype(np.int32))
+            ref, l1 = oracle_rows(oracle.gemv_q1g128, m.signs, m.scales, xh, n, cores, rows)
+            worst = max(worst, check_within(y.cpu().numpy().view(np.uint16)[:, rows], ref, l1,
+                                            f"q1 {name} B={batch}"))
+            case = {"matrix": name, "n": n, "k": k, "batch": batch, "us_per_call": round(us, 2),
+                    "gbs": round(nbytes / us / 1e3, 1),
+                    "pct_of_hbm_peak": round(100.0 * nbytes / us / 1e3 / HBM_PEAK_GBS, 2)}
+            cases.append(case)
+            if head is None:
+                head = (us, nbytes)
+            log(f"q1 {name} {n}x{k} B={batch}: {us:.2f} us, {nbytes / us / 1e3:.0f} GB/s")
+        del pool
+        torch.cuda.empty_cache()
+    us, nbytes = head
+    gbs = nbytes / us / 1e3
+    # the oracle on all host cores: every row of the 5120x5120 matrix at batch 1
+    m = synth.q1_matrix(5120, 5120, workload=synth.W_Q1_SQUARE, matrix=0)
+    xh = synth.activations(1, 5120, workload=synth.W_Q1_MLP, extra=201)
+    t0 = time.perf_counter()
+    reps = 0
+    while time.perf_counter() - t0 < 2.0:
+        oracle_rows(oracle.gemv_q1g128, m.signs, m.scales, xh, 5120, cores)
+        reps += 1
+    dt = time.perf_counter() - t0
+    out = {
+        "metric": "packed-weight HBM GB/s of single Q1_0_g128 GEMVs (5120x5120 at batch 1)",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "gemv_per_s": round(1e6 / us, 1),
+        "config": {"workload": "Q1_0_g128 GEMV 5120x5120, batch 1 (and the MLP projections "
+                               "gate/up 17408x5120, down 5120x17408 at batch 1, 4, 16 in cases)",
+                   "rotation": ">= 1 GiB of weight copies", "launch": "HIP graph",
+                   "parallelism": "single GPU"},
+        "cases": cases,
+        "parity": {"rows_checked_per_case": 256, "worst_err_over_l1": float(f"{worst:.3e}"),
+                   "tolerance": "2e-3 * sum|s*w*x|"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "q1_gemv_kernel<1>", "avg_launch_us": round(us, 3),
+                     "bytes_per_launch": nbytes},
+        "cpu_baseline": {"value": round(reps * m.shape[0] * m.shape[1] * 9 / 64 / dt / 1e9, 4),
+                         "unit": "GB/s", "cores": cores, "kind": "oracle",
+                         "cpu_model": cpu_model,
+                         "sample": f"{reps} full 5120x5120 batch-1 GEMVs, rows split over "
+                                   f"{cores} threads, in {dt:.1f} s"},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def mlp2bit_bench(args, lbq, synth, torch, np, dev) -> int:
+    """The 2-bit integer MLP through lbq_mlp_2bit_i16: 1024 input vectors of 256 int16 bucket
+    counts (uniform 0..127) through the 256-192-128-40 network with uniform 2-bit codes, one
+    launch per step; logits and argmax are compared with the oracle bit for bit."""
+    layers = synth.mlp2bit_layers()
+    xh = synth.mlp2bit_inputs()
+    B = xh.shape[0]
+    lw = [torch.from_numpy(lbq.lbq_pack_2bit(c)).to(dev) for c in layers]
+    x = torch.from_numpy(xh).to(dev)
+    logits = torch.empty((B, synth.MLP_DIMS[-1]), dtype=torch.int16, device=dev)
+    am = torch.empty((B,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(max(1, args.warmup)):
+        lbq.lbq_mlp_2bit_i16(lw, synth.MLP_DIMS, x, logits, am, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        lbq.lbq_mlp_2bit_i16(lw, synth.MLP_DIMS, x, logits, am, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    import oracle
+    t0 = time.perf_counter()
+    ref_logits, ref_am = oracle.mlp_2bit(layers, list(synth.MLP_DIMS), xh)
+    dt = time.perf_counter() - t0
+    assert np.array_equal(logits.cpu().numpy(), ref_logits), "2-bit MLP logits differ"
+    assert np.array_equal(am.cpu().numpy(), ref_am), "2-bit MLP argmax differs"
+    tmacs = B * Z80_MACS_PER_EVAL / (us * 1e-6) / 1e12
+    log(f"mlp2bit: {us:.2f} us per launch of {B} vectors, {tmacs:.3f} T MAC/s, bit-exact")
+    out = {
+        "metric": "2-bit integer MLP evaluations per second (1024 vectors, 256-192-128-40)",
+        "value": round(B / (us * 1e-6), 1),
+        "unit": "evals/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int16 x 2-bit -> int32 (mod 2^16)",
+        "data": "synthetic",
+        "gmac_per_s": round(tmacs * 1e3, 1),
+        "config": {"workload": f"Z80-uLM-shaped 2-bit MLP, {B} vectors, 256-192-128-40",
+                   "parallelism": "single GPU", "parity": "logits and argmax bit-exact"},
+        "roofline": {"bound": "alu", "achieved": round(tmacs, 3), "peak": ALU_DOT2_PEAK_TMACS,
+                     "unit": "T 2-bit MAC/s (v_dot2_i32_i16 issue rate)",
+                     "frac": round(tmacs / ALU_DOT2_PEAK_TMACS, 4), "traffic": None,
+                     "kernel": "mlp2bit_kernel", "avg_launch_us": round(us, 3)},
+        "cpu_baseline": {"value": round(B / dt, 1), "unit": "evals/s", "cores": 1,
+                         "kind": "oracle", "sample": f"all {B} vectors, one host thread"},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
 
 
 def tern_layer_bench(args, lbq, synth, torch, np, dev) -> int:

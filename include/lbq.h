@@ -358,6 +358,18 @@ lbq_status lbq_decode_step_q1g128(const lbq_q1_layer* layers, int32_t n_layers, 
                                   uint16_t* d_act, int32_t batch, float eps, void* stream);
 
 
+/* ------------------------------------------------------------------------------------------
+ * Measurement aid (no operation of the pages): the achievable HBM read bandwidth that the
+ * GEMVs' streamed bytes are compared with. Reads `bytes` of d_src once with 16-byte
+ * nontemporal loads spread over `workgroups` workgroups of 256 threads, and writes one XOR
+ * checksum word per workgroup to d_sink[0 .. workgroups - 1].
+ *   d_src : device, 16-byte aligned, bytes a multiple of 16
+ *   d_sink: device uint32 [workgroups], 4-byte aligned, not overlapping d_src
+ * Requires 1 <= workgroups <= 65536.
+ * ------------------------------------------------------------------------------------------ */
+lbq_status lbq_hbm_read_probe(const void* d_src, size_t bytes, uint32_t* d_sink,
+                              int32_t workgroups, void* stream);
+
 /* The batch-1 decode step of lbq_decode_step_q1g128 for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same kernels and the same results, bit for bit, with the stage workspace taken from a

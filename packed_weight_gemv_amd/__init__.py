@@ -76,6 +76,7 @@ def load():
         "lbq_decode_act_elems": ([i32, i32, i32, i32, i32], sz),
         "lbq_decode_act_offset": ([i32, i32, i32, i32, i32, i32, i32], i64),
         "lbq_decode_step_q1g128": ([P, i32, i32, i32, i32, P, P, i32, ctypes.c_float, P], i32),
+        "lbq_hbm_read_probe": ([P, sz, P, i32, P], i32),
         "lbq_decode_step_q1g128_noalloc": ([P, i32, i32, i32, i32, P, P, i32, ctypes.c_float,
                                             P], i32),
     }
@@ -340,6 +341,13 @@ def lbq_decode_step_q1g128_noalloc(layer_array, n_layers, hidden, kv, ffn, x0, a
     _check("lbq_decode_step_q1g128_noalloc", load().lbq_decode_step_q1g128_noalloc(
         ctypes.cast(layer_array, ctypes.c_void_p), n_layers, hidden, kv, ffn, _dptr(x0),
         _dptr(act), B, float(eps), _stream(stream)))
+
+
+def lbq_hbm_read_probe(src, sink, workgroups: int, stream=None) -> None:
+    """Streams every byte of the device tensor `src` once (bandwidth reference)."""
+    nbytes = src.numel() * src.element_size()
+    _check("lbq_hbm_read_probe", load().lbq_hbm_read_probe(
+        _dptr(src), nbytes, _dptr(sink), int(workgroups), _stream(stream)))
 
 
 def act_view(act, slot: str, layer: int, n_layers, hidden, kv, ffn, batch):

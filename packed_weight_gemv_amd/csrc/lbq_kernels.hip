@@ -1006,6 +1006,51 @@ extern "C" lbq_status lbq_gemv_tern_g160(const void* d_w, int32_t n, int32_t k,
   return launch_status();
 }
 
+// ---------------------------------------------------------------------------------------------
+// streaming-read probe: the achievable HBM read bandwidth that the GEMVs are measured against
+// ---------------------------------------------------------------------------------------------
+constexpr int kProbeThreads = 256;
+constexpr int kProbeUnroll = 8;
+
+__global__ __launch_bounds__(kProbeThreads) void hbm_read_kernel(const u32x4* src, size_t n16,
+                                                                 uint32_t* sink) {
+  const size_t stride = (size_t)gridDim.x * kProbeThreads;
+  size_t i = (size_t)blockIdx.x * kProbeThreads + threadIdx.x;
+  uint32_t acc = 0;
+  // kProbeUnroll independent 16-byte loads in flight per thread, then the tail one at a time
+  for (; i + (kProbeUnroll - 1) * stride < n16; i += kProbeUnroll * stride) {
+    u32x4 v[kProbeUnroll];
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 v = __builtin_nontemporal_load(src + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  // one word per workgroup: the XOR of its threads' words
+  __shared__ uint32_t red[kProbeThreads];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int j = 0; j < kProbeThreads; ++j) t ^= red[j];
+    sink[blockIdx.x] = t;
+  }
+}
+
+extern "C" lbq_status lbq_hbm_read_probe(const void* d_src, size_t bytes, uint32_t* d_sink,
+                                         int32_t workgroups, void* stream) {
+  if (bytes == 0 || bytes % 16 != 0 || workgroups < 1 || workgroups > 65536) return LBQ_E_SHAPE;
+  if (!d_src || !d_sink) return LBQ_E_NULL;
+  if ((uintptr_t)d_src % 16 || (uintptr_t)d_sink % 4) return LBQ_E_ALIGN;
+  if (overlaps(d_sink, (size_t)workgroups * 4, d_src, bytes)) return LBQ_E_ALIAS;
+  hipLaunchKernelGGL(hbm_read_kernel, dim3(workgroups), dim3(kProbeThreads), 0,
+                     (hipStream_t)stream, (const u32x4*)d_src, bytes / 16, d_sink);
+  return launch_status();
+}
+
 extern "C" lbq_status lbq_rms_rescale_bf16(const uint16_t* d_y, const uint16_t* d_y2,
                                            uint16_t* d_x, int32_t n, int32_t batch, float eps,
                                            void* stream) {

@@ -26,7 +26,7 @@ def lib():
 
 def test_library_exports_every_declared_function(lib):
     names = _declared_functions()
-    assert len(names) == 29
+    assert len(names) == 30
     for name in names:
         assert hasattr(lib, name), name
         assert name in dir(lbq) or name in ("lbq_status_string",), f"binding lacks {name}"
