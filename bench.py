@@ -610,7 +610,8 @@ def q1_gemv_bench(args, lbq, synth, torch, np, dev) -> int:
 def mlp2bit_bench(args, lbq, synth, torch, np, dev) -> int:
     """The 2-bit integer MLP through lbq_mlp_2bit_i16: 1024 input vectors of 256 int16 bucket
     counts (uniform 0..127) through the 256-192-128-40 network with uniform 2-bit codes, one
-    launch per step; logits and argmax are compared with the oracle bit for bit."""
+    launch per step, launches replayed from a HIP graph; logits and argmax are compared with the
+    oracle bit for bit."""
     layers = synth.mlp2bit_layers()
     xh = synth.mlp2bit_inputs()
     B = xh.shape[0]
@@ -619,16 +620,11 @@ def mlp2bit_bench(args, lbq, synth, torch, np, dev) -> int:
     logits = torch.empty((B, synth.MLP_DIMS[-1]), dtype=torch.int16, device=dev)
     am = torch.empty((B,), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
-    for _ in range(max(1, args.warmup)):
-        lbq.lbq_mlp_2bit_i16(lw, synth.MLP_DIMS, x, logits, am, stream=stream)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        lbq.lbq_mlp_2bit_i16(lw, synth.MLP_DIMS, x, logits, am, stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    cap = torch.cuda.Stream()
+    # one launch per step, 32 steps per replay of a HIP graph
+    us = graph_time_us(torch, lambda w: lbq.lbq_mlp_2bit_i16(w, synth.MLP_DIMS, x, logits, am,
+                                                             stream=cap),
+                       [lw] * 32, args, cap, stream)
     import oracle
     t0 = time.perf_counter()
     ref_logits, ref_am = oracle.mlp_2bit(layers, list(synth.MLP_DIMS), xh)

@@ -441,23 +441,144 @@ __global__ __launch_bounds__(64 * kI4Waves) void i4_gemv_kernel(
 
 // ---------------------------------------------------------------------------------------------
 // 2-bit integer MLP, all layers fused in one kernel. A workgroup carries kMlpVec input vectors
-// through every layer with the activations in LDS. Per neuron the kernel accumulates
-// sum_k c_k a_k exactly in int32 (c = code 0..3) and subtracts 2 sum_k a_k: the same value as
-// sum_k (c_k - 2) a_k, and since reduction modulo 2^16 is a ring homomorphism, truncating it
-// once to 16 bits gives exactly the 16-bit register-pair result of wrapping after every
-// multiply-accumulate. Then the arithmetic shift right by 2 and, between hidden layers, ReLU.
+// through every layer with the activations in LDS. The sum of a neuron is the exact integer
+// sum_k (c_k - 2) a_k (c = code 0..3); since reduction modulo 2^16 is a ring homomorphism,
+// truncating it once to 16 bits gives exactly the 16-bit register-pair result of wrapping
+// after every multiply-accumulate. Then the arithmetic shift right by 2 and, between hidden
+// layers, ReLU.
+//
+// mlp2bit_lds_kernel: the codes of all layers are copied into LDS once per workgroup, each row
+// padded with zero bytes to whole dwords (16 codes); activations are padded with zeros to
+// match, so a padded code (weight -2) meets a zero input. Four lanes share a neuron, each taking
+// a quarter of its row; a lane decodes a pair of codes once into two int16 weights (c - 2) and
+// applies it to every vector with v_dot2_i32_i16 (the activation pair read is the same for the
+// 64 lanes of a wave, an LDS broadcast). Networks whose padded codes exceed kMlpLdsBytes use
+// mlp2bit_kernel, which reads the codes from global memory.
 // ---------------------------------------------------------------------------------------------
 constexpr int kMlpVec = 4;
+constexpr int kMlpThreads = 768;
+constexpr int kMlpLdsBytes = 96 * 1024;
+constexpr int kMlpPad = LBQ_MLP_MAX_DIM + 16;   // activation row, zero-padded to whole dwords
 struct MlpArgs {
   const uint8_t* w[LBQ_MLP_MAX_LAYERS];
   int dims[LBQ_MLP_MAX_LAYERS + 1];
   int n_layers;
+  int dword_rows;   // every row of every layer starts and ends on a dword boundary
 };
+typedef short short2_t __attribute__((ext_vector_type(2)));
 
+__device__ __forceinline__ void mlp_store_logits(const int16_t (*act)[kMlpPad], int nout,
+                                                 int nv, int v0, int16_t* logits,
+                                                 int32_t* argmax) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < nv * nout; i += blockDim.x)
+    logits[(size_t)v0 * nout + i] = act[i / nout][i % nout];
+  if (argmax && tid < nv) {   // lowest index among ties
+    int best = 0;
+    for (int j = 1; j < nout; ++j)
+      if (act[tid][j] > act[tid][best]) best = j;
+    argmax[v0 + tid] = best;
+  }
+}
+
+__global__ __launch_bounds__(kMlpThreads) void mlp2bit_lds_kernel(
+    MlpArgs P, const int16_t* __restrict__ x, int16_t* __restrict__ logits,
+    int32_t* __restrict__ argmax, int batch) {
+  __shared__ __attribute__((aligned(16))) uint32_t wlds[kMlpLdsBytes / 4];
+  __shared__ __attribute__((aligned(16))) int16_t act[2][kMlpVec][kMlpPad];
+  const int tid = threadIdx.x;
+  const int v0 = blockIdx.x * kMlpVec;
+  const int nv = min(kMlpVec, batch - v0);
+  // codes of every layer: row r of layer l at wlds[woff[l] + r * kw], kw = ceil(k / 16) dwords,
+  // assembled byte by byte from the canonical rows (k / 4 bytes each), zero bytes past the row
+  int woff[LBQ_MLP_MAX_LAYERS];
+  {
+    int off = 0;
+    for (int l = 0; l < P.n_layers; ++l) {
+      woff[l] = off;
+      const int rb = P.dims[l] / 4, kw = (P.dims[l] + 15) / 16, nout = P.dims[l + 1];
+      const uint8_t* src = P.w[l];
+      if (P.dword_rows) {   // rows are whole dwords: a straight copy
+        const uint32_t* s4 = (const uint32_t*)src;
+        for (int i = tid; i < nout * kw; i += kMlpThreads) wlds[off + i] = s4[i];
+      } else {
+        for (int i = tid; i < nout * kw; i += kMlpThreads) {
+          const int r = i / kw, jb = 4 * (i - r * kw);
+          uint32_t d = 0;
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            if (jb + b < rb) d |= (uint32_t)src[(size_t)r * rb + jb + b] << (8 * b);
+          wlds[off + i] = d;
+        }
+      }
+      off += nout * kw;
+    }
+  }
+  const int d0 = P.dims[0], d0p = (d0 + 15) & ~15;
+  for (int i = tid; i < kMlpVec * d0p; i += kMlpThreads) {
+    const int v = i / d0p, j = i - v * d0p;
+    act[0][v][j] = (v < nv && j < d0) ? x[(size_t)(v0 + v) * d0 + j] : (int16_t)0;
+  }
+  int cur = 0;
+  for (int l = 0; l < P.n_layers; ++l) {
+    const int nout = P.dims[l + 1], kw = (P.dims[l] + 15) / 16;
+    const int per = (kw + 3) / 4;   // dwords per quarter row
+    const bool relu = l < P.n_layers - 1;
+    const int noutp = (nout + 15) & ~15;
+    __syncthreads();
+    for (int t0 = 0; t0 < 4 * noutp; t0 += kMlpThreads) {
+      const int task = t0 + tid, r = task >> 2, part = task & 3;
+      int acc[kMlpVec];
+#pragma unroll
+      for (int v = 0; v < kMlpVec; ++v) acc[v] = 0;
+      if (r < nout) {
+        const uint32_t* wr = wlds + woff[l] + r * kw;
+        const int j1 = min(kw, (part + 1) * per);
+        for (int j = part * per; j < j1; ++j) {
+          const uint32_t d = wr[j];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            // codes of inputs 16j + 2i and 16j + 2i + 1 as a pair of int16 (c - 2)
+            const uint32_t cu = ((d >> (4 * i)) & 3u) | (((d >> (4 * i + 2)) & 3u) << 16);
+            const short2_t w2 = __builtin_bit_cast(short2_t, cu) - (short2_t){2, 2};
+#pragma unroll
+            for (int v = 0; v < kMlpVec; ++v) {
+              const uint32_t a = ((const uint32_t*)act[cur][v])[8 * j + i];
+              acc[v] = __builtin_amdgcn_sdot2(w2, __builtin_bit_cast(short2_t, a), acc[v], false);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < kMlpVec; ++v) {
+        acc[v] += __shfl_xor(acc[v], 1, 64);
+        acc[v] += __shfl_xor(acc[v], 2, 64);
+      }
+      if (part == 0 && r < noutp) {
+#pragma unroll
+        for (int v = 0; v < kMlpVec; ++v) {
+          int16_t h = 0;   // rows past nout: the zero padding of the next layer's input
+          if (r < nout) {
+            const int16_t sv = (int16_t)(uint16_t)(uint32_t)acc[v];   // modulo 2^16
+            h = (int16_t)(sv >> 2);                                     // floor(s / 4)
+            if (relu && h < 0) h = 0;
+          }
+          act[cur ^ 1][v][r] = h;
+        }
+      }
+    }
+    cur ^= 1;
+  }
+  __syncthreads();
+  mlp_store_logits(act[cur], P.dims[P.n_layers], nv, v0, logits, argmax);
+}
+
+// The general kernel: codes read from global memory, one thread per (vector, neuron), the
+// exact int32 sum_k c_k a_k minus 2 sum_k a_k.
 __global__ __launch_bounds__(256) void mlp2bit_kernel(MlpArgs P, const int16_t* __restrict__ x,
                                                       int16_t* __restrict__ logits,
                                                       int32_t* __restrict__ argmax, int batch) {
-  __shared__ int16_t act[2][kMlpVec][LBQ_MLP_MAX_DIM];
+  __shared__ int16_t act[2][kMlpVec][kMlpPad];
   __shared__ int32_t asum[kMlpVec];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int v0 = blockIdx.x * kMlpVec;
@@ -497,15 +618,7 @@ __global__ __launch_bounds__(256) void mlp2bit_kernel(MlpArgs P, const int16_t* 
     cur ^= 1;
   }
   __syncthreads();
-  const int nout = P.dims[P.n_layers];
-  for (int i = tid; i < nv * nout; i += 256)
-    logits[(size_t)v0 * nout + i] = act[cur][i / nout][i % nout];
-  if (argmax && tid < nv) {
-    int best = 0;
-    for (int j = 1; j < nout; ++j)
-      if (act[cur][tid][j] > act[cur][tid][best]) best = j;
-    argmax[v0 + tid] = best;
-  }
+  mlp_store_logits(act[cur], P.dims[P.n_layers], nv, v0, logits, argmax);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -861,8 +974,17 @@ extern "C" lbq_status lbq_mlp_2bit_i16(const void* const* d_layer_w, const int32
       return LBQ_E_ALIAS;
   }
   const int grid = (batch + kMlpVec - 1) / kMlpVec;
-  hipLaunchKernelGGL(mlp2bit_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, P, d_x,
-                     d_logits, d_argmax, batch);
+  P.dword_rows = 1;
+  for (int l = 0; l < n_layers; ++l)
+    if (dims[l] % 16 != 0 || (uintptr_t)d_layer_w[l] % 4 != 0) P.dword_rows = 0;
+  size_t lds_words = 0;
+  for (int l = 0; l < n_layers; ++l) lds_words += (size_t)dims[l + 1] * ((dims[l] + 15) / 16);
+  if (lds_words * 4 <= (size_t)kMlpLdsBytes)
+    hipLaunchKernelGGL(mlp2bit_lds_kernel, dim3(grid), dim3(kMlpThreads), 0, (hipStream_t)stream,
+                       P, d_x, d_logits, d_argmax, batch);
+  else
+    hipLaunchKernelGGL(mlp2bit_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, P, d_x,
+                       d_logits, d_argmax, batch);
   return launch_status();
 }
 
