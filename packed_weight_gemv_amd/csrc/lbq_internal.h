@@ -90,4 +90,10 @@ lbq_status stage_decode_q1(const lbq_q1_layer* layers, int n_layers, int hidden,
                            const uint16_t* d_x0, uint16_t* d_act, float eps, void* stream,
                            bool no_alloc);
 
+// Q1_0_g128 GEMV for 2 <= batch <= 16 vectors on the matrix cores (lbq_q1mb.hip); the caller
+// has validated pointers, shapes and aliasing, and d_x is 16-byte aligned. Uses the stream's
+// split-K workspace when k is split.
+lbq_status q1_gemv_mb(const void* d_w, int n, int k, const uint16_t* d_x, uint16_t* d_y,
+                      int batch, void* stream);
+
 }  // namespace lbq

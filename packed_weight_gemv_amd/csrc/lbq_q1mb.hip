@@ -1,0 +1,306 @@
+// lbq_q1mb.hip - Q1_0_g128 GEMV for 2 to 16 activation vectors on the gfx950 matrix cores
+// (the 1-bit format of the Bonsai-27B-gguf digest, "technical architecture highlights").
+//
+// A workgroup of four waves takes one 64-row tile over a slice of k (up to four super-groups of
+// eight 128-weight groups). A unit is one group of the tile: four sub-tiles of 16 rows, each
+// taken in four 32-deep steps of v_mfma_f32_16x16x32_bf16 with the activation vectors as the
+// rows of the A operand (vector m in row m) and 16 weight rows as the 16 columns of B. So the
+// matrix cores work on all vectors at once, and the weights are expanded once for all of them.
+//
+//  * Weights: as loaded, lane l holds the 16-byte sign record of row l (dword r = weights
+//    32 r .. 32 r + 31 of the group); a 4 x 4 transpose across the four 16-lane rows (two
+//    32-lane swaps, two 16-lane swaps) leaves lane (n, h) = (lane mod 16, lane / 16) with dword
+//    h of row 16 t + n in register t. Step s takes that dword's 4-bit fields 2 s and 2 s + 1
+//    (weights 32 h + 8 s .. + 7), each expanded to four bf16 +-1 by one read of a 16-entry LDS
+//    table of 8-byte entries (128 bytes: 32 distinct banks, so a wave's reads never conflict).
+//  * Activations: the A operand of step s for lane (m, h) is x[m][128 g + 32 h + 8 s .. + 7],
+//    16 contiguous bytes read straight from memory (the lanes of absent vectors read nothing);
+//    every workgroup of the same k slice reads the same bytes, which stay in the L2.
+//  * Products of +-1 and bf16 are exact and the matrix cores sum them in fp32; each group's sum
+//    is weighted by its fp16 scale and accumulated in fp32 (lane (n, h) holds vectors
+//    4 h .. 4 h + 3 of row 16 t + n in accumulator t).
+//  * The four waves' sums are added in wave order; slices of k go through the split-K
+//    workspace, and the last workgroup of a tile adds them in slice order (deterministic).
+#include <hip/hip_runtime.h>
+
+#include "lbq_internal.h"
+
+using namespace lbq;
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxSupers = 4;                 // super-groups of one slice of k
+constexpr int kSlots = kMaxSupers * kSuper / kWaves;   // units per wave: 8
+constexpr int kMaxVec = 16;
+constexpr int kSuperBytes = kBlock * (1 + kSuper);
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) const u32x2 lds_cu32x2;
+
+__device__ __forceinline__ float f16(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+// fp32 -> bf16, round to nearest, ties to even (NaN -> quiet NaN)
+__device__ __forceinline__ uint32_t to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+struct MbLds {
+  uint32_t lut[32];                         // 16 entries of four bf16 +-1
+  uint8_t sblk[kMaxSupers][kBlock];         // scale blocks, as [group][row % 16][row / 16]
+  float red[kWaves][kMaxVec][kTileRows];    // per-wave sums [vector][row]
+};
+
+// Table byte offset (8 bytes per entry) of the 4-bit field at bits [8 q + 3, 8 q + 6] of `rot`.
+// Plain C, not inline assembly: the compiler does not guard inline assembly against the
+// matrix-core hazards (a VALU write to a register an MFMA still reads or will write).
+__device__ __forceinline__ uint32_t field_off(uint32_t rot, int q) {
+  return (rot >> (8 * q)) & 0x78u;
+}
+
+// 4 x 4 transpose across the wave's four 16-lane rows: on return, register t of lane (n, h)
+// holds what register h of lane (n, t) held.
+__device__ __forceinline__ void transpose_rows(u32x4& v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+  const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  v = u32x4{c[0], c[1], d[0], d[1]};
+}
+
+// The A operand of one unit: the four 16-byte steps of vector m = lane mod 16 (zero for lanes
+// of absent vectors), inputs 32 h .. 32 h + 31 of group g.
+__device__ __forceinline__ void load_x(const uint16_t* x, int k, int g, int batch, u32x4 (&a)[4]) {
+  const int lane = threadIdx.x & 63, m = lane & 15, h = lane >> 4;
+  if (m < batch) {
+    const u32x4* p = (const u32x4*)(x + (size_t)m * k + kGroup * g + 32 * h);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a[s] = p[s];
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a[s] = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// One unit: acc[t][i] += scale(row 16 t + n) * (row 16 t + n . x[4 h + i] over the group).
+// Record bits: dword h holds weights 32 h + b at bit (b + 2) mod 32, so the 4-bit field f sits
+// at bits [4 f + 2, 4 f + 5]; rotating right by 31 puts the even fields at bits [8 i + 3,
+// 8 i + 6] (f = 2 i), by 3 the odd ones.
+__device__ __forceinline__ void unit_product(u32x4 rec, const u32x4 (&a)[4], uint32_t lut,
+                                             uint32_t sa, f32x4 (&acc)[4]) {
+  transpose_rows(rec);
+  uint32_t re[4], ro[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    re[t] = __builtin_amdgcn_alignbit(rec[t], rec[t], 31);
+    ro[t] = __builtin_amdgcn_alignbit(rec[t], rec[t], 3);
+  }
+  f32x4 c[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) c[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const u32x2 lo = *(lds_cu32x2*)(uintptr_t)(lut + field_off(re[t], s));
+      const u32x2 hi = *(lds_cu32x2*)(uintptr_t)(lut + field_off(ro[t], s));
+      const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
+      c[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[s]),
+                                                     __builtin_bit_cast(bf16x8, w), c[t], 0, 0, 0);
+    }
+  }
+  const u32x2 sv = *(lds_cu32x2*)(uintptr_t)sa;
+  const float sc[4] = {f16(sv.x & 0xFFFFu), f16(sv.x >> 16), f16(sv.y & 0xFFFFu), f16(sv.y >> 16)};
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[t][i] = fmaf(c[t][i], sc[t], acc[t][i]);
+}
+
+// grid (tiles, splits): workgroup (tile, j) takes super-groups [j spw, (j + 1) spw) of the tile.
+__global__ __launch_bounds__(kThreads) void q1_mb_kernel(
+    const uint8_t* __restrict__ w, const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
+    float* __restrict__ partial, unsigned* __restrict__ counters, int n, int k, int np,
+    int groups, int supers, long long tile_bytes, int batch, int spw, int splits) {
+  __shared__ MbLds L;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n16 = lane & 15, h = lane >> 4;
+  const int tile = blockIdx.x, split = blockIdx.y;
+  const int s0 = split * spw;
+  const int s1 = s0 + spw < supers ? s0 + spw : supers;
+  const int g0 = s0 * kSuper;
+  const int g1 = s1 * kSuper < groups ? s1 * kSuper : groups;
+  const int units = g1 - g0;
+  const uint8_t* tb = w + (size_t)tile * tile_bytes;
+  // ---- the weight table; a scale block per wave; every unit record of the wave ------------
+  if (tid < 32) {
+    const int e = tid >> 1, j0 = 2 * (tid & 1);
+    const uint32_t lo = ((e >> j0) & 1) ? 0x3F80u : 0xBF80u;
+    const uint32_t hi = ((e >> (j0 + 1)) & 1) ? 0x3F80u : 0xBF80u;
+    L.lut[tid] = lo | hi << 16;
+  }
+  const int nsb = s1 - s0;
+  const int sb = wave < nsb ? wave : nsb - 1;   // a repeated block is stored twice, same bytes
+  const u32x4 sreg = *(const u32x4*)(tb + (size_t)(s0 + sb) * kSuperBytes + lane * 16);
+  u32x4 rec[kSlots];
+#pragma unroll
+  for (int j = 0; j < kSlots; ++j) {
+    int u = wave + kWaves * j;
+    u = u < units ? u : 0;   // past the wave's last unit: a spare load of unit 0
+    const int g = g0 + u;
+    rec[j] = __builtin_nontemporal_load(
+        (const u32x4*)(tb + (size_t)(g >> 3) * kSuperBytes + kBlock * (1 + (g & 7)) + lane * 16));
+  }
+  u32x4 a[2][4];
+  load_x(x, k, g0 + (wave < units ? wave : 0), batch, a[0]);
+  {
+    // scale block stored as [group][row % 16][row / 16]: the four scales a lane applies to a
+    // unit (rows n, 16 + n, 32 + n, 48 + n) are one 8-byte read
+    uint16_t* d = (uint16_t*)L.sblk[sb] + (lane & 15) * 4 + (lane >> 4);
+#pragma unroll
+    for (int g = 0; g < kSuper; ++g) d[g * kTileRows] = (uint16_t)(sreg[g >> 1] >> (16 * (g & 1)));
+  }
+  // the LDS writes are complete before the barrier; no wait for the loads in flight
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  // ---- the units ---------------------------------------------------------------------------
+  const uint32_t lut = lds_addr(L.lut);
+  const uint32_t sl = lds_addr(L.sblk) + 8 * n16;
+  f32x4 acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kSlots; ++j) {
+    const int u = wave + kWaves * j;
+    if (u >= units) break;
+    if (j + 1 < kSlots) {   // the next unit's activations are requested before this unit runs
+      const int un = u + kWaves;
+      load_x(x, k, g0 + (un < units ? un : u), batch, a[(j + 1) & 1]);
+    }
+    const int g = g0 + u;
+    const uint32_t sa = sl + (uint32_t)((g >> 3) - s0) * kBlock + (g & 7) * (kTileRows * 2);
+    unit_product(rec[j], a[j & 1], lut, sa, acc);
+  }
+  // ---- the waves' sums in wave order, then the output or the slice's partial sums ----------
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) L.red[wave][4 * h + i][16 * t + n16] = acc[t][i];
+  __syncthreads();
+  const int row = tile * kTileRows + lane;
+  float sum[kMaxVec / kWaves];
+#pragma unroll
+  for (int q = 0; q < kMaxVec / kWaves; ++q) {
+    const int v = wave + kWaves * q;
+    float s = L.red[0][v][lane];
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww) s += L.red[ww][v][lane];
+    sum[q] = s;
+  }
+  if (splits == 1) {
+#pragma unroll
+    for (int q = 0; q < kMaxVec / kWaves; ++q) {
+      const int v = wave + kWaves * q;
+      if (v < batch && row < n) y[(size_t)v * n + row] = (uint16_t)to_bf16(sum[q]);
+    }
+    return;
+  }
+#pragma unroll
+  for (int q = 0; q < kMaxVec / kWaves; ++q) {
+    const int v = wave + kWaves * q;
+    if (v < batch)
+      __hip_atomic_store(&partial[((size_t)split * kMaxVec + v) * np + row], sum[q],
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // every workgroup of the tile has stored its partial sums (agent-scope stores, complete
+  // before the count); the last one adds the slices in slice order and re-arms the counter
+  __shared__ unsigned s_last;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  unsigned* counter = counters + tile;
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == (unsigned)splits - 1u ? 1u : 0u;
+  }
+  __syncthreads();
+  if (!s_last) return;
+#pragma unroll
+  for (int q = 0; q < kMaxVec / kWaves; ++q) {
+    const int v = wave + kWaves * q;
+    if (v >= batch) continue;
+    float s = 0.f;
+    for (int j0 = 0; j0 < splits; j0 += 8) {   // eight slices' loads in flight at a time
+      float t8[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj)
+        t8[jj] = j0 + jj < splits
+                     ? __hip_atomic_load(&partial[((size_t)(j0 + jj) * kMaxVec + v) * np + row],
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                     : 0.f;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj)
+        if (j0 + jj < splits) s += t8[jj];
+    }
+    if (row < n) y[(size_t)v * n + row] = (uint16_t)to_bf16(s);
+  }
+  if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+int cus_of_device() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1)
+      c = 256;
+    cached[dev] = c;
+  }
+  return cached[dev];
+}
+
+}  // namespace
+
+// Batched Q1 GEMV (2 <= batch <= 16) on the matrix cores. Pointers, shapes and aliasing are
+// validated by the caller; d_x is 16-byte aligned.
+lbq_status lbq::q1_gemv_mb(const void* d_w, int n, int k, const uint16_t* d_x, uint16_t* d_y,
+                           int batch, void* stream) {
+  Geometry g;
+  if (!make_geometry(n, k, kQ1GroupBlocks, &g)) return LBQ_E_SHAPE;
+  if (batch < 1 || batch > kMaxVec) return LBQ_E_UNSUPPORTED;
+  // slices of k: enough workgroups to give every compute unit about four, each slice at most
+  // kMaxSupers super-groups deep
+  const int supers = (int)g.supers;
+  const long long want = 4LL * cus_of_device();
+  int splits = (int)((want + g.tiles - 1) / g.tiles);
+  if (splits > supers) splits = supers;
+  if (splits < (supers + kMaxSupers - 1) / kMaxSupers) splits = (supers + kMaxSupers - 1) / kMaxSupers;
+  if (splits < 1) splits = 1;
+  const int spw = (supers + splits - 1) / splits;
+  splits = (supers + spw - 1) / spw;
+  unsigned* counters = nullptr;
+  float* partials = nullptr;
+  if (splits > 1) {
+    if ((size_t)g.tiles * sizeof(unsigned) > kSplitCounterBytes) return LBQ_E_SHAPE;
+    const lbq_status st = splitk_workspace((size_t)splits * kMaxVec * g.np * sizeof(float),
+                                           stream, &counters, &partials);
+    if (st != LBQ_OK) return st;
+  }
+  hipLaunchKernelGGL(q1_mb_kernel, dim3((unsigned)g.tiles, (unsigned)splits), dim3(kThreads), 0,
+                     (hipStream_t)stream, (const uint8_t*)d_w, d_x, d_y, partials, counters, n, k,
+                     (int)g.np, (int)g.groups, supers, (long long)g.tile_bytes, batch, spw, splits);
+  return hipGetLastError() == hipSuccess ? LBQ_OK : LBQ_E_DEVICE;
+}
