@@ -95,5 +95,13 @@ lbq_status stage_decode_q1(const lbq_q1_layer* layers, int n_layers, int hidden,
 // split-K workspace when k is split.
 lbq_status q1_gemv_mb(const void* d_w, int n, int k, const uint16_t* d_x, uint16_t* d_y,
                       int batch, void* stream);
+// Several such GEMVs (at most 8, the same batch) in one launch.
+struct MbJob {
+  const void* w;
+  const uint16_t* x;
+  uint16_t* y;
+  int n, k;
+};
+lbq_status q1_gemv_mb_multi(const MbJob* jobs, int njobs, int batch, void* stream);
 
 }  // namespace lbq

@@ -651,6 +651,71 @@ __global__ __launch_bounds__(256) void rms_kernel(const uint16_t* __restrict__ y
   }
 }
 
+// The same rescale for rows of up to kRmsMaxN elements in 16-byte chunks (n % 8 == 0, 16-byte
+// aligned rows): 1024 threads per row, every chunk of the thread loaded at once and kept in
+// registers, the sum of squares taken over the thread's chunks in order, then within each wave
+// by a fixed butterfly of lane exchanges and over the 16 waves in order (the same bits on every
+// call).
+constexpr int kRmsThreads = 1024;
+constexpr int kRmsRounds = 4;
+constexpr int kRmsMaxN = 8 * kRmsThreads * kRmsRounds;   // 32768
+
+__device__ __forceinline__ float rms_wave_sum(float v) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+__global__ __launch_bounds__(kRmsThreads) void rms_wide_kernel(const uint16_t* __restrict__ y,
+                                                               const uint16_t* __restrict__ y2,
+                                                               uint16_t* __restrict__ out, int n,
+                                                               float eps) {
+  __shared__ float red[kRmsThreads / 64];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int nch = n / 8;
+  const u32x4* yb = (const u32x4*)(y + (size_t)b * n);
+  const u32x4* y2b = y2 ? (const u32x4*)(y2 + (size_t)b * n) : nullptr;
+  u32x4 v[kRmsRounds], v2[kRmsRounds];
+#pragma unroll
+  for (int r = 0; r < kRmsRounds; ++r) {
+    const int c = tid + kRmsThreads * r;
+    v[r] = c < nch ? yb[c] : u32x4{0u, 0u, 0u, 0u};
+    v2[r] = (y2b && c < nch) ? y2b[c] : u32x4{0u, 0u, 0u, 0u};
+  }
+  float h[kRmsRounds][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int r = 0; r < kRmsRounds; ++r)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t wv = v[r][i >> 1], wv2 = v2[r][i >> 1];
+      float hv = (i & 1) ? bf16_hi(wv) : bf16_lo(wv);
+      if (y2b) hv *= (i & 1) ? bf16_hi(wv2) : bf16_lo(wv2);
+      h[r][i] = hv;
+      ss = fmaf(hv, hv, ss);
+    }
+  const float wsum = rms_wave_sum(ss);
+  if ((tid & 63) == 0) red[tid >> 6] = wsum;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < kRmsThreads / 64; ++i) tot += red[i];
+  const float denom = sqrtf(tot / (float)n + eps);
+  u32x4* ob = (u32x4*)(out + (size_t)b * n);
+#pragma unroll
+  for (int r = 0; r < kRmsRounds; ++r) {
+    const int c = tid + kRmsThreads * r;
+    if (c < nch) {
+      u32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[i] = (uint32_t)f32_to_bf16(h[r][2 * i] / denom) |
+               (uint32_t)f32_to_bf16(h[r][2 * i + 1] / denom) << 16;
+      ob[c] = o;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // INT4 weights x int8 activations with integer dot products.
 //
@@ -1186,8 +1251,14 @@ extern "C" lbq_status lbq_rms_rescale_bf16(const uint16_t* d_y, const uint16_t* 
   const size_t bytes = (size_t)batch * n * 2;
   if (overlaps(d_x, bytes, d_y, bytes) || (d_y2 && overlaps(d_x, bytes, d_y2, bytes)))
     return LBQ_E_ALIAS;
-  hipLaunchKernelGGL(rms_kernel, dim3(batch), dim3(256), 0, (hipStream_t)stream, d_y, d_y2, d_x,
-                     n, eps);
+  const bool wide = n % 8 == 0 && n <= kRmsMaxN && (uintptr_t)d_y % 16 == 0 &&
+                    (uintptr_t)d_x % 16 == 0 && (!d_y2 || (uintptr_t)d_y2 % 16 == 0);
+  if (wide)
+    hipLaunchKernelGGL(rms_wide_kernel, dim3(batch), dim3(kRmsThreads), 0, (hipStream_t)stream,
+                       d_y, d_y2, d_x, n, eps);
+  else
+    hipLaunchKernelGGL(rms_kernel, dim3(batch), dim3(256), 0, (hipStream_t)stream, d_y, d_y2, d_x,
+                       n, eps);
   return launch_status();
 }
 
@@ -1242,6 +1313,37 @@ extern "C" lbq_status lbq_decode_step_q1g128(const lbq_q1_layer* layers, int32_t
     return LBQ_E_DEVICE;
   lbq_status st = LBQ_OK;
 #define CHECK(expr) do { st = (expr); if (st != LBQ_OK) return st; } while (0)
+  if (batch >= 2 && batch <= 16 && (uintptr_t)d_act % 16 == 0) {
+    // 2-16 vectors: five launches per layer. The products that read x_l (q, k, v, gate, up) and
+    // o of the layer before (from xo_{l-1}) share one launch of the matrix-core GEMV; then the
+    // rescales of q and of gate * up, down, and the rescale that forms x_{l+1}. Every slot of
+    // the record is 16-byte aligned (the slots are whole multiples of 128 elements).
+    for (int l = 0; l < n_layers; ++l) {
+      const lbq_q1_layer& L = layers[l];
+      const uint16_t* x = at(l, LBQ_ACT_X);
+      MbJob jobs[6] = {{L.q, x, at(l, LBQ_ACT_Q), hidden, hidden},
+                       {L.k, x, at(l, LBQ_ACT_K), kv, hidden},
+                       {L.v, x, at(l, LBQ_ACT_V), kv, hidden},
+                       {L.gate, x, at(l, LBQ_ACT_GATE), ffn, hidden},
+                       {L.up, x, at(l, LBQ_ACT_UP), ffn, hidden},
+                       {nullptr, nullptr, nullptr, 0, 0}};
+      int nj = 5;
+      if (l > 0) jobs[nj++] = {layers[l - 1].o, at(l - 1, LBQ_ACT_XO), at(l - 1, LBQ_ACT_O), hidden, hidden};
+      CHECK(q1_gemv_mb_multi(jobs, nj, batch, s));
+      CHECK(lbq_rms_rescale_bf16(at(l, LBQ_ACT_Q), nullptr, at(l, LBQ_ACT_XO), hidden, batch, eps, s));
+      CHECK(lbq_rms_rescale_bf16(at(l, LBQ_ACT_GATE), at(l, LBQ_ACT_UP), at(l, LBQ_ACT_XD), ffn,
+                                 batch, eps, s));
+      CHECK(q1_gemv_mb(L.down, hidden, ffn, at(l, LBQ_ACT_XD), at(l, LBQ_ACT_DOWN), batch, s));
+      uint16_t* xn = (l + 1 < n_layers) ? at(l + 1, LBQ_ACT_X)
+                                        : d_act + lbq_decode_act_offset(n_layers, LBQ_ACT_NSLOTS,
+                                                                        n_layers, hidden, kv, ffn,
+                                                                        batch);
+      CHECK(lbq_rms_rescale_bf16(at(l, LBQ_ACT_DOWN), nullptr, xn, hidden, batch, eps, s));
+    }
+    const int l = n_layers - 1;
+    CHECK(q1_gemv_mb(layers[l].o, hidden, hidden, at(l, LBQ_ACT_XO), at(l, LBQ_ACT_O), batch, s));
+    return LBQ_OK;
+  }
   for (int l = 0; l < n_layers; ++l) {
     const lbq_q1_layer& L = layers[l];
     const uint16_t* x = at(l, LBQ_ACT_X);

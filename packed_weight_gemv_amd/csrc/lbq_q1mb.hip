@@ -23,6 +23,8 @@
 //    workspace, and the last workgroup of a tile adds them in slice order (deterministic).
 #include <hip/hip_runtime.h>
 
+#include <string.h>
+
 #include "lbq_internal.h"
 
 using namespace lbq;
@@ -128,16 +130,58 @@ __device__ __forceinline__ void unit_product(u32x4 rec, const u32x4 (&a)[4], uin
     for (int i = 0; i < 4; ++i) acc[t][i] = fmaf(c[t][i], sc[t], acc[t][i]);
 }
 
-// grid (tiles, splits): workgroup (tile, j) takes super-groups [j spw, (j + 1) spw) of the tile.
-__global__ __launch_bounds__(kThreads) void q1_mb_kernel(
-    const uint8_t* __restrict__ w, const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
-    float* __restrict__ partial, unsigned* __restrict__ counters, int n, int k, int np,
-    int groups, int supers, long long tile_bytes, int batch, int spw, int splits) {
+// One matrix of a launch: workgroup wg0 + tile * splits + j takes super-groups
+// [j spw, (j + 1) spw) of the tile.
+struct MbMat {
+  const uint8_t* w;
+  const uint16_t* x;
+  uint16_t* y;
+  float* partial;        // [splits][16][np] (splits > 1)
+  unsigned* counters;    // [tiles] (splits > 1)
+  long long tile_bytes;
+  int n, k, np, groups, supers, spw, splits, wg0;
+};
+constexpr int kMaxMats = 8;
+struct MbArgs {
+  MbMat m[kMaxMats];
+  int nmats, batch;
+};
+
+// Matrix i of the launch (i uniform), read field by field with constant indices (a dynamic
+// index into the argument block would be lowered through scratch memory).
+__device__ __forceinline__ MbMat pick_mat(const MbArgs& A, int i) {
+  switch (i) {
+    case 0: return A.m[0];
+    case 1: return A.m[1];
+    case 2: return A.m[2];
+    case 3: return A.m[3];
+    case 4: return A.m[4];
+    case 5: return A.m[5];
+    case 6: return A.m[6];
+    default: return A.m[7];
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void q1_mb_kernel(MbArgs A) {
   __shared__ MbLds L;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, h = lane >> 4;
-  const int tile = blockIdx.x, split = blockIdx.y;
+  int mi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxMats; ++i)
+    if (i < A.nmats && (int)blockIdx.x >= A.m[i].wg0) mi = i;
+  const MbMat M = pick_mat(A, mi);
+  const uint8_t* __restrict__ w = M.w;
+  const uint16_t* __restrict__ x = M.x;
+  uint16_t* __restrict__ y = M.y;
+  float* __restrict__ partial = M.partial;
+  unsigned* __restrict__ counters = M.counters;
+  const int n = M.n, k = M.k, np = M.np, groups = M.groups, supers = M.supers;
+  const int spw = M.spw, splits = M.splits, batch = A.batch;
+  const long long tile_bytes = M.tile_bytes;
+  const int local = (int)blockIdx.x - M.wg0;
+  const int tile = local / splits, split = local - tile * splits;
   const int s0 = split * spw;
   const int s1 = s0 + spw < supers ? s0 + spw : supers;
   const int g0 = s0 * kSuper;
@@ -274,33 +318,69 @@ int cus_of_device() {
 
 }  // namespace
 
-// Batched Q1 GEMV (2 <= batch <= 16) on the matrix cores. Pointers, shapes and aliasing are
-// validated by the caller; d_x is 16-byte aligned.
+// Batched Q1 GEMVs (2 <= batch <= 16 vectors) on the matrix cores, several matrices in one
+// launch. Pointers, shapes and aliasing are validated by the caller; every x is 16-byte aligned.
+lbq_status lbq::q1_gemv_mb_multi(const MbJob* jobs, int njobs, int batch, void* stream) {
+  if (njobs < 1 || njobs > kMaxMats || batch < 1 || batch > kMaxVec) return LBQ_E_UNSUPPORTED;
+  MbArgs A;
+  memset(&A, 0, sizeof(A));
+  A.nmats = njobs;
+  A.batch = batch;
+  size_t part_floats = 0, ncounters = 0;
+  long long wgs = 0;
+  const long long want = 4LL * cus_of_device();
+  for (int i = 0; i < njobs; ++i) {
+    Geometry g;
+    if (!make_geometry(jobs[i].n, jobs[i].k, kQ1GroupBlocks, &g)) return LBQ_E_SHAPE;
+    // slices of k: enough workgroups to give every compute unit about four, each slice at
+    // most kMaxSupers super-groups deep
+    const int supers = (int)g.supers;
+    int splits = (int)((want + g.tiles - 1) / g.tiles);
+    if (splits > supers) splits = supers;
+    if (splits < (supers + kMaxSupers - 1) / kMaxSupers) splits = (supers + kMaxSupers - 1) / kMaxSupers;
+    if (splits < 1) splits = 1;
+    const int spw = (supers + splits - 1) / splits;
+    splits = (supers + spw - 1) / spw;
+    MbMat& M = A.m[i];
+    M.w = (const uint8_t*)jobs[i].w;
+    M.x = jobs[i].x;
+    M.y = jobs[i].y;
+    M.tile_bytes = g.tile_bytes;
+    M.n = jobs[i].n;
+    M.k = jobs[i].k;
+    M.np = (int)g.np;
+    M.groups = (int)g.groups;
+    M.supers = supers;
+    M.spw = spw;
+    M.splits = splits;
+    M.wg0 = (int)wgs;
+    wgs += g.tiles * splits;
+    if (splits > 1) {
+      M.partial = (float*)(uintptr_t)part_floats;   // offsets until the workspace is known
+      M.counters = (unsigned*)(uintptr_t)ncounters;
+      part_floats += (size_t)splits * kMaxVec * g.np;
+      ncounters += (size_t)g.tiles;
+    }
+  }
+  if (wgs > 0x7FFFFFFFLL) return LBQ_E_SHAPE;
+  if (part_floats > 0) {
+    if (ncounters * sizeof(unsigned) > kSplitCounterBytes) return LBQ_E_SHAPE;
+    unsigned* counters = nullptr;
+    float* partials = nullptr;
+    const lbq_status st = splitk_workspace(part_floats * sizeof(float), stream, &counters, &partials);
+    if (st != LBQ_OK) return st;
+    for (int i = 0; i < njobs; ++i)
+      if (A.m[i].splits > 1) {
+        A.m[i].partial = partials + (uintptr_t)A.m[i].partial;
+        A.m[i].counters = counters + (uintptr_t)A.m[i].counters;
+      }
+  }
+  hipLaunchKernelGGL(q1_mb_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, (hipStream_t)stream, A);
+  return hipGetLastError() == hipSuccess ? LBQ_OK : LBQ_E_DEVICE;
+}
+
 lbq_status lbq::q1_gemv_mb(const void* d_w, int n, int k, const uint16_t* d_x, uint16_t* d_y,
                            int batch, void* stream) {
-  Geometry g;
-  if (!make_geometry(n, k, kQ1GroupBlocks, &g)) return LBQ_E_SHAPE;
-  if (batch < 1 || batch > kMaxVec) return LBQ_E_UNSUPPORTED;
-  // slices of k: enough workgroups to give every compute unit about four, each slice at most
-  // kMaxSupers super-groups deep
-  const int supers = (int)g.supers;
-  const long long want = 4LL * cus_of_device();
-  int splits = (int)((want + g.tiles - 1) / g.tiles);
-  if (splits > supers) splits = supers;
-  if (splits < (supers + kMaxSupers - 1) / kMaxSupers) splits = (supers + kMaxSupers - 1) / kMaxSupers;
-  if (splits < 1) splits = 1;
-  const int spw = (supers + splits - 1) / splits;
-  splits = (supers + spw - 1) / spw;
-  unsigned* counters = nullptr;
-  float* partials = nullptr;
-  if (splits > 1) {
-    if ((size_t)g.tiles * sizeof(unsigned) > kSplitCounterBytes) return LBQ_E_SHAPE;
-    const lbq_status st = splitk_workspace((size_t)splits * kMaxVec * g.np * sizeof(float),
-                                           stream, &counters, &partials);
-    if (st != LBQ_OK) return st;
-  }
-  hipLaunchKernelGGL(q1_mb_kernel, dim3((unsigned)g.tiles, (unsigned)splits), dim3(kThreads), 0,
-                     (hipStream_t)stream, (const uint8_t*)d_w, d_x, d_y, partials, counters, n, k,
-                     (int)g.np, (int)g.groups, supers, (long long)g.tile_bytes, batch, spw, splits);
-  return hipGetLastError() == hipSuccess ? LBQ_OK : LBQ_E_DEVICE;
+  const MbJob job{d_w, d_x, d_y, n, k};
+  return q1_gemv_mb_multi(&job, 1, batch, stream);
 }
