@@ -666,11 +666,26 @@ __device__ __forceinline__ float rms_wave_sum(float v) {
   return v;
 }
 
-__global__ __launch_bounds__(kRmsThreads) void rms_wide_kernel(const uint16_t* __restrict__ y,
-                                                               const uint16_t* __restrict__ y2,
-                                                               uint16_t* __restrict__ out, int n,
-                                                               float eps) {
+// Up to two independent rescales per launch (blockIdx.y selects one).
+struct RmsJob {
+  const uint16_t* y;
+  const uint16_t* y2;
+  uint16_t* out;
+  int n;
+};
+struct RmsJobs {
+  RmsJob j[2];
+  float eps;
+};
+
+__global__ __launch_bounds__(kRmsThreads) void rms_wide_kernel(RmsJobs J) {
   __shared__ float red[kRmsThreads / 64];
+  const RmsJob job = blockIdx.y == 0 ? J.j[0] : J.j[1];
+  const uint16_t* __restrict__ y = job.y;
+  const uint16_t* __restrict__ y2 = job.y2;
+  uint16_t* __restrict__ out = job.out;
+  const int n = job.n;
+  const float eps = J.eps;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int nch = n / 8;
   const u32x4* yb = (const u32x4*)(y + (size_t)b * n);
@@ -1253,10 +1268,12 @@ extern "C" lbq_status lbq_rms_rescale_bf16(const uint16_t* d_y, const uint16_t* 
     return LBQ_E_ALIAS;
   const bool wide = n % 8 == 0 && n <= kRmsMaxN && (uintptr_t)d_y % 16 == 0 &&
                     (uintptr_t)d_x % 16 == 0 && (!d_y2 || (uintptr_t)d_y2 % 16 == 0);
-  if (wide)
-    hipLaunchKernelGGL(rms_wide_kernel, dim3(batch), dim3(kRmsThreads), 0, (hipStream_t)stream,
-                       d_y, d_y2, d_x, n, eps);
-  else
+  if (wide) {
+    RmsJobs J;
+    J.j[0] = J.j[1] = RmsJob{d_y, d_y2, d_x, n};
+    J.eps = eps;
+    hipLaunchKernelGGL(rms_wide_kernel, dim3(batch, 1), dim3(kRmsThreads), 0, (hipStream_t)stream, J);
+  } else
     hipLaunchKernelGGL(rms_kernel, dim3(batch), dim3(256), 0, (hipStream_t)stream, d_y, d_y2, d_x,
                        n, eps);
   return launch_status();
@@ -1313,10 +1330,11 @@ extern "C" lbq_status lbq_decode_step_q1g128(const lbq_q1_layer* layers, int32_t
     return LBQ_E_DEVICE;
   lbq_status st = LBQ_OK;
 #define CHECK(expr) do { st = (expr); if (st != LBQ_OK) return st; } while (0)
-  if (batch >= 2 && batch <= 16 && (uintptr_t)d_act % 16 == 0) {
-    // 2-16 vectors: five launches per layer. The products that read x_l (q, k, v, gate, up) and
+  if (batch >= 2 && batch <= 16 && (uintptr_t)d_act % 16 == 0 && hidden <= kRmsMaxN &&
+      ffn <= kRmsMaxN) {
+    // 2-16 vectors: four launches per layer. The products that read x_l (q, k, v, gate, up) and
     // o of the layer before (from xo_{l-1}) share one launch of the matrix-core GEMV; then the
-    // rescales of q and of gate * up, down, and the rescale that forms x_{l+1}. Every slot of
+    // rescales of q and of gate * up (one launch), down, and the rescale that forms x_{l+1}. Every slot of
     // the record is 16-byte aligned (the slots are whole multiples of 128 elements).
     for (int l = 0; l < n_layers; ++l) {
       const lbq_q1_layer& L = layers[l];
@@ -1330,9 +1348,14 @@ extern "C" lbq_status lbq_decode_step_q1g128(const lbq_q1_layer* layers, int32_t
       int nj = 5;
       if (l > 0) jobs[nj++] = {layers[l - 1].o, at(l - 1, LBQ_ACT_XO), at(l - 1, LBQ_ACT_O), hidden, hidden};
       CHECK(q1_gemv_mb_multi(jobs, nj, batch, s));
-      CHECK(lbq_rms_rescale_bf16(at(l, LBQ_ACT_Q), nullptr, at(l, LBQ_ACT_XO), hidden, batch, eps, s));
-      CHECK(lbq_rms_rescale_bf16(at(l, LBQ_ACT_GATE), at(l, LBQ_ACT_UP), at(l, LBQ_ACT_XD), ffn,
-                                 batch, eps, s));
+      {   // xo = rms(q) and xd = rms(gate * up) in one launch
+        RmsJobs J;
+        J.j[0] = RmsJob{at(l, LBQ_ACT_Q), nullptr, at(l, LBQ_ACT_XO), hidden};
+        J.j[1] = RmsJob{at(l, LBQ_ACT_GATE), at(l, LBQ_ACT_UP), at(l, LBQ_ACT_XD), ffn};
+        J.eps = eps;
+        hipLaunchKernelGGL(rms_wide_kernel, dim3(batch, 2), dim3(kRmsThreads), 0, s, J);
+        CHECK(launch_status());
+      }
       CHECK(q1_gemv_mb(L.down, hidden, ffn, at(l, LBQ_ACT_XD), at(l, LBQ_ACT_DOWN), batch, s));
       uint16_t* xn = (l + 1 < n_layers) ? at(l + 1, LBQ_ACT_X)
                                         : d_act + lbq_decode_act_offset(n_layers, LBQ_ACT_NSLOTS,

@@ -328,12 +328,12 @@ lbq_status lbq::q1_gemv_mb_multi(const MbJob* jobs, int njobs, int batch, void* 
   A.batch = batch;
   size_t part_floats = 0, ncounters = 0;
   long long wgs = 0;
-  const long long want = 4LL * cus_of_device();
+  const long long want = 2LL * cus_of_device();
   for (int i = 0; i < njobs; ++i) {
     Geometry g;
     if (!make_geometry(jobs[i].n, jobs[i].k, kQ1GroupBlocks, &g)) return LBQ_E_SHAPE;
-    // slices of k: enough workgroups to give every compute unit about four, each slice at
-    // most kMaxSupers super-groups deep
+    // slices of k: enough workgroups to give every compute unit about two, each slice at most
+    // kMaxSupers super-groups deep (more, shorter slices only add split-K round trips)
     const int supers = (int)g.supers;
     int splits = (int)((want + g.tiles - 1) / g.tiles);
     if (splits > supers) splits = supers;
