@@ -319,8 +319,8 @@ def main() -> int:
         kern_avg_ms, kern_bytes = step_kernel_ms, bytes_per_step
     else:
         # host-driven step: every Q1 GEMV launch of a step bracketed by events
-        kern_name = ("per-projection Q1 launches (the matrix-core product gemm_kernel for "
-                     "batch >= 2)")
+        kern_name = ("q1_mb_kernel (the batched matrix-core GEMV, each of a step's Q1 "
+                     "projections launched and timed on its own)")
         gemv_ms, gemv_bytes, launches = 0.0, 0, 0
         src = {"q": "x", "k": "x", "v": "x", "gate": "x", "up": "x", "o": "xo", "down": "xd"}
         for _ in range(max(1, args.kernel_steps)):
@@ -436,7 +436,7 @@ def main() -> int:
                 f"({chain['oracle_seconds']} s)")
 
     out = {
-        "metric": "packed-weight HBM GB/s (% of peak) + decode tok/s-equiv, batch 1, 27B-shape",
+        "metric": f"packed-weight HBM GB/s (% of peak) + decode tok/s-equiv, batch {B}, 27B-shape",
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
