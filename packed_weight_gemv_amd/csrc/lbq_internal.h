@@ -103,5 +103,8 @@ struct MbJob {
   int n, k;
 };
 lbq_status q1_gemv_mb_multi(const MbJob* jobs, int njobs, int batch, void* stream);
+// INT4 g128 GEMV for 2 <= batch <= 16 vectors on the matrix cores (same rules).
+lbq_status i4_gemv_mb(const void* d_w, int n, int k, const uint16_t* d_x, uint16_t* d_y,
+                      int batch, void* stream);
 
 }  // namespace lbq

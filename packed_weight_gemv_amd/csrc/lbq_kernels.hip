@@ -1083,10 +1083,11 @@ static lbq_status gemv_common(Fmt fmt, const void* d_w, int32_t n, int32_t k,
     return LBQ_E_ALIAS;
   hipStream_t s = (hipStream_t)stream;
   // two or more vectors: the matrix cores (they need 16-byte aligned rows of x; other
-  // alignments take the per-row lookup kernels below). Q1 with at most 16 vectors runs all
-  // vectors through one product per weight group; more vectors take the GEMM.
-  if (fmt == Fmt::Q1 && batch >= 2 && batch <= 16 && (uintptr_t)d_x % 16 == 0)
-    return q1_gemv_mb(d_w, n, k, d_x, d_y, batch, stream);
+  // alignments take the per-row kernels below). At most 16 vectors run through one product per
+  // weight group; more vectors take the GEMM.
+  if (batch >= 2 && batch <= 16 && (uintptr_t)d_x % 16 == 0)
+    return fmt == Fmt::Q1 ? q1_gemv_mb(d_w, n, k, d_x, d_y, batch, stream)
+                          : i4_gemv_mb(d_w, n, k, d_x, d_y, batch, stream);
   if (batch >= 2 && (uintptr_t)d_x % 16 == 0)
     return fmt == Fmt::Q1 ? lbq_gemm_q1g128(d_w, n, k, d_x, d_y, batch, stream)
                           : lbq_gemm_i4g128(d_w, n, k, d_x, d_y, batch, stream);

@@ -1,5 +1,7 @@
-// lbq_q1mb.hip - Q1_0_g128 GEMV for 2 to 16 activation vectors on the gfx950 matrix cores
-// (the 1-bit format of the Bonsai-27B-gguf digest, "technical architecture highlights").
+// lbq_q1mb.hip - packed-weight GEMV for 2 to 16 activation vectors on the gfx950 matrix cores:
+// Q1_0_g128 (the 1-bit format of the Bonsai-27B-gguf digest, "technical architecture
+// highlights") and INT4 g128 (the Acorn page, "int4 quantization quality: group quantization
+// (g=128)").
 //
 // A workgroup of four waves takes one 64-row tile over a slice of k (up to four super-groups of
 // eight 128-weight groups). A unit is one group of the tile: four sub-tiles of 16 rows, each
@@ -16,9 +18,15 @@
 //  * Activations: the A operand of step s for lane (m, h) is x[m][128 g + 32 h + 8 s .. + 7],
 //    16 contiguous bytes read straight from memory (the lanes of absent vectors read nothing);
 //    every workgroup of the same k slice reads the same bytes, which stay in the L2.
-//  * Products of +-1 and bf16 are exact and the matrix cores sum them in fp32; each group's sum
-//    is weighted by its fp16 scale and accumulated in fp32 (lane (n, h) holds vectors
-//    4 h .. 4 h + 3 of row 16 t + n in accumulator t).
+//  * INT4: lane (n, h) loads, for each sub-tile t, the 16-byte piece h of row 16 t + n (weights
+//    32 h .. 32 h + 31 of the group, one wave load = four contiguous 256-byte runs), so no
+//    transpose is needed; dword s of the piece (weights 32 h + 8 s .. + 7) unpacks in registers
+//    to the exact bf16 values 1 + c/16 of the offset-binary codes c = q + 8. Then
+//    sum q x = 16 sum (1 + c/16) x - 24 sum x, and sum x over the group comes from one more
+//    product per step against a B operand of bf16 ones.
+//  * Products of +-1 (Q1) or 1 + c/16 (INT4) and bf16 are exact and the matrix cores sum them in
+//    fp32; each group's sum is weighted by its fp16 scale and accumulated in fp32 (lane (n, h)
+//    holds vectors 4 h .. 4 h + 3 of row 16 t + n in accumulator t).
 //  * The four waves' sums are added in wave order; slices of k go through the split-K
 //    workspace, and the last workgroup of a tile adds them in slice order (deterministic).
 #include <hip/hip_runtime.h>
@@ -36,7 +44,8 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxSupers = 4;                 // super-groups of one slice of k
 constexpr int kSlots = kMaxSupers * kSuper / kWaves;   // units per wave: 8
 constexpr int kMaxVec = 16;
-constexpr int kSuperBytes = kBlock * (1 + kSuper);
+constexpr int kQ1SuperBytes = kBlock * (1 + kSuper * kQ1GroupBlocks);
+constexpr int kI4SuperBytes = kBlock * (1 + kSuper * kI4GroupBlocks);
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -81,6 +90,18 @@ __device__ __forceinline__ void transpose_rows(u32x4& v) {
   v = u32x4{c[0], c[1], d[0], d[1]};
 }
 
+// INT4: the eight offset-binary codes of one dword (element 2 p at bits [4 p, 4 p + 3], element
+// 2 p + 1 at bits [16 + 4 p, 16 + 4 p + 3]) as the bf16 values 1 + c/16, in element order: each
+// code goes to mantissa bits 3-6 of a bf16 one (a bit-field insert).
+__device__ __forceinline__ uint32_t bfi(uint32_t a, uint32_t m, uint32_t c) {
+  return (a & m) | (c & ~m);
+}
+__device__ __forceinline__ u32x4 i4_unpack(uint32_t d) {
+  constexpr uint32_t ones = 0x3F803F80u;
+  return u32x4{bfi(d << 3, 0x00780078u, ones), bfi(d >> 1, 0x00780078u, ones),
+               bfi(d >> 5, 0x00780078u, ones), bfi(d >> 9, 0x00780078u, ones)};
+}
+
 // The A operand of one unit: the four 16-byte steps of vector m = lane mod 16 (zero for lanes
 // of absent vectors), inputs 32 h .. 32 h + 31 of group g.
 __device__ __forceinline__ void load_x(const uint16_t* x, int k, int g, int batch, u32x4 (&a)[4]) {
@@ -99,8 +120,8 @@ __device__ __forceinline__ void load_x(const uint16_t* x, int k, int g, int batc
 // Record bits: dword h holds weights 32 h + b at bit (b + 2) mod 32, so the 4-bit field f sits
 // at bits [4 f + 2, 4 f + 5]; rotating right by 31 puts the even fields at bits [8 i + 3,
 // 8 i + 6] (f = 2 i), by 3 the odd ones.
-__device__ __forceinline__ void unit_product(u32x4 rec, const u32x4 (&a)[4], uint32_t lut,
-                                             uint32_t sa, f32x4 (&acc)[4]) {
+__device__ __forceinline__ void q1_unit_product(u32x4 rec, const u32x4 (&a)[4], uint32_t lut,
+                                                uint32_t sa, f32x4 (&acc)[4]) {
   transpose_rows(rec);
   uint32_t re[4], ro[4];
 #pragma unroll
@@ -128,6 +149,32 @@ __device__ __forceinline__ void unit_product(u32x4 rec, const u32x4 (&a)[4], uin
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[t][i] = fmaf(c[t][i], sc[t], acc[t][i]);
+}
+
+// INT4 unit: rec[t] = piece h of row 16 t + n. acc[t][i] += scale(row 16 t + n) *
+// (16 sum (1 + c/16) x[4 h + i] - 24 sum x[4 h + i]) over the group.
+__device__ __forceinline__ void i4_unit_product(const u32x4 (&rec)[4], const u32x4 (&a)[4],
+                                                uint32_t sa, f32x4 (&acc)[4]) {
+  f32x4 c[4], cs = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) c[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const bf16x8 as = __builtin_bit_cast(bf16x8, a[s]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      c[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as, __builtin_bit_cast(bf16x8, i4_unpack(rec[t][s])),
+                                                     c[t], 0, 0, 0);
+    cs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as, __builtin_bit_cast(bf16x8, ones), cs, 0, 0, 0);
+  }
+  const u32x2 sv = *(lds_cu32x2*)(uintptr_t)sa;
+  const float sc[4] = {f16(sv.x & 0xFFFFu), f16(sv.x >> 16), f16(sv.y & 0xFFFFu), f16(sv.y >> 16)};
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc[t][i] = fmaf(fmaf(16.f, c[t][i], -24.f * cs[i]), sc[t], acc[t][i]);
 }
 
 // One matrix of a launch: workgroup wg0 + tile * splits + j takes super-groups
@@ -162,7 +209,14 @@ __device__ __forceinline__ MbMat pick_mat(const MbArgs& A, int i) {
   }
 }
 
-__global__ __launch_bounds__(kThreads) void q1_mb_kernel(MbArgs A) {
+// FMT 0: Q1_0_g128, 1: INT4 g128.
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void mb_kernel(MbArgs A) {
+  constexpr int kSuperBytes = FMT == 0 ? kQ1SuperBytes : kI4SuperBytes;
+  constexpr int kGroupBytes = FMT == 0 ? kQ1GroupBlocks * kBlock : kI4GroupBlocks * kBlock;
+  // unit records requested ahead: all of the wave's for Q1 (16 bytes per lane each), two for
+  // INT4 (64 bytes per lane each)
+  constexpr int kAhead = FMT == 0 ? kSlots : 2;
   __shared__ MbLds L;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -188,8 +242,8 @@ __global__ __launch_bounds__(kThreads) void q1_mb_kernel(MbArgs A) {
   const int g1 = s1 * kSuper < groups ? s1 * kSuper : groups;
   const int units = g1 - g0;
   const uint8_t* tb = w + (size_t)tile * tile_bytes;
-  // ---- the weight table; a scale block per wave; every unit record of the wave ------------
-  if (tid < 32) {
+  // ---- the weight table; a scale block per wave; the first unit records of the wave --------
+  if (FMT == 0 && tid < 32) {
     const int e = tid >> 1, j0 = 2 * (tid & 1);
     const uint32_t lo = ((e >> j0) & 1) ? 0x3F80u : 0xBF80u;
     const uint32_t hi = ((e >> (j0 + 1)) & 1) ? 0x3F80u : 0xBF80u;
@@ -198,15 +252,24 @@ __global__ __launch_bounds__(kThreads) void q1_mb_kernel(MbArgs A) {
   const int nsb = s1 - s0;
   const int sb = wave < nsb ? wave : nsb - 1;   // a repeated block is stored twice, same bytes
   const u32x4 sreg = *(const u32x4*)(tb + (size_t)(s0 + sb) * kSuperBytes + lane * 16);
-  u32x4 rec[kSlots];
-#pragma unroll
-  for (int j = 0; j < kSlots; ++j) {
+  // unit j's records: Q1 rec[j][0] = row `lane`; INT4 rec[j][t] = piece h of row 16 t + n
+  u32x4 rec[kSlots][FMT == 0 ? 1 : 4];
+  auto issue = [&](int j) {
     int u = wave + kWaves * j;
     u = u < units ? u : 0;   // past the wave's last unit: a spare load of unit 0
     const int g = g0 + u;
-    rec[j] = __builtin_nontemporal_load(
-        (const u32x4*)(tb + (size_t)(g >> 3) * kSuperBytes + kBlock * (1 + (g & 7)) + lane * 16));
-  }
+    const uint8_t* gb = tb + (size_t)(g >> 3) * kSuperBytes + kBlock + (size_t)(g & 7) * kGroupBytes;
+    if constexpr (FMT == 0) {
+      rec[j][0] = __builtin_nontemporal_load((const u32x4*)(gb + lane * 16));
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        rec[j][t] = __builtin_nontemporal_load(
+            (const u32x4*)(gb + (size_t)h * kBlock + (16 * t + n16) * 16));
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < kAhead; ++j) issue(j);
   u32x4 a[2][4];
   load_x(x, k, g0 + (wave < units ? wave : 0), batch, a[0]);
   {
@@ -230,13 +293,15 @@ __global__ __launch_bounds__(kThreads) void q1_mb_kernel(MbArgs A) {
   for (int j = 0; j < kSlots; ++j) {
     const int u = wave + kWaves * j;
     if (u >= units) break;
+    if (j + kAhead < kSlots) issue(j + kAhead);
     if (j + 1 < kSlots) {   // the next unit's activations are requested before this unit runs
       const int un = u + kWaves;
       load_x(x, k, g0 + (un < units ? un : u), batch, a[(j + 1) & 1]);
     }
     const int g = g0 + u;
     const uint32_t sa = sl + (uint32_t)((g >> 3) - s0) * kBlock + (g & 7) * (kTileRows * 2);
-    unit_product(rec[j], a[j & 1], lut, sa, acc);
+    if constexpr (FMT == 0) q1_unit_product(rec[j][0], a[j & 1], lut, sa, acc);
+    else i4_unit_product(rec[j], a[j & 1], sa, acc);
   }
   // ---- the waves' sums in wave order, then the output or the slice's partial sums ----------
 #pragma unroll
@@ -318,9 +383,11 @@ int cus_of_device() {
 
 }  // namespace
 
-// Batched Q1 GEMVs (2 <= batch <= 16 vectors) on the matrix cores, several matrices in one
+// Batched GEMVs (2 <= batch <= 16 vectors) on the matrix cores, several matrices in one
 // launch. Pointers, shapes and aliasing are validated by the caller; every x is 16-byte aligned.
-lbq_status lbq::q1_gemv_mb_multi(const MbJob* jobs, int njobs, int batch, void* stream) {
+namespace {
+template <int FMT>
+lbq_status mb_launch(const MbJob* jobs, int njobs, int batch, void* stream) {
   if (njobs < 1 || njobs > kMaxMats || batch < 1 || batch > kMaxVec) return LBQ_E_UNSUPPORTED;
   MbArgs A;
   memset(&A, 0, sizeof(A));
@@ -331,7 +398,8 @@ lbq_status lbq::q1_gemv_mb_multi(const MbJob* jobs, int njobs, int batch, void* 
   const long long want = 2LL * cus_of_device();
   for (int i = 0; i < njobs; ++i) {
     Geometry g;
-    if (!make_geometry(jobs[i].n, jobs[i].k, kQ1GroupBlocks, &g)) return LBQ_E_SHAPE;
+    if (!make_geometry(jobs[i].n, jobs[i].k, FMT == 0 ? kQ1GroupBlocks : kI4GroupBlocks, &g))
+      return LBQ_E_SHAPE;
     // slices of k: enough workgroups to give every compute unit about two, each slice at most
     // kMaxSupers super-groups deep (more, shorter slices only add split-K round trips)
     const int supers = (int)g.supers;
@@ -375,8 +443,19 @@ lbq_status lbq::q1_gemv_mb_multi(const MbJob* jobs, int njobs, int batch, void* 
         A.m[i].counters = counters + (uintptr_t)A.m[i].counters;
       }
   }
-  hipLaunchKernelGGL(q1_mb_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, (hipStream_t)stream, A);
+  hipLaunchKernelGGL(mb_kernel<FMT>, dim3((unsigned)wgs), dim3(kThreads), 0, (hipStream_t)stream, A);
   return hipGetLastError() == hipSuccess ? LBQ_OK : LBQ_E_DEVICE;
+}
+}  // namespace
+
+lbq_status lbq::q1_gemv_mb_multi(const MbJob* jobs, int njobs, int batch, void* stream) {
+  return mb_launch<0>(jobs, njobs, batch, stream);
+}
+
+lbq_status lbq::i4_gemv_mb(const void* d_w, int n, int k, const uint16_t* d_x, uint16_t* d_y,
+                           int batch, void* stream) {
+  const MbJob job{d_w, d_x, d_y, n, k};
+  return mb_launch<1>(&job, 1, batch, stream);
 }
 
 lbq_status lbq::q1_gemv_mb(const void* d_w, int n, int k, const uint16_t* d_x, uint16_t* d_y,

@@ -39,6 +39,18 @@ def test_parity_batches(lbq, batch):
     check_within(y, ref, l1, f"i4 batch {batch}")
 
 
+@pytest.mark.parametrize("n,k,batch", [(130, 1024, 5), (64, 128, 3), (333, 9216, 16),
+                                         (65, 3200, 7), (1, 384, 2)])
+def test_parity_matrix_core_batches_ragged(lbq, n, k, batch):
+    """2-16 vectors run on the matrix cores: one k slice (k <= 1024), many slices, a last
+    super-group with one group, rows past a tile boundary, a single row."""
+    m = synth.i4_matrix(n, k, workload=33, matrix=n + k)
+    x = synth.activations(batch, k, workload=33, matrix=n + k, extra=batch)
+    y = _run(lbq, m, x)
+    ref, l1 = oracle.gemv_i4g128(m.nib, m.scales, x)
+    check_within(y, ref, l1, f"i4 {n}x{k} B={batch}")
+
+
 @pytest.mark.parametrize("name,n,k", [(nm, n, k) for nm, n, k in synth.I4_SHAPES
                                       if nm in ("q", "k", "gate", "down")])
 @pytest.mark.parametrize("batch", [1, 8])
