@@ -181,9 +181,11 @@ lbq_status lbq_unpack_q1g128(const void* src, int32_t n, int32_t k, uint8_t* sig
  *   d_w : device layout (lbq_pack_q1g128), 16-byte aligned
  *   d_x : bf16 [batch][k], 4-byte aligned     d_y : bf16 [batch][n], 4-byte aligned
  * Requires k % 128 == 0, 1 <= n, 0 <= batch <= LBQ_MAX_BATCH (0 = no-op). d_y must not
- * overlap d_x or the weights. With batch >= 2 and d_x 16-byte aligned the call is the
- * matrix-core product lbq_gemm_q1g128 (same result rule; within each group the matrix cores sum
- * the exact products in their own order). Large-k calls split the reduction over workgroups
+ * overlap d_x or the weights. With d_x 16-byte aligned, 2 to 16 vectors (and one vector when
+ * the matrix has fewer 64-row tiles than the device has compute units) run on the matrix cores,
+ * all vectors through one product per weight group; more than 16 vectors are the GEMM
+ * lbq_gemm_q1g128 (same result rule either way; within each group the matrix cores sum the
+ * exact products in their own order). Large-k calls split the reduction over workgroups
  * through the stream's split-K workspace (see the conventions above). LBQ_E_NOMEM if it cannot
  * be allocated (e.g. on a stream's first such call inside graph capture). */
 lbq_status lbq_gemv_q1g128(const void* d_w, int32_t n, int32_t k, const uint16_t* d_x,
@@ -220,7 +222,9 @@ lbq_status lbq_unpack_i4g128(const void* src, int32_t n, int32_t k, uint8_t* nib
                              uint16_t* scales);
 
 /* y[b][row] = bf16_rne( sum_g f32(scale[row][g]) * sum_{j in g} q[row][j] * x[b][j] ), fp32
- * accumulation. Same pointer, alignment, batch and workspace rules as lbq_gemv_q1g128. */
+ * accumulation. Same pointer, alignment, batch and workspace rules as lbq_gemv_q1g128 (one
+ * vector always takes the per-row kernel; 2 to 16 vectors the matrix cores, where a group's sum
+ * is formed as 16 sum (1 + c/16) x - 24 sum x from the offset codes c = q + 8). */
 lbq_status lbq_gemv_i4g128(const void* d_w, int32_t n, int32_t k, const uint16_t* d_x,
                            uint16_t* d_y, int32_t batch, void* stream);
 

@@ -90,7 +90,7 @@ lbq_status stage_decode_q1(const lbq_q1_layer* layers, int n_layers, int hidden,
                            const uint16_t* d_x0, uint16_t* d_act, float eps, void* stream,
                            bool no_alloc);
 
-// Q1_0_g128 GEMV for 2 <= batch <= 16 vectors on the matrix cores (lbq_q1mb.hip); the caller
+// Q1_0_g128 GEMV for 1 <= batch <= 16 vectors on the matrix cores (lbq_q1mb.hip); the caller
 // has validated pointers, shapes and aliasing, and d_x is 16-byte aligned. Uses the stream's
 // split-K workspace when k is split.
 lbq_status q1_gemv_mb(const void* d_w, int n, int k, const uint16_t* d_x, uint16_t* d_y,
@@ -103,6 +103,8 @@ struct MbJob {
   int n, k;
 };
 lbq_status q1_gemv_mb_multi(const MbJob* jobs, int njobs, int batch, void* stream);
+// Compute units of the current device (cached per device).
+int device_cus();
 // INT4 g128 GEMV for 2 <= batch <= 16 vectors on the matrix cores (same rules).
 lbq_status i4_gemv_mb(const void* d_w, int n, int k, const uint16_t* d_x, uint16_t* d_y,
                       int batch, void* stream);

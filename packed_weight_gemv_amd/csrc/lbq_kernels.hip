@@ -1088,6 +1088,11 @@ static lbq_status gemv_common(Fmt fmt, const void* d_w, int32_t n, int32_t k,
   if (batch >= 2 && batch <= 16 && (uintptr_t)d_x % 16 == 0)
     return fmt == Fmt::Q1 ? q1_gemv_mb(d_w, n, k, d_x, d_y, batch, stream)
                           : i4_gemv_mb(d_w, n, k, d_x, d_y, batch, stream);
+  // one vector, Q1, fewer 64-row tiles than compute units (5120 x 5120, 5120 x 17408): the
+  // matrix-core kernel's deeper k slices beat the per-row lookups (measured 7.6 vs 9.2 us and
+  // 10.6 vs 15.8 us); taller matrices keep the lookup kernel
+  if (fmt == Fmt::Q1 && batch == 1 && (uintptr_t)d_x % 16 == 0 && g.tiles < device_cus())
+    return q1_gemv_mb(d_w, n, k, d_x, d_y, batch, stream);
   if (batch >= 2 && (uintptr_t)d_x % 16 == 0)
     return fmt == Fmt::Q1 ? lbq_gemm_q1g128(d_w, n, k, d_x, d_y, batch, stream)
                           : lbq_gemm_i4g128(d_w, n, k, d_x, d_y, batch, stream);

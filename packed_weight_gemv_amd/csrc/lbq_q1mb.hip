@@ -383,8 +383,10 @@ int cus_of_device() {
 
 }  // namespace
 
-// Batched GEMVs (2 <= batch <= 16 vectors) on the matrix cores, several matrices in one
-// launch. Pointers, shapes and aliasing are validated by the caller; every x is 16-byte aligned.
+int lbq::device_cus() { return cus_of_device(); }
+
+// GEMVs of up to 16 vectors on the matrix cores, several matrices in one launch. Pointers,
+// shapes and aliasing are validated by the caller; every x is 16-byte aligned.
 namespace {
 template <int FMT>
 lbq_status mb_launch(const MbJob* jobs, int njobs, int batch, void* stream) {
