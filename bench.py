@@ -39,7 +39,8 @@ HBM_PEAK_GBS = 8000.0
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "q1_stage_decode_64L.md")
 I4_PROFILE = os.path.join(ROOT, "profiles", "i4_layer_gemv.md")
 TERN_PROFILE = os.path.join(ROOT, "profiles", "tern_layer_gemv.md")
-I4_KERNELS = os.path.join(ROOT, "packed_weight_gemv_amd", "csrc", "lbq_kernels.hip")
+I4_KERNELS = [os.path.join(ROOT, "packed_weight_gemv_amd", "csrc", f)
+              for f in ("lbq_kernels.hip", "lbq_q1mb.hip")]
 STEP_SOURCES = [os.path.join(ROOT, "packed_weight_gemv_amd", "csrc", f)
                 for f in ("lbq_stage.hip", "lbq_internal.h")]
 
@@ -74,8 +75,11 @@ def i4_layer_traffic(key: str, profile: str = None):
     profile = profile or I4_PROFILE
     if not os.path.exists(profile):
         return None
-    with open(I4_KERNELS, "rb") as fh:
-        cur = hashlib.sha256(fh.read()).hexdigest()
+    h = hashlib.sha256()
+    for f in I4_KERNELS:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    cur = h.hexdigest()
     sha, traffic = None, None
     with open(profile) as fh:
         for line in fh:
@@ -318,29 +322,40 @@ def main() -> int:
                      f"{2 * L + 1} launches)")
         kern_avg_ms, kern_bytes = step_kernel_ms, bytes_per_step
     else:
-        # host-driven step: every Q1 GEMV launch of a step bracketed by events
-        kern_name = ("q1_mb_kernel (the batched matrix-core GEMV, each of a step's Q1 "
-                     "projections launched and timed on its own)")
-        gemv_ms, gemv_bytes, launches = 0.0, 0, 0
+        # batched step: each projection's GEMV timed on its own, as a HIP graph of back-to-back
+        # calls over different layers' weights (so every call streams its weights from HBM and
+        # no host gap falls between the launches)
+        kern_name = ("q1_mb_kernel (the batched matrix-core GEMV; each projection of the step "
+                     "launched alone, back to back over the layers)")
         src = {"q": "x", "k": "x", "v": "x", "gate": "x", "up": "x", "o": "xo", "down": "xd"}
-        for _ in range(max(1, args.kernel_steps)):
-            lst = []
-            for l in range(L):
-                for nm in ("q", "k", "v", "gate", "up", "o", "down"):
-                    n, k = shapes[nm]
-                    xin = lbq.act_view(act, src[nm], l, L, hid, kv, ffn, B)
-                    yout = lbq.act_view(act, nm, l, L, hid, kv, ffn, B)
-                    e0 = torch.cuda.Event(enable_timing=True)
-                    e1 = torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
-                    lbq.lbq_gemv_q1g128(layers[l][nm], n, k, xin, yout)
-                    e1.record(stream)
-                    lst.append((e0, e1, n * k * 9 // 64))
+        gemv_ms, gemv_bytes, launches = 0.0, 0, 0
+        cap = torch.cuda.Stream()
+        for nm in ("q", "k", "v", "gate", "up", "o", "down"):
+            n, k = shapes[nm]
+            calls = [(layers[l][nm], lbq.act_view(act, src[nm], l, L, hid, kv, ffn, B),
+                      lbq.act_view(act, nm, l, L, hid, kv, ffn, B)) for l in range(L)]
+            with torch.cuda.stream(cap):
+                for w_, xin, yout in calls:
+                    lbq.lbq_gemv_q1g128(w_, n, k, xin, yout, stream=cap)
             torch.cuda.synchronize()
-            for e0, e1, nb in lst:
-                gemv_ms += e0.elapsed_time(e1)
-                gemv_bytes += nb
-                launches += 1
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                for w_, xin, yout in calls:
+                    lbq.lbq_gemv_q1g128(w_, n, k, xin, yout, stream=cap)
+            g.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            reps = max(1, args.kernel_steps)
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            gemv_ms += e0.elapsed_time(e1) / reps
+            gemv_bytes += L * (n * k * 9 // 64)
+            launches += L
+            del g
         kern_avg_ms = gemv_ms / launches
         kern_bytes = gemv_bytes / launches
         run()   # restore the activation record of a full step for the parity check below
