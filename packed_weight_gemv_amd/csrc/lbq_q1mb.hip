@@ -3,8 +3,8 @@
 // highlights") and INT4 g128 (the Acorn page, "int4 quantization quality: group quantization
 // (g=128)").
 //
-// A workgroup of four waves takes one 64-row tile over a slice of k (up to four super-groups of
-// eight 128-weight groups). A unit is one group of the tile: four sub-tiles of 16 rows, each
+// A workgroup of four waves takes one 64-row tile over a slice of k (up to five super-groups of
+// eight 128-weight groups: a 5120-deep product in one slice). A unit is one group of the tile: four sub-tiles of 16 rows, each
 // taken in four 32-deep steps of v_mfma_f32_16x16x32_bf16 with the activation vectors as the
 // rows of the A operand (vector m in row m) and 16 weight rows as the 16 columns of B. So the
 // matrix cores work on all vectors at once, and the weights are expanded once for all of them.
@@ -41,8 +41,9 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kMaxSupers = 4;                 // super-groups of one slice of k
-constexpr int kSlots = kMaxSupers * kSuper / kWaves;   // units per wave: 8
+constexpr int kMaxSupers = 5;                 // super-groups of one slice of k (5120 inputs)
+constexpr int kSlots = kMaxSupers * kSuper / kWaves;   // units per wave: 10
+constexpr int kBlocksPerWave = (kMaxSupers + kWaves - 1) / kWaves;   // scale blocks staged
 constexpr int kMaxVec = 16;
 constexpr int kQ1SuperBytes = kBlock * (1 + kSuper * kQ1GroupBlocks);
 constexpr int kI4SuperBytes = kBlock * (1 + kSuper * kI4GroupBlocks);
@@ -194,21 +195,6 @@ struct MbArgs {
   int nmats, batch;
 };
 
-// Matrix i of the launch (i uniform), read field by field with constant indices (a dynamic
-// index into the argument block would be lowered through scratch memory).
-__device__ __forceinline__ MbMat pick_mat(const MbArgs& A, int i) {
-  switch (i) {
-    case 0: return A.m[0];
-    case 1: return A.m[1];
-    case 2: return A.m[2];
-    case 3: return A.m[3];
-    case 4: return A.m[4];
-    case 5: return A.m[5];
-    case 6: return A.m[6];
-    default: return A.m[7];
-  }
-}
-
 // FMT 0: Q1_0_g128, 1: INT4 g128.
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void mb_kernel(MbArgs A) {
@@ -225,7 +211,9 @@ __global__ __launch_bounds__(kThreads) void mb_kernel(MbArgs A) {
 #pragma unroll
   for (int i = 1; i < kMaxMats; ++i)
     if (i < A.nmats && (int)blockIdx.x >= A.m[i].wg0) mi = i;
-  const MbMat M = pick_mat(A, mi);
+  // read in place from the argument block (a copy in registers would be indexed, and so kept
+  // in scratch memory)
+  const MbMat& M = A.m[mi];
   const uint8_t* __restrict__ w = M.w;
   const uint16_t* __restrict__ x = M.x;
   uint16_t* __restrict__ y = M.y;
@@ -250,8 +238,14 @@ __global__ __launch_bounds__(kThreads) void mb_kernel(MbArgs A) {
     L.lut[tid] = lo | hi << 16;
   }
   const int nsb = s1 - s0;
-  const int sb = wave < nsb ? wave : nsb - 1;   // a repeated block is stored twice, same bytes
-  const u32x4 sreg = *(const u32x4*)(tb + (size_t)(s0 + sb) * kSuperBytes + lane * 16);
+  int sb[kBlocksPerWave];
+  u32x4 sreg[kBlocksPerWave];
+#pragma unroll
+  for (int i = 0; i < kBlocksPerWave; ++i) {
+    const int b = wave + kWaves * i;
+    sb[i] = b < nsb ? b : nsb - 1;   // a repeated block is stored twice, same bytes
+    sreg[i] = *(const u32x4*)(tb + (size_t)(s0 + sb[i]) * kSuperBytes + lane * 16);
+  }
   // unit j's records: Q1 rec[j][0] = row `lane`; INT4 rec[j][t] = piece h of row 16 t + n
   u32x4 rec[kSlots][FMT == 0 ? 1 : 4];
   auto issue = [&](int j) {
@@ -275,9 +269,13 @@ __global__ __launch_bounds__(kThreads) void mb_kernel(MbArgs A) {
   {
     // scale block stored as [group][row % 16][row / 16]: the four scales a lane applies to a
     // unit (rows n, 16 + n, 32 + n, 48 + n) are one 8-byte read
-    uint16_t* d = (uint16_t*)L.sblk[sb] + (lane & 15) * 4 + (lane >> 4);
 #pragma unroll
-    for (int g = 0; g < kSuper; ++g) d[g * kTileRows] = (uint16_t)(sreg[g >> 1] >> (16 * (g & 1)));
+    for (int i = 0; i < kBlocksPerWave; ++i) {
+      uint16_t* d = (uint16_t*)L.sblk[sb[i]] + (lane & 15) * 4 + (lane >> 4);
+#pragma unroll
+      for (int g = 0; g < kSuper; ++g)
+        d[g * kTileRows] = (uint16_t)(sreg[i][g >> 1] >> (16 * (g & 1)));
+    }
   }
   // the LDS writes are complete before the barrier; no wait for the loads in flight
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -397,15 +395,22 @@ lbq_status mb_launch(const MbJob* jobs, int njobs, int batch, void* stream) {
   A.batch = batch;
   size_t part_floats = 0, ncounters = 0;
   long long wgs = 0;
+  // slices of k: about two workgroups per compute unit over the whole launch (all of them
+  // resident at once), each slice at most kMaxSupers super-groups deep; more, shorter slices
+  // only add split-K round trips
   const long long want = 2LL * cus_of_device();
+  long long all_tiles = 0;
   for (int i = 0; i < njobs; ++i) {
     Geometry g;
     if (!make_geometry(jobs[i].n, jobs[i].k, FMT == 0 ? kQ1GroupBlocks : kI4GroupBlocks, &g))
       return LBQ_E_SHAPE;
-    // slices of k: enough workgroups to give every compute unit about two, each slice at most
-    // kMaxSupers super-groups deep (more, shorter slices only add split-K round trips)
+    all_tiles += g.tiles;
+  }
+  for (int i = 0; i < njobs; ++i) {
+    Geometry g;
+    make_geometry(jobs[i].n, jobs[i].k, FMT == 0 ? kQ1GroupBlocks : kI4GroupBlocks, &g);
     const int supers = (int)g.supers;
-    int splits = (int)((want + g.tiles - 1) / g.tiles);
+    int splits = (int)(want / all_tiles);
     if (splits > supers) splits = supers;
     if (splits < (supers + kMaxSupers - 1) / kMaxSupers) splits = (supers + kMaxSupers - 1) / kMaxSupers;
     if (splits < 1) splits = 1;
