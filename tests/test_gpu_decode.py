@@ -58,7 +58,7 @@ def _check_step(lbq, mats, act, L, hid, kv, ffn, batch, layers_to_check, rows=No
         _check_rms(view("down", l), nxt)
 
 
-@pytest.mark.parametrize("batch", [1, 8])
+@pytest.mark.parametrize("batch", [1, 2, 5, 8, 16])
 def test_decode_step_small_stream_teacher_forced(lbq, batch):
     L, hid, kv, ffn = 3, 384, 128, 640
     mats, layers = _build_stream(lbq, L, hid, kv, ffn)

@@ -78,14 +78,17 @@ def test_per_call_gemvs_in_a_graph_match_eager(lbq, path):
         assert np.array_equal(r[0], bits(y_eager))
 
 
-def test_batch1_decode_step_in_a_graph_matches_eager_and_is_deterministic(lbq):
+@pytest.mark.parametrize("batch", [1, 4])
+def test_decode_step_in_a_graph_matches_eager_and_is_deterministic(lbq, batch):
+    """Batch 1 runs the stage kernels, batch 4 the matrix-core GEMV launches (split-K tile
+    counters re-armed by every launch) and the wide rescale launches between them."""
     L, hid, kv, ffn = 2, 1024, 256, 2048
     layers = [{nm: to_dev(lbq.lbq_pack_q1g128(*(lambda mm: (mm.signs, mm.scales))(
         synth.stream_matrix(l, nm, hidden=hid, kv=kv, ffn=ffn)))) for nm in synth.STREAM_MATRICES}
         for l in range(L)]
     arr = lbq.make_layers(layers)
-    x0 = to_dev(synth.activations(1, hid, workload=72))
-    n = lbq.lbq_decode_act_elems(L, hid, kv, ffn, 1)
+    x0 = to_dev(synth.activations(batch, hid, workload=72))
+    n = lbq.lbq_decode_act_elems(L, hid, kv, ffn, batch)
     act_a = torch.zeros(n, dtype=torch.int16, device="cuda:0")
     act_b = torch.zeros(n, dtype=torch.int16, device="cuda:0")
     act_g = torch.zeros(n, dtype=torch.int16, device="cuda:0")
