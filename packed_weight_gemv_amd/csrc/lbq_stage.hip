@@ -19,7 +19,9 @@
 //    units at once (a unit is one 128-weight group of one 64-row tile: 16 bytes per lane) and
 //    wait for the tables. Waves 0-7 (prologue waves) first request the input vector and the scale
 //    blocks of the workgroup's tiles (1 KiB each, staged in LDS through registers), form the
-//    input, build the tables and publish them, and only then request their own units. A wave
+//    input, build the tables in rounds of 16 groups, publishing each round as it is written
+//    (a stream wave starts on a unit as soon as the round holding its group is out), and only
+//    then request their own units. A wave
 //    issues its memory instructions in order and stalls at issue while the compute unit's
 //    memory pipeline is full, so a wave that requested weights up front could do nothing else
 //    until they arrive; the split keeps the weights streaming while the tables are built. The
@@ -38,7 +40,12 @@
 //    aligned fields (x4, the table's byte stride), an SDWA add places one on the group's table
 //    base, and one LDS read fetches the entry; two entries join the int32 sum per add3.
 //  * Sums that every workgroup must agree on (the sum of squares of a rescale) are taken in one
-//    fixed order: DPP steps inside a wave, then the waves in order.
+//    fixed order: DPP steps inside a wave, then the waves in order. Stage 2's total (of the
+//    pair-tile sums) is formed by every wave on its own, in one fixed order, so no wave waits
+//    for another before building its tables.
+//  * Per unit, the tile, group, scale-block and table indices are uniform and kept in scalar
+//    registers (selects, no multiplies); the vector units issue only the lookups and the unit's
+//    weighting and accumulation.
 //  * The activation slots (x, q, k, v, gate, up, xo, o, xd, down) are written as the
 //    per-projection path writes them.
 #include <hip/hip_runtime.h>
@@ -73,7 +80,9 @@ constexpr int kPRounds = (1280 + kPThreads - 1) / kPThreads;   // stage-1 input:
                                                               // pt + kPThreads r
 constexpr int kPRounds2 = (1536 + kPThreads - 1) / kPThreads;  // stage-2 input: 4-input chunks
                                                               // pt + kPThreads r (48 groups)
-constexpr int kStRounds = (1024 + kPThreads - 1) / kPThreads;  // the pair sums, pt + kPThreads r
+constexpr int kStLoads = 1024 / 64;   // the pair sums, lane + 64 r (every wave adds all of them)
+constexpr int kTabRounds = kPRounds2 > kPRounds ? kPRounds2 : kPRounds;   // table rounds
+constexpr int kGroupsPerRound = kPThreads / (kGroup / 4);   // 16 groups of tables per round
 constexpr size_t kPartFloats = (size_t)kMaxSlots * kTabGroups * kGroup;   // 28,672 floats
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -216,8 +225,8 @@ struct StLds {
   float red[kMaxTiles][kWaves][64];           // per-wave partial sums of each tile
   float fac[kTabGroups];                      // 2^(E_g - 22)
   float ssum[kPWaves];                        // per-wave sums of squares of the prologue waves
-  unsigned arrived_sum, arrived_tab, arrived_scl;   // prologue waves done with their sums /
-                                                    // tables / scale-block copies
+  unsigned arrived_sum;                // prologue waves done with their sums
+  unsigned arrived_tab[kTabRounds];    // prologue waves done with round r of the tables
 };
 
 // Counters in LDS through which the prologue waves hand their LDS results to the other waves
@@ -418,39 +427,52 @@ __device__ __forceinline__ int unit_isum(u32x4 rec, uint32_t tab) {
 }
 
 // The lookups of a wave's units: each unit's group sum times the group's fixed-point factor
-// (LDS `fac`) and the row's fp16 scale (the staged scale blocks, awaited once the first group
-// sum is formed). Stage 1: tile ti = u / G, group u mod G, table group = group, scale block
-// ti * S + group / 8. Stage 2 (G = units of the piece, S unused): table group u, scale block
-// (ga + u) / 8 - j0.
+// (LDS `fac`) and the row's fp16 scale (the staged scale blocks). Stage 1: tile ti = u / G, group
+// u mod G, table group = group, scale block ti * S + group / 8. Stage 2 (G = units of the piece,
+// S unused): table group u, scale block (ga + u) / 8 - j0. Before its first unit of table group
+// t the wave waits for the table round that holds t (t / kGroupsPerRound); the prologue waves
+// store the scale blocks before their first round, so that wait covers them too.
 template <int MU, bool STAGE1>
 __device__ __forceinline__ void lookup_units(const WaveUnits<MU>& W, int G, int S, int ga, int j0,
                                              const StLds& L, float (&acc)[kMaxTiles]) {
   const int lane = threadIdx.x & 63;
   const uint32_t tab0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)L.tab;
-  const uint32_t sbl0 =
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)L.sblk;
+  const uint32_t sbl = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)L.sblk +
+                       lane * 2;
   const uint32_t fac0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const float*)L.fac;
+  // Unit, tile, group and block indices are the same in every lane: they are kept in scalar
+  // registers and formed without multiplies (uniform selects), so the vector units spend their
+  // issue slots on the lookups.
+  const int u0 = __builtin_amdgcn_readfirstlane(W.u0);
+  const int u1 = __builtin_amdgcn_readfirstlane(W.u1);
+  const int Gs = __builtin_amdgcn_readfirstlane(G);
+  const int Ss = __builtin_amdgcn_readfirstlane(S);
+  int ready = -1;   // table rounds 0 .. ready are complete
 #pragma unroll
   for (int j = 0; j < MU; ++j) {
-    const int u = W.u0 + W.stride * j;
-    if (u >= W.u1) break;
+    const int u = u0 + W.stride * j;
+    if (u >= u1) break;
     int ti = 0, gt = u, blk;
     if (STAGE1) {
-      ti = (u >= G) + (u >= 2 * G);
-      gt = u - ti * G;
-      blk = ti * S + (gt >> 3);
+      ti = u >= Gs ? (u >= 2 * Gs ? 2 : 1) : 0;
+      gt = u - (ti == 0 ? 0 : (ti == 1 ? Gs : 2 * Gs));
+      blk = (ti == 0 ? 0 : (ti == 1 ? Ss : 2 * Ss)) + (gt >> 3);
     } else {
       blk = ((ga + u) >> 3) - j0;
     }
     const int gs = STAGE1 ? gt : ga + u;   // group within the row (for the scale)
-    const uint32_t sb = sbl0 + (uint32_t)blk * kBlock + (gs & 7) * (2 * kTileRows) + lane * 2;
+    const uint32_t soff = (uint32_t)blk * kBlock + (uint32_t)(gs & 7) * (2 * kTileRows);
+    const int need = gt / kGroupsPerRound;
+    if (need > ready) {
+      wait_count(const_cast<unsigned*>(&L.arrived_tab[need]), kPWaves);
+      ready = need;
+    }
     const int isum = unit_isum(W.rec[j], tab0 + (uint32_t)gt * kGroupTabBytes);
-    if (j == 0) wait_count(const_cast<unsigned*>(&L.arrived_scl), kPWaves);
     const float f = *(__attribute__((address_space(3))) const float*)(uintptr_t)(fac0 + gt * 4);
-    const float v = (float)isum * f * f16(*(lds_cu16*)(uintptr_t)sb);
-    if (ti == 0) acc[0] += v;
-    else if (ti == 1) acc[1] += v;
-    else acc[2] += v;
+    const float v = (float)isum * f * f16(*(lds_cu16*)(uintptr_t)(sbl + soff));
+    acc[0] += ti == 0 ? v : 0.f;   // selects on a scalar condition: no branches
+    acc[1] += ti == 1 ? v : 0.f;
+    acc[2] += ti == 2 ? v : 0.f;
   }
 }
 
@@ -486,7 +508,6 @@ __device__ void stage1_run(const S1Args& A, StLds& L, int T, const LaneTile (&lt
       W.stride = kSWaves;
       W.u1 = us;
       issue_units<kUnitsS1>(W, addr, lt[0].w);
-      wait_count(&L.arrived_tab, kPWaves);
       lookup_units<kUnitsS1, true>(W, G, S, 0, 0, L, acc);
     }
   } else {
@@ -555,7 +576,12 @@ __device__ void stage1_run(const S1Args& A, StLds& L, int T, const LaneTile (&lt
       denom = sqrtf(tot / (float)n_in + A.eps);
       rden = 1.f / denom;
     }
-    // ---- bf16 inputs, record slots, fixed point, tables ------------------------------------
+    if (UNITS) {
+#pragma unroll
+      for (int k = 0; k < kB; ++k) store_block(L.sblk[sblk[k]], sreg[k]);
+    }
+    // ---- bf16 inputs, record slots, fixed point, tables (each round published as it is
+    //      written: round r holds table groups kGroupsPerRound r ..) -------------------------
     char* tab = (char*)L.tab;
 #pragma unroll
     for (int r = 0; r < kPRounds; ++r) {
@@ -581,20 +607,14 @@ __device__ void stage1_run(const S1Args& A, StLds& L, int T, const LaneTile (&lt
         put_table(tab, (uint32_t)c * 64, v, 22 - E, lane);
         if ((c & 31) == 0) L.fac[c >> 5] = __builtin_ldexpf(1.f, E - 22);
       }
+      arrive(&L.arrived_tab[r]);
     }
-    arrive(&L.arrived_tab);
-    if (UNITS) {
-#pragma unroll
-      for (int k = 0; k < kB; ++k) store_block(L.sblk[sblk[k]], sreg[k]);
-    }
-    arrive(&L.arrived_scl);
     if (UNITS) {
       WaveUnits<kUnitsP1> W;
       W.u0 = us + rw;
       W.stride = kPWaves;
       W.u1 = nunits;
       issue_units<kUnitsP1>(W, addr, lt[0].w);
-      wait_count(&L.arrived_tab, kPWaves);
       lookup_units<kUnitsP1, true>(W, G, S, 0, 0, L, acc);
     }
   }
@@ -631,8 +651,8 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(S1Args A) {
   const int b = blockIdx.x, lane = threadIdx.x & 63;
   if (threadIdx.x == 0) {
     L.arrived_sum = 0;
-    L.arrived_tab = 0;
-    L.arrived_scl = 0;
+#pragma unroll
+    for (int r = 0; r < kTabRounds; ++r) L.arrived_tab[r] = 0;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // zeros land before any arrival
   }
   const bool is_x = b < A.x_wgs;
@@ -666,8 +686,8 @@ __global__ __launch_bounds__(kThreads) void stage2_kernel(S2Args A) {
   const int rw = role_index(wave);
   if (tid == 0) {
     L.arrived_sum = 0;
-    L.arrived_tab = 0;
-    L.arrived_scl = 0;
+#pragma unroll
+    for (int r = 0; r < kTabRounds; ++r) L.arrived_tab[r] = 0;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // zeros land before any arrival
   }
   const int t = blockIdx.x / A.pieces, p = blockIdx.x - t * A.pieces;
@@ -687,7 +707,6 @@ __global__ __launch_bounds__(kThreads) void stage2_kernel(S2Args A) {
     W.stride = kSWaves;
     W.u1 = us;
     issue_units<kUnitsS2>(W, addr, spare);
-    wait_count(&L.arrived_tab, kPWaves);
     lookup_units<kUnitsS2, false>(W, nunits, 0, ga, j0, L, acc);
   } else {
     // ---- prologue waves: the pair tiles' sums of squares, this piece's gate and up, and the
@@ -695,10 +714,10 @@ __global__ __launch_bounds__(kThreads) void stage2_kernel(S2Args A) {
     const int pt = rw * 64 + lane;   // 0 .. 511
     const int npair = A.ffn / 32;
     const int c4a = ga * (kGroup / 4), n4 = nunits * (kGroup / 4);
-    float st[kStRounds];
+    float st[kStLoads];   // every wave loads all pair sums: lane takes lane + 64 r
 #pragma unroll
-    for (int r = 0; r < kStRounds; ++r) {
-      const int i = pt + kPThreads * r;
+    for (int r = 0; r < kStLoads; ++r) {
+      const int i = lane + 64 * r;
       st[r] = A.stat[i < npair ? i : npair - 1];
     }
     uint2 go[kPRounds2], uo[kPRounds2];
@@ -713,14 +732,18 @@ __global__ __launch_bounds__(kThreads) void stage2_kernel(S2Args A) {
     const int sb = rw < nblk ? rw : nblk - 1;   // a repeated block: same bytes twice
     const u32x4 sreg = load_block(tw + (size_t)(j0 + sb) * kSuperBytes);
     issue_barrier();
-    // ---- the rescale of h = gate * up (the pair tiles' sums in a fixed order) --------------
+    // ---- the rescale of h = gate * up: every wave adds the pair tiles' sums itself, in one
+    //      fixed order (each lane its sums in order, then the wave's fixed DPP steps), so all
+    //      waves of all workgroups hold the same total and none waits for another ------------
     float ss = 0.f;
 #pragma unroll
-    for (int r = 0; r < kStRounds; ++r) ss += pt + kPThreads * r < npair ? st[r] : 0.f;
-    const float tot = prologue_sum(ss, L, rw);
+    for (int r = 0; r < kStLoads; ++r) ss += lane + 64 * r < npair ? st[r] : 0.f;
+    const float tot = wave_sum(ss);
     const float denom = sqrtf(tot / (float)A.ffn + A.eps);
     const float rden = 1.f / denom;
-    // ---- xd over the piece: record (pieces of tile 0), fixed point, tables -----------------
+    store_block(L.sblk[sb], sreg);
+    // ---- xd over the piece: record (pieces of tile 0), fixed point, tables; each round is
+    //      published as it is written -----------------------------------------------------
     char* tab = (char*)L.tab;
 #pragma unroll
     for (int r = 0; r < kPRounds2; ++r) {
@@ -748,16 +771,13 @@ __global__ __launch_bounds__(kThreads) void stage2_kernel(S2Args A) {
         put_table(tab, (uint32_t)i * 64, v, 22 - E, lane);
         if ((i & 31) == 0) L.fac[i >> 5] = __builtin_ldexpf(1.f, E - 22);
       }
+      arrive(&L.arrived_tab[r]);
     }
-    arrive(&L.arrived_tab);
-    store_block(L.sblk[sb], sreg);
-    arrive(&L.arrived_scl);
     WaveUnits<kUnitsP2> W;
     W.u0 = us + rw;
     W.stride = kPWaves;
     W.u1 = nunits;
     issue_units<kUnitsP2>(W, addr, spare);
-    wait_count(&L.arrived_tab, kPWaves);
     lookup_units<kUnitsP2, false>(W, nunits, 0, ga, j0, L, acc);
   }
   L.red[0][wave][lane] = acc[0];
@@ -847,7 +867,7 @@ lbq_status lbq::stage_decode_q1(const lbq_q1_layer* layers, int n_layers, int hi
   const int G = hidden / kGroup, FG = ffn / kGroup;
   const int S = ceil_div(G, kSuper);
   if (G > kTabGroups || hidden / 4 > kPRounds * kPThreads) return LBQ_E_UNSUPPORTED;
-  if ((size_t)ffn / 32 > kStatFloats || ffn / 32 > kStRounds * kPThreads) return LBQ_E_UNSUPPORTED;
+  if ((size_t)ffn / 32 > kStatFloats || ffn / 32 > kStLoads * 64) return LBQ_E_UNSUPPORTED;
   // tiles per stage-1 workgroup: within the units of its waves and the scale blocks it stages
   const int wg_units1 = kSWaves * kUnitsS1 + kPWaves * kUnitsP1;
   int tmax = kMaxTiles;
