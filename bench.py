@@ -610,8 +610,8 @@ def q1_gemv_bench(args, lbq, synth, torch, np, dev) -> int:
                    "tolerance": "2e-3 * sum|s*w*x|"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "mb_kernel<0> (the matrix-core GEMV, which takes batch-1 "
-                               "matrices with fewer 64-row tiles than compute units)",
+                     "kernel": "stage1_kernel (the stage-1 lookup kernel, which takes "
+                               "batch-1 GEMVs with k <= 7168)",
                      "avg_launch_us": round(us, 3), "bytes_per_launch": nbytes},
         "cpu_baseline": {"value": round(reps * m.shape[0] * m.shape[1] * 9 / 64 / dt / 1e9, 4),
                          "unit": "GB/s", "cores": cores, "kind": "oracle",

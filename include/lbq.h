@@ -181,9 +181,13 @@ lbq_status lbq_unpack_q1g128(const void* src, int32_t n, int32_t k, uint8_t* sig
  *   d_w : device layout (lbq_pack_q1g128), 16-byte aligned
  *   d_x : bf16 [batch][k], 4-byte aligned     d_y : bf16 [batch][n], 4-byte aligned
  * Requires k % 128 == 0, 1 <= n, 0 <= batch <= LBQ_MAX_BATCH (0 = no-op). d_y must not
- * overlap d_x or the weights. With d_x 16-byte aligned, 2 to 16 vectors (and one vector when
- * the matrix has fewer 64-row tiles than the device has compute units) run on the matrix cores,
- * all vectors through one product per weight group; more than 16 vectors are the GEMM
+ * overlap d_x or the weights. One vector with d_x 8-byte aligned and k <= 7168 runs on the
+ * stage-1 lookup kernel (no workspace): a group's 128 signed inputs are summed exactly as
+ * integers on the fixed point 2^(E-22), 2^E above the group's largest input magnitude (inputs
+ * more than 2^15 times smaller than that are rounded to it), then weighted by the fp16 scale
+ * and accumulated in fp32. With d_x 16-byte aligned, 2 to 16 vectors (and one vector of a
+ * deeper matrix with fewer 64-row tiles than the device has compute units) run on the matrix
+ * cores, all vectors through one product per weight group; more than 16 vectors are the GEMM
  * lbq_gemm_q1g128 (same result rule either way; within each group the matrix cores sum the
  * exact products in their own order). Large-k calls split the reduction over workgroups
  * through the stream's split-K workspace (see the conventions above). LBQ_E_NOMEM if it cannot

@@ -90,6 +90,14 @@ lbq_status stage_decode_q1(const lbq_q1_layer* layers, int n_layers, int hidden,
                            const uint16_t* d_x0, uint16_t* d_act, float eps, void* stream,
                            bool no_alloc);
 
+// One batch-1 Q1_0_g128 GEMV through the stage-1 kernel (lbq_stage.hip), the input used as it
+// is: one workgroup per compute unit takes up to three 64-row tiles over the whole of k and
+// builds the sign-sum tables of x once for them. Needs no workspace. The caller has validated
+// pointers, shapes and aliasing; LBQ_E_UNSUPPORTED (nothing launched) where it does not apply
+// (k beyond the table capacity, x not 8-byte aligned, more tiles than three per compute unit).
+lbq_status stage_gemv_q1(const void* d_w, int n, int k, const uint16_t* d_x, uint16_t* d_y,
+                         void* stream);
+
 // Q1_0_g128 GEMV for 1 <= batch <= 16 vectors on the matrix cores (lbq_q1mb.hip); the caller
 // has validated pointers, shapes and aliasing, and d_x is 16-byte aligned. Uses the stream's
 // split-K workspace when k is split.

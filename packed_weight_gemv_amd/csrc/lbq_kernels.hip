@@ -1088,9 +1088,16 @@ static lbq_status gemv_common(Fmt fmt, const void* d_w, int32_t n, int32_t k,
   if (batch >= 2 && batch <= 16 && (uintptr_t)d_x % 16 == 0)
     return fmt == Fmt::Q1 ? q1_gemv_mb(d_w, n, k, d_x, d_y, batch, stream)
                           : i4_gemv_mb(d_w, n, k, d_x, d_y, batch, stream);
-  // one vector, Q1, fewer 64-row tiles than compute units (5120 x 5120, 5120 x 17408): the
-  // matrix-core kernel's deeper k slices beat the per-row lookups (measured 7.6 vs 9.2 us and
-  // 10.6 vs 15.8 us); taller matrices keep the lookup kernel
+  // one vector, Q1, k within the stage kernel's table capacity (k <= 7168, x 8-byte aligned):
+  // the stage-1 kernel, which builds the sign-sum tables of x once per workgroup for up to three
+  // tiles and streams them with its wave roles
+  if (fmt == Fmt::Q1 && batch == 1) {
+    const lbq_status st = stage_gemv_q1(d_w, n, k, d_x, d_y, stream);
+    if (st != LBQ_E_UNSUPPORTED) return st;
+  }
+  // one vector, Q1, deeper than the stage kernel's tables (5120 x 17408) and fewer 64-row tiles
+  // than compute units: the matrix-core kernel's k slices beat the per-row lookups (measured
+  // 10.6 vs 15.8 us); taller matrices keep the per-row lookup kernel
   if (fmt == Fmt::Q1 && batch == 1 && (uintptr_t)d_x % 16 == 0 && g.tiles < device_cus())
     return q1_gemv_mb(d_w, n, k, d_x, d_y, batch, stream);
   if (batch >= 2 && (uintptr_t)d_x % 16 == 0)

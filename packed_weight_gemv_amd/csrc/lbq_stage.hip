@@ -976,3 +976,36 @@ lbq_status lbq::stage_decode_q1(const lbq_q1_layer* layers, int n_layers, int hi
   }
   return hipGetLastError() == hipSuccess ? LBQ_OK : LBQ_E_DEVICE;
 }
+
+// One batch-1 GEMV through stage 1 (KIND 0: the input as it is). The tiles of the matrix are
+// the x list's single tiles; workgroups take up to three each, one workgroup per compute unit.
+lbq_status lbq::stage_gemv_q1(const void* d_w, int n, int k, const uint16_t* d_x, uint16_t* d_y,
+                              void* stream) {
+  if (k % kGroup || (uintptr_t)d_x % 8) return LBQ_E_UNSUPPORTED;
+  const int G = k / kGroup, S = ceil_div(G, kSuper);
+  if (G > kTabGroups || k / 4 > kPRounds * kPThreads) return LBQ_E_UNSUPPORTED;
+  const int wg_units1 = kSWaves * kUnitsS1 + kPWaves * kUnitsP1;
+  int tmax = kMaxTiles;
+  if (tmax > wg_units1 / G) tmax = wg_units1 / G;
+  if (tmax > kMaxBlocks / S) tmax = kMaxBlocks / S;
+  if (tmax < 1) return LBQ_E_UNSUPPORTED;
+  int cus = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return LBQ_E_DEVICE;
+  S1Args A;
+  memset(&A, 0, sizeof(A));
+  A.mats[0] = st_mat(d_w, n, k, d_y);
+  A.nsingle = A.mats[0].tiles;
+  A.npair = 0;
+  A.hidden = k;
+  A.x0 = d_x;
+  const int tiles = A.nsingle;
+  int xw = cus < tiles ? cus : tiles;
+  if (xw < ceil_div(tiles, tmax)) return LBQ_E_UNSUPPORTED;
+  A.x_wgs = xw;
+  A.x_q = tiles / xw;
+  A.x_r = tiles % xw;
+  hipLaunchKernelGGL(stage1_kernel, dim3(xw), dim3(kThreads), 0, (hipStream_t)stream, A);
+  return hipGetLastError() == hipSuccess ? LBQ_OK : LBQ_E_DEVICE;
+}
