@@ -3,7 +3,7 @@
 // highlights") and INT4 g128 (the Acorn page, "int4 quantization quality: group quantization
 // (g=128)").
 //
-// A workgroup of four waves takes one 64-row tile over a slice of k (up to five super-groups of
+// A workgroup of eight waves takes one 64-row tile over a slice of k (up to five super-groups of
 // eight 128-weight groups: a 5120-deep product in one slice). A unit is one group of the tile: four sub-tiles of 16 rows, each
 // taken in four 32-deep steps of v_mfma_f32_16x16x32_bf16 with the activation vectors as the
 // rows of the A operand (vector m in row m) and 16 weight rows as the 16 columns of B. So the
@@ -27,7 +27,7 @@
 //  * Products of +-1 (Q1) or 1 + c/16 (INT4) and bf16 are exact and the matrix cores sum them in
 //    fp32; each group's sum is weighted by its fp16 scale and accumulated in fp32 (lane (n, h)
 //    holds vectors 4 h .. 4 h + 3 of row 16 t + n in accumulator t).
-//  * The four waves' sums are added in wave order; slices of k go through the split-K
+//  * The eight waves' sums are added in wave order; slices of k go through the split-K
 //    workspace, and the last workgroup of a tile adds them in slice order (deterministic).
 #include <hip/hip_runtime.h>
 
@@ -39,12 +39,17 @@ using namespace lbq;
 
 namespace {
 
-constexpr int kWaves = 4;
+// Eight waves of five units each (a 5120-deep slice): at 92 VGPRs five waves fit per SIMD, and a
+// wave's serial chain of units is half as long as with four waves of ten (measured: the batch-8
+// decode step 2.61 -> 2.48 ms, gate 17408x5120 at 4 vectors 12.8 -> 10.9 us). kWaves divides
+// both the units of a slice (40) and the vectors (16).
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxSupers = 5;                 // super-groups of one slice of k (5120 inputs)
-constexpr int kSlots = kMaxSupers * kSuper / kWaves;   // units per wave: 10
+constexpr int kSlots = kMaxSupers * kSuper / kWaves;   // units per wave: 5
 constexpr int kBlocksPerWave = (kMaxSupers + kWaves - 1) / kWaves;   // scale blocks staged
 constexpr int kMaxVec = 16;
+static_assert(kMaxSupers * kSuper % kWaves == 0 && kMaxVec % kWaves == 0, "wave split");
 constexpr int kQ1SuperBytes = kBlock * (1 + kSuper * kQ1GroupBlocks);
 constexpr int kI4SuperBytes = kBlock * (1 + kSuper * kI4GroupBlocks);
 
