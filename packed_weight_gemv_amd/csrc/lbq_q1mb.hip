@@ -3,7 +3,7 @@
 // highlights") and INT4 g128 (the Acorn page, "int4 quantization quality: group quantization
 // (g=128)").
 //
-// A workgroup of eight waves takes one 64-row tile over a slice of k (up to five super-groups of
+// A workgroup of eight waves (Q1; four for INT4) takes one 64-row tile over a slice of k (up to five super-groups of
 // eight 128-weight groups: a 5120-deep product in one slice). A unit is one group of the tile: four sub-tiles of 16 rows, each
 // taken in four 32-deep steps of v_mfma_f32_16x16x32_bf16 with the activation vectors as the
 // rows of the A operand (vector m in row m) and 16 weight rows as the 16 columns of B. So the
@@ -27,7 +27,7 @@
 //  * Products of +-1 (Q1) or 1 + c/16 (INT4) and bf16 are exact and the matrix cores sum them in
 //    fp32; each group's sum is weighted by its fp16 scale and accumulated in fp32 (lane (n, h)
 //    holds vectors 4 h .. 4 h + 3 of row 16 t + n in accumulator t).
-//  * The eight waves' sums are added in wave order; slices of k go through the split-K
+//  * The waves' sums are added in wave order; slices of k go through the split-K
 //    workspace, and the last workgroup of a tile adds them in slice order (deterministic).
 #include <hip/hip_runtime.h>
 
@@ -39,17 +39,22 @@ using namespace lbq;
 
 namespace {
 
-// Eight waves of five units each (a 5120-deep slice): at 92 VGPRs five waves fit per SIMD, and a
-// wave's serial chain of units is half as long as with four waves of ten (measured: the batch-8
-// decode step 2.61 -> 2.48 ms, gate 17408x5120 at 4 vectors 12.8 -> 10.9 us). kWaves divides
-// both the units of a slice (40) and the vectors (16).
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxSupers = 5;                 // super-groups of one slice of k (5120 inputs)
-constexpr int kSlots = kMaxSupers * kSuper / kWaves;   // units per wave: 5
-constexpr int kBlocksPerWave = (kMaxSupers + kWaves - 1) / kWaves;   // scale blocks staged
 constexpr int kMaxVec = 16;
-static_assert(kMaxSupers * kSuper % kWaves == 0 && kMaxVec % kWaves == 0, "wave split");
+// Waves per workgroup by format. Q1: eight waves of five units each (a 5120-deep slice) - at 92
+// VGPRs five waves fit per SIMD, and a wave's serial chain of units is half as long as with four
+// waves of ten (measured: the batch-8 decode step 2.61 -> 2.48 ms, gate 17408x5120 at 4 vectors
+// 12.8 -> 10.9 us). INT4: four waves of ten (its 64-byte unit records keep it at 130 VGPRs, three
+// waves per SIMD, and eight waves measured slower on the tall matrices: 12288x4096 at 8 vectors
+// 13.2 -> 16.4 us). The wave count divides both the units of a slice (40) and the vectors (16).
+template <int FMT>
+struct MbShape {
+  static constexpr int waves = FMT == 0 ? 8 : 4;
+  static constexpr int threads = 64 * waves;
+  static constexpr int slots = kMaxSupers * kSuper / waves;           // units per wave
+  static constexpr int blocks_per_wave = (kMaxSupers + waves - 1) / waves;   // scale blocks
+  static_assert(kMaxSupers * kSuper % waves == 0 && kMaxVec % waves == 0, "wave split");
+};
 constexpr int kQ1SuperBytes = kBlock * (1 + kSuper * kQ1GroupBlocks);
 constexpr int kI4SuperBytes = kBlock * (1 + kSuper * kI4GroupBlocks);
 
@@ -73,10 +78,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
 
+template <int W>
 struct MbLds {
   uint32_t lut[32];                         // 16 entries of four bf16 +-1
   uint8_t sblk[kMaxSupers][kBlock];         // scale blocks, as [group][row % 16][row / 16]
-  float red[kWaves][kMaxVec][kTileRows];    // per-wave sums [vector][row]
+  float red[W][kMaxVec][kTileRows];         // per-wave sums [wave][vector][row]
 };
 
 // Table byte offset (8 bytes per entry) of the 4-bit field at bits [8 q + 3, 8 q + 6] of `rot`.
@@ -202,13 +208,16 @@ struct MbArgs {
 
 // FMT 0: Q1_0_g128, 1: INT4 g128.
 template <int FMT>
-__global__ __launch_bounds__(kThreads) void mb_kernel(MbArgs A) {
+__global__ __launch_bounds__(MbShape<FMT>::threads) void mb_kernel(MbArgs A) {
+  constexpr int kWaves = MbShape<FMT>::waves;
+  constexpr int kSlots = MbShape<FMT>::slots;
+  constexpr int kBlocksPerWave = MbShape<FMT>::blocks_per_wave;
   constexpr int kSuperBytes = FMT == 0 ? kQ1SuperBytes : kI4SuperBytes;
   constexpr int kGroupBytes = FMT == 0 ? kQ1GroupBlocks * kBlock : kI4GroupBlocks * kBlock;
   // unit records requested ahead: all of the wave's for Q1 (16 bytes per lane each), two for
   // INT4 (64 bytes per lane each)
   constexpr int kAhead = FMT == 0 ? kSlots : 2;
-  __shared__ MbLds L;
+  __shared__ MbLds<kWaves> L;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, h = lane >> 4;
@@ -455,7 +464,8 @@ lbq_status mb_launch(const MbJob* jobs, int njobs, int batch, void* stream) {
         A.m[i].counters = counters + (uintptr_t)A.m[i].counters;
       }
   }
-  hipLaunchKernelGGL(mb_kernel<FMT>, dim3((unsigned)wgs), dim3(kThreads), 0, (hipStream_t)stream, A);
+  hipLaunchKernelGGL(mb_kernel<FMT>, dim3((unsigned)wgs), dim3(MbShape<FMT>::threads), 0,
+                     (hipStream_t)stream, A);
   return hipGetLastError() == hipSuccess ? LBQ_OK : LBQ_E_DEVICE;
 }
 }  // namespace
