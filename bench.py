@@ -627,28 +627,50 @@ def mlp2bit_bench(args, lbq, synth, torch, np, dev) -> int:
     """The 2-bit integer MLP through lbq_mlp_2bit_i16: 1024 input vectors of 256 int16 bucket
     counts (uniform 0..127) through the 256-192-128-40 network with uniform 2-bit codes, one
     launch per step, launches replayed from a HIP graph; logits and argmax are compared with the
-    oracle bit for bit."""
+    oracle bit for bit. Also timed, as cases: the same vectors through balanced codes (uniform
+    over 1..3, weights -1, 0, +1: the uniform codes' mean weight of -1/2 drives every ReLU input
+    negative, so their logits are all zero, and this case shows the time does not depend on the
+    values), and 65,536 vectors (throughput context; the first and last 1024 checked)."""
+    import oracle
+    dims = list(synth.MLP_DIMS)
     layers = synth.mlp2bit_layers()
-    xh = synth.mlp2bit_inputs()
-    B = xh.shape[0]
-    lw = [torch.from_numpy(lbq.lbq_pack_2bit(c)).to(dev) for c in layers]
-    x = torch.from_numpy(xh).to(dev)
-    logits = torch.empty((B, synth.MLP_DIMS[-1]), dtype=torch.int16, device=dev)
-    am = torch.empty((B,), dtype=torch.int32, device=dev)
+    balanced = []   # canonical bytes of codes uniform over 1..3 (four per byte, first code lowest)
+    for l in range(len(dims) - 1):
+        r = synth.rng(synth.W_MLP2BIT, l, 0, synth.KIND_STRESS)
+        v = r.integers(1, 4, size=(dims[l + 1], dims[l] // 4, 4)).astype(np.uint8)
+        balanced.append((v[..., 0] | v[..., 1] << 2 | v[..., 2] << 4 | v[..., 3] << 6)
+                        .astype(np.uint8))
     stream = torch.cuda.current_stream()
     cap = torch.cuda.Stream()
-    # one launch per step, 32 steps per replay of a HIP graph
-    us = graph_time_us(torch, lambda w: lbq.lbq_mlp_2bit_i16(w, synth.MLP_DIMS, x, logits, am,
-                                                             stream=cap),
-                       [lw] * 32, args, cap, stream)
-    import oracle
-    t0 = time.perf_counter()
-    ref_logits, ref_am = oracle.mlp_2bit(layers, list(synth.MLP_DIMS), xh)
-    dt = time.perf_counter() - t0
-    assert np.array_equal(logits.cpu().numpy(), ref_logits), "2-bit MLP logits differ"
-    assert np.array_equal(am.cpu().numpy(), ref_am), "2-bit MLP argmax differs"
-    tmacs = B * Z80_MACS_PER_EVAL / (us * 1e-6) / 1e12
-    log(f"mlp2bit: {us:.2f} us per launch of {B} vectors, {tmacs:.3f} T MAC/s, bit-exact")
+    cases = []
+    head = None
+    for name, codes, B in (("uniform codes", layers, 1024), ("balanced codes", balanced, 1024),
+                           ("uniform codes", layers, 65536)):
+        xh = synth.mlp2bit_inputs(batch=B)
+        lw = [torch.from_numpy(lbq.lbq_pack_2bit(c)).to(dev) for c in codes]
+        x = torch.from_numpy(xh).to(dev)
+        logits = torch.empty((B, dims[-1]), dtype=torch.int16, device=dev)
+        am = torch.empty((B,), dtype=torch.int32, device=dev)
+        # one launch per step, 32 steps per replay of a HIP graph
+        us = graph_time_us(torch, lambda w: lbq.lbq_mlp_2bit_i16(w, dims, x, logits, am,
+                                                                 stream=cap),
+                           [lw] * 32, args, cap, stream)
+        rows = np.arange(B) if B <= 1024 else np.r_[0:1024, B - 1024:B]
+        t0 = time.perf_counter()
+        ref_logits, ref_am = oracle.mlp_2bit(codes, dims, xh[rows])
+        dt = time.perf_counter() - t0
+        assert np.array_equal(logits.cpu().numpy()[rows], ref_logits), f"2-bit MLP logits differ ({name})"
+        assert np.array_equal(am.cpu().numpy()[rows], ref_am), f"2-bit MLP argmax differs ({name})"
+        tmacs = B * Z80_MACS_PER_EVAL / (us * 1e-6) / 1e12
+        log(f"mlp2bit {name}, {B} vectors: {us:.2f} us per launch, {tmacs:.3f} T MAC/s, "
+            f"bit-exact on {rows.size} vectors")
+        cases.append({"codes": name, "vectors": B, "us_per_launch": round(us, 3),
+                      "evals_per_s": round(B / (us * 1e-6), 1), "gmac_per_s": round(tmacs * 1e3, 1),
+                      "pct_of_dot2_issue_rate": round(100.0 * tmacs / ALU_DOT2_PEAK_TMACS, 2),
+                      "vectors_checked": int(rows.size)})
+        if head is None:
+            head = (us, B, tmacs, dt)
+    us, B, tmacs, dt = head
     out = {
         "metric": "2-bit integer MLP evaluations per second (1024 vectors, 256-192-128-40)",
         "value": round(B / (us * 1e-6), 1),
@@ -665,10 +687,11 @@ def mlp2bit_bench(args, lbq, synth, torch, np, dev) -> int:
         "gmac_per_s": round(tmacs * 1e3, 1),
         "config": {"workload": f"Z80-uLM-shaped 2-bit MLP, {B} vectors, 256-192-128-40",
                    "parallelism": "single GPU", "parity": "logits and argmax bit-exact"},
+        "cases": cases,
         "roofline": {"bound": "alu", "achieved": round(tmacs, 3), "peak": ALU_DOT2_PEAK_TMACS,
                      "unit": "T 2-bit MAC/s (v_dot2_i32_i16 issue rate)",
                      "frac": round(tmacs / ALU_DOT2_PEAK_TMACS, 4), "traffic": None,
-                     "kernel": "mlp2bit_kernel", "avg_launch_us": round(us, 3)},
+                     "kernel": "mlp2bit_lds_kernel", "avg_launch_us": round(us, 3)},
         "cpu_baseline": {"value": round(B / dt, 1), "unit": "evals/s", "cores": 1,
                          "kind": "oracle", "sample": f"all {B} vectors, one host thread"},
     }

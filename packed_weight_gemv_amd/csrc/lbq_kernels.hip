@@ -464,6 +464,8 @@ struct MlpArgs {
   int dims[LBQ_MLP_MAX_LAYERS + 1];
   int n_layers;
   int dword_rows;   // every row of every layer starts and ends on a dword boundary
+  int vec16;        // also: every layer's codes and x are 16-byte aligned, each layer's codes are
+                    // whole 16-byte pieces and dims[0] % 16 == 0 (the prologue's 16-byte path)
 };
 typedef short short2_t __attribute__((ext_vector_type(2)));
 
@@ -492,7 +494,49 @@ __global__ __launch_bounds__(kMlpThreads) void mlp2bit_lds_kernel(
   // codes of every layer: row r of layer l at wlds[woff[l] + r * kw], kw = ceil(k / 16) dwords,
   // assembled byte by byte from the canonical rows (k / 4 bytes each), zero bytes past the row
   int woff[LBQ_MLP_MAX_LAYERS];
-  {
+  const int d0 = P.dims[0], d0p = (d0 + 15) & ~15;
+  if (P.vec16) {
+    // Whole-dword rows, 16-byte pieces: the layers' codes are contiguous in LDS, so piece i of
+    // the concatenated layers goes to LDS piece i. Every piece of the codes and of this
+    // workgroup's input rows is requested before any is stored (one memory round trip instead
+    // of one per loop iteration).
+    int cum[LBQ_MLP_MAX_LAYERS + 1];   // first piece of each layer
+    cum[0] = 0;
+#pragma unroll
+    for (int l = 0; l < LBQ_MLP_MAX_LAYERS; ++l) {
+      woff[l] = 4 * cum[l];
+      cum[l + 1] = cum[l] + (l < P.n_layers ? P.dims[l + 1] * (P.dims[l] / 16) / 4 : 0);
+    }
+    const int total = cum[LBQ_MLP_MAX_LAYERS];
+    constexpr int kLoads = kMlpLdsBytes / 16 / kMlpThreads;
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    u32x4_t cv[kLoads];
+#pragma unroll
+    for (int it = 0; it < kLoads; ++it) {
+      const int i = tid + it * kMlpThreads;
+      if (i < total) {
+        const uint8_t* src = P.w[0];
+        int base = 0;
+#pragma unroll
+        for (int l = 1; l < LBQ_MLP_MAX_LAYERS; ++l)
+          if (l < P.n_layers && i >= cum[l]) {
+            src = P.w[l];
+            base = cum[l];
+          }
+        cv[it] = ((const u32x4_t*)src)[i - base];
+      }
+    }
+    const int xq = d0 / 8;   // 16-byte pieces of an input row (kMlpVec * xq <= kMlpThreads)
+    const int xr = tid / xq, xp = tid - xr * xq;
+    u32x4_t xv = {0u, 0u, 0u, 0u};
+    if (xr < nv) xv = ((const u32x4_t*)(x + (size_t)(v0 + xr) * d0))[xp];
+#pragma unroll
+    for (int it = 0; it < kLoads; ++it) {
+      const int i = tid + it * kMlpThreads;
+      if (i < total) ((u32x4_t*)wlds)[i] = cv[it];
+    }
+    if (xr < kMlpVec) *(u32x4_t*)&act[0][xr][8 * xp] = xv;
+  } else {
     int off = 0;
     for (int l = 0; l < P.n_layers; ++l) {
       woff[l] = off;
@@ -513,11 +557,10 @@ __global__ __launch_bounds__(kMlpThreads) void mlp2bit_lds_kernel(
       }
       off += nout * kw;
     }
-  }
-  const int d0 = P.dims[0], d0p = (d0 + 15) & ~15;
-  for (int i = tid; i < kMlpVec * d0p; i += kMlpThreads) {
-    const int v = i / d0p, j = i - v * d0p;
-    act[0][v][j] = (v < nv && j < d0) ? x[(size_t)(v0 + v) * d0 + j] : (int16_t)0;
+    for (int i = tid; i < kMlpVec * d0p; i += kMlpThreads) {
+      const int v = i / d0p, j = i - v * d0p;
+      act[0][v][j] = (v < nv && j < d0) ? x[(size_t)(v0 + v) * d0 + j] : (int16_t)0;
+    }
   }
   int cur = 0;
   for (int l = 0; l < P.n_layers; ++l) {
@@ -1057,6 +1100,9 @@ extern "C" lbq_status lbq_mlp_2bit_i16(const void* const* d_layer_w, const int32
   P.dword_rows = 1;
   for (int l = 0; l < n_layers; ++l)
     if (dims[l] % 16 != 0 || (uintptr_t)d_layer_w[l] % 4 != 0) P.dword_rows = 0;
+  P.vec16 = P.dword_rows && dims[0] % 16 == 0 && (uintptr_t)d_x % 16 == 0;
+  for (int l = 0; l < n_layers; ++l)
+    if ((uintptr_t)d_layer_w[l] % 16 != 0 || (dims[l + 1] * (dims[l] / 16)) % 4 != 0) P.vec16 = 0;
   size_t lds_words = 0;
   for (int l = 0; l < n_layers; ++l) lds_words += (size_t)dims[l + 1] * ((dims[l] + 15) / 16);
   if (lds_words * 4 <= (size_t)kMlpLdsBytes)
