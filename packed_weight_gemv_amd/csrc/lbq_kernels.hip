@@ -439,29 +439,32 @@ __global__ __launch_bounds__(64 * kI4Waves) void i4_gemv_kernel(
   if (supers > 1) splitk_finish(partial, counters + tile, y, n, np, supers, batch, row, wave == 0);
 }
 
-// One vector, k <= 4096: one workgroup per 64-row tile over the whole of k, S super-groups of
-// four waves each (the waves of super-group sg do what a workgroup of i4_gemv_kernel does for
-// (tile, sg)). The 4 S waves' sums are added in LDS in wave order and the row is written as
-// bf16: no split-K partial sums, no finish and no workspace. A whole tile (up to 135 KiB of
-// codes) streams into one compute unit; with one workgroup per tile the launch has no fabric
-// round trips after its loads.
+// One vector: a workgroup takes S consecutive super-groups of one 64-row tile, four waves each
+// (the waves of a super-group do what a workgroup of i4_gemv_kernel does for it). The 4 S waves'
+// sums are added in LDS in wave order; with one slice of S super-groups per tile (k <= 1024 S)
+// the row is written as bf16 directly, otherwise each slice stores its fp32 partial sums and the
+// last workgroup of the tile adds them in slice order (splitk_finish). Fewer, deeper slices than
+// i4_gemv_kernel's one workgroup per super-group: fewer partial sums and fewer workgroups to
+// finish, each streaming up to 135 KiB of codes.
 template <int S>
 __global__ __launch_bounds__(64 * kI4Waves * S) void i4_gemv_tile_kernel(
     const uint8_t* __restrict__ w, const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
-    int n, int k, int groups, long long tile_bytes) {
+    float* __restrict__ partial, unsigned* __restrict__ counters, int n, int k, int np,
+    int groups, int supers, int splits, long long tile_bytes) {
   __shared__ __attribute__((aligned(16))) uint32_t xs[S * kSuper][kGroup / 2];   // bf16 pairs
   __shared__ float gsum[S * kSuper];
   __shared__ float red[kI4Waves * S][64];
-  const int tile = blockIdx.x;
+  const int tile = blockIdx.x, slice = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int sg = wave / kI4Waves, wq = wave - sg * kI4Waves;
-  const int g0 = sg * kSuper;
-  const int gcount = min(kSuper, groups - g0);
+  const int ls = wave / kI4Waves, wq = wave - ls * kI4Waves;   // super-group of the slice, wave in it
+  const int sg = slice * S + ls;                                // super-group of the row
+  const int g0 = sg * kSuper, l0 = ls * kSuper;                 // first group: row / LDS
+  const int gcount = sg < supers ? min(kSuper, groups - g0) : 0;
   const int gw = kI4GroupsPerWave * wq;
   const uint8_t* base = w + (size_t)tile * tile_bytes + (size_t)sg * (kBlock * (1 + kSuper * kI4GroupBlocks));
   u32x4 wv[kI4GroupsPerWave][4];
   i4_load_wave_groups(base, gw, gcount, lane, wv);
-  const uint32_t scw = *(const uint32_t*)(base + lane * 16 + 4 * wq);
+  const uint32_t scw = gcount > 0 ? *(const uint32_t*)(base + lane * 16 + 4 * wq) : 0u;
   const float scale[2] = {f16_to_f32(scw & 0xFFFF), f16_to_f32(scw >> 16)};
   const int row = tile * kTileRows + lane;
   // staging lane map: lanes 0-15 / 16-31 hold 8 values each of groups gw / gw + 1 (lanes 32-63
@@ -482,8 +485,8 @@ __global__ __launch_bounds__(64 * kI4Waves * S) void i4_gemv_tile_kernel(
   if (qown) {
     u32x4 v;
     v.x = xv[0]; v.y = xv[1]; v.z = xv[2]; v.w = xv[3];
-    *(u32x4*)&xs[g0 + qg][4 * qpiece] = v;
-    if (qpiece == 0) gsum[g0 + qg] = sx;
+    *(u32x4*)&xs[l0 + qg][4 * qpiece] = v;
+    if (qpiece == 0) gsum[l0 + qg] = sx;
   }
   __syncthreads();
   float acc = 0.f;
@@ -502,14 +505,14 @@ __global__ __launch_bounds__(64 * kI4Waves * S) void i4_gemv_tile_kernel(
         const uint32_t t1 = ((sv >> 1) & 0x00780078u) | 0x3F803F80u;
         const uint32_t t2 = ((sv >> 5) & 0x00780078u) | 0x3F803F80u;
         const uint32_t t3 = ((sv >> 9) & 0x00780078u) | 0x3F803F80u;
-        const u32x4 xq = *(const u32x4*)&xs[g0 + gi][16 * m + 4 * ww];
+        const u32x4 xq = *(const u32x4*)&xs[l0 + gi][16 * m + 4 * ww];
         a = dot2_bf16(t0, xq.x, a);
         a = dot2_bf16(t1, xq.y, a);
         a = dot2_bf16(t2, xq.z, a);
         a = dot2_bf16(t3, xq.w, a);
       }
     }
-    acc = fmaf(scale[i], fmaf(16.f, a, -24.f * gsum[g0 + gi]), acc);
+    acc = fmaf(scale[i], fmaf(16.f, a, -24.f * gsum[l0 + gi]), acc);
   }
   red[wave][lane] = acc;
   __syncthreads();
@@ -517,8 +520,13 @@ __global__ __launch_bounds__(64 * kI4Waves * S) void i4_gemv_tile_kernel(
     float sum = red[0][lane];
 #pragma unroll
     for (int v = 1; v < kI4Waves * S; ++v) sum += red[v][lane];
-    if (row < n) y[row] = f32_to_bf16(sum);
+    if (splits == 1) {
+      if (row < n) y[row] = f32_to_bf16(sum);
+    } else {
+      st_coherent(&partial[(size_t)slice * np + row], sum);
+    }
   }
+  if (splits > 1) splitk_finish(partial, counters + tile, y, n, np, splits, 1, row, wave == 0);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1231,22 +1239,34 @@ static lbq_status gemv_common(Fmt fmt, const void* d_w, int32_t n, int32_t k,
   if (batch >= 2 && (uintptr_t)d_x % 16 == 0)
     return fmt == Fmt::Q1 ? lbq_gemm_q1g128(d_w, n, k, d_x, d_y, batch, stream)
                           : lbq_gemm_i4g128(d_w, n, k, d_x, d_y, batch, stream);
-  // one vector, INT4, k <= 4096, at least half as many tiles as compute units: one workgroup per
-  // tile over the whole of k (no split-K; 12288 x 4096 9.6 us, was 12.0). Matrices with fewer
-  // tiles keep the split-K kernel below, which spreads them over more compute units (4096 x 4096
-  // 7.6 us there, 8.5 us with a workgroup per tile).
-  if (fmt == Fmt::I4 && batch == 1 && g.supers <= 4 && 2 * g.tiles >= device_cus()) {
-    const dim3 tg((unsigned)g.tiles);
-    const dim3 tb((unsigned)(64 * kI4Waves * g.supers));
+  // one vector, INT4: slices of S = 4 (else 2) super-groups per workgroup when that still gives
+  // at least half as many workgroups as compute units (12288 x 4096: one slice per tile, 9.6 us,
+  // was 12.0); otherwise the per-super-group kernel below, which spreads small matrices over
+  // more compute units (4096 x 4096 7.6 us there, 8.5 us with a workgroup per tile)
+  if (fmt == Fmt::I4 && batch == 1) {
+    const int half = (device_cus() + 1) / 2;
+    int S = 0;
+    if (g.tiles * ((g.supers + 3) / 4) >= half) S = 4;
+    else if (g.supers > 1 && g.tiles * ((g.supers + 1) / 2) >= half) S = 2;
+    if (S > 0) {
+      const int splits = (int)((g.supers + S - 1) / S);
+      unsigned* counters = nullptr;
+      float* partials = nullptr;
+      if (splits > 1) {
+        if (g.tiles * sizeof(unsigned) > kCounterBytes) return LBQ_E_SHAPE;
+        const lbq_status st = get_workspace((size_t)splits * g.np * sizeof(float), s, &counters,
+                                            &partials);
+        if (st != LBQ_OK) return st;
+      }
+      const dim3 tg((unsigned)g.tiles, (unsigned)splits);
 #define LAUNCH_I4T(S_)                                                                           \
-  hipLaunchKernelGGL(i4_gemv_tile_kernel<S_>, tg, tb, 0, s, (const uint8_t*)d_w, d_x, d_y, n, k,  \
-                     (int)g.groups, (long long)g.tile_bytes)
-    if (g.supers == 1) LAUNCH_I4T(1);
-    else if (g.supers == 2) LAUNCH_I4T(2);
-    else if (g.supers == 3) LAUNCH_I4T(3);
-    else LAUNCH_I4T(4);
+  hipLaunchKernelGGL(i4_gemv_tile_kernel<S_>, tg, dim3(64 * kI4Waves * S_), 0, s,                 \
+                     (const uint8_t*)d_w, d_x, d_y, partials, counters, n, k, (int)g.np,         \
+                     (int)g.groups, (int)g.supers, splits, (long long)g.tile_bytes)
+      if (S == 4) LAUNCH_I4T(4); else LAUNCH_I4T(2);
 #undef LAUNCH_I4T
-    return launch_status();
+      return launch_status();
+    }
   }
   // the split-K workspace of this stream
   unsigned* counters = nullptr;
