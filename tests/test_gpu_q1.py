@@ -147,3 +147,22 @@ def test_parity_batches_with_rows_not_16_byte_aligned(lbq, batch):
     torch.cuda.synchronize()
     ref, l1 = oracle.gemv_q1g128(m.signs, m.scales, x)
     check_within(bits(y), ref, l1, f"q1 unaligned batch {batch}")
+
+
+@pytest.mark.parametrize("offset,n,k", [(2, 200, 2176), (4, 200, 2176), (4, 1, 7168), (2, 64, 7168)])
+def test_parity_one_vector_at_4_and_8_byte_alignment(lbq, offset, n, k):
+    # one vector at 4 bytes past an aligned address (the per-row kernel) and at 8 bytes past it
+    # (the stage-1 lookup kernel, which needs 8-byte aligned input; k = 7168 is its table
+    # capacity)
+    m = synth.q1_matrix(n, k, workload=27, matrix=offset)
+    x = synth.activations(1, k, workload=27, extra=offset)
+    buf = torch.zeros(k + 16, dtype=torch.int16, device="cuda:0")
+    xv = buf[offset:offset + k].view(1, k)
+    assert xv.data_ptr() % 16 == 2 * offset
+    xv.copy_(to_dev(x))
+    w = to_dev(lbq.lbq_pack_q1g128(m.signs, m.scales))
+    y = empty_bf16(1, n)
+    lbq.lbq_gemv_q1g128(w, n, k, xv, y)
+    torch.cuda.synchronize()
+    ref, l1 = oracle.gemv_q1g128(m.signs, m.scales, x)
+    check_within(bits(y), ref, l1, f"q1 one vector at offset {2 * offset} B, {n}x{k}")
