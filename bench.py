@@ -158,7 +158,7 @@ def parse():
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly")
-    ap.add_argument("--cpu-layers", type=int, default=2,
+    ap.add_argument("--cpu-layers", type=int, default=40,
                     help="layers of the stream the CPU oracle baseline runs on all host cores "
                          "(0 = skip the baseline, the sampled parity and the chain check)")
     ap.add_argument("--rounds", type=int, default=3,
