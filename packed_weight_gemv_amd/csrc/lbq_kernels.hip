@@ -539,10 +539,11 @@ __global__ __launch_bounds__(64 * kI4Waves * S) void i4_gemv_tile_kernel(
 //
 // mlp2bit_lds_kernel: the codes of all layers are copied into LDS once per workgroup, each row
 // padded with zero bytes to whole dwords (16 codes); activations are padded with zeros to
-// match, so a padded code (weight -2) meets a zero input. Four lanes share a neuron, each taking
-// a quarter of its row; a lane decodes a pair of codes once into two int16 weights (c - 2) and
-// applies it to every vector with v_dot2_i32_i16 (the activation pair read is the same for the
-// 64 lanes of a wave, an LDS broadcast). Networks whose padded codes exceed kMlpLdsBytes use
+// match, so a padded code (weight -2) meets a zero input. Four lanes share a neuron, lane q
+// taking dwords q, q + 4, ... of its row; a lane decodes a pair of codes once into two int16
+// weights (c - 2) and applies it to every vector with v_dot2_i32_i16 (the 16 lanes of a wave
+// with the same q read the same activation pair, an LDS broadcast, and the four q fall on
+// different banks). Networks whose padded codes exceed kMlpLdsBytes use
 // mlp2bit_kernel, which reads the codes from global memory.
 // ---------------------------------------------------------------------------------------------
 constexpr int kMlpVec = 4;
@@ -576,8 +577,11 @@ __device__ __forceinline__ void mlp_store_logits(const int16_t (*act)[kMlpPad], 
 __global__ __launch_bounds__(kMlpThreads) void mlp2bit_lds_kernel(
     MlpArgs P, const int16_t* __restrict__ x, int16_t* __restrict__ logits,
     int32_t* __restrict__ argmax, int batch) {
-  __shared__ __attribute__((aligned(16))) uint32_t wlds[kMlpLdsBytes / 4];
-  __shared__ __attribute__((aligned(16))) int16_t act[2][kMlpVec][kMlpPad];
+  // the activations at the bottom of LDS: their reads in the inner loop then fit the LDS
+  // instructions' 16-bit immediate offsets (no address add per read); the codes above them
+  __shared__ __attribute__((aligned(16))) uint32_t mlp_lds[kMlpVec * kMlpPad + kMlpLdsBytes / 4];
+  int16_t (*act)[kMlpVec][kMlpPad] = reinterpret_cast<int16_t (*)[kMlpVec][kMlpPad]>(mlp_lds);
+  uint32_t* wlds = mlp_lds + kMlpVec * kMlpPad;   // 2 x kMlpVec x kMlpPad int16 below
   const int tid = threadIdx.x;
   const int v0 = blockIdx.x * kMlpVec;
   const int nv = min(kMlpVec, batch - v0);
@@ -655,7 +659,6 @@ __global__ __launch_bounds__(kMlpThreads) void mlp2bit_lds_kernel(
   int cur = 0;
   for (int l = 0; l < P.n_layers; ++l) {
     const int nout = P.dims[l + 1], kw = (P.dims[l] + 15) / 16;
-    const int per = (kw + 3) / 4;   // dwords per quarter row
     const bool relu = l < P.n_layers - 1;
     const int noutp = (nout + 15) & ~15;
     __syncthreads();
@@ -666,8 +669,9 @@ __global__ __launch_bounds__(kMlpThreads) void mlp2bit_lds_kernel(
       for (int v = 0; v < kMlpVec; ++v) acc[v] = 0;
       if (r < nout) {
         const uint32_t* wr = wlds + woff[l] + r * kw;
-        const int j1 = min(kw, (part + 1) * per);
-        for (int j = part * per; j < j1; ++j) {
+        // every fourth dword of the row: the four lanes' activation reads are 32 bytes apart,
+        // on different banks
+        for (int j = part; j < kw; j += 4) {
           const uint32_t d = wr[j];
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
