@@ -97,6 +97,19 @@ def test_odd_shapes_and_depths(lbq, dims, batch):
                                                   extra=47))
 
 
+@pytest.mark.parametrize("dims", [[1024, 256, 512], [1024, 256, 516]])
+def test_codes_at_the_lds_capacity(lbq, dims):
+    """Padded codes of exactly 96 KiB (256 x 64 + 512 x 16 dwords: the largest network the
+    LDS kernel takes, its codes reaching the top of the workgroup's LDS above the activations)
+    and 256 bytes more (the kernel that reads the codes from global memory); 9 vectors, so the
+    last workgroup carries one."""
+    r = np.random.default_rng(48)
+    codes = [_codes_from_values(r.integers(1, 4, size=(dims[l + 1], dims[l])))
+             for l in range(len(dims) - 1)]
+    _check(lbq, codes, dims, synth.mlp2bit_inputs(batch=9, width=dims[0], lo=-3000, hi=3000,
+                                                  extra=49))
+
+
 def test_argmax_optional(lbq):
     dims = list(synth.MLP_DIMS)
     codes = synth.mlp2bit_layers(extra=48)
